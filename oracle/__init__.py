@@ -1,0 +1,132 @@
+"""Plain CPU reference (oracle) for the flash-attention training forward.
+
+TEST INFRASTRUCTURE ONLY: only tests/, the smoke check of __graft_entry__ and
+the bench's cpu_baseline leg may import this package. It shares no code with
+the GPU path (flash_attention_forward_fa_amd) and never imports it.
+
+The arithmetic lives in fa_oracle.c (single precision, following the CPU
+oracle of the method's page, "mlx-native 0.9.0",
+tests/test_flash_attn_train.rs, section "CPU oracle - forward O + logsumexp
+L"). This wrapper widens bf16 inputs to f32 (exact), calls it, and rounds O
+to bf16 the way that page's oracle_for_bf16 helper does.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+_lib = None
+
+
+def _bind(path):
+    lib = ctypes.CDLL(path)
+    i64, vp = ctypes.c_int64, ctypes.c_void_p
+    lib.fa_oracle_fwd.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, i64,
+                                  ctypes.c_float, ctypes.c_int, vp, vp, ctypes.c_int]
+    lib.fa_oracle_fwd.restype = ctypes.c_int
+    lib.fa_oracle_fwd_rows.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, i64,
+                                       ctypes.c_float, ctypes.c_int, vp, i64, vp, vp,
+                                       ctypes.c_int]
+    lib.fa_oracle_fwd_rows.restype = ctypes.c_int
+    lib.fa_oracle_round_bf16.argtypes = [vp, vp, i64]
+    lib.fa_oracle_round_bf16.restype = None
+    return lib
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_build.LIB):
+            _build.build()
+        _lib = _bind(_build.LIB)
+    return _lib
+
+
+def default_threads():
+    n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def widen_bf16(bits):
+    """bf16 bit patterns (uint16) -> float32 values, exact."""
+    b = np.ascontiguousarray(bits, dtype=np.uint16)
+    return (b.astype(np.uint32) << 16).view(np.float32)
+
+
+def round_bf16(x, lib=None):
+    """float32 -> bf16 bit patterns (uint16), round to nearest even."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty(x.shape, dtype=np.uint16)
+    if x.size:
+        (lib or _load()).fa_oracle_round_bf16(x.ctypes.data, out.ctypes.data, x.size)
+    return out
+
+
+def _f32(a):
+    if a is None:
+        return None
+    a = np.asarray(a)
+    if a.dtype == np.uint16:
+        return widen_bf16(a)
+    return np.ascontiguousarray(a, dtype=np.float32)
+
+
+def _ptr(a):
+    return None if a is None or a.size == 0 else a.ctypes.data
+
+
+def _check(rc, what):
+    if rc != 0:
+        raise ValueError(f"{what} rejected its arguments (code {rc})")
+
+
+def fwd(q, k, v, mask, B, H, Hkv, ql, kl, D, scale, causal, n_threads=None, lib=None):
+    """Full forward. q/k/v: bf16 bits (uint16) or float32 arrays; mask f32 or None.
+
+    Returns (O_f32 [B,H,ql,D], O_bf16_bits [B,H,ql,D], L [B,H,ql])."""
+    qf, kf, vf, mf = _f32(q), _f32(k), _f32(v), _f32(mask)
+    O = np.empty((B, H, ql, D), dtype=np.float32)
+    L = np.empty((B, H, ql), dtype=np.float32)
+    lib = lib or _load()
+    rc = lib.fa_oracle_fwd(_ptr(qf), _ptr(kf), _ptr(vf), _ptr(mf), B, H, Hkv, ql, kl, D,
+                               float(scale), int(bool(causal)), _ptr(O), _ptr(L),
+                               n_threads or default_threads())
+    _check(rc, "fa_oracle_fwd")
+    return O, round_bf16(O, lib), L
+
+
+def fwd_rows(q, k, v, mask, B, H, Hkv, ql, kl, D, scale, causal, rows, n_threads=None,
+             lib=None):
+    """Selected flat rows ((b*H + h)*ql + i). Returns (O_f32 [n,D], O_bf16 [n,D], L [n])."""
+    qf, kf, vf, mf = _f32(q), _f32(k), _f32(v), _f32(mask)
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    n = rows.size
+    O = np.empty((n, D), dtype=np.float32)
+    L = np.empty((n,), dtype=np.float32)
+    lib = lib or _load()
+    rc = lib.fa_oracle_fwd_rows(_ptr(qf), _ptr(kf), _ptr(vf), _ptr(mf), B, H, Hkv, ql, kl,
+                                    D, float(scale), int(bool(causal)), _ptr(rows), n, _ptr(O),
+                                    _ptr(L), n_threads or default_threads())
+    _check(rc, "fa_oracle_fwd_rows")
+    return O, round_bf16(O, lib), L
+
+
+def bind(lib_path):
+    """A fwd(...) callable over another build of fa_oracle.c (used by the
+    mutation tests, which plant mistakes in a copy of the source)."""
+    lib = _bind(lib_path)
+
+    def f(*args, **kw):
+        return fwd(*args, lib=lib, **kw)
+    return f
+
+
+def fwd_workload(w, inputs, rows=None, n_threads=None):
+    """Oracle on a fagen.Workload and its generated inputs (all rows, or `rows`)."""
+    args = (inputs["q"], inputs["k"], inputs["v"], inputs["mask"],
+            w.B, w.H, w.Hkv, w.ql, w.kl, w.D, w.scale, w.causal)
+    if rows is None:
+        return fwd(*args, n_threads=n_threads)
+    return fwd_rows(*args, rows, n_threads=n_threads)

@@ -1,0 +1,240 @@
+/*
+ * fa_oracle.c - plain CPU reference for the flash-attention training forward.
+ *
+ * TEST INFRASTRUCTURE ONLY. Only the tests, the smoke check and the CPU
+ * baseline of the bench may call this code. It shares no code, header,
+ * constant or helper with the GPU path.
+ *
+ * What it computes follows the CPU oracle on the method's page
+ * ("mlx-native 0.9.0", tests/test_flash_attn_train.rs, section "CPU oracle -
+ * forward O + logsumexp L", function sdpa_reference_with_logsumexp), restated
+ * here in single precision:
+ *
+ *   for every batch b, query head h, query row i (kv head = h / (H / Hkv)):
+ *     s_j = (sum_d q[i,d] * k[j,d]) * (scale * log2 e)       dot left to right
+ *     s_j += log2 e * mask[i,j]                               if a mask is given
+ *     s_j = -inf   for j > max(kl - ql, 0) + i                if causal
+ *     m   = max(-FLT_MAX / 2, max_j s_j)                      finite sentinel
+ *     p_j = exp2(s_j - m),  S = sum_j p_j                     left to right
+ *     L_i = m * ln 2 + ln S                                   (S = 0 -> -inf)
+ *     O_i = sum_j (p_j / S') v_j,  S' = (S == 0 ? 1 : S)       left to right
+ *
+ * The mask is additive in natural-log units (hence the log2 e factor in the
+ * base-2 score space). The causal alignment is bottom-right with the offset
+ * clamped at zero, as on the page (kl.saturating_sub(ql) + q_pos). O is
+ * returned in f32; fa_oracle_round_bf16 rounds it to bf16 the way the page's
+ * oracle_for_bf16 helper does before comparing against a bf16 output.
+ *
+ * Arithmetic is IEEE f32 with no contraction (built with -ffp-contract=off),
+ * exp2f/logf from the C library.
+ */
+#include <float.h>
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+static const float ORACLE_LOG2E = 1.44269504088896340736f;
+static const float ORACLE_LN2 = 0.693147180559945309417f;
+
+typedef struct {
+    const float *q, *k, *v, *mask;
+    int64_t H, Hkv, ql, kl, D;
+    float scale;
+    int causal;
+} oracle_problem;
+
+/* One query row, flat index row = (b*H + h)*ql + i. o_row gets D floats. */
+static void oracle_row(const oracle_problem *p, int64_t row, float *o_row, float *l_out,
+                       float *s)
+{
+    const int64_t D = p->D, kl = p->kl, ql = p->ql;
+    const int64_t i = row % ql;
+    const int64_t bh = row / ql;
+    const int64_t h = bh % p->H;
+    const int64_t b = bh / p->H;
+    const int64_t kvh = h / (p->H / p->Hkv);
+    const float q_scale = p->scale * ORACLE_LOG2E;
+    const float *qr = p->q + row * D;
+    const float *kh = p->k + (b * p->Hkv + kvh) * kl * D;
+    const float *vh = p->v + (b * p->Hkv + kvh) * kl * D;
+
+    /* scaled dot products in base-2 units */
+    for (int64_t j = 0; j < kl; ++j) {
+        float dot = 0.0f;
+        for (int64_t d = 0; d < D; ++d)
+            dot += qr[d] * kh[j * D + d];
+        s[j] = dot * q_scale;
+    }
+    /* additive mask, natural-log units converted to base 2 */
+    if (p->mask) {
+        const float *mr = p->mask + row * kl;
+        for (int64_t j = 0; j < kl; ++j)
+            s[j] += ORACLE_LOG2E * mr[j];
+    }
+    /* causal: key j is visible to row i iff j <= max(kl - ql, 0) + i */
+    if (p->causal) {
+        const int64_t q_abs = (kl > ql ? kl - ql : 0) + i;
+        for (int64_t j = q_abs + 1; j < kl; ++j)
+            s[j] = -INFINITY;
+    }
+    /* row max with the finite sentinel -FLT_MAX/2 */
+    float m = -FLT_MAX / 2.0f;
+    for (int64_t j = 0; j < kl; ++j)
+        if (s[j] > m)
+            m = s[j];
+    /* exponentials (base 2) and their sum */
+    float sum = 0.0f;
+    for (int64_t j = 0; j < kl; ++j) {
+        s[j] = exp2f(s[j] - m);
+        sum += s[j];
+    }
+    *l_out = m * ORACLE_LN2 + logf(sum);
+    /* normalised weighted sum of V rows; per output element the terms are
+       added in key order, exactly as a d-outer / j-inner loop would */
+    const float safe = (sum == 0.0f) ? 1.0f : sum;
+    for (int64_t d = 0; d < D; ++d)
+        o_row[d] = 0.0f;
+    for (int64_t j = 0; j < kl; ++j) {
+        const float w = s[j] / safe;
+        const float *vr = vh + j * D;
+        for (int64_t d = 0; d < D; ++d)
+            o_row[d] += w * vr[d];
+    }
+}
+
+typedef struct {
+    const oracle_problem *p;
+    const int64_t *rows; /* NULL: rows are 0..n-1 */
+    int64_t begin, end;
+    float *O, *L;
+    int failed;
+} oracle_job;
+
+static void *oracle_worker(void *arg)
+{
+    oracle_job *j = (oracle_job *)arg;
+    float *s = (float *)malloc(sizeof(float) * (size_t)(j->p->kl > 0 ? j->p->kl : 1));
+    if (!s) {
+        j->failed = 1;
+        return NULL;
+    }
+    for (int64_t t = j->begin; t < j->end; ++t) {
+        int64_t row = j->rows ? j->rows[t] : t;
+        oracle_row(j->p, row, j->O + t * j->p->D, j->L + t, s);
+    }
+    free(s);
+    return NULL;
+}
+
+static int oracle_validate(const float *q, const float *k, const float *v, int64_t B,
+                           int64_t H, int64_t Hkv, int64_t ql, int64_t kl, int64_t D)
+{
+    if (B < 0 || ql < 0 || kl < 0 || H < 1 || Hkv < 1 || D < 1)
+        return 2;
+    if (H % Hkv != 0)
+        return 3;
+    if (B * H * ql > 0 && !q)
+        return 1;
+    if (B * Hkv * kl > 0 && (!k || !v))
+        return 1;
+    return 0;
+}
+
+static int oracle_run(const oracle_problem *p, const int64_t *rows, int64_t n_rows, float *O,
+                      float *L, int n_threads)
+{
+    if (n_rows <= 0)
+        return 0;
+    if (!O || !L)
+        return 1;
+    if (n_threads < 1)
+        n_threads = 1;
+    if (n_threads > 256)
+        n_threads = 256;
+    if (n_threads > n_rows)
+        n_threads = (int)n_rows;
+    oracle_job jobs[256];
+    pthread_t tid[256];
+    for (int t = 0; t < n_threads; ++t) {
+        jobs[t].p = p;
+        jobs[t].rows = rows;
+        jobs[t].begin = n_rows * t / n_threads;
+        jobs[t].end = n_rows * (t + 1) / n_threads;
+        jobs[t].O = O;
+        jobs[t].L = L;
+        jobs[t].failed = 0;
+    }
+    int started = 0;
+    for (int t = 1; t < n_threads; ++t) {
+        if (pthread_create(&tid[t], NULL, oracle_worker, &jobs[t]) != 0)
+            break;
+        started = t;
+    }
+    /* rows of threads that could not be started are done on this thread */
+    for (int t = started + 1; t < n_threads; ++t)
+        oracle_worker(&jobs[t]);
+    oracle_worker(&jobs[0]);
+    for (int t = 1; t <= started; ++t)
+        pthread_join(tid[t], NULL);
+    for (int t = 0; t < n_threads; ++t)
+        if (jobs[t].failed)
+            return 4;
+    return 0;
+}
+
+/*
+ * Full forward. Inputs are f32 host arrays (bf16 values widened exactly):
+ * q [B,H,ql,D], k/v [B,Hkv,kl,D], mask [B,H,ql,kl] or NULL.
+ * Outputs: O [B,H,ql,D] f32, L [B,H,ql] f32.
+ * Returns 0 on success, 1 null pointer, 2 bad size, 3 H % Hkv != 0,
+ * 4 out of host memory.
+ */
+int fa_oracle_fwd(const float *q, const float *k, const float *v, const float *mask, int64_t B,
+                  int64_t H, int64_t Hkv, int64_t ql, int64_t kl, int64_t D, float scale,
+                  int causal, float *O, float *L, int n_threads)
+{
+    int rc = oracle_validate(q, k, v, B, H, Hkv, ql, kl, D);
+    if (rc)
+        return rc;
+    oracle_problem p = {q, k, v, mask, H, Hkv, ql, kl, D, scale, causal};
+    return oracle_run(&p, NULL, B * H * ql, O, L, n_threads);
+}
+
+/*
+ * Selected rows only: rows[t] is a flat row index (b*H + h)*ql + i; O gets
+ * [n_rows, D] and L [n_rows]. Same inputs and return codes as fa_oracle_fwd,
+ * plus 2 when a row index is out of range.
+ */
+int fa_oracle_fwd_rows(const float *q, const float *k, const float *v, const float *mask,
+                       int64_t B, int64_t H, int64_t Hkv, int64_t ql, int64_t kl, int64_t D,
+                       float scale, int causal, const int64_t *rows, int64_t n_rows, float *O,
+                       float *L, int n_threads)
+{
+    int rc = oracle_validate(q, k, v, B, H, Hkv, ql, kl, D);
+    if (rc)
+        return rc;
+    if (n_rows > 0 && !rows)
+        return 1;
+    for (int64_t t = 0; t < n_rows; ++t)
+        if (rows[t] < 0 || rows[t] >= B * H * ql)
+            return 2;
+    oracle_problem p = {q, k, v, mask, H, Hkv, ql, kl, D, scale, causal};
+    return oracle_run(&p, rows, n_rows, O, L, n_threads);
+}
+
+/* f32 -> bf16 bits, round to nearest, ties to even (NaN stays a quiet NaN). */
+void fa_oracle_round_bf16(const float *x, uint16_t *out, int64_t n)
+{
+    for (int64_t t = 0; t < n; ++t) {
+        uint32_t u;
+        memcpy(&u, &x[t], 4);
+        if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu) != 0) {
+            out[t] = (uint16_t)((u >> 16) | 0x0040u);
+            continue;
+        }
+        uint32_t lsb = (u >> 16) & 1u;
+        out[t] = (uint16_t)((u + 0x7FFFu + lsb) >> 16);
+    }
+}

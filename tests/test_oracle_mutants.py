@@ -1,0 +1,81 @@
+"""Planted mistakes in a copy of the oracle must each fail at least one pin.
+
+Each mutant is a one-line edit of oracle/fa_oracle.c of the kind a plausible
+bug would make (a dropped term, a wrong sign, index or unit, a transposed
+operand, a missing guard). The copy is built on the CPU in a temporary
+directory and run through tests/pins.py; the real oracle passes all pins
+(test_oracle.py), so a mutant that passes them all would mean a blind spot.
+"""
+import os
+import subprocess
+import tempfile
+
+import pytest
+
+import oracle
+from tests import pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "fa_oracle.c")
+
+MUTANTS = {
+    "mask_in_natural_units": ("s[j] += ORACLE_LOG2E * mr[j];", "s[j] += mr[j];"),
+    "mask_dropped": ("if (p->mask) {", "if (0) {"),
+    "exp_sign_flipped": ("s[j] = exp2f(s[j] - m);", "s[j] = exp2f(m - s[j]);"),
+    "causal_off_by_one": ("for (int64_t j = q_abs + 1; j < kl; ++j)",
+                          "for (int64_t j = q_abs; j < kl; ++j)"),
+    "causal_offset_dropped": ("const int64_t q_abs = (kl > ql ? kl - ql : 0) + i;",
+                              "const int64_t q_abs = i;"),
+    "causal_offset_unclamped": [("const int64_t q_abs = (kl > ql ? kl - ql : 0) + i;",
+                                 "const int64_t q_abs = (kl - ql) + i;"),
+                                ("for (int64_t j = q_abs + 1; j < kl; ++j)",
+                                 "for (int64_t j = (q_abs + 1 > 0 ? q_abs + 1 : 0); j < kl; ++j)")],
+    "gqa_modulo_map": ("const int64_t kvh = h / (p->H / p->Hkv);",
+                       "const int64_t kvh = h % p->Hkv;"),
+    "k_transposed": ("dot += qr[d] * kh[j * D + d];", "dot += qr[d] * kh[d * kl + j];"),
+    "scale_dropped": ("s[j] = dot * q_scale;", "s[j] = dot * ORACLE_LOG2E;"),
+    "log2e_dropped": ("const float q_scale = p->scale * ORACLE_LOG2E;",
+                      "const float q_scale = p->scale;"),
+    "lse_without_max": ("*l_out = m * ORACLE_LN2 + logf(sum);", "*l_out = logf(sum);"),
+    "lse_base2_max": ("*l_out = m * ORACLE_LN2 + logf(sum);", "*l_out = m + logf(sum);"),
+    "no_normalisation": ("const float w = s[j] / safe;", "const float w = s[j];"),
+    "infinite_sentinel": ("float m = -FLT_MAX / 2.0f;", "float m = -INFINITY;"),
+    "no_empty_row_guard": ("const float safe = (sum == 0.0f) ? 1.0f : sum;",
+                           "const float safe = sum;"),
+    "v_from_head_zero": ("const float *vh = p->v + (b * p->Hkv + kvh) * kl * D;",
+                         "const float *vh = p->v + (b * p->Hkv) * kl * D;"),
+    "k_batch_dropped": ("const float *kh = p->k + (b * p->Hkv + kvh) * kl * D;",
+                        "const float *kh = p->k + kvh * kl * D;"),
+    "v_row_off_by_one": ("const float *vr = vh + j * D;",
+                         "const float *vr = vh + (j + 1 < kl ? j + 1 : j) * D;"),
+    "max_skips_last_key": ("for (int64_t j = 0; j < kl; ++j)\n        if (s[j] > m)",
+                           "for (int64_t j = 0; j + 1 < kl; ++j)\n        if (s[j] > m)"),
+}
+
+
+def _build_mutant(tmp, name, edits):
+    src = open(SRC).read()
+    if isinstance(edits, tuple):
+        edits = [edits]
+    for old, new in edits:
+        assert src.count(old) == 1, f"mutation site for {name} not unique"
+        src = src.replace(old, new)
+    path_c = os.path.join(tmp, f"{name}.c")
+    path_so = os.path.join(tmp, f"lib{name}.so")
+    with open(path_c, "w") as f:
+        f.write(src)
+    subprocess.run(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
+                    "-pthread", "-o", path_so, path_c, "-lm"], check=True)
+    return path_so
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_planted_mistake(name):
+    with tempfile.TemporaryDirectory() as tmp:
+        fwd = oracle.bind(_build_mutant(tmp, name, MUTANTS[name]))
+        caught = []
+        for pin_name, pin in pins.ALL_PINS:
+            try:
+                pin(fwd)
+            except (AssertionError, ValueError, FloatingPointError):
+                caught.append(pin_name)
+        assert caught, f"no pin catches mutant {name}"
