@@ -1,0 +1,191 @@
+#!/usr/bin/env python3
+"""Throughput of the flash-attention training forward (O + L) on one MI355X.
+
+One step = one forward pass over each of the two training-scale workloads:
+  d64_b8_h16_q4096_k4096_causal          (head_dim 64, B8 H16, 4k tokens)
+  d256_gqa_b2_h16kv4_q8192_k8192_causal  (head_dim 256, GQA 16/4, 8k tokens)
+with seeded synthetic bf16 inputs already resident in HBM. Reported value:
+metric FLOP (4*B*H*ql*kl*D, halved for causal) of the step / step time, in
+TFLOP/s. Each kernel launch is bracketed by HIP events on the stream it runs
+on. The CPU oracle is timed on a strided sample of the same rows on the host.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME|both]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/clk
+PEAK_HBM_GBS = 8000.0
+HEADLINE = ["d64_b8_h16_q4096_k4096_causal", "d256_gqa_b2_h16kv4_q8192_k8192_causal"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCE = os.path.join(ROOT, "flash_attention_forward_fa_amd", "csrc", "fa_fwd.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash():
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def stored_traffic(workload):
+    """HBM bytes per launch measured by rocprofv3 --pmc (FETCH_SIZE, WRITE_SIZE),
+    if they were taken on the current kernel source; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    entry = t.get(workload)
+    if not entry or entry.get("kernel_source_sha") != kernel_source_hash():
+        return None
+    return entry.get("bytes_per_launch")
+
+
+def cpu_baseline(workloads, inputs, target_rows):
+    """The oracle, as it stands, on a strided sample of rows of each workload."""
+    import numpy as np
+    import oracle
+    threads = oracle.default_threads()
+    total_flop = 0.0
+    total_s = 0.0
+    parts = []
+    for w in workloads:
+        n_rows = w.B * w.H * w.ql
+        stride = max(1, n_rows // target_rows[w.name])
+        rows = np.arange(0, n_rows, stride, dtype=np.int64)
+        t0 = time.perf_counter()
+        oracle.fwd_workload(w, inputs[w.name], rows=rows, n_threads=threads)
+        dt = time.perf_counter() - t0
+        flop = w.metric_flop * rows.size / n_rows
+        total_flop += flop
+        total_s += dt
+        parts.append(f"{w.name}: every {stride}th row ({rows.size} rows, {dt:.1f} s)")
+        log(f"cpu_baseline {w.name}: {rows.size} rows in {dt:.2f} s "
+            f"({flop / dt / 1e9:.2f} GFLOP/s)")
+    return {"value": total_flop / total_s / 1e12, "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle", "sample": "; ".join(parts) +
+            "; metric FLOP of the sampled rows / oracle wall time"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="both")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=0,
+                    help="rows per workload for the CPU baseline (0: default sample)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the forward shards by batch or KV-head group with no communication).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import fagen
+    import flash_attention_forward_fa_amd as fa
+
+    names = HEADLINE if args.workload == "both" else [args.workload]
+    workloads = [fagen.WORKLOADS[n] for n in names]
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+
+    inputs, dev_inputs, outputs = {}, {}, {}
+    for w in workloads:
+        t0 = time.perf_counter()
+        inp = fagen.generate(w)
+        inputs[w.name] = inp
+        to = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        dev_inputs[w.name] = (to(inp["q"]), to(inp["k"]), to(inp["v"]))
+        q = dev_inputs[w.name][0]
+        outputs[w.name] = (torch.empty_like(q),
+                           torch.empty((w.B, w.H, w.ql), dtype=torch.float32, device=dev))
+        log(f"inputs {w.name}: generated and uploaded in {time.perf_counter() - t0:.1f} s")
+
+    def launch(w):
+        q, k, v = dev_inputs[w.name]
+        O, L = outputs[w.name]
+        fa.train_fwd(q, k, v, scale=w.scale, causal=w.causal, out=O, lse=L)
+
+    for i in range(args.warmup):
+        for w in workloads:
+            launch(w)
+    torch.cuda.synchronize()
+    log(f"warmup: {args.warmup} steps done")
+
+    ev = {w.name: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(args.steps)] for w in workloads}
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    for s in range(args.steps):
+        for w in workloads:
+            a, b = ev[w.name][s]
+            a.record(stream)
+            launch(w)
+            b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    log(f"timed: {args.steps} steps in {wall:.3f} s wall")
+
+    per = {}
+    total_ms = 0.0
+    total_flop = 0
+    for w in workloads:
+        ms = [a.elapsed_time(b) for a, b in ev[w.name]]
+        avg = float(np.mean(ms))
+        total_ms += avg
+        total_flop += w.metric_flop
+        alg_bytes = (2 * w.B * w.H * w.ql * w.D + 2 * 2 * w.B * w.Hkv * w.kl * w.D
+                     + 4 * w.B * w.H * w.ql)
+        per[w.name] = {"ms_avg": avg, "ms_min": float(np.min(ms)), "ms_median": float(np.median(ms)),
+                       "tflops": w.metric_flop / (avg * 1e-3) / 1e12,
+                       "frac_of_peak": w.metric_flop / (avg * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                       "metric_flop": w.metric_flop, "algorithmic_bytes": alg_bytes}
+        log(f"{w.name}: {avg * 1e3:.1f} us/launch, {per[w.name]['tflops']:.1f} TFLOP/s "
+            f"({100 * per[w.name]['frac_of_peak']:.1f}% of bf16 peak)")
+
+    dom = max(workloads, key=lambda w: per[w.name]["ms_avg"])
+    dp = per[dom.name]
+    traffic = stored_traffic(dom.name)
+    roofline = {"bound": "mfma", "achieved": dp["tflops"], "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": dp["tflops"] / PEAK_BF16_TFLOPS,
+                "traffic": traffic, "kernel": f"fa_fwd_kernel<D={dom.D},causal={dom.causal}>",
+                "workload": dom.name}
+
+    value = total_flop / (total_ms * 1e-3) / 1e12
+    result = {
+        "metric": "fwd TFLOP/s (O+L, bf16, causal, D=64/256) and % of MI355X bf16 MFMA peak",
+        "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": total_ms, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "frac_of_peak": value / PEAK_BF16_TFLOPS,
+        "config": {"workload": "+".join(names),
+                   "workloads": {w.name: {"B": w.B, "H": w.H, "Hkv": w.Hkv, "ql": w.ql,
+                                          "kl": w.kl, "D": w.D, "causal": w.causal,
+                                          "sigma": w.sigma} for w in workloads},
+                   "parallelism": "none (one GPU)"},
+        "per_workload": per,
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        target = {w.name: (args.cpu_rows or (65536 if w.D == 64 else 8192)) for w in workloads}
+        result["cpu_baseline"] = cpu_baseline(workloads, inputs, target)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,104 @@
+"""Flash-attention training forward (O and L) on AMD MI355X.
+
+A thin binding over libfa.so (include/fa.h): argument marshalling only. Every
+step of the computation runs in the library's gfx950 kernels; PyTorch only
+provides device memory and the current stream. There is no fallback: if the
+library is missing or the tensors are not on a GPU, the call raises.
+"""
+import ctypes
+import math
+import os
+
+from . import build as _build
+
+LIB_PATH = _build.LIB
+
+FA_STATUS = {
+    0: "FA_OK", 1: "FA_ERR_NULL_POINTER", 2: "FA_ERR_BAD_SIZE", 3: "FA_ERR_HEAD_GROUPING",
+    4: "FA_ERR_HEAD_DIM", 5: "FA_ERR_SCALE", 6: "FA_ERR_ALIGNMENT", 7: "FA_ERR_TOO_LARGE",
+    8: "FA_ERR_LAUNCH",
+}
+
+_lib = None
+
+
+class FAError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"{FA_STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+def lib():
+    """The loaded C library (ctypes). Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m flash_attention_forward_fa_amd.build`")
+        l = ctypes.CDLL(LIB_PATH)
+        vp, ci = ctypes.c_void_p, ctypes.c_int
+        l.fa_train_fwd.argtypes = [vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, ctypes.c_float, ci,
+                                   vp, vp, vp]
+        l.fa_train_fwd.restype = ci
+        l.fa_status_string.argtypes = [ci]
+        l.fa_status_string.restype = ctypes.c_char_p
+        _lib = l
+    return _lib
+
+
+def status_string(status):
+    return lib().fa_status_string(int(status)).decode()
+
+
+def fa_train_fwd(q, k, v, mask, batch, n_heads, n_kv_heads, ql, kl, head_dim, scale, causal,
+                 O, L, stream):
+    """The C entry point with raw integer pointers (0 for NULL); returns the status."""
+    return lib().fa_train_fwd(q or None, k or None, v or None, mask or None, batch, n_heads,
+                              n_kv_heads, ql, kl, head_dim, float(scale), int(bool(causal)),
+                              O or None, L or None, stream or None)
+
+
+def train_fwd(q, k, v, mask=None, scale=None, causal=False, out=None, lse=None, stream=None):
+    """O, L = train_fwd(q, k, v, mask=None, scale=None, causal=False)
+
+    q: bf16 [B, H, ql, D]; k, v: bf16 [B, Hkv, kl, D] (contiguous, same GPU);
+    mask: None or f32 [B, H, ql, kl] additive (natural-log units);
+    scale: defaults to 1/sqrt(D); causal: bottom-right aligned.
+    Returns O (bf16 [B, H, ql, D]) and L (f32 [B, H, ql]). Enqueued on the
+    current stream of q's device (or `stream`, a torch.cuda.Stream).
+    """
+    import torch
+
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.bfloat16:
+            raise TypeError(f"{name} must be a bfloat16 tensor")
+        if t.dim() != 4 or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError(f"{name} must be a contiguous 4-d tensor on a GPU")
+    B, H, ql, D = q.shape
+    Bk, Hkv, kl, Dk = k.shape
+    if tuple(v.shape) != tuple(k.shape) or Bk != B or Dk != D:
+        raise ValueError("k and v must be [B, Hkv, kl, D] with q's B and D")
+    if k.device != q.device or v.device != q.device:
+        raise ValueError("q, k and v must be on the same device")
+    if mask is not None:
+        if mask.dtype != torch.float32 or not mask.is_contiguous() or mask.device != q.device:
+            raise ValueError("mask must be a contiguous float32 tensor on q's device")
+        if tuple(mask.shape) != (B, H, ql, kl):
+            raise ValueError(f"mask must have shape {(B, H, ql, kl)}")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    O = out if out is not None else torch.empty_like(q)
+    L = lse if lse is not None else torch.empty((B, H, ql), dtype=torch.float32, device=q.device)
+    if O.shape != q.shape or O.dtype != torch.bfloat16 or not O.is_contiguous():
+        raise ValueError("out must be a contiguous bf16 tensor shaped like q")
+    if tuple(L.shape) != (B, H, ql) or L.dtype != torch.float32 or not L.is_contiguous():
+        raise ValueError("lse must be a contiguous f32 tensor [B, H, ql]")
+    s = stream if stream is not None else torch.cuda.current_stream(q.device)
+    with torch.cuda.device(q.device):
+        status = fa_train_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                              mask.data_ptr() if mask is not None else 0,
+                              B, H, Hkv, ql, kl, D, scale, causal, O.data_ptr(), L.data_ptr(),
+                              s.cuda_stream)
+    if status != 0:
+        raise FAError(status, status_string(status))
+    return O, L

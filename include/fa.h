@@ -1,0 +1,78 @@
+/*
+ * fa.h - C ABI of the flash-attention training forward for AMD MI355X (gfx950).
+ *
+ * The operation is the forward pass of softmax attention as used in training:
+ * it returns the attention output O and, for the backward pass, the per-row
+ * natural-log logsumexp L. Its definition is the CPU oracle of the method's
+ * page ("mlx-native 0.9.0", tests/test_flash_attn_train.rs, doc comment and
+ * section "CPU oracle - forward O + logsumexp L"), the launch parameters are
+ * those of that page's FlashAttnTrainParams (section "Test helpers",
+ * run_train_fwd), and the causal alignment is the one that oracle uses:
+ *
+ *   per batch b, query head h, query row i, with kv head g = h / (H / Hkv):
+ *     s_j = scale * <q[b,h,i,:], k[b,g,j,:]> + mask[b,h,i,j]    (natural log)
+ *     key j is hidden when causal and j > max(kl - ql, 0) + i
+ *     L[b,h,i]   = log(sum_j exp(s_j))        over visible keys (-inf if none)
+ *     O[b,h,i,:] = sum_j exp(s_j - L[b,h,i]) * v[b,g,j,:]        (0 if none)
+ *
+ * All tensors are contiguous row-major, in device memory owned by the caller.
+ * The library allocates nothing, keeps no global mutable state and never
+ * synchronises: work is enqueued on `stream` and the call returns.
+ */
+#ifndef FA_MI355X_FA_H
+#define FA_MI355X_FA_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes returned by every entry point. */
+enum fa_status {
+    FA_OK = 0,
+    FA_ERR_NULL_POINTER = 1,   /* q, k, v, O or L is NULL while its tensor is non-empty */
+    FA_ERR_BAD_SIZE = 2,       /* batch, ql or kl < 0; n_heads or n_kv_heads < 1      */
+    FA_ERR_HEAD_GROUPING = 3,  /* n_heads is not a multiple of n_kv_heads              */
+    FA_ERR_HEAD_DIM = 4,       /* head_dim is neither 64 nor 256                        */
+    FA_ERR_SCALE = 5,          /* scale is NaN or infinite                              */
+    FA_ERR_ALIGNMENT = 6,      /* q, k, v or O not 16-byte aligned; mask or L not 4-byte */
+    FA_ERR_TOO_LARGE = 7,      /* a grid or index would overflow the kernel's limits    */
+    FA_ERR_LAUNCH = 8          /* the HIP launch failed (hipGetLastError)               */
+};
+
+/*
+ * fa_train_fwd - enqueue one training forward pass.
+ *
+ *   q     bf16 bits [batch, n_heads,    ql, head_dim]  (device, read)
+ *   k     bf16 bits [batch, n_kv_heads, kl, head_dim]  (device, read)
+ *   v     bf16 bits [batch, n_kv_heads, kl, head_dim]  (device, read)
+ *   mask  f32 [batch, n_heads, ql, kl] additive mask in natural-log units, or
+ *         NULL for none (device, read). Entries may be -inf (hidden key); +inf
+ *         and NaN are outside the contract.
+ *   batch, n_heads, n_kv_heads, ql, kl, head_dim: sizes; n_heads must be a
+ *         multiple of n_kv_heads (query head h reads kv head h / (n_heads /
+ *         n_kv_heads)); head_dim is 64 or 256.
+ *   scale finite softmax scale (usually 1/sqrt(head_dim)); negative allowed.
+ *   causal nonzero: key j hidden from query row i when j > max(kl - ql, 0) + i.
+ *   O     bf16 bits [batch, n_heads, ql, head_dim] (device, written; no
+ *         pre-zeroing needed). A row with no visible key gets +0.
+ *   L     f32 [batch, n_heads, ql] natural-log logsumexp (device, written);
+ *         -inf for a row with no visible key.
+ *   stream hipStream_t to enqueue on (NULL: the default stream).
+ *
+ * Arguments are validated on the host before any HIP call; on error nothing is
+ * enqueued and a nonzero fa_status is returned. batch*ql == 0 is a successful
+ * no-op; kl == 0 gives every row O = 0 and L = -inf. Input and output buffers
+ * must not overlap. The call never aborts and never synchronises.
+ */
+int fa_train_fwd(const void *q, const void *k, const void *v, const float *mask, int batch,
+                 int n_heads, int n_kv_heads, int ql, int kl, int head_dim, float scale,
+                 int causal, void *O, float *L, void *stream);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char *fa_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_MI355X_FA_H */

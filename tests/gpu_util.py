@@ -1,0 +1,56 @@
+"""Helpers of the GPU tests: upload generated inputs, run the HIP forward
+through the binding, and compare with the oracle element by element."""
+import numpy as np
+
+import flash_attention_forward_fa_amd as fa
+
+
+def to_dev(bits_or_f32, dev):
+    import torch
+    a = np.ascontiguousarray(bits_or_f32)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+    return torch.from_numpy(a.astype(np.float32)).to(dev)
+
+
+def run(inputs, w, dev="cuda:0", scale=None):
+    """HIP forward on the generated inputs of workload-like `w`; returns
+    (O as float32 numpy, L numpy, raw O bits)."""
+    import torch
+    q, k, v = (to_dev(inputs[n], dev) for n in ("q", "k", "v"))
+    mask = None if inputs.get("mask") is None else to_dev(inputs["mask"], dev)
+    O, L = fa.train_fwd(q, k, v, mask=mask, scale=w.scale if scale is None else scale,
+                        causal=w.causal)
+    torch.cuda.synchronize()
+    bits = O.view(torch.int16).cpu().numpy().view(np.uint16)
+    return widen(bits), L.cpu().numpy(), bits
+
+
+def widen(bits):
+    return (np.asarray(bits, np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def tolerances(kl):
+    """Absolute bounds on O and L: 5e-3 / 3e-3 up to 256 keys, 1e-2 / 1e-2 beyond."""
+    return (5e-3, 3e-3) if kl <= 256 else (1e-2, 1e-2)
+
+
+def compare(o_gpu, l_gpu, o_bits, ob_ref, l_ref, tol_o, tol_l, label=""):
+    """Element-wise parity: fully masked rows exact (O = +0 bits, L = -inf),
+    every other element within the absolute bounds; no NaN anywhere.
+    Returns (max |dO|, max |dL|, relative RMS of dO)."""
+    o_ref = widen(ob_ref)
+    assert not np.isnan(o_gpu).any() and not np.isnan(l_gpu).any(), f"{label}: NaN in output"
+    dead = np.isneginf(l_ref)
+    assert np.array_equal(np.isneginf(l_gpu), dead), f"{label}: -inf rows of L differ"
+    assert np.all(o_bits[dead] == 0), f"{label}: fully masked rows must be +0 bits"
+    live = ~dead
+    if not live.any():
+        return 0.0, 0.0, 0.0
+    d_o = np.abs(o_gpu[live] - o_ref[live])
+    d_l = np.abs(l_gpu[live] - l_ref[live])
+    err_o, err_l = float(d_o.max()), float(d_l.max())
+    rms = float(np.sqrt((d_o ** 2).mean() / max((o_ref[live] ** 2).mean(), 1e-30)))
+    assert err_o <= tol_o, f"{label}: max|dO| = {err_o:.3e} > {tol_o:.1e}"
+    assert err_l <= tol_l, f"{label}: max|dL| = {err_l:.3e} > {tol_l:.1e}"
+    return err_o, err_l, rms

@@ -1,0 +1,88 @@
+"""The C-ABI library: it loads, exports every function include/*.h declares,
+and rejects invalid arguments on the host before any HIP call (no GPU needed:
+every call here fails validation or is an empty no-op, so nothing is ever
+launched)."""
+import glob
+import math
+import os
+import re
+import subprocess
+
+import pytest
+
+import flash_attention_forward_fa_amd as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    names = set()
+    for path in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(path).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        for m in re.finditer(r"\b([A-Za-z_]\w*)\s*\([^;{)]*\)\s*;", text):
+            names.add(m.group(1))
+    return names
+
+
+def test_header_declares_the_entry_points():
+    names = _declared_functions()
+    assert {"fa_train_fwd", "fa_status_string"} <= names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = fa.lib()
+    out = subprocess.run(["nm", "-D", "--defined-only", fa.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    for name in _declared_functions():
+        assert name in exported, name
+        assert hasattr(lib, name), name
+
+
+def test_status_strings_cover_all_codes():
+    for code in range(0, 9):
+        s = fa.status_string(code)
+        assert s and s != "unknown status"
+    assert fa.status_string(12345) == "unknown status"
+
+
+A = 0x10000  # a 16-byte aligned fake address; never dereferenced (validation fails first)
+
+GOOD = dict(q=A, k=A, v=A, mask=0, batch=1, n_heads=2, n_kv_heads=1, ql=8, kl=8, head_dim=64,
+            scale=0.125, causal=0, O=A, L=A, stream=0)
+
+
+def _call(**over):
+    args = dict(GOOD)
+    args.update(over)
+    return fa.fa_train_fwd(**args)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(q=0), 1), (dict(k=0), 1), (dict(v=0), 1), (dict(O=0), 1), (dict(L=0), 1),
+    (dict(batch=-1), 2), (dict(ql=-1), 2), (dict(kl=-3), 2), (dict(n_heads=0), 2),
+    (dict(n_kv_heads=0), 2), (dict(n_heads=3, n_kv_heads=2), 3), (dict(head_dim=128), 4),
+    (dict(head_dim=0), 4), (dict(scale=math.nan), 5), (dict(scale=math.inf), 5),
+    (dict(scale=-math.inf), 5), (dict(q=A + 2), 6), (dict(k=A + 8), 6), (dict(O=A + 4), 6),
+    (dict(mask=A + 2), 6), (dict(L=A + 1), 6),
+    (dict(batch=65536, n_heads=65536, n_kv_heads=1, ql=1), 7),
+])
+def test_invalid_arguments_are_rejected(over, code):
+    assert _call(**over) == code
+
+
+@pytest.mark.parametrize("over", [dict(batch=0), dict(ql=0), dict(batch=0, q=0, k=0, v=0, O=0,
+                                                                   L=0)])
+def test_empty_problems_are_noops(over):
+    assert _call(**over) == 0
+
+
+def test_python_binding_fails_loudly_without_gpu_tensors():
+    import torch
+    q = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        fa.train_fwd(q, q, q)
+    with pytest.raises(TypeError):
+        fa.train_fwd(q.float(), q, q)
