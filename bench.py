@@ -182,7 +182,7 @@ def main():
         "roofline": roofline,
     }
     if not args.no_cpu_baseline:
-        target = {w.name: (args.cpu_rows or (65536 if w.D == 64 else 8192)) for w in workloads}
+        target = {w.name: (args.cpu_rows or (524288 if w.D == 64 else 65536)) for w in workloads}
         result["cpu_baseline"] = cpu_baseline(workloads, inputs, target)
     print(json.dumps(result), flush=True)
 

@@ -42,6 +42,10 @@ constexpr int kPad = 8;                         // bf16 padding per LDS row
 // A wave whose rows may see fewer keys than this uses the compensated P.V
 // product (P split into a bf16 high part and a bf16 remainder).
 constexpr int kPreciseKeys = 128;
+// ... and so does a wave in which some output row reaches this magnitude
+// after the plain pass: from |O| = 0.5 on, one bf16 rounding step of O is
+// 2^-8 or more, and a pre-rounding error of bf16(P) size flips it.
+constexpr float kRecheckO = 0.5f;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -142,8 +146,17 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_kernel(FwdArgs a) {
   const bool wave_active = qw0 < ql;
   const int wave_last = min(qw0 + kRowsPerWave, ql) - 1;
   const int wave_kend = CAUSAL ? min(kl, off + wave_last + 1) : kl;
-  const bool precise =
+  // P.V precision: the plain product rounds P to bf16; the compensated one adds
+  // the bf16 remainder P - bf16(P) in a second MFMA. Waves whose rows may see
+  // few keys (by position only) and the masked variant start compensated. In
+  // any other wave, a row whose plain result reaches |O| >= kRecheckO is
+  // recomputed by a compensated second pass over the keys; every other row
+  // keeps its first-pass result, so a row's output never depends on the data
+  // of its neighbours.
+  bool precise =
       HAS_MASK || (CAUSAL ? (min(kl, off + qw0 + 1) < kPreciseKeys) : (kl < kPreciseKeys));
+  bool compute = wave_active;
+  bool redo_row = false;  // this lane's row is rewritten by the second pass
 
   float m_run = -FLT_MAX / 2.0f;  // running max, base-2 units
   float l_run = 0.0f;             // this lane's partial row sum
@@ -151,6 +164,7 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_kernel(FwdArgs a) {
 #pragma unroll
   for (int d = 0; d < NDB; ++d) oacc[d] = f32x16{};
 
+  for (int pass = 0; pass < 2; ++pass) {
   for (int kt = 0; kt < n_kt; ++kt) {
     const int kbase = kt * kBlockN;
     __syncthreads();
@@ -180,7 +194,7 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_kernel(FwdArgs a) {
       }
     }
     __syncthreads();
-    if (!wave_active || kbase >= wave_kend) continue;
+    if (!compute || kbase >= wave_kend) continue;
 
     // ---- S^T = K Q^T (raw scores, f32) ----
     f32x16 sacc[NKB];
@@ -277,25 +291,51 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_kernel(FwdArgs a) {
         }
       }
   }
-
-  // ---- epilogue: O = O_acc / l (0 for an empty row), L = (m + log2 l) ln 2 ----
-  const float l_tot = wave_half_swap_sum(l_run);
-  if (!row_ok) return;
-  const bool empty = !(l_tot > 0.0f);
-  const float inv = empty ? 0.0f : __builtin_amdgcn_rcpf(l_tot);
-  uint16_t* orow = a.o + ((int64_t)bh * ql + qrow) * D;
+    // ---- finish the pass: rows that are final write O and L ----
+    const float l_tot = wave_half_swap_sum(l_run);
+    bool need = false;
+    if (pass == 0 && compute && !precise) {
+      float omax = 0.0f;
 #pragma unroll
-  for (int d = 0; d < NDB; ++d)
+      for (int d = 0; d < NDB; ++d)
 #pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      bf16x4 ov;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) ov[e] = empty ? (__bf16)0.0f : (__bf16)(oacc[d][4 * g4 + e] * inv);
-      *reinterpret_cast<bf16x4*>(orow + 32 * d + 8 * g4 + 4 * hh) = ov;
+        for (int i = 0; i < 16; ++i) omax = __builtin_fmaxf(omax, __builtin_fabsf(oacc[d][i]));
+      omax = wave_half_swap_max(omax);  // max |O_acc| of this lane's row
+      need = row_ok && l_tot > 0.0f && omax >= kRecheckO * l_tot;
     }
-  if (hh == 0)
-    a.l[(int64_t)bh * ql + qrow] =
-        empty ? -INFINITY : (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
+    if (row_ok && (pass == 0 ? !need : redo_row)) {
+      // O = O_acc / l (+0 for an empty row), L = (m + log2 l) ln 2
+      const bool empty = !(l_tot > 0.0f);
+      const float inv = empty ? 0.0f : __builtin_amdgcn_rcpf(l_tot);
+      uint16_t* orow = a.o + ((int64_t)bh * ql + qrow) * D;
+#pragma unroll
+      for (int d = 0; d < NDB; ++d)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          bf16x4 ov;
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            ov[e] = empty ? (__bf16)0.0f : (__bf16)(oacc[d][4 * g4 + e] * inv);
+          *reinterpret_cast<bf16x4*>(orow + 32 * d + 8 * g4 + 4 * hh) = ov;
+        }
+      if (hh == 0)
+        a.l[(int64_t)bh * ql + qrow] =
+            empty ? -INFINITY : (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
+    }
+    if (pass == 1) break;
+    // ---- compensated second pass for the waves that have such rows ----
+    redo_row = need;
+    const bool wave_redo = __any(need);
+    if (!__syncthreads_or(wave_redo)) break;
+    compute = wave_redo;
+    if (wave_redo) {
+      precise = true;
+      m_run = -FLT_MAX / 2.0f;
+      l_run = 0.0f;
+#pragma unroll
+      for (int d = 0; d < NDB; ++d) oacc[d] = f32x16{};
+    }
+  }
 }
 
 template <int D, bool CAUSAL, bool HAS_MASK>

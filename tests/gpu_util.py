@@ -35,10 +35,19 @@ def tolerances(kl):
     return (5e-3, 3e-3) if kl <= 256 else (1e-2, 1e-2)
 
 
-def compare(o_gpu, l_gpu, o_bits, ob_ref, l_ref, tol_o, tol_l, label=""):
+def bf16_step(x):
+    """Size of one bf16 rounding step (2^-7 relative) at |x| (float32 array)."""
+    ax = np.maximum(np.abs(np.asarray(x, np.float32)), np.float32(2.0 ** -126))
+    return np.exp2(np.floor(np.log2(ax)) - 7)
+
+
+def compare(o_gpu, l_gpu, o_bits, ob_ref, l_ref, tol_o, tol_l, label="", one_step_ok=False):
     """Element-wise parity: fully masked rows exact (O = +0 bits, L = -inf),
-    every other element within the absolute bounds; no NaN anywhere.
-    Returns (max |dO|, max |dL|, relative RMS of dO)."""
+    every other element within the absolute bounds; no NaN anywhere. With
+    one_step_ok, an O element may also differ by one bf16 rounding step of the
+    reference value (for inputs whose scores are far larger than those of the
+    five workloads, where f32 evaluation order alone moves O across rounding
+    boundaries). Returns (max |dO|, max |dL|, relative RMS of dO)."""
     o_ref = widen(ob_ref)
     assert not np.isnan(o_gpu).any() and not np.isnan(l_gpu).any(), f"{label}: NaN in output"
     dead = np.isneginf(l_ref)
@@ -51,6 +60,10 @@ def compare(o_gpu, l_gpu, o_bits, ob_ref, l_ref, tol_o, tol_l, label=""):
     d_l = np.abs(l_gpu[live] - l_ref[live])
     err_o, err_l = float(d_o.max()), float(d_l.max())
     rms = float(np.sqrt((d_o ** 2).mean() / max((o_ref[live] ** 2).mean(), 1e-30)))
-    assert err_o <= tol_o, f"{label}: max|dO| = {err_o:.3e} > {tol_o:.1e}"
+    if one_step_ok:
+        excess = d_o - np.maximum(tol_o, bf16_step(o_ref[live]) * 1.001)
+        assert excess.max() <= 0, f"{label}: |dO| beyond one bf16 step: {err_o:.3e}"
+    else:
+        assert err_o <= tol_o, f"{label}: max|dO| = {err_o:.3e} > {tol_o:.1e}"
     assert err_l <= tol_l, f"{label}: max|dL| = {err_l:.3e} > {tol_l:.1e}"
     return err_o, err_l, rms

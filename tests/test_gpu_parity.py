@@ -123,7 +123,10 @@ def test_other_scales(D, scale):
     o, l, bits = gu.run(inp, w, scale=scale)
     _, ob, lr = oracle.fwd(inp["q"], inp["k"], inp["v"], None, w.B, w.H, w.Hkv, w.ql, w.kl, w.D,
                            scale, True)
-    gu.compare(o, l, bits, ob, lr, 5e-3, 3e-3, f"scale {scale}")
+    # at scale 0.5 the scores are up to 4x (D=64) or 8x (D=256) those of the
+    # workloads' 1/sqrt(D): rows are nearly one-hot and |O| reaches |V|, so an
+    # O element may differ from the oracle by one bf16 rounding step.
+    gu.compare(o, l, bits, ob, lr, 5e-3, 3e-3, f"scale {scale}", one_step_ok=abs(scale) > 0.3)
 
 
 def test_kl_zero_and_empty_problems():
