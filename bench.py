@@ -149,7 +149,8 @@ def main():
         avg = float(np.mean(ms))
         total_ms += avg
         total_flop += w.metric_flop
-        alg_bytes = (2 * w.B * w.H * w.ql * w.D + 2 * 2 * w.B * w.Hkv * w.kl * w.D
+        # Q and O (bf16), K and V (bf16, each read once), L (f32)
+        alg_bytes = (2 * 2 * w.B * w.H * w.ql * w.D + 2 * 2 * w.B * w.Hkv * w.kl * w.D
                      + 4 * w.B * w.H * w.ql)
         per[w.name] = {"ms_avg": avg, "ms_min": float(np.min(ms)), "ms_median": float(np.median(ms)),
                        "tflops": w.metric_flop / (avg * 1e-3) / 1e12,

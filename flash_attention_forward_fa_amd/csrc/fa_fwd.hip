@@ -4,19 +4,21 @@
 // ("mlx-native 0.9.0", tests/test_flash_attn_train.rs, doc comment and section
 // "CPU oracle - forward O + logsumexp L"): per query row, base-2 scores
 // s = scale*log2(e)*<q,k> (+ log2(e)*mask), bottom-right causal masking with the
-// offset max(kl - ql, 0), a row max seeded with the finite sentinel -FLT_MAX/2,
-// p = exp2(s - m), L = m*ln2 + ln(sum p), O = sum(p v) / sum p, and O = 0,
-// L = -inf for a row with no visible key. The kernel reaches the same values
-// tile by tile with an online (streaming) softmax over key tiles.
+// offset max(kl - ql, 0), p = exp2(s - m), L = m*ln2 + ln(sum p),
+// O = sum(p v) / sum p, and O = 0, L = -inf for a row with no visible key. The
+// kernel reaches the same values tile by tile with an online (streaming)
+// softmax over key tiles.
 //
 // Work decomposition: one workgroup of 4 waves per (batch, head, 128 query
-// rows); each wave owns 32 query rows. Per key tile of 64 keys, K is staged in
-// LDS as [key][d] and V as its transpose [d][key]; every wave then computes
-//   S^T = K Q^T    (v_mfma_f32_32x32x16_bf16: 32 keys x 32 queries per block)
-//   O^T += V^T P^T (same instruction: 32 head-dims x 32 queries per block)
-// so that in both products lane l holds query row (l mod 32): the row max,
-// the row sum and the O rescale are per-lane scalars, and the only cross-lane
-// step is one v_permlane32_swap between the two half-waves.
+// rows); each wave owns 32 query rows (two blocks of 16). Per key tile, K and
+// V are copied from HBM straight into LDS (global_load_lds_dwordx4, no VGPR
+// staging) into one of two buffers while the previous tile is being computed.
+// Every wave then computes, with v_mfma_f32_16x16x32_bf16,
+//   S^T = K Q^T     (K rows read from LDS with ds_read_b128)
+//   O^T += V^T P^T  (V^T read from the row-major V tile with ds_read_b64_tr_b16)
+// so that in both products a lane holds one query row per 16-row block: row
+// max, row sum and rescale are per-lane scalars after a reduction over the
+// four 16-lane groups (v_permlane32_swap, v_permlane16_swap).
 #include <hip/hip_runtime.h>
 
 #include <float.h>
@@ -29,23 +31,39 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kRowsPerWave = 32;
+constexpr int kQB = 2;                          // 16-row query blocks per wave
+constexpr int kRowsPerWave = 16 * kQB;
 constexpr int kBlockM = kWaves * kRowsPerWave;  // query rows per workgroup
-constexpr int kBlockN = 64;                     // keys per tile
-constexpr int kPad = 8;                         // bf16 padding per LDS row
-// A wave whose rows may see fewer keys than this uses the compensated P.V
-// product (P split into a bf16 high part and a bf16 remainder).
+
+// Keys per tile: 64 for D=64, 32 for D=256 (8 and 16 KiB each of K and V).
+template <int D> struct TileN;
+template <> struct TileN<64> { static constexpr int value = 64; };
+template <> struct TileN<256> { static constexpr int value = 32; };
+
+// A wave whose rows may see fewer keys than this starts with the compensated
+// P.V product (P split into a bf16 high part and a bf16 remainder).
 constexpr int kPreciseKeys = 128;
-// ... and so does a wave in which some output row reaches this magnitude
-// after the plain pass: from |O| = 0.5 on, one bf16 rounding step of O is
-// 2^-8 or more, and a pre-rounding error of bf16(P) size flips it.
+// After a plain pass, a row is recomputed compensated when |O| reaches this
+// (one bf16 rounding step of O is then 2^-8 or more, and an error of the size
+// of bf16(P)'s rounding can flip it) ...
 constexpr float kRecheckO = 0.5f;
+// ... or when its softmax is concentrated on so few keys (sum of the weights
+// relative to the largest one below this) that the bf16 rounding of the
+// row-sum terms does not average out.
+constexpr float kRecheckL = 16.0f;
+// The max used in exp2 is only raised when a tile's max exceeds it by more
+// than this (base-2 units): P <= 2^kLazy and O is rarely rescaled.
+constexpr float kLazy = 8.0f;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -65,42 +83,87 @@ struct FwdArgs {
   uint32_t q_sign; // 0x80008000 flips the sign of both bf16 halves (scale < 0)
 };
 
-__device__ __forceinline__ float wave_half_swap_max(float x) {
-  // lanes l and l^32 exchange values; each keeps the larger
+__device__ __forceinline__ float swap32(float x, bool take_max) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __builtin_fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  const float a = __uint_as_float(r[0]), b = __uint_as_float(r[1]);
+  return take_max ? __builtin_fmaxf(a, b) : a + b;
+}
+__device__ __forceinline__ float swap16(float x, bool take_max) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float a = __uint_as_float(r[0]), b = __uint_as_float(r[1]);
+  return take_max ? __builtin_fmaxf(a, b) : a + b;
+}
+// max / sum over the four 16-lane groups (lanes l, l^16, l^32, l^48)
+__device__ __forceinline__ float group_max(float x) { return swap16(swap32(x, true), true); }
+__device__ __forceinline__ float group_sum(float x) { return swap16(swap32(x, false), false); }
+
+// Row of a 32-key chunk that lane row m of key block kb (16 keys) loads as the
+// S^T A operand. With it, the four accumulators a lane of group g receives for
+// blocks 2j and 2j+1 are keys 32j + 8g + (0..7): exactly the B-operand order
+// of the P.V product, so P never moves between lanes.
+__device__ __forceinline__ int key_of(int kb, int m) {
+  return 32 * (kb >> 1) + 8 * (m >> 2) + 4 * (kb & 1) + (m & 3);
 }
 
-__device__ __forceinline__ float wave_half_swap_sum(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+// LDS layouts (bf16, row-major [key][d], 16-byte chunks permuted per row):
+// K: chunk c of row r sits at slot c ^ kswz(r), so the eight rows that eight
+//    consecutive lanes of one ds_read_b128 reach (keys key_of(kb, 0..7)) fall
+//    on distinct banks.
+// V: chunk c of row r sits at slot c ^ vswz(r), so the four rows one 16-lane
+//    group of ds_read_b64_tr_b16 reads fall on distinct banks.
+__device__ __forceinline__ int kswz(int r) { return (r & 3) | ((r >> 1) & 4); }
+__device__ __forceinline__ int vswz(int r) { return 2 * (r & 3); }
+
+// Issue the copy of one K or V tile (rows kbase .. kbase+BN-1, clamped to the
+// last valid row) from HBM into an LDS buffer. Each thread moves 16-byte
+// chunks; a wave writes 1 KiB of consecutive LDS per instruction, so a row's
+// chunk permutation is realised by choosing which global chunk each lane
+// fetches.
+template <int D, int BN, bool IS_K>
+__device__ __forceinline__ void issue_tile(const uint16_t* src, int kbase, int kl, uint16_t* lds,
+                                           int tid) {
+  constexpr int CH = D / 8;  // chunks per row
+  constexpr int ROUNDS = BN * CH / kThreads;
+  const int wave_base = tid & ~63;
+#pragma unroll
+  for (int u = 0; u < ROUNDS; ++u) {
+    const int p = u * kThreads + tid;  // LDS slot (16-byte units)
+    const int r = p / CH;
+    const int c = (p % CH) ^ (IS_K ? kswz(r) : vswz(r));
+    const int key = min(kbase + r, kl - 1);
+    const uint16_t* src_chunk = src + (int64_t)key * D + c * 8;
+    __builtin_amdgcn_global_load_lds(src_chunk, (lds_void*)(lds + (u * kThreads + wave_base) * 8),
+                                     16, 0, 0);
+  }
 }
 
-// Row (key) of the K tile that lane row m of a 32-key block loads: bits 2 and
-// 3 swapped. With this order the 16 accumulators a lane receives from the
-// 32x32 product hold, per 8-register group, 8 consecutive keys
-// (key = 16*(i/8) + 8*(lane/32) + i%8), which is exactly the B-operand order
-// the P.V product needs.
-__device__ __forceinline__ int key_perm(int m) {
-  return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
+__device__ __forceinline__ void wait_vmem() {
+  // vmcnt(0); expcnt and lgkmcnt left at their maxima
+  __builtin_amdgcn_s_waitcnt(0x0F70);
 }
 
 template <int D, bool CAUSAL, bool HAS_MASK>
-__global__ __launch_bounds__(kThreads) void fa_fwd_kernel(FwdArgs a) {
-  constexpr int DCH = D / 8;           // 16-byte chunks per K/V row
-  constexpr int KS = D + kPad;         // LDS row stride of K (elements)
-  constexpr int VS = kBlockN + kPad;   // LDS row stride of V^T (elements)
-  constexpr int NKB = kBlockN / 32;    // 32-key blocks per tile
-  constexpr int NDB = D / 32;          // 32-dim blocks of O
-  constexpr int NQS = D / 16;          // 16-dim steps of Q.K
-  __shared__ __attribute__((aligned(16))) uint16_t ks[kBlockN * KS];
-  __shared__ __attribute__((aligned(16))) uint16_t vt[D * VS];
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 : 1))) void fa_fwd_kernel(FwdArgs a) {
+  constexpr int BN = TileN<D>::value;
+  constexpr int NKB = BN / 16;  // 16-key blocks per tile
+  constexpr int NKC = BN / 32;  // 32-key chunks per tile (P.V contraction steps)
+  constexpr int NDB = D / 16;   // 16-dim blocks of O
+  constexpr int NDS = D / 32;   // 32-dim steps of Q.K
+  constexpr int TILE = BN * D;  // elements per K or V tile
+  __shared__ __attribute__((aligned(1024))) uint16_t k0s[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t v0s[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t k1s[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t v1s[TILE];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  // The wave index is made provably wave-uniform so that every condition
+  // derived from it (tile skipping, compensated product, second pass) compiles
+  // to a scalar branch: an MFMA left inside an EXEC-masked region still
+  // accumulates (with whatever its operand registers hold) when EXEC is zero.
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
-  const int n = lane & 31;   // query row within the wave
-  const int hh = lane >> 5;  // half-wave
+  const int c16 = lane & 15;  // query column within a 16-row block / A-operand row
+  const int grp = lane >> 4;  // 16-lane group
 
   // ---- work item: heaviest causal tiles first; heads grouped per XCD ----
   const int BH = a.B * a.H;
@@ -120,222 +183,271 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_kernel(FwdArgs a) {
   const int ql = a.ql, kl = a.kl, off = a.causal_off;
   const int q0 = qtile * kBlockM;
   const int qw0 = q0 + wave * kRowsPerWave;
-  const int qrow = qw0 + n;
-  const bool row_ok = qrow < ql;
-  const int qrow_c = row_ok ? qrow : ql - 1;
-
-  const uint16_t* qp = a.q + ((int64_t)bh * ql + qrow_c) * D;
   const int64_t kv_off = (int64_t)(b * a.Hkv + g) * kl * D;
   const uint16_t* kp = a.k + kv_off;
   const uint16_t* vp = a.v + kv_off;
 
-  // ---- Q^T as the B operand: lane holds row qrow, dims 16s + 8hh .. +7 ----
-  bf16x8 qop[NQS];
-#pragma unroll
-  for (int s = 0; s < NQS; ++s) {
-    u32x4 raw = *reinterpret_cast<const u32x4*>(qp + 16 * s + 8 * hh);
-    raw ^= a.q_sign;
-    qop[s] = __builtin_bit_cast(bf16x8, raw);
+  // ---- key range; the first tile's copy starts before Q is read ----
+  const int last_row = min(q0 + kBlockM, ql) - 1;
+  const int kend = CAUSAL ? min(kl, off + last_row + 1) : kl;
+  const int n_kt = (kend + BN - 1) / BN;
+  if (n_kt > 0) {
+    issue_tile<D, BN, true>(kp, 0, kl, k0s, tid);
+    issue_tile<D, BN, false>(vp, 0, kl, v0s, tid);
   }
 
-  // ---- key range ----
-  const int last_row = (q0 + kBlockM < ql ? q0 + kBlockM : ql) - 1;
-  int kend = kl;
-  if (CAUSAL) kend = min(kl, off + last_row + 1);
-  const int n_kt = (kend + kBlockN - 1) / kBlockN;
+  // ---- Q^T as the B operand: block qb, step s: row qw0+16qb+c16, dims 32s+8grp.. ----
+  bf16x8 qop[kQB][NDS];
+#pragma unroll
+  for (int qb = 0; qb < kQB; ++qb) {
+    const int qrow = min(qw0 + 16 * qb + c16, ql - 1);
+    const uint16_t* qp = a.q + ((int64_t)bh * ql + qrow) * D + 8 * grp;
+#pragma unroll
+    for (int s = 0; s < NDS; ++s) {
+      u32x4 raw = *reinterpret_cast<const u32x4*>(qp + 32 * s);
+      raw ^= a.q_sign;
+      qop[qb][s] = __builtin_bit_cast(bf16x8, raw);
+    }
+  }
+
   const bool wave_active = qw0 < ql;
   const int wave_last = min(qw0 + kRowsPerWave, ql) - 1;
   const int wave_kend = CAUSAL ? min(kl, off + wave_last + 1) : kl;
-  // P.V precision: the plain product rounds P to bf16; the compensated one adds
-  // the bf16 remainder P - bf16(P) in a second MFMA. Waves whose rows may see
-  // few keys (by position only) and the masked variant start compensated. In
-  // any other wave, a row whose plain result reaches |O| >= kRecheckO is
-  // recomputed by a compensated second pass over the keys; every other row
-  // keeps its first-pass result, so a row's output never depends on the data
-  // of its neighbours.
   bool precise =
       HAS_MASK || (CAUSAL ? (min(kl, off + qw0 + 1) < kPreciseKeys) : (kl < kPreciseKeys));
   bool compute = wave_active;
-  bool redo_row = false;  // this lane's row is rewritten by the second pass
+  bool redo[kQB];
 
-  float m_run = -FLT_MAX / 2.0f;  // running max, base-2 units
-  float l_run = 0.0f;             // this lane's partial row sum
-  f32x16 oacc[NDB];
+  float m_use[kQB], m_top[kQB], l_run[kQB];
+  f32x4 oacc[NDB][kQB];
 #pragma unroll
-  for (int d = 0; d < NDB; ++d) oacc[d] = f32x16{};
+  for (int qb = 0; qb < kQB; ++qb) {
+    m_use[qb] = -FLT_MAX / 2.0f;  // max used in exp2 (base 2)
+    m_top[qb] = -FLT_MAX / 2.0f;  // true running max (base 2)
+    l_run[qb] = 0.0f;             // this lane's partial row sum
+    redo[qb] = false;
+#pragma unroll
+    for (int d = 0; d < NDB; ++d) oacc[d][qb] = f32x4{};
+  }
 
-  for (int pass = 0; pass < 2; ++pass) {
-  for (int kt = 0; kt < n_kt; ++kt) {
-    const int kbase = kt * kBlockN;
+  // One key tile: wait for its copy, start the next one, compute.
+  auto step = [&](int kt, const uint16_t* ks, const uint16_t* vs, uint16_t* nks, uint16_t* nvs) {
+    const int kbase = kt * BN;
+    wait_vmem();
     __syncthreads();
-    // ---- stage K tile [key][d] ----
-#pragma unroll
-    for (int c = tid; c < kBlockN * DCH; c += kThreads) {
-      const int row = c / DCH, ch = c % DCH;
-      const int key = kbase + row;
-      u32x4 val = u32x4{};
-      if (key < kl) val = *reinterpret_cast<const u32x4*>(kp + (int64_t)key * D + ch * 8);
-      *reinterpret_cast<u32x4*>(ks + row * KS + ch * 8) = val;
+    if (kt + 1 < n_kt) {
+      issue_tile<D, BN, true>(kp, kbase + BN, kl, nks, tid);
+      issue_tile<D, BN, false>(vp, kbase + BN, kl, nvs, tid);
     }
-    // ---- stage V tile transposed [d][key], two keys per 32-bit LDS word ----
-#pragma unroll
-    for (int u = tid; u < (kBlockN / 2) * DCH; u += kThreads) {
-      const int pr = u / DCH, ch = u % DCH;
-      const int key0 = kbase + 2 * pr;
-      u32x4 v0 = u32x4{}, v1 = u32x4{};
-      if (key0 < kl) v0 = *reinterpret_cast<const u32x4*>(vp + (int64_t)key0 * D + ch * 8);
-      if (key0 + 1 < kl) v1 = *reinterpret_cast<const u32x4*>(vp + (int64_t)(key0 + 1) * D + ch * 8);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const uint32_t w0 = v0[j >> 1], w1 = v1[j >> 1];
-        const uint32_t word = (j & 1) ? ((w0 >> 16) | (w1 & 0xFFFF0000u))
-                                      : ((w0 & 0xFFFFu) | (w1 << 16));
-        *reinterpret_cast<uint32_t*>(vt + (ch * 8 + j) * VS + 2 * pr) = word;
-      }
-    }
-    __syncthreads();
-    if (!compute || kbase >= wave_kend) continue;
+    if (!compute || kbase >= wave_kend) return;
 
     // ---- S^T = K Q^T (raw scores, f32) ----
-    f32x16 sacc[NKB];
+    f32x4 sacc[NKB][kQB];
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      sacc[kb] = f32x16{};
-      const uint16_t* krow = ks + (32 * kb + key_perm(n)) * KS + 8 * hh;
+    for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int s = 0; s < NQS; ++s) {
-        const bf16x8 kop = *reinterpret_cast<const bf16x8*>(krow + 16 * s);
-        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[s], sacc[kb], 0, 0, 0);
+      for (int qb = 0; qb < kQB; ++qb) sacc[kb][qb] = f32x4{};
+#pragma unroll
+    for (int s = 0; s < NDS; ++s)
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        const int r = key_of(kb, c16);
+        const int chunk = 4 * s + grp;
+        const bf16x8 kop = *reinterpret_cast<const bf16x8*>(ks + r * D + 8 * (chunk ^ kswz(r)));
+#pragma unroll
+        for (int qb = 0; qb < kQB; ++qb)
+          sacc[kb][qb] =
+              __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop[qb][s], sacc[kb][qb], 0, 0, 0);
       }
-    }
 
     // ---- masks: tail keys, causal, additive ----
-    const int qabs = off + qrow;
     if (HAS_MASK) {
-      const float* mrow = a.mask + ((int64_t)bh * ql + qrow_c) * kl;
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = kbase + 32 * kb + 16 * (i >> 3) + 8 * hh + (i & 7);
-          const bool vis = key < kl && (!CAUSAL || key <= qabs);
-          sacc[kb][i] = vis ? __builtin_fmaf(sacc[kb][i], a.c, kLog2e * mrow[key]) : -INFINITY;
-        }
-    } else {
-      const bool edge = (kbase + kBlockN > kl) || (CAUSAL && kbase + kBlockN - 1 > off + qw0);
-      if (edge) {
+      for (int qb = 0; qb < kQB; ++qb) {
+        const int qrow = qw0 + 16 * qb + c16;
+        const float* mrow = a.mask + ((int64_t)bh * ql + min(qrow, ql - 1)) * kl;
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = kbase + 32 * kb + 16 * (i >> 3) + 8 * hh + (i & 7);
-            const bool vis = key < kl && (!CAUSAL || key <= qabs);
-            if (!vis) sacc[kb][i] = -INFINITY;
+          for (int i = 0; i < 4; ++i) {
+            const int key = kbase + 32 * (kb >> 1) + 8 * grp + 4 * (kb & 1) + i;
+            const bool vis = key < kl && (!CAUSAL || key <= off + qrow);
+            sacc[kb][qb][i] =
+                vis ? __builtin_fmaf(sacc[kb][qb][i], a.c, kLog2e * mrow[key]) : -INFINITY;
+          }
+      }
+    } else if ((kbase + BN > kl) || (CAUSAL && kbase + BN - 1 > off + qw0)) {
+#pragma unroll
+      for (int qb = 0; qb < kQB; ++qb) {
+        const int qabs = off + qw0 + 16 * qb + c16;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int key = kbase + 32 * (kb >> 1) + 8 * grp + 4 * (kb & 1) + i;
+            if (key >= kl || (CAUSAL && key > qabs)) sacc[kb][qb][i] = -INFINITY;
           }
       }
     }
 
-    // ---- online softmax (base 2) ----
-    float mx = -INFINITY;
+    // ---- online softmax (base 2), lazy rescale ----
+    // (the decision to raise is taken per row, so a row's result never
+    // depends on its neighbours' scores)
+    float m_new[kQB];
+    bool raise = false;
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
+    for (int qb = 0; qb < kQB; ++qb) {
+      float mx = -INFINITY;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mx = __builtin_fmaxf(mx, sacc[kb][i]);
-    mx = wave_half_swap_max(mx);
-    // scale is applied in f32 here (c > 0, so max(c*r) == c*max(r))
-    const float m_new = __builtin_fmaxf(m_run, HAS_MASK ? mx : mx * a.c);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    float psum = 0.0f;
+      for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
+        for (int i = 0; i < 4; ++i) mx = __builtin_fmaxf(mx, sacc[kb][qb][i]);
+      mx = group_max(mx);
+      const float tmax = HAS_MASK ? mx : mx * a.c;  // c > 0: max(c*r) == c*max(r)
+      m_top[qb] = __builtin_fmaxf(m_top[qb], tmax);
+      const bool r = tmax > m_use[qb] + kLazy;
+      m_new[qb] = r ? tmax : m_use[qb];
+      raise |= r;
+    }
+    if (__any(raise)) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float x = HAS_MASK ? sacc[kb][i] - m_new : __builtin_fmaf(sacc[kb][i], a.c, -m_new);
-        const float p = __builtin_amdgcn_exp2f(x);
-        sacc[kb][i] = p;
-        psum += p;
+      for (int qb = 0; qb < kQB; ++qb) {
+        const float alpha = __builtin_amdgcn_exp2f(m_use[qb] - m_new[qb]);
+        m_use[qb] = m_new[qb];
+        l_run[qb] *= alpha;
+#pragma unroll
+        for (int d = 0; d < NDB; ++d) oacc[d][qb] *= alpha;
       }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
+    }
+
+    // ---- P = exp2(s - m) in bf16 (+ remainder when compensated), row sums ----
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+    bf16x8 phi[NKC][kQB], plo[NKC][kQB];
 #pragma unroll
-    for (int d = 0; d < NDB; ++d)
+    for (int qb = 0; qb < kQB; ++qb) {
+      const float mneg = -m_use[qb];
+      float ls = l_run[qb];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) oacc[d][i] *= alpha;
+      for (int j = 0; j < NKC; ++j) {
+        float p[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float sv = sacc[2 * j + (e >> 2)][qb][e & 3];
+          p[e] = __builtin_amdgcn_exp2f(HAS_MASK ? sv + mneg : __builtin_fmaf(sv, a.c, mneg));
+          phi[j][qb][e] = (__bf16)p[e];
+        }
+#pragma unroll
+        for (int e = 0; e < 8; e += 2)
+          ls = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{phi[j][qb][e], phi[j][qb][e + 1]}, ones, ls,
+                                               false);
+        if (precise) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) plo[j][qb][e] = (__bf16)(p[e] - (float)phi[j][qb][e]);
+#pragma unroll
+          for (int e = 0; e < 8; e += 2)
+            ls = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{plo[j][qb][e], plo[j][qb][e + 1]}, ones,
+                                                 ls, false);
+        }
+      }
+      l_run[qb] = ls;
+    }
 
     // ---- O^T += V^T P^T ----
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
+    for (int d = 0; d < NDB; ++d)
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        bf16x8 phi;
+      for (int j = 0; j < NKC; ++j) {
+        // V^T operand: dims 16d + c16, keys 32j + 8grp + (0..7), from two
+        // transposing reads of four keys each
+        s16x4 half[2];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) phi[e] = (__bf16)sacc[kb][8 * half + e];
-        const uint16_t* vcol = vt + n * VS + 32 * kb + 16 * half + 8 * hh;
-        if (precise) {
-          bf16x8 plo;
+        for (int t = 0; t < 2; ++t) {
+          const int r = 32 * j + 8 * grp + 4 * t + (c16 >> 2);
+          const int col = 16 * d + 4 * (c16 & 3);
+          const uint16_t* addr = vs + r * D + 8 * ((col >> 3) ^ vswz(r)) + (col & 7);
+          half[t] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)addr);
+        }
+        const bf16x8 vop = __builtin_bit_cast(
+            bf16x8, __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
-          for (int e = 0; e < 8; ++e)
-            plo[e] = (__bf16)(sacc[kb][8 * half + e] - (float)phi[e]);
-#pragma unroll
-          for (int d = 0; d < NDB; ++d) {
-            const bf16x8 vop = *reinterpret_cast<const bf16x8*>(vcol + 32 * d * VS);
-            oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, phi, oacc[d], 0, 0, 0);
-            oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, plo, oacc[d], 0, 0, 0);
-          }
-        } else {
-#pragma unroll
-          for (int d = 0; d < NDB; ++d) {
-            const bf16x8 vop = *reinterpret_cast<const bf16x8*>(vcol + 32 * d * VS);
-            oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, phi, oacc[d], 0, 0, 0);
-          }
+        for (int qb = 0; qb < kQB; ++qb) {
+          oacc[d][qb] =
+              __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, phi[j][qb], oacc[d][qb], 0, 0, 0);
+          if (precise)
+            oacc[d][qb] =
+                __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, plo[j][qb], oacc[d][qb], 0, 0, 0);
         }
       }
-  }
-    // ---- finish the pass: rows that are final write O and L ----
-    const float l_tot = wave_half_swap_sum(l_run);
-    bool need = false;
-    if (pass == 0 && compute && !precise) {
-      float omax = 0.0f;
-#pragma unroll
-      for (int d = 0; d < NDB; ++d)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) omax = __builtin_fmaxf(omax, __builtin_fabsf(oacc[d][i]));
-      omax = wave_half_swap_max(omax);  // max |O_acc| of this lane's row
-      need = row_ok && l_tot > 0.0f && omax >= kRecheckO * l_tot;
+  };
+
+  for (int pass = 0; pass < 2; ++pass) {
+    if (pass == 1 && n_kt > 0) {
+      // every wave finished the first pass (barrier in __syncthreads_or):
+      // buffer 0 is free for tile 0 again
+      issue_tile<D, BN, true>(kp, 0, kl, k0s, tid);
+      issue_tile<D, BN, false>(vp, 0, kl, v0s, tid);
     }
-    if (row_ok && (pass == 0 ? !need : redo_row)) {
-      // O = O_acc / l (+0 for an empty row), L = (m + log2 l) ln 2
-      const bool empty = !(l_tot > 0.0f);
-      const float inv = empty ? 0.0f : __builtin_amdgcn_rcpf(l_tot);
-      uint16_t* orow = a.o + ((int64_t)bh * ql + qrow) * D;
+    for (int kt = 0; kt < n_kt; kt += 2) {
+      step(kt, k0s, v0s, k1s, v1s);
+      if (kt + 1 < n_kt) step(kt + 1, k1s, v1s, k0s, v0s);
+    }
+
+    // ---- finish the pass: rows that are final write O and L ----
+    bool need_any = false;
 #pragma unroll
-      for (int d = 0; d < NDB; ++d)
+    for (int qb = 0; qb < kQB; ++qb) {
+      const int qrow = qw0 + 16 * qb + c16;
+      const bool row_ok = compute && qrow < ql;
+      const float l_tot = group_sum(l_run[qb]);
+      bool need = false;
+      if (pass == 0 && !precise) {
+        float omax = 0.0f;
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
+        for (int d = 0; d < NDB; ++d)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) omax = __builtin_fmaxf(omax, __builtin_fabsf(oacc[d][qb][i]));
+        omax = group_max(omax);
+        const float l_rel = l_tot * __builtin_amdgcn_exp2f(m_use[qb] - m_top[qb]);
+        need = row_ok && l_tot > 0.0f && (omax >= kRecheckO * l_tot || l_rel < kRecheckL);
+      }
+      if (row_ok && (pass == 0 ? !need : redo[qb])) {
+        // O = O_acc / l (+0 for an empty row), L = (m + log2 l) ln 2
+        const bool empty = !(l_tot > 0.0f);
+        const float inv = empty ? 0.0f : __builtin_amdgcn_rcpf(l_tot);
+        uint16_t* orow = a.o + ((int64_t)bh * ql + qrow) * D + 4 * grp;
+#pragma unroll
+        for (int d = 0; d < NDB; ++d) {
           bf16x4 ov;
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            ov[e] = empty ? (__bf16)0.0f : (__bf16)(oacc[d][4 * g4 + e] * inv);
-          *reinterpret_cast<bf16x4*>(orow + 32 * d + 8 * g4 + 4 * hh) = ov;
+          for (int i = 0; i < 4; ++i)
+            ov[i] = empty ? (__bf16)0.0f : (__bf16)(oacc[d][qb][i] * inv);
+          *reinterpret_cast<bf16x4*>(orow + 16 * d) = ov;
         }
-      if (hh == 0)
-        a.l[(int64_t)bh * ql + qrow] =
-            empty ? -INFINITY : (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
+        if (grp == 0)
+          a.l[(int64_t)bh * ql + qrow] =
+              empty ? -INFINITY : (m_use[qb] + __builtin_amdgcn_logf(l_tot)) * kLn2;
+      }
+      redo[qb] = need;
+      need_any |= need;
     }
     if (pass == 1) break;
     // ---- compensated second pass for the waves that have such rows ----
-    redo_row = need;
-    const bool wave_redo = __any(need);
+    const bool wave_redo = __any(need_any);
     if (!__syncthreads_or(wave_redo)) break;
     compute = wave_redo;
     if (wave_redo) {
       precise = true;
-      m_run = -FLT_MAX / 2.0f;
-      l_run = 0.0f;
 #pragma unroll
-      for (int d = 0; d < NDB; ++d) oacc[d] = f32x16{};
+      for (int qb = 0; qb < kQB; ++qb) {
+        m_use[qb] = -FLT_MAX / 2.0f;
+        m_top[qb] = -FLT_MAX / 2.0f;
+        l_run[qb] = 0.0f;
+#pragma unroll
+        for (int d = 0; d < NDB; ++d) oacc[d][qb] = f32x4{};
+      }
     }
   }
+  wait_vmem();  // no LDS copy may still be in flight when the workgroup ends
 }
 
 template <int D, bool CAUSAL, bool HAS_MASK>

@@ -1,0 +1,60 @@
+"""Checks on the gfx950 machine code of the forward kernels (no GPU needed:
+hipcc cross-compiles the kernels to assembly here).
+
+- No v_mfma instruction may sit inside an EXEC-masked region (between an
+  s_*_saveexec and the s_or_b64 exec that restores EXEC). Such an MFMA still
+  accumulates when EXEC is zero, so a wave-uniform condition that the compiler
+  could not prove uniform silently corrupts O.
+- The hot variants (no mask) must not spill registers to scratch.
+"""
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def isa(tmp_path_factory):
+    from flash_attention_forward_fa_amd import build
+    out = tmp_path_factory.mktemp("isa") / "fa_fwd.s"
+    flags = [f for f in build.FLAGS if f not in ("-fPIC", "-shared")]
+    subprocess.run([build.HIPCC, *flags, "--cuda-device-only", "-S", "-o", str(out),
+                    *build.SOURCES], check=True, capture_output=True)
+    text = out.read_text()
+    kernels = {}
+    name = None
+    for line in text.split("\n"):
+        m = re.match(r"^(_Z\w*fa_fwd_kernel\w+):", line)
+        if m:
+            name = m.group(1)
+            kernels[name] = []
+        elif name is not None:
+            kernels[name].append(line)
+    return kernels
+
+
+def test_all_variants_present(isa):
+    assert len(isa) == 8
+
+
+def test_no_mfma_under_exec_mask(isa):
+    for name, lines in isa.items():
+        depth = 0
+        for line in lines:
+            if re.search(r"s_(and|andn2|or)_saveexec_b64", line):
+                depth += 1
+            elif re.search(r"s_or_b64 exec, exec", line):
+                depth = max(0, depth - 1)
+            elif "v_mfma" in line:
+                assert depth == 0, f"{name}: MFMA inside an EXEC-masked region: {line.strip()}"
+
+
+def test_hot_variants_do_not_spill(isa):
+    for name, lines in isa.items():
+        if "Lb0EEEv" not in name:  # HAS_MASK=false variants
+            continue
+        body = "\n".join(lines)
+        assert "scratch_store" not in body and "buffer_store_dword" not in body, name
