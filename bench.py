@@ -86,6 +86,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=0,
                     help="rows per workload for the CPU baseline (0: default sample)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="also run 3 device-to-device copies of MIB MiB (a plain copy kernel of "
+                         "known traffic, to calibrate rocprofv3 FETCH_SIZE/WRITE_SIZE)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -140,6 +143,15 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall
     log(f"timed: {args.steps} steps in {wall:.3f} s wall")
+
+    if args.copy_calibration:
+        n = args.copy_calibration * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy calibration: 3 copies of {args.copy_calibration} MiB done")
 
     per = {}
     total_ms = 0.0
