@@ -106,13 +106,19 @@ __device__ __forceinline__ int key_of(int kb, int m) {
 }
 
 // LDS layouts (bf16, row-major [key][d], 16-byte chunks permuted per row):
-// K: chunk c of row r sits at slot c ^ kswz(r), so the eight rows that eight
-//    consecutive lanes of one ds_read_b128 reach (keys key_of(kb, 0..7)) fall
-//    on distinct banks.
-// V: chunk c of row r sits at slot c ^ vswz(r), so the four rows one 16-lane
-//    group of ds_read_b64_tr_b16 reads fall on distinct banks.
-__device__ __forceinline__ int kswz(int r) { return (r & 3) | ((r >> 1) & 4); }
-__device__ __forceinline__ int vswz(int r) { return 2 * (r & 3); }
+// chunk c of K row r sits at slot c ^ kswz<D>(r), chunk c of V row r at slot
+// c ^ vswz<D>(r). The permutations were chosen by measuring LDS bank-conflict
+// cycles (SQ_LDS_BANK_CONFLICT) for the exact access patterns of this kernel:
+// the K rows one ds_read_b128 reaches (keys key_of(kb, 0..15)) and the V rows
+// the 16-lane groups of one ds_read_b64_tr_b16 reach (four rows per group)
+// all come out conflict-free with these, for 128-byte (D=64) and 512-byte
+// (D=256) rows.
+template <int D> __device__ __forceinline__ int kswz(int r) {
+  return D == 64 ? ((r & 3) | ((r >> 1) & 4)) : ((r & 3) | ((r >> 1) & 12));
+}
+template <int D> __device__ __forceinline__ int vswz(int r) {
+  return D == 64 ? 2 * (((r >> 1) & 1) | ((r >> 2) & 2)) : 2 * ((r & 3) | ((r >> 1) & 4));
+}
 
 // Issue the copy of one K or V tile (rows kbase .. kbase+BN-1, clamped to the
 // last valid row) from HBM into an LDS buffer. Each thread moves 16-byte
@@ -129,7 +135,7 @@ __device__ __forceinline__ void issue_tile(const uint16_t* src, int kbase, int k
   for (int u = 0; u < ROUNDS; ++u) {
     const int p = u * kThreads + tid;  // LDS slot (16-byte units)
     const int r = p / CH;
-    const int c = (p % CH) ^ (IS_K ? kswz(r) : vswz(r));
+    const int c = (p % CH) ^ (IS_K ? kswz<D>(r) : vswz<D>(r));
     const int key = min(kbase + r, kl - 1);
     const uint16_t* src_chunk = src + (int64_t)key * D + c * 8;
     __builtin_amdgcn_global_load_lds(src_chunk, (lds_void*)(lds + (u * kThreads + wave_base) * 8),
@@ -165,7 +171,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 6
   const int c16 = lane & 15;  // query column within a 16-row block / A-operand row
   const int grp = lane >> 4;  // 16-lane group
 
-  // ---- work item: heaviest causal tiles first; heads grouped per XCD ----
+  // ---- work item ----
+  // Workgroups are handed to the 8 XCDs round-robin (bid mod 8). When B*H is a
+  // multiple of 8, XCD x owns the heads [x*per, (x+1)*per) (so one KV group
+  // stays within one XCD's L2) and walks its query tiles heaviest (most keys)
+  // first across all its heads, so the cheap tiles fill the tail. (Running one
+  // head at a time per XCD was measured slower.)
   const int BH = a.B * a.H;
   const int bid = blockIdx.x;
   int qt_rev, bh;
@@ -253,7 +264,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 6
       for (int kb = 0; kb < NKB; ++kb) {
         const int r = key_of(kb, c16);
         const int chunk = 4 * s + grp;
-        const bf16x8 kop = *reinterpret_cast<const bf16x8*>(ks + r * D + 8 * (chunk ^ kswz(r)));
+        const bf16x8 kop = *reinterpret_cast<const bf16x8*>(ks + r * D + 8 * (chunk ^ kswz<D>(r)));
 #pragma unroll
         for (int qb = 0; qb < kQB; ++qb)
           sacc[kb][qb] =
@@ -364,7 +375,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 6
         for (int t = 0; t < 2; ++t) {
           const int r = 32 * j + 8 * grp + 4 * t + (c16 >> 2);
           const int col = 16 * d + 4 * (c16 & 3);
-          const uint16_t* addr = vs + r * D + 8 * ((col >> 3) ^ vswz(r)) + (col & 7);
+          const uint16_t* addr = vs + r * D + 8 * ((col >> 3) ^ vswz<D>(r)) + (col & 7);
           half[t] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)addr);
         }
         const bf16x8 vop = __builtin_bit_cast(
