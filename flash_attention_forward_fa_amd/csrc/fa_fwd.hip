@@ -25,6 +25,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "fa.h"
 
 namespace {
@@ -41,14 +43,16 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kQB = 2;                          // 16-row query blocks per wave
-constexpr int kRowsPerWave = 16 * kQB;
-constexpr int kBlockM = kWaves * kRowsPerWave;  // query rows per workgroup
 
-// Keys per tile: 64 for D=64, 32 for D=256 (8 and 16 KiB each of K and V).
-template <int D> struct TileN;
-template <> struct TileN<64> { static constexpr int value = 64; };
-template <> struct TileN<256> { static constexpr int value = 32; };
+// Per head dim: QB 16-row query blocks per wave and BN keys per tile.
+//   D=64:  2 blocks (32 rows per wave, 128 per workgroup), 64-key tiles.
+//   D=256: 1 block (16 rows per wave, 64 per workgroup), 32-key tiles; the
+//          O accumulator of 16 rows x 256 dims is 64 registers per lane, so
+//          two workgroups share a compute unit.
+template <int D> struct Cfg;
+template <> struct Cfg<64> { static constexpr int QB = 2, BN = 64; };
+template <> struct Cfg<256> { static constexpr int QB = 1, BN = 32; };
+template <int D> constexpr int block_m() { return kWaves * 16 * Cfg<D>::QB; }
 
 // A wave whose rows may see fewer keys than this starts with the compensated
 // P.V product (P split into a bf16 high part and a bf16 remainder).
@@ -77,7 +81,7 @@ struct FwdArgs {
   float* l;
   int B, H, Hkv, ql, kl;
   int group;       // H / Hkv
-  int n_qtiles;    // ceil(ql / kBlockM)
+  int n_qtiles;    // ceil(ql / rows per workgroup)
   int causal_off;  // max(kl - ql, 0)
   float c;         // |scale| * log2(e), at least FLT_MIN
   uint32_t q_sign; // 0x80008000 flips the sign of both bf16 halves (scale < 0)
@@ -149,8 +153,11 @@ __device__ __forceinline__ void wait_vmem() {
 }
 
 template <int D, bool CAUSAL, bool HAS_MASK>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 : 1))) void fa_fwd_kernel(FwdArgs a) {
-  constexpr int BN = TileN<D>::value;
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void fa_fwd_kernel(FwdArgs a) {
+  constexpr int BN = Cfg<D>::BN;
+  constexpr int kQB = Cfg<D>::QB;
+  constexpr int kRowsPerWave = 16 * kQB;
+  constexpr int kBlockM = block_m<D>();
   constexpr int NKB = BN / 16;  // 16-key blocks per tile
   constexpr int NKC = BN / 32;  // 32-key chunks per tile (P.V contraction steps)
   constexpr int NDB = D / 16;   // 16-dim blocks of O
@@ -242,7 +249,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 6
   }
 
   // One key tile: wait for its copy, start the next one, compute.
-  auto step = [&](int kt, const uint16_t* ks, const uint16_t* vs, uint16_t* nks, uint16_t* nvs) {
+  auto step = [&](auto precise_tag, int kt, const uint16_t* ks, const uint16_t* vs, uint16_t* nks,
+                  uint16_t* nvs) {
+    constexpr bool PRECISE = decltype(precise_tag)::value;
     const int kbase = kt * BN;
     wait_vmem();
     __syncthreads();
@@ -269,6 +278,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 6
         for (int qb = 0; qb < kQB; ++qb)
           sacc[kb][qb] =
               __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop[qb][s], sacc[kb][qb], 0, 0, 0);
+        // D=256: keep the scheduler from hoisting all K reads (register pressure)
+        if (D == 256 && kb == NKB - 1 && (s & 1) == 1) __builtin_amdgcn_sched_barrier(0);
       }
 
     // ---- masks: tail keys, causal, additive ----
@@ -351,7 +362,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 6
         for (int e = 0; e < 8; e += 2)
           ls = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{phi[j][qb][e], phi[j][qb][e + 1]}, ones, ls,
                                                false);
-        if (precise) {
+        if (PRECISE) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) plo[j][qb][e] = (__bf16)(p[e] - (float)phi[j][qb][e]);
 #pragma unroll
@@ -384,10 +395,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 6
         for (int qb = 0; qb < kQB; ++qb) {
           oacc[d][qb] =
               __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, phi[j][qb], oacc[d][qb], 0, 0, 0);
-          if (precise)
+          if (PRECISE)
             oacc[d][qb] =
                 __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, plo[j][qb], oacc[d][qb], 0, 0, 0);
         }
+        // D=256: the same for the V reads
+        if (D == 256 && j == NKC - 1 && (d & 3) == 3) __builtin_amdgcn_sched_barrier(0);
       }
   };
 
@@ -398,9 +411,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 6
       issue_tile<D, BN, true>(kp, 0, kl, k0s, tid);
       issue_tile<D, BN, false>(vp, 0, kl, v0s, tid);
     }
-    for (int kt = 0; kt < n_kt; kt += 2) {
-      step(kt, k0s, v0s, k1s, v1s);
-      if (kt + 1 < n_kt) step(kt + 1, k1s, v1s, k0s, v0s);
+    // The plain / compensated choice is hoisted out of the key loop (it is
+    // uniform per wave; the barrier count per loop is the same either way).
+    if (precise) {
+      for (int kt = 0; kt < n_kt; ++kt) {
+        const bool odd = kt & 1;
+        step(std::true_type{}, kt, odd ? k1s : k0s, odd ? v1s : v0s, odd ? k0s : k1s,
+             odd ? v0s : v1s);
+      }
+    } else {
+      for (int kt = 0; kt < n_kt; ++kt) {
+        const bool odd = kt & 1;
+        step(std::false_type{}, kt, odd ? k1s : k0s, odd ? v1s : v0s, odd ? k0s : k1s,
+             odd ? v0s : v1s);
+      }
     }
 
     // ---- finish the pass: rows that are final write O and L ----
@@ -494,7 +518,8 @@ extern "C" int fa_train_fwd(const void* q, const void* k, const void* v, const f
   if (!aligned(q, 16) || !aligned(O, 16) || !aligned(L, 4) ||
       (kv_used && (!aligned(k, 16) || !aligned(v, 16))) || (mask && !aligned(mask, 4)))
     return FA_ERR_ALIGNMENT;
-  const int64_t n_qtiles = ((int64_t)ql + kBlockM - 1) / kBlockM;
+  const int bm = head_dim == 64 ? block_m<64>() : block_m<256>();
+  const int64_t n_qtiles = ((int64_t)ql + bm - 1) / bm;
   const int64_t grid = n_qtiles * batch * n_heads;
   if (grid > 0x7fffffffLL || (int64_t)batch * n_heads > 0x7fffffffLL) return FA_ERR_TOO_LARGE;
 
