@@ -69,6 +69,13 @@ constexpr float kRecheckL = 16.0f;
 // than this (base-2 units): P <= 2^kLazy and O is rarely rescaled.
 constexpr float kLazy = 8.0f;
 
+// Kernel modes. The plain kernel runs the bf16-P product and marks the rows
+// that need the compensated product by writing kRowFlag into their L (their O
+// is not written); the compensated kernel then recomputes exactly those rows
+// (kFlagged), or every row when an additive mask is given (kAll).
+constexpr int kPlain = 0, kAll = 1, kFlagged = 2;
+constexpr uint32_t kRowFlag = 0x7FC0FA00u;  // a quiet NaN; never a valid L
+
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -152,8 +159,10 @@ __device__ __forceinline__ void wait_vmem() {
   __builtin_amdgcn_s_waitcnt(0x0F70);
 }
 
-template <int D, bool CAUSAL, bool HAS_MASK>
+template <int D, bool CAUSAL, bool HAS_MASK, int MODE>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void fa_fwd_kernel(FwdArgs a) {
+  static_assert(MODE != kPlain || !HAS_MASK, "the masked forward always runs compensated");
+  constexpr bool PRECISE = MODE != kPlain;
   constexpr int BN = Cfg<D>::BN;
   constexpr int kQB = Cfg<D>::QB;
   constexpr int kRowsPerWave = 16 * kQB;
@@ -205,10 +214,48 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   const uint16_t* kp = a.k + kv_off;
   const uint16_t* vp = a.v + kv_off;
 
-  // ---- key range; the first tile's copy starts before Q is read ----
+  // ---- key range ----
   const int last_row = min(q0 + kBlockM, ql) - 1;
   const int kend = CAUSAL ? min(kl, off + last_row + 1) : kl;
   const int n_kt = (kend + BN - 1) / BN;
+  const bool wave_active = qw0 < ql;
+  const int wave_last = min(qw0 + kRowsPerWave, ql) - 1;
+  const int wave_kend = CAUSAL ? min(kl, off + wave_last + 1) : kl;
+  float* lrow_base = a.l + (int64_t)bh * ql;
+
+  // ---- which rows this workgroup computes ----
+  // Rows that may see fewer than kPreciseKeys keys (a property of their
+  // position) always take the compensated product.
+  auto short_rows = [&](int first_row) {
+    return CAUSAL ? (min(kl, off + first_row + 1) < kPreciseKeys) : (kl < kPreciseKeys);
+  };
+  bool compute = wave_active;
+  bool mine[kQB];  // kFlagged: this lane's row of block qb is to be recomputed
+#pragma unroll
+  for (int qb = 0; qb < kQB; ++qb) mine[qb] = false;
+  if (MODE == kPlain) {
+    if (short_rows(qw0)) {
+      // hand these rows to the compensated kernel
+#pragma unroll
+      for (int qb = 0; qb < kQB; ++qb) {
+        const int qrow = qw0 + 16 * qb + c16;
+        if (grp == 0 && qrow < ql) lrow_base[qrow] = __uint_as_float(kRowFlag);
+      }
+      compute = false;
+    }
+    // the last wave's rows start latest: if they are short, all are
+    if (short_rows(q0 + (kWaves - 1) * kRowsPerWave)) return;
+  } else if (MODE == kFlagged) {
+    bool any = false;
+#pragma unroll
+    for (int qb = 0; qb < kQB; ++qb) {
+      const int qrow = qw0 + 16 * qb + c16;
+      if (qrow < ql) mine[qb] = __float_as_uint(lrow_base[qrow]) == kRowFlag;
+      any |= mine[qb];
+    }
+    compute = __any(any);
+    if (!__syncthreads_or(compute)) return;
+  }
   if (n_kt > 0) {
     issue_tile<D, BN, true>(kp, 0, kl, k0s, tid);
     issue_tile<D, BN, false>(vp, 0, kl, v0s, tid);
@@ -228,14 +275,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     }
   }
 
-  const bool wave_active = qw0 < ql;
-  const int wave_last = min(qw0 + kRowsPerWave, ql) - 1;
-  const int wave_kend = CAUSAL ? min(kl, off + wave_last + 1) : kl;
-  bool precise =
-      HAS_MASK || (CAUSAL ? (min(kl, off + qw0 + 1) < kPreciseKeys) : (kl < kPreciseKeys));
-  bool compute = wave_active;
-  bool redo[kQB];
-
   float m_use[kQB], m_top[kQB], l_run[kQB];
   f32x4 oacc[NDB][kQB];
 #pragma unroll
@@ -243,15 +282,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     m_use[qb] = -FLT_MAX / 2.0f;  // max used in exp2 (base 2)
     m_top[qb] = -FLT_MAX / 2.0f;  // true running max (base 2)
     l_run[qb] = 0.0f;             // this lane's partial row sum
-    redo[qb] = false;
 #pragma unroll
     for (int d = 0; d < NDB; ++d) oacc[d][qb] = f32x4{};
   }
 
   // One key tile: wait for its copy, start the next one, compute.
-  auto step = [&](auto precise_tag, int kt, const uint16_t* ks, const uint16_t* vs, uint16_t* nks,
-                  uint16_t* nvs) {
-    constexpr bool PRECISE = decltype(precise_tag)::value;
+  auto step = [&](int kt, const uint16_t* ks, const uint16_t* vs, uint16_t* nks, uint16_t* nvs) {
     const int kbase = kt * BN;
     wait_vmem();
     __syncthreads();
@@ -404,100 +440,73 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       }
   };
 
-  for (int pass = 0; pass < 2; ++pass) {
-    if (pass == 1 && n_kt > 0) {
-      // every wave finished the first pass (barrier in __syncthreads_or):
-      // buffer 0 is free for tile 0 again
-      issue_tile<D, BN, true>(kp, 0, kl, k0s, tid);
-      issue_tile<D, BN, false>(vp, 0, kl, v0s, tid);
-    }
-    // The plain / compensated choice is hoisted out of the key loop (it is
-    // uniform per wave; the barrier count per loop is the same either way).
-    if (precise) {
-      for (int kt = 0; kt < n_kt; ++kt) {
-        const bool odd = kt & 1;
-        step(std::true_type{}, kt, odd ? k1s : k0s, odd ? v1s : v0s, odd ? k0s : k1s,
-             odd ? v0s : v1s);
-      }
-    } else {
-      for (int kt = 0; kt < n_kt; ++kt) {
-        const bool odd = kt & 1;
-        step(std::false_type{}, kt, odd ? k1s : k0s, odd ? v1s : v0s, odd ? k0s : k1s,
-             odd ? v0s : v1s);
-      }
-    }
+  for (int kt = 0; kt < n_kt; ++kt) {
+    const bool odd = kt & 1;
+    step(kt, odd ? k1s : k0s, odd ? v1s : v0s, odd ? k0s : k1s, odd ? v0s : v1s);
+  }
 
-    // ---- finish the pass: rows that are final write O and L ----
-    bool need_any = false;
+  // ---- epilogue: O = O_acc / l (+0 for an empty row), L = (m + log2 l) ln 2 ----
 #pragma unroll
-    for (int qb = 0; qb < kQB; ++qb) {
-      const int qrow = qw0 + 16 * qb + c16;
-      const bool row_ok = compute && qrow < ql;
-      const float l_tot = group_sum(l_run[qb]);
-      bool need = false;
-      if (pass == 0 && !precise) {
-        float omax = 0.0f;
+  for (int qb = 0; qb < kQB; ++qb) {
+    const int qrow = qw0 + 16 * qb + c16;
+    const bool row_ok = compute && qrow < ql;
+    const float l_tot = group_sum(l_run[qb]);
+    bool write = row_ok;
+    if (MODE == kPlain) {
+      // rows whose plain result is not accurate enough go to the compensated kernel
+      float omax = 0.0f;
 #pragma unroll
-        for (int d = 0; d < NDB; ++d)
+      for (int d = 0; d < NDB; ++d)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) omax = __builtin_fmaxf(omax, __builtin_fabsf(oacc[d][qb][i]));
-        omax = group_max(omax);
-        const float l_rel = l_tot * __builtin_amdgcn_exp2f(m_use[qb] - m_top[qb]);
-        need = row_ok && l_tot > 0.0f && (omax >= kRecheckO * l_tot || l_rel < kRecheckL);
-      }
-      if (row_ok && (pass == 0 ? !need : redo[qb])) {
-        // O = O_acc / l (+0 for an empty row), L = (m + log2 l) ln 2
-        const bool empty = !(l_tot > 0.0f);
-        const float inv = empty ? 0.0f : __builtin_amdgcn_rcpf(l_tot);
-        uint16_t* orow = a.o + ((int64_t)bh * ql + qrow) * D + 4 * grp;
-#pragma unroll
-        for (int d = 0; d < NDB; ++d) {
-          bf16x4 ov;
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            ov[i] = empty ? (__bf16)0.0f : (__bf16)(oacc[d][qb][i] * inv);
-          *reinterpret_cast<bf16x4*>(orow + 16 * d) = ov;
-        }
-        if (grp == 0)
-          a.l[(int64_t)bh * ql + qrow] =
-              empty ? -INFINITY : (m_use[qb] + __builtin_amdgcn_logf(l_tot)) * kLn2;
-      }
-      redo[qb] = need;
-      need_any |= need;
+        for (int i = 0; i < 4; ++i) omax = __builtin_fmaxf(omax, __builtin_fabsf(oacc[d][qb][i]));
+      omax = group_max(omax);
+      const float l_rel = l_tot * __builtin_amdgcn_exp2f(m_use[qb] - m_top[qb]);
+      const bool need = row_ok && l_tot > 0.0f && (omax >= kRecheckO * l_tot || l_rel < kRecheckL);
+      if (need && grp == 0) lrow_base[qrow] = __uint_as_float(kRowFlag);
+      write = row_ok && !need;
+    } else if (MODE == kFlagged) {
+      write = row_ok && mine[qb];
     }
-    if (pass == 1) break;
-    // ---- compensated second pass for the waves that have such rows ----
-    const bool wave_redo = __any(need_any);
-    if (!__syncthreads_or(wave_redo)) break;
-    compute = wave_redo;
-    if (wave_redo) {
-      precise = true;
+    if (write) {
+      const bool empty = !(l_tot > 0.0f);
+      const float inv = empty ? 0.0f : __builtin_amdgcn_rcpf(l_tot);
+      uint16_t* orow = a.o + ((int64_t)bh * ql + qrow) * D + 4 * grp;
 #pragma unroll
-      for (int qb = 0; qb < kQB; ++qb) {
-        m_use[qb] = -FLT_MAX / 2.0f;
-        m_top[qb] = -FLT_MAX / 2.0f;
-        l_run[qb] = 0.0f;
+      for (int d = 0; d < NDB; ++d) {
+        bf16x4 ov;
 #pragma unroll
-        for (int d = 0; d < NDB; ++d) oacc[d][qb] = f32x4{};
+        for (int i = 0; i < 4; ++i) ov[i] = empty ? (__bf16)0.0f : (__bf16)(oacc[d][qb][i] * inv);
+        *reinterpret_cast<bf16x4*>(orow + 16 * d) = ov;
       }
+      if (grp == 0)
+        lrow_base[qrow] = empty ? -INFINITY : (m_use[qb] + __builtin_amdgcn_logf(l_tot)) * kLn2;
     }
   }
   wait_vmem();  // no LDS copy may still be in flight when the workgroup ends
 }
 
-template <int D, bool CAUSAL, bool HAS_MASK>
+template <int D, bool CAUSAL, bool HAS_MASK, int MODE>
 hipError_t launch(const FwdArgs& a, unsigned grid, hipStream_t stream) {
-  hipLaunchKernelGGL((fa_fwd_kernel<D, CAUSAL, HAS_MASK>), dim3(grid), dim3(kThreads), 0, stream,
-                     a);
+  hipLaunchKernelGGL((fa_fwd_kernel<D, CAUSAL, HAS_MASK, MODE>), dim3(grid), dim3(kThreads), 0,
+                     stream, a);
   return hipGetLastError();
+}
+
+// Masked: one compensated launch. Unmasked: the plain launch, then the
+// compensated launch for the rows it flagged (same stream, so in order).
+template <int D, bool CAUSAL>
+hipError_t dispatch_c(const FwdArgs& a, bool has_mask, unsigned grid, hipStream_t stream) {
+  if (has_mask) return launch<D, CAUSAL, true, kAll>(a, grid, stream);
+  hipError_t e = launch<D, CAUSAL, false, kPlain>(a, grid, stream);
+  if (e != hipSuccess) return e;
+  return launch<D, CAUSAL, false, kFlagged>(a, grid, stream);
 }
 
 template <int D>
 hipError_t dispatch_d(const FwdArgs& a, bool causal, bool has_mask, unsigned grid,
                       hipStream_t stream) {
-  if (causal)
-    return has_mask ? launch<D, true, true>(a, grid, stream) : launch<D, true, false>(a, grid, stream);
-  return has_mask ? launch<D, false, true>(a, grid, stream) : launch<D, false, false>(a, grid, stream);
+  return causal ? dispatch_c<D, true>(a, has_mask, grid, stream)
+                : dispatch_c<D, false>(a, has_mask, grid, stream);
 }
 
 bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }

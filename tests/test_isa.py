@@ -38,7 +38,7 @@ def isa(tmp_path_factory):
 
 
 def test_all_variants_present(isa):
-    assert len(isa) == 8
+    assert len(isa) == 12  # head_dim x causal x {plain, compensated flagged, compensated masked}
 
 
 def test_no_mfma_under_exec_mask(isa):
