@@ -9,23 +9,32 @@
 // kernel reaches the same values tile by tile with an online (streaming)
 // softmax over key tiles.
 //
-// Work decomposition: one workgroup of 4 waves per (batch, head, 128 query
-// rows); each wave owns 32 query rows (two blocks of 16). Per key tile, K and
-// V are copied from HBM straight into LDS (global_load_lds_dwordx4, no VGPR
-// staging) into one of two buffers while the previous tile is being computed.
-// Every wave then computes, with v_mfma_f32_16x16x32_bf16,
+// Work decomposition: one workgroup of 4 waves per (batch, head, query tile);
+// each wave owns 32 query rows (D=64, two blocks of 16) or 16 rows (D=256).
+// Per key tile, K and V are copied from HBM straight into LDS
+// (buffer_load_dwordx4 ... lds, no VGPR staging) into one of two buffers while
+// the previous tile is being computed. Every wave then computes, with
+// v_mfma_f32_16x16x32_bf16,
 //   S^T = K Q^T     (K rows read from LDS with ds_read_b128)
 //   O^T += V^T P^T  (V^T read from the row-major V tile with ds_read_b64_tr_b16)
 // so that in both products a lane holds one query row per 16-row block: row
 // max, row sum and rescale are per-lane scalars after a reduction over the
 // four 16-lane groups (v_permlane32_swap, v_permlane16_swap).
+//
+// Accuracy: P enters the bf16 MFMA rounded to bf16. Where that is not accurate
+// enough the product is compensated (a second MFMA with P's bf16 remainder):
+// for query tiles whose rows may see fewer than 128 keys (one compensated
+// launch), and for rows the plain launch finds with |O| >= 1, which a rescue
+// launch recomputes.
 #include <hip/hip_runtime.h>
 
 #include <float.h>
 #include <math.h>
 #include <stdint.h>
 
-#include <type_traits>
+#include <map>
+#include <mutex>
+#include <utility>
 
 #include "fa.h"
 
@@ -54,27 +63,36 @@ template <> struct Cfg<64> { static constexpr int QB = 2, BN = 64; };
 template <> struct Cfg<256> { static constexpr int QB = 1, BN = 32; };
 template <int D> constexpr int block_m() { return kWaves * 16 * Cfg<D>::QB; }
 
-// A wave whose rows may see fewer keys than this starts with the compensated
-// P.V product (P split into a bf16 high part and a bf16 remainder).
+// Query tiles with a row that may see fewer keys than this (a property of
+// their position) are computed with the compensated P.V product (P split into
+// a bf16 high part and a bf16 remainder) from the start.
 constexpr int kPreciseKeys = 128;
-// After a plain pass, a row is recomputed compensated when |O| reaches this
-// (one bf16 rounding step of O is then 2^-8 or more, and an error of the size
-// of bf16(P)'s rounding can flip it) ...
-constexpr float kRecheckO = 0.5f;
-// ... or when its softmax is concentrated on so few keys (sum of the weights
-// relative to the largest one below this) that the bf16 rounding of the
-// row-sum terms does not average out.
-constexpr float kRecheckL = 16.0f;
+// After a plain pass, a row is recomputed compensated when some |O| element
+// reaches this: one bf16 rounding step of O is then 2^-7 or more, so the
+// error bf16(P) leaves in O before its own rounding (about 2^-10 at most on
+// the workloads) can move it by a step larger than 5e-3. Below it a moved
+// rounding costs at most 2^-8. (L needs no such check: bf16(P) changes the
+// row sum by a relative 2^-9 at most.)
+constexpr float kRecheckO = 1.0f;
 // The max used in exp2 is only raised when a tile's max exceeds it by more
 // than this (base-2 units): P <= 2^kLazy and O is rarely rescaled.
 constexpr float kLazy = 8.0f;
 
-// Kernel modes. The plain kernel runs the bf16-P product and marks the rows
-// that need the compensated product by writing kRowFlag into their L (their O
-// is not written); the compensated kernel then recomputes exactly those rows
-// (kFlagged), or every row when an additive mask is given (kAll).
-constexpr int kPlain = 0, kAll = 1, kFlagged = 2;
+// Kernel modes. The plain kernel (kPlain) runs the bf16-P product and marks
+// the rows that need the compensated product by writing kRowFlag into their L
+// (their O is not written) and queueing their query tile; the rescue kernel
+// then recomputes those rows compensated. The compensated kernel (kAll)
+// computes every row of its tiles: the tiles with short rows, or all tiles
+// when an additive mask is given.
+constexpr int kPlain = 0, kAll = 1;
 constexpr uint32_t kRowFlag = 0x7FC0FA00u;  // a quiet NaN; never a valid L
+
+// Work queue of query tiles for the rescue kernel (device memory, int words):
+// [0] number of queued tiles, [1] next tile to take, [2] rescue workgroups
+// finished, [3] unused, [4..] tile ids (bh * n_qtiles + query tile). The
+// rescue kernel's last workgroup zeroes words 0..2, so the queue is empty
+// between calls.
+constexpr int kQueueHeader = 4;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -89,10 +107,19 @@ struct FwdArgs {
   int B, H, Hkv, ql, kl;
   int group;       // H / Hkv
   int n_qtiles;    // ceil(ql / rows per workgroup)
+  int qt_base;     // this launch computes query tiles [qt_base, qt_base + qt_count)
+  int qt_count;
   int causal_off;  // max(kl - ql, 0)
   float c;         // |scale| * log2(e), at least FLT_MIN
   uint32_t q_sign; // 0x80008000 flips the sign of both bf16 halves (scale < 0)
+  int* queue;      // rescue work queue (kPlain, rescue kernel)
 };
+
+// Queue a query tile for the rescue kernel (one lane).
+__device__ __forceinline__ void queue_tile(int* queue, int id) {
+  const int slot = atomicAdd(queue, 1);
+  queue[kQueueHeader + slot] = id;
+}
 
 __device__ __forceinline__ float swap32(float x, bool take_max) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -131,26 +158,61 @@ template <int D> __device__ __forceinline__ int vswz(int r) {
   return D == 64 ? 2 * (((r >> 1) & 1) | ((r >> 2) & 2)) : 2 * ((r & 3) | ((r >> 1) & 4));
 }
 
-// Issue the copy of one K or V tile (rows kbase .. kbase+BN-1, clamped to the
-// last valid row) from HBM into an LDS buffer. Each thread moves 16-byte
-// chunks; a wave writes 1 KiB of consecutive LDS per instruction, so a row's
-// chunk permutation is realised by choosing which global chunk each lane
-// fetches.
+// Buffer resource word 3 for raw (untyped) buffer loads on gfx9-family parts.
+constexpr int kRsrcWord3 = 0x00020000;
+
+// Copy of one K or V tile (keys kbase .. kbase+BN-1) from HBM straight into an
+// LDS buffer with buffer_load_dwordx4 ... lds (no VGPR staging). Each thread
+// moves 16-byte chunks; a wave writes 1 KiB of consecutive LDS per
+// instruction, so a row's chunk permutation is realised by choosing which
+// global chunk each lane fetches. `off` holds this thread's byte offsets
+// within a full tile (computed once by copy_offsets); the buffer descriptor is
+// rebased on the tile so that the per-tile work is scalar. A tile that runs
+// past the last key repeats the last key's row (those keys are masked out).
+template <int D, int BN>
+struct CopyShape {
+  static constexpr int CH = D / 8;                   // 16-byte chunks per row
+  static constexpr int ROUNDS = BN * CH / kThreads;  // chunks per thread
+  static_assert(ROUNDS * kThreads == BN * CH, "tile not a multiple of the workgroup");
+};
+
+template <int D, bool IS_K>
+__device__ __forceinline__ int chunk_offset(int p, int row) {
+  constexpr int CH = D / 8;
+  const int r = p / CH;
+  return (row * D + 8 * ((p % CH) ^ (IS_K ? kswz<D>(r) : vswz<D>(r)))) * 2;
+}
+
+template <int D, int BN, bool IS_K>
+__device__ __forceinline__ void copy_offsets(int tid, int (&off)[CopyShape<D, BN>::ROUNDS]) {
+#pragma unroll
+  for (int u = 0; u < CopyShape<D, BN>::ROUNDS; ++u) {
+    const int p = u * kThreads + tid;  // LDS slot (16-byte units)
+    off[u] = chunk_offset<D, IS_K>(p, p / (D / 8));
+  }
+}
+
 template <int D, int BN, bool IS_K>
 __device__ __forceinline__ void issue_tile(const uint16_t* src, int kbase, int kl, uint16_t* lds,
-                                           int tid) {
-  constexpr int CH = D / 8;  // chunks per row
-  constexpr int ROUNDS = BN * CH / kThreads;
+                                           int tid, const int (&off)[CopyShape<D, BN>::ROUNDS]) {
+  constexpr int ROUNDS = CopyShape<D, BN>::ROUNDS;
+  const int rows = kl - kbase;
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(src + (int64_t)kbase * D), 0, rows * D * 2, kRsrcWord3);
   const int wave_base = tid & ~63;
+  if (rows >= BN) {
 #pragma unroll
-  for (int u = 0; u < ROUNDS; ++u) {
-    const int p = u * kThreads + tid;  // LDS slot (16-byte units)
-    const int r = p / CH;
-    const int c = (p % CH) ^ (IS_K ? kswz<D>(r) : vswz<D>(r));
-    const int key = min(kbase + r, kl - 1);
-    const uint16_t* src_chunk = src + (int64_t)key * D + c * 8;
-    __builtin_amdgcn_global_load_lds(src_chunk, (lds_void*)(lds + (u * kThreads + wave_base) * 8),
-                                     16, 0, 0);
+    for (int u = 0; u < ROUNDS; ++u)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, (lds_void*)(lds + (u * kThreads + wave_base) * 8), 16, off[u], 0, 0, 0);
+  } else {
+#pragma unroll
+    for (int u = 0; u < ROUNDS; ++u) {
+      const int p = u * kThreads + tid;
+      const int o = chunk_offset<D, IS_K>(p, min(p / (D / 8), rows - 1));
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, (lds_void*)(lds + (u * kThreads + wave_base) * 8), 16, o, 0, 0, 0);
+    }
   }
 }
 
@@ -162,6 +224,7 @@ __device__ __forceinline__ void wait_vmem() {
 template <int D, bool CAUSAL, bool HAS_MASK, int MODE>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void fa_fwd_kernel(FwdArgs a) {
   static_assert(MODE != kPlain || !HAS_MASK, "the masked forward always runs compensated");
+#if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
   constexpr bool PRECISE = MODE != kPlain;
   constexpr int BN = Cfg<D>::BN;
   constexpr int kQB = Cfg<D>::QB;
@@ -179,9 +242,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 
   const int tid = threadIdx.x;
   // The wave index is made provably wave-uniform so that every condition
-  // derived from it (tile skipping, compensated product, second pass) compiles
-  // to a scalar branch: an MFMA left inside an EXEC-masked region still
-  // accumulates (with whatever its operand registers hold) when EXEC is zero.
+  // derived from it (tile skipping, masking, row selection) compiles to a
+  // scalar branch: an MFMA left inside an EXEC-masked region still accumulates
+  // (with whatever its operand registers hold) when EXEC is zero.
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int c16 = lane & 15;  // query column within a 16-row block / A-operand row
@@ -204,7 +267,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     qt_rev = bid / BH;
     bh = bid % BH;
   }
-  const int qtile = a.n_qtiles - 1 - qt_rev;
+  const int qtile = a.qt_base + a.qt_count - 1 - qt_rev;
   const int b = bh / a.H, h = bh % a.H;
   const int g = h / a.group;
   const int ql = a.ql, kl = a.kl, off = a.causal_off;
@@ -223,43 +286,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   const int wave_kend = CAUSAL ? min(kl, off + wave_last + 1) : kl;
   float* lrow_base = a.l + (int64_t)bh * ql;
 
-  // ---- which rows this workgroup computes ----
-  // Rows that may see fewer than kPreciseKeys keys (a property of their
-  // position) always take the compensated product.
-  auto short_rows = [&](int first_row) {
-    return CAUSAL ? (min(kl, off + first_row + 1) < kPreciseKeys) : (kl < kPreciseKeys);
-  };
-  bool compute = wave_active;
-  bool mine[kQB];  // kFlagged: this lane's row of block qb is to be recomputed
-#pragma unroll
-  for (int qb = 0; qb < kQB; ++qb) mine[qb] = false;
-  if (MODE == kPlain) {
-    if (short_rows(qw0)) {
-      // hand these rows to the compensated kernel
-#pragma unroll
-      for (int qb = 0; qb < kQB; ++qb) {
-        const int qrow = qw0 + 16 * qb + c16;
-        if (grp == 0 && qrow < ql) lrow_base[qrow] = __uint_as_float(kRowFlag);
-      }
-      compute = false;
-    }
-    // the last wave's rows start latest: if they are short, all are
-    if (short_rows(q0 + (kWaves - 1) * kRowsPerWave)) return;
-  } else if (MODE == kFlagged) {
-    bool any = false;
-#pragma unroll
-    for (int qb = 0; qb < kQB; ++qb) {
-      const int qrow = qw0 + 16 * qb + c16;
-      if (qrow < ql) mine[qb] = __float_as_uint(lrow_base[qrow]) == kRowFlag;
-      any |= mine[qb];
-    }
-    compute = __any(any);
-    if (!__syncthreads_or(compute)) return;
-  }
-  if (n_kt > 0) {
-    issue_tile<D, BN, true>(kp, 0, kl, k0s, tid);
-    issue_tile<D, BN, false>(vp, 0, kl, v0s, tid);
-  }
+  const bool compute = wave_active;
+  bool queue_me = false;  // kPlain: some row of this workgroup goes to the rescue kernel
+  const int tile_id = bh * a.n_qtiles + qtile;
+
+  int koff[CopyShape<D, BN>::ROUNDS], voff[CopyShape<D, BN>::ROUNDS];
+  copy_offsets<D, BN, true>(tid, koff);
+  copy_offsets<D, BN, false>(tid, voff);
+  auto issue_k = [&](int kt, uint16_t* dst) { issue_tile<D, BN, true>(kp, kt * BN, kl, dst, tid, koff); };
+  auto issue_v = [&](int kt, uint16_t* dst) { issue_tile<D, BN, false>(vp, kt * BN, kl, dst, tid, voff); };
+  if (n_kt > 0) issue_k(0, k0s);
 
   // ---- Q^T as the B operand: block qb, step s: row qw0+16qb+c16, dims 32s+8grp.. ----
   bf16x8 qop[kQB][NDS];
@@ -275,30 +311,27 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     }
   }
 
-  float m_use[kQB], m_top[kQB], l_run[kQB];
+  float m_use[kQB], l_run[kQB];
   f32x4 oacc[NDB][kQB];
 #pragma unroll
   for (int qb = 0; qb < kQB; ++qb) {
     m_use[qb] = -FLT_MAX / 2.0f;  // max used in exp2 (base 2)
-    m_top[qb] = -FLT_MAX / 2.0f;  // true running max (base 2)
     l_run[qb] = 0.0f;             // this lane's partial row sum
 #pragma unroll
     for (int d = 0; d < NDB; ++d) oacc[d][qb] = f32x4{};
   }
 
-  // One key tile: wait for its copy, start the next one, compute.
-  auto step = [&](int kt, const uint16_t* ks, const uint16_t* vs, uint16_t* nks, uint16_t* nvs) {
-    const int kbase = kt * BN;
-    wait_vmem();
-    __syncthreads();
-    if (kt + 1 < n_kt) {
-      issue_tile<D, BN, true>(kp, kbase + BN, kl, nks, tid);
-      issue_tile<D, BN, false>(vp, kbase + BN, kl, nvs, tid);
-    }
-    if (!compute || kbase >= wave_kend) return;
+  // The wave's own key tiles, and the first of them that needs a mask (the
+  // partial last tile, or the causal diagonal of the wave's first row).
+  const int n_kw = (compute && wave_kend > 0) ? (wave_kend + BN - 1) / BN : 0;
+  int mask_from = HAS_MASK ? 0 : n_kw;
+  if (!HAS_MASK) {
+    if (kl % BN != 0) mask_from = min(mask_from, kl / BN);
+    if (CAUSAL) mask_from = min(mask_from, (off + qw0 + 1) / BN);
+  }
 
-    // ---- S^T = K Q^T (raw scores, f32) ----
-    f32x4 sacc[NKB][kQB];
+  // ---- S^T = K Q^T (raw scores, f32) for the tile in ks ----
+  auto scores = [&](const uint16_t* ks, f32x4 (&sacc)[NKB][kQB]) {
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
@@ -317,41 +350,34 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         // D=256: keep the scheduler from hoisting all K reads (register pressure)
         if (D == 256 && kb == NKB - 1 && (s & 1) == 1) __builtin_amdgcn_sched_barrier(0);
       }
+  };
 
-    // ---- masks: tail keys, causal, additive ----
-    if (HAS_MASK) {
+  // ---- masks of tile kt: tail keys, causal, additive ----
+  auto apply_mask = [&](int kt, f32x4 (&sacc)[NKB][kQB]) {
+    const int kbase = kt * BN;
 #pragma unroll
-      for (int qb = 0; qb < kQB; ++qb) {
-        const int qrow = qw0 + 16 * qb + c16;
-        const float* mrow = a.mask + ((int64_t)bh * ql + min(qrow, ql - 1)) * kl;
+    for (int qb = 0; qb < kQB; ++qb) {
+      const int qrow = qw0 + 16 * qb + c16;
+      const float* mrow = HAS_MASK ? a.mask + ((int64_t)bh * ql + min(qrow, ql - 1)) * kl : nullptr;
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
+      for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int key = kbase + 32 * (kb >> 1) + 8 * grp + 4 * (kb & 1) + i;
-            const bool vis = key < kl && (!CAUSAL || key <= off + qrow);
+        for (int i = 0; i < 4; ++i) {
+          const int key = kbase + 32 * (kb >> 1) + 8 * grp + 4 * (kb & 1) + i;
+          const bool vis = key < kl && (!CAUSAL || key <= off + qrow);
+          if (HAS_MASK)
             sacc[kb][qb][i] =
                 vis ? __builtin_fmaf(sacc[kb][qb][i], a.c, kLog2e * mrow[key]) : -INFINITY;
-          }
-      }
-    } else if ((kbase + BN > kl) || (CAUSAL && kbase + BN - 1 > off + qw0)) {
-#pragma unroll
-      for (int qb = 0; qb < kQB; ++qb) {
-        const int qabs = off + qw0 + 16 * qb + c16;
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int key = kbase + 32 * (kb >> 1) + 8 * grp + 4 * (kb & 1) + i;
-            if (key >= kl || (CAUSAL && key > qabs)) sacc[kb][qb][i] = -INFINITY;
-          }
-      }
+          else if (!vis)
+            sacc[kb][qb][i] = -INFINITY;
+        }
     }
+  };
 
-    // ---- online softmax (base 2), lazy rescale ----
-    // (the decision to raise is taken per row, so a row's result never
-    // depends on its neighbours' scores)
-    float m_new[kQB];
+  // ---- online softmax (base 2): row max of a tile, lazy raise ----
+  // (the decision to raise is taken per row, so a row's result never depends
+  // on its neighbours' scores)
+  auto row_max = [&](const f32x4 (&sacc)[NKB][kQB], float (&m_new)[kQB]) {
     bool raise = false;
 #pragma unroll
     for (int qb = 0; qb < kQB; ++qb) {
@@ -362,25 +388,27 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         for (int i = 0; i < 4; ++i) mx = __builtin_fmaxf(mx, sacc[kb][qb][i]);
       mx = group_max(mx);
       const float tmax = HAS_MASK ? mx : mx * a.c;  // c > 0: max(c*r) == c*max(r)
-      m_top[qb] = __builtin_fmaxf(m_top[qb], tmax);
       const bool r = tmax > m_use[qb] + kLazy;
       m_new[qb] = r ? tmax : m_use[qb];
       raise |= r;
     }
-    if (__any(raise)) {
+    return raise;
+  };
+  auto rescale = [&](const float (&m_new)[kQB]) {
 #pragma unroll
-      for (int qb = 0; qb < kQB; ++qb) {
-        const float alpha = __builtin_amdgcn_exp2f(m_use[qb] - m_new[qb]);
-        m_use[qb] = m_new[qb];
-        l_run[qb] *= alpha;
+    for (int qb = 0; qb < kQB; ++qb) {
+      const float alpha = __builtin_amdgcn_exp2f(m_use[qb] - m_new[qb]);
+      m_use[qb] = m_new[qb];
+      l_run[qb] *= alpha;
 #pragma unroll
-        for (int d = 0; d < NDB; ++d) oacc[d][qb] *= alpha;
-      }
+      for (int d = 0; d < NDB; ++d) oacc[d][qb] *= alpha;
     }
+  };
 
-    // ---- P = exp2(s - m) in bf16 (+ remainder when compensated), row sums ----
+  // ---- P = exp2(s - m) in bf16 (+ remainder when compensated), row sums ----
+  auto probs = [&](const f32x4 (&sacc)[NKB][kQB], bf16x8 (&phi)[NKC][kQB],
+                   bf16x8 (&plo)[NKC][kQB]) {
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-    bf16x8 phi[NKC][kQB], plo[NKC][kQB];
 #pragma unroll
     for (int qb = 0; qb < kQB; ++qb) {
       const float mneg = -m_use[qb];
@@ -409,8 +437,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       }
       l_run[qb] = ls;
     }
+  };
 
-    // ---- O^T += V^T P^T ----
+  // ---- O^T += V^T P^T for the tile in vs ----
+  auto pv = [&](const uint16_t* vs, const bf16x8 (&phi)[NKC][kQB], const bf16x8 (&plo)[NKC][kQB]) {
 #pragma unroll
     for (int d = 0; d < NDB; ++d)
 #pragma unroll
@@ -440,9 +470,27 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       }
   };
 
+  // ---- the key loop ----
+  // one tile per step: wait for its copy, start the next one, compute it
+  if (n_kt > 0) issue_v(0, v0s);
   for (int kt = 0; kt < n_kt; ++kt) {
     const bool odd = kt & 1;
-    step(kt, odd ? k1s : k0s, odd ? v1s : v0s, odd ? k0s : k1s, odd ? v0s : v1s);
+    wait_vmem();
+    __syncthreads();
+    if (kt + 1 < n_kt) {
+      issue_k(kt + 1, odd ? k0s : k1s);
+      issue_v(kt + 1, odd ? v0s : v1s);
+    }
+    if (kt < n_kw) {
+      f32x4 s[NKB][kQB];
+      scores(odd ? k1s : k0s, s);
+      if (kt >= mask_from) apply_mask(kt, s);
+      float m_new[kQB];
+      if (__any(row_max(s, m_new))) rescale(m_new);
+      bf16x8 phi[NKC][kQB], plo[NKC][kQB];
+      probs(s, phi, plo);
+      pv(odd ? v1s : v0s, phi, plo);
+    }
   }
 
   // ---- epilogue: O = O_acc / l (+0 for an empty row), L = (m + log2 l) ln 2 ----
@@ -460,12 +508,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
         for (int i = 0; i < 4; ++i) omax = __builtin_fmaxf(omax, __builtin_fabsf(oacc[d][qb][i]));
       omax = group_max(omax);
-      const float l_rel = l_tot * __builtin_amdgcn_exp2f(m_use[qb] - m_top[qb]);
-      const bool need = row_ok && l_tot > 0.0f && (omax >= kRecheckO * l_tot || l_rel < kRecheckL);
+      const bool need = row_ok && l_tot > 0.0f && omax >= kRecheckO * l_tot;
       if (need && grp == 0) lrow_base[qrow] = __uint_as_float(kRowFlag);
+      queue_me |= need;
       write = row_ok && !need;
-    } else if (MODE == kFlagged) {
-      write = row_ok && mine[qb];
     }
     if (write) {
       const bool empty = !(l_tot > 0.0f);
@@ -482,7 +528,305 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         lrow_base[qrow] = empty ? -INFINITY : (m_use[qb] + __builtin_amdgcn_logf(l_tot)) * kLn2;
     }
   }
+  if (MODE == kPlain && __syncthreads_or(queue_me) && tid == 0) queue_tile(a.queue, tile_id);
   wait_vmem();  // no LDS copy may still be in flight when the workgroup ends
+#endif
+}
+
+// ---- rescue kernel: compensated recomputation of the queued query tiles ----
+// A persistent grid takes queued query tiles (the rows of one workgroup of the
+// plain kernel) one at a time and recomputes their flagged rows with the
+// compensated P.V product (P as a bf16 high part plus a bf16 remainder), in
+// passes of PR rows, skipping passes without a flagged row. In a pass the four
+// waves split every 64-key tile four ways (16 keys each), so the pass walks
+// the key range four times faster than one wave would; each wave keeps its own
+// online-softmax state (max, row sum, O) over its keys, and the four partial
+// results are merged through LDS at the end of the pass. Only rows whose L
+// holds kRowFlag are written.
+constexpr int kRescueBN = 64;
+template <int D> struct RescueCfg;
+template <> struct RescueCfg<64> { static constexpr int QB = 4, STAGES = 4, PER_CU = 2; };
+template <> struct RescueCfg<256> { static constexpr int QB = 1, STAGES = 2, PER_CU = 1; };
+
+// s_waitcnt with vmcnt(N); expcnt and lgkmcnt left at their maxima
+template <int N> __device__ __forceinline__ void wait_vmem_le() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads) void fa_rescue_kernel(FwdArgs a) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  constexpr int QB = RescueCfg<D>::QB;  // 16-row blocks per pass
+  constexpr int NST = RescueCfg<D>::STAGES;
+  constexpr int BN = kRescueBN;
+  constexpr int PR = 16 * QB;       // rows per pass
+  constexpr int BM = block_m<D>();  // rows per queued tile
+  constexpr int NPASS = BM / PR;
+  constexpr int NDS = D / 32;
+  constexpr int NDB = D / 16;
+  constexpr int TILE = BN * D;
+  constexpr int ROUNDS = CopyShape<D, BN>::ROUNDS;
+  constexpr int LOADS_PER_TILE = 2 * ROUNDS;  // K and V copies per thread
+  static_assert(NPASS * PR == BM && BM <= kThreads, "passes must tile the query tile");
+  static_assert(4 * PR * D * 4 <= NST * 2 * TILE * 2, "merge buffer must fit the K/V stages");
+  // K/V stages; after a pass the same memory holds the waves' partial O
+  __shared__ __attribute__((aligned(1024))) uint16_t stage[NST][2][TILE];
+  __shared__ float red_ml[2 * 4 * PR];  // the waves' partial max and row sum
+  __shared__ int item_sh;
+  __shared__ unsigned pass_sh;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  const int lane = tid & 63;
+  const int c16 = lane & 15;
+  const int grp = lane >> 4;
+  const int ql = a.ql, kl = a.kl, off = a.causal_off;
+  int* queue = a.queue;
+  const int n_items = queue[0];
+
+  int koff[ROUNDS], voff[ROUNDS];
+  copy_offsets<D, BN, true>(tid, koff);
+  copy_offsets<D, BN, false>(tid, voff);
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+
+  for (;;) {
+    if (tid == 0) {
+      item_sh = atomicAdd(queue + 1, 1);
+      pass_sh = 0;
+    }
+    __syncthreads();
+    const int it = __builtin_amdgcn_readfirstlane(item_sh);
+    if (it >= n_items) break;
+    const int id = queue[kQueueHeader + it];
+    const int bh = id / a.n_qtiles, q0 = (id % a.n_qtiles) * BM;
+    const int b = bh / a.H, h = bh % a.H, g = h / a.group;
+    const int64_t kv_off = (int64_t)(b * a.Hkv + g) * kl * D;
+    const uint16_t* kp = a.k + kv_off;
+    const uint16_t* vp = a.v + kv_off;
+    float* lrow = a.l + (int64_t)bh * ql;
+
+    // which passes hold a flagged row
+    if (tid < BM && q0 + tid < ql && __float_as_uint(lrow[q0 + tid]) == kRowFlag)
+      atomicOr(&pass_sh, 1u << (tid / PR));
+    __syncthreads();
+    const unsigned passes = __builtin_amdgcn_readfirstlane(pass_sh);
+
+    for (int ps = 0; ps < NPASS; ++ps) {
+      if (!((passes >> ps) & 1u)) continue;
+      const int r0 = q0 + ps * PR;
+      const int kend = CAUSAL ? min(kl, off + min(r0 + PR, ql)) : kl;
+      const int n_t = (kend + BN - 1) / BN;
+
+#pragma unroll
+      for (int st = 0; st < NST - 1; ++st)
+        if (st < n_t) {
+          issue_tile<D, BN, true>(kp, st * BN, kl, stage[st][0], tid, koff);
+          issue_tile<D, BN, false>(vp, st * BN, kl, stage[st][1], tid, voff);
+        }
+
+      bf16x8 qop[QB][NDS];
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const int qrow = min(r0 + 16 * qb + c16, ql - 1);
+        const uint16_t* qp = a.q + ((int64_t)bh * ql + qrow) * D + 8 * grp;
+#pragma unroll
+        for (int s = 0; s < NDS; ++s) {
+          u32x4 raw = *reinterpret_cast<const u32x4*>(qp + 32 * s);
+          raw ^= a.q_sign;
+          qop[qb][s] = __builtin_bit_cast(bf16x8, raw);
+        }
+      }
+      float m_use[QB], l_run[QB];
+      f32x4 oacc[NDB][QB];
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        m_use[qb] = -FLT_MAX / 2.0f;
+        l_run[qb] = 0.0f;
+#pragma unroll
+        for (int d = 0; d < NDB; ++d) oacc[d][qb] = f32x4{};
+      }
+
+      for (int t = 0; t < n_t; ++t) {
+        if (t + NST - 2 < n_t)
+          wait_vmem_le<(NST - 2) * LOADS_PER_TILE>();
+        else
+          wait_vmem();
+        __syncthreads();
+        if (t + NST - 1 < n_t) {
+          const int st = (t + NST - 1) % NST;
+          issue_tile<D, BN, true>(kp, (t + NST - 1) * BN, kl, stage[st][0], tid, koff);
+          issue_tile<D, BN, false>(vp, (t + NST - 1) * BN, kl, stage[st][1], tid, voff);
+        }
+        const int kbase = t * BN + 16 * wave;  // this wave's 16 keys
+        if (kbase >= kend) continue;
+        const uint16_t* ks = stage[t % NST][0];
+        const uint16_t* vs = stage[t % NST][1];
+        const int r = 16 * wave + c16;
+
+        // S^T (16 keys x 16 rows per block): lane holds keys kbase + 4grp + i
+        f32x4 sacc[QB];
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) sacc[qb] = f32x4{};
+#pragma unroll
+        for (int s = 0; s < NDS; ++s) {
+          const bf16x8 kop =
+              *reinterpret_cast<const bf16x8*>(ks + r * D + 8 * ((4 * s + grp) ^ kswz<D>(r)));
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb)
+            sacc[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop[qb][s], sacc[qb], 0, 0, 0);
+        }
+        if (kbase + 16 > kl || (CAUSAL && kbase + 15 > off + r0)) {
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) {
+            const int qabs = off + r0 + 16 * qb + c16;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int key = kbase + 4 * grp + i;
+              if (key >= kl || (CAUSAL && key > qabs)) sacc[qb][i] = -INFINITY;
+            }
+          }
+        }
+        // online softmax over this wave's keys (base 2, lazy raise, per row)
+        float m_new[QB];
+        bool raise = false;
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          const float mx = __builtin_fmaxf(__builtin_fmaxf(sacc[qb][0], sacc[qb][1]),
+                                           __builtin_fmaxf(sacc[qb][2], sacc[qb][3]));
+          const float tmax = group_max(mx) * a.c;
+          const bool rs = tmax > m_use[qb] + kLazy;
+          m_new[qb] = rs ? tmax : m_use[qb];
+          raise |= rs;
+        }
+        if (__any(raise)) {
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) {
+            const float alpha = __builtin_amdgcn_exp2f(m_use[qb] - m_new[qb]);
+            m_use[qb] = m_new[qb];
+            l_run[qb] *= alpha;
+#pragma unroll
+            for (int d = 0; d < NDB; ++d) oacc[d][qb] *= alpha;
+          }
+        }
+        s16x4 phi[QB], plo[QB];
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          bf16x4 hi, lo;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[qb][i], a.c, -m_use[qb]));
+            hi[i] = (__bf16)p;
+            lo[i] = (__bf16)(p - (float)hi[i]);
+          }
+          float ls = l_run[qb];
+          ls = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{hi[0], hi[1]}, ones, ls, false);
+          ls = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{hi[2], hi[3]}, ones, ls, false);
+          ls = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{lo[0], lo[1]}, ones, ls, false);
+          ls = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{lo[2], lo[3]}, ones, ls, false);
+          l_run[qb] = ls;
+          phi[qb] = __builtin_bit_cast(s16x4, hi);
+          plo[qb] = __builtin_bit_cast(s16x4, lo);
+        }
+        // O^T += V^T P^T: V^T operand = dims 16d + c16, keys kbase + 4grp + (0..3)
+#pragma unroll
+        for (int d = 0; d < NDB; ++d) {
+          const int vr = 16 * wave + 4 * grp + (c16 >> 2);
+          const int col = 16 * d + 4 * (c16 & 3);
+          const s16x4 vop = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_s16x4*)(vs + vr * D + 8 * ((col >> 3) ^ vswz<D>(vr)) + (col & 7)));
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) {
+            oacc[d][qb] =
+                __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vop, phi[qb], oacc[d][qb], 0, 0, 0);
+            oacc[d][qb] =
+                __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vop, plo[qb], oacc[d][qb], 0, 0, 0);
+          }
+        }
+      }
+
+      // ---- merge the four waves' partial results ----
+      wait_vmem();
+      __syncthreads();  // every wave is done with the K/V stages
+      float* red_o = reinterpret_cast<float*>(&stage[0][0][0]);  // [wave][row][dim]
+      float* red_m = red_ml;                                      // [wave][row]
+      float* red_l = red_ml + 4 * PR;
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const int row = 16 * qb + c16;
+#pragma unroll
+        for (int d = 0; d < NDB; ++d)
+          *reinterpret_cast<f32x4*>(red_o + (wave * PR + row) * D + 16 * d + 4 * grp) = oacc[d][qb];
+        const float l_tot = group_sum(l_run[qb]);
+        if (grp == 0) {
+          red_m[wave * PR + row] = m_use[qb];
+          red_l[wave * PR + row] = l_tot;
+        }
+      }
+      __syncthreads();
+      {
+        constexpr int TPR = kThreads / PR;  // threads per row
+        constexpr int DPT = D / TPR;        // dims per thread
+        const int row = tid / TPR, d0 = (tid % TPR) * DPT;
+        const int qrow = r0 + row;
+        if (qrow < ql && __float_as_uint(lrow[qrow]) == kRowFlag) {
+          float mw[4], m_all = -FLT_MAX;
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            mw[w] = red_m[w * PR + row];
+            m_all = __builtin_fmaxf(m_all, mw[w]);
+          }
+          float sw[4], l_all = 0.0f;
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            sw[w] = __builtin_amdgcn_exp2f(mw[w] - m_all);
+            l_all += red_l[w * PR + row] * sw[w];
+          }
+          const bool empty = !(l_all > 0.0f);
+          const float inv = empty ? 0.0f : __builtin_amdgcn_rcpf(l_all);
+          uint16_t* orow = a.o + ((int64_t)bh * ql + qrow) * D + d0;
+#pragma unroll
+          for (int e = 0; e < DPT; e += 4) {
+            f32x4 acc = f32x4{};
+#pragma unroll
+            for (int w = 0; w < 4; ++w)
+              acc += *reinterpret_cast<const f32x4*>(red_o + (w * PR + row) * D + d0 + e) * sw[w];
+            bf16x4 ov;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) ov[i] = empty ? (__bf16)0.0f : (__bf16)(acc[i] * inv);
+            *reinterpret_cast<bf16x4*>(orow + e) = ov;
+          }
+        }
+      }
+      __syncthreads();  // flags read, merge buffers free for the next pass
+      if (tid % (kThreads / PR) == 0) {
+        const int row = tid / (kThreads / PR);
+        const int qrow = r0 + row;
+        if (qrow < ql && __float_as_uint(lrow[qrow]) == kRowFlag) {
+          float m_all = -FLT_MAX, l_all = 0.0f;
+#pragma unroll
+          for (int w = 0; w < 4; ++w) m_all = __builtin_fmaxf(m_all, red_m[w * PR + row]);
+#pragma unroll
+          for (int w = 0; w < 4; ++w)
+            l_all += red_l[w * PR + row] * __builtin_amdgcn_exp2f(red_m[w * PR + row] - m_all);
+          lrow[qrow] = l_all > 0.0f ? (m_all + __builtin_amdgcn_logf(l_all)) * kLn2 : -INFINITY;
+        }
+      }
+      __syncthreads();  // red_ml is reused by the next pass
+    }
+    __syncthreads();  // item_sh and pass_sh are rewritten for the next tile
+  }
+
+  // the last workgroup to finish leaves the queue empty for the next call
+  if (tid == 0) {
+    __threadfence();
+    if (atomicAdd(queue + 2, 1) == (int)gridDim.x - 1) {
+      queue[0] = 0;
+      queue[1] = 0;
+      queue[2] = 0;
+    }
+  }
+#endif
 }
 
 template <int D, bool CAUSAL, bool HAS_MASK, int MODE>
@@ -492,24 +836,78 @@ hipError_t launch(const FwdArgs& a, unsigned grid, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Masked: one compensated launch. Unmasked: the plain launch, then the
-// compensated launch for the rows it flagged (same stream, so in order).
+// Masked: one compensated launch over all query tiles. Unmasked: the
+// compensated launch over the tiles with short rows (the first ones), the plain
+// launch over the others, then the rescue launch for the rows the plain launch
+// flagged (one stream, so in order). The rescue grid is persistent: a few
+// workgroups per compute unit, each taking queued tiles until the queue is
+// drained.
 template <int D, bool CAUSAL>
-hipError_t dispatch_c(const FwdArgs& a, bool has_mask, unsigned grid, hipStream_t stream) {
-  if (has_mask) return launch<D, CAUSAL, true, kAll>(a, grid, stream);
-  hipError_t e = launch<D, CAUSAL, false, kPlain>(a, grid, stream);
-  if (e != hipSuccess) return e;
-  return launch<D, CAUSAL, false, kFlagged>(a, grid, stream);
+hipError_t dispatch_c(FwdArgs a, bool has_mask, int n_short, hipStream_t stream) {
+  const unsigned bh = (unsigned)(a.B * a.H);
+  const int n_qt = a.n_qtiles;
+  if (has_mask) {
+    a.qt_base = 0;
+    a.qt_count = n_qt;
+    return launch<D, CAUSAL, true, kAll>(a, bh * n_qt, stream);
+  }
+  if (n_short > 0) {
+    a.qt_base = 0;
+    a.qt_count = n_short;
+    hipError_t e = launch<D, CAUSAL, false, kAll>(a, bh * n_short, stream);
+    if (e != hipSuccess) return e;
+  }
+  if (n_short < n_qt) {
+    a.qt_base = n_short;
+    a.qt_count = n_qt - n_short;
+    hipError_t e = launch<D, CAUSAL, false, kPlain>(a, bh * (n_qt - n_short), stream);
+    if (e != hipSuccess) return e;
+    const int64_t tiles = (int64_t)bh * (n_qt - n_short);
+    const unsigned rgrid = (unsigned)std::min<int64_t>(tiles, 256 * RescueCfg<D>::PER_CU);
+    hipLaunchKernelGGL((fa_rescue_kernel<D, CAUSAL>), dim3(rgrid), dim3(kThreads), 0, stream, a);
+    return hipGetLastError();
+  }
+  return hipSuccess;
 }
 
 template <int D>
-hipError_t dispatch_d(const FwdArgs& a, bool causal, bool has_mask, unsigned grid,
+hipError_t dispatch_d(const FwdArgs& a, bool causal, bool has_mask, int n_short,
                       hipStream_t stream) {
-  return causal ? dispatch_c<D, true>(a, has_mask, grid, stream)
-                : dispatch_c<D, false>(a, has_mask, grid, stream);
+  return causal ? dispatch_c<D, true>(a, has_mask, n_short, stream)
+                : dispatch_c<D, false>(a, has_mask, n_short, stream);
 }
 
 bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+
+// One rescue work queue per (device, stream), allocated on first use (zeroed,
+// synchronously) and replaced by a larger one when a bigger problem arrives;
+// kept until the process ends. Calls on one stream run in order, so they can
+// share it; calls on different streams get different queues.
+int* rescue_queue(hipStream_t stream, int64_t n_ids, hipError_t* err) {
+  static std::mutex mu;
+  static std::map<std::pair<int, hipStream_t>, std::pair<int*, int64_t>> queues;
+  int dev = 0;
+  if ((*err = hipGetDevice(&dev)) != hipSuccess) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  auto& slot = queues[{dev, stream}];
+  if (slot.first && slot.second >= n_ids) return slot.first;
+  if (slot.first) {
+    // the old queue may still be in use by work enqueued on this stream
+    if ((*err = hipStreamSynchronize(stream)) != hipSuccess) return nullptr;
+    (void)hipFree(slot.first);
+    slot = {nullptr, 0};
+  }
+  const int64_t cap = std::max<int64_t>(n_ids, 1024);
+  const size_t bytes = (size_t)(kQueueHeader + cap) * sizeof(int);
+  int* q = nullptr;
+  if ((*err = hipMalloc(&q, bytes)) != hipSuccess) return nullptr;
+  if ((*err = hipMemset(q, 0, bytes)) != hipSuccess) {
+    (void)hipFree(q);
+    return nullptr;
+  }
+  slot = {q, cap};
+  return q;
+}
 
 }  // namespace
 
@@ -530,7 +928,9 @@ extern "C" int fa_train_fwd(const void* q, const void* k, const void* v, const f
   const int bm = head_dim == 64 ? block_m<64>() : block_m<256>();
   const int64_t n_qtiles = ((int64_t)ql + bm - 1) / bm;
   const int64_t grid = n_qtiles * batch * n_heads;
-  if (grid > 0x7fffffffLL || (int64_t)batch * n_heads > 0x7fffffffLL) return FA_ERR_TOO_LARGE;
+  if (grid > 0x7fffffffLL || (int64_t)batch * n_heads > 0x7fffffffLL ||
+      (int64_t)kl * head_dim * 2 > 0x7fffffffLL)  // one head's K or V must fit a buffer descriptor
+    return FA_ERR_TOO_LARGE;
 
   FwdArgs a;
   a.q = static_cast<const uint16_t*>(q);
@@ -552,10 +952,23 @@ extern "C" int fa_train_fwd(const void* q, const void* k, const void* v, const f
   // produces round to 0 in f32, so the weights are the same uniform ones).
   a.c = fmaxf(fabsf(scale) * kLog2e, FLT_MIN);
   a.q_sign = signbit(scale) ? 0x80008000u : 0u;
+  a.queue = nullptr;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t err = head_dim == 64 ? dispatch_d<64>(a, causal != 0, mask != nullptr, (unsigned)grid, s)
-                                  : dispatch_d<256>(a, causal != 0, mask != nullptr, (unsigned)grid, s);
+  if (!mask) {
+    hipError_t qerr = hipSuccess;
+    a.queue = rescue_queue(s, grid, &qerr);
+    if (!a.queue) return qerr == hipErrorOutOfMemory ? FA_ERR_NO_MEMORY : FA_ERR_LAUNCH;
+  }
+  // query tiles whose first row may see fewer than kPreciseKeys keys
+  int64_t n_short = 0;
+  if (kl < kPreciseKeys)
+    n_short = n_qtiles;
+  else if (causal && a.causal_off + 1 < kPreciseKeys)
+    n_short = std::min<int64_t>(n_qtiles, (kPreciseKeys - 1 - a.causal_off + bm - 1) / bm);
+  hipError_t err =
+      head_dim == 64 ? dispatch_d<64>(a, causal != 0, mask != nullptr, (int)n_short, s)
+                     : dispatch_d<256>(a, causal != 0, mask != nullptr, (int)n_short, s);
   return err == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
@@ -570,6 +983,7 @@ extern "C" const char* fa_status_string(int status) {
     case FA_ERR_ALIGNMENT: return "misaligned tensor (q, k, v, O need 16 bytes; mask, L 4 bytes)";
     case FA_ERR_TOO_LARGE: return "problem too large for the kernel's grid or index range";
     case FA_ERR_LAUNCH: return "HIP kernel launch failed";
+    case FA_ERR_NO_MEMORY: return "could not allocate the rescue work queue";
     default: return "unknown status";
   }
 }

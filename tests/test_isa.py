@@ -5,8 +5,9 @@ hipcc cross-compiles the kernels to assembly here).
   s_*_saveexec and the s_or_b64 exec that restores EXEC). Such an MFMA still
   accumulates when EXEC is zero, so a wave-uniform condition that the compiler
   could not prove uniform silently corrupts O.
-- The key-tile loop (the innermost loop, "Depth=2" in the compiler's block
-  annotations) must not touch scratch memory (register spills) in any variant.
+- The key-tile loop (the innermost loop: the deepest "Depth=N" in the
+  compiler's block annotations) must not touch scratch memory (register
+  spills) in any variant.
 """
 import os
 import re
@@ -28,7 +29,7 @@ def isa(tmp_path_factory):
     kernels = {}
     name = None
     for line in text.split("\n"):
-        m = re.match(r"^(_Z\w*fa_fwd_kernel\w+):", line)
+        m = re.match(r"^(_Z\w*fa_(?:fwd|rescue)_kernel\w+):", line)
         if m:
             name = m.group(1)
             kernels[name] = []
@@ -38,7 +39,7 @@ def isa(tmp_path_factory):
 
 
 def test_all_variants_present(isa):
-    assert len(isa) == 12  # head_dim x causal x {plain, compensated flagged, compensated masked}
+    assert len(isa) == 16  # head_dim x causal x {plain, compensated, compensated masked, rescue}
 
 
 def test_no_mfma_under_exec_mask(isa):
@@ -55,9 +56,12 @@ def test_no_mfma_under_exec_mask(isa):
 
 def test_key_loop_does_not_spill(isa):
     for name, lines in isa.items():
+        depths = [int(m.group(1)) for line in lines for m in [re.search(r"Depth=(\d+)", line)] if m]
+        assert depths, f"{name}: no loop found"
+        deepest = f"Depth={max(depths)}"
         in_inner = False
         for line in lines:
             if re.match(r"^\.LBB\w+:", line) or re.match(r"^; %bb\.\d+:", line):
-                in_inner = "Depth=2" in line
+                in_inner = deepest in line
             elif in_inner and re.search(r"\bscratch_(load|store)", line):
                 raise AssertionError(f"{name}: spill in the key loop: {line.strip()}")
