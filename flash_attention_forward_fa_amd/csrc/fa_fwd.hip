@@ -59,8 +59,8 @@ constexpr int kThreads = 256;  // rescue kernel: 4 waves
 //   D=256: 1 block (16 rows per wave, 128 per workgroup), 32-key tiles; the
 //          O accumulator of 16 rows x 256 dims is 64 registers per lane.
 template <int D> struct Cfg;
-template <> struct Cfg<64> { static constexpr int W = 8, QB = 2, BN = 64; };
-template <> struct Cfg<256> { static constexpr int W = 8, QB = 1, BN = 32; };
+template <> struct Cfg<64> { static constexpr int W = 8, QB = 2, BN = 64, WPE = 4; };
+template <> struct Cfg<256> { static constexpr int W = 8, QB = 1, BN = 32, WPE = 2; };
 template <int D> constexpr int block_m() { return Cfg<D>::W * 16 * Cfg<D>::QB; }
 
 // Query tiles with a row that may see fewer keys than this (a property of
@@ -133,6 +133,18 @@ __device__ __forceinline__ float swap16(float x, bool take_max) {
 }
 // max / sum over the four 16-lane groups (lanes l, l^16, l^32, l^48)
 __device__ __forceinline__ float group_max(float x) { return swap16(swap32(x, true), true); }
+// group_max of two values at once: the first swap pairs the upper half of x
+// with the lower half of y, so one max reduces x in lanes 0-31 and y in lanes
+// 32-63; after the 16-lane step a last swap hands each half's result back to
+// all lanes.
+__device__ __forceinline__ void group_max2(float& x, float& y) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+  const float h = __builtin_fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  const float f = swap16(h, true);
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(f), __float_as_uint(f), false, false);
+  x = __uint_as_float(b[0]);
+  y = __uint_as_float(b[1]);
+}
 __device__ __forceinline__ float group_sum(float x) { return swap16(swap32(x, false), false); }
 
 // Row of a 32-key chunk that lane row m of key block kb (16 keys) loads as the
@@ -194,12 +206,12 @@ __device__ __forceinline__ void copy_offsets(int tid, int (&off)[CopyShape<D, BN
 
 template <int D, int BN, int NT, bool IS_K>
 __device__ __forceinline__ void issue_tile(const uint16_t* src, int kbase, int kl, uint16_t* lds,
-                                           int tid, const int (&off)[CopyShape<D, BN, NT>::ROUNDS]) {
+                                           int tid, int wave_base,
+                                           const int (&off)[CopyShape<D, BN, NT>::ROUNDS]) {
   constexpr int ROUNDS = CopyShape<D, BN, NT>::ROUNDS;
   const int rows = kl - kbase;
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(src + (int64_t)kbase * D), 0, rows * D * 2, kRsrcWord3);
-  const int wave_base = tid & ~63;
   if (rows >= BN) {
 #pragma unroll
     for (int u = 0; u < ROUNDS; ++u)
@@ -222,7 +234,8 @@ __device__ __forceinline__ void wait_vmem() {
 }
 
 template <int D, bool CAUSAL, bool HAS_MASK, int MODE>
-__global__ __launch_bounds__(64 * Cfg<D>::W) __attribute__((amdgpu_waves_per_eu(2))) void fa_fwd_kernel(FwdArgs a) {
+__global__ __launch_bounds__(64 * Cfg<D>::W)
+__attribute__((amdgpu_waves_per_eu(MODE == kPlain ? Cfg<D>::WPE : 2))) void fa_fwd_kernel(FwdArgs a) {
   static_assert(MODE != kPlain || !HAS_MASK, "the masked forward always runs compensated");
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
   constexpr bool PRECISE = MODE != kPlain;
@@ -254,16 +267,20 @@ __global__ __launch_bounds__(64 * Cfg<D>::W) __attribute__((amdgpu_waves_per_eu(
   // ---- work item ----
   // Workgroups are handed to the 8 XCDs round-robin (bid mod 8). When B*H is a
   // multiple of 8, XCD x owns the heads [x*per, (x+1)*per) (so one KV group
-  // stays within one XCD's L2) and walks its query tiles heaviest (most keys)
-  // first across all its heads, so the cheap tiles fill the tail. (Running one
-  // head at a time per XCD was measured slower.)
+  // stays within one XCD's L2), takes them in groups of 8 (when per is a
+  // multiple of 8; fewer K/V in flight per L2) and walks each group's query
+  // tiles heaviest (most keys) first, so the cheap tiles fill the tail.
+  // (Groups of 1, 2 or 4 heads were measured slower, 8 faster than all.)
   const int BH = a.B * a.H;
   const int bid = blockIdx.x;
   int qt_rev, bh;
   if ((BH & 7) == 0) {
     const int xcd = bid & 7, tl = bid >> 3, per = BH >> 3;
-    qt_rev = tl / per;
-    bh = xcd * per + tl % per;
+    const int gh = (per & 7) == 0 ? 8 : per;  // heads per group
+    const int gsz = gh * a.qt_count;          // workgroups per group
+    const int gi = tl / gsz, r = tl % gsz;
+    qt_rev = r / gh;
+    bh = xcd * per + gi * gh + r % gh;
   } else {
     qt_rev = bid / BH;
     bh = bid % BH;
@@ -295,10 +312,10 @@ __global__ __launch_bounds__(64 * Cfg<D>::W) __attribute__((amdgpu_waves_per_eu(
   copy_offsets<D, BN, NT, true>(tid, koff);
   copy_offsets<D, BN, NT, false>(tid, voff);
   auto issue_k = [&](int kt, uint16_t* dst) {
-    issue_tile<D, BN, NT, true>(kp, kt * BN, kl, dst, tid, koff);
+    issue_tile<D, BN, NT, true>(kp, kt * BN, kl, dst, tid, 64 * wave, koff);
   };
   auto issue_v = [&](int kt, uint16_t* dst) {
-    issue_tile<D, BN, NT, false>(vp, kt * BN, kl, dst, tid, voff);
+    issue_tile<D, BN, NT, false>(vp, kt * BN, kl, dst, tid, 64 * wave, voff);
   };
   if (n_kt > 0) issue_k(0, k0s);
 
@@ -316,12 +333,16 @@ __global__ __launch_bounds__(64 * Cfg<D>::W) __attribute__((amdgpu_waves_per_eu(
     }
   }
 
-  float m_use[kQB], l_run[kQB];
+  // m_use: the max used in exp2 (base 2); thr: raw score above which a tile
+  // raises it (m_use + kLazy in raw units); l_run: this lane's partial row sum.
+  float m_use[kQB], thr[kQB], l_run[kQB];
   f32x4 oacc[NDB][kQB];
+  const float inv_c = HAS_MASK ? 1.0f : 1.0f / a.c;
 #pragma unroll
   for (int qb = 0; qb < kQB; ++qb) {
-    m_use[qb] = -FLT_MAX / 2.0f;  // max used in exp2 (base 2)
-    l_run[qb] = 0.0f;             // this lane's partial row sum
+    m_use[qb] = -FLT_MAX / 2.0f;
+    thr[qb] = -INFINITY;
+    l_run[qb] = 0.0f;
 #pragma unroll
     for (int d = 0; d < NDB; ++d) oacc[d][qb] = f32x4{};
   }
@@ -382,28 +403,36 @@ __global__ __launch_bounds__(64 * Cfg<D>::W) __attribute__((amdgpu_waves_per_eu(
   // ---- online softmax (base 2): row max of a tile, lazy raise ----
   // (the decision to raise is taken per row, so a row's result never depends
   // on its neighbours' scores)
-  auto row_max = [&](const f32x4 (&sacc)[NKB][kQB], float (&m_new)[kQB]) {
-    bool raise = false;
+  // (the max is compared with thr in raw-score units; c > 0, so
+  // max(c*r) == c*max(r))
+  auto row_max = [&](const f32x4 (&sacc)[NKB][kQB], float (&mx)[kQB]) {
 #pragma unroll
     for (int qb = 0; qb < kQB; ++qb) {
-      float mx = -INFINITY;
+      mx[qb] = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) mx = __builtin_fmaxf(mx, sacc[kb][qb][i]);
-      mx = group_max(mx);
-      const float tmax = HAS_MASK ? mx : mx * a.c;  // c > 0: max(c*r) == c*max(r)
-      const bool r = tmax > m_use[qb] + kLazy;
-      m_new[qb] = r ? tmax : m_use[qb];
-      raise |= r;
+        for (int i = 0; i < 4; ++i) mx[qb] = __builtin_fmaxf(mx[qb], sacc[kb][qb][i]);
     }
+    if constexpr (kQB == 2) {
+      group_max2(mx[0], mx[1]);
+    } else {
+#pragma unroll
+      for (int qb = 0; qb < kQB; ++qb) mx[qb] = group_max(mx[qb]);
+    }
+    bool raise = false;
+#pragma unroll
+    for (int qb = 0; qb < kQB; ++qb) raise |= mx[qb] > thr[qb];
     return raise;
   };
-  auto rescale = [&](const float (&m_new)[kQB]) {
+  auto rescale = [&](const float (&mx)[kQB]) {
 #pragma unroll
     for (int qb = 0; qb < kQB; ++qb) {
-      const float alpha = __builtin_amdgcn_exp2f(m_use[qb] - m_new[qb]);
-      m_use[qb] = m_new[qb];
+      const bool r = mx[qb] > thr[qb];
+      const float m_new = r ? (HAS_MASK ? mx[qb] : mx[qb] * a.c) : m_use[qb];
+      const float alpha = __builtin_amdgcn_exp2f(m_use[qb] - m_new);
+      m_use[qb] = m_new;
+      thr[qb] = r ? (m_new + kLazy) * inv_c : thr[qb];
       l_run[qb] *= alpha;
 #pragma unroll
       for (int d = 0; d < NDB; ++d) oacc[d][qb] *= alpha;
@@ -490,8 +519,8 @@ __global__ __launch_bounds__(64 * Cfg<D>::W) __attribute__((amdgpu_waves_per_eu(
       f32x4 s[NKB][kQB];
       scores(odd ? k1s : k0s, s);
       if (kt >= mask_from) apply_mask(kt, s);
-      float m_new[kQB];
-      if (__any(row_max(s, m_new))) rescale(m_new);
+      float mx[kQB];
+      if (__any(row_max(s, mx))) rescale(mx);
       bf16x8 phi[NKC][kQB], plo[NKC][kQB];
       probs(s, phi, plo);
       pv(odd ? v1s : v0s, phi, plo);
@@ -626,8 +655,8 @@ __global__ __launch_bounds__(kThreads) void fa_rescue_kernel(FwdArgs a) {
 #pragma unroll
       for (int st = 0; st < NST - 1; ++st)
         if (st < n_t) {
-          issue_tile<D, BN, kThreads, true>(kp, st * BN, kl, stage[st][0], tid, koff);
-          issue_tile<D, BN, kThreads, false>(vp, st * BN, kl, stage[st][1], tid, voff);
+          issue_tile<D, BN, kThreads, true>(kp, st * BN, kl, stage[st][0], tid, 64 * wave, koff);
+          issue_tile<D, BN, kThreads, false>(vp, st * BN, kl, stage[st][1], tid, 64 * wave, voff);
         }
 
       bf16x8 qop[QB][NDS];
@@ -660,8 +689,10 @@ __global__ __launch_bounds__(kThreads) void fa_rescue_kernel(FwdArgs a) {
         __syncthreads();
         if (t + NST - 1 < n_t) {
           const int st = (t + NST - 1) % NST;
-          issue_tile<D, BN, kThreads, true>(kp, (t + NST - 1) * BN, kl, stage[st][0], tid, koff);
-          issue_tile<D, BN, kThreads, false>(vp, (t + NST - 1) * BN, kl, stage[st][1], tid, voff);
+          issue_tile<D, BN, kThreads, true>(kp, (t + NST - 1) * BN, kl, stage[st][0], tid,
+                                            64 * wave, koff);
+          issue_tile<D, BN, kThreads, false>(vp, (t + NST - 1) * BN, kl, stage[st][1], tid,
+                                             64 * wave, voff);
         }
         const int kbase = t * BN + 16 * wave;  // this wave's 16 keys
         if (kbase >= kend) continue;
