@@ -176,7 +176,9 @@ def main():
     traffic = stored_traffic(dom.name)
     roofline = {"bound": "mfma", "achieved": dp["tflops"], "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": dp["tflops"] / PEAK_BF16_TFLOPS,
-                "traffic": traffic, "kernel": f"fa_fwd_kernel<D={dom.D},causal={dom.causal}>",
+                "traffic": traffic,
+                "kernel": f"fa_train_fwd launches (plain fa_fwd_kernel<{dom.D}, causal> + "
+                          f"compensated short-tile + rescue)",
                 "workload": dom.name}
 
     value = total_flop / (total_ms * 1e-3) / 1e12
