@@ -230,6 +230,13 @@ __device__ __forceinline__ void issue_tile(const uint16_t* src, int kbase, int k
   }
 }
 
+// Wave priority for the next instructions, pinned in place.
+template <int P> __device__ __forceinline__ void set_prio() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_setprio(P);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 __device__ __forceinline__ void wait_vmem() {
   // vmcnt(0); expcnt and lgkmcnt left at their maxima
   __builtin_amdgcn_s_waitcnt(0x0F70);
@@ -577,14 +584,21 @@ __attribute__((amdgpu_waves_per_eu(MODE == kPlain ? Cfg<D>::WPE : 2))) void fa_f
       issue_v(kt + 1, odd ? v0s : v1s);
     }
     if (kt < n_kw) {
+      // A wave issuing its MFMA blocks gets a raised priority (s_setprio), so
+      // it is not held back behind the other waves' VALU work; measured best
+      // around the P.V block for D=64 and around both blocks for D=256.
       f32x4 s[NKB][kQB];
+      if (D == 256) set_prio<2>();
       scores(odd ? k1s : k0s, s);
+      if (D == 256) set_prio<0>();
       if (kt >= mask_from) apply_mask(kt, s);
       float mx[kQB];
       if (__any(row_max(s, mx))) rescale(mx);
       bf16x8 phi[NKC][kQB], plo[NKC][kQB];
       probs(s, phi, plo);
+      set_prio<2>();
       pv(odd ? v1s : v0s, phi, plo);
+      set_prio<0>();
     }
   }
 
