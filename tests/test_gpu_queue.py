@@ -1,0 +1,82 @@
+"""GPU tests of the rescue work queue that the library keeps per (device,
+stream): it is empty again after every call, grows when a larger problem
+arrives, and calls on different streams do not share it. Inputs have V scaled
+by 4 so that many rows reach |O| >= 1 and take the rescue path."""
+import numpy as np
+import pytest
+
+import fagen
+import oracle
+from tests import gpu_util as gu
+from tests.test_gpu_parity import _times4
+
+pytestmark = pytest.mark.gpu
+
+
+def _inputs(w):
+    inp = dict(fagen.generate(w))
+    inp["v"] = _times4(inp["v"])
+    return inp
+
+
+_keep = []
+
+
+def _upload(torch, inp):
+    t = tuple(gu.to_dev(inp[n], "cuda:0") for n in ("q", "k", "v"))
+    _keep.extend(t)  # inputs stay allocated until the streams are synchronised
+    return t
+
+
+def _launch(fa, torch, qkv, w, stream=None):
+    q, k, v = qkv
+    return fa.train_fwd(q, k, v, scale=w.scale, causal=w.causal, stream=stream)
+
+
+def _bits(O):
+    import torch
+    return O.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("D", [64, 256])
+def test_queue_is_reused_grown_and_per_stream(D):
+    import torch
+    import flash_attention_forward_fa_amd as fa
+    small = fagen.Workload("q_small", 1, 2, 1, 300, 300, D, True, seed_offset=4000 + D)
+    large = fagen.Workload("q_large", 2, 4, 2, 1100, 1100, D, True, seed_offset=4100 + D)
+    print(f"case queue D={D}", flush=True)
+    inp_s, inp_l = _inputs(small), _inputs(large)
+    dev_s, dev_l = _upload(torch, inp_s), _upload(torch, inp_l)
+    torch.cuda.synchronize()
+
+    # small first (queue sized for it), then large (queue replaced), then small again
+    O1, L1 = _launch(fa, torch, dev_s, small)
+    O2, L2 = _launch(fa, torch, dev_l, large)
+    O3, L3 = _launch(fa, torch, dev_s, small)
+    torch.cuda.synchronize()
+    for (O, L, w, inp) in ((O1, L1, small, inp_s), (O2, L2, large, inp_l)):
+        _, ob, lr = oracle.fwd_workload(w, inp)
+        big = int((np.abs(gu.widen(ob)) >= 1).any(axis=-1).sum())
+        assert big >= 20, big
+        bits = _bits(O)
+        gu.compare(gu.widen(bits), L.cpu().numpy(), bits, ob, lr, 1e-2, 1e-2,
+                   f"queue {w.name} D={D}", one_step_ok=True)
+    assert np.array_equal(_bits(O1), _bits(O3))
+    assert np.array_equal(L1.cpu().numpy().view(np.uint32), L3.cpu().numpy().view(np.uint32))
+
+    # both problems at once on two new streams: each stream has its own queue
+    # (the first call on a stream allocates its queue, which synchronises that
+    # stream only; the launches are then in flight together)
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    _keep.extend(_launch(fa, torch, dev_s, small, stream=s1))
+    _keep.extend(_launch(fa, torch, dev_s, small, stream=s2))
+    torch.cuda.synchronize()
+    O4, L4 = _launch(fa, torch, dev_l, large, stream=s1)
+    O5, L5 = _launch(fa, torch, dev_s, small, stream=s2)
+    torch.cuda.synchronize()
+    assert np.array_equal(_bits(O4), _bits(O2))
+    assert np.array_equal(L4.cpu().numpy().view(np.uint32), L2.cpu().numpy().view(np.uint32))
+    assert np.array_equal(_bits(O5), _bits(O1))
+    assert np.array_equal(L5.cpu().numpy().view(np.uint32), L1.cpu().numpy().view(np.uint32))
+    _keep.clear()
+    print(f"queue D={D}: reuse, growth and two streams bit-identical", flush=True)
