@@ -90,10 +90,11 @@ constexpr int kPlain = 0, kAll = 1;
 constexpr uint32_t kRowFlag = 0x7FC0FA00u;  // a quiet NaN; never a valid L
 
 // Work queue of query tiles for the rescue kernel (device memory, int words):
-// [0] number of queued tiles, [1] next tile to take, [2] rescue workgroups
-// finished, [3] unused, [4..] tile ids (bh * n_qtiles + query tile). The
-// rescue kernel's last workgroup zeroes words 0..2, so the queue is empty
-// between calls.
+// two counter sets, [0..1] and [2..3] (number of queued tiles, next tile to
+// take), used by alternate calls on a stream, then the tile ids
+// (bh * n_qtiles + query tile) from word 4. A call's rescue launch zeroes the
+// other set, which the next call uses; no workgroup has to wait for the others
+// to finish, and an empty queue costs one load per workgroup.
 constexpr int kQueueHeader = 4;
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -114,13 +115,16 @@ struct FwdArgs {
   int causal_off;  // max(kl - ql, 0)
   float c;         // |scale| * log2(e), at least FLT_MIN
   uint32_t q_sign; // 0x80008000 flips the sign of both bf16 halves (scale < 0)
-  int* queue;      // rescue work queue (kPlain, rescue kernel)
+  int* qcount;     // this call's counter set of the rescue work queue
+  int* qother;     // the other counter set (zeroed by this call's rescue launch)
+  int* qitems;     // queued tile ids
+  int qcap;        // capacity of qitems
 };
 
 // Queue a query tile for the rescue kernel (one lane).
-__device__ __forceinline__ void queue_tile(int* queue, int id) {
-  const int slot = atomicAdd(queue, 1);
-  queue[kQueueHeader + slot] = id;
+__device__ __forceinline__ void queue_tile(const FwdArgs& a, int id) {
+  const int slot = atomicAdd(a.qcount, 1);
+  if (slot < a.qcap) a.qitems[slot] = id;
 }
 
 __device__ __forceinline__ float swap32(float x, bool take_max) {
@@ -637,7 +641,7 @@ __attribute__((amdgpu_waves_per_eu(MODE == kPlain ? Cfg<D>::WPE : 2))) void fa_f
         lrow_base[qrow] = empty ? -INFINITY : (m_use[qb] + __builtin_amdgcn_logf(l_tot)) * kLn2;
     }
   }
-  if (MODE == kPlain && __syncthreads_or(queue_me) && tid == 0) queue_tile(a.queue, tile_id);
+  if (MODE == kPlain && __syncthreads_or(queue_me) && tid == 0) queue_tile(a, tile_id);
   wait_vmem();  // no LDS copy may still be in flight when the workgroup ends
 #endif
 }
@@ -691,8 +695,12 @@ __global__ __launch_bounds__(kThreads) void fa_rescue_kernel(FwdArgs a) {
   const int c16 = lane & 15;
   const int grp = lane >> 4;
   const int ql = a.ql, kl = a.kl, off = a.causal_off;
-  int* queue = a.queue;
-  const int n_items = queue[0];
+  const int n_items = min(a.qcount[0], a.qcap);
+  if (blockIdx.x == 0 && tid == 0) {  // empty the next call's counter set
+    a.qother[0] = 0;
+    a.qother[1] = 0;
+  }
+  if ((int)blockIdx.x >= n_items) return;  // no work item could reach this workgroup
 
   int koff[ROUNDS], voff[ROUNDS];
   copy_offsets<D, BN, kThreads, true>(tid, koff);
@@ -701,13 +709,13 @@ __global__ __launch_bounds__(kThreads) void fa_rescue_kernel(FwdArgs a) {
 
   for (;;) {
     if (tid == 0) {
-      item_sh = atomicAdd(queue + 1, 1);
+      item_sh = atomicAdd(a.qcount + 1, 1);
       pass_sh = 0;
     }
     __syncthreads();
     const int it = __builtin_amdgcn_readfirstlane(item_sh);
     if (it >= n_items) break;
-    const int id = queue[kQueueHeader + it];
+    const int id = a.qitems[it];
     const int bh = id / a.n_qtiles, q0 = (id % a.n_qtiles) * BM;
     const int b = bh / a.H, h = bh % a.H, g = h / a.group;
     const int64_t kv_off = (int64_t)(b * a.Hkv + g) * kl * D;
@@ -928,15 +936,6 @@ __global__ __launch_bounds__(kThreads) void fa_rescue_kernel(FwdArgs a) {
     __syncthreads();  // item_sh and pass_sh are rewritten for the next tile
   }
 
-  // the last workgroup to finish leaves the queue empty for the next call
-  if (tid == 0) {
-    __threadfence();
-    if (atomicAdd(queue + 2, 1) == (int)gridDim.x - 1) {
-      queue[0] = 0;
-      queue[1] = 0;
-      queue[2] = 0;
-    }
-  }
 #endif
 }
 
@@ -993,31 +992,46 @@ bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p
 // One rescue work queue per (device, stream), allocated on first use (zeroed,
 // synchronously) and replaced by a larger one when a bigger problem arrives;
 // kept until the process ends. Calls on one stream run in order, so they can
-// share it; calls on different streams get different queues.
-int* rescue_queue(hipStream_t stream, int64_t n_ids, hipError_t* err) {
+// share it; calls on different streams get different queues. Each call that
+// launches the rescue kernel takes the next counter set (set_args).
+struct RescueQueue {
+  int* ptr = nullptr;
+  int64_t cap = 0;
+  int parity = 0;
+};
+
+hipError_t rescue_queue(hipStream_t stream, int64_t n_ids, FwdArgs* a) {
   static std::mutex mu;
-  static std::map<std::pair<int, hipStream_t>, std::pair<int*, int64_t>> queues;
+  static std::map<std::pair<int, hipStream_t>, RescueQueue> queues;
   int dev = 0;
-  if ((*err = hipGetDevice(&dev)) != hipSuccess) return nullptr;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
   std::lock_guard<std::mutex> lock(mu);
-  auto& slot = queues[{dev, stream}];
-  if (slot.first && slot.second >= n_ids) return slot.first;
-  if (slot.first) {
-    // the old queue may still be in use by work enqueued on this stream
-    if ((*err = hipStreamSynchronize(stream)) != hipSuccess) return nullptr;
-    (void)hipFree(slot.first);
-    slot = {nullptr, 0};
+  RescueQueue& rq = queues[{dev, stream}];
+  if (!rq.ptr || rq.cap < n_ids) {
+    if (rq.ptr) {
+      // the old queue may still be in use by work enqueued on this stream
+      if ((err = hipStreamSynchronize(stream)) != hipSuccess) return err;
+      (void)hipFree(rq.ptr);
+      rq = RescueQueue{};
+    }
+    const int64_t cap = std::max<int64_t>(n_ids, 1024);
+    const size_t bytes = (size_t)(kQueueHeader + cap) * sizeof(int);
+    int* q = nullptr;
+    if ((err = hipMalloc(&q, bytes)) != hipSuccess) return err;
+    if ((err = hipMemset(q, 0, bytes)) != hipSuccess) {
+      (void)hipFree(q);
+      return err;
+    }
+    rq.ptr = q;
+    rq.cap = cap;
   }
-  const int64_t cap = std::max<int64_t>(n_ids, 1024);
-  const size_t bytes = (size_t)(kQueueHeader + cap) * sizeof(int);
-  int* q = nullptr;
-  if ((*err = hipMalloc(&q, bytes)) != hipSuccess) return nullptr;
-  if ((*err = hipMemset(q, 0, bytes)) != hipSuccess) {
-    (void)hipFree(q);
-    return nullptr;
-  }
-  slot = {q, cap};
-  return q;
+  a->qcount = rq.ptr + 2 * rq.parity;
+  a->qother = rq.ptr + 2 * (1 - rq.parity);
+  a->qitems = rq.ptr + kQueueHeader;
+  a->qcap = (int)std::min<int64_t>(rq.cap, 0x7fffffff);
+  rq.parity ^= 1;
+  return hipSuccess;
 }
 
 }  // namespace
@@ -1063,23 +1077,28 @@ extern "C" int fa_train_fwd(const void* q, const void* k, const void* v, const f
   // produces round to 0 in f32, so the weights are the same uniform ones).
   a.c = fmaxf(fabsf(scale) * kLog2e, FLT_MIN);
   a.q_sign = signbit(scale) ? 0x80008000u : 0u;
-  a.queue = nullptr;
+  a.qcount = a.qother = a.qitems = nullptr;
+  a.qcap = 0;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (!mask) {
-    hipError_t qerr = hipSuccess;
-    a.queue = rescue_queue(s, grid, &qerr);
-    if (!a.queue) return qerr == hipErrorOutOfMemory ? FA_ERR_NO_MEMORY : FA_ERR_LAUNCH;
-  }
   // query tiles whose first row may see fewer than kPreciseKeys keys
   int64_t n_short = 0;
   if (kl < kPreciseKeys)
     n_short = n_qtiles;
   else if (causal && a.causal_off + 1 < kPreciseKeys)
     n_short = std::min<int64_t>(n_qtiles, (kPreciseKeys - 1 - a.causal_off + bm - 1) / bm);
+  const bool plain = !mask && n_short < n_qtiles;  // plain and rescue launches follow
+  if (plain) {
+    const hipError_t qerr = rescue_queue(s, (n_qtiles - n_short) * batch * n_heads, &a);
+    if (qerr != hipSuccess) return qerr == hipErrorOutOfMemory ? FA_ERR_NO_MEMORY : FA_ERR_LAUNCH;
+  }
   hipError_t err =
       head_dim == 64 ? dispatch_d<64>(a, causal != 0, mask != nullptr, (int)n_short, s)
                      : dispatch_d<256>(a, causal != 0, mask != nullptr, (int)n_short, s);
+  if (err != hipSuccess && plain) {
+    // the rescue launch did not zero the next counter set: clear both
+    (void)hipMemsetAsync(std::min(a.qcount, a.qother), 0, kQueueHeader * sizeof(int), s);
+  }
   return err == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
