@@ -16,7 +16,7 @@ LIB_PATH = _build.LIB
 FA_STATUS = {
     0: "FA_OK", 1: "FA_ERR_NULL_POINTER", 2: "FA_ERR_BAD_SIZE", 3: "FA_ERR_HEAD_GROUPING",
     4: "FA_ERR_HEAD_DIM", 5: "FA_ERR_SCALE", 6: "FA_ERR_ALIGNMENT", 7: "FA_ERR_TOO_LARGE",
-    8: "FA_ERR_LAUNCH", 9: "FA_ERR_NO_MEMORY",
+    8: "FA_ERR_LAUNCH",
 }
 
 _lib = None

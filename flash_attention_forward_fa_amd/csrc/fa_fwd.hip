@@ -32,9 +32,7 @@
 #include <math.h>
 #include <stdint.h>
 
-#include <map>
-#include <mutex>
-#include <utility>
+#include <algorithm>
 
 #include "fa.h"
 
@@ -82,20 +80,12 @@ constexpr float kLazy = 8.0f;
 
 // Kernel modes. The plain kernel (kPlain) runs the bf16-P product and marks
 // the rows that need the compensated product by writing kRowFlag into their L
-// (their O is not written) and queueing their query tile; the rescue kernel
-// then recomputes those rows compensated. The compensated kernel (kAll)
+// (their O is not written); the rescue kernel then finds those rows and
+// recomputes them compensated. The compensated kernel (kAll)
 // computes every row of its tiles: the tiles with short rows, or all tiles
 // when an additive mask is given.
 constexpr int kPlain = 0, kAll = 1;
 constexpr uint32_t kRowFlag = 0x7FC0FA00u;  // a quiet NaN; never a valid L
-
-// Work queue of query tiles for the rescue kernel (device memory, int words):
-// two counter sets, [0..1] and [2..3] (number of queued tiles, next tile to
-// take), used by alternate calls on a stream, then the tile ids
-// (bh * n_qtiles + query tile) from word 4. A call's rescue launch zeroes the
-// other set, which the next call uses; no workgroup has to wait for the others
-// to finish, and an empty queue costs one load per workgroup.
-constexpr int kQueueHeader = 4;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -115,17 +105,7 @@ struct FwdArgs {
   int causal_off;  // max(kl - ql, 0)
   float c;         // |scale| * log2(e), at least FLT_MIN
   uint32_t q_sign; // 0x80008000 flips the sign of both bf16 halves (scale < 0)
-  int* qcount;     // this call's counter set of the rescue work queue
-  int* qother;     // the other counter set (zeroed by this call's rescue launch)
-  int* qitems;     // queued tile ids
-  int qcap;        // capacity of qitems
 };
-
-// Queue a query tile for the rescue kernel (one lane).
-__device__ __forceinline__ void queue_tile(const FwdArgs& a, int id) {
-  const int slot = atomicAdd(a.qcount, 1);
-  if (slot < a.qcap) a.qitems[slot] = id;
-}
 
 __device__ __forceinline__ float swap32(float x, bool take_max) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -318,8 +298,6 @@ __attribute__((amdgpu_waves_per_eu(MODE == kPlain ? Cfg<D>::WPE : 2))) void fa_f
   float* lrow_base = a.l + (int64_t)bh * ql;
 
   const bool compute = wave_active;
-  bool queue_me = false;  // kPlain: some row of this workgroup goes to the rescue kernel
-  const int tile_id = bh * a.n_qtiles + qtile;
 
   int koff[CopyShape<D, BN, NT>::ROUNDS], voff[CopyShape<D, BN, NT>::ROUNDS];
   copy_offsets<D, BN, NT, true>(tid, koff);
@@ -623,7 +601,6 @@ __attribute__((amdgpu_waves_per_eu(MODE == kPlain ? Cfg<D>::WPE : 2))) void fa_f
       omax = group_max(omax);
       const bool need = row_ok && l_tot > 0.0f && omax >= kRecheckO * l_tot;
       if (need && grp == 0) lrow_base[qrow] = __uint_as_float(kRowFlag);
-      queue_me |= need;
       write = row_ok && !need;
     }
     if (write) {
@@ -641,16 +618,15 @@ __attribute__((amdgpu_waves_per_eu(MODE == kPlain ? Cfg<D>::WPE : 2))) void fa_f
         lrow_base[qrow] = empty ? -INFINITY : (m_use[qb] + __builtin_amdgcn_logf(l_tot)) * kLn2;
     }
   }
-  if (MODE == kPlain && __syncthreads_or(queue_me) && tid == 0) queue_tile(a, tile_id);
   wait_vmem();  // no LDS copy may still be in flight when the workgroup ends
 #endif
 }
 
-// ---- rescue kernel: compensated recomputation of the queued query tiles ----
-// A persistent grid takes queued query tiles (the rows of one workgroup of the
-// plain kernel) one at a time and recomputes their flagged rows with the
-// compensated P.V product (P as a bf16 high part plus a bf16 remainder), in
-// passes of PR rows, skipping passes without a flagged row. In a pass the four
+// ---- rescue kernel: compensated recomputation of the flagged rows ----
+// A persistent grid reads the markers the plain kernel left in L, query tile
+// by query tile (the rows of one plain workgroup), and recomputes the flagged
+// rows with the compensated P.V product (P as a bf16 high part plus a bf16
+// remainder), in passes of PR rows, skipping passes without a flagged row. In a pass the four
 // waves split every 64-key tile four ways (16 keys each), so the pass walks
 // the key range four times faster than one wave would; each wave keeps its own
 // online-softmax state (max, row sum, O) over its keys, and the four partial
@@ -674,7 +650,7 @@ __global__ __launch_bounds__(kThreads) void fa_rescue_kernel(FwdArgs a) {
   constexpr int NST = RescueCfg<D>::STAGES;
   constexpr int BN = kRescueBN;
   constexpr int PR = 16 * QB;       // rows per pass
-  constexpr int BM = block_m<D>();  // rows per queued tile
+  constexpr int BM = block_m<D>();  // rows per query tile
   constexpr int NPASS = BM / PR;
   constexpr int NDS = D / 32;
   constexpr int NDB = D / 16;
@@ -686,8 +662,8 @@ __global__ __launch_bounds__(kThreads) void fa_rescue_kernel(FwdArgs a) {
   // K/V stages; after a pass the same memory holds the waves' partial O
   __shared__ __attribute__((aligned(1024))) uint16_t stage[NST][2][TILE];
   __shared__ float red_ml[2 * 4 * PR];  // the waves' partial max and row sum
-  __shared__ int item_sh;
-  __shared__ unsigned pass_sh;
+  constexpr int SCAN = 8;  // query tiles whose markers a workgroup reads in one batch
+  __shared__ unsigned pass_sh[SCAN];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
@@ -695,39 +671,54 @@ __global__ __launch_bounds__(kThreads) void fa_rescue_kernel(FwdArgs a) {
   const int c16 = lane & 15;
   const int grp = lane >> 4;
   const int ql = a.ql, kl = a.kl, off = a.causal_off;
-  const int n_items = min(a.qcount[0], a.qcap);
-  if (blockIdx.x == 0 && tid == 0) {  // empty the next call's counter set
-    a.qother[0] = 0;
-    a.qother[1] = 0;
-  }
-  if ((int)blockIdx.x >= n_items) return;  // no work item could reach this workgroup
+  // The plain launch's query tiles, heaviest first (as it ran them): tile t is
+  // query tile qt_base + qt_count - 1 - t / BH of head t % BH. Workgroup g
+  // takes tiles g, g + G, g + 2G, ... (G workgroups), SCAN at a time.
+  const int BH = a.B * a.H;
+  const int n_tiles = BH * a.qt_count;
+  const int G = gridDim.x;
+  auto tile_of = [&](int t, int& bh, int& q0) {
+    bh = t % BH;
+    q0 = (a.qt_base + a.qt_count - 1 - t / BH) * BM;
+  };
 
   int koff[ROUNDS], voff[ROUNDS];
   copy_offsets<D, BN, kThreads, true>(tid, koff);
   copy_offsets<D, BN, kThreads, false>(tid, voff);
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-  for (;;) {
-    if (tid == 0) {
-      item_sh = atomicAdd(a.qcount + 1, 1);
-      pass_sh = 0;
+  for (int base = blockIdx.x; base < n_tiles; base += SCAN * G) {
+    // which passes of the SCAN tiles hold a flagged row (thread tid reads the
+    // marker of row tid of each tile; the loads are issued together)
+    bool flg[SCAN];
+#pragma unroll
+    for (int k = 0; k < SCAN; ++k) {
+      const int t = base + k * G;
+      flg[k] = false;
+      if (t < n_tiles && tid < BM) {
+        int bh, q0;
+        tile_of(t, bh, q0);
+        if (q0 + tid < ql)
+          flg[k] = __float_as_uint(a.l[(int64_t)bh * ql + q0 + tid]) == kRowFlag;
+      }
     }
+    if (tid < SCAN) pass_sh[tid] = 0;
     __syncthreads();
-    const int it = __builtin_amdgcn_readfirstlane(item_sh);
-    if (it >= n_items) break;
-    const int id = a.qitems[it];
-    const int bh = id / a.n_qtiles, q0 = (id % a.n_qtiles) * BM;
+#pragma unroll
+    for (int k = 0; k < SCAN; ++k)
+      if (flg[k]) atomicOr(&pass_sh[k], 1u << (tid / PR));
+    __syncthreads();
+
+  for (int k = 0; k < SCAN; ++k) {
+    const unsigned passes = __builtin_amdgcn_readfirstlane(pass_sh[k]);
+    if (passes == 0) continue;
+    int bh, q0;
+    tile_of(base + k * G, bh, q0);
     const int b = bh / a.H, h = bh % a.H, g = h / a.group;
     const int64_t kv_off = (int64_t)(b * a.Hkv + g) * kl * D;
     const uint16_t* kp = a.k + kv_off;
     const uint16_t* vp = a.v + kv_off;
     float* lrow = a.l + (int64_t)bh * ql;
-
-    // which passes hold a flagged row
-    if (tid < BM && q0 + tid < ql && __float_as_uint(lrow[q0 + tid]) == kRowFlag)
-      atomicOr(&pass_sh, 1u << (tid / PR));
-    __syncthreads();
-    const unsigned passes = __builtin_amdgcn_readfirstlane(pass_sh);
 
     for (int ps = 0; ps < NPASS; ++ps) {
       if (!((passes >> ps) & 1u)) continue;
@@ -933,7 +924,8 @@ __global__ __launch_bounds__(kThreads) void fa_rescue_kernel(FwdArgs a) {
       }
       __syncthreads();  // red_ml is reused by the next pass
     }
-    __syncthreads();  // item_sh and pass_sh are rewritten for the next tile
+  }
+    __syncthreads();  // pass_sh is rewritten for the next tiles
   }
 
 #endif
@@ -950,8 +942,8 @@ hipError_t launch(const FwdArgs& a, unsigned grid, hipStream_t stream) {
 // compensated launch over the tiles with short rows (the first ones), the plain
 // launch over the others, then the rescue launch for the rows the plain launch
 // flagged (one stream, so in order). The rescue grid is persistent: a few
-// workgroups per compute unit, each taking queued tiles until the queue is
-// drained.
+// workgroups per compute unit, each reading the row markers of its share of
+// the plain launch's tiles.
 template <int D, bool CAUSAL>
 hipError_t dispatch_c(FwdArgs a, bool has_mask, int n_short, hipStream_t stream) {
   const unsigned bh = (unsigned)(a.B * a.H);
@@ -988,51 +980,6 @@ hipError_t dispatch_d(const FwdArgs& a, bool causal, bool has_mask, int n_short,
 }
 
 bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
-
-// One rescue work queue per (device, stream), allocated on first use (zeroed,
-// synchronously) and replaced by a larger one when a bigger problem arrives;
-// kept until the process ends. Calls on one stream run in order, so they can
-// share it; calls on different streams get different queues. Each call that
-// launches the rescue kernel takes the next counter set (set_args).
-struct RescueQueue {
-  int* ptr = nullptr;
-  int64_t cap = 0;
-  int parity = 0;
-};
-
-hipError_t rescue_queue(hipStream_t stream, int64_t n_ids, FwdArgs* a) {
-  static std::mutex mu;
-  static std::map<std::pair<int, hipStream_t>, RescueQueue> queues;
-  int dev = 0;
-  hipError_t err = hipGetDevice(&dev);
-  if (err != hipSuccess) return err;
-  std::lock_guard<std::mutex> lock(mu);
-  RescueQueue& rq = queues[{dev, stream}];
-  if (!rq.ptr || rq.cap < n_ids) {
-    if (rq.ptr) {
-      // the old queue may still be in use by work enqueued on this stream
-      if ((err = hipStreamSynchronize(stream)) != hipSuccess) return err;
-      (void)hipFree(rq.ptr);
-      rq = RescueQueue{};
-    }
-    const int64_t cap = std::max<int64_t>(n_ids, 1024);
-    const size_t bytes = (size_t)(kQueueHeader + cap) * sizeof(int);
-    int* q = nullptr;
-    if ((err = hipMalloc(&q, bytes)) != hipSuccess) return err;
-    if ((err = hipMemset(q, 0, bytes)) != hipSuccess) {
-      (void)hipFree(q);
-      return err;
-    }
-    rq.ptr = q;
-    rq.cap = cap;
-  }
-  a->qcount = rq.ptr + 2 * rq.parity;
-  a->qother = rq.ptr + 2 * (1 - rq.parity);
-  a->qitems = rq.ptr + kQueueHeader;
-  a->qcap = (int)std::min<int64_t>(rq.cap, 0x7fffffff);
-  rq.parity ^= 1;
-  return hipSuccess;
-}
 
 }  // namespace
 
@@ -1077,8 +1024,6 @@ extern "C" int fa_train_fwd(const void* q, const void* k, const void* v, const f
   // produces round to 0 in f32, so the weights are the same uniform ones).
   a.c = fmaxf(fabsf(scale) * kLog2e, FLT_MIN);
   a.q_sign = signbit(scale) ? 0x80008000u : 0u;
-  a.qcount = a.qother = a.qitems = nullptr;
-  a.qcap = 0;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   // query tiles whose first row may see fewer than kPreciseKeys keys
@@ -1087,18 +1032,9 @@ extern "C" int fa_train_fwd(const void* q, const void* k, const void* v, const f
     n_short = n_qtiles;
   else if (causal && a.causal_off + 1 < kPreciseKeys)
     n_short = std::min<int64_t>(n_qtiles, (kPreciseKeys - 1 - a.causal_off + bm - 1) / bm);
-  const bool plain = !mask && n_short < n_qtiles;  // plain and rescue launches follow
-  if (plain) {
-    const hipError_t qerr = rescue_queue(s, (n_qtiles - n_short) * batch * n_heads, &a);
-    if (qerr != hipSuccess) return qerr == hipErrorOutOfMemory ? FA_ERR_NO_MEMORY : FA_ERR_LAUNCH;
-  }
   hipError_t err =
       head_dim == 64 ? dispatch_d<64>(a, causal != 0, mask != nullptr, (int)n_short, s)
                      : dispatch_d<256>(a, causal != 0, mask != nullptr, (int)n_short, s);
-  if (err != hipSuccess && plain) {
-    // the rescue launch did not zero the next counter set: clear both
-    (void)hipMemsetAsync(std::min(a.qcount, a.qother), 0, kQueueHeader * sizeof(int), s);
-  }
   return err == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
@@ -1113,7 +1049,6 @@ extern "C" const char* fa_status_string(int status) {
     case FA_ERR_ALIGNMENT: return "misaligned tensor (q, k, v, O need 16 bytes; mask, L 4 bytes)";
     case FA_ERR_TOO_LARGE: return "problem too large for the kernel's grid or index range";
     case FA_ERR_LAUNCH: return "HIP kernel launch failed";
-    case FA_ERR_NO_MEMORY: return "could not allocate the rescue work queue";
     default: return "unknown status";
   }
 }

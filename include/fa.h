@@ -16,11 +16,8 @@
  *     O[b,h,i,:] = sum_j exp(s_j - L[b,h,i]) * v[b,g,j,:]        (0 if none)
  *
  * All tensors are contiguous row-major, in device memory owned by the caller.
- * Work is enqueued on `stream` and the call returns. The library owns one
- * small work queue per (device, stream) for the rows it recomputes with the
- * compensated product (4 bytes per 16 or 32 query rows, allocated on the first
- * call that needs it and kept until the process ends); only that allocation,
- * or its replacement by a larger one, synchronises the stream.
+ * The library allocates nothing, keeps no global mutable state and never
+ * synchronises: work is enqueued on `stream` and the call returns.
  */
 #ifndef FA_MI355X_FA_H
 #define FA_MI355X_FA_H
@@ -39,8 +36,7 @@ enum fa_status {
     FA_ERR_SCALE = 5,          /* scale is NaN or infinite                              */
     FA_ERR_ALIGNMENT = 6,      /* q, k, v or O not 16-byte aligned; mask or L not 4-byte */
     FA_ERR_TOO_LARGE = 7,      /* a grid or index would overflow the kernel's limits    */
-    FA_ERR_LAUNCH = 8,         /* the HIP launch failed (hipGetLastError)               */
-    FA_ERR_NO_MEMORY = 9       /* the work queue could not be allocated                 */
+    FA_ERR_LAUNCH = 8          /* the HIP launch failed (hipGetLastError)               */
 };
 
 /*
@@ -66,8 +62,9 @@ enum fa_status {
  * Arguments are validated on the host before any HIP call; on error nothing is
  * enqueued and a nonzero fa_status is returned. batch*ql == 0 is a successful
  * no-op; kl == 0 gives every row O = 0 and L = -inf. Input and output buffers
- * must not overlap. The call never aborts; it synchronises only when it
- * (re)allocates the work queue of its (device, stream).
+ * must not overlap. The call never aborts and never synchronises. (Internally
+ * L also carries a marker for rows a second launch recomputes; only the final
+ * values are visible once the stream has completed.)
  */
 int fa_train_fwd(const void *q, const void *k, const void *v, const float *mask, int batch,
                  int n_heads, int n_kv_heads, int ql, int kl, int head_dim, float scale,

@@ -43,15 +43,23 @@ def test_all_variants_present(isa):
 
 
 def test_no_mfma_under_exec_mask(isa):
+    # A masked region opens with s_*_saveexec_b64 sX or s_mov_b64 sX, exec
+    # (the old EXEC saved in sX) and closes with s_or_b64 exec, exec, sX. Regions may be closed by
+    # restoring an outer saved mask, which also closes every region opened
+    # after it, so the open regions are kept as a stack of saved registers.
     for name, lines in isa.items():
-        depth = 0
+        open_regions = []
         for line in lines:
-            if re.search(r"s_(and|andn2|or)_saveexec_b64", line):
-                depth += 1
-            elif re.search(r"s_or_b64 exec, exec", line):
-                depth = max(0, depth - 1)
+            m = (re.search(r"s_(?:and|andn2|or)_saveexec_b64 (s\[\d+:\d+\])", line)
+                 or re.search(r"s_mov_b64 (s\[\d+:\d+\]), exec$", line.strip()))
+            c = re.search(r"s_or_b64 exec, exec, (s\[\d+:\d+\])", line)
+            if m:
+                open_regions.append(m.group(1))
+            elif c:
+                if c.group(1) in open_regions:
+                    del open_regions[open_regions.index(c.group(1)):]
             elif "v_mfma" in line:
-                assert depth == 0, f"{name}: MFMA inside an EXEC-masked region: {line.strip()}"
+                assert not open_regions, f"{name}: MFMA inside an EXEC-masked region: {line.strip()}"
 
 
 def test_key_loop_does_not_spill(isa):
