@@ -78,13 +78,14 @@ constexpr float kRecheckO = 1.0f;
 // than this (base-2 units): P <= 2^kLazy and O is rarely rescaled.
 constexpr float kLazy = 8.0f;
 
-// Kernel modes. The plain kernel (kPlain) runs the bf16-P product and marks
-// the rows that need the compensated product by writing kRowFlag into their L
+// Kernel modes. In the mixed kernel (kMixed) the query tiles below
+// n_precise (those with a row that may see fewer than kPreciseKeys keys) run
+// the compensated P.V product; the others run the bf16-P product and mark the
+// rows that need the compensated product by writing kRowFlag into their L
 // (their O is not written); the rescue kernel then finds those rows and
-// recomputes them compensated. The compensated kernel (kAll)
-// computes every row of its tiles: the tiles with short rows, or all tiles
-// when an additive mask is given.
-constexpr int kPlain = 0, kAll = 1;
+// recomputes them compensated. The compensated kernel (kAll) computes every
+// row of every tile compensated (the masked forward).
+constexpr int kMixed = 0, kAll = 1;
 constexpr uint32_t kRowFlag = 0x7FC0FA00u;  // a quiet NaN; never a valid L
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -102,6 +103,7 @@ struct FwdArgs {
   int n_qtiles;    // ceil(ql / rows per workgroup)
   int qt_base;     // this launch computes query tiles [qt_base, qt_base + qt_count)
   int qt_count;
+  int n_precise;   // kMixed: query tiles below this run compensated
   int causal_off;  // max(kl - ql, 0)
   float c;         // |scale| * log2(e), at least FLT_MIN
   uint32_t q_sign; // 0x80008000 flips the sign of both bf16 halves (scale < 0)
@@ -226,12 +228,13 @@ __device__ __forceinline__ void wait_vmem() {
   __builtin_amdgcn_s_waitcnt(0x0F70);
 }
 
-template <int D, bool CAUSAL, bool HAS_MASK, int MODE>
-__global__ __launch_bounds__(64 * Cfg<D>::W)
-__attribute__((amdgpu_waves_per_eu(MODE == kPlain ? Cfg<D>::WPE : 2))) void fa_fwd_kernel(FwdArgs a) {
-  static_assert(MODE != kPlain || !HAS_MASK, "the masked forward always runs compensated");
-#if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
-  constexpr bool PRECISE = MODE != kPlain;
+// One query tile of one head: rows qtile * block_m .. of head bh. PRECISE
+// selects the compensated P.V product; without it, rows that need it are
+// marked in L instead of written.
+template <int D, bool CAUSAL, bool HAS_MASK, bool PRECISE>
+__device__ __forceinline__ void fwd_tile(const FwdArgs& a, int qtile, int bh, uint16_t* k0s,
+                                         uint16_t* v0s, uint16_t* k1s, uint16_t* v1s) {
+  static_assert(PRECISE || !HAS_MASK, "the masked forward always runs compensated");
   constexpr int BN = Cfg<D>::BN;
   constexpr int kQB = Cfg<D>::QB;
   constexpr int kRowsPerWave = 16 * kQB;
@@ -242,12 +245,13 @@ __attribute__((amdgpu_waves_per_eu(MODE == kPlain ? Cfg<D>::WPE : 2))) void fa_f
   constexpr int NDS = D / 32;   // 32-dim steps of Q.K
   constexpr int TILE = BN * D;  // elements per K or V tile
   constexpr int NT = 64 * Cfg<D>::W;  // threads per workgroup
-  __shared__ __attribute__((aligned(1024))) uint16_t k0s[TILE];
-  __shared__ __attribute__((aligned(1024))) uint16_t v0s[TILE];
-  __shared__ __attribute__((aligned(1024))) uint16_t k1s[TILE];
-  __shared__ __attribute__((aligned(1024))) uint16_t v1s[TILE];
+  static_assert(TILE > 0, "empty tile");
 
-  const int tid = threadIdx.x;
+  // (the opaque copy keeps the compiler from hoisting the thread-index
+  // arithmetic of both tile variants of the mixed kernel above their branch,
+  // where it would stay live, and spill, across both)
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
   // The wave index is made provably wave-uniform so that every condition
   // derived from it (tile skipping, masking, row selection) compiles to a
   // scalar branch: an MFMA left inside an EXEC-masked region still accumulates
@@ -257,28 +261,6 @@ __attribute__((amdgpu_waves_per_eu(MODE == kPlain ? Cfg<D>::WPE : 2))) void fa_f
   const int c16 = lane & 15;  // query column within a 16-row block / A-operand row
   const int grp = lane >> 4;  // 16-lane group
 
-  // ---- work item ----
-  // Workgroups are handed to the 8 XCDs round-robin (bid mod 8). When B*H is a
-  // multiple of 8, XCD x owns the heads [x*per, (x+1)*per) (so one KV group
-  // stays within one XCD's L2), takes them in groups of 8 (when per is a
-  // multiple of 8; fewer K/V in flight per L2) and walks each group's query
-  // tiles heaviest (most keys) first, so the cheap tiles fill the tail.
-  // (Groups of 1, 2 or 4 heads were measured slower, 8 faster than all.)
-  const int BH = a.B * a.H;
-  const int bid = blockIdx.x;
-  int qt_rev, bh;
-  if ((BH & 7) == 0) {
-    const int xcd = bid & 7, tl = bid >> 3, per = BH >> 3;
-    const int gh = (per & 7) == 0 ? 8 : per;  // heads per group
-    const int gsz = gh * a.qt_count;          // workgroups per group
-    const int gi = tl / gsz, r = tl % gsz;
-    qt_rev = r / gh;
-    bh = xcd * per + gi * gh + r % gh;
-  } else {
-    qt_rev = bid / BH;
-    bh = bid % BH;
-  }
-  const int qtile = a.qt_base + a.qt_count - 1 - qt_rev;
   const int b = bh / a.H, h = bh % a.H;
   const int g = h / a.group;
   const int ql = a.ql, kl = a.kl, off = a.causal_off;
@@ -591,7 +573,7 @@ __attribute__((amdgpu_waves_per_eu(MODE == kPlain ? Cfg<D>::WPE : 2))) void fa_f
     const bool row_ok = compute && qrow < ql;
     const float l_tot = group_sum(l_run[qb]);
     bool write = row_ok;
-    if (MODE == kPlain) {
+    if (!PRECISE) {
       // rows whose plain result is not accurate enough go to the compensated kernel
       float omax = 0.0f;
 #pragma unroll
@@ -619,6 +601,50 @@ __attribute__((amdgpu_waves_per_eu(MODE == kPlain ? Cfg<D>::WPE : 2))) void fa_f
     }
   }
   wait_vmem();  // no LDS copy may still be in flight when the workgroup ends
+}
+
+template <int D, bool CAUSAL, bool HAS_MASK, int MODE>
+__global__ __launch_bounds__(64 * Cfg<D>::W)
+__attribute__((amdgpu_waves_per_eu(MODE == kMixed ? Cfg<D>::WPE : 2))) void fa_fwd_kernel(FwdArgs a) {
+  static_assert(MODE != kMixed || !HAS_MASK, "the masked forward always runs compensated");
+#if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
+  constexpr int TILE = Cfg<D>::BN * D;
+  __shared__ __attribute__((aligned(1024))) uint16_t k0s[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t v0s[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t k1s[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t v1s[TILE];
+
+  // ---- work item ----
+  // Workgroups are handed to the 8 XCDs round-robin (bid mod 8). When B*H is a
+  // multiple of 8, XCD x owns the heads [x*per, (x+1)*per) (so one KV group
+  // stays within one XCD's L2), takes them in groups of 8 (when per is a
+  // multiple of 8; fewer K/V in flight per L2) and walks each group's query
+  // tiles heaviest (most keys) first, so the cheap tiles fill the tail.
+  // (Groups of 1, 2 or 4 heads were measured slower, 8 faster than all.)
+  const int BH = a.B * a.H;
+  const int bid = blockIdx.x;
+  int qt_rev, bh;
+  if ((BH & 7) == 0) {
+    const int xcd = bid & 7, tl = bid >> 3, per = BH >> 3;
+    const int gh = (per & 7) == 0 ? 8 : per;  // heads per group
+    const int gsz = gh * a.qt_count;          // workgroups per group
+    const int gi = tl / gsz, r = tl % gsz;
+    qt_rev = r / gh;
+    bh = xcd * per + gi * gh + r % gh;
+  } else {
+    qt_rev = bid / BH;
+    bh = bid % BH;
+  }
+  const int qtile = a.qt_base + a.qt_count - 1 - qt_rev;
+  if constexpr (MODE == kMixed) {
+    // the compensated tiles are the lightest, so they run last and fill the tail
+    if (qtile < a.n_precise)
+      fwd_tile<D, CAUSAL, false, true>(a, qtile, bh, k0s, v0s, k1s, v1s);
+    else
+      fwd_tile<D, CAUSAL, false, false>(a, qtile, bh, k0s, v0s, k1s, v1s);
+  } else {
+    fwd_tile<D, CAUSAL, HAS_MASK, true>(a, qtile, bh, k0s, v0s, k1s, v1s);
+  }
 #endif
 }
 
@@ -938,38 +964,31 @@ hipError_t launch(const FwdArgs& a, unsigned grid, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Masked: one compensated launch over all query tiles. Unmasked: the
-// compensated launch over the tiles with short rows (the first ones), the plain
-// launch over the others, then the rescue launch for the rows the plain launch
-// flagged (one stream, so in order). The rescue grid is persistent: a few
-// workgroups per compute unit, each reading the row markers of its share of
-// the plain launch's tiles.
+// Masked: one compensated launch over all query tiles. Unmasked: the mixed
+// launch over all tiles (compensated for the tiles with short rows, the first
+// n_short ones; plain for the others), then, when there are plain tiles, the
+// rescue launch for the rows they flagged (one stream, so in order). The
+// rescue grid is persistent: a few workgroups per compute unit, each reading
+// the row markers of its share of the plain tiles.
 template <int D, bool CAUSAL>
 hipError_t dispatch_c(FwdArgs a, bool has_mask, int n_short, hipStream_t stream) {
   const unsigned bh = (unsigned)(a.B * a.H);
   const int n_qt = a.n_qtiles;
+  a.qt_base = 0;
+  a.qt_count = n_qt;
   if (has_mask) {
-    a.qt_base = 0;
-    a.qt_count = n_qt;
+    a.n_precise = n_qt;
     return launch<D, CAUSAL, true, kAll>(a, bh * n_qt, stream);
   }
-  if (n_short > 0) {
-    a.qt_base = 0;
-    a.qt_count = n_short;
-    hipError_t e = launch<D, CAUSAL, false, kAll>(a, bh * n_short, stream);
-    if (e != hipSuccess) return e;
-  }
-  if (n_short < n_qt) {
-    a.qt_base = n_short;
-    a.qt_count = n_qt - n_short;
-    hipError_t e = launch<D, CAUSAL, false, kPlain>(a, bh * (n_qt - n_short), stream);
-    if (e != hipSuccess) return e;
-    const int64_t tiles = (int64_t)bh * (n_qt - n_short);
-    const unsigned rgrid = (unsigned)std::min<int64_t>(tiles, 256 * RescueCfg<D>::PER_CU);
-    hipLaunchKernelGGL((fa_rescue_kernel<D, CAUSAL>), dim3(rgrid), dim3(kThreads), 0, stream, a);
-    return hipGetLastError();
-  }
-  return hipSuccess;
+  a.n_precise = n_short;
+  hipError_t e = launch<D, CAUSAL, false, kMixed>(a, bh * n_qt, stream);
+  if (e != hipSuccess || n_short >= n_qt) return e;
+  a.qt_base = n_short;
+  a.qt_count = n_qt - n_short;
+  const int64_t tiles = (int64_t)bh * (n_qt - n_short);
+  const unsigned rgrid = (unsigned)std::min<int64_t>(tiles, 256 * RescueCfg<D>::PER_CU);
+  hipLaunchKernelGGL((fa_rescue_kernel<D, CAUSAL>), dim3(rgrid), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
 }
 
 template <int D>
