@@ -23,9 +23,8 @@
 //
 // Accuracy: P enters the bf16 MFMA rounded to bf16. Where that is not accurate
 // enough the product is compensated (a second MFMA with P's bf16 remainder):
-// for query tiles whose rows may see fewer than 128 keys (one compensated
-// launch), and for rows the plain launch finds with |O| >= 1, which a rescue
-// launch recomputes.
+// for query tiles whose rows may see fewer than 128 keys, and for rows whose
+// plain result has some |O| >= 1, which their workgroup computes again.
 #include <hip/hip_runtime.h>
 
 #include <float.h>
@@ -47,8 +46,6 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) void lds_void;
-
-constexpr int kThreads = 256;  // rescue kernel: 4 waves
 
 // Per head dim: W waves per workgroup, QB 16-row query blocks per wave and BN
 // keys per tile. Eight waves (two per SIMD) share each K/V tile copy, which
@@ -80,13 +77,11 @@ constexpr float kLazy = 8.0f;
 
 // Kernel modes. In the mixed kernel (kMixed) the query tiles below
 // n_precise (those with a row that may see fewer than kPreciseKeys keys) run
-// the compensated P.V product; the others run the bf16-P product and mark the
-// rows that need the compensated product by writing kRowFlag into their L
-// (their O is not written); the rescue kernel then finds those rows and
-// recomputes them compensated. The compensated kernel (kAll) computes every
-// row of every tile compensated (the masked forward).
+// the compensated P.V product; the others run the bf16-P product, and when
+// some of their rows need the compensated product the workgroup runs the tile
+// again, compensated, for those rows only. The compensated kernel (kAll)
+// computes every row of every tile compensated (the masked forward).
 constexpr int kMixed = 0, kAll = 1;
-constexpr uint32_t kRowFlag = 0x7FC0FA00u;  // a quiet NaN; never a valid L
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -229,12 +224,18 @@ __device__ __forceinline__ void wait_vmem() {
 }
 
 // One query tile of one head: rows qtile * block_m .. of head bh. PRECISE
-// selects the compensated P.V product; without it, rows that need it are
-// marked in L instead of written.
-template <int D, bool CAUSAL, bool HAS_MASK, bool PRECISE>
-__device__ __forceinline__ void fwd_tile(const FwdArgs& a, int qtile, int bh, uint16_t* k0s,
-                                         uint16_t* v0s, uint16_t* k1s, uint16_t* v1s) {
+// selects the compensated P.V product. Without it, a row whose result needs
+// that product is not written; its lane's redo[qb] is set instead, and the
+// return value tells the whole workgroup whether any of its rows needs it
+// (wg_flags: one int per wave). With REDO (and PRECISE), only the rows with
+// redo set are computed and written (waves without such a row only take part
+// in the tile copies).
+template <int D, bool CAUSAL, bool HAS_MASK, bool PRECISE, bool REDO>
+__device__ __forceinline__ bool fwd_tile(const FwdArgs& a, int qtile, int bh, uint16_t* k0s,
+                                         uint16_t* v0s, uint16_t* k1s, uint16_t* v1s,
+                                         bool (&redo)[Cfg<D>::QB], int* wg_flags) {
   static_assert(PRECISE || !HAS_MASK, "the masked forward always runs compensated");
+  static_assert(PRECISE || !REDO, "a redo runs compensated");
   constexpr int BN = Cfg<D>::BN;
   constexpr int kQB = Cfg<D>::QB;
   constexpr int kRowsPerWave = 16 * kQB;
@@ -279,7 +280,10 @@ __device__ __forceinline__ void fwd_tile(const FwdArgs& a, int qtile, int bh, ui
   const int wave_kend = CAUSAL ? min(kl, off + wave_last + 1) : kl;
   float* lrow_base = a.l + (int64_t)bh * ql;
 
-  const bool compute = wave_active;
+  bool wave_redo = false;
+#pragma unroll
+  for (int qb = 0; qb < kQB; ++qb) wave_redo |= redo[qb];
+  const bool compute = wave_active && (!REDO || __any(wave_redo));
 
   int koff[CopyShape<D, BN, NT>::ROUNDS], voff[CopyShape<D, BN, NT>::ROUNDS];
   copy_offsets<D, BN, NT, true>(tid, koff);
@@ -567,27 +571,46 @@ __device__ __forceinline__ void fwd_tile(const FwdArgs& a, int qtile, int bh, ui
   }
 
   // ---- epilogue: O = O_acc / l (+0 for an empty row), L = (m + log2 l) ln 2 ----
+  float l_tot[kQB];
+  bool write[kQB];
+  bool wg_any = false;
 #pragma unroll
   for (int qb = 0; qb < kQB; ++qb) {
     const int qrow = qw0 + 16 * qb + c16;
     const bool row_ok = compute && qrow < ql;
-    const float l_tot = group_sum(l_run[qb]);
-    bool write = row_ok;
+    l_tot[qb] = group_sum(l_run[qb]);
+    write[qb] = REDO ? row_ok && redo[qb] : row_ok;
     if (!PRECISE) {
-      // rows whose plain result is not accurate enough go to the compensated kernel
+      // rows whose plain result is not accurate enough are redone compensated
       float omax = 0.0f;
 #pragma unroll
       for (int d = 0; d < NDB; ++d)
 #pragma unroll
         for (int i = 0; i < 4; ++i) omax = __builtin_fmaxf(omax, __builtin_fabsf(oacc[d][qb][i]));
       omax = group_max(omax);
-      const bool need = row_ok && l_tot > 0.0f && omax >= kRecheckO * l_tot;
-      if (need && grp == 0) lrow_base[qrow] = __uint_as_float(kRowFlag);
-      write = row_ok && !need;
+      redo[qb] = row_ok && l_tot[qb] > 0.0f && omax >= kRecheckO * l_tot[qb];
+      write[qb] = row_ok && !redo[qb];
     }
-    if (write) {
-      const bool empty = !(l_tot > 0.0f);
-      const float inv = empty ? 0.0f : __builtin_amdgcn_rcpf(l_tot);
+  }
+  if (!PRECISE) {
+    // one flag per wave, then every wave reads all of them (every tile copy
+    // has landed here: the last key step waited for its own)
+    bool mine = false;
+#pragma unroll
+    for (int qb = 0; qb < kQB; ++qb) mine |= redo[qb];
+    const bool wave_any = __any(mine);
+    if (lane == 0) wg_flags[wave] = wave_any;
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < Cfg<D>::W; ++w) wg_any |= wg_flags[w] != 0;
+  }
+#pragma unroll
+  for (int qb = 0; qb < kQB; ++qb) {
+    const int qrow = qw0 + 16 * qb + c16;
+    if (write[qb]) {
+      const float lt = l_tot[qb];
+      const bool empty = !(lt > 0.0f);
+      const float inv = empty ? 0.0f : __builtin_amdgcn_rcpf(lt);
       uint16_t* orow = a.o + ((int64_t)bh * ql + qrow) * D + 4 * grp;
 #pragma unroll
       for (int d = 0; d < NDB; ++d) {
@@ -597,10 +620,13 @@ __device__ __forceinline__ void fwd_tile(const FwdArgs& a, int qtile, int bh, ui
         *reinterpret_cast<bf16x4*>(orow + 16 * d) = ov;
       }
       if (grp == 0)
-        lrow_base[qrow] = empty ? -INFINITY : (m_use[qb] + __builtin_amdgcn_logf(l_tot)) * kLn2;
+        lrow_base[qrow] = empty ? -INFINITY : (m_use[qb] + __builtin_amdgcn_logf(lt)) * kLn2;
     }
   }
-  wait_vmem();  // no LDS copy may still be in flight when the workgroup ends
+  // no LDS copy may still be in flight when the workgroup ends (waiting for
+  // the stores here too was measured faster for D=256 than leaving them)
+  wait_vmem();
+  return wg_any;
 }
 
 template <int D, bool CAUSAL, bool HAS_MASK, int MODE>
@@ -613,6 +639,7 @@ __attribute__((amdgpu_waves_per_eu(MODE == kMixed ? Cfg<D>::WPE : 2))) void fa_f
   __shared__ __attribute__((aligned(1024))) uint16_t v0s[TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t k1s[TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t v1s[TILE];
+  __shared__ int wg_flags[Cfg<D>::W];
 
   // ---- work item ----
   // Workgroups are handed to the 8 XCDs round-robin (bid mod 8). When B*H is a
@@ -636,324 +663,20 @@ __attribute__((amdgpu_waves_per_eu(MODE == kMixed ? Cfg<D>::WPE : 2))) void fa_f
     bh = bid % BH;
   }
   const int qtile = a.qt_base + a.qt_count - 1 - qt_rev;
+  bool redo[Cfg<D>::QB] = {};
   if constexpr (MODE == kMixed) {
     // the compensated tiles are the lightest, so they run last and fill the tail
-    if (qtile < a.n_precise)
-      fwd_tile<D, CAUSAL, false, true>(a, qtile, bh, k0s, v0s, k1s, v1s);
-    else
-      fwd_tile<D, CAUSAL, false, false>(a, qtile, bh, k0s, v0s, k1s, v1s);
+    if (qtile < a.n_precise) {
+      fwd_tile<D, CAUSAL, false, true, false>(a, qtile, bh, k0s, v0s, k1s, v1s, redo, wg_flags);
+    } else if (fwd_tile<D, CAUSAL, false, false, false>(a, qtile, bh, k0s, v0s, k1s, v1s, redo,
+                                                        wg_flags)) {
+      // (the plain pass's last barrier came after every wave's last LDS read,
+      // so the redo's copies may reuse the tile buffers)
+      fwd_tile<D, CAUSAL, false, true, true>(a, qtile, bh, k0s, v0s, k1s, v1s, redo, wg_flags);
+    }
   } else {
-    fwd_tile<D, CAUSAL, HAS_MASK, true>(a, qtile, bh, k0s, v0s, k1s, v1s);
+    fwd_tile<D, CAUSAL, HAS_MASK, true, false>(a, qtile, bh, k0s, v0s, k1s, v1s, redo, wg_flags);
   }
-#endif
-}
-
-// ---- rescue kernel: compensated recomputation of the flagged rows ----
-// A persistent grid reads the markers the plain kernel left in L, query tile
-// by query tile (the rows of one plain workgroup), and recomputes the flagged
-// rows with the compensated P.V product (P as a bf16 high part plus a bf16
-// remainder), in passes of PR rows, skipping passes without a flagged row. In a pass the four
-// waves split every 64-key tile four ways (16 keys each), so the pass walks
-// the key range four times faster than one wave would; each wave keeps its own
-// online-softmax state (max, row sum, O) over its keys, and the four partial
-// results are merged through LDS at the end of the pass. Only rows whose L
-// holds kRowFlag are written.
-constexpr int kRescueBN = 64;
-template <int D> struct RescueCfg;
-template <> struct RescueCfg<64> { static constexpr int QB = 4, STAGES = 4, PER_CU = 2; };
-template <> struct RescueCfg<256> { static constexpr int QB = 1, STAGES = 2, PER_CU = 1; };
-
-// s_waitcnt with vmcnt(N); expcnt and lgkmcnt left at their maxima
-template <int N> __device__ __forceinline__ void wait_vmem_le() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
-
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads) void fa_rescue_kernel(FwdArgs a) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  constexpr int QB = RescueCfg<D>::QB;  // 16-row blocks per pass
-  constexpr int NST = RescueCfg<D>::STAGES;
-  constexpr int BN = kRescueBN;
-  constexpr int PR = 16 * QB;       // rows per pass
-  constexpr int BM = block_m<D>();  // rows per query tile
-  constexpr int NPASS = BM / PR;
-  constexpr int NDS = D / 32;
-  constexpr int NDB = D / 16;
-  constexpr int TILE = BN * D;
-  constexpr int ROUNDS = CopyShape<D, BN, kThreads>::ROUNDS;
-  constexpr int LOADS_PER_TILE = 2 * ROUNDS;  // K and V copies per thread
-  static_assert(NPASS * PR == BM && BM <= kThreads, "passes must tile the query tile");
-  static_assert(4 * PR * D * 4 <= NST * 2 * TILE * 2, "merge buffer must fit the K/V stages");
-  // K/V stages; after a pass the same memory holds the waves' partial O
-  __shared__ __attribute__((aligned(1024))) uint16_t stage[NST][2][TILE];
-  __shared__ float red_ml[2 * 4 * PR];  // the waves' partial max and row sum
-  constexpr int SCAN = 8;  // query tiles whose markers a workgroup reads in one batch
-  __shared__ unsigned pass_sh[SCAN];
-
-  const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
-  const int lane = tid & 63;
-  const int c16 = lane & 15;
-  const int grp = lane >> 4;
-  const int ql = a.ql, kl = a.kl, off = a.causal_off;
-  // The plain launch's query tiles, heaviest first (as it ran them): tile t is
-  // query tile qt_base + qt_count - 1 - t / BH of head t % BH. Workgroup g
-  // takes tiles g, g + G, g + 2G, ... (G workgroups), SCAN at a time.
-  const int BH = a.B * a.H;
-  const int n_tiles = BH * a.qt_count;
-  const int G = gridDim.x;
-  auto tile_of = [&](int t, int& bh, int& q0) {
-    bh = t % BH;
-    q0 = (a.qt_base + a.qt_count - 1 - t / BH) * BM;
-  };
-
-  int koff[ROUNDS], voff[ROUNDS];
-  copy_offsets<D, BN, kThreads, true>(tid, koff);
-  copy_offsets<D, BN, kThreads, false>(tid, voff);
-  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-
-  for (int base = blockIdx.x; base < n_tiles; base += SCAN * G) {
-    // which passes of the SCAN tiles hold a flagged row (thread tid reads the
-    // marker of row tid of each tile; the loads are issued together)
-    bool flg[SCAN];
-#pragma unroll
-    for (int k = 0; k < SCAN; ++k) {
-      const int t = base + k * G;
-      flg[k] = false;
-      if (t < n_tiles && tid < BM) {
-        int bh, q0;
-        tile_of(t, bh, q0);
-        if (q0 + tid < ql)
-          flg[k] = __float_as_uint(a.l[(int64_t)bh * ql + q0 + tid]) == kRowFlag;
-      }
-    }
-    if (tid < SCAN) pass_sh[tid] = 0;
-    __syncthreads();
-#pragma unroll
-    for (int k = 0; k < SCAN; ++k)
-      if (flg[k]) atomicOr(&pass_sh[k], 1u << (tid / PR));
-    __syncthreads();
-
-  for (int k = 0; k < SCAN; ++k) {
-    const unsigned passes = __builtin_amdgcn_readfirstlane(pass_sh[k]);
-    if (passes == 0) continue;
-    int bh, q0;
-    tile_of(base + k * G, bh, q0);
-    const int b = bh / a.H, h = bh % a.H, g = h / a.group;
-    const int64_t kv_off = (int64_t)(b * a.Hkv + g) * kl * D;
-    const uint16_t* kp = a.k + kv_off;
-    const uint16_t* vp = a.v + kv_off;
-    float* lrow = a.l + (int64_t)bh * ql;
-
-    for (int ps = 0; ps < NPASS; ++ps) {
-      if (!((passes >> ps) & 1u)) continue;
-      const int r0 = q0 + ps * PR;
-      const int kend = CAUSAL ? min(kl, off + min(r0 + PR, ql)) : kl;
-      const int n_t = (kend + BN - 1) / BN;
-
-#pragma unroll
-      for (int st = 0; st < NST - 1; ++st)
-        if (st < n_t) {
-          issue_tile<D, BN, kThreads, true>(kp, st * BN, kl, stage[st][0], tid, 64 * wave, koff);
-          issue_tile<D, BN, kThreads, false>(vp, st * BN, kl, stage[st][1], tid, 64 * wave, voff);
-        }
-
-      bf16x8 qop[QB][NDS];
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        const int qrow = min(r0 + 16 * qb + c16, ql - 1);
-        const uint16_t* qp = a.q + ((int64_t)bh * ql + qrow) * D + 8 * grp;
-#pragma unroll
-        for (int s = 0; s < NDS; ++s) {
-          u32x4 raw = *reinterpret_cast<const u32x4*>(qp + 32 * s);
-          raw ^= a.q_sign;
-          qop[qb][s] = __builtin_bit_cast(bf16x8, raw);
-        }
-      }
-      float m_use[QB], l_run[QB];
-      f32x4 oacc[NDB][QB];
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        m_use[qb] = -FLT_MAX / 2.0f;
-        l_run[qb] = 0.0f;
-#pragma unroll
-        for (int d = 0; d < NDB; ++d) oacc[d][qb] = f32x4{};
-      }
-
-      for (int t = 0; t < n_t; ++t) {
-        if (t + NST - 2 < n_t)
-          wait_vmem_le<(NST - 2) * LOADS_PER_TILE>();
-        else
-          wait_vmem();
-        __syncthreads();
-        if (t + NST - 1 < n_t) {
-          const int st = (t + NST - 1) % NST;
-          issue_tile<D, BN, kThreads, true>(kp, (t + NST - 1) * BN, kl, stage[st][0], tid,
-                                            64 * wave, koff);
-          issue_tile<D, BN, kThreads, false>(vp, (t + NST - 1) * BN, kl, stage[st][1], tid,
-                                             64 * wave, voff);
-        }
-        const int kbase = t * BN + 16 * wave;  // this wave's 16 keys
-        if (kbase >= kend) continue;
-        const uint16_t* ks = stage[t % NST][0];
-        const uint16_t* vs = stage[t % NST][1];
-        const int r = 16 * wave + c16;
-
-        // S^T (16 keys x 16 rows per block): lane holds keys kbase + 4grp + i
-        f32x4 sacc[QB];
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) sacc[qb] = f32x4{};
-#pragma unroll
-        for (int s = 0; s < NDS; ++s) {
-          const bf16x8 kop =
-              *reinterpret_cast<const bf16x8*>(ks + r * D + 8 * ((4 * s + grp) ^ kswz<D>(r)));
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb)
-            sacc[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop[qb][s], sacc[qb], 0, 0, 0);
-        }
-        if (kbase + 16 > kl || (CAUSAL && kbase + 15 > off + r0)) {
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb) {
-            const int qabs = off + r0 + 16 * qb + c16;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int key = kbase + 4 * grp + i;
-              if (key >= kl || (CAUSAL && key > qabs)) sacc[qb][i] = -INFINITY;
-            }
-          }
-        }
-        // online softmax over this wave's keys (base 2, lazy raise, per row)
-        float m_new[QB];
-        bool raise = false;
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          const float mx = __builtin_fmaxf(__builtin_fmaxf(sacc[qb][0], sacc[qb][1]),
-                                           __builtin_fmaxf(sacc[qb][2], sacc[qb][3]));
-          const float tmax = group_max(mx) * a.c;
-          const bool rs = tmax > m_use[qb] + kLazy;
-          m_new[qb] = rs ? tmax : m_use[qb];
-          raise |= rs;
-        }
-        if (__any(raise)) {
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb) {
-            const float alpha = __builtin_amdgcn_exp2f(m_use[qb] - m_new[qb]);
-            m_use[qb] = m_new[qb];
-            l_run[qb] *= alpha;
-#pragma unroll
-            for (int d = 0; d < NDB; ++d) oacc[d][qb] *= alpha;
-          }
-        }
-        s16x4 phi[QB], plo[QB];
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          bf16x4 hi, lo;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[qb][i], a.c, -m_use[qb]));
-            hi[i] = (__bf16)p;
-            lo[i] = (__bf16)(p - (float)hi[i]);
-          }
-          float ls = l_run[qb];
-          ls = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{hi[0], hi[1]}, ones, ls, false);
-          ls = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{hi[2], hi[3]}, ones, ls, false);
-          ls = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{lo[0], lo[1]}, ones, ls, false);
-          ls = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{lo[2], lo[3]}, ones, ls, false);
-          l_run[qb] = ls;
-          phi[qb] = __builtin_bit_cast(s16x4, hi);
-          plo[qb] = __builtin_bit_cast(s16x4, lo);
-        }
-        // O^T += V^T P^T: V^T operand = dims 16d + c16, keys kbase + 4grp + (0..3)
-#pragma unroll
-        for (int d = 0; d < NDB; ++d) {
-          const int vr = 16 * wave + 4 * grp + (c16 >> 2);
-          const int col = 16 * d + 4 * (c16 & 3);
-          const s16x4 vop = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_s16x4*)(vs + vr * D + 8 * ((col >> 3) ^ vswz<D>(vr)) + (col & 7)));
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb) {
-            oacc[d][qb] =
-                __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vop, phi[qb], oacc[d][qb], 0, 0, 0);
-            oacc[d][qb] =
-                __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vop, plo[qb], oacc[d][qb], 0, 0, 0);
-          }
-        }
-      }
-
-      // ---- merge the four waves' partial results ----
-      wait_vmem();
-      __syncthreads();  // every wave is done with the K/V stages
-      float* red_o = reinterpret_cast<float*>(&stage[0][0][0]);  // [wave][row][dim]
-      float* red_m = red_ml;                                      // [wave][row]
-      float* red_l = red_ml + 4 * PR;
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        const int row = 16 * qb + c16;
-#pragma unroll
-        for (int d = 0; d < NDB; ++d)
-          *reinterpret_cast<f32x4*>(red_o + (wave * PR + row) * D + 16 * d + 4 * grp) = oacc[d][qb];
-        const float l_tot = group_sum(l_run[qb]);
-        if (grp == 0) {
-          red_m[wave * PR + row] = m_use[qb];
-          red_l[wave * PR + row] = l_tot;
-        }
-      }
-      __syncthreads();
-      {
-        constexpr int TPR = kThreads / PR;  // threads per row
-        constexpr int DPT = D / TPR;        // dims per thread
-        const int row = tid / TPR, d0 = (tid % TPR) * DPT;
-        const int qrow = r0 + row;
-        if (qrow < ql && __float_as_uint(lrow[qrow]) == kRowFlag) {
-          float mw[4], m_all = -FLT_MAX;
-#pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            mw[w] = red_m[w * PR + row];
-            m_all = __builtin_fmaxf(m_all, mw[w]);
-          }
-          float sw[4], l_all = 0.0f;
-#pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            sw[w] = __builtin_amdgcn_exp2f(mw[w] - m_all);
-            l_all += red_l[w * PR + row] * sw[w];
-          }
-          const bool empty = !(l_all > 0.0f);
-          const float inv = empty ? 0.0f : __builtin_amdgcn_rcpf(l_all);
-          uint16_t* orow = a.o + ((int64_t)bh * ql + qrow) * D + d0;
-#pragma unroll
-          for (int e = 0; e < DPT; e += 4) {
-            f32x4 acc = f32x4{};
-#pragma unroll
-            for (int w = 0; w < 4; ++w)
-              acc += *reinterpret_cast<const f32x4*>(red_o + (w * PR + row) * D + d0 + e) * sw[w];
-            bf16x4 ov;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) ov[i] = empty ? (__bf16)0.0f : (__bf16)(acc[i] * inv);
-            *reinterpret_cast<bf16x4*>(orow + e) = ov;
-          }
-        }
-      }
-      __syncthreads();  // flags read, merge buffers free for the next pass
-      if (tid % (kThreads / PR) == 0) {
-        const int row = tid / (kThreads / PR);
-        const int qrow = r0 + row;
-        if (qrow < ql && __float_as_uint(lrow[qrow]) == kRowFlag) {
-          float m_all = -FLT_MAX, l_all = 0.0f;
-#pragma unroll
-          for (int w = 0; w < 4; ++w) m_all = __builtin_fmaxf(m_all, red_m[w * PR + row]);
-#pragma unroll
-          for (int w = 0; w < 4; ++w)
-            l_all += red_l[w * PR + row] * __builtin_amdgcn_exp2f(red_m[w * PR + row] - m_all);
-          lrow[qrow] = l_all > 0.0f ? (m_all + __builtin_amdgcn_logf(l_all)) * kLn2 : -INFINITY;
-        }
-      }
-      __syncthreads();  // red_ml is reused by the next pass
-    }
-  }
-    __syncthreads();  // pass_sh is rewritten for the next tiles
-  }
-
 #endif
 }
 
@@ -966,10 +689,8 @@ hipError_t launch(const FwdArgs& a, unsigned grid, hipStream_t stream) {
 
 // Masked: one compensated launch over all query tiles. Unmasked: the mixed
 // launch over all tiles (compensated for the tiles with short rows, the first
-// n_short ones; plain for the others), then, when there are plain tiles, the
-// rescue launch for the rows they flagged (one stream, so in order). The
-// rescue grid is persistent: a few workgroups per compute unit, each reading
-// the row markers of its share of the plain tiles.
+// n_short ones; plain for the others, with a compensated redo of the rows
+// that need it inside the same workgroup).
 template <int D, bool CAUSAL>
 hipError_t dispatch_c(FwdArgs a, bool has_mask, int n_short, hipStream_t stream) {
   const unsigned bh = (unsigned)(a.B * a.H);
@@ -981,14 +702,7 @@ hipError_t dispatch_c(FwdArgs a, bool has_mask, int n_short, hipStream_t stream)
     return launch<D, CAUSAL, true, kAll>(a, bh * n_qt, stream);
   }
   a.n_precise = n_short;
-  hipError_t e = launch<D, CAUSAL, false, kMixed>(a, bh * n_qt, stream);
-  if (e != hipSuccess || n_short >= n_qt) return e;
-  a.qt_base = n_short;
-  a.qt_count = n_qt - n_short;
-  const int64_t tiles = (int64_t)bh * (n_qt - n_short);
-  const unsigned rgrid = (unsigned)std::min<int64_t>(tiles, 256 * RescueCfg<D>::PER_CU);
-  hipLaunchKernelGGL((fa_rescue_kernel<D, CAUSAL>), dim3(rgrid), dim3(kThreads), 0, stream, a);
-  return hipGetLastError();
+  return launch<D, CAUSAL, false, kMixed>(a, bh * n_qt, stream);
 }
 
 template <int D>

@@ -62,9 +62,7 @@ enum fa_status {
  * Arguments are validated on the host before any HIP call; on error nothing is
  * enqueued and a nonzero fa_status is returned. batch*ql == 0 is a successful
  * no-op; kl == 0 gives every row O = 0 and L = -inf. Input and output buffers
- * must not overlap. The call never aborts and never synchronises. (Internally
- * L also carries a marker for rows a second launch recomputes; only the final
- * values are visible once the stream has completed.)
+ * must not overlap. The call never aborts and never synchronises.
  */
 int fa_train_fwd(const void *q, const void *k, const void *v, const float *mask, int batch,
                  int n_heads, int n_kv_heads, int ql, int kl, int head_dim, float scale,

@@ -2,7 +2,7 @@
 calls before it (a small problem, a larger one, the small one again give
 bit-identical results) nor on calls running at the same time on another
 stream. Inputs have V scaled by 4 so that many rows reach |O| >= 1 and take
-the rescue launch, whose markers live in L between the launches of a call."""
+the compensated redo of their query tile."""
 import numpy as np
 import pytest
 

@@ -139,22 +139,22 @@ def _times4(bits):
 
 @pytest.mark.parametrize("D", [64, 256])
 @pytest.mark.parametrize("causal", [True, False])
-def test_large_outputs_take_the_rescue_path(D, causal):
-    """V times 4: many rows reach |O| >= 1, which the plain launch hands to
-    the rescue launch (compensated recomputation), in query tiles whose key
+def test_large_outputs_take_the_compensated_redo(D, causal):
+    """V times 4: many rows reach |O| >= 1, which the plain pass of a query
+    tile hands to the workgroup's compensated redo, in query tiles whose key
     ranges run from under 128 keys to 700. At |O| >= 2 one bf16 step of O
     exceeds the 1e-2 bound and f32 evaluation order alone can move O across a
     rounding boundary, so an element may differ by one step."""
-    w = fagen.Workload("rescue", 1, 2, 1, 700, 700, D, causal, seed_offset=3000 + D + causal)
-    print(f"case rescue D={D} causal={causal}", flush=True)
+    w = fagen.Workload("redo", 1, 2, 1, 700, 700, D, causal, seed_offset=3000 + D + causal)
+    print(f"case redo D={D} causal={causal}", flush=True)
     inp = dict(fagen.generate(w))
     inp["v"] = _times4(inp["v"])
     o, l, bits = gu.run(inp, w)
     _, ob, lr = oracle.fwd_workload(w, inp)
     big_rows = int((np.abs(gu.widen(ob)) >= 1).any(axis=-1).sum())
     assert big_rows >= 20, big_rows
-    eo, el, rms = gu.compare(o, l, bits, ob, lr, 1e-2, 1e-2, f"rescue D={D}", one_step_ok=True)
-    print(f"rescue D={D} causal={causal}: {big_rows} rows with |O|>=1, dO={eo:.3e} dL={el:.3e} "
+    eo, el, rms = gu.compare(o, l, bits, ob, lr, 1e-2, 1e-2, f"redo D={D}", one_step_ok=True)
+    print(f"redo D={D} causal={causal}: {big_rows} rows with |O|>=1, dO={eo:.3e} dL={el:.3e} "
           f"relRMS={rms:.2e}")
     assert rms <= 5e-3  # the plain bf16-P rows carry about 2^-10 relative
 
