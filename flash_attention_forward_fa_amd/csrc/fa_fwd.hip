@@ -414,7 +414,10 @@ __device__ __forceinline__ bool fwd_tile(const FwdArgs& a, int qtile, int bh, ui
   // on its neighbours' scores)
   // (the max is compared with thr in raw-score units; c > 0, so
   // max(c*r) == c*max(r))
-  auto row_max = [&](const f32x4 (&sacc)[NKB][kQB], float (&mx)[kQB]) {
+  // The lane's own part of the row max (16 of the tile's keys for each of its
+  // rows) already tells whether the row max exceeds thr; only when some lane
+  // of the wave finds that is the max completed over the four 16-lane groups.
+  auto part_max = [&](const f32x4 (&sacc)[NKB][kQB], float (&mx)[kQB]) {
 #pragma unroll
     for (int qb = 0; qb < kQB; ++qb) {
       mx[qb] = -INFINITY;
@@ -423,16 +426,18 @@ __device__ __forceinline__ bool fwd_tile(const FwdArgs& a, int qtile, int bh, ui
 #pragma unroll
         for (int i = 0; i < 4; ++i) mx[qb] = __builtin_fmaxf(mx[qb], sacc[kb][qb][i]);
     }
+    bool raise = false;
+#pragma unroll
+    for (int qb = 0; qb < kQB; ++qb) raise |= mx[qb] > thr[qb];
+    return raise;
+  };
+  auto complete_max = [&](float (&mx)[kQB]) {
     if constexpr (kQB == 2) {
       group_max2(mx[0], mx[1]);
     } else {
 #pragma unroll
       for (int qb = 0; qb < kQB; ++qb) mx[qb] = group_max(mx[qb]);
     }
-    bool raise = false;
-#pragma unroll
-    for (int qb = 0; qb < kQB; ++qb) raise |= mx[qb] > thr[qb];
-    return raise;
   };
   auto rescale = [&](const float (&mx)[kQB]) {
 #pragma unroll
@@ -561,7 +566,10 @@ __device__ __forceinline__ bool fwd_tile(const FwdArgs& a, int qtile, int bh, ui
       if (D == 256) set_prio<0>();
       if (kt >= mask_from) apply_mask(kt, s);
       float mx[kQB];
-      if (__any(row_max(s, mx))) rescale(mx);
+      if (__any(part_max(s, mx))) {
+        complete_max(mx);
+        rescale(mx);
+      }
       bf16x8 phi[NKC][kQB], plo[NKC][kQB];
       probs(s, phi, plo);
       set_prio<2>();
