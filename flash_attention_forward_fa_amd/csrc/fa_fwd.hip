@@ -393,19 +393,27 @@ __device__ __forceinline__ bool fwd_tile(const FwdArgs& a, int qtile, int bh, ui
 #pragma unroll
     for (int qb = 0; qb < kQB; ++qb) {
       const int qrow = qw0 + 16 * qb + c16;
-      const float* mrow = HAS_MASK ? a.mask + ((int64_t)bh * ql + min(qrow, ql - 1)) * kl : nullptr;
+      if constexpr (HAS_MASK) {
+        const float* mrow = a.mask + ((int64_t)bh * ql + min(qrow, ql - 1)) * kl;
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
+        for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = kbase + 32 * (kb >> 1) + 8 * grp + 4 * (kb & 1) + i;
-          const bool vis = key < kl && (!CAUSAL || key <= off + qrow);
-          if (HAS_MASK)
+          for (int i = 0; i < 4; ++i) {
+            const int key = kbase + 32 * (kb >> 1) + 8 * grp + 4 * (kb & 1) + i;
+            const bool vis = key < kl && (!CAUSAL || key <= off + qrow);
             sacc[kb][qb][i] =
                 vis ? __builtin_fmaf(sacc[kb][qb][i], a.c, kLog2e * mrow[key]) : -INFINITY;
-          else if (!vis)
-            sacc[kb][qb][i] = -INFINITY;
-        }
+          }
+      } else {
+        // the last visible key of the row, relative to this lane's first key
+        // of the tile; each score then needs one compare with a constant
+        const int last = (CAUSAL ? min(kl - 1, off + qrow) : kl - 1) - kbase - 8 * grp;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (32 * (kb >> 1) + 4 * (kb & 1) + i > last) sacc[kb][qb][i] = -INFINITY;
+      }
     }
   };
 
