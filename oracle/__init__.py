@@ -1,4 +1,5 @@
-"""Plain CPU reference (oracle) for the flash-attention training forward.
+"""Plain CPU reference (oracle) for the flash-attention training forward
+and its backward.
 
 TEST INFRASTRUCTURE ONLY: only tests/, the smoke check of __graft_entry__ and
 the bench's cpu_baseline leg may import this package. It shares no code with
@@ -32,6 +33,9 @@ def _bind(path):
     lib.fa_oracle_fwd_rows.restype = ctypes.c_int
     lib.fa_oracle_round_bf16.argtypes = [vp, vp, i64]
     lib.fa_oracle_round_bf16.restype = None
+    lib.fa_oracle_bwd.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64,
+                                  ctypes.c_float, ctypes.c_int, vp, vp, vp, ctypes.c_int]
+    lib.fa_oracle_bwd.restype = ctypes.c_int
     return lib
 
 
@@ -113,6 +117,26 @@ def fwd_rows(q, k, v, mask, B, H, Hkv, ql, kl, D, scale, causal, rows, n_threads
     return O, round_bf16(O, lib), L
 
 
+def bwd(q, k, v, mask, L, dO, B, H, Hkv, ql, kl, D, scale, causal, n_threads=None,
+        lib=None):
+    """Backward (the page's FA-2 backward oracle). q/k/v/dO: bf16 bits or f32;
+    mask f32 or None; L: the forward's natural-log logsumexp [B,H,ql].
+
+    Returns (dQ [B,H,ql,D], dK [B,Hkv,kl,D], dV [B,Hkv,kl,D]), all f32."""
+    qf, kf, vf, mf, lf, gf = _f32(q), _f32(k), _f32(v), _f32(mask), _f32(L), _f32(dO)
+    dQ = np.empty((B, H, ql, D), dtype=np.float32)
+    dK = np.empty((B, Hkv, kl, D), dtype=np.float32)
+    dV = np.empty((B, Hkv, kl, D), dtype=np.float32)
+    lib = lib or _load()
+    rc = lib.fa_oracle_bwd(_ptr(qf), _ptr(kf), _ptr(vf), _ptr(mf), _ptr(lf), _ptr(gf), B, H,
+                           Hkv, ql, kl, D, float(scale), int(bool(causal)), _ptr(dQ), _ptr(dK),
+                           _ptr(dV), n_threads or default_threads())
+    _check(rc, "fa_oracle_bwd")
+    if kl == 0:
+        dQ[...] = 0.0
+    return dQ, dK, dV
+
+
 def bind(lib_path):
     """A fwd(...) callable over another build of fa_oracle.c (used by the
     mutation tests, which plant mistakes in a copy of the source)."""
@@ -120,6 +144,15 @@ def bind(lib_path):
 
     def f(*args, **kw):
         return fwd(*args, lib=lib, **kw)
+    return f
+
+
+def bind_bwd(lib_path):
+    """A bwd(...) callable over another build of fa_oracle.c (mutation tests)."""
+    lib = _bind(lib_path)
+
+    def f(*args, **kw):
+        return bwd(*args, lib=lib, **kw)
     return f
 
 

@@ -27,6 +27,21 @@
  *
  * Arithmetic is IEEE f32 with no contraction (built with -ffp-contract=off),
  * exp2f/logf from the C library.
+ *
+ * The backward (fa_oracle_bwd) follows the same page's CPU oracle for the
+ * FA-2 backward pass (section "Phase 2 - backward kernel helpers", function
+ * sdpa_backward_reference_f32), in natural-log units as written there:
+ *
+ *   S_ij  = scale * (q_i . k_j)  (+ mask_ij; a -inf mask entry gives -inf),
+ *           -inf for a causally hidden key (same alignment as the forward)
+ *   P_ij  = exp(S_ij - L_i)      (0 where S_ij = -inf)
+ *   dP_ij = dO_i . v_j
+ *   D_i   = sum_j P_ij * dP_ij
+ *   dS_ij = P_ij * (dP_ij - D_i)
+ *   dV_j += P_ij * dO_i,  dQ_i += scale * dS_ij * k_j,  dK_j += scale * dS_ij * q_i
+ *
+ * dK and dV of a kv head accumulate over every query head of its group; the
+ * sums run in the page's loop order (query head, query row, key).
  */
 #include <float.h>
 #include <math.h>
@@ -237,4 +252,160 @@ void fa_oracle_round_bf16(const float *x, uint16_t *out, int64_t n)
         uint32_t lsb = (u >> 16) & 1u;
         out[t] = (uint16_t)((u + 0x7FFFu + lsb) >> 16);
     }
+}
+
+/* ---- backward ---- */
+
+typedef struct {
+    const float *q, *k, *v, *mask, *L, *dO;
+    float *dQ, *dK, *dV;
+    int64_t H, Hkv, ql, kl, D;
+    float scale;
+    int causal;
+} oracle_bwd_problem;
+
+/* Every query head of kv head (b, kvh), rows in order; dK/dV of that kv head
+   and dQ of its query heads are written only here. */
+static void oracle_bwd_group(const oracle_bwd_problem *p, int64_t b, int64_t kvh, float *s,
+                             float *pr)
+{
+    const int64_t D = p->D, kl = p->kl, ql = p->ql, G = p->H / p->Hkv;
+    const float *kh = p->k + (b * p->Hkv + kvh) * kl * D;
+    const float *vh = p->v + (b * p->Hkv + kvh) * kl * D;
+    float *dkh = p->dK + (b * p->Hkv + kvh) * kl * D;
+    float *dvh = p->dV + (b * p->Hkv + kvh) * kl * D;
+    for (int64_t t = 0; t < kl * D; ++t) {
+        dkh[t] = 0.0f;
+        dvh[t] = 0.0f;
+    }
+    for (int64_t h = kvh * G; h < (kvh + 1) * G; ++h) {
+        for (int64_t i = 0; i < ql; ++i) {
+            const int64_t row = (b * p->H + h) * ql + i;
+            const float *qr = p->q + row * D;
+            const float *dor = p->dO + row * D;
+            float *dqr = p->dQ + row * D;
+            const float l_i = p->L[row];
+            for (int64_t d = 0; d < D; ++d)
+                dqr[d] = 0.0f;
+            /* scores in natural-log units, masks */
+            for (int64_t j = 0; j < kl; ++j) {
+                float dot = 0.0f;
+                for (int64_t d = 0; d < D; ++d)
+                    dot += qr[d] * kh[j * D + d];
+                s[j] = p->scale * dot;
+                if (p->mask) {
+                    const float m = p->mask[row * kl + j];
+                    if (m == -INFINITY)
+                        s[j] = -INFINITY;
+                    else
+                        s[j] += m;
+                }
+            }
+            if (p->causal) {
+                const int64_t q_abs = (kl > ql ? kl - ql : 0) + i;
+                for (int64_t j = q_abs + 1; j < kl; ++j)
+                    s[j] = -INFINITY;
+            }
+            /* P from the forward's L */
+            for (int64_t j = 0; j < kl; ++j)
+                pr[j] = (s[j] == -INFINITY) ? 0.0f : expf(s[j] - l_i);
+            /* D_i = sum_j P_ij dP_ij; s[] now holds dP */
+            float d_i = 0.0f;
+            for (int64_t j = 0; j < kl; ++j) {
+                float dp = 0.0f;
+                for (int64_t d = 0; d < D; ++d)
+                    dp += dor[d] * vh[j * D + d];
+                s[j] = dp;
+                d_i += pr[j] * dp;
+            }
+            for (int64_t j = 0; j < kl; ++j) {
+                const float ds = pr[j] * (s[j] - d_i);
+                for (int64_t d = 0; d < D; ++d)
+                    dvh[j * D + d] += pr[j] * dor[d];
+                for (int64_t d = 0; d < D; ++d) {
+                    dqr[d] += p->scale * ds * kh[j * D + d];
+                    dkh[j * D + d] += p->scale * ds * qr[d];
+                }
+            }
+        }
+    }
+}
+
+typedef struct {
+    const oracle_bwd_problem *p;
+    int64_t begin, end; /* kv-head groups (b * Hkv + kvh) */
+    int failed;
+} oracle_bwd_job;
+
+static void *oracle_bwd_worker(void *arg)
+{
+    oracle_bwd_job *j = (oracle_bwd_job *)arg;
+    const size_t n = (size_t)(j->p->kl > 0 ? j->p->kl : 1);
+    float *s = (float *)malloc(sizeof(float) * n);
+    float *pr = (float *)malloc(sizeof(float) * n);
+    if (!s || !pr) {
+        free(s);
+        free(pr);
+        j->failed = 1;
+        return NULL;
+    }
+    for (int64_t g = j->begin; g < j->end; ++g)
+        oracle_bwd_group(j->p, g / j->p->Hkv, g % j->p->Hkv, s, pr);
+    free(s);
+    free(pr);
+    return NULL;
+}
+
+/*
+ * Backward. Inputs are f32 host arrays: q, dO [B,H,ql,D]; k, v [B,Hkv,kl,D];
+ * mask [B,H,ql,kl] or NULL; L [B,H,ql] (natural-log logsumexp of the forward).
+ * Outputs dQ [B,H,ql,D], dK and dV [B,Hkv,kl,D], f32. Same return codes as
+ * fa_oracle_fwd.
+ */
+int fa_oracle_bwd(const float *q, const float *k, const float *v, const float *mask,
+                  const float *L, const float *dO, int64_t B, int64_t H, int64_t Hkv, int64_t ql,
+                  int64_t kl, int64_t D, float scale, int causal, float *dQ, float *dK, float *dV,
+                  int n_threads)
+{
+    int rc = oracle_validate(q, k, v, B, H, Hkv, ql, kl, D);
+    if (rc)
+        return rc;
+    if (B * H * ql > 0 && (!L || !dO || !dQ))
+        return 1;
+    if (B * Hkv * kl > 0 && (!dK || !dV))
+        return 1;
+    oracle_bwd_problem p = {q, k, v, mask, L, dO, dQ, dK, dV, H, Hkv, ql, kl, D, scale, causal};
+    const int64_t groups = B * Hkv;
+    if (groups <= 0)
+        return 0;
+    if (n_threads < 1)
+        n_threads = 1;
+    if (n_threads > 256)
+        n_threads = 256;
+    if (n_threads > groups)
+        n_threads = (int)groups;
+    oracle_bwd_job jobs[256];
+    pthread_t tid[256];
+    for (int t = 0; t < n_threads; ++t) {
+        jobs[t].p = &p;
+        jobs[t].begin = groups * t / n_threads;
+        jobs[t].end = groups * (t + 1) / n_threads;
+        jobs[t].failed = 0;
+    }
+    int started = 0;
+    for (int t = 1; t < n_threads; ++t) {
+        if (pthread_create(&tid[t], NULL, oracle_bwd_worker, &jobs[t]) != 0)
+            break;
+        started = t;
+    }
+    for (int t = started + 1; t < n_threads; ++t)
+        oracle_bwd_worker(&jobs[t]);
+    oracle_bwd_worker(&jobs[0]);
+    for (int t = 1; t <= started; ++t)
+        pthread_join(tid[t], NULL);
+    for (int t = 0; t < n_threads; ++t)
+        if (jobs[t].failed)
+            return 4;
+    /* a query head with ql > 0 but kv heads with kl == 0: dQ is zero */
+    return 0;
 }

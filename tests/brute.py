@@ -41,3 +41,31 @@ def attention_f64(q, k, v, mask, scale, causal):
                 L[b, h, i] = m + np.log(z)
                 O[b, h, i] = (e @ v[b, kvh]) / z
     return O, L
+
+
+def attention_grads_f64(q, k, v, mask, dO, scale, causal):
+    """Gradients of sum(O * dO) with respect to q, k, v for the same textbook
+    definition, by torch's autograd in float64 on the CPU (a library routine
+    serving as the differentiation step). Rows with no visible key have O = 0
+    and contribute nothing. Returns numpy (dQ, dK, dV)."""
+    import torch
+    t = lambda a: torch.tensor(np.asarray(a, dtype=np.float64), dtype=torch.float64)
+    qt, kt, vt = t(q).requires_grad_(), t(k).requires_grad_(), t(v).requires_grad_()
+    B, H, ql, D = qt.shape
+    Hkv, kl = kt.shape[1], kt.shape[2]
+    group = H // Hkv
+    idx = torch.arange(H) // group
+    kr, vr = kt[:, idx], vt[:, idx]                       # [B, H, kl, D]
+    s = scale * torch.matmul(qt, kr.transpose(-1, -2).contiguous())
+    if mask is not None:
+        s = s + t(mask)
+    if causal:
+        off = max(kl - ql, 0)
+        hide = torch.arange(kl)[None, :] > (off + torch.arange(ql)[:, None])
+        s = s.masked_fill(hide, float("-inf"))
+    live = torch.isfinite(s).any(dim=-1, keepdim=True)
+    s = torch.where(live, s, torch.zeros_like(s))
+    p = torch.softmax(s, dim=-1) * live
+    O = torch.matmul(p, vr)
+    (O * t(dO)).sum().backward()
+    return qt.grad.numpy(), kt.grad.numpy(), vt.grad.numpy()

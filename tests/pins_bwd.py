@@ -1,0 +1,133 @@
+"""Pins for a backward oracle callable bwd(q, k, v, mask, L, dO, B, H, Hkv,
+ql, kl, D, scale, causal) -> (dQ, dK, dV).
+
+Each pin checks the backward against something other than its own code:
+torch's float64 autograd of the textbook definition (tests/brute.py), central
+finite differences of the float64 forward, closed forms (constant V rows give
+dQ = dK = 0; zero dO gives zero gradients) and the GQA invariance. L is taken
+from the float64 forward, so these pins do not lean on the forward oracle.
+Functions, not tests, so that test_oracle_mutants.py can run them against
+deliberately broken builds of the oracle.
+"""
+import math
+
+import numpy as np
+
+import fagen
+from tests.brute import attention_f64, attention_grads_f64
+from tests.pins import _finite_mask, _inputs, _widen
+
+
+def _case(seed, B, H, Hkv, ql, kl, D, masked):
+    q, k, v = _inputs(seed, B, H, Hkv, ql, kl, D)
+    dO = fagen.normal_bf16(seed, 7, (B, H, ql, D), 1.0)
+    mask = _finite_mask(seed, B, H, ql, kl) if masked else None
+    return q, k, v, dO, mask
+
+
+def _lse(q, k, v, mask, scale, causal):
+    _, L = attention_f64(_widen(q), _widen(k), _widen(v), mask, scale, causal)
+    return L.astype(np.float32)
+
+
+def pin_bwd_autograd(bwd, B, H, Hkv, ql, kl, D, causal, masked, seed, scale=None):
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    q, k, v, dO, mask = _case(seed, B, H, Hkv, ql, kl, D, masked)
+    L = _lse(q, k, v, mask, scale, causal)
+    got = bwd(q, k, v, mask, L, dO, B, H, Hkv, ql, kl, D, scale, causal)
+    ref = attention_grads_f64(_widen(q).reshape(B, H, ql, D), _widen(k).reshape(B, Hkv, kl, D),
+                              _widen(v).reshape(B, Hkv, kl, D), mask,
+                              _widen(dO).reshape(B, H, ql, D), scale, causal)
+    for name, g, r in zip(("dQ", "dK", "dV"), got, ref):
+        err = np.abs(g - r).max() if r.size else 0.0
+        tol = 2e-5 * max(1.0, np.abs(r).max() if r.size else 1.0)
+        assert err <= tol, f"{name} vs f64 autograd: {err:.3e} > {tol:.3e}"
+
+
+def pin_bwd_finite_difference(bwd, seed=31):
+    """Central differences of sum(O * dO) of the float64 forward, at a few
+    entries of Q, K and V (the page's falsifier, at more than one entry)."""
+    B, H, Hkv, ql, kl, D, scale = 1, 2, 1, 6, 9, 8, 0.4
+    q, k, v, dO, _ = _case(seed, B, H, Hkv, ql, kl, D, False)
+    qf, kf, vf, gf = (_widen(x).astype(np.float64) for x in (q, k, v, dO))
+    qf, gf = qf.reshape(B, H, ql, D), gf.reshape(B, H, ql, D)
+    kf, vf = kf.reshape(B, Hkv, kl, D), vf.reshape(B, Hkv, kl, D)
+    L = _lse(q, k, v, None, scale, True)
+    dQ, dK, dV = bwd(q, k, v, None, L, dO, B, H, Hkv, ql, kl, D, scale, True)
+    loss = lambda a, b_, c: float((attention_f64(a, b_, c, None, scale, True)[0] * gf).sum())
+    h = 1e-4
+    rng = np.random.default_rng(seed)
+    for which, grad in (("q", dQ), ("k", dK), ("v", dV)):
+        base = {"q": qf, "k": kf, "v": vf}[which]
+        for _ in range(4):
+            ix = tuple(int(rng.integers(0, n)) for n in base.shape)
+            plus, minus = base.copy(), base.copy()
+            plus[ix] += h
+            minus[ix] -= h
+            args_p = [qf, kf, vf]
+            args_m = [qf, kf, vf]
+            pos = "qkv".index(which)
+            args_p[pos], args_m[pos] = plus, minus
+            fd = (loss(*args_p) - loss(*args_m)) / (2 * h)
+            assert abs(fd - grad[ix]) <= 1e-4 * max(1.0, abs(fd)), \
+                f"d{which.upper()}{ix}: finite difference {fd:.6f}, oracle {grad[ix]:.6f}"
+
+
+def pin_bwd_constant_v(bwd):
+    """Every V row equal to one vector c: dP_ij = dO_i . c is the same for all j,
+    so dS = P (dP - D) = 0 and dQ = dK = 0; dV_j = sum_i P_ij dO_i."""
+    B, H, Hkv, ql, kl, D, scale = 1, 2, 2, 7, 11, 16, 0.35
+    q, k, _, dO, _ = _case(41, B, H, Hkv, ql, kl, D, False)
+    c = fagen.normal_bf16(41, 5, (D,), 1.0)
+    v = np.tile(c, B * Hkv * kl).reshape(B, Hkv, kl, D)
+    L = _lse(q, k, v, None, scale, True)
+    dQ, dK, dV = bwd(q, k, v, None, L, dO, B, H, Hkv, ql, kl, D, scale, True)
+    assert np.abs(dQ).max() <= 2e-6 and np.abs(dK).max() <= 2e-6, "constant V: dQ, dK not 0"
+    _, _, dVr = attention_grads_f64(_widen(q).reshape(B, H, ql, D), _widen(k).reshape(B, Hkv, kl, D),
+                                    _widen(v).reshape(B, Hkv, kl, D), None,
+                                    _widen(dO).reshape(B, H, ql, D), scale, True)
+    assert np.abs(dV - dVr).max() <= 1e-5 * max(1.0, np.abs(dVr).max())
+
+
+def pin_bwd_zero_do(bwd):
+    B, H, Hkv, ql, kl, D, scale = 1, 2, 1, 5, 6, 8, 0.5
+    q, k, v, _, mask = _case(43, B, H, Hkv, ql, kl, D, True)
+    dO = np.zeros((B, H, ql, D), np.uint16)
+    L = _lse(q, k, v, mask, scale, False)
+    for g in bwd(q, k, v, mask, L, dO, B, H, Hkv, ql, kl, D, scale, False):
+        assert np.all(g == 0), "zero upstream gradient must give zero gradients"
+
+
+def pin_bwd_gqa(bwd):
+    """Hkv < H equals the same problem with every query head given its own
+    copy of its kv head, and dK, dV summed over each group."""
+    B, H, Hkv, ql, kl, D, scale = 2, 4, 2, 6, 7, 8, 0.3
+    q, k, v, dO, mask = _case(47, B, H, Hkv, ql, kl, D, True)
+    L = _lse(q, k, v, mask, scale, True)
+    dQ, dK, dV = bwd(q, k, v, mask, L, dO, B, H, Hkv, ql, kl, D, scale, True)
+    rep = lambda a: np.repeat(a.reshape(B, Hkv, kl, D), H // Hkv, axis=1)
+    dQ2, dK2, dV2 = bwd(q, rep(k), rep(v), mask, L, dO, B, H, H, ql, kl, D, scale, True)
+    fold = lambda a: a.reshape(B, Hkv, H // Hkv, kl, D).sum(axis=2)
+    assert np.abs(dQ - dQ2).max() <= 1e-6 * max(1.0, np.abs(dQ).max())
+    assert np.abs(dK - fold(dK2)).max() <= 1e-5 * max(1.0, np.abs(dK).max())
+    assert np.abs(dV - fold(dV2)).max() <= 1e-5 * max(1.0, np.abs(dV).max())
+
+
+AUTOGRAD_CASES = [
+    # B, H, Hkv, ql, kl, D, causal, masked, seed
+    (1, 1, 1, 1, 1, 4, False, False, 1),
+    (1, 2, 2, 5, 7, 8, False, False, 2),
+    (1, 2, 1, 9, 9, 8, True, False, 3),
+    (2, 4, 2, 7, 13, 16, True, True, 4),
+    (1, 4, 1, 12, 5, 8, True, False, 5),    # ql > kl: offset clamped at 0
+    (1, 2, 2, 17, 33, 64, True, True, 6),
+    (1, 1, 1, 8, 8, 64, False, True, 7),
+]
+
+ALL_PINS = [(f"autograd{c}", (lambda c: lambda f: pin_bwd_autograd(f, *c))(c))
+            for c in AUTOGRAD_CASES] + [
+    ("finite_difference", pin_bwd_finite_difference),
+    ("constant_v", pin_bwd_constant_v),
+    ("zero_do", pin_bwd_zero_do),
+    ("gqa", pin_bwd_gqa),
+]

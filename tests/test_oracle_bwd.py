@@ -1,0 +1,19 @@
+"""The backward oracle against its pins (CPU only)."""
+import pytest
+
+import oracle
+from tests import pins_bwd
+
+
+@pytest.mark.parametrize("name,pin", pins_bwd.ALL_PINS, ids=[n for n, _ in pins_bwd.ALL_PINS])
+def test_backward_oracle_pin(name, pin):
+    pin(oracle.bwd)
+
+
+def test_backward_oracle_kl_zero_gives_zero_dq():
+    import numpy as np
+    q = np.zeros((1, 1, 3, 4), np.uint16)
+    k = np.zeros((1, 1, 0, 4), np.uint16)
+    L = np.full((1, 1, 3), -np.inf, np.float32)
+    dQ, dK, dV = oracle.bwd(q, k, k, None, L, q, 1, 1, 1, 3, 0, 4, 0.5, False)
+    assert dQ.shape == (1, 1, 3, 4) and np.all(dQ == 0) and dK.size == 0 and dV.size == 0

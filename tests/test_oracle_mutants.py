@@ -19,19 +19,20 @@ SRC = os.path.join(os.path.dirname(oracle.__file__), "fa_oracle.c")
 
 MUTANTS = {
     "mask_in_natural_units": ("s[j] += ORACLE_LOG2E * mr[j];", "s[j] += mr[j];"),
-    "mask_dropped": ("if (p->mask) {", "if (0) {"),
+    "mask_dropped": ("\n    if (p->mask) {", "\n    if (0) {"),
     "exp_sign_flipped": ("s[j] = exp2f(s[j] - m);", "s[j] = exp2f(m - s[j]);"),
-    "causal_off_by_one": ("for (int64_t j = q_abs + 1; j < kl; ++j)",
-                          "for (int64_t j = q_abs; j < kl; ++j)"),
-    "causal_offset_dropped": ("const int64_t q_abs = (kl > ql ? kl - ql : 0) + i;",
-                              "const int64_t q_abs = i;"),
-    "causal_offset_unclamped": [("const int64_t q_abs = (kl > ql ? kl - ql : 0) + i;",
-                                 "const int64_t q_abs = (kl - ql) + i;"),
-                                ("for (int64_t j = q_abs + 1; j < kl; ++j)",
-                                 "for (int64_t j = (q_abs + 1 > 0 ? q_abs + 1 : 0); j < kl; ++j)")],
+    "causal_off_by_one": ("\n        for (int64_t j = q_abs + 1; j < kl; ++j)",
+                          "\n        for (int64_t j = q_abs; j < kl; ++j)"),
+    "causal_offset_dropped": ("\n        const int64_t q_abs = (kl > ql ? kl - ql : 0) + i;",
+                              "\n        const int64_t q_abs = i;"),
+    "causal_offset_unclamped": [("\n        const int64_t q_abs = (kl > ql ? kl - ql : 0) + i;",
+                                 "\n        const int64_t q_abs = (kl - ql) + i;"),
+                                ("\n        for (int64_t j = q_abs + 1; j < kl; ++j)",
+                                 "\n        for (int64_t j = (q_abs + 1 > 0 ? q_abs + 1 : 0); j < kl; ++j)")],
     "gqa_modulo_map": ("const int64_t kvh = h / (p->H / p->Hkv);",
                        "const int64_t kvh = h % p->Hkv;"),
-    "k_transposed": ("dot += qr[d] * kh[j * D + d];", "dot += qr[d] * kh[d * kl + j];"),
+    "k_transposed": ("\n            dot += qr[d] * kh[j * D + d];",
+                     "\n            dot += qr[d] * kh[d * kl + j];"),
     "scale_dropped": ("s[j] = dot * q_scale;", "s[j] = dot * ORACLE_LOG2E;"),
     "log2e_dropped": ("const float q_scale = p->scale * ORACLE_LOG2E;",
                       "const float q_scale = p->scale;"),
@@ -41,10 +42,10 @@ MUTANTS = {
     "infinite_sentinel": ("float m = -FLT_MAX / 2.0f;", "float m = -INFINITY;"),
     "no_empty_row_guard": ("const float safe = (sum == 0.0f) ? 1.0f : sum;",
                            "const float safe = sum;"),
-    "v_from_head_zero": ("const float *vh = p->v + (b * p->Hkv + kvh) * kl * D;",
-                         "const float *vh = p->v + (b * p->Hkv) * kl * D;"),
-    "k_batch_dropped": ("const float *kh = p->k + (b * p->Hkv + kvh) * kl * D;",
-                        "const float *kh = p->k + kvh * kl * D;"),
+    "v_from_head_zero": ("\n    const float *vh = p->v + (b * p->Hkv + kvh) * kl * D;\n\n",
+                         "\n    const float *vh = p->v + (b * p->Hkv) * kl * D;\n\n"),
+    "k_batch_dropped": ("const float *qr = p->q + row * D;\n    const float *kh = p->k + (b * p->Hkv + kvh) * kl * D;",
+                        "const float *qr = p->q + row * D;\n    const float *kh = p->k + kvh * kl * D;"),
     "v_row_off_by_one": ("const float *vr = vh + j * D;",
                          "const float *vr = vh + (j + 1 < kl ? j + 1 : j) * D;"),
     "max_skips_last_key": ("for (int64_t j = 0; j < kl; ++j)\n        if (s[j] > m)",
@@ -79,3 +80,40 @@ def test_pins_catch_planted_mistake(name):
             except (AssertionError, ValueError, FloatingPointError):
                 caught.append(pin_name)
         assert caught, f"no pin catches mutant {name}"
+
+
+# Planted mistakes in the backward part of the oracle, caught by tests/pins_bwd.py.
+BWD_MUTANTS = {
+    "bwd_dq_scale_dropped": ("dqr[d] += p->scale * ds * kh[j * D + d];",
+                             "dqr[d] += ds * kh[j * D + d];"),
+    "bwd_ds_sign_flipped": ("const float ds = pr[j] * (s[j] - d_i);",
+                            "const float ds = pr[j] * (d_i - s[j]);"),
+    "bwd_D_dropped": ("d_i += pr[j] * dp;", "d_i += 0.0f * dp;"),
+    "bwd_p_base2": ("expf(s[j] - l_i)", "exp2f(s[j] - l_i)"),
+    "bwd_causal_off_by_one": ("for (int64_t j = q_abs + 1; j < kl; ++j)\n                    s[j] = -INFINITY;",
+                              "for (int64_t j = q_abs + 2; j < kl; ++j)\n                    s[j] = -INFINITY;"),
+    "bwd_dk_uses_k": ("dkh[j * D + d] += p->scale * ds * qr[d];",
+                      "dkh[j * D + d] += p->scale * ds * kh[j * D + d];"),
+    "bwd_dv_uses_q": ("dvh[j * D + d] += pr[j] * dor[d];", "dvh[j * D + d] += pr[j] * qr[d];"),
+    "bwd_group_first_head_only": ("for (int64_t h = kvh * G; h < (kvh + 1) * G; ++h) {",
+                                  "for (int64_t h = kvh * G; h < kvh * G + 1; ++h) {"),
+    "bwd_mask_ignored": ("if (p->mask) {\n                    const float m = p->mask[row * kl + j];",
+                         "if (0) {\n                    const float m = p->mask[row * kl + j];"),
+    "bwd_dp_uses_q": ("dp += dor[d] * vh[j * D + d];", "dp += qr[d] * vh[j * D + d];"),
+    "bwd_mask_base2": ("s[j] += m;", "s[j] += 1.44269504f * m;"),
+    "bwd_lse_ignored": ("expf(s[j] - l_i)", "expf(s[j])"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(BWD_MUTANTS))
+def test_backward_pins_catch_planted_mistake(name):
+    from tests import pins_bwd
+    with tempfile.TemporaryDirectory() as tmp:
+        bwd = oracle.bind_bwd(_build_mutant(tmp, name, BWD_MUTANTS[name]))
+        caught = []
+        for pin_name, pin in pins_bwd.ALL_PINS:
+            try:
+                pin(bwd)
+            except (AssertionError, ValueError, FloatingPointError):
+                caught.append(pin_name)
+        assert caught, f"no backward pin catches mutant {name}"
