@@ -1,4 +1,5 @@
-"""Flash-attention training forward (O and L) on AMD MI355X.
+"""Flash-attention training forward (O and L) and backward (dQ, dK, dV) on AMD
+MI355X.
 
 A thin binding over libfa.so (include/fa.h): argument marshalling only. Every
 step of the computation runs in the library's gfx950 kernels; PyTorch only
@@ -40,6 +41,9 @@ def lib():
         l.fa_train_fwd.argtypes = [vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, ctypes.c_float, ci,
                                    vp, vp, vp]
         l.fa_train_fwd.restype = ci
+        l.fa_train_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci,
+                                   ctypes.c_float, ci, vp, vp, vp, vp]
+        l.fa_train_bwd.restype = ci
         l.fa_status_string.argtypes = [ci]
         l.fa_status_string.restype = ctypes.c_char_p
         _lib = l
@@ -102,3 +106,54 @@ def train_fwd(q, k, v, mask=None, scale=None, causal=False, out=None, lse=None, 
     if status != 0:
         raise FAError(status, status_string(status))
     return O, L
+
+
+def fa_train_bwd(q, k, v, mask, O, L, dO, batch, n_heads, n_kv_heads, ql, kl, head_dim, scale,
+                 causal, dQ, dK, dV, stream):
+    """The C entry point with raw integer pointers (0 for NULL); returns the status."""
+    return lib().fa_train_bwd(q or None, k or None, v or None, mask or None, O or None,
+                              L or None, dO or None, batch, n_heads, n_kv_heads, ql, kl, head_dim,
+                              float(scale), int(bool(causal)), dQ or None, dK or None, dV or None,
+                              stream or None)
+
+
+def train_bwd(q, k, v, O, L, dO, mask=None, scale=None, causal=False, stream=None):
+    """dQ, dK, dV = train_bwd(q, k, v, O, L, dO, mask=None, scale=None, causal=False)
+
+    The backward of train_fwd: q, k, v, mask, scale, causal as given to it; O
+    and L its outputs; dO (bf16, shaped like O) the upstream gradient. Returns
+    bf16 dQ (like q), dK and dV (like k), enqueued on the current stream.
+    """
+    import torch
+
+    for name, t in (("q", q), ("k", k), ("v", v), ("O", O), ("dO", dO)):
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.bfloat16:
+            raise TypeError(f"{name} must be a bfloat16 tensor")
+        if t.dim() != 4 or not t.is_contiguous() or not t.is_cuda or t.device != q.device:
+            raise ValueError(f"{name} must be a contiguous 4-d tensor on q's GPU")
+    B, H, ql, D = q.shape
+    Bk, Hkv, kl, Dk = k.shape
+    if tuple(v.shape) != tuple(k.shape) or Bk != B or Dk != D:
+        raise ValueError("k and v must be [B, Hkv, kl, D] with q's B and D")
+    if O.shape != q.shape or dO.shape != q.shape:
+        raise ValueError("O and dO must be shaped like q")
+    if (L.dtype != torch.float32 or tuple(L.shape) != (B, H, ql) or not L.is_contiguous()
+            or L.device != q.device):
+        raise ValueError("L must be a contiguous f32 tensor [B, H, ql] on q's device")
+    if mask is not None:
+        if mask.dtype != torch.float32 or not mask.is_contiguous() or mask.device != q.device:
+            raise ValueError("mask must be a contiguous float32 tensor on q's device")
+        if tuple(mask.shape) != (B, H, ql, kl):
+            raise ValueError(f"mask must have shape {(B, H, ql, kl)}")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    dQ, dK, dV = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    s = stream if stream is not None else torch.cuda.current_stream(q.device)
+    with torch.cuda.device(q.device):
+        status = fa_train_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                              mask.data_ptr() if mask is not None else 0, O.data_ptr(),
+                              L.data_ptr(), dO.data_ptr(), B, H, Hkv, ql, kl, D, scale, causal,
+                              dQ.data_ptr(), dK.data_ptr(), dV.data_ptr(), s.cuda_stream)
+    if status != 0:
+        raise FAError(status, status_string(status))
+    return dQ, dK, dV

@@ -1,4 +1,4 @@
-"""Builds libfa.so, the C-ABI library of the gfx950 forward kernels, with hipcc.
+"""Builds libfa.so, the C-ABI library of the gfx950 forward and backward kernels, with hipcc.
 
 Flags:
   --offload-arch=gfx950           MI355X only (CDNA4)
@@ -14,7 +14,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libfa.so")
-SOURCES = [os.path.join(HERE, "csrc", "fa_fwd.hip")]
+SOURCES = [os.path.join(HERE, "csrc", "fa_fwd.hip"), os.path.join(HERE, "csrc", "fa_bwd.hip")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

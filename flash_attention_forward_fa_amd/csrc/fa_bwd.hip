@@ -1,0 +1,482 @@
+// fa_bwd.hip - flash-attention training backward (dQ, dK, dV) for AMD MI355X
+// (gfx950).
+//
+// What is computed is the FA-2 backward of the method's page ("mlx-native
+// 0.9.0", tests/test_flash_attn_train.rs, section "Phase 2 - backward kernel
+// helpers", the CPU oracle sdpa_backward_reference_f32), with the forward's
+// causal alignment (key j hidden from query row i when j > max(kl - ql, 0) + i):
+//
+//   S_ij  = scale * q_i . k_j (+ mask_ij)       P_ij = exp(S_ij - L_i)
+//   dP_ij = dO_i . v_j                          D_i  = sum_d O_id dO_id
+//   dS_ij = P_ij (dP_ij - D_i)
+//   dQ_i  = scale * sum_j dS_ij k_j             dK_j = scale * sum_i dS_ij q_i
+//   dV_j  = sum_i P_ij dO_i                     (dK, dV summed over a GQA group)
+//
+// (D_i = rowsum(dO_i * O_i) equals the page's sum_j P_ij dP_ij when O is the
+// forward's output.) Two launches, no atomics and no workspace: one kernel
+// template serves both. A workgroup keeps a block of "fixed" rows in registers
+// and streams tiles of the other side through LDS:
+//
+//   dQ pass  (kBwdQ):  fixed = query rows (Q, dO, L, D), streamed = keys (K, V)
+//   dKV pass (kBwdKV): fixed = key rows (K, V), streamed = query rows of every
+//                      head of the group (Q, dO, and L, D per row)
+//
+// Per streamed tile every wave computes, with v_mfma_f32_16x16x32_bf16 and the
+// same operand layouts as the forward kernel,
+//   S^T  = Y1 X1^T (raw scores)   dP^T = Y2 X2^T
+// (Y1/Y2 = streamed K/V or Q/dO rows read from LDS as the A operand, rows
+// permuted by key_of so that the products' C layout is the next product's B
+// layout; X1/X2 = fixed Q/dO or K/V rows held as the B operand), then P and dS
+// element by element, and
+//   dQ pass:  dQ^T += Y1^T dS^T
+//   dKV pass: dK^T += Y1^T dS,  dV^T += Y2^T P
+// with Y1^T, Y2^T read from the LDS tiles by ds_read_b64_tr_b16. P and dS
+// enter the MFMAs rounded to bf16; the sums are f32.
+#include <hip/hip_runtime.h>
+
+#include <float.h>
+#include <math.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "fa.h"
+#include "fa_common.h"
+
+namespace {
+
+constexpr int kBwdQ = 0, kBwdKV = 1;
+
+// Per head dim and pass: W waves, FB fixed 16-row blocks per wave, BN streamed
+// rows per tile, WPE waves per SIMD (register budget).
+template <int D, int PASS> struct BwdCfg;
+template <> struct BwdCfg<64, kBwdQ> { static constexpr int W = 8, FB = 2, BN = 64, WPE = 2; };
+template <> struct BwdCfg<64, kBwdKV> { static constexpr int W = 8, FB = 2, BN = 64, WPE = 2; };
+template <> struct BwdCfg<256, kBwdQ> { static constexpr int W = 8, FB = 1, BN = 64, WPE = 2; };
+template <> struct BwdCfg<256, kBwdKV> { static constexpr int W = 4, FB = 1, BN = 64, WPE = 1; };
+template <int D, int PASS> constexpr int fixed_rows() {
+  return BwdCfg<D, PASS>::W * 16 * BwdCfg<D, PASS>::FB;
+}
+
+struct BwdArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* o;
+  const uint16_t* dO;
+  const float* L;
+  const float* mask;
+  uint16_t* dq;
+  uint16_t* dk;
+  uint16_t* dv;
+  int B, H, Hkv, ql, kl;
+  int group;         // H / Hkv
+  int n_ftiles;      // fixed-row tiles per (batch, head) of the fixed side
+  int causal_off;    // max(kl - ql, 0)
+  float scale;       // signed softmax scale (multiplies dQ and dK)
+  float c;           // scale * log2(e), never 0 (exp2 argument factor)
+};
+
+// log2-units logsumexp of a row; a row with no visible key (L = -inf) gets
+// +inf, so that every P of that row is 0
+__device__ __forceinline__ float lse2(float l) { return l == -INFINITY ? INFINITY : l * kLog2e; }
+
+template <int D, int PASS, bool CAUSAL, bool HAS_MASK>
+__global__ __launch_bounds__((64 * BwdCfg<D, PASS>::W))
+__attribute__((amdgpu_waves_per_eu(BwdCfg<D, PASS>::WPE))) void fa_bwd_kernel(BwdArgs a) {
+#if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
+  using C = BwdCfg<D, PASS>;
+  constexpr int BN = C::BN;
+  constexpr int FB = C::FB;
+  constexpr int FR = fixed_rows<D, PASS>();
+  constexpr int NKB = BN / 16;  // 16-row blocks of a streamed tile
+  constexpr int NKC = BN / 32;  // 32-row chunks (contraction steps of the second products)
+  constexpr int NDB = D / 16;   // 16-dim blocks
+  constexpr int NDS = D / 32;   // 32-dim steps
+  constexpr int TILE = BN * D;
+  constexpr int NT = 64 * C::W;
+  constexpr bool KV = PASS == kBwdKV;
+  __shared__ __attribute__((aligned(1024))) uint16_t y1s[2][TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t y2s[2][TILE];
+  __shared__ float srow[2][2][BN];  // dKV pass: L2 and D of the streamed rows
+
+  const int tid = threadIdx.x;
+  // wave-uniform wave index: every wave-level condition is a scalar branch
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int c16 = lane & 15;
+  const int grp = lane >> 4;
+
+  // ---- work item: heaviest first under causal masking ----
+  // dQ pass: late query tiles see the most keys; dKV pass: early key tiles are
+  // seen by the most queries.
+  const int nfh = KV ? a.B * a.Hkv : a.B * a.H;  // fixed (batch, head) pairs
+  const int bid = blockIdx.x;
+  const int fhead = bid % nfh;
+  const int ftile = KV ? bid / nfh : a.n_ftiles - 1 - bid / nfh;
+  const int b = fhead / (KV ? a.Hkv : a.H);
+  const int hf = fhead % (KV ? a.Hkv : a.H);     // fixed head (query head or kv head)
+  const int g = KV ? hf : hf / a.group;           // kv head
+  const int ql = a.ql, kl = a.kl, off = a.causal_off;
+  const int nfixed = KV ? kl : ql;
+  const int nstream = KV ? ql : kl;
+  const int f0 = ftile * FR;
+  const int fw0 = f0 + wave * 16 * FB;  // this wave's first fixed row
+  const bool wave_active = fw0 < nfixed;
+
+  const int64_t kv_base = (int64_t)(b * a.Hkv + g) * kl * D;
+  const uint16_t* x1p = KV ? a.k + kv_base : a.q + (int64_t)fhead * ql * D;
+  const uint16_t* x2p = KV ? a.v + kv_base : a.dO + (int64_t)fhead * ql * D;
+
+  // ---- fixed rows as B operands: block fb, step s: row fw0+16fb+c16, dims 32s+8grp.. ----
+  bf16x8 x1op[FB][NDS], x2op[FB][NDS];
+#pragma unroll
+  for (int fb = 0; fb < FB; ++fb) {
+    const int r = min(fw0 + 16 * fb + c16, nfixed - 1);
+#pragma unroll
+    for (int s = 0; s < NDS; ++s) {
+      x1op[fb][s] = __builtin_bit_cast(
+          bf16x8, *reinterpret_cast<const u32x4*>(x1p + (int64_t)r * D + 32 * s + 8 * grp));
+      x2op[fb][s] = __builtin_bit_cast(
+          bf16x8, *reinterpret_cast<const u32x4*>(x2p + (int64_t)r * D + 32 * s + 8 * grp));
+    }
+  }
+  // dQ pass: L2 and D of the fixed rows (D from the same dims as the dO operand,
+  // summed over the four 16-lane groups)
+  float l2f[FB], dfx[FB];
+  if constexpr (!KV) {
+#pragma unroll
+    for (int fb = 0; fb < FB; ++fb) {
+      const int r = min(fw0 + 16 * fb + c16, nfixed - 1);
+      float part = 0.0f;
+#pragma unroll
+      for (int s = 0; s < NDS; ++s) {
+        const bf16x8 ov = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const u32x4*>(a.o + ((int64_t)fhead * ql + r) * D + 32 * s +
+                                                     8 * grp));
+#pragma unroll
+        for (int e = 0; e < 8; ++e) part += (float)ov[e] * (float)x2op[fb][s][e];
+      }
+      dfx[fb] = group_sum(part);
+      l2f[fb] = lse2(a.L[(int64_t)fhead * ql + r]);
+    }
+  }
+
+  // ---- accumulators: dQ^T, or dK^T and dV^T (dims x fixed rows) ----
+  f32x4 acc1[NDB][FB], acc2[NDB][FB];
+#pragma unroll
+  for (int d = 0; d < NDB; ++d)
+#pragma unroll
+    for (int fb = 0; fb < FB; ++fb) {
+      acc1[d][fb] = f32x4{};
+      acc2[d][fb] = f32x4{};
+    }
+
+  // ---- streamed range ----
+  // dQ pass: keys 0 .. kend of kv head g. dKV pass: for every query head of the
+  // group, the query tiles from the first one that sees the workgroup's first key.
+  const int flast = min(f0 + FR, nfixed) - 1;
+  int n_per = 0, st_lo = 0;
+  if constexpr (!KV) {
+    const int kend = CAUSAL ? min(kl, off + flast + 1) : kl;
+    n_per = kend > 0 ? (kend + BN - 1) / BN : 0;
+  } else {
+    const int n_qt = (ql + BN - 1) / BN;
+    st_lo = CAUSAL ? max(0, f0 - off) / BN : 0;
+    n_per = max(0, n_qt - st_lo);
+  }
+  const int n_st = KV ? a.group * n_per : n_per;
+  auto tile_head = [&](int t) { return KV ? g * a.group + t / n_per : hf; };
+  auto tile_first = [&](int t) { return KV ? (st_lo + t % n_per) * BN : t * BN; };
+  auto y1_src = [&](int t) -> const uint16_t* {
+    return KV ? a.q + (int64_t)(b * a.H + tile_head(t)) * ql * D : a.k + kv_base;
+  };
+  auto y2_src = [&](int t) -> const uint16_t* {
+    return KV ? a.dO + (int64_t)(b * a.H + tile_head(t)) * ql * D : a.v + kv_base;
+  };
+
+  int y1off[CopyShape<D, BN, NT>::ROUNDS], y2off[CopyShape<D, BN, NT>::ROUNDS];
+  copy_offsets<D, BN, NT, true>(tid, y1off);
+  copy_offsets<D, BN, NT, false>(tid, y2off);
+  auto issue = [&](int t) {
+    const int buf = t & 1;
+    issue_tile<D, BN, NT, true>(y1_src(t), tile_first(t), nstream, y1s[buf], tid, 64 * wave, y1off);
+    issue_tile<D, BN, NT, false>(y2_src(t), tile_first(t), nstream, y2s[buf], tid, 64 * wave,
+                                 y2off);
+  };
+  // dKV pass: L2 and D of the streamed rows of tile t into srow[t & 1]
+  // (NT / BN threads per row, each summing D / (NT / BN) dims)
+  auto stream_rows = [&](int t) {
+    if constexpr (KV) {
+      constexpr int TPR = NT / BN;
+      constexpr int DPT = D / TPR;
+      const int r = tid / TPR, part = tid % TPR;
+      const int qi = min(tile_first(t) + r, ql - 1);
+      const int64_t row = (int64_t)(b * a.H + tile_head(t)) * ql + qi;
+      float acc = 0.0f;
+#pragma unroll
+      for (int c = 0; c < DPT / 8; ++c) {
+        const int64_t at = row * D + part * DPT + 8 * c;
+        const bf16x8 ov = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(a.o + at));
+        const bf16x8 gv = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(a.dO + at));
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc += (float)ov[e] * (float)gv[e];
+      }
+#pragma unroll
+      for (int m = 1; m < TPR; m <<= 1) acc += __shfl_xor(acc, m, 64);
+      if (part == 0) {
+        srow[t & 1][0][r] = lse2(a.L[row]);
+        srow[t & 1][1][r] = acc;
+      }
+    }
+  };
+
+  // ---- operand reads from the LDS tiles ----
+  // row read (A operand of S^T / dP^T): streamed row key_of(kb, c16), dims 32s + 8grp..
+  auto rread = [&](const uint16_t* buf, bool is_y1, int s, int kb) {
+    const int r = key_of(kb, c16);
+    const int sw = is_y1 ? kswz<D>(r) : vswz<D>(r);
+    return *reinterpret_cast<const bf16x8*>(buf + r * D + 8 * ((4 * s + grp) ^ sw));
+  };
+  // transposed read (A operand of the second products): dims 16d + c16, streamed
+  // rows 32j + 8grp + (0..7)
+  auto tread = [&](const uint16_t* buf, bool is_y1, int d, int j) {
+    s16x4 half[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int r = 32 * j + 8 * grp + 4 * t + (c16 >> 2);
+      const int col = 16 * d + 4 * (c16 & 3);
+      const int sw = is_y1 ? kswz<D>(r) : vswz<D>(r);
+      const uint16_t* addr = buf + r * D + 8 * ((col >> 3) ^ sw) + (col & 7);
+      half[t] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)addr);
+    }
+    return __builtin_bit_cast(bf16x8,
+                              __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  auto products = [&](const uint16_t* buf, bool is_y1, const bf16x8 (&xop)[FB][NDS],
+                      f32x4 (&out)[NKB][FB]) {
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int fb = 0; fb < FB; ++fb) out[kb][fb] = f32x4{};
+#pragma unroll
+    for (int s = 0; s < NDS; ++s)
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        const bf16x8 yop = rread(buf, is_y1, s, kb);
+#pragma unroll
+        for (int fb = 0; fb < FB; ++fb)
+          out[kb][fb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(yop, xop[fb][s], out[kb][fb], 0, 0, 0);
+      }
+  };
+
+  // ---- the streamed loop: wait for tile t, start tile t+1, compute tile t ----
+  if (n_st > 0) {
+    issue(0);
+    stream_rows(0);
+  }
+  for (int t = 0; t < n_st; ++t) {
+    const int buf = t & 1;
+    wait_vmem();
+    __syncthreads();
+    if (t + 1 < n_st) {
+      issue(t + 1);
+      stream_rows(t + 1);
+    }
+    const int sbase = tile_first(t);
+    // does this wave see any (streamed, fixed) pair of the tile, and does the
+    // tile need per-element masks?
+    bool any = wave_active, need_mask;
+    if constexpr (!KV) {
+      const int wlast = min(fw0 + 16 * FB, nfixed) - 1;
+      if (CAUSAL) any = any && sbase <= off + wlast;
+      need_mask = sbase + BN > kl || (CAUSAL && sbase + BN - 1 > off + fw0);
+    } else {
+      const int wlast = min(fw0 + 16 * FB, nfixed) - 1;
+      if (CAUSAL) any = any && sbase + BN - 1 >= fw0 - off;
+      need_mask = sbase + BN > ql || (CAUSAL && sbase < wlast - off);
+    }
+    if (!any) continue;
+    const uint16_t* b1 = y1s[buf];
+    const uint16_t* b2 = y2s[buf];
+    f32x4 sacc[NKB][FB], dpacc[NKB][FB];
+    products(b1, true, x1op, sacc);
+    products(b2, false, x2op, dpacc);
+    bf16x8 pb[NKC][FB], dsb[NKC][FB];
+#pragma unroll
+    for (int fb = 0; fb < FB; ++fb) {
+      const int frow = fw0 + 16 * fb + c16;  // fixed row of this lane
+#pragma unroll
+      for (int j = 0; j < NKC; ++j)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int kb = 2 * j + (e >> 2), i = e & 3;
+          const int srel = 32 * (kb >> 1) + 8 * grp + 4 * (kb & 1) + i;  // streamed row in tile
+          const int sr = sbase + srel;
+          const float s = sacc[kb][fb][i];
+          float l2, dd;
+          if constexpr (KV) {
+            l2 = srow[buf][0][srel];
+            dd = srow[buf][1][srel];
+          } else {
+            l2 = l2f[fb];
+            dd = dfx[fb];
+          }
+          const int qi = KV ? sr : frow, kj = KV ? frow : sr;
+          bool vis = true;
+          if (need_mask) vis = (KV ? qi < ql : kj < kl) && (!CAUSAL || kj <= off + qi);
+          float x;
+          if constexpr (HAS_MASK) {
+            const int h = KV ? tile_head(t) : hf;
+            const float m = a.mask[((int64_t)(b * a.H + h) * ql + min(qi, ql - 1)) * kl +
+                                   min(kj, kl - 1)];
+            vis = vis && m != -INFINITY;
+            x = __builtin_fmaf(s, a.c, kLog2e * m) - l2;
+          } else {
+            x = __builtin_fmaf(s, a.c, -l2);
+          }
+          const float p = vis ? __builtin_amdgcn_exp2f(x) : 0.0f;
+          const float ds = p * (dpacc[kb][fb][i] - dd);
+          pb[j][fb][e] = (__bf16)p;
+          dsb[j][fb][e] = (__bf16)ds;
+          // (with a mask, one chunk's mask loads at a time: all of them in
+          // flight at once would not fit the registers)
+          if (HAS_MASK && e == 7) __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    // second products: dQ^T += Y1^T dS^T, or dK^T += Y1^T dS and dV^T += Y2^T P
+#pragma unroll
+    for (int d = 0; d < NDB; ++d)
+#pragma unroll
+      for (int j = 0; j < NKC; ++j) {
+        const bf16x8 t1 = tread(b1, true, d, j);
+#pragma unroll
+        for (int fb = 0; fb < FB; ++fb)
+          acc1[d][fb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(t1, dsb[j][fb], acc1[d][fb], 0, 0, 0);
+        if constexpr (KV) {
+          const bf16x8 t2 = tread(b2, false, d, j);
+#pragma unroll
+          for (int fb = 0; fb < FB; ++fb)
+            acc2[d][fb] =
+                __builtin_amdgcn_mfma_f32_16x16x32_bf16(t2, pb[j][fb], acc2[d][fb], 0, 0, 0);
+        }
+      }
+  }
+
+  // ---- epilogue: scale and store (fixed row c16 of block fb, dims 16d + 4grp + i) ----
+#pragma unroll
+  for (int fb = 0; fb < FB; ++fb) {
+    const int frow = fw0 + 16 * fb + c16;
+    if (!(wave_active && frow < nfixed)) continue;
+    uint16_t* d1 = KV ? a.dk + kv_base + (int64_t)frow * D : a.dq + ((int64_t)fhead * ql + frow) * D;
+#pragma unroll
+    for (int d = 0; d < NDB; ++d) {
+      bf16x4 ov;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ov[i] = (__bf16)(acc1[d][fb][i] * a.scale);
+      *reinterpret_cast<bf16x4*>(d1 + 16 * d + 4 * grp) = ov;
+    }
+    if constexpr (KV) {
+      uint16_t* d2 = a.dv + kv_base + (int64_t)frow * D;
+#pragma unroll
+      for (int d = 0; d < NDB; ++d) {
+        bf16x4 ov;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ov[i] = (__bf16)acc2[d][fb][i];
+        *reinterpret_cast<bf16x4*>(d2 + 16 * d + 4 * grp) = ov;
+      }
+    }
+  }
+  wait_vmem();  // no LDS copy may still be in flight when the workgroup ends
+#endif
+}
+
+template <int D, int PASS, bool CAUSAL, bool HAS_MASK>
+hipError_t launch_bwd(const BwdArgs& a, unsigned grid, hipStream_t stream) {
+  hipLaunchKernelGGL((fa_bwd_kernel<D, PASS, CAUSAL, HAS_MASK>), dim3(grid),
+                     dim3(64 * BwdCfg<D, PASS>::W), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <int D, bool CAUSAL, bool HAS_MASK>
+hipError_t dispatch_bwd(BwdArgs a, hipStream_t stream) {
+  if (a.ql > 0) {
+    a.n_ftiles = (a.ql + fixed_rows<D, kBwdQ>() - 1) / fixed_rows<D, kBwdQ>();
+    hipError_t e = launch_bwd<D, kBwdQ, CAUSAL, HAS_MASK>(
+        a, (unsigned)(a.n_ftiles * a.B * a.H), stream);
+    if (e != hipSuccess) return e;
+  }
+  if (a.kl > 0) {
+    a.n_ftiles = (a.kl + fixed_rows<D, kBwdKV>() - 1) / fixed_rows<D, kBwdKV>();
+    return launch_bwd<D, kBwdKV, CAUSAL, HAS_MASK>(a, (unsigned)(a.n_ftiles * a.B * a.Hkv),
+                                                  stream);
+  }
+  return hipSuccess;
+}
+
+template <int D>
+hipError_t dispatch_bwd_d(const BwdArgs& a, bool causal, bool has_mask, hipStream_t s) {
+  if (causal)
+    return has_mask ? dispatch_bwd<D, true, true>(a, s) : dispatch_bwd<D, true, false>(a, s);
+  return has_mask ? dispatch_bwd<D, false, true>(a, s) : dispatch_bwd<D, false, false>(a, s);
+}
+
+bool aligned_to(const void* p, uintptr_t n) { return ((uintptr_t)p % n) == 0; }
+
+}  // namespace
+
+extern "C" int fa_train_bwd(const void* q, const void* k, const void* v, const float* mask,
+                            const void* O, const float* L, const void* dO, int batch, int n_heads,
+                            int n_kv_heads, int ql, int kl, int head_dim, float scale, int causal,
+                            void* dQ, void* dK, void* dV, void* stream) {
+  if (batch < 0 || ql < 0 || kl < 0 || n_heads < 1 || n_kv_heads < 1) return FA_ERR_BAD_SIZE;
+  if (n_heads % n_kv_heads != 0) return FA_ERR_HEAD_GROUPING;
+  if (head_dim != 64 && head_dim != 256) return FA_ERR_HEAD_DIM;
+  if (!isfinite(scale)) return FA_ERR_SCALE;
+  const int64_t qrows = (int64_t)batch * n_heads * ql;
+  const int64_t krows = (int64_t)batch * n_kv_heads * kl;
+  if (qrows == 0 && krows == 0) return FA_OK;
+  if (qrows > 0 && (!q || !O || !L || !dO || !dQ)) return FA_ERR_NULL_POINTER;
+  if (krows > 0 && (!k || !v || !dK || !dV)) return FA_ERR_NULL_POINTER;
+  if (qrows > 0 && krows > 0 && (!q || !k || !v)) return FA_ERR_NULL_POINTER;
+  const void* a16[] = {q, k, v, O, dO, dQ, dK, dV};
+  for (const void* p : a16)
+    if (p && !aligned_to(p, 16)) return FA_ERR_ALIGNMENT;
+  if ((L && !aligned_to(L, 4)) || (mask && !aligned_to(mask, 4))) return FA_ERR_ALIGNMENT;
+  const int64_t rq = head_dim == 64 ? fixed_rows<64, kBwdQ>() : fixed_rows<256, kBwdQ>();
+  const int64_t rk = head_dim == 64 ? fixed_rows<64, kBwdKV>() : fixed_rows<256, kBwdKV>();
+  if ((ql + rq - 1) / rq * batch * n_heads > 0x7fffffffLL ||
+      (kl + rk - 1) / rk * batch * n_kv_heads > 0x7fffffffLL ||
+      (int64_t)kl * head_dim * 2 > 0x7fffffffLL || (int64_t)ql * head_dim * 2 > 0x7fffffffLL)
+    return FA_ERR_TOO_LARGE;
+
+  BwdArgs a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.o = static_cast<const uint16_t*>(O);
+  a.dO = static_cast<const uint16_t*>(dO);
+  a.L = L;
+  a.mask = mask;
+  a.dq = static_cast<uint16_t*>(dQ);
+  a.dk = static_cast<uint16_t*>(dK);
+  a.dv = static_cast<uint16_t*>(dV);
+  a.B = batch;
+  a.H = n_heads;
+  a.Hkv = n_kv_heads;
+  a.ql = ql;
+  a.kl = kl;
+  a.group = n_heads / n_kv_heads;
+  a.n_ftiles = 0;
+  a.causal_off = kl > ql ? kl - ql : 0;
+  a.scale = scale;
+  // a zero scale runs with the smallest normal exp2 factor (the scores it
+  // produces round to 0, so P is the same uniform one); dQ and dK use the
+  // true scale and come out 0
+  const float c = scale * kLog2e;
+  a.c = c == 0.0f ? FLT_MIN : c;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t err = head_dim == 64 ? dispatch_bwd_d<64>(a, causal != 0, mask != nullptr, s)
+                                        : dispatch_bwd_d<256>(a, causal != 0, mask != nullptr, s);
+  return err == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}

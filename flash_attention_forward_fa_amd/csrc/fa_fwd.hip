@@ -34,18 +34,9 @@
 #include <algorithm>
 
 #include "fa.h"
+#include "fa_common.h"
 
 namespace {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-typedef __attribute__((address_space(3))) void lds_void;
 
 // Per head dim: W waves per workgroup, QB 16-row query blocks per wave and BN
 // keys per tile. Eight waves (two per SIMD) share each K/V tile copy, which
@@ -83,8 +74,6 @@ constexpr float kLazy = 8.0f;
 // computes every row of every tile compensated (the masked forward).
 constexpr int kMixed = 0, kAll = 1;
 
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
 
 struct FwdArgs {
   const uint16_t* q;
@@ -104,124 +93,6 @@ struct FwdArgs {
   uint32_t q_sign; // 0x80008000 flips the sign of both bf16 halves (scale < 0)
 };
 
-__device__ __forceinline__ float swap32(float x, bool take_max) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  const float a = __uint_as_float(r[0]), b = __uint_as_float(r[1]);
-  return take_max ? __builtin_fmaxf(a, b) : a + b;
-}
-__device__ __forceinline__ float swap16(float x, bool take_max) {
-  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  const float a = __uint_as_float(r[0]), b = __uint_as_float(r[1]);
-  return take_max ? __builtin_fmaxf(a, b) : a + b;
-}
-// max / sum over the four 16-lane groups (lanes l, l^16, l^32, l^48)
-__device__ __forceinline__ float group_max(float x) { return swap16(swap32(x, true), true); }
-// group_max of two values at once: the first swap pairs the upper half of x
-// with the lower half of y, so one max reduces x in lanes 0-31 and y in lanes
-// 32-63; after the 16-lane step a last swap hands each half's result back to
-// all lanes.
-__device__ __forceinline__ void group_max2(float& x, float& y) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false, false);
-  const float h = __builtin_fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-  const float f = swap16(h, true);
-  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(f), __float_as_uint(f), false, false);
-  x = __uint_as_float(b[0]);
-  y = __uint_as_float(b[1]);
-}
-__device__ __forceinline__ float group_sum(float x) { return swap16(swap32(x, false), false); }
-
-// Row of a 32-key chunk that lane row m of key block kb (16 keys) loads as the
-// S^T A operand. With it, the four accumulators a lane of group g receives for
-// blocks 2j and 2j+1 are keys 32j + 8g + (0..7): exactly the B-operand order
-// of the P.V product, so P never moves between lanes.
-__device__ __forceinline__ int key_of(int kb, int m) {
-  return 32 * (kb >> 1) + 8 * (m >> 2) + 4 * (kb & 1) + (m & 3);
-}
-
-// LDS layouts (bf16, row-major [key][d], 16-byte chunks permuted per row):
-// chunk c of K row r sits at slot c ^ kswz<D>(r), chunk c of V row r at slot
-// c ^ vswz<D>(r). The permutations were chosen by measuring LDS bank-conflict
-// cycles (SQ_LDS_BANK_CONFLICT) for the exact access patterns of this kernel:
-// the K rows one ds_read_b128 reaches (keys key_of(kb, 0..15)) and the V rows
-// the 16-lane groups of one ds_read_b64_tr_b16 reach (four rows per group)
-// all come out conflict-free with these, for 128-byte (D=64) and 512-byte
-// (D=256) rows.
-template <int D> __device__ __forceinline__ int kswz(int r) {
-  return D == 64 ? ((r & 3) | ((r >> 1) & 4)) : ((r & 3) | ((r >> 1) & 12));
-}
-template <int D> __device__ __forceinline__ int vswz(int r) {
-  return D == 64 ? 2 * (((r >> 1) & 1) | ((r >> 2) & 2)) : 2 * ((r & 3) | ((r >> 1) & 4));
-}
-
-// Buffer resource word 3 for raw (untyped) buffer loads on gfx9-family parts.
-constexpr int kRsrcWord3 = 0x00020000;
-
-// Copy of one K or V tile (keys kbase .. kbase+BN-1) from HBM straight into an
-// LDS buffer with buffer_load_dwordx4 ... lds (no VGPR staging). Each thread
-// moves 16-byte chunks; a wave writes 1 KiB of consecutive LDS per
-// instruction, so a row's chunk permutation is realised by choosing which
-// global chunk each lane fetches. `off` holds this thread's byte offsets
-// within a full tile (computed once by copy_offsets); the buffer descriptor is
-// rebased on the tile so that the per-tile work is scalar. A tile that runs
-// past the last key repeats the last key's row (those keys are masked out).
-template <int D, int BN, int NT>
-struct CopyShape {
-  static constexpr int CH = D / 8;             // 16-byte chunks per row
-  static constexpr int ROUNDS = BN * CH / NT;  // chunks per thread
-  static_assert(ROUNDS * NT == BN * CH, "tile not a multiple of the workgroup");
-};
-
-template <int D, bool IS_K>
-__device__ __forceinline__ int chunk_offset(int p, int row) {
-  constexpr int CH = D / 8;
-  const int r = p / CH;
-  return (row * D + 8 * ((p % CH) ^ (IS_K ? kswz<D>(r) : vswz<D>(r)))) * 2;
-}
-
-template <int D, int BN, int NT, bool IS_K>
-__device__ __forceinline__ void copy_offsets(int tid, int (&off)[CopyShape<D, BN, NT>::ROUNDS]) {
-#pragma unroll
-  for (int u = 0; u < CopyShape<D, BN, NT>::ROUNDS; ++u) {
-    const int p = u * NT + tid;  // LDS slot (16-byte units)
-    off[u] = chunk_offset<D, IS_K>(p, p / (D / 8));
-  }
-}
-
-template <int D, int BN, int NT, bool IS_K>
-__device__ __forceinline__ void issue_tile(const uint16_t* src, int kbase, int kl, uint16_t* lds,
-                                           int tid, int wave_base,
-                                           const int (&off)[CopyShape<D, BN, NT>::ROUNDS]) {
-  constexpr int ROUNDS = CopyShape<D, BN, NT>::ROUNDS;
-  const int rows = kl - kbase;
-  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(src + (int64_t)kbase * D), 0, rows * D * 2, kRsrcWord3);
-  if (rows >= BN) {
-#pragma unroll
-    for (int u = 0; u < ROUNDS; ++u)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rs, (lds_void*)(lds + (u * NT + wave_base) * 8), 16, off[u], 0, 0, 0);
-  } else {
-#pragma unroll
-    for (int u = 0; u < ROUNDS; ++u) {
-      const int p = u * NT + tid;
-      const int o = chunk_offset<D, IS_K>(p, min(p / (D / 8), rows - 1));
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rs, (lds_void*)(lds + (u * NT + wave_base) * 8), 16, o, 0, 0, 0);
-    }
-  }
-}
-
-// Wave priority for the next instructions, pinned in place.
-template <int P> __device__ __forceinline__ void set_prio() {
-  __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_setprio(P);
-  __builtin_amdgcn_sched_barrier(0);
-}
-
-__device__ __forceinline__ void wait_vmem() {
-  // vmcnt(0); expcnt and lgkmcnt left at their maxima
-  __builtin_amdgcn_s_waitcnt(0x0F70);
-}
 
 // One query tile of one head: rows qtile * block_m .. of head bh. PRECISE
 // selects the compensated P.V product. Without it, a row whose result needs

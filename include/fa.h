@@ -1,5 +1,6 @@
 /*
- * fa.h - C ABI of the flash-attention training forward for AMD MI355X (gfx950).
+ * fa.h - C ABI of the flash-attention training forward (and its backward) for
+ * AMD MI355X (gfx950).
  *
  * The operation is the forward pass of softmax attention as used in training:
  * it returns the attention output O and, for the backward pass, the per-row
@@ -67,6 +68,42 @@ enum fa_status {
 int fa_train_fwd(const void *q, const void *k, const void *v, const float *mask, int batch,
                  int n_heads, int n_kv_heads, int ql, int kl, int head_dim, float scale,
                  int causal, void *O, float *L, void *stream);
+
+/*
+ * fa_train_bwd - enqueue the training backward pass of the same attention.
+ *
+ * Computes the gradients of a loss with upstream gradient dO = dLoss/dO, as
+ * the FA-2 backward oracle of the method's page does ("mlx-native 0.9.0",
+ * tests/test_flash_attn_train.rs, section "Phase 2 - backward kernel
+ * helpers", sdpa_backward_reference_f32), with the forward's causal rule:
+ *
+ *   P_ij  = exp(s_ij - L_i)  (s_ij as in fa_train_fwd; 0 for a hidden key)
+ *   D_i   = sum_d O_id dO_id,   dS_ij = P_ij (dO_i . v_j - D_i)
+ *   dQ_i  = scale * sum_j dS_ij k_j,   dK_j = scale * sum_i dS_ij q_i,
+ *   dV_j  = sum_i P_ij dO_i      (dK, dV summed over every query head of a
+ *                                  kv head's group)
+ *
+ *   q, k, v, mask, batch .. causal: as for fa_train_fwd (same meaning, same
+ *         layouts and constraints).
+ *   O     bf16 bits [batch, n_heads, ql, head_dim]: the forward's output (read).
+ *   L     f32 [batch, n_heads, ql]: the forward's logsumexp (read); -inf rows
+ *         (no visible key) give zero gradients.
+ *   dO    bf16 bits [batch, n_heads, ql, head_dim] (read).
+ *   dQ    bf16 bits [batch, n_heads, ql, head_dim] (written, fully).
+ *   dK    bf16 bits [batch, n_kv_heads, kl, head_dim] (written, fully).
+ *   dV    bf16 bits [batch, n_kv_heads, kl, head_dim] (written, fully).
+ *   stream hipStream_t to enqueue on (NULL: the default stream).
+ *
+ * Two kernel launches on `stream` (dQ, then dK and dV); no atomics, so the
+ * result is deterministic. Same validation and status codes as fa_train_fwd
+ * (all of q, k, v, O, L, dO, dQ, dK, dV are required for non-empty tensors;
+ * 16-byte alignment for the bf16 buffers). The library allocates nothing and
+ * never synchronises. Buffers must not overlap.
+ */
+int fa_train_bwd(const void *q, const void *k, const void *v, const float *mask, const void *O,
+                 const float *L, const void *dO, int batch, int n_heads, int n_kv_heads, int ql,
+                 int kl, int head_dim, float scale, int causal, void *dQ, void *dK, void *dV,
+                 void *stream);
 
 /* Static, human-readable name of a status code (never NULL). */
 const char *fa_status_string(int status);

@@ -28,7 +28,7 @@ def _declared_functions():
 
 def test_header_declares_the_entry_points():
     names = _declared_functions()
-    assert {"fa_train_fwd", "fa_status_string"} <= names
+    assert {"fa_train_fwd", "fa_train_bwd", "fa_status_string"} <= names
 
 
 def test_library_exports_every_declared_symbol():
@@ -86,3 +86,42 @@ def test_python_binding_fails_loudly_without_gpu_tensors():
         fa.train_fwd(q, q, q)
     with pytest.raises(TypeError):
         fa.train_fwd(q.float(), q, q)
+
+
+BWD_GOOD = dict(q=A, k=A, v=A, mask=0, O=A, L=A, dO=A, batch=1, n_heads=2, n_kv_heads=1, ql=8,
+                kl=8, head_dim=64, scale=0.125, causal=0, dQ=A, dK=A, dV=A, stream=0)
+
+
+def _call_bwd(**over):
+    args = dict(BWD_GOOD)
+    args.update(over)
+    return fa.fa_train_bwd(**args)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(q=0), 1), (dict(k=0), 1), (dict(v=0), 1), (dict(O=0), 1), (dict(L=0), 1),
+    (dict(dO=0), 1), (dict(dQ=0), 1), (dict(dK=0), 1), (dict(dV=0), 1),
+    (dict(batch=-1), 2), (dict(ql=-1), 2), (dict(kl=-3), 2), (dict(n_heads=0), 2),
+    (dict(n_kv_heads=0), 2), (dict(n_heads=3, n_kv_heads=2), 3), (dict(head_dim=128), 4),
+    (dict(scale=math.nan), 5), (dict(scale=-math.inf), 5), (dict(q=A + 2), 6),
+    (dict(dO=A + 8), 6), (dict(dK=A + 4), 6), (dict(dV=A + 2), 6), (dict(mask=A + 2), 6),
+    (dict(L=A + 1), 6), (dict(batch=65536, n_heads=65536, n_kv_heads=1, ql=1), 7),
+])
+def test_backward_invalid_arguments_are_rejected(over, code):
+    assert _call_bwd(**over) == code
+
+
+@pytest.mark.parametrize("over", [dict(batch=0), dict(ql=0, kl=0),
+                                  dict(batch=0, q=0, k=0, v=0, O=0, L=0, dO=0, dQ=0, dK=0, dV=0)])
+def test_backward_empty_problems_are_noops(over):
+    assert _call_bwd(**over) == 0
+
+
+def test_backward_binding_fails_loudly_without_gpu_tensors():
+    import torch
+    q = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
+    L = torch.zeros(1, 1, 4)
+    with pytest.raises(ValueError):
+        fa.train_bwd(q, q, q, q, L, q)
+    with pytest.raises(TypeError):
+        fa.train_bwd(q.float(), q, q, q, L, q)

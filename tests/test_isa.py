@@ -1,4 +1,4 @@
-"""Checks on the gfx950 machine code of the forward kernels (no GPU needed:
+"""Checks on the gfx950 machine code of the forward and backward kernels (no GPU needed:
 hipcc cross-compiles the kernels to assembly here).
 
 - No v_mfma instruction may be reachable inside an EXEC-masked region
@@ -22,15 +22,17 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 @pytest.fixture(scope="module")
 def isa(tmp_path_factory):
     from flash_attention_forward_fa_amd import build
-    out = tmp_path_factory.mktemp("isa") / "fa_fwd.s"
     flags = [f for f in build.FLAGS if f not in ("-fPIC", "-shared")]
-    subprocess.run([build.HIPCC, *flags, "--cuda-device-only", "-S", "-o", str(out),
-                    *build.SOURCES], check=True, capture_output=True)
-    text = out.read_text()
+    text = ""
+    for src in build.SOURCES:
+        out = tmp_path_factory.mktemp("isa") / (os.path.basename(src) + ".s")
+        subprocess.run([build.HIPCC, *flags, "--cuda-device-only", "-S", "-o", str(out), src],
+                       check=True, capture_output=True)
+        text += out.read_text() + "\n"
     kernels = {}
     name = None
     for line in text.split("\n"):
-        m = re.match(r"^(_Z\w*fa_fwd_kernel\w+):", line)
+        m = re.match(r"^(_Z\w*fa_(?:fwd|bwd)_kernel\w+):", line)
         if m:
             name = m.group(1)
             kernels[name] = []
@@ -40,7 +42,10 @@ def isa(tmp_path_factory):
 
 
 def test_all_variants_present(isa):
-    assert len(isa) == 8  # head_dim x causal x {mixed plain/compensated, compensated masked}
+    fwd = [n for n in isa if "fa_fwd_kernel" in n]
+    bwd = [n for n in isa if "fa_bwd_kernel" in n]
+    assert len(fwd) == 8  # head_dim x causal x {mixed plain/compensated, compensated masked}
+    assert len(bwd) == 16  # head_dim x {dQ, dKV} x causal x mask
 
 
 _OPEN = (re.compile(r"s_(?:and|andn2|or)_saveexec_b64 (s\[\d+:\d+\])"),
