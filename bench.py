@@ -84,6 +84,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="both")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--backward-steps", type=int, default=10,
+                    help="timed backward calls per workload after the forward (0: none)")
     ap.add_argument("--cpu-rows", type=int, default=0,
                     help="rows per workload for the CPU baseline (0: default sample)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -144,6 +146,33 @@ def main():
     wall = time.perf_counter() - t_wall
     log(f"timed: {args.steps} steps in {wall:.3f} s wall")
 
+    # The backward of the same calls (not part of the headline metric): its own
+    # HIP-event timing, fewer steps, the forward's O and L as inputs and a
+    # seeded upstream gradient.
+    bwd = {}
+    if args.backward_steps > 0:
+        for w in workloads:
+            q, k, v = dev_inputs[w.name]
+            O, L = outputs[w.name]
+            dO = torch.from_numpy(fagen.normal_bf16(w.seed, 6, (w.B, w.H, w.ql, w.D))
+                                  .view(np.int16)).view(torch.bfloat16).to(dev)
+            for _ in range(3):
+                fa.train_bwd(q, k, v, O, L, dO, scale=w.scale, causal=w.causal)
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(args.backward_steps):
+                fa.train_bwd(q, k, v, O, L, dO, scale=w.scale, causal=w.causal)
+            b.record(stream)
+            torch.cuda.synchronize()
+            ms = a.elapsed_time(b) / args.backward_steps
+            # the FA-2 count: dQ, dK, dV, dP and the recomputed S, 2.5x the forward
+            flop = 2.5 * w.metric_flop
+            bwd[w.name] = {"ms_avg": ms, "flop_fa2": flop, "tflops": flop / (ms * 1e-3) / 1e12,
+                           "frac_of_peak": flop / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+            log(f"{w.name}: backward {ms * 1e3:.1f} us/call, {bwd[w.name]['tflops']:.1f} TFLOP/s "
+                f"(FA-2 count)")
+
     if args.copy_calibration:
         n = args.copy_calibration * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device=dev)
@@ -195,6 +224,8 @@ def main():
         "per_workload": per,
         "roofline": roofline,
     }
+    if bwd:
+        result["backward"] = bwd
     if not args.no_cpu_baseline:
         target = {w.name: (args.cpu_rows or (524288 if w.D == 64 else 65536)) for w in workloads}
         result["cpu_baseline"] = cpu_baseline(workloads, inputs, target)
