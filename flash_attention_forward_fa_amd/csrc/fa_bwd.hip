@@ -48,12 +48,13 @@ namespace {
 constexpr int kBwdQ = 0, kBwdKV = 1;
 
 // Per head dim and pass: W waves, FB fixed 16-row blocks per wave, BN streamed
-// rows per tile, WPE waves per SIMD (register budget).
+// rows per tile, WPE waves per SIMD (register budget). The D=256 dK/dV pass
+// streams three tiles (Q, dO, O) through 96 KiB of LDS in 32-row tiles.
 template <int D, int PASS> struct BwdCfg;
 template <> struct BwdCfg<64, kBwdQ> { static constexpr int W = 8, FB = 2, BN = 64, WPE = 2; };
 template <> struct BwdCfg<64, kBwdKV> { static constexpr int W = 8, FB = 2, BN = 64, WPE = 2; };
 template <> struct BwdCfg<256, kBwdQ> { static constexpr int W = 8, FB = 1, BN = 64, WPE = 2; };
-template <> struct BwdCfg<256, kBwdKV> { static constexpr int W = 4, FB = 1, BN = 64, WPE = 1; };
+template <> struct BwdCfg<256, kBwdKV> { static constexpr int W = 4, FB = 1, BN = 32, WPE = 1; };
 template <int D, int PASS> constexpr int fixed_rows() {
   return BwdCfg<D, PASS>::W * 16 * BwdCfg<D, PASS>::FB;
 }
@@ -98,7 +99,8 @@ __attribute__((amdgpu_waves_per_eu(BwdCfg<D, PASS>::WPE))) void fa_bwd_kernel(Bw
   constexpr bool KV = PASS == kBwdKV;
   __shared__ __attribute__((aligned(1024))) uint16_t y1s[2][TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t y2s[2][TILE];
-  __shared__ float srow[2][2][BN];  // dKV pass: L2 and D of the streamed rows
+  __shared__ __attribute__((aligned(1024))) uint16_t yos[2][KV ? TILE : 8];  // dKV pass: O
+  __shared__ float srow[2][BN];  // dKV pass: L2 and D of the streamed rows
 
   const int tid = threadIdx.x;
   // wave-uniform wave index: every wave-level condition is a scalar branch
@@ -203,30 +205,35 @@ __attribute__((amdgpu_waves_per_eu(BwdCfg<D, PASS>::WPE))) void fa_bwd_kernel(Bw
     issue_tile<D, BN, NT, true>(y1_src(t), tile_first(t), nstream, y1s[buf], tid, 64 * wave, y1off);
     issue_tile<D, BN, NT, false>(y2_src(t), tile_first(t), nstream, y2s[buf], tid, 64 * wave,
                                  y2off);
+    if constexpr (KV)
+      issue_tile<D, BN, NT, false>(a.o + (int64_t)(b * a.H + tile_head(t)) * ql * D, tile_first(t),
+                                   nstream, yos[buf], tid, 64 * wave, y2off);
   };
-  // dKV pass: L2 and D of the streamed rows of tile t into srow[t & 1]
-  // (NT / BN threads per row, each summing D / (NT / BN) dims)
-  auto stream_rows = [&](int t) {
+  // dKV pass: L2 and D of the streamed rows of tile t (landed in LDS) into
+  // srow (NT / BN threads per row, each summing D / (NT / BN) dims of O * dO)
+  auto stream_rows = [&](int t, int sbase, int th) {
     if constexpr (KV) {
       constexpr int TPR = NT / BN;
       constexpr int DPT = D / TPR;
       const int r = tid / TPR, part = tid % TPR;
-      const int qi = min(tile_first(t) + r, ql - 1);
-      const int64_t row = (int64_t)(b * a.H + tile_head(t)) * ql + qi;
+      const int buf = t & 1;
+      const int qi = min(sbase + r, ql - 1);
+      const float lv = a.L[(int64_t)(b * a.H + th) * ql + qi];
       float acc = 0.0f;
 #pragma unroll
       for (int c = 0; c < DPT / 8; ++c) {
-        const int64_t at = row * D + part * DPT + 8 * c;
-        const bf16x8 ov = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(a.o + at));
-        const bf16x8 gv = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(a.dO + at));
+        const int ch = part * (DPT / 8) + c;  // 16-byte chunk of the row
+        const int slot = r * D + 8 * (ch ^ vswz<D>(r));
+        const bf16x8 ov = *reinterpret_cast<const bf16x8*>(&yos[buf][slot]);
+        const bf16x8 gv = *reinterpret_cast<const bf16x8*>(&y2s[buf][slot]);
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc += (float)ov[e] * (float)gv[e];
       }
 #pragma unroll
       for (int m = 1; m < TPR; m <<= 1) acc += __shfl_xor(acc, m, 64);
       if (part == 0) {
-        srow[t & 1][0][r] = lse2(a.L[row]);
-        srow[t & 1][1][r] = acc;
+        srow[0][r] = lse2(lv);
+        srow[1][r] = acc;
       }
     }
   };
@@ -271,19 +278,19 @@ __attribute__((amdgpu_waves_per_eu(BwdCfg<D, PASS>::WPE))) void fa_bwd_kernel(Bw
   };
 
   // ---- the streamed loop: wait for tile t, start tile t+1, compute tile t ----
-  if (n_st > 0) {
-    issue(0);
-    stream_rows(0);
-  }
+  if (n_st > 0) issue(0);
   for (int t = 0; t < n_st; ++t) {
     const int buf = t & 1;
     wait_vmem();
     __syncthreads();
-    if (t + 1 < n_st) {
-      issue(t + 1);
-      stream_rows(t + 1);
+    if (t + 1 < n_st) issue(t + 1);
+    // (made provably uniform: every wave-level decision below depends on them)
+    const int sbase = __builtin_amdgcn_readfirstlane(tile_first(t));
+    const int th = __builtin_amdgcn_readfirstlane(tile_head(t));
+    if constexpr (KV) {
+      stream_rows(t, sbase, th);
+      __syncthreads();
     }
-    const int sbase = tile_first(t);
     // does this wave see any (streamed, fixed) pair of the tile, and does the
     // tile need per-element masks?
     bool any = wave_active, need_mask;
@@ -316,8 +323,8 @@ __attribute__((amdgpu_waves_per_eu(BwdCfg<D, PASS>::WPE))) void fa_bwd_kernel(Bw
           const float s = sacc[kb][fb][i];
           float l2, dd;
           if constexpr (KV) {
-            l2 = srow[buf][0][srel];
-            dd = srow[buf][1][srel];
+            l2 = srow[0][srel];
+            dd = srow[1][srel];
           } else {
             l2 = l2f[fb];
             dd = dfx[fb];
@@ -327,7 +334,7 @@ __attribute__((amdgpu_waves_per_eu(BwdCfg<D, PASS>::WPE))) void fa_bwd_kernel(Bw
           if (need_mask) vis = (KV ? qi < ql : kj < kl) && (!CAUSAL || kj <= off + qi);
           float x;
           if constexpr (HAS_MASK) {
-            const int h = KV ? tile_head(t) : hf;
+            const int h = KV ? th : hf;
             const float m = a.mask[((int64_t)(b * a.H + h) * ql + min(qi, ql - 1)) * kl +
                                    min(kj, kl - 1)];
             vis = vis && m != -INFINITY;
