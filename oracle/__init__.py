@@ -31,6 +31,9 @@ def _bind(path):
                                        ctypes.c_float, ctypes.c_int, vp, i64, vp, vp,
                                        ctypes.c_int]
     lib.fa_oracle_fwd_rows.restype = ctypes.c_int
+    lib.fa_oracle_fwd_swa.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, i64,
+                                      ctypes.c_float, i64, vp, i64, vp, vp, ctypes.c_int]
+    lib.fa_oracle_fwd_swa.restype = ctypes.c_int
     lib.fa_oracle_round_bf16.argtypes = [vp, vp, i64]
     lib.fa_oracle_round_bf16.restype = None
     lib.fa_oracle_bwd.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64,
@@ -86,14 +89,22 @@ def _check(rc, what):
         raise ValueError(f"{what} rejected its arguments (code {rc})")
 
 
-def fwd(q, k, v, mask, B, H, Hkv, ql, kl, D, scale, causal, n_threads=None, lib=None):
+def fwd(q, k, v, mask, B, H, Hkv, ql, kl, D, scale, causal, n_threads=None, lib=None,
+        window=None):
     """Full forward. q/k/v: bf16 bits (uint16) or float32 arrays; mask f32 or None.
+    window: None, or a sliding window (>= 0, implies the causal rule).
 
     Returns (O_f32 [B,H,ql,D], O_bf16_bits [B,H,ql,D], L [B,H,ql])."""
     qf, kf, vf, mf = _f32(q), _f32(k), _f32(v), _f32(mask)
     O = np.empty((B, H, ql, D), dtype=np.float32)
     L = np.empty((B, H, ql), dtype=np.float32)
     lib = lib or _load()
+    if window is not None:
+        rc = lib.fa_oracle_fwd_swa(_ptr(qf), _ptr(kf), _ptr(vf), _ptr(mf), B, H, Hkv, ql, kl,
+                                   D, float(scale), int(window), None, 0, _ptr(O), _ptr(L),
+                                   n_threads or default_threads())
+        _check(rc, "fa_oracle_fwd_swa")
+        return O, round_bf16(O, lib), L
     rc = lib.fa_oracle_fwd(_ptr(qf), _ptr(kf), _ptr(vf), _ptr(mf), B, H, Hkv, ql, kl, D,
                                float(scale), int(bool(causal)), _ptr(O), _ptr(L),
                                n_threads or default_threads())
@@ -102,7 +113,7 @@ def fwd(q, k, v, mask, B, H, Hkv, ql, kl, D, scale, causal, n_threads=None, lib=
 
 
 def fwd_rows(q, k, v, mask, B, H, Hkv, ql, kl, D, scale, causal, rows, n_threads=None,
-             lib=None):
+             lib=None, window=None):
     """Selected flat rows ((b*H + h)*ql + i). Returns (O_f32 [n,D], O_bf16 [n,D], L [n])."""
     qf, kf, vf, mf = _f32(q), _f32(k), _f32(v), _f32(mask)
     rows = np.ascontiguousarray(rows, dtype=np.int64)
@@ -110,6 +121,12 @@ def fwd_rows(q, k, v, mask, B, H, Hkv, ql, kl, D, scale, causal, rows, n_threads
     O = np.empty((n, D), dtype=np.float32)
     L = np.empty((n,), dtype=np.float32)
     lib = lib or _load()
+    if window is not None:
+        rc = lib.fa_oracle_fwd_swa(_ptr(qf), _ptr(kf), _ptr(vf), _ptr(mf), B, H, Hkv, ql, kl,
+                                   D, float(scale), int(window), rows.ctypes.data, n, _ptr(O),
+                                   _ptr(L), n_threads or default_threads())
+        _check(rc, "fa_oracle_fwd_swa")
+        return O, round_bf16(O, lib), L
     rc = lib.fa_oracle_fwd_rows(_ptr(qf), _ptr(kf), _ptr(vf), _ptr(mf), B, H, Hkv, ql, kl,
                                     D, float(scale), int(bool(causal)), _ptr(rows), n, _ptr(O),
                                     _ptr(L), n_threads or default_threads())
@@ -156,10 +173,10 @@ def bind_bwd(lib_path):
     return f
 
 
-def fwd_workload(w, inputs, rows=None, n_threads=None):
+def fwd_workload(w, inputs, rows=None, n_threads=None, window=None):
     """Oracle on a fagen.Workload and its generated inputs (all rows, or `rows`)."""
     args = (inputs["q"], inputs["k"], inputs["v"], inputs["mask"],
             w.B, w.H, w.Hkv, w.ql, w.kl, w.D, w.scale, w.causal)
     if rows is None:
-        return fwd(*args, n_threads=n_threads)
-    return fwd_rows(*args, rows, n_threads=n_threads)
+        return fwd(*args, n_threads=n_threads, window=window)
+    return fwd_rows(*args, rows, n_threads=n_threads, window=window)

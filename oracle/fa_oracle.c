@@ -14,6 +14,7 @@
  *     s_j = (sum_d q[i,d] * k[j,d]) * (scale * log2 e)       dot left to right
  *     s_j += log2 e * mask[i,j]                               if a mask is given
  *     s_j = -inf   for j > max(kl - ql, 0) + i                if causal
+ *     s_j = -inf   for j < max(kl - ql, 0) + i - window       sliding window
  *     m   = max(-FLT_MAX / 2, max_j s_j)                      finite sentinel
  *     p_j = exp2(s_j - m),  S = sum_j p_j                     left to right
  *     L_i = m * ln 2 + ln S                                   (S = 0 -> -inf)
@@ -24,6 +25,13 @@
  * clamped at zero, as on the page (kl.saturating_sub(ql) + q_pos). O is
  * returned in f32; fa_oracle_round_bf16 rounds it to bf16 the way the page's
  * oracle_for_bf16 helper does before comparing against a bf16 output.
+ *
+ * Sliding window (the same page, section 7, "SLIDING-WINDOW MASK (SWA)
+ * PARITY"): the page builds it as an additive mask that keeps key j for row i
+ * iff j <= i and j + window >= i. fa_oracle_fwd_swa applies that predicate
+ * directly, with the causal rule's bottom-right alignment (i replaced by
+ * q_abs = max(kl - ql, 0) + i, the same position the causal rule uses; the
+ * two agree when ql = kl, the page's case): window + 1 keys at most.
  *
  * Arithmetic is IEEE f32 with no contraction (built with -ffp-contract=off),
  * exp2f/logf from the C library.
@@ -58,6 +66,7 @@ typedef struct {
     int64_t H, Hkv, ql, kl, D;
     float scale;
     int causal;
+    int64_t window; /* < 0: no sliding window */
 } oracle_problem;
 
 /* One query row, flat index row = (b*H + h)*ql + i. o_row gets D floats. */
@@ -88,10 +97,15 @@ static void oracle_row(const oracle_problem *p, int64_t row, float *o_row, float
         for (int64_t j = 0; j < kl; ++j)
             s[j] += ORACLE_LOG2E * mr[j];
     }
-    /* causal: key j is visible to row i iff j <= max(kl - ql, 0) + i */
+    /* causal: key j is visible to row i iff j <= q_abs = max(kl - ql, 0) + i */
+    const int64_t q_abs = (kl > ql ? kl - ql : 0) + i;
     if (p->causal) {
-        const int64_t q_abs = (kl > ql ? kl - ql : 0) + i;
         for (int64_t j = q_abs + 1; j < kl; ++j)
+            s[j] = -INFINITY;
+    }
+    /* sliding window: keys more than `window` positions before q_abs are hidden */
+    if (p->window >= 0) {
+        for (int64_t j = 0; j < q_abs - p->window && j < kl; ++j)
             s[j] = -INFINITY;
     }
     /* row max with the finite sentinel -FLT_MAX/2 */
@@ -213,7 +227,7 @@ int fa_oracle_fwd(const float *q, const float *k, const float *v, const float *m
     int rc = oracle_validate(q, k, v, B, H, Hkv, ql, kl, D);
     if (rc)
         return rc;
-    oracle_problem p = {q, k, v, mask, H, Hkv, ql, kl, D, scale, causal};
+    oracle_problem p = {q, k, v, mask, H, Hkv, ql, kl, D, scale, causal, -1};
     return oracle_run(&p, NULL, B * H * ql, O, L, n_threads);
 }
 
@@ -235,7 +249,34 @@ int fa_oracle_fwd_rows(const float *q, const float *k, const float *v, const flo
     for (int64_t t = 0; t < n_rows; ++t)
         if (rows[t] < 0 || rows[t] >= B * H * ql)
             return 2;
-    oracle_problem p = {q, k, v, mask, H, Hkv, ql, kl, D, scale, causal};
+    oracle_problem p = {q, k, v, mask, H, Hkv, ql, kl, D, scale, causal, -1};
+    return oracle_run(&p, rows, n_rows, O, L, n_threads);
+}
+
+/*
+ * Sliding-window causal forward: key j is visible to row i iff
+ * q_abs - window <= j <= q_abs, q_abs = max(kl - ql, 0) + i, window >= 0
+ * (plus the additive mask when one is given). rows == NULL computes every
+ * row (O [B,H,ql,D], L [B,H,ql]); otherwise the n_rows flat rows listed
+ * (O [n_rows,D], L [n_rows]). Return codes as fa_oracle_fwd_rows, plus 2 for
+ * a negative window.
+ */
+int fa_oracle_fwd_swa(const float *q, const float *k, const float *v, const float *mask,
+                      int64_t B, int64_t H, int64_t Hkv, int64_t ql, int64_t kl, int64_t D,
+                      float scale, int64_t window, const int64_t *rows, int64_t n_rows,
+                      float *O, float *L, int n_threads)
+{
+    int rc = oracle_validate(q, k, v, B, H, Hkv, ql, kl, D);
+    if (rc)
+        return rc;
+    if (window < 0)
+        return 2;
+    oracle_problem p = {q, k, v, mask, H, Hkv, ql, kl, D, scale, 1, window};
+    if (!rows)
+        return oracle_run(&p, NULL, B * H * ql, O, L, n_threads);
+    for (int64_t t = 0; t < n_rows; ++t)
+        if (rows[t] < 0 || rows[t] >= B * H * ql)
+            return 2;
     return oracle_run(&p, rows, n_rows, O, L, n_threads);
 }
 

@@ -5,13 +5,15 @@ the oracle (never the GPU path's arithmetic, never the oracle's code).
 
 in natural exp/log, with key j visible to query row i under the causal rule
 iff j <= max(kl - ql, 0) + i (the page's bottom-right alignment, offset
-clamped at zero). A row with no visible key gives O = 0 and L = -inf.
+clamped at zero). With a sliding window w (which implies the causal rule),
+key j is visible iff off + i - w <= j <= off + i, off = max(kl - ql, 0).
+A row with no visible key gives O = 0 and L = -inf.
 GQA: query head h reads kv head h // (H // Hkv).
 """
 import numpy as np
 
 
-def attention_f64(q, k, v, mask, scale, causal):
+def attention_f64(q, k, v, mask, scale, causal, window=None):
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
@@ -27,10 +29,12 @@ def attention_f64(q, k, v, mask, scale, causal):
             s = scale * (q[b, h] @ k[b, kvh].T)
             if mask is not None:
                 s = s + np.asarray(mask[b, h], dtype=np.float64)
-            if causal:
-                i = np.arange(ql)[:, None]
-                j = np.arange(kl)[None, :]
+            i = np.arange(ql)[:, None]
+            j = np.arange(kl)[None, :]
+            if causal or window is not None:
                 s = np.where(j > off + i, -np.inf, s)
+            if window is not None:
+                s = np.where(j < off + i - window, -np.inf, s)
             for i in range(ql):
                 row = s[i]
                 if kl == 0 or not np.isfinite(row).any():

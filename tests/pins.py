@@ -41,12 +41,13 @@ def _finite_mask(seed, B, H, ql, kl, p=0.2):
     return np.where(np.isneginf(m), -np.inf, vals).astype(np.float32)
 
 
-def pin_brute_force(fwd, B, H, Hkv, ql, kl, D, causal, masked, seed, scale=None):
+def pin_brute_force(fwd, B, H, Hkv, ql, kl, D, causal, masked, seed, scale=None, window=None):
     scale = 1.0 / math.sqrt(D) if scale is None else scale
     q, k, v = _inputs(seed, B, H, Hkv, ql, kl, D)
     mask = _finite_mask(seed, B, H, ql, kl) if masked else None
-    O, Ob, L = fwd(q, k, v, mask, B, H, Hkv, ql, kl, D, scale, causal)
-    Oref, Lref = attention_f64(_widen(q), _widen(k), _widen(v), mask, scale, causal)
+    kw = {} if window is None else {"window": window}
+    O, Ob, L = fwd(q, k, v, mask, B, H, Hkv, ql, kl, D, scale, causal, **kw)
+    Oref, Lref = attention_f64(_widen(q), _widen(k), _widen(v), mask, scale, causal, window)
     empty = np.isneginf(Lref)
     assert np.array_equal(np.isneginf(L), empty), "fully masked rows differ"
     assert np.all(O[empty] == 0) and not np.signbit(O[empty]).any(), "empty row O != +0"
@@ -238,6 +239,82 @@ def pin_dominant_key(fwd):
     assert np.isfinite(L).all() and np.isfinite(O).all()
 
 
+def swa_mask(B, H, ql, kl, window):
+    """The page's sliding-window additive mask (section 7): 0 where
+    j <= q_abs and j + window >= q_abs, -inf elsewhere, with q_abs = i + the
+    causal offset max(kl - ql, 0)."""
+    off = max(kl - ql, 0)
+    i = np.arange(ql)[:, None] + off
+    j = np.arange(kl)[None, :]
+    keep = (j <= i) & (j + window >= i)
+    m = np.where(keep, 0.0, -np.inf).astype(np.float32)
+    return np.broadcast_to(m, (B, H, ql, kl)).copy()
+
+
+def pin_window_is_the_page_mask(fwd):
+    """A native window gives bit-for-bit what the page's construction gives:
+    the same predicate written into an additive 0/-inf mask, run without the
+    causal flag (adding 0 leaves a score unchanged; -inf hides it)."""
+    for (ql, kl, w) in [(20, 20, 5), (9, 23, 3), (23, 9, 4), (12, 12, 0), (7, 7, 30)]:
+        B, H, Hkv, D = 1, 4, 2, 8
+        q, k, v = _inputs(300 + ql + kl + w, B, H, Hkv, ql, kl, D)
+        a = fwd(q, k, v, None, B, H, Hkv, ql, kl, D, 0.4, True, window=w)
+        b = fwd(q, k, v, swa_mask(B, H, ql, kl, w), B, H, Hkv, ql, kl, D, 0.4, False)
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[2], b[2]), (ql, kl, w)
+
+
+def pin_window_alignment(fwd):
+    """Key j is visible to row i iff q_abs - w <= j <= q_abs: perturbing V row
+    j changes exactly those rows, bit for bit (Q = 0, so every visible key
+    weighs 1/n_i and no change can hide in rounding)."""
+    D = 8
+    for ql, kl, w in [(6, 10, 2), (10, 6, 3), (8, 8, 0), (8, 8, 4)]:
+        B, H, Hkv = 1, 1, 1
+        _, k, v = _inputs(51 + ql + w, B, H, Hkv, ql, kl, D)
+        q = np.zeros((B, H, ql, D), np.uint16)
+        off = max(kl - ql, 0)
+        base = fwd(q, k, v, None, B, H, Hkv, ql, kl, D, 0.5, True, window=w)[0]
+        for j in range(kl):
+            vp = v.copy()
+            vp[0, 0, j] = _bf16_bits(np.array([7.0], np.float32))[0]
+            out = fwd(q, k, vp, None, B, H, Hkv, ql, kl, D, 0.5, True, window=w)[0]
+            for i in range(ql):
+                changed = not np.array_equal(out[0, 0, i], base[0, 0, i])
+                assert changed == (off + i - w <= j <= off + i), (ql, kl, w, i, j)
+
+
+def pin_window_zero(fwd):
+    """window = 0: each row sees only key q_abs, so O is that V row exactly and
+    L its natural-log score scale * q.k (rows with q_abs >= kl see nothing)."""
+    B, H, Hkv, D = 1, 2, 1, 16
+    for ql, kl in [(9, 9), (5, 11), (11, 5)]:
+        q, k, v = _inputs(61 + ql, B, H, Hkv, ql, kl, D)
+        O, Ob, L = fwd(q, k, v, None, B, H, Hkv, ql, kl, D, 0.25, True, window=0)
+        off = max(kl - ql, 0)
+        qf, kf = _widen(q).astype(np.float64), _widen(k).astype(np.float64)
+        for h in range(H):
+            for i in range(ql):
+                j = off + i
+                if j >= kl:
+                    assert np.isneginf(L[0, h, i]) and np.all(O[0, h, i] == 0)
+                    continue
+                assert np.array_equal(Ob[0, h, i], v[0, 0, j]), (h, i)
+                s = 0.25 * float(qf[0, h, i] @ kf[0, 0, j])
+                assert abs(L[0, h, i] - s) <= 1e-5 * max(1.0, abs(s)), (h, i, L[0, h, i], s)
+
+
+def pin_window_wide_is_causal(fwd):
+    """A window at least as wide as every row's visible range hides nothing the
+    causal rule leaves visible: bit-identical to the causal forward."""
+    B, H, Hkv, ql, kl, D = 2, 2, 1, 10, 14, 8
+    q, k, v = _inputs(71, B, H, Hkv, ql, kl, D)
+    mask = _finite_mask(72, B, H, ql, kl)
+    for w in (kl - 1, kl, 10 * kl):
+        a = fwd(q, k, v, mask, B, H, Hkv, ql, kl, D, 0.3, True, window=w)
+        b = fwd(q, k, v, mask, B, H, Hkv, ql, kl, D, 0.3, True)
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[2], b[2]), w
+
+
 ALL_PINS = [
     ("hand_worked", pin_hand_worked),
     ("brute_small", lambda f: pin_brute_force(f, 2, 4, 2, 9, 13, 8, True, True, 1)),
@@ -252,4 +329,9 @@ ALL_PINS = [
     ("causal_alignment", pin_causal_alignment),
     ("gqa_repeat", pin_gqa_repeat),
     ("dominant_key", pin_dominant_key),
+    ("window_brute", lambda f: pin_brute_force(f, 2, 4, 2, 13, 17, 8, True, True, 4, window=5)),
+    ("window_page_mask", pin_window_is_the_page_mask),
+    ("window_alignment", pin_window_alignment),
+    ("window_zero", pin_window_zero),
+    ("window_wide", pin_window_wide_is_causal),
 ]

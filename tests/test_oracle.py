@@ -141,3 +141,46 @@ def test_workload_outputs_are_finite_and_sane():
 
 def test_dominant_key_one_hot():
     pins.pin_dominant_key(oracle.fwd)
+
+
+# ---- sliding window (the method page, section 7) ----
+
+@pytest.mark.parametrize("D", [4, 8])
+@pytest.mark.parametrize("ql,kl", [(1, 1), (16, 16), (7, 19), (19, 7), (33, 33)])
+@pytest.mark.parametrize("window", [0, 1, 5, 16, 40])
+@pytest.mark.parametrize("masked", [False, True])
+def test_window_matches_f64_brute_force(D, ql, kl, window, masked):
+    pins.pin_brute_force(oracle.fwd, B=1, H=4, Hkv=2, ql=ql, kl=kl, D=D, causal=True,
+                         masked=masked, seed=ql * 97 + kl * 7 + window, window=window)
+
+
+def test_window_is_the_page_mask():
+    pins.pin_window_is_the_page_mask(oracle.fwd)
+
+
+def test_window_alignment():
+    pins.pin_window_alignment(oracle.fwd)
+
+
+def test_window_zero_closed_form():
+    pins.pin_window_zero(oracle.fwd)
+
+
+def test_window_wider_than_rows_is_causal():
+    pins.pin_window_wide_is_causal(oracle.fwd)
+
+
+def test_window_rows_match_full():
+    B, H, Hkv, ql, kl, D = 2, 4, 2, 21, 30, 8
+    q, k, v = pins._inputs(81, B, H, Hkv, ql, kl, D)
+    full = oracle.fwd(q, k, v, None, B, H, Hkv, ql, kl, D, 0.3, True, window=6)
+    rows = np.array([0, 5, 20, 21, 100, B * H * ql - 1], np.int64)
+    part = oracle.fwd_rows(q, k, v, None, B, H, Hkv, ql, kl, D, 0.3, True, rows, window=6)
+    assert np.array_equal(part[0], full[0].reshape(-1, D)[rows])
+    assert np.array_equal(part[2], full[2].reshape(-1)[rows])
+
+
+def test_window_negative_is_rejected():
+    q, k, v = pins._inputs(82, 1, 1, 1, 4, 4, 8)
+    with pytest.raises(ValueError):
+        oracle.fwd(q, k, v, None, 1, 1, 1, 4, 4, 8, 0.3, True, window=-1)

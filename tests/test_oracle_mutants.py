@@ -23,10 +23,10 @@ MUTANTS = {
     "exp_sign_flipped": ("s[j] = exp2f(s[j] - m);", "s[j] = exp2f(m - s[j]);"),
     "causal_off_by_one": ("\n        for (int64_t j = q_abs + 1; j < kl; ++j)",
                           "\n        for (int64_t j = q_abs; j < kl; ++j)"),
-    "causal_offset_dropped": ("\n        const int64_t q_abs = (kl > ql ? kl - ql : 0) + i;",
-                              "\n        const int64_t q_abs = i;"),
-    "causal_offset_unclamped": [("\n        const int64_t q_abs = (kl > ql ? kl - ql : 0) + i;",
-                                 "\n        const int64_t q_abs = (kl - ql) + i;"),
+    "causal_offset_dropped": ("\n    const int64_t q_abs = (kl > ql ? kl - ql : 0) + i;",
+                              "\n    const int64_t q_abs = i;"),
+    "causal_offset_unclamped": [("\n    const int64_t q_abs = (kl > ql ? kl - ql : 0) + i;",
+                                 "\n    const int64_t q_abs = (kl - ql) + i;"),
                                 ("\n        for (int64_t j = q_abs + 1; j < kl; ++j)",
                                  "\n        for (int64_t j = (q_abs + 1 > 0 ? q_abs + 1 : 0); j < kl; ++j)")],
     "gqa_modulo_map": ("const int64_t kvh = h / (p->H / p->Hkv);",
@@ -48,6 +48,15 @@ MUTANTS = {
                         "const float *qr = p->q + row * D;\n    const float *kh = p->k + kvh * kl * D;"),
     "v_row_off_by_one": ("const float *vr = vh + j * D;",
                          "const float *vr = vh + (j + 1 < kl ? j + 1 : j) * D;"),
+    "window_off_by_one": ("for (int64_t j = 0; j < q_abs - p->window && j < kl; ++j)",
+                          "for (int64_t j = 0; j <= q_abs - p->window && j < kl; ++j)"),
+    "window_too_wide": ("for (int64_t j = 0; j < q_abs - p->window && j < kl; ++j)",
+                        "for (int64_t j = 0; j < q_abs - p->window - 1 && j < kl; ++j)"),
+    "window_offset_dropped": ("for (int64_t j = 0; j < q_abs - p->window && j < kl; ++j)",
+                              "for (int64_t j = 0; j < i - p->window && j < kl; ++j)"),
+    "window_ignored": ("\n    if (p->window >= 0) {", "\n    if (0) {"),
+    "window_without_causal": ("oracle_problem p = {q, k, v, mask, H, Hkv, ql, kl, D, scale, 1, window};",
+                              "oracle_problem p = {q, k, v, mask, H, Hkv, ql, kl, D, scale, 0, window};"),
     "max_skips_last_key": ("for (int64_t j = 0; j < kl; ++j)\n        if (s[j] > m)",
                            "for (int64_t j = 0; j + 1 < kl; ++j)\n        if (s[j] > m)"),
 }
