@@ -17,7 +17,7 @@ LIB_PATH = _build.LIB
 FA_STATUS = {
     0: "FA_OK", 1: "FA_ERR_NULL_POINTER", 2: "FA_ERR_BAD_SIZE", 3: "FA_ERR_HEAD_GROUPING",
     4: "FA_ERR_HEAD_DIM", 5: "FA_ERR_SCALE", 6: "FA_ERR_ALIGNMENT", 7: "FA_ERR_TOO_LARGE",
-    8: "FA_ERR_LAUNCH",
+    8: "FA_ERR_LAUNCH", 9: "FA_ERR_WINDOW",
 }
 
 _lib = None
@@ -41,6 +41,9 @@ def lib():
         l.fa_train_fwd.argtypes = [vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, ctypes.c_float, ci,
                                    vp, vp, vp]
         l.fa_train_fwd.restype = ci
+        l.fa_train_fwd_swa.argtypes = [vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, ctypes.c_float,
+                                       ci, vp, vp, vp]
+        l.fa_train_fwd_swa.restype = ci
         l.fa_train_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci,
                                    ctypes.c_float, ci, vp, vp, vp, vp]
         l.fa_train_bwd.restype = ci
@@ -62,6 +65,14 @@ def fa_train_fwd(q, k, v, mask, batch, n_heads, n_kv_heads, ql, kl, head_dim, sc
                               O or None, L or None, stream or None)
 
 
+def fa_train_fwd_swa(q, k, v, mask, batch, n_heads, n_kv_heads, ql, kl, head_dim, scale, window,
+                     O, L, stream):
+    """The C entry point with raw integer pointers (0 for NULL); returns the status."""
+    return lib().fa_train_fwd_swa(q or None, k or None, v or None, mask or None, batch, n_heads,
+                                  n_kv_heads, ql, kl, head_dim, float(scale), int(window),
+                                  O or None, L or None, stream or None)
+
+
 def train_fwd(q, k, v, mask=None, scale=None, causal=False, out=None, lse=None, stream=None):
     """O, L = train_fwd(q, k, v, mask=None, scale=None, causal=False)
 
@@ -71,6 +82,20 @@ def train_fwd(q, k, v, mask=None, scale=None, causal=False, out=None, lse=None, 
     Returns O (bf16 [B, H, ql, D]) and L (f32 [B, H, ql]). Enqueued on the
     current stream of q's device (or `stream`, a torch.cuda.Stream).
     """
+    return _train_fwd(q, k, v, mask, scale, causal, None, out, lse, stream)
+
+
+def train_fwd_swa(q, k, v, window, mask=None, scale=None, out=None, lse=None, stream=None):
+    """O, L = train_fwd_swa(q, k, v, window, mask=None, scale=None)
+
+    Sliding-window causal forward: key j is visible to query row i iff
+    q_abs - window <= j <= q_abs, q_abs = max(kl - ql, 0) + i. Arguments and
+    results as for train_fwd (the causal rule is implied).
+    """
+    return _train_fwd(q, k, v, mask, scale, True, int(window), out, lse, stream)
+
+
+def _train_fwd(q, k, v, mask, scale, causal, window, out, lse, stream):
     import torch
 
     for name, t in (("q", q), ("k", k), ("v", v)):
@@ -98,11 +123,15 @@ def train_fwd(q, k, v, mask=None, scale=None, causal=False, out=None, lse=None, 
     if tuple(L.shape) != (B, H, ql) or L.dtype != torch.float32 or not L.is_contiguous():
         raise ValueError("lse must be a contiguous f32 tensor [B, H, ql]")
     s = stream if stream is not None else torch.cuda.current_stream(q.device)
+    mptr = mask.data_ptr() if mask is not None else 0
     with torch.cuda.device(q.device):
-        status = fa_train_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(),
-                              mask.data_ptr() if mask is not None else 0,
-                              B, H, Hkv, ql, kl, D, scale, causal, O.data_ptr(), L.data_ptr(),
-                              s.cuda_stream)
+        if window is None:
+            status = fa_train_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), mptr, B, H, Hkv, ql,
+                                  kl, D, scale, causal, O.data_ptr(), L.data_ptr(), s.cuda_stream)
+        else:
+            status = fa_train_fwd_swa(q.data_ptr(), k.data_ptr(), v.data_ptr(), mptr, B, H, Hkv,
+                                      ql, kl, D, scale, window, O.data_ptr(), L.data_ptr(),
+                                      s.cuda_stream)
     if status != 0:
         raise FAError(status, status_string(status))
     return O, L

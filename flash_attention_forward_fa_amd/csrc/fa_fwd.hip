@@ -21,6 +21,11 @@
 // max, row sum and rescale are per-lane scalars after a reduction over the
 // four 16-lane groups (v_permlane32_swap, v_permlane16_swap).
 //
+// Sliding window (the same page, section 7, where it is built as an additive
+// mask): key j is visible to row i iff q_abs - window <= j <= q_abs, q_abs =
+// max(kl - ql, 0) + i. The WINDOW variants skip the key tiles below the band
+// and mask only the tiles that cross one of its edges.
+//
 // Accuracy: P enters the bf16 MFMA rounded to bf16. Where that is not accurate
 // enough the product is compensated (a second MFMA with P's bf16 remainder):
 // for query tiles whose rows may see fewer than 128 keys, and for rows whose
@@ -89,6 +94,7 @@ struct FwdArgs {
   int qt_count;
   int n_precise;   // kMixed: query tiles below this run compensated
   int causal_off;  // max(kl - ql, 0)
+  int window;      // WINDOW variants: keys below q_abs - window are hidden
   float c;         // |scale| * log2(e), at least FLT_MIN
   uint32_t q_sign; // 0x80008000 flips the sign of both bf16 halves (scale < 0)
 };
@@ -101,12 +107,13 @@ struct FwdArgs {
 // (wg_flags: one int per wave). With REDO (and PRECISE), only the rows with
 // redo set are computed and written (waves without such a row only take part
 // in the tile copies).
-template <int D, bool CAUSAL, bool HAS_MASK, bool PRECISE, bool REDO>
+template <int D, bool CAUSAL, bool WINDOW, bool HAS_MASK, bool PRECISE, bool REDO>
 __device__ __forceinline__ bool fwd_tile(const FwdArgs& a, int qtile, int bh, uint16_t* k0s,
                                          uint16_t* v0s, uint16_t* k1s, uint16_t* v1s,
                                          bool (&redo)[Cfg<D>::QB], int* wg_flags) {
   static_assert(PRECISE || !HAS_MASK, "the masked forward always runs compensated");
   static_assert(PRECISE || !REDO, "a redo runs compensated");
+  static_assert(CAUSAL || !WINDOW, "the sliding window includes the causal rule");
   constexpr int BN = Cfg<D>::BN;
   constexpr int kQB = Cfg<D>::QB;
   constexpr int kRowsPerWave = 16 * kQB;
@@ -146,9 +153,13 @@ __device__ __forceinline__ bool fwd_tile(const FwdArgs& a, int qtile, int bh, ui
   const int last_row = min(q0 + kBlockM, ql) - 1;
   const int kend = CAUSAL ? min(kl, off + last_row + 1) : kl;
   const int n_kt = (kend + BN - 1) / BN;
+  // under a sliding window no row of the workgroup (of the wave) sees a key
+  // below off + (its first row) - window: those key tiles are skipped
+  const int kt_first = WINDOW ? max(0, off + q0 - a.window) / BN : 0;
   const bool wave_active = qw0 < ql;
   const int wave_last = min(qw0 + kRowsPerWave, ql) - 1;
   const int wave_kend = CAUSAL ? min(kl, off + wave_last + 1) : kl;
+  const int wave_kt_first = WINDOW ? max(0, off + qw0 - a.window) / BN : 0;
   float* lrow_base = a.l + (int64_t)bh * ql;
 
   bool wave_redo = false;
@@ -165,7 +176,7 @@ __device__ __forceinline__ bool fwd_tile(const FwdArgs& a, int qtile, int bh, ui
   auto issue_v = [&](int kt, uint16_t* dst) {
     issue_tile<D, BN, NT, false>(vp, kt * BN, kl, dst, tid, 64 * wave, voff);
   };
-  if (n_kt > 0) issue_k(0, k0s);
+  if (n_kt > kt_first) issue_k(kt_first, (kt_first & 1) ? k1s : k0s);
 
   // ---- Q^T as the B operand: block qb, step s: row qw0+16qb+c16, dims 32s+8grp.. ----
   bf16x8 qop[kQB][NDS];
@@ -203,6 +214,10 @@ __device__ __forceinline__ bool fwd_tile(const FwdArgs& a, int qtile, int bh, ui
     if (kl % BN != 0) mask_from = min(mask_from, kl / BN);
     if (CAUSAL) mask_from = min(mask_from, (off + qw0 + 1) / BN);
   }
+  // and the tiles below lo_end, which hold keys that the wave's last row no
+  // longer sees (the window's lower edge)
+  const int lo_gap = WINDOW ? off + wave_last - a.window : 0;
+  const int lo_end = lo_gap > 0 ? (lo_gap + BN - 1) / BN : 0;
 
   // ---- S^T = K Q^T (raw scores, f32) for the tile in ks ----
   auto kread = [&](const uint16_t* ks, int s, int kb) {
@@ -271,19 +286,24 @@ __device__ __forceinline__ bool fwd_tile(const FwdArgs& a, int qtile, int bh, ui
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int key = kbase + 32 * (kb >> 1) + 8 * grp + 4 * (kb & 1) + i;
-            const bool vis = key < kl && (!CAUSAL || key <= off + qrow);
+            const bool vis = key < kl && (!CAUSAL || key <= off + qrow) &&
+                             (!WINDOW || key >= off + qrow - a.window);
             sacc[kb][qb][i] =
                 vis ? __builtin_fmaf(sacc[kb][qb][i], a.c, kLog2e * mrow[key]) : -INFINITY;
           }
       } else {
-        // the last visible key of the row, relative to this lane's first key
-        // of the tile; each score then needs one compare with a constant
+        // the last (and, under a window, the first) visible key of the row,
+        // relative to this lane's first key of the tile; each score then needs
+        // one compare with a constant per edge
         const int last = (CAUSAL ? min(kl - 1, off + qrow) : kl - 1) - kbase - 8 * grp;
+        const int first = WINDOW ? off + qrow - a.window - kbase - 8 * grp : 0;
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (32 * (kb >> 1) + 4 * (kb & 1) + i > last) sacc[kb][qb][i] = -INFINITY;
+          for (int i = 0; i < 4; ++i) {
+            const int idx = 32 * (kb >> 1) + 4 * (kb & 1) + i;
+            if (idx > last || (WINDOW && idx < first)) sacc[kb][qb][i] = -INFINITY;
+          }
       }
     }
   };
@@ -426,8 +446,8 @@ __device__ __forceinline__ bool fwd_tile(const FwdArgs& a, int qtile, int bh, ui
 
   // ---- the key loop ----
   // one tile per step: wait for its copy, start the next one, compute it
-  if (n_kt > 0) issue_v(0, v0s);
-  for (int kt = 0; kt < n_kt; ++kt) {
+  if (n_kt > kt_first) issue_v(kt_first, (kt_first & 1) ? v1s : v0s);
+  for (int kt = kt_first; kt < n_kt; ++kt) {
     const bool odd = kt & 1;
     wait_vmem();
     __syncthreads();
@@ -435,7 +455,7 @@ __device__ __forceinline__ bool fwd_tile(const FwdArgs& a, int qtile, int bh, ui
       issue_k(kt + 1, odd ? k0s : k1s);
       issue_v(kt + 1, odd ? v0s : v1s);
     }
-    if (kt < n_kw) {
+    if (kt >= wave_kt_first && kt < n_kw) {
       // A wave issuing its MFMA blocks gets a raised priority (s_setprio), so
       // it is not held back behind the other waves' VALU work; measured best
       // around the P.V block for D=64 and around both blocks for D=256.
@@ -443,7 +463,7 @@ __device__ __forceinline__ bool fwd_tile(const FwdArgs& a, int qtile, int bh, ui
       if (D == 256) set_prio<2>();
       scores(odd ? k1s : k0s, s);
       if (D == 256) set_prio<0>();
-      if (kt >= mask_from) apply_mask(kt, s);
+      if (kt >= mask_from || (WINDOW && kt < lo_end)) apply_mask(kt, s);
       float mx[kQB];
       if (__any(part_max(s, mx))) {
         complete_max(mx);
@@ -516,7 +536,7 @@ __device__ __forceinline__ bool fwd_tile(const FwdArgs& a, int qtile, int bh, ui
   return wg_any;
 }
 
-template <int D, bool CAUSAL, bool HAS_MASK, int MODE>
+template <int D, bool CAUSAL, bool WINDOW, bool HAS_MASK, int MODE>
 __global__ __launch_bounds__(64 * Cfg<D>::W)
 __attribute__((amdgpu_waves_per_eu(MODE == kMixed ? Cfg<D>::WPE : 2))) void fa_fwd_kernel(FwdArgs a) {
   static_assert(MODE != kMixed || !HAS_MASK, "the masked forward always runs compensated");
@@ -554,23 +574,26 @@ __attribute__((amdgpu_waves_per_eu(MODE == kMixed ? Cfg<D>::WPE : 2))) void fa_f
   if constexpr (MODE == kMixed) {
     // the compensated tiles are the lightest, so they run last and fill the tail
     if (qtile < a.n_precise) {
-      fwd_tile<D, CAUSAL, false, true, false>(a, qtile, bh, k0s, v0s, k1s, v1s, redo, wg_flags);
-    } else if (fwd_tile<D, CAUSAL, false, false, false>(a, qtile, bh, k0s, v0s, k1s, v1s, redo,
-                                                        wg_flags)) {
+      fwd_tile<D, CAUSAL, WINDOW, false, true, false>(a, qtile, bh, k0s, v0s, k1s, v1s, redo,
+                                                      wg_flags);
+    } else if (fwd_tile<D, CAUSAL, WINDOW, false, false, false>(a, qtile, bh, k0s, v0s, k1s, v1s,
+                                                                redo, wg_flags)) {
       // (the plain pass's last barrier came after every wave's last LDS read,
       // so the redo's copies may reuse the tile buffers)
-      fwd_tile<D, CAUSAL, false, true, true>(a, qtile, bh, k0s, v0s, k1s, v1s, redo, wg_flags);
+      fwd_tile<D, CAUSAL, WINDOW, false, true, true>(a, qtile, bh, k0s, v0s, k1s, v1s, redo,
+                                                     wg_flags);
     }
   } else {
-    fwd_tile<D, CAUSAL, HAS_MASK, true, false>(a, qtile, bh, k0s, v0s, k1s, v1s, redo, wg_flags);
+    fwd_tile<D, CAUSAL, WINDOW, HAS_MASK, true, false>(a, qtile, bh, k0s, v0s, k1s, v1s, redo,
+                                                       wg_flags);
   }
 #endif
 }
 
-template <int D, bool CAUSAL, bool HAS_MASK, int MODE>
+template <int D, bool CAUSAL, bool WINDOW, bool HAS_MASK, int MODE>
 hipError_t launch(const FwdArgs& a, unsigned grid, hipStream_t stream) {
-  hipLaunchKernelGGL((fa_fwd_kernel<D, CAUSAL, HAS_MASK, MODE>), dim3(grid), dim3(64 * Cfg<D>::W), 0,
-                     stream, a);
+  hipLaunchKernelGGL((fa_fwd_kernel<D, CAUSAL, WINDOW, HAS_MASK, MODE>), dim3(grid),
+                     dim3(64 * Cfg<D>::W), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -578,7 +601,7 @@ hipError_t launch(const FwdArgs& a, unsigned grid, hipStream_t stream) {
 // launch over all tiles (compensated for the tiles with short rows, the first
 // n_short ones; plain for the others, with a compensated redo of the rows
 // that need it inside the same workgroup).
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool WINDOW>
 hipError_t dispatch_c(FwdArgs a, bool has_mask, int n_short, hipStream_t stream) {
   const unsigned bh = (unsigned)(a.B * a.H);
   const int n_qt = a.n_qtiles;
@@ -586,26 +609,26 @@ hipError_t dispatch_c(FwdArgs a, bool has_mask, int n_short, hipStream_t stream)
   a.qt_count = n_qt;
   if (has_mask) {
     a.n_precise = n_qt;
-    return launch<D, CAUSAL, true, kAll>(a, bh * n_qt, stream);
+    return launch<D, CAUSAL, WINDOW, true, kAll>(a, bh * n_qt, stream);
   }
   a.n_precise = n_short;
-  return launch<D, CAUSAL, false, kMixed>(a, bh * n_qt, stream);
+  return launch<D, CAUSAL, WINDOW, false, kMixed>(a, bh * n_qt, stream);
 }
 
 template <int D>
-hipError_t dispatch_d(const FwdArgs& a, bool causal, bool has_mask, int n_short,
+hipError_t dispatch_d(const FwdArgs& a, bool causal, bool window, bool has_mask, int n_short,
                       hipStream_t stream) {
-  return causal ? dispatch_c<D, true>(a, has_mask, n_short, stream)
-                : dispatch_c<D, false>(a, has_mask, n_short, stream);
+  if (window) return dispatch_c<D, true, true>(a, has_mask, n_short, stream);
+  return causal ? dispatch_c<D, true, false>(a, has_mask, n_short, stream)
+                : dispatch_c<D, false, false>(a, has_mask, n_short, stream);
 }
 
 bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
 
-}  // namespace
-
-extern "C" int fa_train_fwd(const void* q, const void* k, const void* v, const float* mask,
-                            int batch, int n_heads, int n_kv_heads, int ql, int kl, int head_dim,
-                            float scale, int causal, void* O, float* L, void* stream) {
+// Shared host path of fa_train_fwd and fa_train_fwd_swa; window < 0: none.
+int train_fwd(const void* q, const void* k, const void* v, const float* mask, int batch,
+              int n_heads, int n_kv_heads, int ql, int kl, int head_dim, float scale, int causal,
+              int window, void* O, float* L, void* stream) {
   if (batch < 0 || ql < 0 || kl < 0 || n_heads < 1 || n_kv_heads < 1) return FA_ERR_BAD_SIZE;
   if (n_heads % n_kv_heads != 0) return FA_ERR_HEAD_GROUPING;
   if (head_dim != 64 && head_dim != 256) return FA_ERR_HEAD_DIM;
@@ -639,6 +662,10 @@ extern "C" int fa_train_fwd(const void* q, const void* k, const void* v, const f
   a.group = n_heads / n_kv_heads;
   a.n_qtiles = (int)n_qtiles;
   a.causal_off = kl > ql ? kl - ql : 0;
+  // a window reaching past the largest q_abs hides nothing more; clamping it
+  // there keeps q_abs - window within int range
+  const bool windowed = window >= 0;
+  a.window = windowed ? (int)std::min<int64_t>(window, (int64_t)a.causal_off + ql) : 0;
   // Masked keys are carried as raw score -inf and scaled inside the kernel, which
   // needs c > 0; a zero scale is run as the smallest normal one (the scores it
   // produces round to 0 in f32, so the weights are the same uniform ones).
@@ -650,12 +677,36 @@ extern "C" int fa_train_fwd(const void* q, const void* k, const void* v, const f
   int64_t n_short = 0;
   if (kl < kPreciseKeys)
     n_short = n_qtiles;
-  else if (causal && a.causal_off + 1 < kPreciseKeys)
+  else if (windowed && (a.window + 1 < kPreciseKeys ||
+                        (ql > kl && (int64_t)ql - 1 > (int64_t)kl + a.window - kPreciseKeys)))
+    // every row sees at most window + 1 keys; with ql > kl the last rows
+    // (q_abs >= kl) see kl + window - q_abs
+    n_short = n_qtiles;
+  else if ((causal || windowed) && a.causal_off + 1 < kPreciseKeys)
     n_short = std::min<int64_t>(n_qtiles, (kPreciseKeys - 1 - a.causal_off + bm - 1) / bm);
   hipError_t err =
-      head_dim == 64 ? dispatch_d<64>(a, causal != 0, mask != nullptr, (int)n_short, s)
-                     : dispatch_d<256>(a, causal != 0, mask != nullptr, (int)n_short, s);
+      head_dim == 64
+          ? dispatch_d<64>(a, causal != 0, windowed, mask != nullptr, (int)n_short, s)
+          : dispatch_d<256>(a, causal != 0, windowed, mask != nullptr, (int)n_short, s);
   return err == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" int fa_train_fwd(const void* q, const void* k, const void* v, const float* mask,
+                            int batch, int n_heads, int n_kv_heads, int ql, int kl, int head_dim,
+                            float scale, int causal, void* O, float* L, void* stream) {
+  return train_fwd(q, k, v, mask, batch, n_heads, n_kv_heads, ql, kl, head_dim, scale, causal, -1,
+                   O, L, stream);
+}
+
+extern "C" int fa_train_fwd_swa(const void* q, const void* k, const void* v, const float* mask,
+                                int batch, int n_heads, int n_kv_heads, int ql, int kl,
+                                int head_dim, float scale, int window, void* O, float* L,
+                                void* stream) {
+  if (window < 0) return FA_ERR_WINDOW;
+  return train_fwd(q, k, v, mask, batch, n_heads, n_kv_heads, ql, kl, head_dim, scale, 1, window,
+                   O, L, stream);
 }
 
 extern "C" const char* fa_status_string(int status) {
@@ -669,6 +720,7 @@ extern "C" const char* fa_status_string(int status) {
     case FA_ERR_ALIGNMENT: return "misaligned tensor (q, k, v, O need 16 bytes; mask, L 4 bytes)";
     case FA_ERR_TOO_LARGE: return "problem too large for the kernel's grid or index range";
     case FA_ERR_LAUNCH: return "HIP kernel launch failed";
+    case FA_ERR_WINDOW: return "sliding window must be >= 0";
     default: return "unknown status";
   }
 }

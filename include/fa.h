@@ -37,7 +37,8 @@ enum fa_status {
     FA_ERR_SCALE = 5,          /* scale is NaN or infinite                              */
     FA_ERR_ALIGNMENT = 6,      /* q, k, v or O not 16-byte aligned; mask or L not 4-byte */
     FA_ERR_TOO_LARGE = 7,      /* a grid or index would overflow the kernel's limits    */
-    FA_ERR_LAUNCH = 8          /* the HIP launch failed (hipGetLastError)               */
+    FA_ERR_LAUNCH = 8,         /* the HIP launch failed (hipGetLastError)               */
+    FA_ERR_WINDOW = 9          /* fa_train_fwd_swa: window < 0                          */
 };
 
 /*
@@ -68,6 +69,35 @@ enum fa_status {
 int fa_train_fwd(const void *q, const void *k, const void *v, const float *mask, int batch,
                  int n_heads, int n_kv_heads, int ql, int kl, int head_dim, float scale,
                  int causal, void *O, float *L, void *stream);
+
+/*
+ * fa_train_fwd_swa - enqueue one training forward pass with sliding-window
+ * causal attention.
+ *
+ * The method's page tests a sliding window by building it as an additive mask
+ * ("mlx-native 0.9.0", tests/test_flash_attn_train.rs, section 7,
+ * "SLIDING-WINDOW MASK (SWA) PARITY": key j kept for row i iff j <= i and
+ * j + window >= i). This entry point applies that band directly, with the
+ * causal rule's bottom-right alignment (the same as the page's when ql = kl):
+ *
+ *   key j is visible to query row i iff  q_abs - window <= j <= q_abs,
+ *   q_abs = max(kl - ql, 0) + i,
+ *
+ * so a row sees at most window + 1 keys; key tiles below the band are never
+ * read. Every other argument, the layouts, ownership and outputs are those of
+ * fa_train_fwd with causal = 1 (an additive mask, when given, applies on top
+ * of the band). A row with no visible key (possible when ql > kl) gets O = 0
+ * and L = -inf.
+ *
+ *   window  >= 0; a window of at least max(kl - ql, 0) + ql - 1 hides nothing
+ *           beyond the causal rule.
+ *
+ * Returns FA_ERR_WINDOW for window < 0, otherwise the statuses of
+ * fa_train_fwd. Never aborts, never synchronises, allocates nothing.
+ */
+int fa_train_fwd_swa(const void *q, const void *k, const void *v, const float *mask, int batch,
+                     int n_heads, int n_kv_heads, int ql, int kl, int head_dim, float scale,
+                     int window, void *O, float *L, void *stream);
 
 /*
  * fa_train_bwd - enqueue the training backward pass of the same attention.

@@ -28,7 +28,7 @@ def _declared_functions():
 
 def test_header_declares_the_entry_points():
     names = _declared_functions()
-    assert {"fa_train_fwd", "fa_train_bwd", "fa_status_string"} <= names
+    assert {"fa_train_fwd", "fa_train_fwd_swa", "fa_train_bwd", "fa_status_string"} <= names
 
 
 def test_library_exports_every_declared_symbol():
@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings_cover_all_codes():
-    for code in range(0, 9):
+    for code in range(0, 10):
         s = fa.status_string(code)
         assert s and s != "unknown status"
     assert fa.status_string(12345) == "unknown status"
@@ -79,6 +79,31 @@ def test_empty_problems_are_noops(over):
     assert _call(**over) == 0
 
 
+SWA_GOOD = {k: v for k, v in GOOD.items() if k != "causal"}
+
+
+def _call_swa(**over):
+    args = dict(SWA_GOOD, window=4)
+    args.update(over)
+    return fa.fa_train_fwd_swa(**args)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(window=-1), 9), (dict(window=-(2 ** 31)), 9), (dict(q=0), 1), (dict(v=0), 1),
+    (dict(L=0), 1), (dict(kl=-1), 2), (dict(n_heads=3, n_kv_heads=2), 3), (dict(head_dim=96), 4),
+    (dict(scale=math.nan), 5), (dict(k=A + 8), 6), (dict(mask=A + 2), 6),
+    (dict(batch=65536, n_heads=65536, n_kv_heads=1, ql=1), 7),
+])
+def test_window_invalid_arguments_are_rejected(over, code):
+    assert _call_swa(**over) == code
+
+
+@pytest.mark.parametrize("over", [dict(batch=0), dict(ql=0, window=0),
+                                  dict(ql=0, q=0, k=0, v=0, O=0, L=0, window=2 ** 31 - 1)])
+def test_window_empty_problems_are_noops(over):
+    assert _call_swa(**over) == 0
+
+
 def test_python_binding_fails_loudly_without_gpu_tensors():
     import torch
     q = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
@@ -86,6 +111,8 @@ def test_python_binding_fails_loudly_without_gpu_tensors():
         fa.train_fwd(q, q, q)
     with pytest.raises(TypeError):
         fa.train_fwd(q.float(), q, q)
+    with pytest.raises(ValueError):
+        fa.train_fwd_swa(q, q, q, 4)
 
 
 BWD_GOOD = dict(q=A, k=A, v=A, mask=0, O=A, L=A, dO=A, batch=1, n_heads=2, n_kv_heads=1, ql=8,
