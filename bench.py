@@ -86,6 +86,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--backward-steps", type=int, default=10,
                     help="timed backward calls per workload after the forward (0: none)")
+    ap.add_argument("--window-steps", type=int, default=10,
+                    help="timed sliding-window forward calls per workload (0: none)")
     ap.add_argument("--cpu-rows", type=int, default=0,
                     help="rows per workload for the CPU baseline (0: default sample)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -173,6 +175,40 @@ def main():
             log(f"{w.name}: backward {ms * 1e3:.1f} us/call, {bwd[w.name]['tflops']:.1f} TFLOP/s "
                 f"(FA-2 count)")
 
+    # The sliding-window forward (fa_train_fwd_swa) on the same inputs, window
+    # 1024 (D=64) or 2048 (D=256); not part of the headline metric. Its FLOP
+    # count is exact: 4*D per visible score.
+    swa = {}
+    if args.window_steps > 0:
+        for w in workloads:
+            q, k, v = dev_inputs[w.name]
+            O, L = outputs[w.name]
+            win = 1024 if w.D == 64 else 2048
+            for _ in range(3):
+                fa.train_fwd_swa(q, k, v, win, scale=w.scale, out=O, lse=L)
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(args.window_steps):
+                fa.train_fwd_swa(q, k, v, win, scale=w.scale, out=O, lse=L)
+            b.record(stream)
+            torch.cuda.synchronize()
+            ms = a.elapsed_time(b) / args.window_steps
+            off = max(w.kl - w.ql, 0)
+            q_abs = off + np.arange(w.ql, dtype=np.int64)
+            visible = int((np.minimum(q_abs, w.kl - 1) - np.maximum(q_abs - win, 0) + 1)
+                          .clip(min=0).sum()) * w.B * w.H
+            flop = 4 * w.D * visible
+            swa[w.name] = {"window": win, "ms_avg": ms, "flop": flop,
+                           "tflops": flop / (ms * 1e-3) / 1e12,
+                           "frac_of_peak": flop / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+            log(f"{w.name}: sliding window {win}: {ms * 1e3:.1f} us/call, "
+                f"{swa[w.name]['tflops']:.1f} TFLOP/s (4*D per visible score)")
+        # leave the causal forward's outputs in place for anything read later
+        for w in workloads:
+            launch(w)
+        torch.cuda.synchronize()
+
     if args.copy_calibration:
         n = args.copy_calibration * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device=dev)
@@ -226,6 +262,8 @@ def main():
     }
     if bwd:
         result["backward"] = bwd
+    if swa:
+        result["sliding_window"] = swa
     if not args.no_cpu_baseline:
         target = {w.name: (args.cpu_rows or (524288 if w.D == 64 else 65536)) for w in workloads}
         result["cpu_baseline"] = cpu_baseline(workloads, inputs, target)
