@@ -17,8 +17,9 @@ LIB_PATH = _build.LIB
 FA_STATUS = {
     0: "FA_OK", 1: "FA_ERR_NULL_POINTER", 2: "FA_ERR_BAD_SIZE", 3: "FA_ERR_HEAD_GROUPING",
     4: "FA_ERR_HEAD_DIM", 5: "FA_ERR_SCALE", 6: "FA_ERR_ALIGNMENT", 7: "FA_ERR_TOO_LARGE",
-    8: "FA_ERR_LAUNCH", 9: "FA_ERR_WINDOW",
+    8: "FA_ERR_LAUNCH", 9: "FA_ERR_WINDOW", 10: "FA_ERR_MASK",
 }
+FA_MASK_F32, FA_MASK_BF16 = 0, 1
 
 _lib = None
 
@@ -44,6 +45,10 @@ def lib():
         l.fa_train_fwd_swa.argtypes = [vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, ctypes.c_float,
                                        ci, vp, vp, vp]
         l.fa_train_fwd_swa.restype = ci
+        i64 = ctypes.c_longlong
+        l.fa_train_fwd_ex.argtypes = [vp, vp, vp, vp, ci, i64, i64, ci, ci, ci, ci, ci, ci,
+                                      ctypes.c_float, ci, ci, vp, vp, vp]
+        l.fa_train_fwd_ex.restype = ci
         l.fa_train_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci,
                                    ctypes.c_float, ci, vp, vp, vp, vp]
         l.fa_train_bwd.restype = ci
@@ -73,6 +78,44 @@ def fa_train_fwd_swa(q, k, v, mask, batch, n_heads, n_kv_heads, ql, kl, head_dim
                                   O or None, L or None, stream or None)
 
 
+def fa_train_fwd_ex(q, k, v, mask, mask_dtype, mask_stride_b, mask_stride_h, batch, n_heads,
+                    n_kv_heads, ql, kl, head_dim, scale, causal, window, O, L, stream):
+    """The C entry point with raw integer pointers (0 for NULL); returns the status."""
+    return lib().fa_train_fwd_ex(q or None, k or None, v or None, mask or None, int(mask_dtype),
+                                 int(mask_stride_b), int(mask_stride_h), batch, n_heads,
+                                 n_kv_heads, ql, kl, head_dim, float(scale), int(bool(causal)),
+                                 int(window), O or None, L or None, stream or None)
+
+
+def train_fwd_ex(q, k, v, mask=None, scale=None, causal=False, window=None, out=None, lse=None,
+                 stream=None):
+    """O, L = train_fwd_ex(q, k, v, mask=None, scale=None, causal=False, window=None)
+
+    train_fwd with every option of fa_train_fwd_ex: mask may be float32 or
+    bfloat16, of shape [B or 1, H or 1, ql, kl] (a size-1 batch or head dim is
+    broadcast; any batch/head strides, rows contiguous); window (>= 0, with
+    causal=True) selects the sliding window of train_fwd_swa.
+    """
+    import torch
+
+    if mask is None:
+        return _train_fwd(q, k, v, None, scale, causal, window, out, lse, stream, ex=True)
+    if mask.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("mask must be float32 or bfloat16")
+    B, H, ql, _ = q.shape
+    kl = k.shape[2]
+    if (mask.dim() != 4 or mask.shape[0] not in (1, B) or mask.shape[1] not in (1, H)
+            or tuple(mask.shape[2:]) != (ql, kl)):
+        raise ValueError(f"mask must have shape [B or 1, H or 1, {ql}, {kl}]")
+    if ql * kl > 0 and ((kl > 1 and mask.stride(3) != 1) or (ql > 1 and mask.stride(2) != kl)):
+        raise ValueError("mask rows must be contiguous (strides [.., .., kl, 1])")
+    sb = mask.stride(0) if mask.shape[0] > 1 else 0
+    sh = mask.stride(1) if mask.shape[1] > 1 else 0
+    return _train_fwd(q, k, v, mask, scale, causal, window, out, lse, stream, ex=True,
+                      mask_layout=(FA_MASK_BF16 if mask.dtype == torch.bfloat16 else FA_MASK_F32,
+                                   sb, sh))
+
+
 def train_fwd(q, k, v, mask=None, scale=None, causal=False, out=None, lse=None, stream=None):
     """O, L = train_fwd(q, k, v, mask=None, scale=None, causal=False)
 
@@ -95,7 +138,8 @@ def train_fwd_swa(q, k, v, window, mask=None, scale=None, out=None, lse=None, st
     return _train_fwd(q, k, v, mask, scale, True, int(window), out, lse, stream)
 
 
-def _train_fwd(q, k, v, mask, scale, causal, window, out, lse, stream):
+def _train_fwd(q, k, v, mask, scale, causal, window, out, lse, stream, ex=False,
+               mask_layout=None):
     import torch
 
     for name, t in (("q", q), ("k", k), ("v", v)):
@@ -109,11 +153,13 @@ def _train_fwd(q, k, v, mask, scale, causal, window, out, lse, stream):
         raise ValueError("k and v must be [B, Hkv, kl, D] with q's B and D")
     if k.device != q.device or v.device != q.device:
         raise ValueError("q, k and v must be on the same device")
-    if mask is not None:
+    if mask is not None and mask_layout is None:
         if mask.dtype != torch.float32 or not mask.is_contiguous() or mask.device != q.device:
             raise ValueError("mask must be a contiguous float32 tensor on q's device")
         if tuple(mask.shape) != (B, H, ql, kl):
             raise ValueError(f"mask must have shape {(B, H, ql, kl)}")
+    if mask is not None and mask.device != q.device:
+        raise ValueError("mask must be on q's device")
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     O = out if out is not None else torch.empty_like(q)
@@ -125,7 +171,13 @@ def _train_fwd(q, k, v, mask, scale, causal, window, out, lse, stream):
     s = stream if stream is not None else torch.cuda.current_stream(q.device)
     mptr = mask.data_ptr() if mask is not None else 0
     with torch.cuda.device(q.device):
-        if window is None:
+        if ex:
+            mdt, sb, sh = mask_layout or (FA_MASK_F32, 0, 0)
+            status = fa_train_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), mptr, mdt, sb, sh,
+                                     B, H, Hkv, ql, kl, D, scale, causal,
+                                     -1 if window is None else window, O.data_ptr(),
+                                     L.data_ptr(), s.cuda_stream)
+        elif window is None:
             status = fa_train_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), mptr, B, H, Hkv, ql,
                                   kl, D, scale, causal, O.data_ptr(), L.data_ptr(), s.cuda_stream)
         else:

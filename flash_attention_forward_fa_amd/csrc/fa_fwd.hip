@@ -78,13 +78,25 @@ constexpr float kLazy = 8.0f;
 // again, compensated, for those rows only. The compensated kernel (kAll)
 // computes every row of every tile compensated (the masked forward).
 constexpr int kMixed = 0, kAll = 1;
+// Additive mask element types (kNoMask: no mask).
+constexpr int kNoMask = 0, kMaskF32 = 1, kMaskBF16 = 2;
+
+// Mask element idx as f32 (a bf16 mask widens exactly).
+template <int MASK>
+__device__ __forceinline__ float mask_at(const void* m, int64_t idx) {
+  if constexpr (MASK == kMaskBF16)
+    return __uint_as_float((uint32_t)static_cast<const uint16_t*>(m)[idx] << 16);
+  else
+    return static_cast<const float*>(m)[idx];
+}
 
 
 struct FwdArgs {
   const uint16_t* q;
   const uint16_t* k;
   const uint16_t* v;
-  const float* mask;
+  const void* mask;          // f32 or bf16 (the kernel's MASK), or null
+  int64_t mask_sb, mask_sh;  // mask strides of batch and head, in elements (0: broadcast)
   uint16_t* o;
   float* l;
   int B, H, Hkv, ql, kl;
@@ -107,10 +119,11 @@ struct FwdArgs {
 // (wg_flags: one int per wave). With REDO (and PRECISE), only the rows with
 // redo set are computed and written (waves without such a row only take part
 // in the tile copies).
-template <int D, bool CAUSAL, bool WINDOW, bool HAS_MASK, bool PRECISE, bool REDO>
+template <int D, bool CAUSAL, bool WINDOW, int MASK, bool PRECISE, bool REDO>
 __device__ __forceinline__ bool fwd_tile(const FwdArgs& a, int qtile, int bh, uint16_t* k0s,
                                          uint16_t* v0s, uint16_t* k1s, uint16_t* v1s,
                                          bool (&redo)[Cfg<D>::QB], int* wg_flags) {
+  constexpr bool HAS_MASK = MASK != kNoMask;
   static_assert(PRECISE || !HAS_MASK, "the masked forward always runs compensated");
   static_assert(PRECISE || !REDO, "a redo runs compensated");
   static_assert(CAUSAL || !WINDOW, "the sliding window includes the causal rule");
@@ -280,7 +293,8 @@ __device__ __forceinline__ bool fwd_tile(const FwdArgs& a, int qtile, int bh, ui
     for (int qb = 0; qb < kQB; ++qb) {
       const int qrow = qw0 + 16 * qb + c16;
       if constexpr (HAS_MASK) {
-        const float* mrow = a.mask + ((int64_t)bh * ql + min(qrow, ql - 1)) * kl;
+        const int64_t mrow =
+            b * a.mask_sb + h * a.mask_sh + (int64_t)min(qrow, ql - 1) * kl;
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
@@ -288,8 +302,9 @@ __device__ __forceinline__ bool fwd_tile(const FwdArgs& a, int qtile, int bh, ui
             const int key = kbase + 32 * (kb >> 1) + 8 * grp + 4 * (kb & 1) + i;
             const bool vis = key < kl && (!CAUSAL || key <= off + qrow) &&
                              (!WINDOW || key >= off + qrow - a.window);
-            sacc[kb][qb][i] =
-                vis ? __builtin_fmaf(sacc[kb][qb][i], a.c, kLog2e * mrow[key]) : -INFINITY;
+            // (the index is clamped so that keys past the end read inside the row)
+            const float mv = mask_at<MASK>(a.mask, mrow + min(key, kl - 1));
+            sacc[kb][qb][i] = vis ? __builtin_fmaf(sacc[kb][qb][i], a.c, kLog2e * mv) : -INFINITY;
           }
       } else {
         // the last (and, under a window, the first) visible key of the row,
@@ -536,10 +551,10 @@ __device__ __forceinline__ bool fwd_tile(const FwdArgs& a, int qtile, int bh, ui
   return wg_any;
 }
 
-template <int D, bool CAUSAL, bool WINDOW, bool HAS_MASK, int MODE>
+template <int D, bool CAUSAL, bool WINDOW, int MASK, int MODE>
 __global__ __launch_bounds__(64 * Cfg<D>::W)
 __attribute__((amdgpu_waves_per_eu(MODE == kMixed ? Cfg<D>::WPE : 2))) void fa_fwd_kernel(FwdArgs a) {
-  static_assert(MODE != kMixed || !HAS_MASK, "the masked forward always runs compensated");
+  static_assert(MODE != kMixed || MASK == kNoMask, "the masked forward always runs compensated");
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
   constexpr int TILE = Cfg<D>::BN * D;
   __shared__ __attribute__((aligned(1024))) uint16_t k0s[TILE];
@@ -574,25 +589,25 @@ __attribute__((amdgpu_waves_per_eu(MODE == kMixed ? Cfg<D>::WPE : 2))) void fa_f
   if constexpr (MODE == kMixed) {
     // the compensated tiles are the lightest, so they run last and fill the tail
     if (qtile < a.n_precise) {
-      fwd_tile<D, CAUSAL, WINDOW, false, true, false>(a, qtile, bh, k0s, v0s, k1s, v1s, redo,
-                                                      wg_flags);
-    } else if (fwd_tile<D, CAUSAL, WINDOW, false, false, false>(a, qtile, bh, k0s, v0s, k1s, v1s,
-                                                                redo, wg_flags)) {
+      fwd_tile<D, CAUSAL, WINDOW, kNoMask, true, false>(a, qtile, bh, k0s, v0s, k1s, v1s, redo,
+                                                        wg_flags);
+    } else if (fwd_tile<D, CAUSAL, WINDOW, kNoMask, false, false>(a, qtile, bh, k0s, v0s, k1s, v1s,
+                                                                  redo, wg_flags)) {
       // (the plain pass's last barrier came after every wave's last LDS read,
       // so the redo's copies may reuse the tile buffers)
-      fwd_tile<D, CAUSAL, WINDOW, false, true, true>(a, qtile, bh, k0s, v0s, k1s, v1s, redo,
-                                                     wg_flags);
+      fwd_tile<D, CAUSAL, WINDOW, kNoMask, true, true>(a, qtile, bh, k0s, v0s, k1s, v1s, redo,
+                                                       wg_flags);
     }
   } else {
-    fwd_tile<D, CAUSAL, WINDOW, HAS_MASK, true, false>(a, qtile, bh, k0s, v0s, k1s, v1s, redo,
-                                                       wg_flags);
+    fwd_tile<D, CAUSAL, WINDOW, MASK, true, false>(a, qtile, bh, k0s, v0s, k1s, v1s, redo,
+                                                   wg_flags);
   }
 #endif
 }
 
-template <int D, bool CAUSAL, bool WINDOW, bool HAS_MASK, int MODE>
+template <int D, bool CAUSAL, bool WINDOW, int MASK, int MODE>
 hipError_t launch(const FwdArgs& a, unsigned grid, hipStream_t stream) {
-  hipLaunchKernelGGL((fa_fwd_kernel<D, CAUSAL, WINDOW, HAS_MASK, MODE>), dim3(grid),
+  hipLaunchKernelGGL((fa_fwd_kernel<D, CAUSAL, WINDOW, MASK, MODE>), dim3(grid),
                      dim3(64 * Cfg<D>::W), 0, stream, a);
   return hipGetLastError();
 }
@@ -602,43 +617,52 @@ hipError_t launch(const FwdArgs& a, unsigned grid, hipStream_t stream) {
 // n_short ones; plain for the others, with a compensated redo of the rows
 // that need it inside the same workgroup).
 template <int D, bool CAUSAL, bool WINDOW>
-hipError_t dispatch_c(FwdArgs a, bool has_mask, int n_short, hipStream_t stream) {
+hipError_t dispatch_c(FwdArgs a, int mask, int n_short, hipStream_t stream) {
   const unsigned bh = (unsigned)(a.B * a.H);
   const int n_qt = a.n_qtiles;
   a.qt_base = 0;
   a.qt_count = n_qt;
-  if (has_mask) {
+  if (mask != kNoMask) {
     a.n_precise = n_qt;
-    return launch<D, CAUSAL, WINDOW, true, kAll>(a, bh * n_qt, stream);
+    return mask == kMaskBF16 ? launch<D, CAUSAL, WINDOW, kMaskBF16, kAll>(a, bh * n_qt, stream)
+                             : launch<D, CAUSAL, WINDOW, kMaskF32, kAll>(a, bh * n_qt, stream);
   }
   a.n_precise = n_short;
-  return launch<D, CAUSAL, WINDOW, false, kMixed>(a, bh * n_qt, stream);
+  return launch<D, CAUSAL, WINDOW, kNoMask, kMixed>(a, bh * n_qt, stream);
 }
 
 template <int D>
-hipError_t dispatch_d(const FwdArgs& a, bool causal, bool window, bool has_mask, int n_short,
+hipError_t dispatch_d(const FwdArgs& a, bool causal, bool window, int mask, int n_short,
                       hipStream_t stream) {
-  if (window) return dispatch_c<D, true, true>(a, has_mask, n_short, stream);
-  return causal ? dispatch_c<D, true, false>(a, has_mask, n_short, stream)
-                : dispatch_c<D, false, false>(a, has_mask, n_short, stream);
+  if (window) return dispatch_c<D, true, true>(a, mask, n_short, stream);
+  return causal ? dispatch_c<D, true, false>(a, mask, n_short, stream)
+                : dispatch_c<D, false, false>(a, mask, n_short, stream);
 }
 
 bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
 
-// Shared host path of fa_train_fwd and fa_train_fwd_swa; window < 0: none.
-int train_fwd(const void* q, const void* k, const void* v, const float* mask, int batch,
-              int n_heads, int n_kv_heads, int ql, int kl, int head_dim, float scale, int causal,
-              int window, void* O, float* L, void* stream) {
+// Shared host path of every forward entry point; window < 0: none (window >= 0
+// requires causal). The mask is mask_dtype (FA_MASK_F32 / FA_MASK_BF16) with
+// batch and head strides in elements; its rows are contiguous (row stride kl).
+int train_fwd(const void* q, const void* k, const void* v, const void* mask, int mask_dtype,
+              int64_t mask_sb, int64_t mask_sh, int batch, int n_heads, int n_kv_heads, int ql,
+              int kl, int head_dim, float scale, int causal, int window, void* O, float* L,
+              void* stream) {
   if (batch < 0 || ql < 0 || kl < 0 || n_heads < 1 || n_kv_heads < 1) return FA_ERR_BAD_SIZE;
   if (n_heads % n_kv_heads != 0) return FA_ERR_HEAD_GROUPING;
   if (head_dim != 64 && head_dim != 256) return FA_ERR_HEAD_DIM;
   if (!isfinite(scale)) return FA_ERR_SCALE;
+  if (window >= 0 && !causal) return FA_ERR_WINDOW;
+  if (mask && ((mask_dtype != FA_MASK_F32 && mask_dtype != FA_MASK_BF16) || mask_sb < 0 ||
+               mask_sh < 0))
+    return FA_ERR_MASK;
   const int64_t rows = (int64_t)batch * n_heads * ql;
   if (rows == 0) return FA_OK;
   const bool kv_used = kl > 0;
   if (!q || !O || !L || (kv_used && (!k || !v))) return FA_ERR_NULL_POINTER;
   if (!aligned(q, 16) || !aligned(O, 16) || !aligned(L, 4) ||
-      (kv_used && (!aligned(k, 16) || !aligned(v, 16))) || (mask && !aligned(mask, 4)))
+      (kv_used && (!aligned(k, 16) || !aligned(v, 16))) ||
+      (mask && !aligned(mask, mask_dtype == FA_MASK_BF16 ? 2 : 4)))
     return FA_ERR_ALIGNMENT;
   const int bm = head_dim == 64 ? block_m<64>() : block_m<256>();
   const int64_t n_qtiles = ((int64_t)ql + bm - 1) / bm;
@@ -652,6 +676,9 @@ int train_fwd(const void* q, const void* k, const void* v, const float* mask, in
   a.k = static_cast<const uint16_t*>(k);
   a.v = static_cast<const uint16_t*>(v);
   a.mask = mask;
+  a.mask_sb = mask_sb;
+  a.mask_sh = mask_sh;
+  const int mask_kind = !mask ? kNoMask : mask_dtype == FA_MASK_BF16 ? kMaskBF16 : kMaskF32;
   a.o = static_cast<uint16_t*>(O);
   a.l = L;
   a.B = batch;
@@ -686,8 +713,8 @@ int train_fwd(const void* q, const void* k, const void* v, const float* mask, in
     n_short = std::min<int64_t>(n_qtiles, (kPreciseKeys - 1 - a.causal_off + bm - 1) / bm);
   hipError_t err =
       head_dim == 64
-          ? dispatch_d<64>(a, causal != 0, windowed, mask != nullptr, (int)n_short, s)
-          : dispatch_d<256>(a, causal != 0, windowed, mask != nullptr, (int)n_short, s);
+          ? dispatch_d<64>(a, causal != 0, windowed, mask_kind, (int)n_short, s)
+          : dispatch_d<256>(a, causal != 0, windowed, mask_kind, (int)n_short, s);
   return err == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
@@ -696,8 +723,9 @@ int train_fwd(const void* q, const void* k, const void* v, const float* mask, in
 extern "C" int fa_train_fwd(const void* q, const void* k, const void* v, const float* mask,
                             int batch, int n_heads, int n_kv_heads, int ql, int kl, int head_dim,
                             float scale, int causal, void* O, float* L, void* stream) {
-  return train_fwd(q, k, v, mask, batch, n_heads, n_kv_heads, ql, kl, head_dim, scale, causal, -1,
-                   O, L, stream);
+  const int64_t head = (int64_t)ql * kl;
+  return train_fwd(q, k, v, mask, FA_MASK_F32, head * n_heads, head, batch, n_heads, n_kv_heads,
+                   ql, kl, head_dim, scale, causal, -1, O, L, stream);
 }
 
 extern "C" int fa_train_fwd_swa(const void* q, const void* k, const void* v, const float* mask,
@@ -705,8 +733,19 @@ extern "C" int fa_train_fwd_swa(const void* q, const void* k, const void* v, con
                                 int head_dim, float scale, int window, void* O, float* L,
                                 void* stream) {
   if (window < 0) return FA_ERR_WINDOW;
-  return train_fwd(q, k, v, mask, batch, n_heads, n_kv_heads, ql, kl, head_dim, scale, 1, window,
-                   O, L, stream);
+  const int64_t head = (int64_t)ql * kl;
+  return train_fwd(q, k, v, mask, FA_MASK_F32, head * n_heads, head, batch, n_heads, n_kv_heads,
+                   ql, kl, head_dim, scale, 1, window, O, L, stream);
+}
+
+extern "C" int fa_train_fwd_ex(const void* q, const void* k, const void* v, const void* mask,
+                               int mask_dtype, long long mask_stride_b, long long mask_stride_h,
+                               int batch, int n_heads, int n_kv_heads, int ql, int kl,
+                               int head_dim, float scale, int causal, int window, void* O,
+                               float* L, void* stream) {
+  return train_fwd(q, k, v, mask, mask_dtype, mask_stride_b, mask_stride_h, batch, n_heads,
+                   n_kv_heads, ql, kl, head_dim, scale, causal, window < 0 ? -1 : window, O, L,
+                   stream);
 }
 
 extern "C" const char* fa_status_string(int status) {
@@ -717,10 +756,12 @@ extern "C" const char* fa_status_string(int status) {
     case FA_ERR_HEAD_GROUPING: return "n_heads is not a multiple of n_kv_heads";
     case FA_ERR_HEAD_DIM: return "head_dim must be 64 or 256";
     case FA_ERR_SCALE: return "scale must be finite";
-    case FA_ERR_ALIGNMENT: return "misaligned tensor (q, k, v, O need 16 bytes; mask, L 4 bytes)";
+    case FA_ERR_ALIGNMENT:
+      return "misaligned tensor (q, k, v, O need 16 bytes; L and an f32 mask 4, a bf16 mask 2)";
     case FA_ERR_TOO_LARGE: return "problem too large for the kernel's grid or index range";
     case FA_ERR_LAUNCH: return "HIP kernel launch failed";
-    case FA_ERR_WINDOW: return "sliding window must be >= 0";
+    case FA_ERR_WINDOW: return "sliding window must be >= 0 and comes with causal masking";
+    case FA_ERR_MASK: return "mask dtype must be FA_MASK_F32 or FA_MASK_BF16, strides >= 0";
     default: return "unknown status";
   }
 }

@@ -38,7 +38,16 @@ enum fa_status {
     FA_ERR_ALIGNMENT = 6,      /* q, k, v or O not 16-byte aligned; mask or L not 4-byte */
     FA_ERR_TOO_LARGE = 7,      /* a grid or index would overflow the kernel's limits    */
     FA_ERR_LAUNCH = 8,         /* the HIP launch failed (hipGetLastError)               */
-    FA_ERR_WINDOW = 9          /* fa_train_fwd_swa: window < 0                          */
+    FA_ERR_WINDOW = 9,         /* window < 0 (fa_train_fwd_swa); window >= 0 without
+                                  causal (fa_train_fwd_ex)                              */
+    FA_ERR_MASK = 10           /* fa_train_fwd_ex: unknown mask dtype or a negative
+                                  mask stride                                           */
+};
+
+/* Element types of an additive mask (fa_train_fwd_ex). */
+enum fa_mask_dtype {
+    FA_MASK_F32 = 0,
+    FA_MASK_BF16 = 1
 };
 
 /*
@@ -98,6 +107,41 @@ int fa_train_fwd(const void *q, const void *k, const void *v, const float *mask,
 int fa_train_fwd_swa(const void *q, const void *k, const void *v, const float *mask, int batch,
                      int n_heads, int n_kv_heads, int ql, int kl, int head_dim, float scale,
                      int window, void *O, float *L, void *stream);
+
+/*
+ * fa_train_fwd_ex - the forward with every option: mask element type, a mask
+ * broadcast over batch and/or heads, causal or sliding-window masking.
+ *
+ * The method's page passes its additive mask as bf16 ("mlx-native 0.9.0",
+ * tests/test_flash_attn_train.rs, section "Test helpers", run_train_fwd and
+ * FlashAttnTrainParams); an adjacent attention API on the pages ("nuvec-core
+ * 0.3.0", tests/fast.rs, attention_kernels_match_the_fallback) takes an
+ * additive mask of shape [1, H, ql, kl] that every batch shares. Both are
+ * accepted here; the operation is the one of fa_train_fwd with
+ *
+ *   mask[b,h,i,j] = mask[b * mask_stride_b + h * mask_stride_h + i * kl + j]
+ *
+ *   mask          NULL, or additive mask elements of type mask_dtype (device,
+ *                 read); each (b, h) slice is ql rows of kl contiguous
+ *                 elements. bf16 values are widened exactly to f32.
+ *   mask_dtype    FA_MASK_F32 or FA_MASK_BF16 (ignored when mask is NULL).
+ *   mask_stride_b, mask_stride_h
+ *                 element strides between batches and between heads, >= 0;
+ *                 0 broadcasts (e.g. 0 and ql*kl for a [1, H, ql, kl] mask).
+ *   causal        as for fa_train_fwd.
+ *   window        < 0: none; >= 0: the sliding window of fa_train_fwd_swa
+ *                 (requires causal != 0).
+ *   all others    as for fa_train_fwd.
+ *
+ * Alignment: an f32 mask 4 bytes, a bf16 mask 2 bytes. Returns the statuses
+ * of fa_train_fwd, FA_ERR_MASK for an unknown dtype or a negative stride,
+ * FA_ERR_WINDOW for a window without causal masking. fa_train_fwd(...) is
+ * fa_train_fwd_ex with an f32 mask, strides H*ql*kl and ql*kl, window -1.
+ */
+int fa_train_fwd_ex(const void *q, const void *k, const void *v, const void *mask,
+                    int mask_dtype, long long mask_stride_b, long long mask_stride_h, int batch,
+                    int n_heads, int n_kv_heads, int ql, int kl, int head_dim, float scale,
+                    int causal, int window, void *O, float *L, void *stream);
 
 /*
  * fa_train_bwd - enqueue the training backward pass of the same attention.

@@ -28,7 +28,8 @@ def _declared_functions():
 
 def test_header_declares_the_entry_points():
     names = _declared_functions()
-    assert {"fa_train_fwd", "fa_train_fwd_swa", "fa_train_bwd", "fa_status_string"} <= names
+    assert {"fa_train_fwd", "fa_train_fwd_swa", "fa_train_fwd_ex", "fa_train_bwd",
+            "fa_status_string"} <= names
 
 
 def test_library_exports_every_declared_symbol():
@@ -42,7 +43,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings_cover_all_codes():
-    for code in range(0, 10):
+    for code in range(0, 11):
         s = fa.status_string(code)
         assert s and s != "unknown status"
     assert fa.status_string(12345) == "unknown status"
@@ -104,6 +105,33 @@ def test_window_empty_problems_are_noops(over):
     assert _call_swa(**over) == 0
 
 
+EX_GOOD = dict(SWA_GOOD, mask=A, mask_dtype=0, mask_stride_b=0, mask_stride_h=64, causal=1,
+               window=-1)
+
+
+def _call_ex(**over):
+    args = dict(EX_GOOD)
+    args.update(over)
+    return fa.fa_train_fwd_ex(**args)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(mask_dtype=2), 10), (dict(mask_dtype=-1), 10), (dict(mask_stride_b=-1), 10),
+    (dict(mask_stride_h=-64), 10), (dict(causal=0, window=3), 9), (dict(mask=A + 2), 6),
+    (dict(mask=A + 1, mask_dtype=1), 6), (dict(q=0), 1), (dict(head_dim=32), 4),
+    (dict(n_heads=3, n_kv_heads=2), 3), (dict(scale=math.inf), 5), (dict(ql=-2), 2),
+    (dict(batch=65536, n_heads=65536, n_kv_heads=1, ql=1), 7),
+])
+def test_ex_invalid_arguments_are_rejected(over, code):
+    assert _call_ex(**over) == code
+
+
+@pytest.mark.parametrize("over", [dict(batch=0), dict(ql=0, mask_dtype=1, mask=A + 2),
+                                  dict(batch=0, mask=0, mask_dtype=7, mask_stride_b=-5)])
+def test_ex_empty_problems_are_noops(over):
+    assert _call_ex(**over) == 0
+
+
 def test_python_binding_fails_loudly_without_gpu_tensors():
     import torch
     q = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
@@ -113,6 +141,8 @@ def test_python_binding_fails_loudly_without_gpu_tensors():
         fa.train_fwd(q.float(), q, q)
     with pytest.raises(ValueError):
         fa.train_fwd_swa(q, q, q, 4)
+    with pytest.raises(ValueError):
+        fa.train_fwd_ex(q, q, q, mask=torch.zeros(1, 1, 4, 4, dtype=torch.bfloat16))
 
 
 BWD_GOOD = dict(q=A, k=A, v=A, mask=0, O=A, L=A, dO=A, batch=1, n_heads=2, n_kv_heads=1, ql=8,

@@ -44,8 +44,8 @@ def isa(tmp_path_factory):
 def test_all_variants_present(isa):
     fwd = [n for n in isa if "fa_fwd_kernel" in n]
     bwd = [n for n in isa if "fa_bwd_kernel" in n]
-    # head_dim x {none, causal, sliding window} x {mixed plain/compensated, compensated masked}
-    assert len(fwd) == 12
+    # head_dim x {none, causal, sliding window} x {mixed, compensated f32 mask, bf16 mask}
+    assert len(fwd) == 18
     assert len(bwd) == 16  # head_dim x {dQ, dKV} x causal x mask
 
 
