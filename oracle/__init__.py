@@ -39,6 +39,9 @@ def _bind(path):
     lib.fa_oracle_bwd.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64,
                                   ctypes.c_float, ctypes.c_int, vp, vp, vp, ctypes.c_int]
     lib.fa_oracle_bwd.restype = ctypes.c_int
+    lib.fa_oracle_bwd_swa.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64,
+                                      ctypes.c_float, ctypes.c_int, i64, vp, vp, vp, ctypes.c_int]
+    lib.fa_oracle_bwd_swa.restype = ctypes.c_int
     return lib
 
 
@@ -135,9 +138,10 @@ def fwd_rows(q, k, v, mask, B, H, Hkv, ql, kl, D, scale, causal, rows, n_threads
 
 
 def bwd(q, k, v, mask, L, dO, B, H, Hkv, ql, kl, D, scale, causal, n_threads=None,
-        lib=None):
+        lib=None, window=None):
     """Backward (the page's FA-2 backward oracle). q/k/v/dO: bf16 bits or f32;
-    mask f32 or None; L: the forward's natural-log logsumexp [B,H,ql].
+    mask f32 or None; L: the forward's natural-log logsumexp [B,H,ql];
+    window: None or a sliding window (>= 0, with causal).
 
     Returns (dQ [B,H,ql,D], dK [B,Hkv,kl,D], dV [B,Hkv,kl,D]), all f32."""
     qf, kf, vf, mf, lf, gf = _f32(q), _f32(k), _f32(v), _f32(mask), _f32(L), _f32(dO)
@@ -145,10 +149,17 @@ def bwd(q, k, v, mask, L, dO, B, H, Hkv, ql, kl, D, scale, causal, n_threads=Non
     dK = np.empty((B, Hkv, kl, D), dtype=np.float32)
     dV = np.empty((B, Hkv, kl, D), dtype=np.float32)
     lib = lib or _load()
-    rc = lib.fa_oracle_bwd(_ptr(qf), _ptr(kf), _ptr(vf), _ptr(mf), _ptr(lf), _ptr(gf), B, H,
-                           Hkv, ql, kl, D, float(scale), int(bool(causal)), _ptr(dQ), _ptr(dK),
-                           _ptr(dV), n_threads or default_threads())
-    _check(rc, "fa_oracle_bwd")
+    if window is not None:
+        rc = lib.fa_oracle_bwd_swa(_ptr(qf), _ptr(kf), _ptr(vf), _ptr(mf), _ptr(lf), _ptr(gf), B,
+                                   H, Hkv, ql, kl, D, float(scale), int(bool(causal)),
+                                   int(window), _ptr(dQ), _ptr(dK), _ptr(dV),
+                                   n_threads or default_threads())
+        _check(rc, "fa_oracle_bwd_swa")
+    else:
+        rc = lib.fa_oracle_bwd(_ptr(qf), _ptr(kf), _ptr(vf), _ptr(mf), _ptr(lf), _ptr(gf), B, H,
+                               Hkv, ql, kl, D, float(scale), int(bool(causal)), _ptr(dQ),
+                               _ptr(dK), _ptr(dV), n_threads or default_threads())
+        _check(rc, "fa_oracle_bwd")
     if kl == 0:
         dQ[...] = 0.0
     return dQ, dK, dV

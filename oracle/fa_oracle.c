@@ -303,6 +303,7 @@ typedef struct {
     int64_t H, Hkv, ql, kl, D;
     float scale;
     int causal;
+    int64_t window; /* < 0: no sliding window */
 } oracle_bwd_problem;
 
 /* Every query head of kv head (b, kvh), rows in order; dK/dV of that kv head
@@ -342,9 +343,14 @@ static void oracle_bwd_group(const oracle_bwd_problem *p, int64_t b, int64_t kvh
                         s[j] += m;
                 }
             }
+            const int64_t q_abs = (kl > ql ? kl - ql : 0) + i;
             if (p->causal) {
-                const int64_t q_abs = (kl > ql ? kl - ql : 0) + i;
                 for (int64_t j = q_abs + 1; j < kl; ++j)
+                    s[j] = -INFINITY;
+            }
+            /* sliding window, as in the forward */
+            if (p->window >= 0) {
+                for (int64_t j = 0; j < q_abs - p->window && j < kl; ++j)
                     s[j] = -INFINITY;
             }
             /* P from the forward's L */
@@ -403,11 +409,32 @@ static void *oracle_bwd_worker(void *arg)
  * Outputs dQ [B,H,ql,D], dK and dV [B,Hkv,kl,D], f32. Same return codes as
  * fa_oracle_fwd.
  */
+static int oracle_bwd_run(const oracle_bwd_problem *pp, int64_t B, int n_threads);
+int fa_oracle_bwd_swa(const float *q, const float *k, const float *v, const float *mask,
+                      const float *L, const float *dO, int64_t B, int64_t H, int64_t Hkv,
+                      int64_t ql, int64_t kl, int64_t D, float scale, int causal, int64_t window,
+                      float *dQ, float *dK, float *dV, int n_threads);
+
 int fa_oracle_bwd(const float *q, const float *k, const float *v, const float *mask,
                   const float *L, const float *dO, int64_t B, int64_t H, int64_t Hkv, int64_t ql,
                   int64_t kl, int64_t D, float scale, int causal, float *dQ, float *dK, float *dV,
                   int n_threads)
 {
+    return fa_oracle_bwd_swa(q, k, v, mask, L, dO, B, H, Hkv, ql, kl, D, scale, causal, -1, dQ,
+                             dK, dV, n_threads);
+}
+
+/*
+ * Backward with an optional sliding window (window >= 0; it comes with the
+ * causal rule, as in fa_oracle_fwd_swa, so causal must then be 1).
+ */
+int fa_oracle_bwd_swa(const float *q, const float *k, const float *v, const float *mask,
+                      const float *L, const float *dO, int64_t B, int64_t H, int64_t Hkv,
+                      int64_t ql, int64_t kl, int64_t D, float scale, int causal, int64_t window,
+                      float *dQ, float *dK, float *dV, int n_threads)
+{
+    if (window >= 0 && !causal)
+        return 2;
     int rc = oracle_validate(q, k, v, B, H, Hkv, ql, kl, D);
     if (rc)
         return rc;
@@ -415,7 +442,15 @@ int fa_oracle_bwd(const float *q, const float *k, const float *v, const float *m
         return 1;
     if (B * Hkv * kl > 0 && (!dK || !dV))
         return 1;
-    oracle_bwd_problem p = {q, k, v, mask, L, dO, dQ, dK, dV, H, Hkv, ql, kl, D, scale, causal};
+    oracle_bwd_problem p = {q, k, v, mask, L, dO, dQ, dK, dV, H, Hkv, ql, kl, D, scale, causal,
+                            window < 0 ? -1 : window};
+    return oracle_bwd_run(&p, B, n_threads);
+}
+
+static int oracle_bwd_run(const oracle_bwd_problem *pp, int64_t B, int n_threads)
+{
+    const oracle_bwd_problem p = *pp;
+    const int64_t Hkv = p.Hkv;
     const int64_t groups = B * Hkv;
     if (groups <= 0)
         return 0;

@@ -47,7 +47,7 @@ def attention_f64(q, k, v, mask, scale, causal, window=None):
     return O, L
 
 
-def attention_grads_f64(q, k, v, mask, dO, scale, causal):
+def attention_grads_f64(q, k, v, mask, dO, scale, causal, window=None):
     """Gradients of sum(O * dO) with respect to q, k, v for the same textbook
     definition, by torch's autograd in float64 on the CPU (a library routine
     serving as the differentiation step). Rows with no visible key have O = 0
@@ -63,10 +63,12 @@ def attention_grads_f64(q, k, v, mask, dO, scale, causal):
     s = scale * torch.matmul(qt, kr.transpose(-1, -2).contiguous())
     if mask is not None:
         s = s + t(mask)
-    if causal:
-        off = max(kl - ql, 0)
-        hide = torch.arange(kl)[None, :] > (off + torch.arange(ql)[:, None])
-        s = s.masked_fill(hide, float("-inf"))
+    off = max(kl - ql, 0)
+    q_abs = off + torch.arange(ql)[:, None]
+    if causal or window is not None:
+        s = s.masked_fill(torch.arange(kl)[None, :] > q_abs, float("-inf"))
+    if window is not None:
+        s = s.masked_fill(torch.arange(kl)[None, :] < q_abs - window, float("-inf"))
     live = torch.isfinite(s).any(dim=-1, keepdim=True)
     s = torch.where(live, s, torch.zeros_like(s))
     p = torch.softmax(s, dim=-1) * live

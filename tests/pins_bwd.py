@@ -25,8 +25,8 @@ def _case(seed, B, H, Hkv, ql, kl, D, masked):
     return q, k, v, dO, mask
 
 
-def _lse(q, k, v, mask, scale, causal):
-    _, L = attention_f64(_widen(q), _widen(k), _widen(v), mask, scale, causal)
+def _lse(q, k, v, mask, scale, causal, window=None):
+    _, L = attention_f64(_widen(q), _widen(k), _widen(v), mask, scale, causal, window)
     return L.astype(np.float32)
 
 
@@ -113,6 +113,36 @@ def pin_bwd_gqa(bwd):
     assert np.abs(dV - fold(dV2)).max() <= 1e-5 * max(1.0, np.abs(dV).max())
 
 
+def pin_bwd_window_autograd(bwd, B, H, Hkv, ql, kl, D, window, masked, seed):
+    """The sliding-window backward against float64 autograd of the textbook
+    definition restricted to the band q_abs - w <= j <= q_abs."""
+    scale = 1.0 / math.sqrt(D)
+    q, k, v, dO, mask = _case(seed, B, H, Hkv, ql, kl, D, masked)
+    L = _lse(q, k, v, mask, scale, True, window)
+    got = bwd(q, k, v, mask, L, dO, B, H, Hkv, ql, kl, D, scale, True, window=window)
+    ref = attention_grads_f64(_widen(q).reshape(B, H, ql, D), _widen(k).reshape(B, Hkv, kl, D),
+                              _widen(v).reshape(B, Hkv, kl, D), mask,
+                              _widen(dO).reshape(B, H, ql, D), scale, True, window)
+    for name, g, r in zip(("dQ", "dK", "dV"), got, ref):
+        err = np.abs(g - r).max() if r.size else 0.0
+        tol = 2e-5 * max(1.0, np.abs(r).max() if r.size else 1.0)
+        assert err <= tol, f"{name} vs f64 autograd (window {window}): {err:.3e} > {tol:.3e}"
+
+
+def pin_bwd_window_is_the_page_mask(bwd):
+    """A native window gives the bits of the page's own construction, the
+    0/-inf band mask run without the causal flag."""
+    from tests.pins import swa_mask
+    for (ql, kl, w) in [(12, 12, 3), (7, 15, 2), (15, 7, 4)]:
+        B, H, Hkv, D, scale = 1, 2, 1, 8, 0.4
+        q, k, v, dO, _ = _case(200 + ql + w, B, H, Hkv, ql, kl, D, False)
+        L = _lse(q, k, v, None, scale, True, w)
+        a = bwd(q, k, v, None, L, dO, B, H, Hkv, ql, kl, D, scale, True, window=w)
+        b = bwd(q, k, v, swa_mask(B, H, ql, kl, w), L, dO, B, H, Hkv, ql, kl, D, scale, False)
+        for x, y in zip(a, b):
+            assert np.array_equal(x, y), (ql, kl, w)
+
+
 AUTOGRAD_CASES = [
     # B, H, Hkv, ql, kl, D, causal, masked, seed
     (1, 1, 1, 1, 1, 4, False, False, 1),
@@ -130,4 +160,10 @@ ALL_PINS = [(f"autograd{c}", (lambda c: lambda f: pin_bwd_autograd(f, *c))(c))
     ("constant_v", pin_bwd_constant_v),
     ("zero_do", pin_bwd_zero_do),
     ("gqa", pin_bwd_gqa),
+    ("window_autograd", lambda f: pin_bwd_window_autograd(f, 2, 4, 2, 13, 13, 8, 4, True, 8)),
+    ("window_autograd_offset", lambda f: pin_bwd_window_autograd(f, 1, 2, 1, 9, 17, 16, 3, False,
+                                                                 9)),
+    ("window_autograd_ql_gt_kl", lambda f: pin_bwd_window_autograd(f, 1, 2, 2, 14, 6, 8, 2, False,
+                                                                   10)),
+    ("window_page_mask", pin_bwd_window_is_the_page_mask),
 ]

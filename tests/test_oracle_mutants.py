@@ -48,12 +48,12 @@ MUTANTS = {
                         "const float *qr = p->q + row * D;\n    const float *kh = p->k + kvh * kl * D;"),
     "v_row_off_by_one": ("const float *vr = vh + j * D;",
                          "const float *vr = vh + (j + 1 < kl ? j + 1 : j) * D;"),
-    "window_off_by_one": ("for (int64_t j = 0; j < q_abs - p->window && j < kl; ++j)",
-                          "for (int64_t j = 0; j <= q_abs - p->window && j < kl; ++j)"),
-    "window_too_wide": ("for (int64_t j = 0; j < q_abs - p->window && j < kl; ++j)",
-                        "for (int64_t j = 0; j < q_abs - p->window - 1 && j < kl; ++j)"),
-    "window_offset_dropped": ("for (int64_t j = 0; j < q_abs - p->window && j < kl; ++j)",
-                              "for (int64_t j = 0; j < i - p->window && j < kl; ++j)"),
+    "window_off_by_one": ("for (int64_t j = 0; j < q_abs - p->window && j < kl; ++j)\n            s[j]",
+                          "for (int64_t j = 0; j <= q_abs - p->window && j < kl; ++j)\n            s[j]"),
+    "window_too_wide": ("for (int64_t j = 0; j < q_abs - p->window && j < kl; ++j)\n            s[j]",
+                        "for (int64_t j = 0; j < q_abs - p->window - 1 && j < kl; ++j)\n            s[j]"),
+    "window_offset_dropped": ("for (int64_t j = 0; j < q_abs - p->window && j < kl; ++j)\n            s[j]",
+                              "for (int64_t j = 0; j < i - p->window && j < kl; ++j)\n            s[j]"),
     "window_ignored": ("\n    if (p->window >= 0) {", "\n    if (0) {"),
     "window_without_causal": ("oracle_problem p = {q, k, v, mask, H, Hkv, ql, kl, D, scale, 1, window};",
                               "oracle_problem p = {q, k, v, mask, H, Hkv, ql, kl, D, scale, 0, window};"),
@@ -111,6 +111,9 @@ BWD_MUTANTS = {
     "bwd_dp_uses_q": ("dp += dor[d] * vh[j * D + d];", "dp += qr[d] * vh[j * D + d];"),
     "bwd_mask_base2": ("s[j] += m;", "s[j] += 1.44269504f * m;"),
     "bwd_lse_ignored": ("expf(s[j] - l_i)", "expf(s[j])"),
+    "bwd_window_off_by_one": ("for (int64_t j = 0; j < q_abs - p->window && j < kl; ++j)\n                    s[j] = -INFINITY;",
+                              "for (int64_t j = 0; j <= q_abs - p->window && j < kl; ++j)\n                    s[j] = -INFINITY;"),
+    "bwd_window_ignored": ("if (p->window >= 0) {\n                for", "if (0) {\n                for"),
 }
 
 
