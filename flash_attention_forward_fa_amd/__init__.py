@@ -52,6 +52,9 @@ def lib():
         l.fa_train_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci,
                                    ctypes.c_float, ci, vp, vp, vp, vp]
         l.fa_train_bwd.restype = ci
+        l.fa_train_bwd_swa.argtypes = [vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci,
+                                       ctypes.c_float, ci, vp, vp, vp, vp]
+        l.fa_train_bwd_swa.restype = ci
         l.fa_status_string.argtypes = [ci]
         l.fa_status_string.restype = ctypes.c_char_p
         _lib = l
@@ -198,6 +201,23 @@ def fa_train_bwd(q, k, v, mask, O, L, dO, batch, n_heads, n_kv_heads, ql, kl, he
                               stream or None)
 
 
+def fa_train_bwd_swa(q, k, v, mask, O, L, dO, batch, n_heads, n_kv_heads, ql, kl, head_dim,
+                     scale, window, dQ, dK, dV, stream):
+    """The C entry point with raw integer pointers (0 for NULL); returns the status."""
+    return lib().fa_train_bwd_swa(q or None, k or None, v or None, mask or None, O or None,
+                                  L or None, dO or None, batch, n_heads, n_kv_heads, ql, kl,
+                                  head_dim, float(scale), int(window), dQ or None, dK or None,
+                                  dV or None, stream or None)
+
+
+def train_bwd_swa(q, k, v, O, L, dO, window, mask=None, scale=None, stream=None):
+    """dQ, dK, dV = train_bwd_swa(q, k, v, O, L, dO, window, mask=None, scale=None)
+
+    The backward of train_fwd_swa (same window); otherwise as train_bwd.
+    """
+    return _train_bwd(q, k, v, O, L, dO, mask, scale, True, int(window), stream)
+
+
 def train_bwd(q, k, v, O, L, dO, mask=None, scale=None, causal=False, stream=None):
     """dQ, dK, dV = train_bwd(q, k, v, O, L, dO, mask=None, scale=None, causal=False)
 
@@ -205,6 +225,10 @@ def train_bwd(q, k, v, O, L, dO, mask=None, scale=None, causal=False, stream=Non
     and L its outputs; dO (bf16, shaped like O) the upstream gradient. Returns
     bf16 dQ (like q), dK and dV (like k), enqueued on the current stream.
     """
+    return _train_bwd(q, k, v, O, L, dO, mask, scale, causal, None, stream)
+
+
+def _train_bwd(q, k, v, O, L, dO, mask, scale, causal, window, stream):
     import torch
 
     for name, t in (("q", q), ("k", k), ("v", v), ("O", O), ("dO", dO)):
@@ -230,11 +254,18 @@ def train_bwd(q, k, v, O, L, dO, mask=None, scale=None, causal=False, stream=Non
         scale = 1.0 / math.sqrt(D)
     dQ, dK, dV = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     s = stream if stream is not None else torch.cuda.current_stream(q.device)
+    mptr = mask.data_ptr() if mask is not None else 0
     with torch.cuda.device(q.device):
-        status = fa_train_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(),
-                              mask.data_ptr() if mask is not None else 0, O.data_ptr(),
-                              L.data_ptr(), dO.data_ptr(), B, H, Hkv, ql, kl, D, scale, causal,
-                              dQ.data_ptr(), dK.data_ptr(), dV.data_ptr(), s.cuda_stream)
+        if window is None:
+            status = fa_train_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), mptr, O.data_ptr(),
+                                  L.data_ptr(), dO.data_ptr(), B, H, Hkv, ql, kl, D, scale,
+                                  causal, dQ.data_ptr(), dK.data_ptr(), dV.data_ptr(),
+                                  s.cuda_stream)
+        else:
+            status = fa_train_bwd_swa(q.data_ptr(), k.data_ptr(), v.data_ptr(), mptr,
+                                      O.data_ptr(), L.data_ptr(), dO.data_ptr(), B, H, Hkv, ql,
+                                      kl, D, scale, window, dQ.data_ptr(), dK.data_ptr(),
+                                      dV.data_ptr(), s.cuda_stream)
     if status != 0:
         raise FAError(status, status_string(status))
     return dQ, dK, dV

@@ -13,7 +13,9 @@
 //   dV_j  = sum_i P_ij dO_i                     (dK, dV summed over a GQA group)
 //
 // (D_i = rowsum(dO_i * O_i) equals the page's sum_j P_ij dP_ij when O is the
-// forward's output.) Two launches, no atomics and no workspace: one kernel
+// forward's output.) The WINDOW variants apply the forward's sliding window
+// (key j visible to row i iff q_abs - window <= j <= q_abs) and stream only the
+// tiles inside the band. Two launches, no atomics and no workspace: one kernel
 // template serves both. A workgroup keeps a block of "fixed" rows in registers
 // and streams tiles of the other side through LDS:
 //
@@ -35,6 +37,7 @@
 #include <hip/hip_runtime.h>
 
 #include <float.h>
+#include <limits.h>
 #include <math.h>
 #include <stdint.h>
 
@@ -74,6 +77,7 @@ struct BwdArgs {
   int group;         // H / Hkv
   int n_ftiles;      // fixed-row tiles per (batch, head) of the fixed side
   int causal_off;    // max(kl - ql, 0)
+  int window;        // WINDOW variants: keys below q_abs - window are hidden
   float scale;       // signed softmax scale (multiplies dQ and dK)
   float c;           // scale * log2(e), never 0 (exp2 argument factor)
 };
@@ -82,7 +86,7 @@ struct BwdArgs {
 // +inf, so that every P of that row is 0
 __device__ __forceinline__ float lse2(float l) { return l == -INFINITY ? INFINITY : l * kLog2e; }
 
-template <int D, int PASS, bool CAUSAL, bool HAS_MASK>
+template <int D, int PASS, bool CAUSAL, bool WINDOW, bool HAS_MASK>
 __global__ __launch_bounds__((64 * BwdCfg<D, PASS>::W))
 __attribute__((amdgpu_waves_per_eu(BwdCfg<D, PASS>::WPE))) void fa_bwd_kernel(BwdArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
@@ -97,6 +101,7 @@ __attribute__((amdgpu_waves_per_eu(BwdCfg<D, PASS>::WPE))) void fa_bwd_kernel(Bw
   constexpr int TILE = BN * D;
   constexpr int NT = 64 * C::W;
   constexpr bool KV = PASS == kBwdKV;
+  static_assert(CAUSAL || !WINDOW, "the sliding window includes the causal rule");
   __shared__ __attribute__((aligned(1024))) uint16_t y1s[2][TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t y2s[2][TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t yos[2][KV ? TILE : 8];  // dKV pass: O
@@ -175,21 +180,26 @@ __attribute__((amdgpu_waves_per_eu(BwdCfg<D, PASS>::WPE))) void fa_bwd_kernel(Bw
     }
 
   // ---- streamed range ----
-  // dQ pass: keys 0 .. kend of kv head g. dKV pass: for every query head of the
-  // group, the query tiles from the first one that sees the workgroup's first key.
+  // dQ pass: keys 0 .. kend of kv head g (under a window, from the first key the
+  // workgroup's first row sees). dKV pass: for every query head of the group,
+  // the query tiles from the first one that sees the workgroup's first key
+  // (under a window, up to the last one that still sees its last key).
   const int flast = min(f0 + FR, nfixed) - 1;
   int n_per = 0, st_lo = 0;
   if constexpr (!KV) {
     const int kend = CAUSAL ? min(kl, off + flast + 1) : kl;
-    n_per = kend > 0 ? (kend + BN - 1) / BN : 0;
+    st_lo = WINDOW ? max(0, off + f0 - a.window) / BN : 0;
+    n_per = kend > 0 ? max(0, (kend + BN - 1) / BN - st_lo) : 0;
   } else {
     const int n_qt = (ql + BN - 1) / BN;
     st_lo = CAUSAL ? max(0, f0 - off) / BN : 0;
-    n_per = max(0, n_qt - st_lo);
+    const int q_last = flast - off + (WINDOW ? a.window : 0);  // last query seeing key flast
+    const int st_hi = !WINDOW ? n_qt : q_last < 0 ? 0 : min(n_qt, q_last / BN + 1);
+    n_per = max(0, st_hi - st_lo);
   }
   const int n_st = KV ? a.group * n_per : n_per;
   auto tile_head = [&](int t) { return KV ? g * a.group + t / n_per : hf; };
-  auto tile_first = [&](int t) { return KV ? (st_lo + t % n_per) * BN : t * BN; };
+  auto tile_first = [&](int t) { return (st_lo + (KV ? t % n_per : t)) * BN; };
   auto y1_src = [&](int t) -> const uint16_t* {
     return KV ? a.q + (int64_t)(b * a.H + tile_head(t)) * ql * D : a.k + kv_base;
   };
@@ -297,11 +307,15 @@ __attribute__((amdgpu_waves_per_eu(BwdCfg<D, PASS>::WPE))) void fa_bwd_kernel(Bw
     if constexpr (!KV) {
       const int wlast = min(fw0 + 16 * FB, nfixed) - 1;
       if (CAUSAL) any = any && sbase <= off + wlast;
-      need_mask = sbase + BN > kl || (CAUSAL && sbase + BN - 1 > off + fw0);
+      if (WINDOW) any = any && sbase + BN - 1 >= off + fw0 - a.window;
+      need_mask = sbase + BN > kl || (CAUSAL && sbase + BN - 1 > off + fw0) ||
+                  (WINDOW && sbase < off + wlast - a.window);
     } else {
       const int wlast = min(fw0 + 16 * FB, nfixed) - 1;
       if (CAUSAL) any = any && sbase + BN - 1 >= fw0 - off;
-      need_mask = sbase + BN > ql || (CAUSAL && sbase < wlast - off);
+      if (WINDOW) any = any && sbase <= wlast - off + a.window;
+      need_mask = sbase + BN > ql || (CAUSAL && sbase < wlast - off) ||
+                  (WINDOW && sbase + BN - 1 > fw0 - off + a.window);
     }
     if (!any) continue;
     const uint16_t* b1 = y1s[buf];
@@ -313,6 +327,17 @@ __attribute__((amdgpu_waves_per_eu(BwdCfg<D, PASS>::WPE))) void fa_bwd_kernel(Bw
 #pragma unroll
     for (int fb = 0; fb < FB; ++fb) {
       const int frow = fw0 + 16 * fb + c16;  // fixed row of this lane
+      // the streamed rows [s_lo, s_hi] this fixed row sees (causal, window);
+      // rows at or past s_end do not exist
+      const int s_end = KV ? ql : kl;
+      int s_lo = INT_MIN, s_hi = INT_MAX;
+      if constexpr (KV) {
+        if (CAUSAL) s_lo = frow - off;
+        if (WINDOW) s_hi = frow - off + a.window;
+      } else {
+        if (WINDOW) s_lo = off + frow - a.window;
+        if (CAUSAL) s_hi = off + frow;
+      }
 #pragma unroll
       for (int j = 0; j < NKC; ++j)
 #pragma unroll
@@ -331,7 +356,7 @@ __attribute__((amdgpu_waves_per_eu(BwdCfg<D, PASS>::WPE))) void fa_bwd_kernel(Bw
           }
           const int qi = KV ? sr : frow, kj = KV ? frow : sr;
           bool vis = true;
-          if (need_mask) vis = (KV ? qi < ql : kj < kl) && (!CAUSAL || kj <= off + qi);
+          if (need_mask) vis = sr < s_end && sr >= s_lo && sr <= s_hi;
           float x;
           if constexpr (HAS_MASK) {
             const int h = KV ? th : hf;
@@ -398,44 +423,49 @@ __attribute__((amdgpu_waves_per_eu(BwdCfg<D, PASS>::WPE))) void fa_bwd_kernel(Bw
 #endif
 }
 
-template <int D, int PASS, bool CAUSAL, bool HAS_MASK>
+template <int D, int PASS, bool CAUSAL, bool WINDOW, bool HAS_MASK>
 hipError_t launch_bwd(const BwdArgs& a, unsigned grid, hipStream_t stream) {
-  hipLaunchKernelGGL((fa_bwd_kernel<D, PASS, CAUSAL, HAS_MASK>), dim3(grid),
+  hipLaunchKernelGGL((fa_bwd_kernel<D, PASS, CAUSAL, WINDOW, HAS_MASK>), dim3(grid),
                      dim3(64 * BwdCfg<D, PASS>::W), 0, stream, a);
   return hipGetLastError();
 }
 
-template <int D, bool CAUSAL, bool HAS_MASK>
+template <int D, bool CAUSAL, bool WINDOW, bool HAS_MASK>
 hipError_t dispatch_bwd(BwdArgs a, hipStream_t stream) {
   if (a.ql > 0) {
     a.n_ftiles = (a.ql + fixed_rows<D, kBwdQ>() - 1) / fixed_rows<D, kBwdQ>();
-    hipError_t e = launch_bwd<D, kBwdQ, CAUSAL, HAS_MASK>(
+    hipError_t e = launch_bwd<D, kBwdQ, CAUSAL, WINDOW, HAS_MASK>(
         a, (unsigned)(a.n_ftiles * a.B * a.H), stream);
     if (e != hipSuccess) return e;
   }
   if (a.kl > 0) {
     a.n_ftiles = (a.kl + fixed_rows<D, kBwdKV>() - 1) / fixed_rows<D, kBwdKV>();
-    return launch_bwd<D, kBwdKV, CAUSAL, HAS_MASK>(a, (unsigned)(a.n_ftiles * a.B * a.Hkv),
-                                                  stream);
+    return launch_bwd<D, kBwdKV, CAUSAL, WINDOW, HAS_MASK>(
+        a, (unsigned)(a.n_ftiles * a.B * a.Hkv), stream);
   }
   return hipSuccess;
 }
 
 template <int D>
-hipError_t dispatch_bwd_d(const BwdArgs& a, bool causal, bool has_mask, hipStream_t s) {
+hipError_t dispatch_bwd_d(const BwdArgs& a, bool causal, bool window, bool has_mask,
+                          hipStream_t s) {
+  if (window)
+    return has_mask ? dispatch_bwd<D, true, true, true>(a, s)
+                    : dispatch_bwd<D, true, true, false>(a, s);
   if (causal)
-    return has_mask ? dispatch_bwd<D, true, true>(a, s) : dispatch_bwd<D, true, false>(a, s);
-  return has_mask ? dispatch_bwd<D, false, true>(a, s) : dispatch_bwd<D, false, false>(a, s);
+    return has_mask ? dispatch_bwd<D, true, false, true>(a, s)
+                    : dispatch_bwd<D, true, false, false>(a, s);
+  return has_mask ? dispatch_bwd<D, false, false, true>(a, s)
+                  : dispatch_bwd<D, false, false, false>(a, s);
 }
 
 bool aligned_to(const void* p, uintptr_t n) { return ((uintptr_t)p % n) == 0; }
 
-}  // namespace
-
-extern "C" int fa_train_bwd(const void* q, const void* k, const void* v, const float* mask,
-                            const void* O, const float* L, const void* dO, int batch, int n_heads,
-                            int n_kv_heads, int ql, int kl, int head_dim, float scale, int causal,
-                            void* dQ, void* dK, void* dV, void* stream) {
+// Shared host path of fa_train_bwd and fa_train_bwd_swa; window < 0: none.
+int train_bwd(const void* q, const void* k, const void* v, const float* mask, const void* O,
+              const float* L, const void* dO, int batch, int n_heads, int n_kv_heads, int ql,
+              int kl, int head_dim, float scale, int causal, int window, void* dQ, void* dK,
+              void* dV, void* stream) {
   if (batch < 0 || ql < 0 || kl < 0 || n_heads < 1 || n_kv_heads < 1) return FA_ERR_BAD_SIZE;
   if (n_heads % n_kv_heads != 0) return FA_ERR_HEAD_GROUPING;
   if (head_dim != 64 && head_dim != 256) return FA_ERR_HEAD_DIM;
@@ -476,6 +506,9 @@ extern "C" int fa_train_bwd(const void* q, const void* k, const void* v, const f
   a.group = n_heads / n_kv_heads;
   a.n_ftiles = 0;
   a.causal_off = kl > ql ? kl - ql : 0;
+  // (a window past the largest q_abs hides nothing more; clamped there so that
+  // q_abs - window stays in int range)
+  a.window = window >= 0 ? (int)std::min<int64_t>(window, (int64_t)a.causal_off + ql) : 0;
   a.scale = scale;
   // a zero scale runs with the smallest normal exp2 factor (the scores it
   // produces round to 0, so P is the same uniform one); dQ and dK use the
@@ -483,7 +516,29 @@ extern "C" int fa_train_bwd(const void* q, const void* k, const void* v, const f
   const float c = scale * kLog2e;
   a.c = c == 0.0f ? FLT_MIN : c;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const hipError_t err = head_dim == 64 ? dispatch_bwd_d<64>(a, causal != 0, mask != nullptr, s)
-                                        : dispatch_bwd_d<256>(a, causal != 0, mask != nullptr, s);
+  const bool windowed = window >= 0;
+  const hipError_t err =
+      head_dim == 64 ? dispatch_bwd_d<64>(a, causal != 0, windowed, mask != nullptr, s)
+                     : dispatch_bwd_d<256>(a, causal != 0, windowed, mask != nullptr, s);
   return err == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" int fa_train_bwd(const void* q, const void* k, const void* v, const float* mask,
+                            const void* O, const float* L, const void* dO, int batch, int n_heads,
+                            int n_kv_heads, int ql, int kl, int head_dim, float scale, int causal,
+                            void* dQ, void* dK, void* dV, void* stream) {
+  return train_bwd(q, k, v, mask, O, L, dO, batch, n_heads, n_kv_heads, ql, kl, head_dim, scale,
+                   causal, -1, dQ, dK, dV, stream);
+}
+
+extern "C" int fa_train_bwd_swa(const void* q, const void* k, const void* v, const float* mask,
+                                const void* O, const float* L, const void* dO, int batch,
+                                int n_heads, int n_kv_heads, int ql, int kl, int head_dim,
+                                float scale, int window, void* dQ, void* dK, void* dV,
+                                void* stream) {
+  if (window < 0) return FA_ERR_WINDOW;
+  return train_bwd(q, k, v, mask, O, L, dO, batch, n_heads, n_kv_heads, ql, kl, head_dim, scale, 1,
+                   window, dQ, dK, dV, stream);
 }

@@ -179,6 +179,20 @@ int fa_train_bwd(const void *q, const void *k, const void *v, const float *mask,
                  int kl, int head_dim, float scale, int causal, void *dQ, void *dK, void *dV,
                  void *stream);
 
+/*
+ * fa_train_bwd_swa - the backward of fa_train_fwd_swa: the gradients of the
+ * sliding-window causal attention (key j visible to query row i iff
+ * q_abs - window <= j <= q_abs, q_abs = max(kl - ql, 0) + i). Arguments,
+ * layouts, outputs and statuses are those of fa_train_bwd with causal = 1 and
+ * `window` in its place (FA_ERR_WINDOW for window < 0); O and L must come from
+ * fa_train_fwd_swa with the same window. Only the key/query tiles inside the
+ * band are read.
+ */
+int fa_train_bwd_swa(const void *q, const void *k, const void *v, const float *mask,
+                     const void *O, const float *L, const void *dO, int batch, int n_heads,
+                     int n_kv_heads, int ql, int kl, int head_dim, float scale, int window,
+                     void *dQ, void *dK, void *dV, void *stream);
+
 /* Static, human-readable name of a status code (never NULL). */
 const char *fa_status_string(int status);
 

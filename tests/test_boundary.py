@@ -29,7 +29,7 @@ def _declared_functions():
 def test_header_declares_the_entry_points():
     names = _declared_functions()
     assert {"fa_train_fwd", "fa_train_fwd_swa", "fa_train_fwd_ex", "fa_train_bwd",
-            "fa_status_string"} <= names
+            "fa_train_bwd_swa", "fa_status_string"} <= names
 
 
 def test_library_exports_every_declared_symbol():
@@ -172,6 +172,13 @@ def test_backward_invalid_arguments_are_rejected(over, code):
                                   dict(batch=0, q=0, k=0, v=0, O=0, L=0, dO=0, dQ=0, dK=0, dV=0)])
 def test_backward_empty_problems_are_noops(over):
     assert _call_bwd(**over) == 0
+
+
+def test_backward_window_rejects_negative_window():
+    args = {k: v for k, v in BWD_GOOD.items() if k != "causal"}
+    assert fa.fa_train_bwd_swa(**args, window=-1) == 9
+    assert fa.fa_train_bwd_swa(**dict(args, q=0), window=3) == 1
+    assert fa.fa_train_bwd_swa(**dict(args, batch=0), window=3) == 0
 
 
 def test_backward_binding_fails_loudly_without_gpu_tensors():

@@ -49,7 +49,7 @@ def _mask(kind, seed, B, H, ql, kl):
     return m
 
 
-def _run_case(name, B, H, Hkv, ql, kl, D, causal, mask_kind, seed_off):
+def _run_case(name, B, H, Hkv, ql, kl, D, causal, mask_kind, seed_off, window=None):
     import torch
     import flash_attention_forward_fa_amd as fa
     print(f"case bwd {name}: B{B} H{H}/{Hkv} ql{ql} kl{kl} D{D} causal={causal} "
@@ -64,12 +64,16 @@ def _run_case(name, B, H, Hkv, ql, kl, D, causal, mask_kind, seed_off):
     dev = "cuda:0"
     qd, kd, vd, gd = (gu.to_dev(x, dev) for x in (q, k, v, dO))
     md = None if mask is None else gu.to_dev(mask, dev)
-    O, L = fa.train_fwd(qd, kd, vd, mask=md, scale=scale, causal=causal)
-    dQ, dK, dV = fa.train_bwd(qd, kd, vd, O, L, gd, mask=md, scale=scale, causal=causal)
+    if window is None:
+        O, L = fa.train_fwd(qd, kd, vd, mask=md, scale=scale, causal=causal)
+        dQ, dK, dV = fa.train_bwd(qd, kd, vd, O, L, gd, mask=md, scale=scale, causal=causal)
+    else:
+        O, L = fa.train_fwd_swa(qd, kd, vd, window, mask=md, scale=scale)
+        dQ, dK, dV = fa.train_bwd_swa(qd, kd, vd, O, L, gd, window, mask=md, scale=scale)
     torch.cuda.synchronize()
     got = [gu.widen(t.view(torch.int16).cpu().numpy().view(np.uint16)) for t in (dQ, dK, dV)]
-    _, _, Lr = oracle.fwd(q, k, v, mask, B, H, Hkv, ql, kl, D, scale, causal)
-    ref = oracle.bwd(q, k, v, mask, Lr, dO, B, H, Hkv, ql, kl, D, scale, causal)
+    _, _, Lr = oracle.fwd(q, k, v, mask, B, H, Hkv, ql, kl, D, scale, causal, window=window)
+    ref = oracle.bwd(q, k, v, mask, Lr, dO, B, H, Hkv, ql, kl, D, scale, causal, window=window)
     errs = []
     for tname, g, r in zip(("dQ", "dK", "dV"), got, ref):
         assert not np.isnan(g).any(), f"{name}: NaN in {tname}"
@@ -129,3 +133,45 @@ def test_backward_constant_v_gives_zero_dq_dk():
     # in f32: dS is rounding noise
     assert float(dQ.float().abs().max()) <= 2e-3
     assert float(dK.float().abs().max()) <= 2e-3
+
+
+WINDOW_CASES = [
+    # name, B, H, Hkv, ql, kl, D, window, mask
+    ("swa_page8", 1, 1, 1, 32, 32, 64, 8, None),       # the page's backward window case
+    ("swa_d64", 2, 4, 2, 300, 300, 64, 100, None),
+    ("swa_d64_wide", 1, 2, 1, 700, 700, 64, 300, None),
+    ("swa_offset", 1, 2, 2, 150, 400, 64, 130, None),
+    ("swa_ql_gt_kl", 1, 2, 1, 400, 150, 64, 90, None),
+    ("swa_masked", 2, 2, 2, 64, 256, 64, 70, "random"),
+    ("swa_d256", 1, 4, 1, 300, 300, 256, 100, None),
+    ("swa_d256_gqa", 2, 8, 2, 260, 260, 256, 64, None),
+    ("swa_d256_masked", 1, 2, 1, 96, 130, 256, 40, "random"),
+    ("swa_zero", 1, 2, 1, 100, 100, 64, 0, None),
+]
+
+
+@pytest.mark.parametrize("case", WINDOW_CASES, ids=[c[0] for c in WINDOW_CASES])
+def test_window_backward_matches_oracle(case):
+    name, B, H, Hkv, ql, kl, D, window, mask = case
+    _run_case(name, B, H, Hkv, ql, kl, D, True, mask, seed_off=200 + WINDOW_CASES.index(case),
+              window=window)
+
+
+def test_window_backward_wide_equals_causal_bit_for_bit():
+    """A window that hides nothing beyond the causal rule gives the causal
+    backward's bits."""
+    import torch
+    import flash_attention_forward_fa_amd as fa
+    for D in (64, 256):
+        B, H, Hkv, ql, kl = 1, 4, 2, 300, 340
+        seed = fagen.SEED_BASE + 7700 + D
+        q, k, v, dO = (gu.to_dev(fagen.normal_bf16(seed, st, shp), "cuda:0") for st, shp in
+                       ((0, (B, H, ql, D)), (1, (B, Hkv, kl, D)), (2, (B, Hkv, kl, D)),
+                        (6, (B, H, ql, D))))
+        print(f"case bwd wide window D={D}", flush=True)
+        O, L = fa.train_fwd(q, k, v, causal=True)
+        a = fa.train_bwd(q, k, v, O, L, dO, causal=True)
+        b = fa.train_bwd_swa(q, k, v, O, L, dO, 10 ** 6)
+        torch.cuda.synchronize()
+        for x, y in zip(a, b):
+            assert torch.equal(x.view(torch.int16), y.view(torch.int16))

@@ -46,7 +46,7 @@ def test_all_variants_present(isa):
     bwd = [n for n in isa if "fa_bwd_kernel" in n]
     # head_dim x {none, causal, sliding window} x {mixed, compensated f32 mask, bf16 mask}
     assert len(fwd) == 18
-    assert len(bwd) == 16  # head_dim x {dQ, dKV} x causal x mask
+    assert len(bwd) == 24  # head_dim x {dQ, dKV} x {none, causal, sliding window} x mask
 
 
 _OPEN = (re.compile(r"s_(?:and|andn2|or)_saveexec_b64 (s\[\d+:\d+\])"),
