@@ -204,6 +204,25 @@ def main():
                            "frac_of_peak": flop / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
             log(f"{w.name}: sliding window {win}: {ms * 1e3:.1f} us/call, "
                 f"{swa[w.name]['tflops']:.1f} TFLOP/s (4*D per visible score)")
+            if args.backward_steps > 0:
+                # its backward on the window forward's O and L (FA-2 count, 10*D
+                # FLOP per visible score)
+                dO = torch.from_numpy(fagen.normal_bf16(w.seed, 6, (w.B, w.H, w.ql, w.D))
+                                      .view(np.int16)).view(torch.bfloat16).to(dev)
+                for _ in range(2):
+                    fa.train_bwd_swa(q, k, v, O, L, dO, win, scale=w.scale)
+                torch.cuda.synchronize()
+                a.record(stream)
+                for _ in range(args.window_steps):
+                    fa.train_bwd_swa(q, k, v, O, L, dO, win, scale=w.scale)
+                b.record(stream)
+                torch.cuda.synchronize()
+                bms = a.elapsed_time(b) / args.window_steps
+                bflop = 2.5 * flop
+                swa[w.name].update({"backward_ms_avg": bms, "backward_flop_fa2": bflop,
+                                    "backward_tflops": bflop / (bms * 1e-3) / 1e12})
+                log(f"{w.name}: sliding window {win} backward: {bms * 1e3:.1f} us/call, "
+                    f"{swa[w.name]['backward_tflops']:.1f} TFLOP/s (FA-2 count)")
         # leave the causal forward's outputs in place for anything read later
         for w in workloads:
             launch(w)
