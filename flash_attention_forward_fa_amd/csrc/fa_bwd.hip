@@ -56,6 +56,8 @@ constexpr int kBwdQ = 0, kBwdKV = 1;
 template <int D, int PASS> struct BwdCfg;
 template <> struct BwdCfg<64, kBwdQ> { static constexpr int W = 8, FB = 2, BN = 64, WPE = 2; };
 template <> struct BwdCfg<64, kBwdKV> { static constexpr int W = 8, FB = 2, BN = 64, WPE = 2; };
+template <> struct BwdCfg<128, kBwdQ> { static constexpr int W = 8, FB = 1, BN = 64, WPE = 2; };
+template <> struct BwdCfg<128, kBwdKV> { static constexpr int W = 8, FB = 1, BN = 64, WPE = 2; };
 template <> struct BwdCfg<256, kBwdQ> { static constexpr int W = 8, FB = 1, BN = 64, WPE = 2; };
 template <> struct BwdCfg<256, kBwdKV> { static constexpr int W = 4, FB = 1, BN = 32, WPE = 1; };
 template <int D, int PASS> constexpr int fixed_rows() {
@@ -468,7 +470,7 @@ int train_bwd(const void* q, const void* k, const void* v, const float* mask, co
               void* dV, void* stream) {
   if (batch < 0 || ql < 0 || kl < 0 || n_heads < 1 || n_kv_heads < 1) return FA_ERR_BAD_SIZE;
   if (n_heads % n_kv_heads != 0) return FA_ERR_HEAD_GROUPING;
-  if (head_dim != 64 && head_dim != 256) return FA_ERR_HEAD_DIM;
+  if (head_dim != 64 && head_dim != 128 && head_dim != 256) return FA_ERR_HEAD_DIM;
   if (!isfinite(scale)) return FA_ERR_SCALE;
   const int64_t qrows = (int64_t)batch * n_heads * ql;
   const int64_t krows = (int64_t)batch * n_kv_heads * kl;
@@ -480,8 +482,12 @@ int train_bwd(const void* q, const void* k, const void* v, const float* mask, co
   for (const void* p : a16)
     if (p && !aligned_to(p, 16)) return FA_ERR_ALIGNMENT;
   if ((L && !aligned_to(L, 4)) || (mask && !aligned_to(mask, 4))) return FA_ERR_ALIGNMENT;
-  const int64_t rq = head_dim == 64 ? fixed_rows<64, kBwdQ>() : fixed_rows<256, kBwdQ>();
-  const int64_t rk = head_dim == 64 ? fixed_rows<64, kBwdKV>() : fixed_rows<256, kBwdKV>();
+  const int64_t rq = head_dim == 64    ? fixed_rows<64, kBwdQ>()
+                     : head_dim == 128 ? fixed_rows<128, kBwdQ>()
+                                       : fixed_rows<256, kBwdQ>();
+  const int64_t rk = head_dim == 64    ? fixed_rows<64, kBwdKV>()
+                     : head_dim == 128 ? fixed_rows<128, kBwdKV>()
+                                       : fixed_rows<256, kBwdKV>();
   if ((ql + rq - 1) / rq * batch * n_heads > 0x7fffffffLL ||
       (kl + rk - 1) / rk * batch * n_kv_heads > 0x7fffffffLL ||
       (int64_t)kl * head_dim * 2 > 0x7fffffffLL || (int64_t)ql * head_dim * 2 > 0x7fffffffLL)
@@ -518,8 +524,9 @@ int train_bwd(const void* q, const void* k, const void* v, const float* mask, co
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool windowed = window >= 0;
   const hipError_t err =
-      head_dim == 64 ? dispatch_bwd_d<64>(a, causal != 0, windowed, mask != nullptr, s)
-                     : dispatch_bwd_d<256>(a, causal != 0, windowed, mask != nullptr, s);
+      head_dim == 64    ? dispatch_bwd_d<64>(a, causal != 0, windowed, mask != nullptr, s)
+      : head_dim == 128 ? dispatch_bwd_d<128>(a, causal != 0, windowed, mask != nullptr, s)
+                        : dispatch_bwd_d<256>(a, causal != 0, windowed, mask != nullptr, s);
   return err == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 

@@ -64,7 +64,8 @@ __device__ __forceinline__ int key_of(int kb, int m) {
 // the K rows one ds_read_b128 reaches (keys key_of(kb, 0..15)) and the V rows
 // the 16-lane groups of one ds_read_b64_tr_b16 reach (four rows per group)
 // all come out conflict-free with these, for 128-byte (D=64) and 512-byte
-// (D=256) rows.
+// (D=256) rows; 256-byte (D=128) rows use the D=256 permutations (any value
+// below the row's 16 chunks is a valid permutation).
 template <int D> __device__ __forceinline__ int kswz(int r) {
   return D == 64 ? ((r & 3) | ((r >> 1) & 4)) : ((r & 3) | ((r >> 1) & 12));
 }

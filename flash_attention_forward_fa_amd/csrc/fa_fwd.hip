@@ -53,6 +53,10 @@ namespace {
 //          the barriers per key against 32 (measured 5% faster).
 template <int D> struct Cfg;
 template <> struct Cfg<64> { static constexpr int W = 8, QB = 2, BN = 64, WPE = 4; };
+//   D=128: 2 blocks (32 rows per wave, 256 per workgroup), 64-key tiles; the O
+//          accumulator of 32 rows x 128 dims is 64 registers per lane, two waves
+//          per SIMD.
+template <> struct Cfg<128> { static constexpr int W = 8, QB = 2, BN = 64, WPE = 2; };
 template <> struct Cfg<256> { static constexpr int W = 8, QB = 1, BN = 64, WPE = 2; };
 template <int D> constexpr int block_m() { return Cfg<D>::W * 16 * Cfg<D>::QB; }
 
@@ -242,7 +246,7 @@ __device__ __forceinline__ bool fwd_tile(const FwdArgs& a, int qtile, int bh, ui
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int qb = 0; qb < kQB; ++qb) sacc[kb][qb] = f32x4{};
-    if constexpr (D == 64) {
+    if constexpr (D <= 128) {
 #pragma unroll
       for (int s = 0; s < NDS; ++s)
 #pragma unroll
@@ -427,7 +431,7 @@ __device__ __forceinline__ bool fwd_tile(const FwdArgs& a, int qtile, int bh, ui
     }
   };
   auto pv = [&](const uint16_t* vs, const bf16x8 (&phi)[NKC][kQB], const bf16x8 (&plo)[NKC][kQB]) {
-    if constexpr (D == 64) {
+    if constexpr (D <= 128) {
 #pragma unroll
       for (int d = 0; d < NDB; ++d)
 #pragma unroll
@@ -650,7 +654,7 @@ int train_fwd(const void* q, const void* k, const void* v, const void* mask, int
               void* stream) {
   if (batch < 0 || ql < 0 || kl < 0 || n_heads < 1 || n_kv_heads < 1) return FA_ERR_BAD_SIZE;
   if (n_heads % n_kv_heads != 0) return FA_ERR_HEAD_GROUPING;
-  if (head_dim != 64 && head_dim != 256) return FA_ERR_HEAD_DIM;
+  if (head_dim != 64 && head_dim != 128 && head_dim != 256) return FA_ERR_HEAD_DIM;
   if (!isfinite(scale)) return FA_ERR_SCALE;
   if (window >= 0 && !causal) return FA_ERR_WINDOW;
   if (mask && ((mask_dtype != FA_MASK_F32 && mask_dtype != FA_MASK_BF16) || mask_sb < 0 ||
@@ -664,7 +668,9 @@ int train_fwd(const void* q, const void* k, const void* v, const void* mask, int
       (kv_used && (!aligned(k, 16) || !aligned(v, 16))) ||
       (mask && !aligned(mask, mask_dtype == FA_MASK_BF16 ? 2 : 4)))
     return FA_ERR_ALIGNMENT;
-  const int bm = head_dim == 64 ? block_m<64>() : block_m<256>();
+  const int bm = head_dim == 64    ? block_m<64>()
+                 : head_dim == 128 ? block_m<128>()
+                                   : block_m<256>();
   const int64_t n_qtiles = ((int64_t)ql + bm - 1) / bm;
   const int64_t grid = n_qtiles * batch * n_heads;
   if (grid > 0x7fffffffLL || (int64_t)batch * n_heads > 0x7fffffffLL ||
@@ -712,9 +718,9 @@ int train_fwd(const void* q, const void* k, const void* v, const void* mask, int
   else if ((causal || windowed) && a.causal_off + 1 < kPreciseKeys)
     n_short = std::min<int64_t>(n_qtiles, (kPreciseKeys - 1 - a.causal_off + bm - 1) / bm);
   hipError_t err =
-      head_dim == 64
-          ? dispatch_d<64>(a, causal != 0, windowed, mask_kind, (int)n_short, s)
-          : dispatch_d<256>(a, causal != 0, windowed, mask_kind, (int)n_short, s);
+      head_dim == 64    ? dispatch_d<64>(a, causal != 0, windowed, mask_kind, (int)n_short, s)
+      : head_dim == 128 ? dispatch_d<128>(a, causal != 0, windowed, mask_kind, (int)n_short, s)
+                        : dispatch_d<256>(a, causal != 0, windowed, mask_kind, (int)n_short, s);
   return err == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
@@ -754,7 +760,7 @@ extern "C" const char* fa_status_string(int status) {
     case FA_ERR_NULL_POINTER: return "a required pointer is NULL";
     case FA_ERR_BAD_SIZE: return "invalid size (batch, ql, kl < 0 or head counts < 1)";
     case FA_ERR_HEAD_GROUPING: return "n_heads is not a multiple of n_kv_heads";
-    case FA_ERR_HEAD_DIM: return "head_dim must be 64 or 256";
+    case FA_ERR_HEAD_DIM: return "head_dim must be 64, 128 or 256";
     case FA_ERR_SCALE: return "scale must be finite";
     case FA_ERR_ALIGNMENT:
       return "misaligned tensor (q, k, v, O need 16 bytes; L and an f32 mask 4, a bf16 mask 2)";

@@ -33,7 +33,7 @@ enum fa_status {
     FA_ERR_NULL_POINTER = 1,   /* q, k, v, O or L is NULL while its tensor is non-empty */
     FA_ERR_BAD_SIZE = 2,       /* batch, ql or kl < 0; n_heads or n_kv_heads < 1      */
     FA_ERR_HEAD_GROUPING = 3,  /* n_heads is not a multiple of n_kv_heads              */
-    FA_ERR_HEAD_DIM = 4,       /* head_dim is neither 64 nor 256                        */
+    FA_ERR_HEAD_DIM = 4,       /* head_dim is not 64, 128 or 256                       */
     FA_ERR_SCALE = 5,          /* scale is NaN or infinite                              */
     FA_ERR_ALIGNMENT = 6,      /* q, k, v or O not 16-byte aligned; mask or L not 4-byte */
     FA_ERR_TOO_LARGE = 7,      /* a grid or index would overflow the kernel's limits    */
@@ -61,7 +61,7 @@ enum fa_mask_dtype {
  *         and NaN are outside the contract.
  *   batch, n_heads, n_kv_heads, ql, kl, head_dim: sizes; n_heads must be a
  *         multiple of n_kv_heads (query head h reads kv head h / (n_heads /
- *         n_kv_heads)); head_dim is 64 or 256.
+ *         n_kv_heads)); head_dim is 64, 128 or 256.
  *   scale finite softmax scale (usually 1/sqrt(head_dim)); negative allowed.
  *   causal nonzero: key j hidden from query row i when j > max(kl - ql, 0) + i.
  *   O     bf16 bits [batch, n_heads, ql, head_dim] (device, written; no

@@ -64,7 +64,7 @@ def _call(**over):
 @pytest.mark.parametrize("over,code", [
     (dict(q=0), 1), (dict(k=0), 1), (dict(v=0), 1), (dict(O=0), 1), (dict(L=0), 1),
     (dict(batch=-1), 2), (dict(ql=-1), 2), (dict(kl=-3), 2), (dict(n_heads=0), 2),
-    (dict(n_kv_heads=0), 2), (dict(n_heads=3, n_kv_heads=2), 3), (dict(head_dim=128), 4),
+    (dict(n_kv_heads=0), 2), (dict(n_heads=3, n_kv_heads=2), 3), (dict(head_dim=96), 4),
     (dict(head_dim=0), 4), (dict(scale=math.nan), 5), (dict(scale=math.inf), 5),
     (dict(scale=-math.inf), 5), (dict(q=A + 2), 6), (dict(k=A + 8), 6), (dict(O=A + 4), 6),
     (dict(mask=A + 2), 6), (dict(L=A + 1), 6),
@@ -159,7 +159,7 @@ def _call_bwd(**over):
     (dict(q=0), 1), (dict(k=0), 1), (dict(v=0), 1), (dict(O=0), 1), (dict(L=0), 1),
     (dict(dO=0), 1), (dict(dQ=0), 1), (dict(dK=0), 1), (dict(dV=0), 1),
     (dict(batch=-1), 2), (dict(ql=-1), 2), (dict(kl=-3), 2), (dict(n_heads=0), 2),
-    (dict(n_kv_heads=0), 2), (dict(n_heads=3, n_kv_heads=2), 3), (dict(head_dim=128), 4),
+    (dict(n_kv_heads=0), 2), (dict(n_heads=3, n_kv_heads=2), 3), (dict(head_dim=96), 4),
     (dict(scale=math.nan), 5), (dict(scale=-math.inf), 5), (dict(q=A + 2), 6),
     (dict(dO=A + 8), 6), (dict(dK=A + 4), 6), (dict(dV=A + 2), 6), (dict(mask=A + 2), 6),
     (dict(L=A + 1), 6), (dict(batch=65536, n_heads=65536, n_kv_heads=1, ql=1), 7),

@@ -34,6 +34,9 @@ CASES = [
     ("masked_d256", 1, 2, 1, 96, 130, 256, False, "random"),
     ("one_row", 1, 2, 2, 1, 1, 64, True, None),
     ("long_d64", 1, 2, 2, 1024, 1024, 64, True, None),
+    ("d128_gqa_causal", 2, 8, 2, 300, 300, 128, True, None),
+    ("d128_masked", 1, 2, 1, 96, 200, 128, False, "random"),
+    ("d128_long", 1, 2, 1, 1024, 1024, 128, True, None),
 ]
 
 
@@ -147,6 +150,7 @@ WINDOW_CASES = [
     ("swa_d256_gqa", 2, 8, 2, 260, 260, 256, 64, None),
     ("swa_d256_masked", 1, 2, 1, 96, 130, 256, 40, "random"),
     ("swa_zero", 1, 2, 1, 100, 100, 64, 0, None),
+    ("swa_d128", 1, 4, 2, 400, 400, 128, 100, None),
 ]
 
 
@@ -162,7 +166,7 @@ def test_window_backward_wide_equals_causal_bit_for_bit():
     backward's bits."""
     import torch
     import flash_attention_forward_fa_amd as fa
-    for D in (64, 256):
+    for D in (64, 128, 256):
         B, H, Hkv, ql, kl = 1, 4, 2, 300, 340
         seed = fagen.SEED_BASE + 7700 + D
         q, k, v, dO = (gu.to_dev(fagen.normal_bf16(seed, st, shp), "cuda:0") for st, shp in

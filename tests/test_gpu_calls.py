@@ -39,7 +39,7 @@ def _bits(O):
     return O.view(torch.int16).cpu().numpy().view(np.uint16)
 
 
-@pytest.mark.parametrize("D", [64, 256])
+@pytest.mark.parametrize("D", [64, 128, 256])
 def test_calls_are_independent_across_sizes_and_streams(D):
     import torch
     import flash_attention_forward_fa_amd as fa

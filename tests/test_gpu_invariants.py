@@ -22,7 +22,7 @@ def _fwd(q, k, v, mask=None, scale=0.125, causal=True):
     return O.view(torch.int16).cpu().numpy().view(np.uint16), L.cpu().numpy()
 
 
-@pytest.mark.parametrize("D", [64, 256])
+@pytest.mark.parametrize("D", [64, 128, 256])
 def test_causal_sentinel_falsifier(D):
     """The method page's section 6 check, at GPU tile sizes: K rows after a
     target query set to 128.0 leave O rows 0..target bit-identical."""
@@ -40,7 +40,7 @@ def test_causal_sentinel_falsifier(D):
         assert np.array_equal(a[1][:, :, :target + 1], b[1][:, :, :target + 1]), target
 
 
-@pytest.mark.parametrize("D", [64, 256])
+@pytest.mark.parametrize("D", [64, 128, 256])
 def test_gqa_equals_repeated_mha(D):
     print(f"case gqa D={D}", flush=True)
     B, H, Hkv, ql, kl = 2, 8, 2, 200, 333

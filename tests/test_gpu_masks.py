@@ -56,6 +56,7 @@ CASES = [
     (2, 4, 1, 64, 96, 256, True, None, 2, 4),
     (2, 2, 2, 130, 130, 256, False, None, 1, 1),
     (1, 2, 1, 70, 300, 256, True, 100, 1, 2),
+    (2, 2, 1, 80, 160, 128, True, None, 1, 2),
 ]
 
 
@@ -79,7 +80,7 @@ def test_mask_options_match_oracle(B, H, Hkv, ql, kl, D, causal, window, mb, mh,
           f"empty rows={int(np.isneginf(lr).sum())}")
 
 
-@pytest.mark.parametrize("D", [64, 256])
+@pytest.mark.parametrize("D", [64, 128, 256])
 def test_bf16_and_f32_masks_of_equal_values_give_equal_bits(D):
     """A 0/-inf mask has the same values in bf16 and f32: the two kernels
     compute the same numbers, so O and L agree bit for bit; the plain

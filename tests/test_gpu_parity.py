@@ -83,7 +83,7 @@ def test_large_workloads_sampled_rows(name):
         assert np.abs(l[:, h, 0] - s0).max() <= 1e-4
 
 
-RAGGED = [
+RAGGED = [  # head_dim 128 (the adjacent attention API's size) at the end
     # (B, H, Hkv, ql, kl, D, causal, masked)
     (1, 1, 1, 1, 1, 64, False, False),
     (1, 2, 1, 17, 33, 64, True, False),
@@ -97,6 +97,10 @@ RAGGED = [
     (1, 2, 2, 64, 96, 256, True, True),
     (1, 1, 1, 300, 40, 256, True, False),   # ql > kl
     (1, 2, 1, 1, 257, 256, True, False),
+    (1, 2, 1, 64, 64, 128, False, False),
+    (1, 2, 1, 150, 150, 128, True, False),
+    (2, 4, 2, 257, 300, 128, True, True),
+    (1, 2, 2, 300, 100, 128, True, False),   # ql > kl
 ]
 
 
@@ -114,7 +118,7 @@ def test_ragged_shapes_match_oracle(B, H, Hkv, ql, kl, D, causal, masked):
     print(f"ragged {(B, H, Hkv, ql, kl, D, causal, masked)}: dO={eo:.3e} dL={el:.3e}")
 
 
-@pytest.mark.parametrize("D", [64, 256])
+@pytest.mark.parametrize("D", [64, 128, 256])
 @pytest.mark.parametrize("scale", [-0.3, 0.0, 0.5])
 def test_other_scales(D, scale):
     w = fagen.Workload("scale", 1, 2, 1, 80, 150, D, True, seed_offset=2000 + D)
@@ -137,7 +141,7 @@ def _times4(bits):
     return np.where(e != 0, b + np.uint16(2 << 7), b).astype(np.uint16)
 
 
-@pytest.mark.parametrize("D", [64, 256])
+@pytest.mark.parametrize("D", [64, 128, 256])
 @pytest.mark.parametrize("causal", [True, False])
 def test_large_outputs_take_the_compensated_redo(D, causal):
     """V times 4: many rows reach |O| >= 1, which the plain pass of a query
@@ -182,8 +186,26 @@ def test_errors_raise_from_binding():
     with pytest.raises(fa.FAError) as e:
         fa.train_fwd(q, k, k)
     assert e.value.status == 3
-    q128 = torch.zeros(1, 1, 4, 128, device="cuda:0", dtype=torch.bfloat16)
+    q96 = torch.zeros(1, 1, 4, 96, device="cuda:0", dtype=torch.bfloat16)
     with pytest.raises(fa.FAError):
-        fa.train_fwd(q128, q128, q128)
+        fa.train_fwd(q96, q96, q96)
     with pytest.raises(fa.FAError):
         fa.train_fwd(q[:, :1], q[:, :1], q[:, :1], scale=math.nan)
+
+
+def test_head_dim_128_gqa_4k_sampled_rows():
+    """head_dim 128 at a training shape (B2, 32 query heads on 8 kv heads,
+    4096 tokens, causal), sampled rows against the oracle, as for the two
+    training-scale workloads."""
+    w = fagen.Workload("d128_b2_h32kv8_q4096_k4096_causal", 2, 32, 8, 4096, 4096, 128, True,
+                       seed_offset=8000)
+    print(f"case {w.name}", flush=True)
+    inp = fagen.generate(w)
+    o, l, bits = gu.run(inp, w)
+    rows = _sample_rows(w, np.random.default_rng(8000))
+    _, ob, lr = oracle.fwd_workload(w, inp, rows=rows)
+    o2, l2, b2 = o.reshape(-1, w.D)[rows], l.reshape(-1)[rows], bits.reshape(-1, w.D)[rows]
+    eo, el, rms = gu.compare(o2, l2, b2, ob, lr, 1e-2, 1e-2, w.name)
+    print(f"{w.name}: {rows.size} rows, max|dO|={eo:.3e} max|dL|={el:.3e} relRMS(O)={rms:.3e}")
+    assert rms <= 1e-2
+    assert np.isfinite(o).all() and np.isfinite(l).all()

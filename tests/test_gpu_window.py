@@ -59,6 +59,8 @@ WINDOWED = [
     (1, 2, 2, 64, 96, 256, 20, True),
     (1, 1, 1, 300, 40, 256, 10, False),      # ql > kl: rows without any key
     (1, 2, 1, 129, 129, 256, 127, False),
+    (1, 2, 1, 500, 500, 128, 150, False),
+    (1, 2, 2, 100, 100, 128, 40, True),
 ]
 
 
@@ -82,7 +84,7 @@ def test_windowed_shapes_match_oracle(B, H, Hkv, ql, kl, D, window, masked):
                                                                  bits[0, :, i].shape))
 
 
-@pytest.mark.parametrize("D", [64, 256])
+@pytest.mark.parametrize("D", [64, 128, 256])
 def test_wide_window_equals_causal_bit_for_bit(D):
     """A window reaching past every row's first key hides nothing more than
     the causal rule: the window kernel gives the causal kernel's bits."""
@@ -100,7 +102,7 @@ def test_wide_window_equals_causal_bit_for_bit(D):
         assert torch.equal(Lc, Lw), window
 
 
-@pytest.mark.parametrize("D", [64, 256])
+@pytest.mark.parametrize("D", [64, 128, 256])
 def test_keys_below_the_window_are_never_seen(D):
     """The page's causal falsifier turned to the window's lower edge: K rows
     below position t are set to 128.0, which would dominate any softmax that

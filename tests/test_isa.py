@@ -44,9 +44,9 @@ def isa(tmp_path_factory):
 def test_all_variants_present(isa):
     fwd = [n for n in isa if "fa_fwd_kernel" in n]
     bwd = [n for n in isa if "fa_bwd_kernel" in n]
-    # head_dim x {none, causal, sliding window} x {mixed, compensated f32 mask, bf16 mask}
-    assert len(fwd) == 18
-    assert len(bwd) == 24  # head_dim x {dQ, dKV} x {none, causal, sliding window} x mask
+    # head_dim (64, 128, 256) x {none, causal, window} x {mixed, compensated f32 mask, bf16 mask}
+    assert len(fwd) == 27
+    assert len(bwd) == 36  # head_dim (3) x {dQ, dKV} x {none, causal, window} x mask
 
 
 _OPEN = (re.compile(r"s_(?:and|andn2|or)_saveexec_b64 (s\[\d+:\d+\])"),
