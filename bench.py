@@ -88,6 +88,8 @@ def main():
                     help="timed backward calls per workload after the forward (0: none)")
     ap.add_argument("--window-steps", type=int, default=10,
                     help="timed sliding-window forward calls per workload (0: none)")
+    ap.add_argument("--d128-steps", type=int, default=10,
+                    help="timed head_dim-128 forward and backward calls (0: none)")
     ap.add_argument("--cpu-rows", type=int, default=0,
                     help="rows per workload for the CPU baseline (0: default sample)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -228,6 +230,43 @@ def main():
             launch(w)
         torch.cuda.synchronize()
 
+    # head_dim 128 (B2, 32 query heads on 8 kv heads, 4096 tokens, causal), the
+    # forward and its backward; not part of the headline metric.
+    d128 = {}
+    if args.d128_steps > 0:
+        w = fagen.Workload("d128_b2_h32kv8_q4096_k4096_causal", 2, 32, 8, 4096, 4096, 128, True,
+                           seed_offset=8000)
+        inp = fagen.generate(w)
+        to = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        q, k, v = to(inp["q"]), to(inp["k"]), to(inp["v"])
+        dO = to(fagen.normal_bf16(w.seed, 6, (w.B, w.H, w.ql, w.D)))
+        O, L = fa.train_fwd(q, k, v, scale=w.scale, causal=True)
+        for _ in range(3):
+            fa.train_fwd(q, k, v, scale=w.scale, causal=True, out=O, lse=L)
+            fa.train_bwd(q, k, v, O, L, dO, scale=w.scale, causal=True)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(args.d128_steps):
+            fa.train_fwd(q, k, v, scale=w.scale, causal=True, out=O, lse=L)
+        b.record(stream)
+        torch.cuda.synchronize()
+        fms = a.elapsed_time(b) / args.d128_steps
+        a.record(stream)
+        for _ in range(args.d128_steps):
+            fa.train_bwd(q, k, v, O, L, dO, scale=w.scale, causal=True)
+        b.record(stream)
+        torch.cuda.synchronize()
+        bms = a.elapsed_time(b) / args.d128_steps
+        d128 = {"workload": w.name, "ms_avg": fms, "metric_flop": w.metric_flop,
+                "tflops": w.metric_flop / (fms * 1e-3) / 1e12,
+                "frac_of_peak": w.metric_flop / (fms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                "backward_ms_avg": bms,
+                "backward_tflops": 2.5 * w.metric_flop / (bms * 1e-3) / 1e12}
+        log(f"{w.name}: {fms * 1e3:.1f} us/call, {d128['tflops']:.1f} TFLOP/s; backward "
+            f"{bms * 1e3:.1f} us/call, {d128['backward_tflops']:.1f} TFLOP/s (FA-2 count)")
+        del q, k, v, dO, O, L
+
     if args.copy_calibration:
         n = args.copy_calibration * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device=dev)
@@ -283,6 +322,8 @@ def main():
         result["backward"] = bwd
     if swa:
         result["sliding_window"] = swa
+    if d128:
+        result["head_dim_128"] = d128
     if not args.no_cpu_baseline:
         target = {w.name: (args.cpu_rows or (524288 if w.D == 64 else 65536)) for w in workloads}
         result["cpu_baseline"] = cpu_baseline(workloads, inputs, target)
