@@ -37,18 +37,19 @@ def kernel_source_hash():
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def stored_traffic(workload):
-    """HBM bytes per launch measured by rocprofv3 --pmc (FETCH_SIZE, WRITE_SIZE),
-    if they were taken on the current kernel source; else None."""
+def stored_counters(workload):
+    """rocprofv3 --pmc figures of the workload's forward launch (HBM bytes from
+    FETCH_SIZE/WRITE_SIZE, MFMA/VALU/LDS activity from the SQ counters), if they
+    were taken on the current kernel source; else an empty dict."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
-        return None
+        return {}
     entry = t.get(workload)
     if not entry or entry.get("kernel_source_sha") != kernel_source_hash():
-        return None
-    return entry.get("bytes_per_launch")
+        return {}
+    return entry
 
 
 def cpu_baseline(workloads, inputs, target_rows):
@@ -296,10 +297,12 @@ def main():
 
     dom = max(workloads, key=lambda w: per[w.name]["ms_avg"])
     dp = per[dom.name]
-    traffic = stored_traffic(dom.name)
+    ctr = stored_counters(dom.name)
     roofline = {"bound": "mfma", "achieved": dp["tflops"], "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": dp["tflops"] / PEAK_BF16_TFLOPS,
-                "traffic": traffic,
+                "traffic": ctr.get("bytes_per_launch"),
+                "mfma_util": ctr.get("mfma_util"), "valu_busy": ctr.get("valu_busy"),
+                "lds_util": ctr.get("lds_util"),
                 "kernel": f"fa_train_fwd: one mixed fa_fwd_kernel<{dom.D}, causal> launch",
                 "workload": dom.name}
 
