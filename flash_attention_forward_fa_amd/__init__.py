@@ -17,7 +17,7 @@ LIB_PATH = _build.LIB
 FA_STATUS = {
     0: "FA_OK", 1: "FA_ERR_NULL_POINTER", 2: "FA_ERR_BAD_SIZE", 3: "FA_ERR_HEAD_GROUPING",
     4: "FA_ERR_HEAD_DIM", 5: "FA_ERR_SCALE", 6: "FA_ERR_ALIGNMENT", 7: "FA_ERR_TOO_LARGE",
-    8: "FA_ERR_LAUNCH", 9: "FA_ERR_WINDOW", 10: "FA_ERR_MASK",
+    8: "FA_ERR_LAUNCH", 9: "FA_ERR_WINDOW", 10: "FA_ERR_MASK", 11: "FA_ERR_SPLIT",
 }
 FA_MASK_F32, FA_MASK_BF16 = 0, 1
 
@@ -49,6 +49,12 @@ def lib():
         l.fa_train_fwd_ex.argtypes = [vp, vp, vp, vp, ci, i64, i64, ci, ci, ci, ci, ci, ci,
                                       ctypes.c_float, ci, ci, vp, vp, vp]
         l.fa_train_fwd_ex.restype = ci
+        ul = ctypes.c_ulong
+        l.fa_train_fwd_split.argtypes = [vp, vp, vp, ci, ci, ci, ci, ci, ci, ctypes.c_float, ci,
+                                         ci, vp, ul, vp, vp, vp]
+        l.fa_train_fwd_split.restype = ci
+        l.fa_train_fwd_split_workspace.argtypes = [ci, ci, ci, ci, ci]
+        l.fa_train_fwd_split_workspace.restype = ul
         l.fa_train_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci,
                                    ctypes.c_float, ci, vp, vp, vp, vp]
         l.fa_train_bwd.restype = ci
@@ -117,6 +123,74 @@ def train_fwd_ex(q, k, v, mask=None, scale=None, causal=False, window=None, out=
     return _train_fwd(q, k, v, mask, scale, causal, window, out, lse, stream, ex=True,
                       mask_layout=(FA_MASK_BF16 if mask.dtype == torch.bfloat16 else FA_MASK_F32,
                                    sb, sh))
+
+
+def fa_train_fwd_split(q, k, v, batch, n_heads, n_kv_heads, ql, kl, head_dim, scale, causal,
+                       n_split, workspace, workspace_bytes, O, L, stream):
+    """The C entry point with raw integer pointers (0 for NULL); returns the status."""
+    return lib().fa_train_fwd_split(q or None, k or None, v or None, batch, n_heads, n_kv_heads,
+                                    ql, kl, head_dim, float(scale), int(bool(causal)),
+                                    int(n_split), workspace or None, int(workspace_bytes),
+                                    O or None, L or None, stream or None)
+
+
+def fa_train_fwd_split_workspace(batch, n_heads, ql, head_dim, n_split):
+    """Workspace bytes fa_train_fwd_split needs (0 for invalid sizes)."""
+    return int(lib().fa_train_fwd_split_workspace(batch, n_heads, ql, head_dim, n_split))
+
+
+def train_fwd_split(q, k, v, n_split, scale=None, causal=False, workspace=None, out=None,
+                    lse=None, stream=None):
+    """O, L = train_fwd_split(q, k, v, n_split, scale=None, causal=False, workspace=None)
+
+    train_fwd (no mask) with the keys split into up to n_split chunks computed
+    by separate workgroups and merged through their logsumexps: for few query
+    tiles against many keys. workspace: a uint8 device tensor of at least
+    fa_train_fwd_split_workspace(...) bytes (allocated here when None).
+    """
+    import torch
+
+    O, L, (B, H, Hkv, ql, kl, D), scale, s = _fwd_outputs(q, k, v, scale, out, lse, stream)
+    need = fa_train_fwd_split_workspace(B, H, ql, D, n_split)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    if (workspace.dtype != torch.uint8 or not workspace.is_contiguous()
+            or workspace.device != q.device):
+        raise ValueError("workspace must be a contiguous uint8 tensor on q's device")
+    with torch.cuda.device(q.device):
+        status = fa_train_fwd_split(q.data_ptr(), k.data_ptr(), v.data_ptr(), B, H, Hkv, ql, kl,
+                                    D, scale, causal, n_split, workspace.data_ptr(),
+                                    workspace.numel(), O.data_ptr(), L.data_ptr(), s.cuda_stream)
+    if status != 0:
+        raise FAError(status, status_string(status))
+    return O, L
+
+
+def _fwd_outputs(q, k, v, scale, out, lse, stream):
+    """Checks q, k, v and the outputs; returns (O, L, sizes, scale, stream)."""
+    import torch
+
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.bfloat16:
+            raise TypeError(f"{name} must be a bfloat16 tensor")
+        if t.dim() != 4 or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError(f"{name} must be a contiguous 4-d tensor on a GPU")
+    B, H, ql, D = q.shape
+    Bk, Hkv, kl, Dk = k.shape
+    if tuple(v.shape) != tuple(k.shape) or Bk != B or Dk != D:
+        raise ValueError("k and v must be [B, Hkv, kl, D] with q's B and D")
+    if k.device != q.device or v.device != q.device:
+        raise ValueError("q, k and v must be on the same device")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    O = out if out is not None else torch.empty_like(q)
+    L = lse if lse is not None else torch.empty((B, H, ql), dtype=torch.float32, device=q.device)
+    if O.shape != q.shape or O.dtype != torch.bfloat16 or not O.is_contiguous():
+        raise ValueError("out must be a contiguous bf16 tensor shaped like q")
+    if tuple(L.shape) != (B, H, ql) or L.dtype != torch.float32 or not L.is_contiguous():
+        raise ValueError("lse must be a contiguous f32 tensor [B, H, ql]")
+    s = stream if stream is not None else torch.cuda.current_stream(q.device)
+    return O, L, (B, H, Hkv, ql, kl, D), scale, s
 
 
 def train_fwd(q, k, v, mask=None, scale=None, causal=False, out=None, lse=None, stream=None):

@@ -81,7 +81,10 @@ constexpr float kLazy = 8.0f;
 // some of their rows need the compensated product the workgroup runs the tile
 // again, compensated, for those rows only. The compensated kernel (kAll)
 // computes every row of every tile compensated (the masked forward).
-constexpr int kMixed = 0, kAll = 1;
+// In the split-KV kernel (kSplit) a workgroup computes one key chunk of its
+// query tile, compensated, and writes the chunk's normalised partial O and its
+// logsumexp to a workspace; a combine kernel merges the chunks through L.
+constexpr int kMixed = 0, kAll = 1, kSplit = 2;
 // Additive mask element types (kNoMask: no mask).
 constexpr int kNoMask = 0, kMaskF32 = 1, kMaskBF16 = 2;
 
@@ -111,6 +114,10 @@ struct FwdArgs {
   int n_precise;   // kMixed: query tiles below this run compensated
   int causal_off;  // max(kl - ql, 0)
   int window;      // WINDOW variants: keys below q_abs - window are hidden
+  int n_split;     // kSplit: key chunks per query tile (grid factor)
+  int kchunk;      // kSplit: keys per chunk (a multiple of the key tile)
+  float* ws_o;     // kSplit: partial O, f32 [n_split, B, H, ql, D]
+  float* ws_l;     // kSplit: partial L, f32 [n_split, B, H, ql]
   float c;         // |scale| * log2(e), at least FLT_MIN
   uint32_t q_sign; // 0x80008000 flips the sign of both bf16 halves (scale < 0)
 };
@@ -123,14 +130,16 @@ struct FwdArgs {
 // (wg_flags: one int per wave). With REDO (and PRECISE), only the rows with
 // redo set are computed and written (waves without such a row only take part
 // in the tile copies).
-template <int D, bool CAUSAL, bool WINDOW, int MASK, bool PRECISE, bool REDO>
+template <int D, bool CAUSAL, bool WINDOW, int MASK, bool PRECISE, bool REDO, bool SPLIT = false>
 __device__ __forceinline__ bool fwd_tile(const FwdArgs& a, int qtile, int bh, uint16_t* k0s,
                                          uint16_t* v0s, uint16_t* k1s, uint16_t* v1s,
-                                         bool (&redo)[Cfg<D>::QB], int* wg_flags) {
+                                         bool (&redo)[Cfg<D>::QB], int* wg_flags, int split = 0) {
   constexpr bool HAS_MASK = MASK != kNoMask;
   static_assert(PRECISE || !HAS_MASK, "the masked forward always runs compensated");
   static_assert(PRECISE || !REDO, "a redo runs compensated");
   static_assert(CAUSAL || !WINDOW, "the sliding window includes the causal rule");
+  static_assert(!SPLIT || (PRECISE && !REDO && !WINDOW && MASK == kNoMask),
+                "split-KV partials: compensated, unmasked, no window");
   constexpr int BN = Cfg<D>::BN;
   constexpr int kQB = Cfg<D>::QB;
   constexpr int kRowsPerWave = 16 * kQB;
@@ -167,16 +176,19 @@ __device__ __forceinline__ bool fwd_tile(const FwdArgs& a, int qtile, int bh, ui
   const uint16_t* vp = a.v + kv_off;
 
   // ---- key range ----
+  // (split-KV: only the keys of chunk `split`, [split*kchunk, (split+1)*kchunk))
+  const int k_hi = SPLIT ? (split + 1) * a.kchunk : kl;
   const int last_row = min(q0 + kBlockM, ql) - 1;
-  const int kend = CAUSAL ? min(kl, off + last_row + 1) : kl;
+  const int kend = min(k_hi, CAUSAL ? min(kl, off + last_row + 1) : kl);
   const int n_kt = (kend + BN - 1) / BN;
   // under a sliding window no row of the workgroup (of the wave) sees a key
   // below off + (its first row) - window: those key tiles are skipped
-  const int kt_first = WINDOW ? max(0, off + q0 - a.window) / BN : 0;
+  const int kt_first = SPLIT ? split * a.kchunk / BN : WINDOW ? max(0, off + q0 - a.window) / BN : 0;
   const bool wave_active = qw0 < ql;
   const int wave_last = min(qw0 + kRowsPerWave, ql) - 1;
-  const int wave_kend = CAUSAL ? min(kl, off + wave_last + 1) : kl;
-  const int wave_kt_first = WINDOW ? max(0, off + qw0 - a.window) / BN : 0;
+  const int wave_kend = min(k_hi, CAUSAL ? min(kl, off + wave_last + 1) : kl);
+  const int wave_kt_first =
+      SPLIT ? kt_first : WINDOW ? max(0, off + qw0 - a.window) / BN : 0;
   float* lrow_base = a.l + (int64_t)bh * ql;
 
   bool wave_redo = false;
@@ -537,16 +549,30 @@ __device__ __forceinline__ bool fwd_tile(const FwdArgs& a, int qtile, int bh, ui
       const float lt = l_tot[qb];
       const bool empty = !(lt > 0.0f);
       const float inv = empty ? 0.0f : __builtin_amdgcn_rcpf(lt);
-      uint16_t* orow = a.o + ((int64_t)bh * ql + qrow) * D + 4 * grp;
+      const float lse = empty ? -INFINITY : (m_use[qb] + __builtin_amdgcn_logf(lt)) * kLn2;
+      if constexpr (SPLIT) {
+        // the chunk's partial: O normalised by its own sum (f32), and its L
+        const int64_t prow = ((int64_t)split * a.B * a.H + bh) * ql + qrow;
+        float* op = a.ws_o + prow * D + 4 * grp;
 #pragma unroll
-      for (int d = 0; d < NDB; ++d) {
-        bf16x4 ov;
+        for (int d = 0; d < NDB; ++d) {
+          f32x4 ov;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) ov[i] = empty ? (__bf16)0.0f : (__bf16)(oacc[d][qb][i] * inv);
-        *reinterpret_cast<bf16x4*>(orow + 16 * d) = ov;
+          for (int i = 0; i < 4; ++i) ov[i] = empty ? 0.0f : oacc[d][qb][i] * inv;
+          *reinterpret_cast<f32x4*>(op + 16 * d) = ov;
+        }
+        if (grp == 0) a.ws_l[prow] = lse;
+      } else {
+        uint16_t* orow = a.o + ((int64_t)bh * ql + qrow) * D + 4 * grp;
+#pragma unroll
+        for (int d = 0; d < NDB; ++d) {
+          bf16x4 ov;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) ov[i] = empty ? (__bf16)0.0f : (__bf16)(oacc[d][qb][i] * inv);
+          *reinterpret_cast<bf16x4*>(orow + 16 * d) = ov;
+        }
+        if (grp == 0) lrow_base[qrow] = lse;
       }
-      if (grp == 0)
-        lrow_base[qrow] = empty ? -INFINITY : (m_use[qb] + __builtin_amdgcn_logf(lt)) * kLn2;
     }
   }
   // no LDS copy may still be in flight when the workgroup ends (waiting for
@@ -558,6 +584,7 @@ __device__ __forceinline__ bool fwd_tile(const FwdArgs& a, int qtile, int bh, ui
 template <int D, bool CAUSAL, bool WINDOW, int MASK, int MODE>
 __global__ __launch_bounds__(64 * Cfg<D>::W)
 __attribute__((amdgpu_waves_per_eu(MODE == kMixed ? Cfg<D>::WPE : 2))) void fa_fwd_kernel(FwdArgs a) {
+  static_assert(MODE != kSplit || (MASK == kNoMask && !WINDOW), "split-KV: unmasked, no window");
   static_assert(MODE != kMixed || MASK == kNoMask, "the masked forward always runs compensated");
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
   constexpr int TILE = Cfg<D>::BN * D;
@@ -574,8 +601,10 @@ __attribute__((amdgpu_waves_per_eu(MODE == kMixed ? Cfg<D>::WPE : 2))) void fa_f
   // multiple of 8; fewer K/V in flight per L2) and walks each group's query
   // tiles heaviest (most keys) first, so the cheap tiles fill the tail.
   // (Groups of 1, 2 or 4 heads were measured slower, 8 faster than all.)
+  // (split-KV: the chunk index is the fastest-varying part of the block index)
   const int BH = a.B * a.H;
-  const int bid = blockIdx.x;
+  const int split = MODE == kSplit ? (int)(blockIdx.x % (unsigned)a.n_split) : 0;
+  const int bid = MODE == kSplit ? (int)(blockIdx.x / (unsigned)a.n_split) : (int)blockIdx.x;
   int qt_rev, bh;
   if ((BH & 7) == 0) {
     const int xcd = bid & 7, tl = bid >> 3, per = BH >> 3;
@@ -602,11 +631,55 @@ __attribute__((amdgpu_waves_per_eu(MODE == kMixed ? Cfg<D>::WPE : 2))) void fa_f
       fwd_tile<D, CAUSAL, WINDOW, kNoMask, true, true>(a, qtile, bh, k0s, v0s, k1s, v1s, redo,
                                                        wg_flags);
     }
+  } else if constexpr (MODE == kSplit) {
+    fwd_tile<D, CAUSAL, false, kNoMask, true, false, true>(a, qtile, bh, k0s, v0s, k1s, v1s, redo,
+                                                           wg_flags, split);
   } else {
     fwd_tile<D, CAUSAL, WINDOW, MASK, true, false>(a, qtile, bh, k0s, v0s, k1s, v1s, redo,
                                                    wg_flags);
   }
 #endif
+}
+
+// Merge of the split-KV partials of each row (one wave per row, lane l holds
+// dims l*P .. l*P+P-1): L = m + ln sum_s exp(L_s - m), O = sum_s exp(L_s - L) O_s,
+// the same merge through L that combines key partitions computed apart.
+struct CombineArgs {
+  const float* ws_o;  // [n_split, rows, D]
+  const float* ws_l;  // [n_split, rows]
+  uint16_t* o;        // bf16 [rows, D]
+  float* l;           // f32 [rows]
+  int64_t rows;       // B * H * ql
+  int n_split;
+};
+
+template <int D>
+__global__ __launch_bounds__(256) void fa_combine_kernel(CombineArgs c) {
+  constexpr int P = D / 64;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= c.rows) return;
+  const int lane = threadIdx.x & 63;
+  float m = -INFINITY;
+  for (int s = 0; s < c.n_split; ++s) m = fmaxf(m, c.ws_l[s * c.rows + row]);
+  float acc[P] = {};
+  float z = 0.0f;
+  if (m != -INFINITY) {
+    for (int s = 0; s < c.n_split; ++s) {
+      // (a chunk with no visible key has L_s = -inf: weight 0, partial O 0)
+      const float w = __builtin_amdgcn_exp2f((c.ws_l[s * c.rows + row] - m) * kLog2e);
+      z += w;
+      const float* op = c.ws_o + (s * c.rows + row) * D + lane * P;
+#pragma unroll
+      for (int e = 0; e < P; ++e) acc[e] += w * op[e];
+    }
+  }
+  const bool empty = m == -INFINITY;
+  const float inv = empty ? 0.0f : 1.0f / z;
+  uint16_t* orow = c.o + row * D + lane * P;
+#pragma unroll
+  for (int e = 0; e < P; ++e)
+    orow[e] = __builtin_bit_cast(uint16_t, empty ? (__bf16)0.0f : (__bf16)(acc[e] * inv));
+  if (lane == 0) c.l[row] = empty ? -INFINITY : m + __builtin_amdgcn_logf(z) * kLn2;
 }
 
 template <int D, bool CAUSAL, bool WINDOW, int MASK, int MODE>
@@ -635,9 +708,33 @@ hipError_t dispatch_c(FwdArgs a, int mask, int n_short, hipStream_t stream) {
   return launch<D, CAUSAL, WINDOW, kNoMask, kMixed>(a, bh * n_qt, stream);
 }
 
+// Split-KV: the partials over all (chunk, head, query tile), then the merge.
+template <int D, bool CAUSAL>
+hipError_t dispatch_split(FwdArgs a, hipStream_t stream) {
+  const unsigned bh = (unsigned)(a.B * a.H);
+  a.qt_base = 0;
+  a.qt_count = a.n_qtiles;
+  a.n_precise = a.n_qtiles;
+  hipError_t e = launch<D, CAUSAL, false, kNoMask, kSplit>(
+      a, bh * (unsigned)a.n_qtiles * (unsigned)a.n_split, stream);
+  if (e != hipSuccess) return e;
+  CombineArgs c;
+  c.ws_o = a.ws_o;
+  c.ws_l = a.ws_l;
+  c.o = a.o;
+  c.l = a.l;
+  c.rows = (int64_t)a.B * a.H * a.ql;
+  c.n_split = a.n_split;
+  hipLaunchKernelGGL(fa_combine_kernel<D>, dim3((unsigned)((c.rows + 3) / 4)), dim3(256), 0, stream,
+                     c);
+  return hipGetLastError();
+}
+
 template <int D>
 hipError_t dispatch_d(const FwdArgs& a, bool causal, bool window, int mask, int n_short,
                       hipStream_t stream) {
+  if (a.n_split > 0)
+    return causal ? dispatch_split<D, true>(a, stream) : dispatch_split<D, false>(a, stream);
   if (window) return dispatch_c<D, true, true>(a, mask, n_short, stream);
   return causal ? dispatch_c<D, true, false>(a, mask, n_short, stream)
                 : dispatch_c<D, false, false>(a, mask, n_short, stream);
@@ -648,10 +745,23 @@ bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p
 // Shared host path of every forward entry point; window < 0: none (window >= 0
 // requires causal). The mask is mask_dtype (FA_MASK_F32 / FA_MASK_BF16) with
 // batch and head strides in elements; its rows are contiguous (row stride kl).
+// Split-KV workspace: partial O (f32, n * rows * D) then, 256-byte aligned,
+// partial L (f32, n * rows).
+int64_t split_o_bytes(int64_t rows, int head_dim, int64_t n) {
+  return (n * rows * head_dim * 4 + 255) / 256 * 256;
+}
+int64_t split_bytes(int64_t rows, int head_dim, int64_t n) {
+  return split_o_bytes(rows, head_dim, n) + n * rows * 4;
+}
+constexpr int kMaxSplit = 65536;
+
+// n_split > 0 selects the split-KV path (no mask, no window) with the given
+// workspace.
 int train_fwd(const void* q, const void* k, const void* v, const void* mask, int mask_dtype,
               int64_t mask_sb, int64_t mask_sh, int batch, int n_heads, int n_kv_heads, int ql,
               int kl, int head_dim, float scale, int causal, int window, void* O, float* L,
-              void* stream) {
+              void* stream, int n_split = 0, void* workspace = nullptr,
+              size_t workspace_bytes = 0) {
   if (batch < 0 || ql < 0 || kl < 0 || n_heads < 1 || n_kv_heads < 1) return FA_ERR_BAD_SIZE;
   if (n_heads % n_kv_heads != 0) return FA_ERR_HEAD_GROUPING;
   if (head_dim != 64 && head_dim != 128 && head_dim != 256) return FA_ERR_HEAD_DIM;
@@ -704,6 +814,25 @@ int train_fwd(const void* q, const void* k, const void* v, const void* mask, int
   // produces round to 0 in f32, so the weights are the same uniform ones).
   a.c = fmaxf(fabsf(scale) * kLog2e, FLT_MIN);
   a.q_sign = signbit(scale) ? 0x80008000u : 0u;
+  a.n_split = 0;
+  a.kchunk = 0;
+  a.ws_o = nullptr;
+  a.ws_l = nullptr;
+  if (n_split > 0 && kl > 0) {
+    // chunks of whole 64-key tiles, each holding at least one key
+    const int64_t per = ((int64_t)kl + n_split - 1) / n_split;
+    const int64_t kchunk = (per + 63) / 64 * 64;
+    const int64_t n_eff = ((int64_t)kl + kchunk - 1) / kchunk;
+    if (!workspace) return FA_ERR_NULL_POINTER;
+    if (!aligned(workspace, 16)) return FA_ERR_ALIGNMENT;
+    if ((int64_t)workspace_bytes < split_bytes(rows, head_dim, n_eff)) return FA_ERR_SPLIT;
+    if (grid * n_eff > 0x7fffffffLL || (rows + 3) / 4 > 0x7fffffffLL) return FA_ERR_TOO_LARGE;
+    a.n_split = (int)n_eff;
+    a.kchunk = (int)kchunk;
+    a.ws_o = static_cast<float*>(workspace);
+    a.ws_l = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                      split_o_bytes(rows, head_dim, n_eff));
+  }
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   // query tiles whose first row may see fewer than kPreciseKeys keys
@@ -744,6 +873,23 @@ extern "C" int fa_train_fwd_swa(const void* q, const void* k, const void* v, con
                    ql, kl, head_dim, scale, 1, window, O, L, stream);
 }
 
+extern "C" unsigned long fa_train_fwd_split_workspace(int batch, int n_heads, int ql, int head_dim,
+                                               int n_split) {
+  if (batch < 0 || n_heads < 1 || ql < 0 || head_dim < 1 || n_split < 1 || n_split > kMaxSplit)
+    return 0;
+  return (unsigned long)split_bytes((int64_t)batch * n_heads * ql, head_dim, n_split);
+}
+
+extern "C" int fa_train_fwd_split(const void* q, const void* k, const void* v, int batch,
+                                  int n_heads, int n_kv_heads, int ql, int kl, int head_dim,
+                                  float scale, int causal, int n_split, void* workspace,
+                                  unsigned long workspace_bytes, void* O, float* L, void* stream) {
+  if (n_split < 1 || n_split > kMaxSplit) return FA_ERR_SPLIT;
+  return train_fwd(q, k, v, nullptr, FA_MASK_F32, 0, 0, batch, n_heads, n_kv_heads, ql, kl,
+                   head_dim, scale, causal, -1, O, L, stream, n_split, workspace,
+                   workspace_bytes);
+}
+
 extern "C" int fa_train_fwd_ex(const void* q, const void* k, const void* v, const void* mask,
                                int mask_dtype, long long mask_stride_b, long long mask_stride_h,
                                int batch, int n_heads, int n_kv_heads, int ql, int kl,
@@ -768,6 +914,7 @@ extern "C" const char* fa_status_string(int status) {
     case FA_ERR_LAUNCH: return "HIP kernel launch failed";
     case FA_ERR_WINDOW: return "sliding window must be >= 0 and comes with causal masking";
     case FA_ERR_MASK: return "mask dtype must be FA_MASK_F32 or FA_MASK_BF16, strides >= 0";
+    case FA_ERR_SPLIT: return "n_split must be in 1..65536 and the workspace large enough";
     default: return "unknown status";
   }
 }

@@ -40,8 +40,10 @@ enum fa_status {
     FA_ERR_LAUNCH = 8,         /* the HIP launch failed (hipGetLastError)               */
     FA_ERR_WINDOW = 9,         /* window < 0 (fa_train_fwd_swa); window >= 0 without
                                   causal (fa_train_fwd_ex)                              */
-    FA_ERR_MASK = 10           /* fa_train_fwd_ex: unknown mask dtype or a negative
+    FA_ERR_MASK = 10,          /* fa_train_fwd_ex: unknown mask dtype or a negative
                                   mask stride                                           */
+    FA_ERR_SPLIT = 11          /* fa_train_fwd_split: n_split outside 1..65536, or the
+                                  workspace smaller than the split needs                */
 };
 
 /* Element types of an additive mask (fa_train_fwd_ex). */
@@ -142,6 +144,42 @@ int fa_train_fwd_ex(const void *q, const void *k, const void *v, const void *mas
                     int mask_dtype, long long mask_stride_b, long long mask_stride_h, int batch,
                     int n_heads, int n_kv_heads, int ql, int kl, int head_dim, float scale,
                     int causal, int window, void *O, float *L, void *stream);
+
+/*
+ * fa_train_fwd_split - the forward of fa_train_fwd (no mask, causal or not)
+ * with the keys split into chunks that separate workgroups compute: for
+ * shapes with few query tiles and many keys (prefill against a long KV cache,
+ * decoding), whose plain launch has fewer workgroups than the GPU has CUs.
+ *
+ * Each chunk c of keys yields, per query row, the softmax over that chunk
+ * alone: a normalised partial O_c and its logsumexp L_c (both f32, in the
+ * workspace); a second kernel merges them, L = log sum_c exp(L_c),
+ * O = sum_c exp(L_c - L) O_c, which is the same softmax over all keys (the
+ * L the method's page returns is exactly what makes the merge possible). Every
+ * chunk runs the compensated P.V product. O and L are as fa_train_fwd's (O
+ * rounded once, from f32, at the merge).
+ *
+ *   n_split    requested chunks, 1..65536; the keys are cut into chunks of
+ *              whole 64-key tiles, ceil(kl / n_split) rounded up, so fewer
+ *              chunks may run.
+ *   workspace  device memory of workspace_bytes >= fa_train_fwd_split_workspace
+ *              (batch, n_heads, ql, head_dim, n_split), 16-byte aligned, owned by
+ *              the caller; its contents on entry do not matter and are
+ *              overwritten. Calls that share a workspace must not overlap.
+ *   others     as for fa_train_fwd.
+ *
+ * Returns FA_ERR_SPLIT for n_split outside 1..65536 or a workspace too small,
+ * otherwise the statuses of fa_train_fwd. kl == 0 needs no workspace.
+ * Two kernel launches; allocates nothing; never synchronises.
+ */
+int fa_train_fwd_split(const void *q, const void *k, const void *v, int batch, int n_heads,
+                       int n_kv_heads, int ql, int kl, int head_dim, float scale, int causal,
+                       int n_split, void *workspace, unsigned long workspace_bytes, void *O,
+                       float *L, void *stream);
+
+/* Workspace bytes fa_train_fwd_split needs for these sizes (0 if invalid). */
+unsigned long fa_train_fwd_split_workspace(int batch, int n_heads, int ql, int head_dim,
+                                           int n_split);
 
 /*
  * fa_train_bwd - enqueue the training backward pass of the same attention.

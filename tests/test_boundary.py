@@ -28,8 +28,9 @@ def _declared_functions():
 
 def test_header_declares_the_entry_points():
     names = _declared_functions()
-    assert {"fa_train_fwd", "fa_train_fwd_swa", "fa_train_fwd_ex", "fa_train_bwd",
-            "fa_train_bwd_swa", "fa_status_string"} <= names
+    assert {"fa_train_fwd", "fa_train_fwd_swa", "fa_train_fwd_ex", "fa_train_fwd_split",
+            "fa_train_fwd_split_workspace", "fa_train_bwd", "fa_train_bwd_swa",
+            "fa_status_string"} <= names
 
 
 def test_library_exports_every_declared_symbol():
@@ -43,7 +44,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings_cover_all_codes():
-    for code in range(0, 11):
+    for code in range(0, 12):
         s = fa.status_string(code)
         assert s and s != "unknown status"
     assert fa.status_string(12345) == "unknown status"
@@ -130,6 +131,40 @@ def test_ex_invalid_arguments_are_rejected(over, code):
                                   dict(batch=0, mask=0, mask_dtype=7, mask_stride_b=-5)])
 def test_ex_empty_problems_are_noops(over):
     assert _call_ex(**over) == 0
+
+
+SPLIT_GOOD = dict(q=A, k=A, v=A, batch=1, n_heads=2, n_kv_heads=1, ql=8, kl=1000, head_dim=64,
+                  scale=0.125, causal=1, n_split=4, workspace=A, workspace_bytes=1 << 20, O=A, L=A,
+                  stream=0)
+
+
+def _call_split(**over):
+    args = dict(SPLIT_GOOD)
+    args.update(over)
+    return fa.fa_train_fwd_split(**args)
+
+
+def test_split_workspace_size():
+    # partial O (f32, 256-byte aligned) then partial L (f32) for every chunk
+    rows, D, n = 2 * 4 * 100, 128, 7
+    o_bytes = (n * rows * D * 4 + 255) // 256 * 256
+    assert fa.fa_train_fwd_split_workspace(2, 4, 100, D, n) == o_bytes + n * rows * 4
+    assert fa.fa_train_fwd_split_workspace(2, 4, 100, D, 0) == 0
+    assert fa.fa_train_fwd_split_workspace(-1, 4, 100, D, 2) == 0
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(n_split=0), 11), (dict(n_split=65537), 11), (dict(workspace_bytes=1000), 11),
+    (dict(workspace=0), 1), (dict(workspace=A + 8), 6), (dict(q=0), 1), (dict(head_dim=96), 4),
+    (dict(n_heads=3, n_kv_heads=2), 3), (dict(scale=math.nan), 5), (dict(kl=-1), 2),
+])
+def test_split_invalid_arguments_are_rejected(over, code):
+    assert _call_split(**over) == code
+
+
+@pytest.mark.parametrize("over", [dict(batch=0), dict(ql=0, workspace=0)])
+def test_split_empty_problems_are_noops(over):
+    assert _call_split(**over) == 0
 
 
 def test_python_binding_fails_loudly_without_gpu_tensors():

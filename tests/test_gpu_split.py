@@ -1,0 +1,107 @@
+"""GPU parity of the split-KV forward (fa_train_fwd_split) against the CPU oracle
+(marked gpu): the same forward definition, computed as key chunks whose
+partial results are merged through their logsumexps. Bounds as for the plain
+forward (O <= 5e-3 and L <= 3e-3 while kl <= 256, 1e-2 beyond); rows with no
+visible key exactly O = +0, L = -inf.
+"""
+import numpy as np
+import pytest
+
+import fagen
+import oracle
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+
+def run_split(inp, w, n_split, workspace=None):
+    import torch
+    import flash_attention_forward_fa_amd as fa
+    q, k, v = (gu.to_dev(inp[n], "cuda:0") for n in ("q", "k", "v"))
+    O, L = fa.train_fwd_split(q, k, v, n_split, scale=w.scale, causal=w.causal,
+                              workspace=workspace)
+    torch.cuda.synchronize()
+    bits = O.view(torch.int16).cpu().numpy().view(np.uint16)
+    return gu.widen(bits), L.cpu().numpy(), bits
+
+
+CASES = [
+    # (B, H, Hkv, ql, kl, D, causal, n_split)
+    (1, 4, 1, 300, 5000, 64, True, 8),      # prefill against a longer cache (offset 4700)
+    (2, 8, 2, 1, 3000, 128, True, 16),      # decoding one token
+    (1, 4, 4, 4, 2100, 64, False, 33),      # a few query rows, ragged chunks
+    (1, 2, 1, 257, 1000, 256, False, 4),
+    (1, 8, 2, 512, 4096, 128, True, 32),
+    (1, 2, 1, 300, 200, 64, True, 3),       # ql > kl: offset 0, early chunks only
+    (1, 2, 2, 100, 100, 64, True, 10),      # more chunks than key tiles
+    (2, 4, 2, 64, 700, 256, True, 1),       # one chunk
+]
+
+
+@pytest.mark.parametrize("B,H,Hkv,ql,kl,D,causal,n_split", CASES)
+def test_split_matches_oracle(B, H, Hkv, ql, kl, D, causal, n_split):
+    w = fagen.Workload("split", B, H, Hkv, ql, kl, D, causal,
+                       seed_offset=9000 + ql + kl + D + n_split)
+    print(f"case split {(B, H, Hkv, ql, kl, D, causal, n_split)}", flush=True)
+    inp = fagen.generate(w)
+    o, l, bits = run_split(inp, w, n_split)
+    _, ob, lr = oracle.fwd_workload(w, inp)
+    tol_o, tol_l = gu.tolerances(kl)
+    eo, el, rms = gu.compare(o, l, bits, ob, lr, tol_o, tol_l, f"split {B,H,ql,kl,D,n_split}")
+    print(f"split {(B, H, Hkv, ql, kl, D, causal, n_split)}: dO={eo:.3e} dL={el:.3e} "
+          f"relRMS={rms:.2e}")
+    assert rms <= 5e-3
+
+
+def test_split_reused_workspace_and_kl_zero():
+    """One workspace serves calls of different sizes in a row (its contents on
+    entry do not matter); kl = 0 gives empty rows without using it."""
+    import torch
+    import flash_attention_forward_fa_amd as fa
+    big = fagen.Workload("split_big", 1, 4, 2, 128, 3000, 64, True, seed_offset=9100)
+    small = fagen.Workload("split_small", 1, 2, 1, 40, 700, 64, True, seed_offset=9101)
+    print("case split workspace reuse", flush=True)
+    need = fa.fa_train_fwd_split_workspace(1, 4, 128, 64, 12)
+    ws = torch.full((need,), 0x7F, dtype=torch.uint8, device="cuda:0")  # NaN-like garbage
+    for w in (big, small, big):
+        inp = fagen.generate(w)
+        o, l, bits = run_split(inp, w, 12, workspace=ws)
+        _, ob, lr = oracle.fwd_workload(w, inp)
+        gu.compare(o, l, bits, ob, lr, 1e-2, 1e-2, f"split reuse {w.name}")
+    q = torch.randn(1, 2, 5, 64, device="cuda:0").to(torch.bfloat16)
+    k = torch.empty(1, 1, 0, 64, device="cuda:0", dtype=torch.bfloat16)
+    O, L = fa.train_fwd_split(q, k, k, 4, workspace=torch.empty(0, dtype=torch.uint8,
+                                                                 device="cuda:0"))
+    torch.cuda.synchronize()
+    assert torch.all(O.float() == 0) and torch.all(torch.isneginf(L))
+
+
+def test_split_long_cache_sampled_rows():
+    """Prefill of 512 tokens against a 32k cache (B1, 32 query heads on 8 kv
+    heads, head_dim 128, causal offset 32256), 32 chunks, sampled rows."""
+    w = fagen.Workload("split_long", 1, 32, 8, 512, 32768, 128, True, seed_offset=9200)
+    print("case split long cache", flush=True)
+    inp = fagen.generate(w)
+    o, l, bits = run_split(inp, w, 32)
+    rng = np.random.default_rng(9200)
+    rows = np.unique(np.concatenate([np.arange(64), rng.integers(0, w.B * w.H * w.ql, 160),
+                                     31 * w.ql + np.arange(w.ql - 32, w.ql)])).astype(np.int64)
+    _, ob, lr = oracle.fwd_workload(w, inp, rows=rows)
+    o2, l2, b2 = o.reshape(-1, w.D)[rows], l.reshape(-1)[rows], bits.reshape(-1, w.D)[rows]
+    eo, el, rms = gu.compare(o2, l2, b2, ob, lr, 1e-2, 1e-2, "split long cache")
+    print(f"split long cache: {rows.size} rows dO={eo:.3e} dL={el:.3e} relRMS={rms:.2e}")
+    assert rms <= 1e-2
+    assert np.isfinite(o).all() and np.isfinite(l).all()
+
+
+def test_split_errors_raise_from_binding():
+    import torch
+    import flash_attention_forward_fa_amd as fa
+    q = torch.zeros(1, 1, 4, 64, device="cuda:0", dtype=torch.bfloat16)
+    with pytest.raises(fa.FAError) as e:
+        fa.train_fwd_split(q, q, q, 0)
+    assert e.value.status == 11
+    with pytest.raises(fa.FAError) as e:
+        fa.train_fwd_split(q, q, q, 2, workspace=torch.empty(16, dtype=torch.uint8,
+                                                             device="cuda:0"))
+    assert e.value.status == 11
