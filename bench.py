@@ -91,6 +91,8 @@ def main():
                     help="timed sliding-window forward calls per workload (0: none)")
     ap.add_argument("--d128-steps", type=int, default=10,
                     help="timed head_dim-128 forward and backward calls (0: none)")
+    ap.add_argument("--split-steps", type=int, default=10,
+                    help="timed long-cache calls, plain and split-KV (0: none)")
     ap.add_argument("--cpu-rows", type=int, default=0,
                     help="rows per workload for the CPU baseline (0: default sample)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -268,6 +270,52 @@ def main():
             f"{bms * 1e3:.1f} us/call, {d128['backward_tflops']:.1f} TFLOP/s (FA-2 count)")
         del q, k, v, dO, O, L
 
+    # Few query tiles against a long KV cache (batch 1, head_dim 128, 32 query
+    # heads on 8 kv heads, causal): prefill of 512 tokens and decoding 1 token
+    # against 32768 keys, whose plain launches have 64 and 32 workgroups, the
+    # plain launch against the split-KV one (8 chunks); not part of the
+    # headline metric. FLOP: 4*D per visible score.
+    split_kv = {}
+    if args.split_steps > 0:
+        for name, B, ql, kl, n_split in (("prefill_b1_h32kv8_q512_k32768_d128", 1, 512, 32768, 8),
+                                         ("decode_b1_h32kv8_q1_k32768_d128", 1, 1, 32768, 8)):
+            w = fagen.Workload(name, B, 32, 8, ql, kl, 128, True, seed_offset=9300 + ql)
+            inp = fagen.generate(w)
+            to = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+            q, k, v = to(inp["q"]), to(inp["k"]), to(inp["v"])
+            O = torch.empty_like(q)
+            L = torch.empty((w.B, w.H, w.ql), dtype=torch.float32, device=dev)
+            ws = torch.empty(fa.fa_train_fwd_split_workspace(w.B, w.H, w.ql, w.D, n_split),
+                             dtype=torch.uint8, device=dev)
+            off = max(kl - ql, 0)
+            visible = int(np.minimum(off + np.arange(ql) + 1, kl).sum()) * w.B * w.H
+            flop = 4 * w.D * visible
+            res = {"n_split": n_split, "flop": flop, "kv_bytes": 2 * 2 * w.B * w.Hkv * kl * w.D}
+            for label, call in (("plain", lambda: fa.train_fwd(q, k, v, scale=w.scale, causal=True,
+                                                               out=O, lse=L)),
+                                ("split", lambda: fa.train_fwd_split(q, k, v, n_split,
+                                                                     scale=w.scale, causal=True,
+                                                                     workspace=ws, out=O,
+                                                                     lse=L))):
+                for _ in range(3):
+                    call()
+                torch.cuda.synchronize()
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                for _ in range(args.split_steps):
+                    call()
+                b.record(stream)
+                torch.cuda.synchronize()
+                ms = a.elapsed_time(b) / args.split_steps
+                res[f"{label}_ms_avg"] = ms
+                res[f"{label}_tflops"] = flop / (ms * 1e-3) / 1e12
+                res[f"{label}_kv_gbs"] = res["kv_bytes"] / (ms * 1e-3) / 1e9
+            split_kv[name] = res
+            log(f"{name}: plain {res['plain_ms_avg'] * 1e3:.1f} us, split({n_split}) "
+                f"{res['split_ms_avg'] * 1e3:.1f} us ({res['split_tflops']:.1f} TFLOP/s, "
+                f"K+V {res['split_kv_gbs']:.0f} GB/s)")
+            del q, k, v, O, L, ws
+
     if args.copy_calibration:
         n = args.copy_calibration * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device=dev)
@@ -327,6 +375,8 @@ def main():
         result["sliding_window"] = swa
     if d128:
         result["head_dim_128"] = d128
+    if split_kv:
+        result["split_kv"] = split_kv
     if not args.no_cpu_baseline:
         target = {w.name: (args.cpu_rows or (524288 if w.D == 64 else 65536)) for w in workloads}
         result["cpu_baseline"] = cpu_baseline(workloads, inputs, target)

@@ -134,6 +134,14 @@ def fa_train_fwd_split(q, k, v, batch, n_heads, n_kv_heads, ql, kl, head_dim, sc
                                     O or None, L or None, stream or None)
 
 
+def suggest_n_split(batch, n_heads, ql, head_dim, n_cu=256):
+    """Chunks for train_fwd_split: about two workgroups per CU in total, or 1
+    (use train_fwd) when the plain launch already has one per CU."""
+    rows = 128 if head_dim == 256 else 256
+    plain = batch * n_heads * ((ql + rows - 1) // rows)
+    return 1 if plain >= n_cu else max(1, (2 * n_cu + plain - 1) // plain)
+
+
 def fa_train_fwd_split_workspace(batch, n_heads, ql, head_dim, n_split):
     """Workspace bytes fa_train_fwd_split needs (0 for invalid sizes)."""
     return int(lib().fa_train_fwd_split_workspace(batch, n_heads, ql, head_dim, n_split))

@@ -161,7 +161,12 @@ int fa_train_fwd_ex(const void *q, const void *k, const void *v, const void *mas
  *
  *   n_split    requested chunks, 1..65536; the keys are cut into chunks of
  *              whole 64-key tiles, ceil(kl / n_split) rounded up, so fewer
- *              chunks may run.
+ *              chunks may run. The split pays while the plain launch has
+ *              fewer workgroups than the GPU has CUs: the plain launch has
+ *              batch * n_heads * ceil(ql / R) workgroups (R = 256 query rows
+ *              for head_dim 64 and 128, 128 for 256); about two workgroups
+ *              per CU in total (n_split ~ 2 * 256 / that count) was fastest
+ *              on MI355X, and at one or more per CU the plain call is faster.
  *   workspace  device memory of workspace_bytes >= fa_train_fwd_split_workspace
  *              (batch, n_heads, ql, head_dim, n_split), 16-byte aligned, owned by
  *              the caller; its contents on entry do not matter and are

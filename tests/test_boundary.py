@@ -224,3 +224,10 @@ def test_backward_binding_fails_loudly_without_gpu_tensors():
         fa.train_bwd(q, q, q, q, L, q)
     with pytest.raises(TypeError):
         fa.train_bwd(q.float(), q, q, q, L, q)
+
+
+def test_suggest_n_split():
+    assert fa.suggest_n_split(1, 32, 512, 128) == 8     # 64 plain workgroups
+    assert fa.suggest_n_split(1, 32, 1, 128) == 16      # 32 plain workgroups
+    assert fa.suggest_n_split(8, 32, 1, 128) == 1       # 256: one per CU already
+    assert fa.suggest_n_split(2, 16, 8192, 256) == 1
