@@ -273,16 +273,18 @@ def main():
             f"{bms * 1e3:.1f} us/call, {d128['backward_tflops']:.1f} TFLOP/s (FA-2 count)")
         del q, k, v, dO, O, L
 
-    # Few query tiles against a long KV cache (batch 1, head_dim 128, 32 query
+    # Few query tiles against a long KV cache (head_dim 128, 32 query
     # heads on 8 kv heads, causal): prefill of 512 tokens and decoding 1 token
-    # against 32768 keys, whose plain launches have 64 and 32 workgroups, the
-    # plain launch against the split-KV one (8 chunks); not part of the
-    # headline metric. FLOP: 4*D per visible score.
+    # (batch 1 and 8) against 32768 keys, the plain launch against the split-KV
+    # one (suggest_n_split chunks); not part of the headline metric. FLOP: 4*D
+    # per visible score; K+V GB/s: the cache's bytes over the call's time.
     split_kv = {}
     if args.split_steps > 0:
-        for name, B, ql, kl, n_split in (("prefill_b1_h32kv8_q512_k32768_d128", 1, 512, 32768, 8),
-                                         ("decode_b1_h32kv8_q1_k32768_d128", 1, 1, 32768, 8)):
+        for name, B, ql, kl in (("prefill_b1_h32kv8_q512_k32768_d128", 1, 512, 32768),
+                                ("decode_b1_h32kv8_q1_k32768_d128", 1, 1, 32768),
+                                ("decode_b8_h32kv8_q1_k32768_d128", 8, 1, 32768)):
             w = fagen.Workload(name, B, 32, 8, ql, kl, 128, True, seed_offset=9300 + ql)
+            n_split = fa.suggest_n_split(B, 32, ql, 128, n_kv_heads=8)
             inp = fagen.generate(w)
             to = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
             q, k, v = to(inp["q"]), to(inp["k"]), to(inp["v"])

@@ -134,10 +134,14 @@ def fa_train_fwd_split(q, k, v, batch, n_heads, n_kv_heads, ql, kl, head_dim, sc
                                     O or None, L or None, stream or None)
 
 
-def suggest_n_split(batch, n_heads, ql, head_dim, n_cu=256):
+def suggest_n_split(batch, n_heads, ql, head_dim, n_kv_heads=None, n_cu=256):
     """Chunks for train_fwd_split: about two workgroups per CU in total, or 1
-    (use train_fwd) when the plain launch already has one per CU."""
+    (use train_fwd) when the plain launch already has one per CU. With one
+    query row per head and GQA (no mask, no window) the library runs a kv
+    group's query heads as one packed head: batch * n_kv_heads launch rows."""
     rows = 128 if head_dim == 256 else 256
+    if ql == 1 and n_kv_heads and n_heads > n_kv_heads:
+        n_heads, ql = n_kv_heads, n_heads // n_kv_heads
     plain = batch * n_heads * ((ql + rows - 1) // rows)
     return 1 if plain >= n_cu else max(1, (2 * n_cu + plain - 1) // plain)
 

@@ -778,6 +778,17 @@ int train_fwd(const void* q, const void* k, const void* v, const void* mask, int
       (kv_used && (!aligned(k, 16) || !aligned(v, 16))) ||
       (mask && !aligned(mask, mask_dtype == FA_MASK_BF16 ? 2 : 4)))
     return FA_ERR_ALIGNMENT;
+  // One query row per head (decoding), no mask, no window: the layout
+  // [B, H, 1, D] of Q, O (and [B, H, 1] of L) is [B, Hkv, H/Hkv, D], so a kv
+  // group's query heads are the rows of one packed head and each K/V tile is
+  // read once per group. Every such row has q_abs = kl - 1 and sees all kl
+  // keys under the causal rule: the packed problem is the non-causal one. The
+  // arithmetic of each row is unchanged (rows are computed independently).
+  if (ql == 1 && n_heads > n_kv_heads && !mask && window < 0) {
+    ql = n_heads / n_kv_heads;
+    n_heads = n_kv_heads;
+    causal = 0;
+  }
   const int bm = head_dim == 64    ? block_m<64>()
                  : head_dim == 128 ? block_m<128>()
                                    : block_m<256>();

@@ -164,9 +164,15 @@ int fa_train_fwd_ex(const void *q, const void *k, const void *v, const void *mas
  *              chunks may run. The split pays while the plain launch has
  *              fewer workgroups than the GPU has CUs: the plain launch has
  *              batch * n_heads * ceil(ql / R) workgroups (R = 256 query rows
- *              for head_dim 64 and 128, 128 for 256); about two workgroups
- *              per CU in total (n_split ~ 2 * 256 / that count) was fastest
- *              on MI355X, and at one or more per CU the plain call is faster.
+ *              for head_dim 64 and 128, 128 for 256), and batch * n_kv_heads
+ *              when ql == 1 (below); about two workgroups per CU in total
+ *              (n_split ~ 2 * 256 / that count) was near the fastest on
+ *              MI355X, and at one or more per CU the plain call is faster.
+ *
+ * Decoding (ql == 1, n_heads > n_kv_heads, no mask, no window; this and the
+ * other forward entry points): [B, H, 1, D] is [B, Hkv, H/Hkv, D], so a kv
+ * group's query heads run as the rows of one head and each K/V tile is read
+ * once per group; each row sees all kl keys either way (same bits).
  *   workspace  device memory of workspace_bytes >= fa_train_fwd_split_workspace
  *              (batch, n_heads, ql, head_dim, n_split), 16-byte aligned, owned by
  *              the caller; its contents on entry do not matter and are

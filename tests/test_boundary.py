@@ -69,7 +69,9 @@ def _call(**over):
     (dict(head_dim=0), 4), (dict(scale=math.nan), 5), (dict(scale=math.inf), 5),
     (dict(scale=-math.inf), 5), (dict(q=A + 2), 6), (dict(k=A + 8), 6), (dict(O=A + 4), 6),
     (dict(mask=A + 2), 6), (dict(L=A + 1), 6),
-    (dict(batch=65536, n_heads=65536, n_kv_heads=1, ql=1), 7),
+    # (ql = 2: with ql = 1 the GQA heads would be packed into 65536-row heads,
+    # a valid size that would reach the launch)
+    (dict(batch=65536, n_heads=65536, n_kv_heads=1, ql=2), 7),
 ])
 def test_invalid_arguments_are_rejected(over, code):
     assert _call(**over) == code
@@ -230,4 +232,6 @@ def test_suggest_n_split():
     assert fa.suggest_n_split(1, 32, 512, 128) == 8     # 64 plain workgroups
     assert fa.suggest_n_split(1, 32, 1, 128) == 16      # 32 plain workgroups
     assert fa.suggest_n_split(8, 32, 1, 128) == 1       # 256: one per CU already
+    assert fa.suggest_n_split(8, 32, 1, 128, n_kv_heads=8) == 8   # packed: 64
+    assert fa.suggest_n_split(1, 32, 1, 128, n_kv_heads=8) == 64  # packed: 8
     assert fa.suggest_n_split(2, 16, 8192, 256) == 1

@@ -101,13 +101,19 @@ RAGGED = [  # head_dim 128 (the adjacent attention API's size) at the end
     (1, 2, 1, 150, 150, 128, True, False),
     (2, 4, 2, 257, 300, 128, True, True),
     (1, 2, 2, 300, 100, 128, True, False),   # ql > kl
+    # one query row per head (decoding): GQA groups run as packed heads
+    (2, 8, 2, 1, 700, 64, True, False),
+    (1, 4, 1, 1, 100, 256, False, False),
+    (1, 8, 1, 1, 5000, 128, True, False),
+    (2, 4, 2, 1, 300, 64, True, True),       # with a mask: not packed
 ]
 
 
 @pytest.mark.parametrize("B,H,Hkv,ql,kl,D,causal,masked", RAGGED)
 def test_ragged_shapes_match_oracle(B, H, Hkv, ql, kl, D, causal, masked):
     w = fagen.Workload("ragged", B, H, Hkv, ql, kl, D, causal,
-                       mask_p=0.1 if masked else None, mask_full_rows=2 if masked else 0,
+                       mask_p=0.1 if masked else None,
+                       mask_full_rows=2 if masked and ql > 2 else 0,
                        seed_offset=1000 + ql * 7 + kl + D)
     print(f"case ragged {w}", flush=True)
     inp = fagen.generate(w)
