@@ -18,6 +18,7 @@ FA_STATUS = {
     0: "FA_OK", 1: "FA_ERR_NULL_POINTER", 2: "FA_ERR_BAD_SIZE", 3: "FA_ERR_HEAD_GROUPING",
     4: "FA_ERR_HEAD_DIM", 5: "FA_ERR_SCALE", 6: "FA_ERR_ALIGNMENT", 7: "FA_ERR_TOO_LARGE",
     8: "FA_ERR_LAUNCH", 9: "FA_ERR_WINDOW", 10: "FA_ERR_MASK", 11: "FA_ERR_SPLIT",
+    12: "FA_ERR_PAGED",
 }
 FA_MASK_F32, FA_MASK_BF16 = 0, 1
 
@@ -55,6 +56,9 @@ def lib():
         l.fa_train_fwd_split.restype = ci
         l.fa_train_fwd_split_workspace.argtypes = [ci, ci, ci, ci, ci]
         l.fa_train_fwd_split_workspace.restype = ul
+        l.fa_paged_fwd.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, ci, ci,
+                                   ctypes.c_float, ci, ci, vp, ul, vp, vp, vp]
+        l.fa_paged_fwd.restype = ci
         l.fa_train_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci,
                                    ctypes.c_float, ci, vp, vp, vp, vp]
         l.fa_train_bwd.restype = ci
@@ -173,6 +177,67 @@ def train_fwd_split(q, k, v, n_split, scale=None, causal=False, workspace=None, 
         status = fa_train_fwd_split(q.data_ptr(), k.data_ptr(), v.data_ptr(), B, H, Hkv, ql, kl,
                                     D, scale, causal, n_split, workspace.data_ptr(),
                                     workspace.numel(), O.data_ptr(), L.data_ptr(), s.cuda_stream)
+    if status != 0:
+        raise FAError(status, status_string(status))
+    return O, L
+
+
+def fa_paged_fwd(q, k_cache, v_cache, block_table, seq_lens, batch, n_heads, n_kv_heads, ql,
+                 n_blocks, block_size, max_blocks, head_dim, scale, causal, n_split, workspace,
+                 workspace_bytes, O, L, stream):
+    """The C entry point with raw integer pointers (0 for NULL); returns the status."""
+    return lib().fa_paged_fwd(q or None, k_cache or None, v_cache or None, block_table or None,
+                              seq_lens or None, batch, n_heads, n_kv_heads, ql, n_blocks,
+                              block_size, max_blocks, head_dim, float(scale), int(bool(causal)),
+                              int(n_split), workspace or None, int(workspace_bytes), O or None,
+                              L or None, stream or None)
+
+
+def paged_fwd(q, k_cache, v_cache, block_table, seq_lens, scale=None, causal=False, n_split=0,
+              workspace=None, out=None, lse=None, stream=None):
+    """O, L = paged_fwd(q, k_cache, v_cache, block_table, seq_lens, scale=None, causal=False,
+                        n_split=0, workspace=None)
+
+    q: bf16 [B, H, ql, D]; k_cache, v_cache: bf16 [n_blocks, Hkv, block_size, D];
+    block_table: int32 [B, max_blocks]; seq_lens: int32 [B] (all on q's GPU).
+    Sequence b attends to its first seq_lens[b] keys (key position p at row
+    p % block_size of block block_table[b, p // block_size]). n_split > 0 uses
+    split-KV with a workspace (allocated here when None).
+    """
+    import torch
+
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.bfloat16:
+            raise TypeError(f"{name} must be a bfloat16 tensor")
+        if t.dim() != 4 or not t.is_contiguous() or not t.is_cuda or t.device != q.device:
+            raise ValueError(f"{name} must be a contiguous 4-d tensor on q's GPU")
+    for name, t in (("block_table", block_table), ("seq_lens", seq_lens)):
+        if (not isinstance(t, torch.Tensor) or t.dtype != torch.int32 or not t.is_contiguous()
+                or t.device != q.device):
+            raise ValueError(f"{name} must be a contiguous int32 tensor on q's device")
+    B, H, ql, D = q.shape
+    n_blocks, Hkv, bs, Dk = k_cache.shape
+    if tuple(v_cache.shape) != tuple(k_cache.shape) or Dk != D:
+        raise ValueError("k_cache and v_cache must be [n_blocks, Hkv, block_size, D]")
+    if block_table.dim() != 2 or block_table.shape[0] != B or tuple(seq_lens.shape) != (B,):
+        raise ValueError("block_table must be [B, max_blocks] and seq_lens [B]")
+    max_blocks = block_table.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    O = out if out is not None else torch.empty_like(q)
+    L = lse if lse is not None else torch.empty((B, H, ql), dtype=torch.float32, device=q.device)
+    ws_ptr, ws_bytes = 0, 0
+    if n_split > 0:
+        if workspace is None:
+            need = fa_train_fwd_split_workspace(B, H, ql, D, n_split)
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel()
+    s = stream if stream is not None else torch.cuda.current_stream(q.device)
+    with torch.cuda.device(q.device):
+        status = fa_paged_fwd(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                              block_table.data_ptr(), seq_lens.data_ptr(), B, H, Hkv, ql,
+                              n_blocks, bs, max_blocks, D, scale, causal, n_split, ws_ptr,
+                              ws_bytes, O.data_ptr(), L.data_ptr(), s.cuda_stream)
     if status != 0:
         raise FAError(status, status_string(status))
     return O, L

@@ -84,7 +84,10 @@ constexpr float kLazy = 8.0f;
 // In the split-KV kernel (kSplit) a workgroup computes one key chunk of its
 // query tile, compensated, and writes the chunk's normalised partial O and its
 // logsumexp to a workspace; a combine kernel merges the chunks through L.
-constexpr int kMixed = 0, kAll = 1, kSplit = 2;
+// The paged kernels (kPaged, kPagedSplit) read K and V from a block-paged
+// cache through a block table, with a key count per sequence; they compute
+// every tile compensated, the second one as split-KV partials.
+constexpr int kMixed = 0, kAll = 1, kSplit = 2, kPaged = 3, kPagedSplit = 4;
 // Additive mask element types (kNoMask: no mask).
 constexpr int kNoMask = 0, kMaskF32 = 1, kMaskBF16 = 2;
 
@@ -118,6 +121,9 @@ struct FwdArgs {
   int kchunk;      // kSplit: keys per chunk (a multiple of the key tile)
   float* ws_o;     // kSplit: partial O, f32 [n_split, B, H, ql, D]
   float* ws_l;     // kSplit: partial L, f32 [n_split, B, H, ql]
+  const int* block_table;  // paged: int32 [B, max_blocks], block of each block_size keys
+  const int* seq_lens;     // paged: int32 [B], keys of each sequence
+  int max_blocks, block_size, n_blocks;  // paged: table width, keys per block, cache blocks
   float c;         // |scale| * log2(e), at least FLT_MIN
   uint32_t q_sign; // 0x80008000 flips the sign of both bf16 halves (scale < 0)
 };
@@ -130,7 +136,8 @@ struct FwdArgs {
 // (wg_flags: one int per wave). With REDO (and PRECISE), only the rows with
 // redo set are computed and written (waves without such a row only take part
 // in the tile copies).
-template <int D, bool CAUSAL, bool WINDOW, int MASK, bool PRECISE, bool REDO, bool SPLIT = false>
+template <int D, bool CAUSAL, bool WINDOW, int MASK, bool PRECISE, bool REDO, bool SPLIT = false,
+          bool PAGED = false>
 __device__ __forceinline__ bool fwd_tile(const FwdArgs& a, int qtile, int bh, uint16_t* k0s,
                                          uint16_t* v0s, uint16_t* k1s, uint16_t* v1s,
                                          bool (&redo)[Cfg<D>::QB], int* wg_flags, int split = 0) {
@@ -140,6 +147,8 @@ __device__ __forceinline__ bool fwd_tile(const FwdArgs& a, int qtile, int bh, ui
   static_assert(CAUSAL || !WINDOW, "the sliding window includes the causal rule");
   static_assert(!SPLIT || (PRECISE && !REDO && !WINDOW && MASK == kNoMask),
                 "split-KV partials: compensated, unmasked, no window");
+  static_assert(!PAGED || (PRECISE && !REDO && !WINDOW && MASK == kNoMask),
+                "paged KV: compensated, unmasked, no window");
   constexpr int BN = Cfg<D>::BN;
   constexpr int kQB = Cfg<D>::QB;
   constexpr int kRowsPerWave = 16 * kQB;
@@ -168,7 +177,12 @@ __device__ __forceinline__ bool fwd_tile(const FwdArgs& a, int qtile, int bh, ui
 
   const int b = bh / a.H, h = bh % a.H;
   const int g = h / a.group;
-  const int ql = a.ql, kl = a.kl, off = a.causal_off;
+  // (paged KV: the sequence's own key count, at most its table's capacity, and
+  // its own causal offset)
+  const int kl = PAGED ? min(max(__builtin_amdgcn_readfirstlane(a.seq_lens[b]), 0),
+                             a.max_blocks * a.block_size)
+                       : a.kl;
+  const int ql = a.ql, off = PAGED ? max(kl - ql, 0) : a.causal_off;
   const int q0 = qtile * kBlockM;
   const int qw0 = q0 + wave * kRowsPerWave;
   const int64_t kv_off = (int64_t)(b * a.Hkv + g) * kl * D;
@@ -199,11 +213,30 @@ __device__ __forceinline__ bool fwd_tile(const FwdArgs& a, int qtile, int bh, ui
   int koff[CopyShape<D, BN, NT>::ROUNDS], voff[CopyShape<D, BN, NT>::ROUNDS];
   copy_offsets<D, BN, NT, true>(tid, koff);
   copy_offsets<D, BN, NT, false>(tid, voff);
+  // paged KV: a tile (block_size is a multiple of BN) lies in one block,
+  // table[b][kt*BN / block_size], from row (kt*BN) % block_size; its copy
+  // descriptor covers only the tile's valid rows. A table entry outside the
+  // cache is clamped into it (wrong keys, never an access outside the cache).
+  auto paged_src = [&](const uint16_t* cache, int kt) {
+    const int pos = kt * BN;
+    int blk = __builtin_amdgcn_readfirstlane(
+        a.block_table[(int64_t)b * a.max_blocks + pos / a.block_size]);
+    blk = min(max(blk, 0), a.n_blocks - 1);
+    return cache + (((int64_t)blk * a.Hkv + g) * a.block_size + pos % a.block_size) * D;
+  };
   auto issue_k = [&](int kt, uint16_t* dst) {
-    issue_tile<D, BN, NT, true>(kp, kt * BN, kl, dst, tid, 64 * wave, koff);
+    if constexpr (PAGED)
+      issue_tile<D, BN, NT, true>(paged_src(a.k, kt), 0, min(BN, kl - kt * BN), dst, tid,
+                                  64 * wave, koff);
+    else
+      issue_tile<D, BN, NT, true>(kp, kt * BN, kl, dst, tid, 64 * wave, koff);
   };
   auto issue_v = [&](int kt, uint16_t* dst) {
-    issue_tile<D, BN, NT, false>(vp, kt * BN, kl, dst, tid, 64 * wave, voff);
+    if constexpr (PAGED)
+      issue_tile<D, BN, NT, false>(paged_src(a.v, kt), 0, min(BN, kl - kt * BN), dst, tid,
+                                   64 * wave, voff);
+    else
+      issue_tile<D, BN, NT, false>(vp, kt * BN, kl, dst, tid, 64 * wave, voff);
   };
   if (n_kt > kt_first) issue_k(kt_first, (kt_first & 1) ? k1s : k0s);
 
@@ -584,7 +617,8 @@ __device__ __forceinline__ bool fwd_tile(const FwdArgs& a, int qtile, int bh, ui
 template <int D, bool CAUSAL, bool WINDOW, int MASK, int MODE>
 __global__ __launch_bounds__(64 * Cfg<D>::W)
 __attribute__((amdgpu_waves_per_eu(MODE == kMixed ? Cfg<D>::WPE : 2))) void fa_fwd_kernel(FwdArgs a) {
-  static_assert(MODE != kSplit || (MASK == kNoMask && !WINDOW), "split-KV: unmasked, no window");
+  static_assert(MODE < kSplit || (MASK == kNoMask && !WINDOW),
+                "split-KV and paged: unmasked, no window");
   static_assert(MODE != kMixed || MASK == kNoMask, "the masked forward always runs compensated");
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
   constexpr int TILE = Cfg<D>::BN * D;
@@ -603,8 +637,9 @@ __attribute__((amdgpu_waves_per_eu(MODE == kMixed ? Cfg<D>::WPE : 2))) void fa_f
   // (Groups of 1, 2 or 4 heads were measured slower, 8 faster than all.)
   // (split-KV: the chunk index is the fastest-varying part of the block index)
   const int BH = a.B * a.H;
-  const int split = MODE == kSplit ? (int)(blockIdx.x % (unsigned)a.n_split) : 0;
-  const int bid = MODE == kSplit ? (int)(blockIdx.x / (unsigned)a.n_split) : (int)blockIdx.x;
+  constexpr bool SPLIT_GRID = MODE == kSplit || MODE == kPagedSplit;
+  const int split = SPLIT_GRID ? (int)(blockIdx.x % (unsigned)a.n_split) : 0;
+  const int bid = SPLIT_GRID ? (int)(blockIdx.x / (unsigned)a.n_split) : (int)blockIdx.x;
   int qt_rev, bh;
   if ((BH & 7) == 0) {
     const int xcd = bid & 7, tl = bid >> 3, per = BH >> 3;
@@ -634,6 +669,12 @@ __attribute__((amdgpu_waves_per_eu(MODE == kMixed ? Cfg<D>::WPE : 2))) void fa_f
   } else if constexpr (MODE == kSplit) {
     fwd_tile<D, CAUSAL, false, kNoMask, true, false, true>(a, qtile, bh, k0s, v0s, k1s, v1s, redo,
                                                            wg_flags, split);
+  } else if constexpr (MODE == kPaged) {
+    fwd_tile<D, CAUSAL, false, kNoMask, true, false, false, true>(a, qtile, bh, k0s, v0s, k1s,
+                                                                  v1s, redo, wg_flags);
+  } else if constexpr (MODE == kPagedSplit) {
+    fwd_tile<D, CAUSAL, false, kNoMask, true, false, true, true>(a, qtile, bh, k0s, v0s, k1s, v1s,
+                                                                 redo, wg_flags, split);
   } else {
     fwd_tile<D, CAUSAL, WINDOW, MASK, true, false>(a, qtile, bh, k0s, v0s, k1s, v1s, redo,
                                                    wg_flags);
@@ -709,13 +750,13 @@ hipError_t dispatch_c(FwdArgs a, int mask, int n_short, hipStream_t stream) {
 }
 
 // Split-KV: the partials over all (chunk, head, query tile), then the merge.
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool PAGED = false>
 hipError_t dispatch_split(FwdArgs a, hipStream_t stream) {
   const unsigned bh = (unsigned)(a.B * a.H);
   a.qt_base = 0;
   a.qt_count = a.n_qtiles;
   a.n_precise = a.n_qtiles;
-  hipError_t e = launch<D, CAUSAL, false, kNoMask, kSplit>(
+  hipError_t e = launch<D, CAUSAL, false, kNoMask, PAGED ? kPagedSplit : kSplit>(
       a, bh * (unsigned)a.n_qtiles * (unsigned)a.n_split, stream);
   if (e != hipSuccess) return e;
   CombineArgs c;
@@ -728,6 +769,20 @@ hipError_t dispatch_split(FwdArgs a, hipStream_t stream) {
   hipLaunchKernelGGL(fa_combine_kernel<D>, dim3((unsigned)((c.rows + 3) / 4)), dim3(256), 0, stream,
                      c);
   return hipGetLastError();
+}
+
+// Paged KV: one compensated launch over all query tiles, or the split-KV pair.
+template <int D>
+hipError_t dispatch_paged(FwdArgs a, bool causal, hipStream_t stream) {
+  if (a.n_split > 0)
+    return causal ? dispatch_split<D, true, true>(a, stream)
+                  : dispatch_split<D, false, true>(a, stream);
+  const unsigned grid = (unsigned)(a.B * a.H) * (unsigned)a.n_qtiles;
+  a.qt_base = 0;
+  a.qt_count = a.n_qtiles;
+  a.n_precise = a.n_qtiles;
+  return causal ? launch<D, true, false, kNoMask, kPaged>(a, grid, stream)
+                : launch<D, false, false, kNoMask, kPaged>(a, grid, stream);
 }
 
 template <int D>
@@ -901,6 +956,85 @@ extern "C" int fa_train_fwd_split(const void* q, const void* k, const void* v, i
                    workspace_bytes);
 }
 
+extern "C" int fa_paged_fwd(const void* q, const void* k_cache, const void* v_cache,
+                            const int* block_table, const int* seq_lens, int batch, int n_heads,
+                            int n_kv_heads, int ql, int n_blocks, int block_size, int max_blocks,
+                            int head_dim, float scale, int causal, int n_split, void* workspace,
+                            unsigned long workspace_bytes, void* O, float* L, void* stream) {
+  if (batch < 0 || ql < 0 || n_heads < 1 || n_kv_heads < 1 || max_blocks < 0 || n_blocks < 0)
+    return FA_ERR_BAD_SIZE;
+  if (n_heads % n_kv_heads != 0) return FA_ERR_HEAD_GROUPING;
+  if (head_dim != 64 && head_dim != 128 && head_dim != 256) return FA_ERR_HEAD_DIM;
+  if (!isfinite(scale)) return FA_ERR_SCALE;
+  if (block_size < 64 || block_size % 64 != 0) return FA_ERR_PAGED;
+  if (n_split < 0 || n_split > kMaxSplit) return FA_ERR_SPLIT;
+  const int64_t rows = (int64_t)batch * n_heads * ql;
+  if (rows == 0) return FA_OK;
+  const int64_t cap = (int64_t)max_blocks * block_size;  // keys a table can address
+  if (cap > 0x7fffffffLL) return FA_ERR_TOO_LARGE;
+  if (cap > 0 && n_blocks < 1) return FA_ERR_PAGED;
+  if (!q || !O || !L || !seq_lens || (cap > 0 && (!k_cache || !v_cache || !block_table)))
+    return FA_ERR_NULL_POINTER;
+  if (!aligned(q, 16) || !aligned(O, 16) || !aligned(L, 4) || !aligned(seq_lens, 4) ||
+      (cap > 0 && (!aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(block_table, 4))))
+    return FA_ERR_ALIGNMENT;
+  // decoding: a kv group's query heads as the rows of one head (as in train_fwd)
+  int H = n_heads, qlen = ql, cz = causal;
+  if (ql == 1 && n_heads > n_kv_heads) {
+    qlen = n_heads / n_kv_heads;
+    H = n_kv_heads;
+    cz = 0;
+  }
+  const int bm = head_dim == 64    ? block_m<64>()
+                 : head_dim == 128 ? block_m<128>()
+                                   : block_m<256>();
+  const int64_t n_qtiles = ((int64_t)qlen + bm - 1) / bm;
+  const int64_t grid = n_qtiles * batch * H;
+  if (grid > 0x7fffffffLL || (int64_t)batch * H > 0x7fffffffLL ||
+      (int64_t)batch * max_blocks > 0x7fffffffLL)
+    return FA_ERR_TOO_LARGE;
+
+  FwdArgs a = {};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k_cache);
+  a.v = static_cast<const uint16_t*>(v_cache);
+  a.o = static_cast<uint16_t*>(O);
+  a.l = L;
+  a.B = batch;
+  a.H = H;
+  a.Hkv = n_kv_heads;
+  a.ql = qlen;
+  a.kl = (int)cap;
+  a.group = H / n_kv_heads;
+  a.n_qtiles = (int)n_qtiles;
+  a.c = fmaxf(fabsf(scale) * kLog2e, FLT_MIN);
+  a.q_sign = signbit(scale) ? 0x80008000u : 0u;
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.max_blocks = max_blocks;
+  a.block_size = block_size;
+  a.n_blocks = n_blocks;
+  if (n_split > 0 && cap > 0) {
+    const int64_t per = (cap + n_split - 1) / n_split;
+    const int64_t kchunk = (per + 63) / 64 * 64;
+    const int64_t n_eff = (cap + kchunk - 1) / kchunk;
+    if (!workspace) return FA_ERR_NULL_POINTER;
+    if (!aligned(workspace, 16)) return FA_ERR_ALIGNMENT;
+    if ((int64_t)workspace_bytes < split_bytes(rows, head_dim, n_eff)) return FA_ERR_SPLIT;
+    if (grid * n_eff > 0x7fffffffLL || (rows + 3) / 4 > 0x7fffffffLL) return FA_ERR_TOO_LARGE;
+    a.n_split = (int)n_eff;
+    a.kchunk = (int)kchunk;
+    a.ws_o = static_cast<float*>(workspace);
+    a.ws_l = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                      split_o_bytes(rows, head_dim, n_eff));
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t err = head_dim == 64    ? dispatch_paged<64>(a, cz != 0, s)
+                         : head_dim == 128 ? dispatch_paged<128>(a, cz != 0, s)
+                                           : dispatch_paged<256>(a, cz != 0, s);
+  return err == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
 extern "C" int fa_train_fwd_ex(const void* q, const void* k, const void* v, const void* mask,
                                int mask_dtype, long long mask_stride_b, long long mask_stride_h,
                                int batch, int n_heads, int n_kv_heads, int ql, int kl,
@@ -926,6 +1060,7 @@ extern "C" const char* fa_status_string(int status) {
     case FA_ERR_WINDOW: return "sliding window must be >= 0 and comes with causal masking";
     case FA_ERR_MASK: return "mask dtype must be FA_MASK_F32 or FA_MASK_BF16, strides >= 0";
     case FA_ERR_SPLIT: return "n_split must be in 1..65536 and the workspace large enough";
+    case FA_ERR_PAGED: return "block_size must be a positive multiple of 64 and the cache non-empty";
     default: return "unknown status";
   }
 }

@@ -42,8 +42,10 @@ enum fa_status {
                                   causal (fa_train_fwd_ex)                              */
     FA_ERR_MASK = 10,          /* fa_train_fwd_ex: unknown mask dtype or a negative
                                   mask stride                                           */
-    FA_ERR_SPLIT = 11          /* fa_train_fwd_split: n_split outside 1..65536, or the
+    FA_ERR_SPLIT = 11,         /* fa_train_fwd_split: n_split outside 1..65536, or the
                                   workspace smaller than the split needs                */
+    FA_ERR_PAGED = 12          /* fa_paged_fwd: block_size not a positive multiple of
+                                  64, or no cache blocks for a non-empty table          */
 };
 
 /* Element types of an additive mask (fa_train_fwd_ex). */
@@ -191,6 +193,45 @@ int fa_train_fwd_split(const void *q, const void *k, const void *v, int batch, i
 /* Workspace bytes fa_train_fwd_split needs for these sizes (0 if invalid). */
 unsigned long fa_train_fwd_split_workspace(int batch, int n_heads, int ql, int head_dim,
                                            int n_split);
+
+/*
+ * fa_paged_fwd - the forward against a block-paged KV cache, one key count per
+ * sequence (prefill against a cache, decoding).
+ *
+ * The cache layout and its test are those of an adjacent attention API on
+ * the pages ("nuvec-core 0.3.0", tests/fast.rs, the paged helper and
+ * paged_attention_equals_contiguous_attention): the result equals the
+ * attention of each sequence b over its first seq_lens[b] keys, laid out
+ * contiguously. With causal, query row i of sequence b sees keys
+ * j <= max(seq_lens[b] - ql, 0) + i (fa_train_fwd's rule per sequence).
+ *
+ *   q           bf16 [batch, n_heads, ql, head_dim] (device, read)
+ *   k_cache,
+ *   v_cache     bf16 [n_blocks, n_kv_heads, block_size, head_dim] (device, read)
+ *   block_table int32 [batch, max_blocks] (device, read): key position p of
+ *               sequence b is row p % block_size of cache block
+ *               block_table[b][p / block_size]; entries outside
+ *               0..n_blocks-1 are clamped into that range (never an access
+ *               outside the cache, but the keys read are then wrong)
+ *   seq_lens    int32 [batch] (device, read): keys of each sequence, clamped
+ *               to 0..max_blocks*block_size
+ *   block_size  a positive multiple of 64 (a key tile lies in one block)
+ *   n_split     0: one launch; >= 1: split-KV with workspace (as for
+ *               fa_train_fwd_split, chunks of max_blocks*block_size keys;
+ *               workspace size from fa_train_fwd_split_workspace)
+ *   O, L        as for fa_train_fwd (a sequence with no key: O = 0, L = -inf)
+ *   others      as for fa_train_fwd; no mask, no window.
+ *
+ * Every tile runs the compensated P.V product. Returns FA_ERR_PAGED for a bad
+ * block_size or an empty cache behind a non-empty table, FA_ERR_SPLIT as for
+ * fa_train_fwd_split, otherwise the statuses of fa_train_fwd. Never
+ * synchronises, allocates nothing.
+ */
+int fa_paged_fwd(const void *q, const void *k_cache, const void *v_cache, const int *block_table,
+                 const int *seq_lens, int batch, int n_heads, int n_kv_heads, int ql, int n_blocks,
+                 int block_size, int max_blocks, int head_dim, float scale, int causal,
+                 int n_split, void *workspace, unsigned long workspace_bytes, void *O, float *L,
+                 void *stream);
 
 /*
  * fa_train_bwd - enqueue the training backward pass of the same attention.

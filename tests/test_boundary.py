@@ -29,7 +29,7 @@ def _declared_functions():
 def test_header_declares_the_entry_points():
     names = _declared_functions()
     assert {"fa_train_fwd", "fa_train_fwd_swa", "fa_train_fwd_ex", "fa_train_fwd_split",
-            "fa_train_fwd_split_workspace", "fa_train_bwd", "fa_train_bwd_swa",
+            "fa_train_fwd_split_workspace", "fa_paged_fwd", "fa_train_bwd", "fa_train_bwd_swa",
             "fa_status_string"} <= names
 
 
@@ -44,7 +44,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings_cover_all_codes():
-    for code in range(0, 12):
+    for code in range(0, 13):
         s = fa.status_string(code)
         assert s and s != "unknown status"
     assert fa.status_string(12345) == "unknown status"
@@ -235,3 +235,33 @@ def test_suggest_n_split():
     assert fa.suggest_n_split(8, 32, 1, 128, n_kv_heads=8) == 8   # packed: 64
     assert fa.suggest_n_split(1, 32, 1, 128, n_kv_heads=8) == 64  # packed: 8
     assert fa.suggest_n_split(2, 16, 8192, 256) == 1
+
+
+PAGED_GOOD = dict(q=A, k_cache=A, v_cache=A, block_table=A, seq_lens=A, batch=2, n_heads=4,
+                  n_kv_heads=2, ql=1, n_blocks=8, block_size=64, max_blocks=4, head_dim=128,
+                  scale=0.1, causal=1, n_split=0, workspace=0, workspace_bytes=0, O=A, L=A,
+                  stream=0)
+
+
+def _call_paged(**over):
+    args = dict(PAGED_GOOD)
+    args.update(over)
+    return fa.fa_paged_fwd(**args)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(block_size=16), 12), (dict(block_size=96), 12), (dict(block_size=0), 12),
+    (dict(n_blocks=0), 12), (dict(block_table=0), 1), (dict(seq_lens=0), 1), (dict(k_cache=0), 1),
+    (dict(q=A + 2), 6), (dict(block_table=A + 2), 6), (dict(seq_lens=A + 1), 6),
+    (dict(head_dim=80), 4), (dict(n_heads=3), 3), (dict(scale=math.inf), 5),
+    (dict(max_blocks=-1), 2), (dict(n_blocks=-1), 2), (dict(n_split=-1), 11),
+    (dict(n_split=4), 1), (dict(n_split=4, workspace=A, workspace_bytes=16), 11),
+    (dict(max_blocks=1 << 25, block_size=128), 7),
+])
+def test_paged_invalid_arguments_are_rejected(over, code):
+    assert _call_paged(**over) == code
+
+
+@pytest.mark.parametrize("over", [dict(batch=0), dict(ql=0, q=0, O=0, L=0)])
+def test_paged_empty_problems_are_noops(over):
+    assert _call_paged(**over) == 0

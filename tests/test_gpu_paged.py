@@ -1,0 +1,121 @@
+"""GPU parity of the paged-KV forward (fa_paged_fwd) against the CPU oracle
+(marked gpu). The layout and the check follow the adjacent attention API on
+the pages (paged caches [n_blocks, Hkv, block_size, D] filled in a shuffled
+block order with a few unused blocks, a block table, a key count per
+sequence): the paged result must equal attention over each sequence's first
+seq_lens[b] keys, which the oracle computes from the contiguous keys. Bounds
+as for the plain forward (by each sequence's key count); a sequence with no
+key gives O = +0 and L = -inf exactly.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import fagen
+import oracle
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+
+def _paged(keys, values, bs, seed):
+    """keys, values: bf16 bits [B, Hkv, N, D] -> (k_cache, v_cache, table) with
+    the blocks of every sequence in a seeded shuffled order plus 3 unused ones."""
+    B, Hkv, N, D = keys.shape
+    per = -(-N // bs)
+    blocks = B * per + 3
+    order = np.random.default_rng(seed).permutation(blocks)
+    kc = np.zeros((blocks, Hkv, bs, D), np.uint16)
+    vc = np.zeros((blocks, Hkv, bs, D), np.uint16)
+    for b in range(B):
+        for j in range(per):
+            blk, n = order[b * per + j], min(bs, N - j * bs)
+            kc[blk, :, :n] = keys[b, :, j * bs:j * bs + n]
+            vc[blk, :, :n] = values[b, :, j * bs:j * bs + n]
+    table = order[:B * per].reshape(B, per).astype(np.int32)
+    return kc, vc, table
+
+
+def _run(case, n_split, seed):
+    import torch
+    import flash_attention_forward_fa_amd as fa
+    B, H, Hkv, ql, D, bs, lens, causal = case
+    N = max(max(lens), 1)
+    s = fagen.SEED_BASE + seed
+    q = fagen.normal_bf16(s, 0, (B, H, ql, D))
+    keys = fagen.normal_bf16(s, 1, (B, Hkv, N, D))
+    values = fagen.normal_bf16(s, 2, (B, Hkv, N, D))
+    kc, vc, table = _paged(keys, values, bs, seed)
+    dev = "cuda:0"
+    O, L = fa.paged_fwd(gu.to_dev(q, dev), gu.to_dev(kc, dev), gu.to_dev(vc, dev),
+                        torch.from_numpy(table).to(dev),
+                        torch.tensor(lens, dtype=torch.int32, device=dev), causal=causal,
+                        n_split=n_split)
+    torch.cuda.synchronize()
+    bits = O.view(torch.int16).cpu().numpy().view(np.uint16)
+    o, l = gu.widen(bits), L.cpu().numpy()
+    scale = 1.0 / math.sqrt(D)
+    for b, n in enumerate(lens):
+        _, ob, lr = oracle.fwd(q[b:b + 1], keys[b:b + 1, :, :n].copy(),
+                               values[b:b + 1, :, :n].copy(), None, 1, H, Hkv, ql, n, D, scale,
+                               causal)
+        tol_o, tol_l = gu.tolerances(n)
+        eo, el, _ = gu.compare(o[b:b + 1], l[b:b + 1], bits[b:b + 1], ob, lr, tol_o, tol_l,
+                               f"paged {case} seq {b}")
+        print(f"paged {case} n_split={n_split} seq {b} (len {n}): dO={eo:.3e} dL={el:.3e}")
+    return o, l
+
+
+CASES = [
+    # (B, H, Hkv, ql, D, block_size, seq_lens, causal)
+    (1, 4, 4, 1, 128, 64, [37], True),
+    (3, 8, 2, 1, 128, 64, [1, 64, 300], True),
+    (2, 4, 1, 4, 64, 64, [4, 77], True),
+    (2, 2, 2, 1, 256, 128, [9, 513], True),
+    (2, 8, 2, 1, 128, 64, [1500, 3000], True),
+    (1, 8, 2, 4, 128, 64, [2100], True),
+    (1, 4, 2, 1, 256, 64, [1100], True),
+    (2, 4, 2, 300, 128, 128, [1000, 450], True),   # prefill against a cache
+    (2, 4, 4, 70, 64, 64, [300, 200], False),
+    (2, 4, 2, 1, 64, 64, [0, 200], True),          # a sequence with no key
+]
+
+
+@pytest.mark.parametrize("n_split", [0, 8])
+@pytest.mark.parametrize("case", CASES, ids=[str(i) for i in range(len(CASES))])
+def test_paged_matches_contiguous_oracle(case, n_split):
+    print(f"case paged {case} n_split={n_split}", flush=True)
+    _run(case, n_split, seed=11000 + CASES.index(case))
+
+
+def test_paged_table_entries_outside_the_cache_are_clamped():
+    """A table entry outside 0..n_blocks-1 reads a clamped block: the call
+    completes with finite output (the keys it read are not that sequence's)."""
+    import torch
+    import flash_attention_forward_fa_amd as fa
+    print("case paged clamp", flush=True)
+    B, H, Hkv, ql, D, bs = 2, 4, 2, 1, 64, 64
+    s = fagen.SEED_BASE + 11900
+    q = gu.to_dev(fagen.normal_bf16(s, 0, (B, H, ql, D)), "cuda:0")
+    kc = gu.to_dev(fagen.normal_bf16(s, 1, (5, Hkv, bs, D)), "cuda:0")
+    vc = gu.to_dev(fagen.normal_bf16(s, 2, (5, Hkv, bs, D)), "cuda:0")
+    table = torch.tensor([[0, 10 ** 9], [-5, 2]], dtype=torch.int32, device="cuda:0")
+    lens = torch.tensor([128, 100], dtype=torch.int32, device="cuda:0")
+    O, L = fa.paged_fwd(q, kc, vc, table, lens, causal=True)
+    torch.cuda.synchronize()
+    assert torch.isfinite(O.float()).all() and torch.isfinite(L).all()
+
+
+def test_paged_errors_raise_from_binding():
+    import torch
+    import flash_attention_forward_fa_amd as fa
+    q = torch.zeros(1, 2, 1, 64, device="cuda:0", dtype=torch.bfloat16)
+    c = torch.zeros(4, 2, 32, 64, device="cuda:0", dtype=torch.bfloat16)
+    t = torch.zeros(1, 2, dtype=torch.int32, device="cuda:0")
+    n = torch.tensor([40], dtype=torch.int32, device="cuda:0")
+    with pytest.raises(fa.FAError) as e:
+        fa.paged_fwd(q, c, c, t, n)
+    assert e.value.status == 12
+    with pytest.raises(ValueError):
+        fa.paged_fwd(q, c, c, t.float(), n)
