@@ -20,7 +20,7 @@ FA_STATUS = {
     8: "FA_ERR_LAUNCH", 9: "FA_ERR_WINDOW", 10: "FA_ERR_MASK", 11: "FA_ERR_SPLIT",
     12: "FA_ERR_PAGED",
 }
-FA_MASK_F32, FA_MASK_BF16 = 0, 1
+FA_MASK_F32, FA_MASK_BF16, FA_MASK_BOOL = 0, 1, 2
 
 _lib = None
 
@@ -105,16 +105,17 @@ def train_fwd_ex(q, k, v, mask=None, scale=None, causal=False, window=None, out=
     """O, L = train_fwd_ex(q, k, v, mask=None, scale=None, causal=False, window=None)
 
     train_fwd with every option of fa_train_fwd_ex: mask may be float32 or
-    bfloat16, of shape [B or 1, H or 1, ql, kl] (a size-1 batch or head dim is
-    broadcast; any batch/head strides, rows contiguous); window (>= 0, with
-    causal=True) selects the sliding window of train_fwd_swa.
+    bfloat16 (additive) or bool (True = visible), of shape [B or 1, H or 1, ql,
+    kl] (a size-1 batch or head dim is broadcast; any batch/head strides, rows
+    contiguous); window (>= 0, with causal=True) selects the sliding window of
+    train_fwd_swa.
     """
     import torch
 
     if mask is None:
         return _train_fwd(q, k, v, None, scale, causal, window, out, lse, stream, ex=True)
-    if mask.dtype not in (torch.float32, torch.bfloat16):
-        raise ValueError("mask must be float32 or bfloat16")
+    if mask.dtype not in (torch.float32, torch.bfloat16, torch.bool):
+        raise ValueError("mask must be float32, bfloat16 or bool")
     B, H, ql, _ = q.shape
     kl = k.shape[2]
     if (mask.dim() != 4 or mask.shape[0] not in (1, B) or mask.shape[1] not in (1, H)
@@ -125,8 +126,8 @@ def train_fwd_ex(q, k, v, mask=None, scale=None, causal=False, window=None, out=
     sb = mask.stride(0) if mask.shape[0] > 1 else 0
     sh = mask.stride(1) if mask.shape[1] > 1 else 0
     return _train_fwd(q, k, v, mask, scale, causal, window, out, lse, stream, ex=True,
-                      mask_layout=(FA_MASK_BF16 if mask.dtype == torch.bfloat16 else FA_MASK_F32,
-                                   sb, sh))
+                      mask_layout=({torch.bfloat16: FA_MASK_BF16, torch.bool: FA_MASK_BOOL}
+                                   .get(mask.dtype, FA_MASK_F32), sb, sh))
 
 
 def fa_train_fwd_split(q, k, v, batch, n_heads, n_kv_heads, ql, kl, head_dim, scale, causal,

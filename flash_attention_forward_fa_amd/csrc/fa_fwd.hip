@@ -88,14 +88,18 @@ constexpr float kLazy = 8.0f;
 // cache through a block table, with a key count per sequence; they compute
 // every tile compensated, the second one as split-KV partials.
 constexpr int kMixed = 0, kAll = 1, kSplit = 2, kPaged = 3, kPagedSplit = 4;
-// Additive mask element types (kNoMask: no mask).
-constexpr int kNoMask = 0, kMaskF32 = 1, kMaskBF16 = 2;
+// Mask element types (kNoMask: no mask): additive f32 or bf16, or boolean
+// (one byte per key, nonzero = visible).
+constexpr int kNoMask = 0, kMaskF32 = 1, kMaskBF16 = 2, kMaskBool = 3;
 
-// Mask element idx as f32 (a bf16 mask widens exactly).
+// Mask element idx as an additive f32 value (a bf16 mask widens exactly; a
+// boolean mask is 0 for a visible key and -inf for a hidden one).
 template <int MASK>
 __device__ __forceinline__ float mask_at(const void* m, int64_t idx) {
   if constexpr (MASK == kMaskBF16)
     return __uint_as_float((uint32_t)static_cast<const uint16_t*>(m)[idx] << 16);
+  else if constexpr (MASK == kMaskBool)
+    return static_cast<const uint8_t*>(m)[idx] ? 0.0f : -INFINITY;
   else
     return static_cast<const float*>(m)[idx];
 }
@@ -105,7 +109,7 @@ struct FwdArgs {
   const uint16_t* q;
   const uint16_t* k;
   const uint16_t* v;
-  const void* mask;          // f32 or bf16 (the kernel's MASK), or null
+  const void* mask;          // f32, bf16 or bool bytes (the kernel's MASK), or null
   int64_t mask_sb, mask_sh;  // mask strides of batch and head, in elements (0: broadcast)
   uint16_t* o;
   float* l;
@@ -742,8 +746,9 @@ hipError_t dispatch_c(FwdArgs a, int mask, int n_short, hipStream_t stream) {
   a.qt_count = n_qt;
   if (mask != kNoMask) {
     a.n_precise = n_qt;
-    return mask == kMaskBF16 ? launch<D, CAUSAL, WINDOW, kMaskBF16, kAll>(a, bh * n_qt, stream)
-                             : launch<D, CAUSAL, WINDOW, kMaskF32, kAll>(a, bh * n_qt, stream);
+    return mask == kMaskBF16   ? launch<D, CAUSAL, WINDOW, kMaskBF16, kAll>(a, bh * n_qt, stream)
+           : mask == kMaskBool ? launch<D, CAUSAL, WINDOW, kMaskBool, kAll>(a, bh * n_qt, stream)
+                               : launch<D, CAUSAL, WINDOW, kMaskF32, kAll>(a, bh * n_qt, stream);
   }
   a.n_precise = n_short;
   return launch<D, CAUSAL, WINDOW, kNoMask, kMixed>(a, bh * n_qt, stream);
@@ -822,8 +827,9 @@ int train_fwd(const void* q, const void* k, const void* v, const void* mask, int
   if (head_dim != 64 && head_dim != 128 && head_dim != 256) return FA_ERR_HEAD_DIM;
   if (!isfinite(scale)) return FA_ERR_SCALE;
   if (window >= 0 && !causal) return FA_ERR_WINDOW;
-  if (mask && ((mask_dtype != FA_MASK_F32 && mask_dtype != FA_MASK_BF16) || mask_sb < 0 ||
-               mask_sh < 0))
+  if (mask && ((mask_dtype != FA_MASK_F32 && mask_dtype != FA_MASK_BF16 &&
+                mask_dtype != FA_MASK_BOOL) ||
+               mask_sb < 0 || mask_sh < 0))
     return FA_ERR_MASK;
   const int64_t rows = (int64_t)batch * n_heads * ql;
   if (rows == 0) return FA_OK;
@@ -831,7 +837,7 @@ int train_fwd(const void* q, const void* k, const void* v, const void* mask, int
   if (!q || !O || !L || (kv_used && (!k || !v))) return FA_ERR_NULL_POINTER;
   if (!aligned(q, 16) || !aligned(O, 16) || !aligned(L, 4) ||
       (kv_used && (!aligned(k, 16) || !aligned(v, 16))) ||
-      (mask && !aligned(mask, mask_dtype == FA_MASK_BF16 ? 2 : 4)))
+      (mask && !aligned(mask, mask_dtype == FA_MASK_BF16 ? 2 : mask_dtype == FA_MASK_BOOL ? 1 : 4)))
     return FA_ERR_ALIGNMENT;
   // One query row per head (decoding), no mask, no window: the layout
   // [B, H, 1, D] of Q, O (and [B, H, 1] of L) is [B, Hkv, H/Hkv, D], so a kv
@@ -860,7 +866,10 @@ int train_fwd(const void* q, const void* k, const void* v, const void* mask, int
   a.mask = mask;
   a.mask_sb = mask_sb;
   a.mask_sh = mask_sh;
-  const int mask_kind = !mask ? kNoMask : mask_dtype == FA_MASK_BF16 ? kMaskBF16 : kMaskF32;
+  const int mask_kind = !mask                          ? kNoMask
+                        : mask_dtype == FA_MASK_BF16 ? kMaskBF16
+                        : mask_dtype == FA_MASK_BOOL ? kMaskBool
+                                                     : kMaskF32;
   a.o = static_cast<uint16_t*>(O);
   a.l = L;
   a.B = batch;
@@ -1058,7 +1067,7 @@ extern "C" const char* fa_status_string(int status) {
     case FA_ERR_TOO_LARGE: return "problem too large for the kernel's grid or index range";
     case FA_ERR_LAUNCH: return "HIP kernel launch failed";
     case FA_ERR_WINDOW: return "sliding window must be >= 0 and comes with causal masking";
-    case FA_ERR_MASK: return "mask dtype must be FA_MASK_F32 or FA_MASK_BF16, strides >= 0";
+    case FA_ERR_MASK: return "mask dtype must be FA_MASK_F32, FA_MASK_BF16 or FA_MASK_BOOL, strides >= 0";
     case FA_ERR_SPLIT: return "n_split must be in 1..65536 and the workspace large enough";
     case FA_ERR_PAGED: return "block_size must be a positive multiple of 64 and the cache non-empty";
     default: return "unknown status";

@@ -50,8 +50,9 @@ enum fa_status {
 
 /* Element types of an additive mask (fa_train_fwd_ex). */
 enum fa_mask_dtype {
-    FA_MASK_F32 = 0,
-    FA_MASK_BF16 = 1
+    FA_MASK_F32 = 0,   /* additive, f32                                  */
+    FA_MASK_BF16 = 1,  /* additive, bf16                                 */
+    FA_MASK_BOOL = 2   /* one byte per key: nonzero visible, zero hidden */
 };
 
 /*
@@ -125,10 +126,13 @@ int fa_train_fwd_swa(const void *q, const void *k, const void *v, const float *m
  *
  *   mask[b,h,i,j] = mask[b * mask_stride_b + h * mask_stride_h + i * kl + j]
  *
- *   mask          NULL, or additive mask elements of type mask_dtype (device,
- *                 read); each (b, h) slice is ql rows of kl contiguous
- *                 elements. bf16 values are widened exactly to f32.
- *   mask_dtype    FA_MASK_F32 or FA_MASK_BF16 (ignored when mask is NULL).
+ *   mask          NULL, or mask elements of type mask_dtype (device, read);
+ *                 each (b, h) slice is ql rows of kl contiguous elements.
+ *                 bf16 values are widened exactly to f32; a boolean mask (the
+ *                 same API's [ql, kl] boolean mask) acts as the additive mask
+ *                 0 where the byte is nonzero and -inf where it is zero.
+ *   mask_dtype    FA_MASK_F32, FA_MASK_BF16 or FA_MASK_BOOL (ignored when mask
+ *                 is NULL).
  *   mask_stride_b, mask_stride_h
  *                 element strides between batches and between heads, >= 0;
  *                 0 broadcasts (e.g. 0 and ql*kl for a [1, H, ql, kl] mask).
@@ -137,7 +141,7 @@ int fa_train_fwd_swa(const void *q, const void *k, const void *v, const float *m
  *                 (requires causal != 0).
  *   all others    as for fa_train_fwd.
  *
- * Alignment: an f32 mask 4 bytes, a bf16 mask 2 bytes. Returns the statuses
+ * Alignment: an f32 mask 4 bytes, a bf16 mask 2 bytes, a boolean mask 1. Returns the statuses
  * of fa_train_fwd, FA_ERR_MASK for an unknown dtype or a negative stride,
  * FA_ERR_WINDOW for a window without causal masking. fa_train_fwd(...) is
  * fa_train_fwd_ex with an f32 mask, strides H*ql*kl and ql*kl, window -1.

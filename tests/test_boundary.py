@@ -119,7 +119,7 @@ def _call_ex(**over):
 
 
 @pytest.mark.parametrize("over,code", [
-    (dict(mask_dtype=2), 10), (dict(mask_dtype=-1), 10), (dict(mask_stride_b=-1), 10),
+    (dict(mask_dtype=3), 10), (dict(mask_dtype=-1), 10), (dict(mask_stride_b=-1), 10),
     (dict(mask_stride_h=-64), 10), (dict(causal=0, window=3), 9), (dict(mask=A + 2), 6),
     (dict(mask=A + 1, mask_dtype=1), 6), (dict(q=0), 1), (dict(head_dim=32), 4),
     (dict(n_heads=3, n_kv_heads=2), 3), (dict(scale=math.inf), 5), (dict(ql=-2), 2),

@@ -179,3 +179,43 @@ def test_ex_errors_raise_from_binding():
         fa.train_fwd_ex(q, q, q, mask=torch.zeros(1, 3, 4, 4, device="cuda:0"))
     with pytest.raises(ValueError):
         fa.train_fwd_ex(q, q, q, mask=torch.zeros(1, 2, 4, 4, device="cuda:0", dtype=torch.half))
+
+
+BOOL_CASES = [
+    # (B, H, Hkv, ql, kl, D, causal, mask batch, mask heads)
+    (2, 4, 4, 33, 45, 64, False, 1, 1),     # the adjacent API's [ql, kl] boolean mask shape
+    (2, 4, 2, 100, 100, 128, True, 1, 1),
+    (1, 2, 1, 64, 96, 256, True, 1, 2),
+    (2, 2, 2, 70, 300, 64, False, 2, 2),    # dense boolean mask
+]
+
+
+@pytest.mark.parametrize("B,H,Hkv,ql,kl,D,causal,mb,mh", BOOL_CASES)
+def test_boolean_mask_matches_oracle_and_the_additive_mask(B, H, Hkv, ql, kl, D, causal, mb, mh):
+    """A boolean mask (True = visible) against the oracle with the equivalent
+    0/-inf f32 mask, and bit for bit against the kernel given that f32 mask.
+    Rows whose mask is all False are empty (O = +0, L = -inf)."""
+    import torch
+    import flash_attention_forward_fa_amd as fa
+    w = fagen.Workload("mask_bool", B, H, Hkv, ql, kl, D, causal,
+                       seed_offset=6500 + ql + kl + D + mb + mh)
+    print(f"case bool mask {(B, H, Hkv, ql, kl, D, causal, mb, mh)}", flush=True)
+    inp = fagen.generate(w)
+    keep = np.isfinite(_finite_mask(w.seed, mb, mh, ql, kl, p=0.3))  # one all-False row per slice
+    add = np.where(keep, 0.0, -np.inf).astype(np.float32)
+    q, k, v = (gu.to_dev(inp[n], "cuda:0") for n in ("q", "k", "v"))
+    Ob, Lb = fa.train_fwd_ex(q, k, v, mask=torch.from_numpy(keep).cuda(), scale=w.scale,
+                             causal=causal)
+    Of, Lf = fa.train_fwd_ex(q, k, v, mask=torch.from_numpy(add).cuda(), scale=w.scale,
+                             causal=causal)
+    torch.cuda.synchronize()
+    assert torch.equal(Ob.view(torch.int16), Of.view(torch.int16)) and torch.equal(Lb, Lf)
+    bits = Ob.view(torch.int16).cpu().numpy().view(np.uint16)
+    dense = np.broadcast_to(add, (B, H, ql, kl)).copy()
+    _, ob, lr = oracle.fwd(inp["q"], inp["k"], inp["v"], dense, B, H, Hkv, ql, kl, D, w.scale,
+                           causal)
+    tol_o, tol_l = gu.tolerances(kl)
+    eo, el, _ = gu.compare(gu.widen(bits), Lb.cpu().numpy(), bits, ob, lr, tol_o, tol_l,
+                           f"bool mask {B,H,ql,kl,D}")
+    assert np.isneginf(lr).any()
+    print(f"bool mask {(B, H, ql, kl, D, causal, mb, mh)}: dO={eo:.3e} dL={el:.3e}")
