@@ -54,14 +54,18 @@ constexpr int kBwdQ = 0, kBwdKV = 1;
 // rows per tile, WPE waves per SIMD (register budget). The D=256 dK/dV pass
 // streams three tiles (Q, dO, O) through 96 KiB of LDS in 32-row tiles.
 template <int D, int PASS> struct BwdCfg;
-template <> struct BwdCfg<64, kBwdQ> { static constexpr int W = 8, FB = 2, BN = 64, WPE = 2; };
-template <> struct BwdCfg<64, kBwdKV> { static constexpr int W = 8, FB = 2, BN = 64, WPE = 2; };
-template <> struct BwdCfg<128, kBwdQ> { static constexpr int W = 8, FB = 1, BN = 64, WPE = 2; };
-template <> struct BwdCfg<128, kBwdKV> { static constexpr int W = 8, FB = 1, BN = 64, WPE = 2; };
-template <> struct BwdCfg<256, kBwdQ> { static constexpr int W = 8, FB = 1, BN = 64, WPE = 2; };
-template <> struct BwdCfg<256, kBwdKV> { static constexpr int W = 4, FB = 1, BN = 32, WPE = 1; };
+// DS waves share each fixed block, each accumulating D/DS of the output dims
+// (the D=256 dK/dV pass: two waves per 16 key rows, each with half of dK and
+// dV, so that the accumulators allow two waves per SIMD; both compute the
+// block's full S and dP).
+template <> struct BwdCfg<64, kBwdQ> { static constexpr int W = 8, FB = 2, BN = 64, WPE = 2, DS = 1; };
+template <> struct BwdCfg<64, kBwdKV> { static constexpr int W = 8, FB = 2, BN = 64, WPE = 2, DS = 1; };
+template <> struct BwdCfg<128, kBwdQ> { static constexpr int W = 8, FB = 1, BN = 64, WPE = 2, DS = 1; };
+template <> struct BwdCfg<128, kBwdKV> { static constexpr int W = 8, FB = 1, BN = 64, WPE = 2, DS = 1; };
+template <> struct BwdCfg<256, kBwdQ> { static constexpr int W = 8, FB = 1, BN = 64, WPE = 2, DS = 1; };
+template <> struct BwdCfg<256, kBwdKV> { static constexpr int W = 8, FB = 1, BN = 32, WPE = 2, DS = 2; };
 template <int D, int PASS> constexpr int fixed_rows() {
-  return BwdCfg<D, PASS>::W * 16 * BwdCfg<D, PASS>::FB;
+  return BwdCfg<D, PASS>::W / BwdCfg<D, PASS>::DS * 16 * BwdCfg<D, PASS>::FB;
 }
 
 struct BwdArgs {
@@ -99,6 +103,9 @@ __attribute__((amdgpu_waves_per_eu(BwdCfg<D, PASS>::WPE))) void fa_bwd_kernel(Bw
   constexpr int NKB = BN / 16;  // 16-row blocks of a streamed tile
   constexpr int NKC = BN / 32;  // 32-row chunks (contraction steps of the second products)
   constexpr int NDB = D / 16;   // 16-dim blocks
+  constexpr int DS = C::DS;
+  constexpr int NDA = NDB / DS;  // 16-dim blocks of this wave's accumulators
+  static_assert(NDA * DS == NDB && C::W % DS == 0, "dims split evenly");
   constexpr int NDS = D / 32;   // 32-dim steps
   constexpr int TILE = BN * D;
   constexpr int NT = 64 * C::W;
@@ -130,7 +137,8 @@ __attribute__((amdgpu_waves_per_eu(BwdCfg<D, PASS>::WPE))) void fa_bwd_kernel(Bw
   const int nfixed = KV ? kl : ql;
   const int nstream = KV ? ql : kl;
   const int f0 = ftile * FR;
-  const int fw0 = f0 + wave * 16 * FB;  // this wave's first fixed row
+  const int dpart = wave / (C::W / DS);  // this wave's part of the output dims
+  const int fw0 = f0 + (wave % (C::W / DS)) * 16 * FB;  // this wave's first fixed row
   const bool wave_active = fw0 < nfixed;
 
   const int64_t kv_base = (int64_t)(b * a.Hkv + g) * kl * D;
@@ -172,9 +180,9 @@ __attribute__((amdgpu_waves_per_eu(BwdCfg<D, PASS>::WPE))) void fa_bwd_kernel(Bw
   }
 
   // ---- accumulators: dQ^T, or dK^T and dV^T (dims x fixed rows) ----
-  f32x4 acc1[NDB][FB], acc2[NDB][FB];
+  f32x4 acc1[NDA][FB], acc2[NDA][FB];
 #pragma unroll
-  for (int d = 0; d < NDB; ++d)
+  for (int d = 0; d < NDA; ++d)
 #pragma unroll
     for (int fb = 0; fb < FB; ++fb) {
       acc1[d][fb] = f32x4{};
@@ -385,19 +393,21 @@ __attribute__((amdgpu_waves_per_eu(BwdCfg<D, PASS>::WPE))) void fa_bwd_kernel(Bw
     // second products: dQ^T += Y1^T dS^T, or dK^T += Y1^T dS and dV^T += Y2^T P
     if constexpr (D == 256) set_prio<2>();
 #pragma unroll
-    for (int d = 0; d < NDB; ++d)
+    for (int da = 0; da < NDA; ++da)
 #pragma unroll
       for (int j = 0; j < NKC; ++j) {
+        const int d = dpart * NDA + da;
         const bf16x8 t1 = tread(b1, true, d, j);
 #pragma unroll
         for (int fb = 0; fb < FB; ++fb)
-          acc1[d][fb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(t1, dsb[j][fb], acc1[d][fb], 0, 0, 0);
+          acc1[da][fb] =
+              __builtin_amdgcn_mfma_f32_16x16x32_bf16(t1, dsb[j][fb], acc1[da][fb], 0, 0, 0);
         if constexpr (KV) {
           const bf16x8 t2 = tread(b2, false, d, j);
 #pragma unroll
           for (int fb = 0; fb < FB; ++fb)
-            acc2[d][fb] =
-                __builtin_amdgcn_mfma_f32_16x16x32_bf16(t2, pb[j][fb], acc2[d][fb], 0, 0, 0);
+            acc2[da][fb] =
+                __builtin_amdgcn_mfma_f32_16x16x32_bf16(t2, pb[j][fb], acc2[da][fb], 0, 0, 0);
         }
       }
     if constexpr (D == 256) set_prio<0>();
@@ -410,19 +420,21 @@ __attribute__((amdgpu_waves_per_eu(BwdCfg<D, PASS>::WPE))) void fa_bwd_kernel(Bw
     if (!(wave_active && frow < nfixed)) continue;
     uint16_t* d1 = KV ? a.dk + kv_base + (int64_t)frow * D : a.dq + ((int64_t)fhead * ql + frow) * D;
 #pragma unroll
-    for (int d = 0; d < NDB; ++d) {
+    for (int da = 0; da < NDA; ++da) {
+      const int d = dpart * NDA + da;
       bf16x4 ov;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) ov[i] = (__bf16)(acc1[d][fb][i] * a.scale);
+      for (int i = 0; i < 4; ++i) ov[i] = (__bf16)(acc1[da][fb][i] * a.scale);
       *reinterpret_cast<bf16x4*>(d1 + 16 * d + 4 * grp) = ov;
     }
     if constexpr (KV) {
       uint16_t* d2 = a.dv + kv_base + (int64_t)frow * D;
 #pragma unroll
-      for (int d = 0; d < NDB; ++d) {
+      for (int da = 0; da < NDA; ++da) {
+        const int d = dpart * NDA + da;
         bf16x4 ov;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) ov[i] = (__bf16)acc2[d][fb][i];
+        for (int i = 0; i < 4; ++i) ov[i] = (__bf16)acc2[da][fb][i];
         *reinterpret_cast<bf16x4*>(d2 + 16 * d + 4 * grp) = ov;
       }
     }
