@@ -65,6 +65,10 @@ def lib():
         l.fa_train_bwd_swa.argtypes = [vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci,
                                        ctypes.c_float, ci, vp, vp, vp, vp]
         l.fa_train_bwd_swa.restype = ci
+        l.fa_train_bwd_ex.argtypes = [vp, vp, vp, vp, ci, ctypes.c_longlong, ctypes.c_longlong,
+                                      vp, vp, vp, ci, ci, ci, ci, ci, ci, ctypes.c_float, ci, ci,
+                                      vp, vp, vp, vp]
+        l.fa_train_bwd_ex.restype = ci
         l.fa_status_string.argtypes = [ci]
         l.fa_status_string.restype = ctypes.c_char_p
         _lib = l
@@ -370,6 +374,53 @@ def train_bwd_swa(q, k, v, O, L, dO, window, mask=None, scale=None, stream=None)
     return _train_bwd(q, k, v, O, L, dO, mask, scale, True, int(window), stream)
 
 
+def fa_train_bwd_ex(q, k, v, mask, mask_dtype, mask_stride_b, mask_stride_h, O, L, dO, batch,
+                    n_heads, n_kv_heads, ql, kl, head_dim, scale, causal, window, dQ, dK, dV,
+                    stream):
+    """The C entry point with raw integer pointers (0 for NULL); returns the status."""
+    return lib().fa_train_bwd_ex(q or None, k or None, v or None, mask or None, int(mask_dtype),
+                                 int(mask_stride_b), int(mask_stride_h), O or None, L or None,
+                                 dO or None, batch, n_heads, n_kv_heads, ql, kl, head_dim,
+                                 float(scale), int(bool(causal)), int(window), dQ or None,
+                                 dK or None, dV or None, stream or None)
+
+
+def train_bwd_ex(q, k, v, O, L, dO, mask=None, scale=None, causal=False, window=None,
+                 stream=None):
+    """dQ, dK, dV = train_bwd_ex(q, k, v, O, L, dO, mask=None, scale=None, causal=False,
+                                 window=None)
+
+    The backward of train_fwd_ex with the same mask (float32, bfloat16 or bool,
+    [B or 1, H or 1, ql, kl]), causal and window arguments.
+    """
+    layout = None
+    if mask is not None:
+        layout = _mask_layout(mask, q, k)
+    return _train_bwd(q, k, v, O, L, dO, mask, scale, causal, window, stream, ex=True,
+                      mask_layout=layout)
+
+
+def _mask_layout(mask, q, k):
+    """(dtype code, batch stride, head stride) of a mask [B or 1, H or 1, ql, kl]."""
+    import torch
+    if not isinstance(mask, torch.Tensor) or mask.dtype not in (torch.float32, torch.bfloat16,
+                                                                 torch.bool):
+        raise ValueError("mask must be float32, bfloat16 or bool")
+    B, H, ql, _ = q.shape
+    kl = k.shape[2]
+    if (mask.dim() != 4 or mask.shape[0] not in (1, B) or mask.shape[1] not in (1, H)
+            or tuple(mask.shape[2:]) != (ql, kl)):
+        raise ValueError(f"mask must have shape [B or 1, H or 1, {ql}, {kl}]")
+    if ql * kl > 0 and ((kl > 1 and mask.stride(3) != 1) or (ql > 1 and mask.stride(2) != kl)):
+        raise ValueError("mask rows must be contiguous (strides [.., .., kl, 1])")
+    if mask.device != q.device:
+        raise ValueError("mask must be on q's device")
+    sb = mask.stride(0) if mask.shape[0] > 1 else 0
+    sh = mask.stride(1) if mask.shape[1] > 1 else 0
+    code = {torch.bfloat16: FA_MASK_BF16, torch.bool: FA_MASK_BOOL}.get(mask.dtype, FA_MASK_F32)
+    return code, sb, sh
+
+
 def train_bwd(q, k, v, O, L, dO, mask=None, scale=None, causal=False, stream=None):
     """dQ, dK, dV = train_bwd(q, k, v, O, L, dO, mask=None, scale=None, causal=False)
 
@@ -380,7 +431,8 @@ def train_bwd(q, k, v, O, L, dO, mask=None, scale=None, causal=False, stream=Non
     return _train_bwd(q, k, v, O, L, dO, mask, scale, causal, None, stream)
 
 
-def _train_bwd(q, k, v, O, L, dO, mask, scale, causal, window, stream):
+def _train_bwd(q, k, v, O, L, dO, mask, scale, causal, window, stream, ex=False,
+               mask_layout=None):
     import torch
 
     for name, t in (("q", q), ("k", k), ("v", v), ("O", O), ("dO", dO)):
@@ -397,7 +449,7 @@ def _train_bwd(q, k, v, O, L, dO, mask, scale, causal, window, stream):
     if (L.dtype != torch.float32 or tuple(L.shape) != (B, H, ql) or not L.is_contiguous()
             or L.device != q.device):
         raise ValueError("L must be a contiguous f32 tensor [B, H, ql] on q's device")
-    if mask is not None:
+    if mask is not None and not ex:
         if mask.dtype != torch.float32 or not mask.is_contiguous() or mask.device != q.device:
             raise ValueError("mask must be a contiguous float32 tensor on q's device")
         if tuple(mask.shape) != (B, H, ql, kl):
@@ -408,7 +460,13 @@ def _train_bwd(q, k, v, O, L, dO, mask, scale, causal, window, stream):
     s = stream if stream is not None else torch.cuda.current_stream(q.device)
     mptr = mask.data_ptr() if mask is not None else 0
     with torch.cuda.device(q.device):
-        if window is None:
+        if ex:
+            mdt, sb, sh = mask_layout or (FA_MASK_F32, 0, 0)
+            status = fa_train_bwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), mptr, mdt, sb, sh,
+                                     O.data_ptr(), L.data_ptr(), dO.data_ptr(), B, H, Hkv, ql, kl,
+                                     D, scale, causal, -1 if window is None else window,
+                                     dQ.data_ptr(), dK.data_ptr(), dV.data_ptr(), s.cuda_stream)
+        elif window is None:
             status = fa_train_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), mptr, O.data_ptr(),
                                   L.data_ptr(), dO.data_ptr(), B, H, Hkv, ql, kl, D, scale,
                                   causal, dQ.data_ptr(), dK.data_ptr(), dV.data_ptr(),

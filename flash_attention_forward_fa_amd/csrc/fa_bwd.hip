@@ -75,7 +75,8 @@ struct BwdArgs {
   const uint16_t* o;
   const uint16_t* dO;
   const float* L;
-  const float* mask;
+  const void* mask;          // f32, bf16 or bool bytes (the kernel's MASK), or null
+  int64_t mask_sb, mask_sh;  // mask strides of batch and head, in elements (0: broadcast)
   uint16_t* dq;
   uint16_t* dk;
   uint16_t* dv;
@@ -92,7 +93,7 @@ struct BwdArgs {
 // +inf, so that every P of that row is 0
 __device__ __forceinline__ float lse2(float l) { return l == -INFINITY ? INFINITY : l * kLog2e; }
 
-template <int D, int PASS, bool CAUSAL, bool WINDOW, bool HAS_MASK>
+template <int D, int PASS, bool CAUSAL, bool WINDOW, int MASK>
 __global__ __launch_bounds__((64 * BwdCfg<D, PASS>::W))
 __attribute__((amdgpu_waves_per_eu(BwdCfg<D, PASS>::WPE))) void fa_bwd_kernel(BwdArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
@@ -110,6 +111,7 @@ __attribute__((amdgpu_waves_per_eu(BwdCfg<D, PASS>::WPE))) void fa_bwd_kernel(Bw
   constexpr int TILE = BN * D;
   constexpr int NT = 64 * C::W;
   constexpr bool KV = PASS == kBwdKV;
+  constexpr bool HAS_MASK = MASK != kNoMask;
   static_assert(CAUSAL || !WINDOW, "the sliding window includes the causal rule");
   __shared__ __attribute__((aligned(1024))) uint16_t y1s[2][TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t y2s[2][TILE];
@@ -374,8 +376,9 @@ __attribute__((amdgpu_waves_per_eu(BwdCfg<D, PASS>::WPE))) void fa_bwd_kernel(Bw
           float x;
           if constexpr (HAS_MASK) {
             const int h = KV ? th : hf;
-            const float m = a.mask[((int64_t)(b * a.H + h) * ql + min(qi, ql - 1)) * kl +
-                                   min(kj, kl - 1)];
+            const float m = mask_at<MASK>(a.mask, b * a.mask_sb + h * a.mask_sh +
+                                                      (int64_t)min(qi, ql - 1) * kl +
+                                                      min(kj, kl - 1));
             vis = vis && m != -INFINITY;
             x = __builtin_fmaf(s, a.c, kLog2e * m) - l2;
           } else {
@@ -443,53 +446,64 @@ __attribute__((amdgpu_waves_per_eu(BwdCfg<D, PASS>::WPE))) void fa_bwd_kernel(Bw
 #endif
 }
 
-template <int D, int PASS, bool CAUSAL, bool WINDOW, bool HAS_MASK>
+template <int D, int PASS, bool CAUSAL, bool WINDOW, int MASK>
 hipError_t launch_bwd(const BwdArgs& a, unsigned grid, hipStream_t stream) {
-  hipLaunchKernelGGL((fa_bwd_kernel<D, PASS, CAUSAL, WINDOW, HAS_MASK>), dim3(grid),
+  hipLaunchKernelGGL((fa_bwd_kernel<D, PASS, CAUSAL, WINDOW, MASK>), dim3(grid),
                      dim3(64 * BwdCfg<D, PASS>::W), 0, stream, a);
   return hipGetLastError();
 }
 
-template <int D, bool CAUSAL, bool WINDOW, bool HAS_MASK>
+template <int D, bool CAUSAL, bool WINDOW, int MASK>
 hipError_t dispatch_bwd(BwdArgs a, hipStream_t stream) {
   if (a.ql > 0) {
     a.n_ftiles = (a.ql + fixed_rows<D, kBwdQ>() - 1) / fixed_rows<D, kBwdQ>();
-    hipError_t e = launch_bwd<D, kBwdQ, CAUSAL, WINDOW, HAS_MASK>(
+    hipError_t e = launch_bwd<D, kBwdQ, CAUSAL, WINDOW, MASK>(
         a, (unsigned)(a.n_ftiles * a.B * a.H), stream);
     if (e != hipSuccess) return e;
   }
   if (a.kl > 0) {
     a.n_ftiles = (a.kl + fixed_rows<D, kBwdKV>() - 1) / fixed_rows<D, kBwdKV>();
-    return launch_bwd<D, kBwdKV, CAUSAL, WINDOW, HAS_MASK>(
+    return launch_bwd<D, kBwdKV, CAUSAL, WINDOW, MASK>(
         a, (unsigned)(a.n_ftiles * a.B * a.Hkv), stream);
   }
   return hipSuccess;
 }
 
+template <int D, bool CAUSAL, bool WINDOW>
+hipError_t dispatch_bwd_m(const BwdArgs& a, int mask, hipStream_t s) {
+  switch (mask) {
+    case kMaskF32: return dispatch_bwd<D, CAUSAL, WINDOW, kMaskF32>(a, s);
+    case kMaskBF16: return dispatch_bwd<D, CAUSAL, WINDOW, kMaskBF16>(a, s);
+    case kMaskBool: return dispatch_bwd<D, CAUSAL, WINDOW, kMaskBool>(a, s);
+    default: return dispatch_bwd<D, CAUSAL, WINDOW, kNoMask>(a, s);
+  }
+}
+
 template <int D>
-hipError_t dispatch_bwd_d(const BwdArgs& a, bool causal, bool window, bool has_mask,
-                          hipStream_t s) {
-  if (window)
-    return has_mask ? dispatch_bwd<D, true, true, true>(a, s)
-                    : dispatch_bwd<D, true, true, false>(a, s);
-  if (causal)
-    return has_mask ? dispatch_bwd<D, true, false, true>(a, s)
-                    : dispatch_bwd<D, true, false, false>(a, s);
-  return has_mask ? dispatch_bwd<D, false, false, true>(a, s)
-                  : dispatch_bwd<D, false, false, false>(a, s);
+hipError_t dispatch_bwd_d(const BwdArgs& a, bool causal, bool window, int mask, hipStream_t s) {
+  if (window) return dispatch_bwd_m<D, true, true>(a, mask, s);
+  return causal ? dispatch_bwd_m<D, true, false>(a, mask, s)
+                : dispatch_bwd_m<D, false, false>(a, mask, s);
 }
 
 bool aligned_to(const void* p, uintptr_t n) { return ((uintptr_t)p % n) == 0; }
 
-// Shared host path of fa_train_bwd and fa_train_bwd_swa; window < 0: none.
-int train_bwd(const void* q, const void* k, const void* v, const float* mask, const void* O,
-              const float* L, const void* dO, int batch, int n_heads, int n_kv_heads, int ql,
-              int kl, int head_dim, float scale, int causal, int window, void* dQ, void* dK,
-              void* dV, void* stream) {
+// Shared host path of the backward entry points; window < 0: none (window >= 0
+// requires causal). The mask is mask_dtype with batch and head strides in
+// elements; its rows are contiguous (row stride kl).
+int train_bwd(const void* q, const void* k, const void* v, const void* mask, int mask_dtype,
+              int64_t mask_sb, int64_t mask_sh, const void* O, const float* L, const void* dO,
+              int batch, int n_heads, int n_kv_heads, int ql, int kl, int head_dim, float scale,
+              int causal, int window, void* dQ, void* dK, void* dV, void* stream) {
   if (batch < 0 || ql < 0 || kl < 0 || n_heads < 1 || n_kv_heads < 1) return FA_ERR_BAD_SIZE;
   if (n_heads % n_kv_heads != 0) return FA_ERR_HEAD_GROUPING;
   if (head_dim != 64 && head_dim != 128 && head_dim != 256) return FA_ERR_HEAD_DIM;
   if (!isfinite(scale)) return FA_ERR_SCALE;
+  if (window >= 0 && !causal) return FA_ERR_WINDOW;
+  if (mask && ((mask_dtype != FA_MASK_F32 && mask_dtype != FA_MASK_BF16 &&
+                mask_dtype != FA_MASK_BOOL) ||
+               mask_sb < 0 || mask_sh < 0))
+    return FA_ERR_MASK;
   const int64_t qrows = (int64_t)batch * n_heads * ql;
   const int64_t krows = (int64_t)batch * n_kv_heads * kl;
   if (qrows == 0 && krows == 0) return FA_OK;
@@ -499,7 +513,8 @@ int train_bwd(const void* q, const void* k, const void* v, const float* mask, co
   const void* a16[] = {q, k, v, O, dO, dQ, dK, dV};
   for (const void* p : a16)
     if (p && !aligned_to(p, 16)) return FA_ERR_ALIGNMENT;
-  if ((L && !aligned_to(L, 4)) || (mask && !aligned_to(mask, 4))) return FA_ERR_ALIGNMENT;
+  const uintptr_t mask_align = mask_dtype == FA_MASK_BF16 ? 2 : mask_dtype == FA_MASK_BOOL ? 1 : 4;
+  if ((L && !aligned_to(L, 4)) || (mask && !aligned_to(mask, mask_align))) return FA_ERR_ALIGNMENT;
   const int64_t rq = head_dim == 64    ? fixed_rows<64, kBwdQ>()
                      : head_dim == 128 ? fixed_rows<128, kBwdQ>()
                                        : fixed_rows<256, kBwdQ>();
@@ -519,6 +534,12 @@ int train_bwd(const void* q, const void* k, const void* v, const float* mask, co
   a.dO = static_cast<const uint16_t*>(dO);
   a.L = L;
   a.mask = mask;
+  a.mask_sb = mask_sb;
+  a.mask_sh = mask_sh;
+  const int mask_kind = !mask                          ? kNoMask
+                        : mask_dtype == FA_MASK_BF16 ? kMaskBF16
+                        : mask_dtype == FA_MASK_BOOL ? kMaskBool
+                                                     : kMaskF32;
   a.dq = static_cast<uint16_t*>(dQ);
   a.dk = static_cast<uint16_t*>(dK);
   a.dv = static_cast<uint16_t*>(dV);
@@ -542,9 +563,9 @@ int train_bwd(const void* q, const void* k, const void* v, const float* mask, co
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool windowed = window >= 0;
   const hipError_t err =
-      head_dim == 64    ? dispatch_bwd_d<64>(a, causal != 0, windowed, mask != nullptr, s)
-      : head_dim == 128 ? dispatch_bwd_d<128>(a, causal != 0, windowed, mask != nullptr, s)
-                        : dispatch_bwd_d<256>(a, causal != 0, windowed, mask != nullptr, s);
+      head_dim == 64    ? dispatch_bwd_d<64>(a, causal != 0, windowed, mask_kind, s)
+      : head_dim == 128 ? dispatch_bwd_d<128>(a, causal != 0, windowed, mask_kind, s)
+                        : dispatch_bwd_d<256>(a, causal != 0, windowed, mask_kind, s);
   return err == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
@@ -554,8 +575,9 @@ extern "C" int fa_train_bwd(const void* q, const void* k, const void* v, const f
                             const void* O, const float* L, const void* dO, int batch, int n_heads,
                             int n_kv_heads, int ql, int kl, int head_dim, float scale, int causal,
                             void* dQ, void* dK, void* dV, void* stream) {
-  return train_bwd(q, k, v, mask, O, L, dO, batch, n_heads, n_kv_heads, ql, kl, head_dim, scale,
-                   causal, -1, dQ, dK, dV, stream);
+  const int64_t head = (int64_t)ql * kl;
+  return train_bwd(q, k, v, mask, FA_MASK_F32, head * n_heads, head, O, L, dO, batch, n_heads,
+                   n_kv_heads, ql, kl, head_dim, scale, causal, -1, dQ, dK, dV, stream);
 }
 
 extern "C" int fa_train_bwd_swa(const void* q, const void* k, const void* v, const float* mask,
@@ -564,6 +586,18 @@ extern "C" int fa_train_bwd_swa(const void* q, const void* k, const void* v, con
                                 float scale, int window, void* dQ, void* dK, void* dV,
                                 void* stream) {
   if (window < 0) return FA_ERR_WINDOW;
-  return train_bwd(q, k, v, mask, O, L, dO, batch, n_heads, n_kv_heads, ql, kl, head_dim, scale, 1,
-                   window, dQ, dK, dV, stream);
+  const int64_t head = (int64_t)ql * kl;
+  return train_bwd(q, k, v, mask, FA_MASK_F32, head * n_heads, head, O, L, dO, batch, n_heads,
+                   n_kv_heads, ql, kl, head_dim, scale, 1, window, dQ, dK, dV, stream);
+}
+
+extern "C" int fa_train_bwd_ex(const void* q, const void* k, const void* v, const void* mask,
+                               int mask_dtype, long long mask_stride_b, long long mask_stride_h,
+                               const void* O, const float* L, const void* dO, int batch,
+                               int n_heads, int n_kv_heads, int ql, int kl, int head_dim,
+                               float scale, int causal, int window, void* dQ, void* dK, void* dV,
+                               void* stream) {
+  return train_bwd(q, k, v, mask, mask_dtype, mask_stride_b, mask_stride_h, O, L, dO, batch,
+                   n_heads, n_kv_heads, ql, kl, head_dim, scale, causal, window < 0 ? -1 : window,
+                   dQ, dK, dV, stream);
 }

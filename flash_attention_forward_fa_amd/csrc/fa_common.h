@@ -1,7 +1,8 @@
 // fa_common.h - device helpers shared by the forward and backward kernels
 // (gfx950): vector types, reductions over the four 16-lane groups of a
 // wave, the key permutation of the Q.K operand, the LDS chunk permutations,
-// the direct-to-LDS tile copy and small scheduling helpers.
+// the direct-to-LDS tile copy, mask element reads and small scheduling
+// helpers.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -129,6 +130,22 @@ __device__ __forceinline__ void issue_tile(const uint16_t* src, int kbase, int k
           rs, (lds_void*)(lds + (u * NT + wave_base) * 8), 16, o, 0, 0, 0);
     }
   }
+}
+
+// Mask element types (kNoMask: no mask): additive f32 or bf16, or boolean
+// (one byte per key, nonzero = visible).
+constexpr int kNoMask = 0, kMaskF32 = 1, kMaskBF16 = 2, kMaskBool = 3;
+
+// Mask element idx as an additive f32 value (a bf16 mask widens exactly; a
+// boolean mask is 0 for a visible key and -inf for a hidden one).
+template <int MASK>
+__device__ __forceinline__ float mask_at(const void* m, int64_t idx) {
+  if constexpr (MASK == kMaskBF16)
+    return __uint_as_float((uint32_t)static_cast<const uint16_t*>(m)[idx] << 16);
+  else if constexpr (MASK == kMaskBool)
+    return static_cast<const uint8_t*>(m)[idx] ? 0.0f : -INFINITY;
+  else
+    return static_cast<const float*>(m)[idx];
 }
 
 // Wave priority for the next instructions, pinned in place.

@@ -88,21 +88,6 @@ constexpr float kLazy = 8.0f;
 // cache through a block table, with a key count per sequence; they compute
 // every tile compensated, the second one as split-KV partials.
 constexpr int kMixed = 0, kAll = 1, kSplit = 2, kPaged = 3, kPagedSplit = 4;
-// Mask element types (kNoMask: no mask): additive f32 or bf16, or boolean
-// (one byte per key, nonzero = visible).
-constexpr int kNoMask = 0, kMaskF32 = 1, kMaskBF16 = 2, kMaskBool = 3;
-
-// Mask element idx as an additive f32 value (a bf16 mask widens exactly; a
-// boolean mask is 0 for a visible key and -inf for a hidden one).
-template <int MASK>
-__device__ __forceinline__ float mask_at(const void* m, int64_t idx) {
-  if constexpr (MASK == kMaskBF16)
-    return __uint_as_float((uint32_t)static_cast<const uint16_t*>(m)[idx] << 16);
-  else if constexpr (MASK == kMaskBool)
-    return static_cast<const uint8_t*>(m)[idx] ? 0.0f : -INFINITY;
-  else
-    return static_cast<const float*>(m)[idx];
-}
 
 
 struct FwdArgs {

@@ -287,6 +287,21 @@ int fa_train_bwd_swa(const void *q, const void *k, const void *v, const float *m
                      int n_kv_heads, int ql, int kl, int head_dim, float scale, int window,
                      void *dQ, void *dK, void *dV, void *stream);
 
+/*
+ * fa_train_bwd_ex - the backward of fa_train_fwd_ex: the same mask options
+ * (mask_dtype, batch/head strides, broadcast), causal and window arguments,
+ * with the meaning given for fa_train_fwd_ex; O and L must come from
+ * fa_train_fwd_ex with the same options. Other arguments, outputs and
+ * statuses as for fa_train_bwd, plus FA_ERR_MASK and FA_ERR_WINDOW as for
+ * fa_train_fwd_ex. fa_train_bwd(...) is fa_train_bwd_ex with an f32 mask,
+ * strides H*ql*kl and ql*kl, window -1.
+ */
+int fa_train_bwd_ex(const void *q, const void *k, const void *v, const void *mask,
+                    int mask_dtype, long long mask_stride_b, long long mask_stride_h,
+                    const void *O, const float *L, const void *dO, int batch, int n_heads,
+                    int n_kv_heads, int ql, int kl, int head_dim, float scale, int causal,
+                    int window, void *dQ, void *dK, void *dV, void *stream);
+
 /* Static, human-readable name of a status code (never NULL). */
 const char *fa_status_string(int status);
 

@@ -30,7 +30,7 @@ def test_header_declares_the_entry_points():
     names = _declared_functions()
     assert {"fa_train_fwd", "fa_train_fwd_swa", "fa_train_fwd_ex", "fa_train_fwd_split",
             "fa_train_fwd_split_workspace", "fa_paged_fwd", "fa_train_bwd", "fa_train_bwd_swa",
-            "fa_status_string"} <= names
+            "fa_train_bwd_ex", "fa_status_string"} <= names
 
 
 def test_library_exports_every_declared_symbol():
@@ -265,3 +265,18 @@ def test_paged_invalid_arguments_are_rejected(over, code):
 @pytest.mark.parametrize("over", [dict(batch=0), dict(ql=0, q=0, O=0, L=0)])
 def test_paged_empty_problems_are_noops(over):
     assert _call_paged(**over) == 0
+
+
+BWD_EX_GOOD = dict({k: v for k, v in BWD_GOOD.items() if k != "mask"}, mask=A, mask_dtype=0,
+                   mask_stride_b=0, mask_stride_h=64, window=-1)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(mask_dtype=3), 10), (dict(mask_stride_h=-1), 10), (dict(causal=0, window=2), 9),
+    (dict(mask=A + 2), 6), (dict(mask=A + 1, mask_dtype=1), 6), (dict(dQ=0), 1),
+    (dict(head_dim=96), 4), (dict(scale=math.nan), 5),
+])
+def test_backward_ex_invalid_arguments_are_rejected(over, code):
+    args = dict(BWD_EX_GOOD)
+    args.update(over)
+    assert fa.fa_train_bwd_ex(**args) == code

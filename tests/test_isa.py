@@ -46,7 +46,7 @@ def test_all_variants_present(isa):
     bwd = [n for n in isa if "fa_bwd_kernel" in n]
     # head_dim (64, 128, 256) x {none, causal, window} x {mixed, compensated f32 mask, bf16 mask}
     assert len(fwd) == 54  # + split-KV, paged, paged split-KV (head_dim x causal), bool masks
-    assert len(bwd) == 36  # head_dim (3) x {dQ, dKV} x {none, causal, window} x mask
+    assert len(bwd) == 72  # head_dim (3) x {dQ, dKV} x {none, causal, window} x mask (4 kinds)
 
 
 _OPEN = (re.compile(r"s_(?:and|andn2|or)_saveexec_b64 (s\[\d+:\d+\])"),
