@@ -317,40 +317,44 @@ def main():
                 res[f"{label}_tflops"] = flop / (ms * 1e-3) / 1e12
                 res[f"{label}_kv_gbs"] = res["kv_bytes"] / (ms * 1e-3) / 1e9
             if ql == 1:
-                # the same keys in a block-paged cache (64-key blocks in a seeded
-                # shuffled order), read through fa_paged_fwd with the same chunks
-                bs = 64
-                per = kl // bs
-                order = torch.from_numpy(np.random.default_rng(ql + B).permutation(B * per)
-                                         .astype(np.int64)).to(dev)
-                kc = torch.empty((B * per, w.Hkv, bs, w.D), dtype=torch.bfloat16, device=dev)
-                vc = torch.empty_like(kc)
-                kc[order] = k.view(B, w.Hkv, per, bs, w.D).permute(0, 2, 1, 3, 4).reshape(
-                    B * per, w.Hkv, bs, w.D)
-                vc[order] = v.view(B, w.Hkv, per, bs, w.D).permute(0, 2, 1, 3, 4).reshape(
-                    B * per, w.Hkv, bs, w.D)
-                table = order.view(B, per).to(torch.int32)
-                lens = torch.full((B,), kl, dtype=torch.int32, device=dev)
-                call = lambda: fa.paged_fwd(q, kc, vc, table, lens, scale=w.scale, causal=True,
-                                            n_split=n_split, workspace=ws, out=O, lse=L)
-                for _ in range(EXTRA_WARMUP):
-                    call()
-                torch.cuda.synchronize()
-                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                a.record(stream)
-                for _ in range(args.split_steps):
-                    call()
-                b.record(stream)
-                torch.cuda.synchronize()
-                ms = a.elapsed_time(b) / args.split_steps
-                res["paged_split_ms_avg"] = ms
-                res["paged_split_kv_gbs"] = res["kv_bytes"] / (ms * 1e-3) / 1e9
-                del kc, vc, table, lens
+                # the same keys in a block-paged cache (blocks of 64 and of 16
+                # keys in a seeded shuffled order), read through fa_paged_fwd
+                # with the same chunks
+                for bs, tag in ((64, "paged_split"), (16, "paged16_split")):
+                    per = kl // bs
+                    order = torch.from_numpy(np.random.default_rng(ql + B).permutation(B * per)
+                                             .astype(np.int64)).to(dev)
+                    kc = torch.empty((B * per, w.Hkv, bs, w.D), dtype=torch.bfloat16, device=dev)
+                    vc = torch.empty_like(kc)
+                    kc[order] = k.view(B, w.Hkv, per, bs, w.D).permute(0, 2, 1, 3, 4).reshape(
+                        B * per, w.Hkv, bs, w.D)
+                    vc[order] = v.view(B, w.Hkv, per, bs, w.D).permute(0, 2, 1, 3, 4).reshape(
+                        B * per, w.Hkv, bs, w.D)
+                    table = order.view(B, per).to(torch.int32)
+                    lens = torch.full((B,), kl, dtype=torch.int32, device=dev)
+                    call = lambda: fa.paged_fwd(q, kc, vc, table, lens, scale=w.scale,
+                                                causal=True, n_split=n_split, workspace=ws,
+                                                out=O, lse=L)
+                    for _ in range(EXTRA_WARMUP):
+                        call()
+                    torch.cuda.synchronize()
+                    a = torch.cuda.Event(enable_timing=True)
+                    b = torch.cuda.Event(enable_timing=True)
+                    a.record(stream)
+                    for _ in range(args.split_steps):
+                        call()
+                    b.record(stream)
+                    torch.cuda.synchronize()
+                    ms = a.elapsed_time(b) / args.split_steps
+                    res[f"{tag}_ms_avg"] = ms
+                    res[f"{tag}_kv_gbs"] = res["kv_bytes"] / (ms * 1e-3) / 1e9
+                    del kc, vc, table, lens
             split_kv[name] = res
             log(f"{name}: plain {res['plain_ms_avg'] * 1e3:.1f} us, split({n_split}) "
                 f"{res['split_ms_avg'] * 1e3:.1f} us ({res['split_tflops']:.1f} TFLOP/s, "
                 f"K+V {res['split_kv_gbs']:.0f} GB/s)"
-                + (f", paged split {res['paged_split_ms_avg'] * 1e3:.1f} us"
+                + (f", paged split {res['paged_split_ms_avg'] * 1e3:.1f} us (64-key blocks), "
+                   f"{res['paged16_split_ms_avg'] * 1e3:.1f} us (16-key blocks)"
                    if "paged_split_ms_avg" in res else ""))
             del q, k, v, O, L, ws
 

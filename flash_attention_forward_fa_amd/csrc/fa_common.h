@@ -132,6 +132,40 @@ __device__ __forceinline__ void issue_tile(const uint16_t* src, int kbase, int k
   }
 }
 
+// The same copy from a block-paged cache whose blocks may be shorter than a
+// tile: block_size a positive multiple of 16. One wave instruction moves
+// 64 chunks = 64 / (D / 8) consecutive tile rows (at most 8), which then lie
+// in one block; its buffer descriptor is based at that block's row of the
+// instruction's first row (a wave-uniform table read), clamped into the cache.
+// Rows past the sequence's last key repeat that key's row, as above.
+template <int D, int BN, int NT, bool IS_K>
+__device__ __forceinline__ void issue_tile_blocks(const uint16_t* cache, const int* table_row,
+                                                  int n_blocks, int n_kv_heads, int g,
+                                                  int block_size, int kbase, int kl, uint16_t* lds,
+                                                  int tid, int wave_base) {
+  constexpr int CH = D / 8;
+  constexpr int RPW = 64 / CH;  // rows per wave instruction
+  constexpr int ROUNDS = CopyShape<D, BN, NT>::ROUNDS;
+  static_assert(RPW >= 1 && 16 % RPW == 0, "a wave instruction must stay in one 16-row block");
+  const int rows = min(BN, kl - kbase);
+#pragma unroll
+  for (int u = 0; u < ROUNDS; ++u) {
+    const int p = u * NT + tid;
+    const int row0 = __builtin_amdgcn_readfirstlane((u * NT + wave_base) / CH);
+    const int base_row = min(row0, rows - 1);
+    const int pos = kbase + base_row;
+    int blk = __builtin_amdgcn_readfirstlane(table_row[pos / block_size]);
+    blk = min(max(blk, 0), n_blocks - 1);
+    const uint16_t* src =
+        cache + (((int64_t)blk * n_kv_heads + g) * block_size + pos % block_size) * D;
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)src, 0, RPW * D * 2, kRsrcWord3);
+    const int o = chunk_offset<D, IS_K>(p, min(p / CH, rows - 1)) - base_row * D * 2;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds + (u * NT + wave_base) * 8), 16,
+                                             o, 0, 0, 0);
+  }
+}
+
 // Mask element types (kNoMask: no mask): additive f32 or bf16, or boolean
 // (one byte per key, nonzero = visible).
 constexpr int kNoMask = 0, kMaskF32 = 1, kMaskBF16 = 2, kMaskBool = 3;

@@ -87,7 +87,10 @@ constexpr float kLazy = 8.0f;
 // The paged kernels (kPaged, kPagedSplit) read K and V from a block-paged
 // cache through a block table, with a key count per sequence; they compute
 // every tile compensated, the second one as split-KV partials.
-constexpr int kMixed = 0, kAll = 1, kSplit = 2, kPaged = 3, kPagedSplit = 4;
+// kPagedBlocks and kPagedBlocksSplit are the same for caches whose blocks are
+// shorter than a key tile (block_size a multiple of 16, not of 64).
+constexpr int kMixed = 0, kAll = 1, kSplit = 2, kPaged = 3, kPagedSplit = 4, kPagedBlocks = 5,
+              kPagedBlocksSplit = 6;
 
 
 struct FwdArgs {
@@ -126,7 +129,7 @@ struct FwdArgs {
 // redo set are computed and written (waves without such a row only take part
 // in the tile copies).
 template <int D, bool CAUSAL, bool WINDOW, int MASK, bool PRECISE, bool REDO, bool SPLIT = false,
-          bool PAGED = false>
+          bool PAGED = false, bool SMALL_BLOCKS = false>
 __device__ __forceinline__ bool fwd_tile(const FwdArgs& a, int qtile, int bh, uint16_t* k0s,
                                          uint16_t* v0s, uint16_t* k1s, uint16_t* v1s,
                                          bool (&redo)[Cfg<D>::QB], int* wg_flags, int split = 0) {
@@ -202,10 +205,13 @@ __device__ __forceinline__ bool fwd_tile(const FwdArgs& a, int qtile, int bh, ui
   int koff[CopyShape<D, BN, NT>::ROUNDS], voff[CopyShape<D, BN, NT>::ROUNDS];
   copy_offsets<D, BN, NT, true>(tid, koff);
   copy_offsets<D, BN, NT, false>(tid, voff);
-  // paged KV: a tile (block_size is a multiple of BN) lies in one block,
-  // table[b][kt*BN / block_size], from row (kt*BN) % block_size; its copy
-  // descriptor covers only the tile's valid rows. A table entry outside the
-  // cache is clamped into it (wrong keys, never an access outside the cache).
+  // paged KV: when block_size is a multiple of BN a tile lies in one block,
+  // table[b][kt*BN / block_size], from row (kt*BN) % block_size, and its copy
+  // descriptor covers only the tile's valid rows; shorter blocks (multiples
+  // of 16) are looked up per wave instruction (issue_tile_blocks). A table
+  // entry outside the cache is clamped into it (wrong keys, never an access
+  // outside the cache).
+  const int* table_row = PAGED ? a.block_table + (int64_t)b * a.max_blocks : nullptr;
   auto paged_src = [&](const uint16_t* cache, int kt) {
     const int pos = kt * BN;
     int blk = __builtin_amdgcn_readfirstlane(
@@ -214,17 +220,25 @@ __device__ __forceinline__ bool fwd_tile(const FwdArgs& a, int qtile, int bh, ui
     return cache + (((int64_t)blk * a.Hkv + g) * a.block_size + pos % a.block_size) * D;
   };
   auto issue_k = [&](int kt, uint16_t* dst) {
-    if constexpr (PAGED)
-      issue_tile<D, BN, NT, true>(paged_src(a.k, kt), 0, min(BN, kl - kt * BN), dst, tid,
-                                  64 * wave, koff);
-    else
+    if constexpr (PAGED) {
+      if constexpr (!SMALL_BLOCKS)
+        issue_tile<D, BN, NT, true>(paged_src(a.k, kt), 0, min(BN, kl - kt * BN), dst, tid,
+                                    64 * wave, koff);
+      else
+        issue_tile_blocks<D, BN, NT, true>(a.k, table_row, a.n_blocks, a.Hkv, g, a.block_size,
+                                           kt * BN, kl, dst, tid, 64 * wave);
+    } else
       issue_tile<D, BN, NT, true>(kp, kt * BN, kl, dst, tid, 64 * wave, koff);
   };
   auto issue_v = [&](int kt, uint16_t* dst) {
-    if constexpr (PAGED)
-      issue_tile<D, BN, NT, false>(paged_src(a.v, kt), 0, min(BN, kl - kt * BN), dst, tid,
-                                   64 * wave, voff);
-    else
+    if constexpr (PAGED) {
+      if constexpr (!SMALL_BLOCKS)
+        issue_tile<D, BN, NT, false>(paged_src(a.v, kt), 0, min(BN, kl - kt * BN), dst, tid,
+                                     64 * wave, voff);
+      else
+        issue_tile_blocks<D, BN, NT, false>(a.v, table_row, a.n_blocks, a.Hkv, g, a.block_size,
+                                            kt * BN, kl, dst, tid, 64 * wave);
+    } else
       issue_tile<D, BN, NT, false>(vp, kt * BN, kl, dst, tid, 64 * wave, voff);
   };
   if (n_kt > kt_first) issue_k(kt_first, (kt_first & 1) ? k1s : k0s);
@@ -626,7 +640,7 @@ __attribute__((amdgpu_waves_per_eu(MODE == kMixed ? Cfg<D>::WPE : 2))) void fa_f
   // (Groups of 1, 2 or 4 heads were measured slower, 8 faster than all.)
   // (split-KV: the chunk index is the fastest-varying part of the block index)
   const int BH = a.B * a.H;
-  constexpr bool SPLIT_GRID = MODE == kSplit || MODE == kPagedSplit;
+  constexpr bool SPLIT_GRID = MODE == kSplit || MODE == kPagedSplit || MODE == kPagedBlocksSplit;
   const int split = SPLIT_GRID ? (int)(blockIdx.x % (unsigned)a.n_split) : 0;
   const int bid = SPLIT_GRID ? (int)(blockIdx.x / (unsigned)a.n_split) : (int)blockIdx.x;
   int qt_rev, bh;
@@ -664,6 +678,12 @@ __attribute__((amdgpu_waves_per_eu(MODE == kMixed ? Cfg<D>::WPE : 2))) void fa_f
   } else if constexpr (MODE == kPagedSplit) {
     fwd_tile<D, CAUSAL, false, kNoMask, true, false, true, true>(a, qtile, bh, k0s, v0s, k1s, v1s,
                                                                  redo, wg_flags, split);
+  } else if constexpr (MODE == kPagedBlocks) {
+    fwd_tile<D, CAUSAL, false, kNoMask, true, false, false, true, true>(a, qtile, bh, k0s, v0s,
+                                                                        k1s, v1s, redo, wg_flags);
+  } else if constexpr (MODE == kPagedBlocksSplit) {
+    fwd_tile<D, CAUSAL, false, kNoMask, true, false, true, true, true>(
+        a, qtile, bh, k0s, v0s, k1s, v1s, redo, wg_flags, split);
   } else {
     fwd_tile<D, CAUSAL, WINDOW, MASK, true, false>(a, qtile, bh, k0s, v0s, k1s, v1s, redo,
                                                    wg_flags);
@@ -740,13 +760,14 @@ hipError_t dispatch_c(FwdArgs a, int mask, int n_short, hipStream_t stream) {
 }
 
 // Split-KV: the partials over all (chunk, head, query tile), then the merge.
-template <int D, bool CAUSAL, bool PAGED = false>
+// (MODE: kSplit, kPagedSplit or kPagedBlocksSplit)
+template <int D, bool CAUSAL, int MODE = kSplit>
 hipError_t dispatch_split(FwdArgs a, hipStream_t stream) {
   const unsigned bh = (unsigned)(a.B * a.H);
   a.qt_base = 0;
   a.qt_count = a.n_qtiles;
   a.n_precise = a.n_qtiles;
-  hipError_t e = launch<D, CAUSAL, false, kNoMask, PAGED ? kPagedSplit : kSplit>(
+  hipError_t e = launch<D, CAUSAL, false, kNoMask, MODE>(
       a, bh * (unsigned)a.n_qtiles * (unsigned)a.n_split, stream);
   if (e != hipSuccess) return e;
   CombineArgs c;
@@ -762,17 +783,24 @@ hipError_t dispatch_split(FwdArgs a, hipStream_t stream) {
 }
 
 // Paged KV: one compensated launch over all query tiles, or the split-KV pair.
-template <int D>
-hipError_t dispatch_paged(FwdArgs a, bool causal, hipStream_t stream) {
+template <int D, int MODE, int SPLIT_MODE>
+hipError_t dispatch_paged_m(FwdArgs a, bool causal, hipStream_t stream) {
   if (a.n_split > 0)
-    return causal ? dispatch_split<D, true, true>(a, stream)
-                  : dispatch_split<D, false, true>(a, stream);
+    return causal ? dispatch_split<D, true, SPLIT_MODE>(a, stream)
+                  : dispatch_split<D, false, SPLIT_MODE>(a, stream);
   const unsigned grid = (unsigned)(a.B * a.H) * (unsigned)a.n_qtiles;
   a.qt_base = 0;
   a.qt_count = a.n_qtiles;
   a.n_precise = a.n_qtiles;
-  return causal ? launch<D, true, false, kNoMask, kPaged>(a, grid, stream)
-                : launch<D, false, false, kNoMask, kPaged>(a, grid, stream);
+  return causal ? launch<D, true, false, kNoMask, MODE>(a, grid, stream)
+                : launch<D, false, false, kNoMask, MODE>(a, grid, stream);
+}
+
+template <int D>
+hipError_t dispatch_paged(const FwdArgs& a, bool causal, hipStream_t stream) {
+  return a.block_size % Cfg<D>::BN == 0
+             ? dispatch_paged_m<D, kPaged, kPagedSplit>(a, causal, stream)
+             : dispatch_paged_m<D, kPagedBlocks, kPagedBlocksSplit>(a, causal, stream);
 }
 
 template <int D>
@@ -960,7 +988,7 @@ extern "C" int fa_paged_fwd(const void* q, const void* k_cache, const void* v_ca
   if (n_heads % n_kv_heads != 0) return FA_ERR_HEAD_GROUPING;
   if (head_dim != 64 && head_dim != 128 && head_dim != 256) return FA_ERR_HEAD_DIM;
   if (!isfinite(scale)) return FA_ERR_SCALE;
-  if (block_size < 64 || block_size % 64 != 0) return FA_ERR_PAGED;
+  if (block_size < 16 || block_size % 16 != 0) return FA_ERR_PAGED;
   if (n_split < 0 || n_split > kMaxSplit) return FA_ERR_SPLIT;
   const int64_t rows = (int64_t)batch * n_heads * ql;
   if (rows == 0) return FA_OK;
@@ -1054,7 +1082,7 @@ extern "C" const char* fa_status_string(int status) {
     case FA_ERR_WINDOW: return "sliding window must be >= 0 and comes with causal masking";
     case FA_ERR_MASK: return "mask dtype must be FA_MASK_F32, FA_MASK_BF16 or FA_MASK_BOOL, strides >= 0";
     case FA_ERR_SPLIT: return "n_split must be in 1..65536 and the workspace large enough";
-    case FA_ERR_PAGED: return "block_size must be a positive multiple of 64 and the cache non-empty";
+    case FA_ERR_PAGED: return "block_size must be a positive multiple of 16 and the cache non-empty";
     default: return "unknown status";
   }
 }

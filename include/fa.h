@@ -45,7 +45,7 @@ enum fa_status {
     FA_ERR_SPLIT = 11,         /* fa_train_fwd_split: n_split outside 1..65536, or the
                                   workspace smaller than the split needs                */
     FA_ERR_PAGED = 12          /* fa_paged_fwd: block_size not a positive multiple of
-                                  64, or no cache blocks for a non-empty table          */
+                                  16, or no cache blocks for a non-empty table          */
 };
 
 /* Element types of an additive mask (fa_train_fwd_ex). */
@@ -219,7 +219,8 @@ unsigned long fa_train_fwd_split_workspace(int batch, int n_heads, int ql, int h
  *               outside the cache, but the keys read are then wrong)
  *   seq_lens    int32 [batch] (device, read): keys of each sequence, clamped
  *               to 0..max_blocks*block_size
- *   block_size  a positive multiple of 64 (a key tile lies in one block)
+ *   block_size  a positive multiple of 16 (multiples of 64: one block per
+ *               64-key tile; shorter blocks: one per copy instruction)
  *   n_split     0: one launch; >= 1: split-KV with workspace (as for
  *               fa_train_fwd_split, chunks of max_blocks*block_size keys;
  *               workspace size from fa_train_fwd_split_workspace)

@@ -250,7 +250,7 @@ def _call_paged(**over):
 
 
 @pytest.mark.parametrize("over,code", [
-    (dict(block_size=16), 12), (dict(block_size=96), 12), (dict(block_size=0), 12),
+    (dict(block_size=8), 12), (dict(block_size=40), 12), (dict(block_size=0), 12),
     (dict(n_blocks=0), 12), (dict(block_table=0), 1), (dict(seq_lens=0), 1), (dict(k_cache=0), 1),
     (dict(q=A + 2), 6), (dict(block_table=A + 2), 6), (dict(seq_lens=A + 1), 6),
     (dict(head_dim=80), 4), (dict(n_heads=3), 3), (dict(scale=math.inf), 5),

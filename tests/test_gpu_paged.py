@@ -79,6 +79,15 @@ CASES = [
     (2, 4, 2, 300, 128, 128, [1000, 450], True),   # prefill against a cache
     (2, 4, 4, 70, 64, 64, [300, 200], False),
     (2, 4, 2, 1, 64, 64, [0, 200], True),          # a sequence with no key
+    # blocks shorter than a 64-key tile (looked up per copy instruction)
+    (1, 4, 4, 1, 128, 16, [37], True),
+    (3, 8, 2, 1, 128, 16, [1, 64, 300], True),
+    (2, 4, 1, 4, 64, 32, [4, 77], True),
+    (2, 2, 2, 1, 256, 16, [9, 513], True),
+    (2, 8, 2, 1, 128, 48, [1500, 3000], True),
+    (2, 4, 2, 300, 128, 16, [1000, 450], True),
+    (2, 4, 4, 70, 64, 96, [300, 200], False),
+    (2, 4, 2, 1, 256, 32, [0, 200], True),
 ]
 
 
@@ -87,6 +96,32 @@ CASES = [
 def test_paged_matches_contiguous_oracle(case, n_split):
     print(f"case paged {case} n_split={n_split}", flush=True)
     _run(case, n_split, seed=11000 + CASES.index(case))
+
+
+@pytest.mark.parametrize("D", [64, 128, 256])
+def test_small_blocks_give_the_bits_of_whole_tile_blocks(D):
+    """The same sequences in blocks of 16 and of 64 keys: only the copies'
+    addressing differs, so O and L agree bit for bit (plain and split)."""
+    import torch
+    import flash_attention_forward_fa_amd as fa
+    B, H, Hkv, ql, lens = 3, 8, 2, 1, [700, 1, 2049]
+    print(f"case paged small vs whole blocks D={D}", flush=True)
+    s = fagen.SEED_BASE + 11800 + D
+    N = max(lens)
+    q = gu.to_dev(fagen.normal_bf16(s, 0, (B, H, ql, D)), "cuda:0")
+    keys = fagen.normal_bf16(s, 1, (B, Hkv, N, D))
+    values = fagen.normal_bf16(s, 2, (B, Hkv, N, D))
+    n = torch.tensor(lens, dtype=torch.int32, device="cuda:0")
+    outs = []
+    for bs in (16, 64):
+        kc, vc, table = _paged(keys, values, bs, 11800 + D + bs)
+        args = (q, gu.to_dev(kc, "cuda:0"), gu.to_dev(vc, "cuda:0"),
+                torch.from_numpy(table).to("cuda:0"), n)
+        outs.append([fa.paged_fwd(*args, causal=True, n_split=ns) for ns in (0, 8)])
+    torch.cuda.synchronize()
+    for (o1, l1), (o2, l2) in zip(*outs):
+        assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+        assert torch.equal(l1, l2)
 
 
 def test_paged_table_entries_outside_the_cache_are_clamped():
@@ -103,15 +138,21 @@ def test_paged_table_entries_outside_the_cache_are_clamped():
     table = torch.tensor([[0, 10 ** 9], [-5, 2]], dtype=torch.int32, device="cuda:0")
     lens = torch.tensor([128, 100], dtype=torch.int32, device="cuda:0")
     O, L = fa.paged_fwd(q, kc, vc, table, lens, causal=True)
+    # blocks of 16 keys: the same clamping on the per-instruction lookup
+    k16, v16 = kc.view(5 * 4, Hkv, 16, D), vc.view(5 * 4, Hkv, 16, D)
+    t16 = torch.tensor([[0, 1, 2, 3, 10 ** 9, -7, 19, 4], [-5, 2, 3, 1 << 30, 0, 0, 0, 0]],
+                       dtype=torch.int32, device="cuda:0")
+    O16, L16 = fa.paged_fwd(q, k16, v16, t16, lens, causal=True)
     torch.cuda.synchronize()
     assert torch.isfinite(O.float()).all() and torch.isfinite(L).all()
+    assert torch.isfinite(O16.float()).all() and torch.isfinite(L16).all()
 
 
 def test_paged_errors_raise_from_binding():
     import torch
     import flash_attention_forward_fa_amd as fa
     q = torch.zeros(1, 2, 1, 64, device="cuda:0", dtype=torch.bfloat16)
-    c = torch.zeros(4, 2, 32, 64, device="cuda:0", dtype=torch.bfloat16)
+    c = torch.zeros(4, 2, 40, 64, device="cuda:0", dtype=torch.bfloat16)
     t = torch.zeros(1, 2, dtype=torch.int32, device="cuda:0")
     n = torch.tensor([40], dtype=torch.int32, device="cuda:0")
     with pytest.raises(fa.FAError) as e:

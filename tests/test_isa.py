@@ -45,7 +45,8 @@ def test_all_variants_present(isa):
     fwd = [n for n in isa if "fa_fwd_kernel" in n]
     bwd = [n for n in isa if "fa_bwd_kernel" in n]
     # head_dim (64, 128, 256) x {none, causal, window} x {mixed, compensated f32 mask, bf16 mask}
-    assert len(fwd) == 54  # + split-KV, paged, paged split-KV (head_dim x causal), bool masks
+    assert len(fwd) == 66  # + split-KV, paged (whole-tile and short blocks), paged split-KV
+    #                       (head_dim x causal each), bool masks
     assert len(bwd) == 72  # head_dim (3) x {dQ, dKV} x {none, causal, window} x mask (4 kinds)
 
 
