@@ -203,7 +203,8 @@ def paged_fwd(q, k_cache, v_cache, block_table, seq_lens, scale=None, causal=Fal
     """O, L = paged_fwd(q, k_cache, v_cache, block_table, seq_lens, scale=None, causal=False,
                         n_split=0, workspace=None)
 
-    q: bf16 [B, H, ql, D]; k_cache, v_cache: bf16 [n_blocks, Hkv, block_size, D];
+    q: bf16 [B, H, ql, D]; k_cache, v_cache: bf16 [n_blocks, Hkv, block_size, D]
+    (block_size a positive multiple of 16);
     block_table: int32 [B, max_blocks]; seq_lens: int32 [B] (all on q's GPU).
     Sequence b attends to its first seq_lens[b] keys (key position p at row
     p % block_size of block block_table[b, p // block_size]). n_split > 0 uses
