@@ -19,6 +19,7 @@ FA_STATUS = {
     4: "FA_ERR_HEAD_DIM", 5: "FA_ERR_SCALE", 6: "FA_ERR_ALIGNMENT", 7: "FA_ERR_TOO_LARGE",
     8: "FA_ERR_LAUNCH", 9: "FA_ERR_WINDOW", 10: "FA_ERR_MASK", 11: "FA_ERR_SPLIT",
     12: "FA_ERR_PAGED",
+    13: "FA_ERR_STRIDE",
 }
 FA_MASK_F32, FA_MASK_BF16, FA_MASK_BOOL = 0, 1, 2
 
@@ -50,6 +51,11 @@ def lib():
         l.fa_train_fwd_ex.argtypes = [vp, vp, vp, vp, ci, i64, i64, ci, ci, ci, ci, ci, ci,
                                       ctypes.c_float, ci, ci, vp, vp, vp]
         l.fa_train_fwd_ex.restype = ci
+        pll = ctypes.POINTER(ctypes.c_longlong)
+        l.fa_train_fwd_strided.argtypes = [vp, pll, vp, pll, vp, pll, ci, ci, ci, ci, ci, ci,
+                                           ctypes.c_float, ci, ci, ci, vp, ctypes.c_ulong, vp,
+                                           pll, vp, vp]
+        l.fa_train_fwd_strided.restype = ci
         ul = ctypes.c_ulong
         l.fa_train_fwd_split.argtypes = [vp, vp, vp, ci, ci, ci, ci, ci, ci, ctypes.c_float, ci,
                                          ci, vp, ul, vp, vp, vp]
@@ -244,6 +250,74 @@ def paged_fwd(q, k_cache, v_cache, block_table, seq_lens, scale=None, causal=Fal
                               block_table.data_ptr(), seq_lens.data_ptr(), B, H, Hkv, ql,
                               n_blocks, bs, max_blocks, D, scale, causal, n_split, ws_ptr,
                               ws_bytes, O.data_ptr(), L.data_ptr(), s.cuda_stream)
+    if status != 0:
+        raise FAError(status, status_string(status))
+    return O, L
+
+
+def _strides3(st):
+    """A (batch, head, row) element-stride triple as a C array, or None."""
+    if st is None:
+        return None
+    return (ctypes.c_longlong * 3)(*(int(x) for x in st))
+
+
+def fa_train_fwd_strided(q, q_strides, k, k_strides, v, v_strides, batch, n_heads, n_kv_heads,
+                         ql, kl, head_dim, scale, causal, window, n_split, workspace,
+                         workspace_bytes, O, o_strides, L, stream):
+    """The C entry point with raw integer pointers (0 for NULL) and stride
+    triples (or None); returns the status."""
+    return lib().fa_train_fwd_strided(
+        q or None, _strides3(q_strides), k or None, _strides3(k_strides), v or None,
+        _strides3(v_strides), batch, n_heads, n_kv_heads, ql, kl, head_dim, float(scale),
+        int(bool(causal)), int(window), int(n_split), workspace or None, int(workspace_bytes),
+        O or None, _strides3(o_strides), L or None, stream or None)
+
+
+def train_fwd_strided(q, k, v, scale=None, causal=False, window=None, n_split=0, workspace=None,
+                      out=None, lse=None, stream=None):
+    """O, L = train_fwd_strided(q, k, v, scale=None, causal=False, window=None, n_split=0)
+
+    The forward on strided views: q [B, H, ql, D], k and v [B, Hkv, kl, D] and
+    out (optional, else a new contiguous tensor) may have any non-negative
+    strides in their first three dimensions (multiples of 8 elements) with
+    head_dim contiguous, e.g. q = x.transpose(1, 2) for x of layout
+    [B, ql, H, D]. L is contiguous [B, H, ql]. n_split > 0 runs split-KV (its
+    workspace allocated here when None).
+    """
+    import torch
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.bfloat16:
+            raise TypeError(f"{name} must be a bfloat16 tensor")
+        if t.dim() != 4 or t.stride(3) != 1 or not t.is_cuda or t.device != q.device:
+            raise ValueError(f"{name} must be a 4-d tensor with contiguous head_dim on q's GPU")
+    B, H, ql, D = q.shape
+    Bk, Hkv, kl, Dk = k.shape
+    if tuple(v.shape) != tuple(k.shape) or Bk != B or Dk != D:
+        raise ValueError("k and v must be [B, Hkv, kl, D] with q's B and D")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    O = out if out is not None else torch.empty((B, H, ql, D), dtype=torch.bfloat16,
+                                                device=q.device)
+    L = lse if lse is not None else torch.empty((B, H, ql), dtype=torch.float32, device=q.device)
+    if tuple(O.shape) != (B, H, ql, D) or O.dtype != torch.bfloat16 or O.stride(3) != 1:
+        raise ValueError("out must be a bf16 tensor shaped like q with contiguous head_dim")
+    if tuple(L.shape) != (B, H, ql) or L.dtype != torch.float32 or not L.is_contiguous():
+        raise ValueError("lse must be a contiguous f32 tensor [B, H, ql]")
+    ws_bytes = 0
+    if n_split > 0:
+        ws_bytes = fa_train_fwd_split_workspace(B, H, ql, D, n_split)
+        if workspace is None:
+            workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+        ws_bytes = workspace.numel() * workspace.element_size()
+    s = stream if stream is not None else torch.cuda.current_stream(q.device)
+    st = lambda t: t.stride()[:3]
+    with torch.cuda.device(q.device):
+        status = fa_train_fwd_strided(
+            q.data_ptr(), st(q), k.data_ptr(), st(k), v.data_ptr(), st(v), B, H, Hkv, ql, kl, D,
+            scale, causal, -1 if window is None else window, n_split,
+            workspace.data_ptr() if workspace is not None else 0, ws_bytes, O.data_ptr(), st(O),
+            L.data_ptr(), s.cuda_stream)
     if status != 0:
         raise FAError(status, status_string(status))
     return O, L

@@ -92,42 +92,46 @@ struct CopyShape {
   static_assert(ROUNDS * NT == BN * CH, "tile not a multiple of the workgroup");
 };
 
+// (rs: the source's row stride in elements, D when its rows are contiguous)
 template <int D, bool IS_K>
-__device__ __forceinline__ int chunk_offset(int p, int row) {
+__device__ __forceinline__ int chunk_offset(int p, int row, int rs = D) {
   constexpr int CH = D / 8;
   const int r = p / CH;
-  return (row * D + 8 * ((p % CH) ^ (IS_K ? kswz<D>(r) : vswz<D>(r)))) * 2;
+  return (row * rs + 8 * ((p % CH) ^ (IS_K ? kswz<D>(r) : vswz<D>(r)))) * 2;
 }
 
 template <int D, int BN, int NT, bool IS_K>
-__device__ __forceinline__ void copy_offsets(int tid, int (&off)[CopyShape<D, BN, NT>::ROUNDS]) {
+__device__ __forceinline__ void copy_offsets(int tid, int (&off)[CopyShape<D, BN, NT>::ROUNDS],
+                                             int rs = D) {
 #pragma unroll
   for (int u = 0; u < CopyShape<D, BN, NT>::ROUNDS; ++u) {
     const int p = u * NT + tid;  // LDS slot (16-byte units)
-    off[u] = chunk_offset<D, IS_K>(p, p / (D / 8));
+    off[u] = chunk_offset<D, IS_K>(p, p / (D / 8), rs);
   }
 }
 
 template <int D, int BN, int NT, bool IS_K>
 __device__ __forceinline__ void issue_tile(const uint16_t* src, int kbase, int kl, uint16_t* lds,
                                            int tid, int wave_base,
-                                           const int (&off)[CopyShape<D, BN, NT>::ROUNDS]) {
+                                           const int (&off)[CopyShape<D, BN, NT>::ROUNDS],
+                                           int rs = D) {
   constexpr int ROUNDS = CopyShape<D, BN, NT>::ROUNDS;
   const int rows = kl - kbase;
-  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(src + (int64_t)kbase * D), 0, rows * D * 2, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(src + (int64_t)kbase * rs), 0, ((min(rows, BN) - 1) * rs + D) * 2, kRsrcWord3);
   if (rows >= BN) {
 #pragma unroll
     for (int u = 0; u < ROUNDS; ++u)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rs, (lds_void*)(lds + (u * NT + wave_base) * 8), 16, off[u], 0, 0, 0);
+          rsrc, (lds_void*)(lds + (u * NT + wave_base) * 8), 16, off[u], 0, 0, 0);
   } else {
 #pragma unroll
     for (int u = 0; u < ROUNDS; ++u) {
-      const int p = u * NT + tid;
-      const int o = chunk_offset<D, IS_K>(p, min(p / (D / 8), rows - 1));
+      // (this thread's row moved back to the last valid one)
+      const int row = (u * NT + tid) / (D / 8);
+      const int o = off[u] - max(row - (rows - 1), 0) * rs * 2;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rs, (lds_void*)(lds + (u * NT + wave_base) * 8), 16, o, 0, 0, 0);
+          rsrc, (lds_void*)(lds + (u * NT + wave_base) * 8), 16, o, 0, 0, 0);
     }
   }
 }

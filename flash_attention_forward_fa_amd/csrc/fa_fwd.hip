@@ -118,6 +118,11 @@ struct FwdArgs {
   int max_blocks, block_size, n_blocks;  // paged: table width, keys per block, cache blocks
   float c;         // |scale| * log2(e), at least FLT_MIN
   uint32_t q_sign; // 0x80008000 flips the sign of both bf16 halves (scale < 0)
+  // element strides of batch, head and row (head_dim is contiguous) of Q, K,
+  // V and O; L is always contiguous [B, H, ql]
+  // (row strides are at most 2^24 elements for K and V, 2^31 - 1 for Q and O)
+  int64_t q_sb, q_sh, k_sb, k_sh, v_sb, v_sh, o_sb, o_sh;
+  int q_sr, k_sr, v_sr, o_sr;
 };
 
 
@@ -177,9 +182,10 @@ __device__ __forceinline__ bool fwd_tile(const FwdArgs& a, int qtile, int bh, ui
   const int ql = a.ql, off = PAGED ? max(kl - ql, 0) : a.causal_off;
   const int q0 = qtile * kBlockM;
   const int qw0 = q0 + wave * kRowsPerWave;
-  const int64_t kv_off = (int64_t)(b * a.Hkv + g) * kl * D;
-  const uint16_t* kp = a.k + kv_off;
-  const uint16_t* vp = a.v + kv_off;
+  const uint16_t* kp = a.k + b * a.k_sb + g * a.k_sh;
+  const uint16_t* vp = a.v + b * a.v_sb + g * a.v_sh;
+  // row strides of the K and V sources (a paged cache's rows are contiguous)
+  const int k_rs = PAGED ? D : a.k_sr, v_rs = PAGED ? D : a.v_sr;
 
   // ---- key range ----
   // (split-KV: only the keys of chunk `split`, [split*kchunk, (split+1)*kchunk))
@@ -203,8 +209,8 @@ __device__ __forceinline__ bool fwd_tile(const FwdArgs& a, int qtile, int bh, ui
   const bool compute = wave_active && (!REDO || __any(wave_redo));
 
   int koff[CopyShape<D, BN, NT>::ROUNDS], voff[CopyShape<D, BN, NT>::ROUNDS];
-  copy_offsets<D, BN, NT, true>(tid, koff);
-  copy_offsets<D, BN, NT, false>(tid, voff);
+  copy_offsets<D, BN, NT, true>(tid, koff, k_rs);
+  copy_offsets<D, BN, NT, false>(tid, voff, v_rs);
   // paged KV: when block_size is a multiple of BN a tile lies in one block,
   // table[b][kt*BN / block_size], from row (kt*BN) % block_size, and its copy
   // descriptor covers only the tile's valid rows; shorter blocks (multiples
@@ -228,7 +234,7 @@ __device__ __forceinline__ bool fwd_tile(const FwdArgs& a, int qtile, int bh, ui
         issue_tile_blocks<D, BN, NT, true>(a.k, table_row, a.n_blocks, a.Hkv, g, a.block_size,
                                            kt * BN, kl, dst, tid, 64 * wave);
     } else
-      issue_tile<D, BN, NT, true>(kp, kt * BN, kl, dst, tid, 64 * wave, koff);
+      issue_tile<D, BN, NT, true>(kp, kt * BN, kl, dst, tid, 64 * wave, koff, k_rs);
   };
   auto issue_v = [&](int kt, uint16_t* dst) {
     if constexpr (PAGED) {
@@ -239,7 +245,7 @@ __device__ __forceinline__ bool fwd_tile(const FwdArgs& a, int qtile, int bh, ui
         issue_tile_blocks<D, BN, NT, false>(a.v, table_row, a.n_blocks, a.Hkv, g, a.block_size,
                                             kt * BN, kl, dst, tid, 64 * wave);
     } else
-      issue_tile<D, BN, NT, false>(vp, kt * BN, kl, dst, tid, 64 * wave, voff);
+      issue_tile<D, BN, NT, false>(vp, kt * BN, kl, dst, tid, 64 * wave, voff, v_rs);
   };
   if (n_kt > kt_first) issue_k(kt_first, (kt_first & 1) ? k1s : k0s);
 
@@ -248,7 +254,7 @@ __device__ __forceinline__ bool fwd_tile(const FwdArgs& a, int qtile, int bh, ui
 #pragma unroll
   for (int qb = 0; qb < kQB; ++qb) {
     const int qrow = min(qw0 + 16 * qb + c16, ql - 1);
-    const uint16_t* qp = a.q + ((int64_t)bh * ql + qrow) * D + 8 * grp;
+    const uint16_t* qp = a.q + b * a.q_sb + h * a.q_sh + (int64_t)qrow * a.q_sr + 8 * grp;
 #pragma unroll
     for (int s = 0; s < NDS; ++s) {
       u32x4 raw = *reinterpret_cast<const u32x4*>(qp + 32 * s);
@@ -599,7 +605,7 @@ __device__ __forceinline__ bool fwd_tile(const FwdArgs& a, int qtile, int bh, ui
         }
         if (grp == 0) a.ws_l[prow] = lse;
       } else {
-        uint16_t* orow = a.o + ((int64_t)bh * ql + qrow) * D + 4 * grp;
+        uint16_t* orow = a.o + b * a.o_sb + h * a.o_sh + (int64_t)qrow * a.o_sr + 4 * grp;
 #pragma unroll
         for (int d = 0; d < NDB; ++d) {
           bf16x4 ov;
@@ -701,6 +707,9 @@ struct CombineArgs {
   float* l;           // f32 [rows]
   int64_t rows;       // B * H * ql
   int n_split;
+  int H, ql;
+  int64_t o_sb, o_sh;  // O's element strides of batch, head and row
+  int o_sr;
 };
 
 template <int D>
@@ -725,7 +734,9 @@ __global__ __launch_bounds__(256) void fa_combine_kernel(CombineArgs c) {
   }
   const bool empty = m == -INFINITY;
   const float inv = empty ? 0.0f : 1.0f / z;
-  uint16_t* orow = c.o + row * D + lane * P;
+  const int64_t bh = row / c.ql;
+  uint16_t* orow = c.o + (bh / c.H) * c.o_sb + (bh % c.H) * c.o_sh + (row % c.ql) * c.o_sr +
+                   lane * P;
 #pragma unroll
   for (int e = 0; e < P; ++e)
     orow[e] = __builtin_bit_cast(uint16_t, empty ? (__bf16)0.0f : (__bf16)(acc[e] * inv));
@@ -777,6 +788,11 @@ hipError_t dispatch_split(FwdArgs a, hipStream_t stream) {
   c.l = a.l;
   c.rows = (int64_t)a.B * a.H * a.ql;
   c.n_split = a.n_split;
+  c.H = a.H;
+  c.ql = a.ql;
+  c.o_sb = a.o_sb;
+  c.o_sh = a.o_sh;
+  c.o_sr = a.o_sr;
   hipLaunchKernelGGL(fa_combine_kernel<D>, dim3((unsigned)((c.rows + 3) / 4)), dim3(256), 0, stream,
                      c);
   return hipGetLastError();
@@ -834,7 +850,7 @@ int train_fwd(const void* q, const void* k, const void* v, const void* mask, int
               int64_t mask_sb, int64_t mask_sh, int batch, int n_heads, int n_kv_heads, int ql,
               int kl, int head_dim, float scale, int causal, int window, void* O, float* L,
               void* stream, int n_split = 0, void* workspace = nullptr,
-              size_t workspace_bytes = 0) {
+              size_t workspace_bytes = 0, const int64_t* strides = nullptr) {
   if (batch < 0 || ql < 0 || kl < 0 || n_heads < 1 || n_kv_heads < 1) return FA_ERR_BAD_SIZE;
   if (n_heads % n_kv_heads != 0) return FA_ERR_HEAD_GROUPING;
   if (head_dim != 64 && head_dim != 128 && head_dim != 256) return FA_ERR_HEAD_DIM;
@@ -844,6 +860,22 @@ int train_fwd(const void* q, const void* k, const void* v, const void* mask, int
                 mask_dtype != FA_MASK_BOOL) ||
                mask_sb < 0 || mask_sh < 0))
     return FA_ERR_MASK;
+  // element strides (batch, head, row) of Q, K, V, O: given, or contiguous
+  int64_t st[12] = {(int64_t)n_heads * ql * head_dim,    (int64_t)ql * head_dim, head_dim,
+                    (int64_t)n_kv_heads * kl * head_dim, (int64_t)kl * head_dim, head_dim,
+                    (int64_t)n_kv_heads * kl * head_dim, (int64_t)kl * head_dim, head_dim,
+                    (int64_t)n_heads * ql * head_dim,    (int64_t)ql * head_dim, head_dim};
+  if (strides) {
+    for (int i = 0; i < 12; ++i) {
+      if (strides[i] < 0) return FA_ERR_STRIDE;
+      // 16-byte rows for the vector loads and stores
+      if (strides[i] % 8 != 0) return FA_ERR_ALIGNMENT;
+      st[i] = strides[i];
+    }
+    // a K/V tile's rows must lie within a 32-bit buffer offset
+    if (st[5] > (1 << 24) || st[8] > (1 << 24) || st[2] > 0x7fffffffLL || st[11] > 0x7fffffffLL)
+      return FA_ERR_TOO_LARGE;
+  }
   const int64_t rows = (int64_t)batch * n_heads * ql;
   if (rows == 0) return FA_OK;
   const bool kv_used = kl > 0;
@@ -858,10 +890,17 @@ int train_fwd(const void* q, const void* k, const void* v, const void* mask, int
   // read once per group. Every such row has q_abs = kl - 1 and sees all kl
   // keys under the causal rule: the packed problem is the non-causal one. The
   // arithmetic of each row is unchanged (rows are computed independently).
+  // (with strides: the group's query heads are rows h*q_sh of the packed
+  // head, whose stride is G*q_sh; O likewise)
   if (ql == 1 && n_heads > n_kv_heads && !mask && window < 0) {
-    ql = n_heads / n_kv_heads;
+    const int G = n_heads / n_kv_heads;
+    ql = G;
     n_heads = n_kv_heads;
     causal = 0;
+    st[2] = st[1];
+    st[1] *= G;
+    st[11] = st[10];
+    st[10] *= G;
   }
   const int bm = head_dim == 64    ? block_m<64>()
                  : head_dim == 128 ? block_m<128>()
@@ -902,6 +941,10 @@ int train_fwd(const void* q, const void* k, const void* v, const void* mask, int
   // produces round to 0 in f32, so the weights are the same uniform ones).
   a.c = fmaxf(fabsf(scale) * kLog2e, FLT_MIN);
   a.q_sign = signbit(scale) ? 0x80008000u : 0u;
+  a.q_sb = st[0], a.q_sh = st[1], a.q_sr = (int)st[2];
+  a.k_sb = st[3], a.k_sh = st[4], a.k_sr = (int)st[5];
+  a.v_sb = st[6], a.v_sh = st[7], a.v_sr = (int)st[8];
+  a.o_sb = st[9], a.o_sh = st[10], a.o_sr = (int)st[11];
   a.n_split = 0;
   a.kchunk = 0;
   a.ws_o = nullptr;
@@ -1031,6 +1074,8 @@ extern "C" int fa_paged_fwd(const void* q, const void* k_cache, const void* v_ca
   a.n_qtiles = (int)n_qtiles;
   a.c = fmaxf(fabsf(scale) * kLog2e, FLT_MIN);
   a.q_sign = signbit(scale) ? 0x80008000u : 0u;
+  a.q_sb = (int64_t)H * qlen * head_dim, a.q_sh = (int64_t)qlen * head_dim, a.q_sr = head_dim;
+  a.o_sb = a.q_sb, a.o_sh = a.q_sh, a.o_sr = a.q_sr;
   a.block_table = block_table;
   a.seq_lens = seq_lens;
   a.max_blocks = max_blocks;
@@ -1067,6 +1112,29 @@ extern "C" int fa_train_fwd_ex(const void* q, const void* k, const void* v, cons
                    stream);
 }
 
+extern "C" int fa_train_fwd_strided(const void* q, const long long* q_strides, const void* k,
+                                    const long long* k_strides, const void* v,
+                                    const long long* v_strides, int batch, int n_heads,
+                                    int n_kv_heads, int ql, int kl, int head_dim, float scale,
+                                    int causal, int window, int n_split, void* workspace,
+                                    unsigned long workspace_bytes, void* O,
+                                    const long long* o_strides, float* L, void* stream) {
+  if (n_split < 0 || n_split > kMaxSplit) return FA_ERR_SPLIT;
+  if (n_split > 0 && window >= 0) return FA_ERR_WINDOW;
+  const long long* given[4] = {q_strides, k_strides, v_strides, o_strides};
+  const long long hq = (long long)ql * head_dim, hk = (long long)kl * head_dim;
+  const long long dflt[4][3] = {{hq * n_heads, hq, head_dim},
+                                {hk * n_kv_heads, hk, head_dim},
+                                {hk * n_kv_heads, hk, head_dim},
+                                {hq * n_heads, hq, head_dim}};
+  int64_t st[12];
+  for (int t = 0; t < 4; ++t)
+    for (int i = 0; i < 3; ++i) st[3 * t + i] = given[t] ? given[t][i] : dflt[t][i];
+  return train_fwd(q, k, v, nullptr, FA_MASK_F32, 0, 0, batch, n_heads, n_kv_heads, ql, kl,
+                   head_dim, scale, causal, window, O, L, stream, n_split, workspace,
+                   workspace_bytes, st);
+}
+
 extern "C" const char* fa_status_string(int status) {
   switch (status) {
     case FA_OK: return "ok";
@@ -1083,6 +1151,7 @@ extern "C" const char* fa_status_string(int status) {
     case FA_ERR_MASK: return "mask dtype must be FA_MASK_F32, FA_MASK_BF16 or FA_MASK_BOOL, strides >= 0";
     case FA_ERR_SPLIT: return "n_split must be in 1..65536 and the workspace large enough";
     case FA_ERR_PAGED: return "block_size must be a positive multiple of 16 and the cache non-empty";
+    case FA_ERR_STRIDE: return "strides must be >= 0";
     default: return "unknown status";
   }
 }

@@ -44,8 +44,9 @@ enum fa_status {
                                   mask stride                                           */
     FA_ERR_SPLIT = 11,         /* fa_train_fwd_split: n_split outside 1..65536, or the
                                   workspace smaller than the split needs                */
-    FA_ERR_PAGED = 12          /* fa_paged_fwd: block_size not a positive multiple of
+    FA_ERR_PAGED = 12,         /* fa_paged_fwd: block_size not a positive multiple of
                                   16, or no cache blocks for a non-empty table          */
+    FA_ERR_STRIDE = 13         /* fa_train_fwd_strided: a negative stride               */
 };
 
 /* Element types of an additive mask (fa_train_fwd_ex). */
@@ -150,6 +151,37 @@ int fa_train_fwd_ex(const void *q, const void *k, const void *v, const void *mas
                     int mask_dtype, long long mask_stride_b, long long mask_stride_h, int batch,
                     int n_heads, int n_kv_heads, int ql, int kl, int head_dim, float scale,
                     int causal, int window, void *O, float *L, void *stream);
+
+/*
+ * fa_train_fwd_strided - fa_train_fwd_ex (without a mask) on strided views of
+ * Q, K, V and O, such as the sequence-major layout [batch, len, heads,
+ * head_dim] that an adjacent attention API on the pages passes as transposed
+ * views ("nuvec-core 0.3.0", tests/fast.rs, attention_kernels_match_the_fallback,
+ * K and V given as views of [B, L, H, D]).
+ *
+ *   q_strides, k_strides, v_strides, o_strides
+ *               host arrays of 3 element strides each: batch, head, row. Element
+ *               (b, h, i, d) of Q is q[b*q_strides[0] + h*q_strides[1] +
+ *               i*q_strides[2] + d]; head_dim is contiguous. Every stride is a
+ *               multiple of 8 elements (16-byte rows; FA_ERR_ALIGNMENT
+ *               otherwise) and >= 0 (FA_ERR_STRIDE); K and V row strides at most
+ *               2^24 elements (FA_ERR_TOO_LARGE). NULL: that tensor contiguous.
+ *               O's rows must not overlap one another or the inputs.
+ *   L           f32 [batch, n_heads, ql], contiguous, as for fa_train_fwd.
+ *   window      as for fa_train_fwd_ex (< 0: none; >= 0 needs causal).
+ *   n_split     0: one launch; >= 1: split-KV with workspace, as for
+ *               fa_train_fwd_split.
+ *   others      as for fa_train_fwd.
+ *
+ * With all four strides NULL this is fa_train_fwd_ex without a mask (or
+ * fa_train_fwd_split with n_split >= 1), bit for bit.
+ */
+int fa_train_fwd_strided(const void *q, const long long *q_strides, const void *k,
+                         const long long *k_strides, const void *v, const long long *v_strides,
+                         int batch, int n_heads, int n_kv_heads, int ql, int kl, int head_dim,
+                         float scale, int causal, int window, int n_split, void *workspace,
+                         unsigned long workspace_bytes, void *O, const long long *o_strides,
+                         float *L, void *stream);
 
 /*
  * fa_train_fwd_split - the forward of fa_train_fwd (no mask, causal or not)
