@@ -56,6 +56,9 @@ def lib():
                                            ctypes.c_float, ci, ci, ci, vp, ctypes.c_ulong, vp,
                                            pll, vp, vp]
         l.fa_train_fwd_strided.restype = ci
+        l.fa_train_bwd_strided.argtypes = [vp, vp, vp, vp, vp, vp, pll, pll, ci, ci, ci, ci, ci,
+                                           ci, ctypes.c_float, ci, ci, vp, vp, vp, vp]
+        l.fa_train_bwd_strided.restype = ci
         ul = ctypes.c_ulong
         l.fa_train_fwd_split.argtypes = [vp, vp, vp, ci, ci, ci, ci, ci, ci, ctypes.c_float, ci,
                                          ci, vp, ul, vp, vp, vp]
@@ -321,6 +324,57 @@ def train_fwd_strided(q, k, v, scale=None, causal=False, window=None, n_split=0,
     if status != 0:
         raise FAError(status, status_string(status))
     return O, L
+
+
+def fa_train_bwd_strided(q, k, v, O, L, dO, q_strides, kv_strides, batch, n_heads, n_kv_heads,
+                         ql, kl, head_dim, scale, causal, window, dQ, dK, dV, stream):
+    """The C entry point with raw integer pointers (0 for NULL) and stride
+    triples (or None); returns the status."""
+    return lib().fa_train_bwd_strided(
+        q or None, k or None, v or None, O or None, L or None, dO or None, _strides3(q_strides),
+        _strides3(kv_strides), batch, n_heads, n_kv_heads, ql, kl, head_dim, float(scale),
+        int(bool(causal)), int(window), dQ or None, dK or None, dV or None, stream or None)
+
+
+def train_bwd_strided(q, k, v, O, L, dO, scale=None, causal=False, window=None, stream=None):
+    """dQ, dK, dV = train_bwd_strided(q, k, v, O, L, dO, scale=None, causal=False,
+                                      window=None)
+
+    The backward on strided views: O and dO must have q's strides, v k's
+    (head_dim contiguous); dQ comes in q's layout, dK and dV in k's.
+    """
+    import torch
+    for name, t in (("q", q), ("k", k), ("v", v), ("O", O), ("dO", dO)):
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.bfloat16:
+            raise TypeError(f"{name} must be a bfloat16 tensor")
+        if t.dim() != 4 or t.stride(3) != 1 or not t.is_cuda or t.device != q.device:
+            raise ValueError(f"{name} must be a 4-d tensor with contiguous head_dim on q's GPU")
+    B, H, ql, D = q.shape
+    Bk, Hkv, kl, Dk = k.shape
+    if tuple(v.shape) != tuple(k.shape) or Bk != B or Dk != D:
+        raise ValueError("k and v must be [B, Hkv, kl, D] with q's B and D")
+    if O.shape != q.shape or dO.shape != q.shape:
+        raise ValueError("O and dO must be shaped like q")
+    if O.stride() != q.stride() or dO.stride() != q.stride() or v.stride() != k.stride():
+        raise ValueError("O and dO need q's strides, v needs k's")
+    if (L.dtype != torch.float32 or tuple(L.shape) != (B, H, ql) or not L.is_contiguous()
+            or L.device != q.device):
+        raise ValueError("L must be a contiguous f32 tensor [B, H, ql] on q's device")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    dQ = torch.empty_strided(q.shape, q.stride(), dtype=torch.bfloat16, device=q.device)
+    dK = torch.empty_strided(k.shape, k.stride(), dtype=torch.bfloat16, device=q.device)
+    dV = torch.empty_strided(k.shape, k.stride(), dtype=torch.bfloat16, device=q.device)
+    s = stream if stream is not None else torch.cuda.current_stream(q.device)
+    with torch.cuda.device(q.device):
+        status = fa_train_bwd_strided(
+            q.data_ptr(), k.data_ptr(), v.data_ptr(), O.data_ptr(), L.data_ptr(), dO.data_ptr(),
+            q.stride()[:3], k.stride()[:3], B, H, Hkv, ql, kl, D, scale, causal,
+            -1 if window is None else window, dQ.data_ptr(), dK.data_ptr(), dV.data_ptr(),
+            s.cuda_stream)
+    if status != 0:
+        raise FAError(status, status_string(status))
+    return dQ, dK, dV
 
 
 def _fwd_outputs(q, k, v, scale, out, lse, stream):

@@ -87,6 +87,10 @@ struct BwdArgs {
   int window;        // WINDOW variants: keys below q_abs - window are hidden
   float scale;       // signed softmax scale (multiplies dQ and dK)
   float c;           // scale * log2(e), never 0 (exp2 argument factor)
+  // element strides of batch, head and row (head_dim contiguous): q_* for Q,
+  // O, dO and dQ, k_* for K, V, dK and dV; L is contiguous [B, H, ql]
+  int64_t q_sb, q_sh, k_sb, k_sh;
+  int q_sr, k_sr;
 };
 
 // log2-units logsumexp of a row; a row with no visible key (L = -inf) gets
@@ -143,9 +147,12 @@ __attribute__((amdgpu_waves_per_eu(BwdCfg<D, PASS>::WPE))) void fa_bwd_kernel(Bw
   const int fw0 = f0 + (wave % (C::W / DS)) * 16 * FB;  // this wave's first fixed row
   const bool wave_active = fw0 < nfixed;
 
-  const int64_t kv_base = (int64_t)(b * a.Hkv + g) * kl * D;
-  const uint16_t* x1p = KV ? a.k + kv_base : a.q + (int64_t)fhead * ql * D;
-  const uint16_t* x2p = KV ? a.v + kv_base : a.dO + (int64_t)fhead * ql * D;
+  const int64_t kv_base = b * a.k_sb + g * a.k_sh;
+  const int64_t qh_base = b * a.q_sb + hf * a.q_sh;  // dQ pass: the fixed query head
+  const uint16_t* x1p = KV ? a.k + kv_base : a.q + qh_base;
+  const uint16_t* x2p = KV ? a.v + kv_base : a.dO + qh_base;
+  const int xr = KV ? a.k_sr : a.q_sr;  // row strides of the fixed and streamed rows
+  const int yr = KV ? a.q_sr : a.k_sr;
 
   // ---- fixed rows as B operands: block fb, step s: row fw0+16fb+c16, dims 32s+8grp.. ----
   bf16x8 x1op[FB][NDS], x2op[FB][NDS];
@@ -155,9 +162,9 @@ __attribute__((amdgpu_waves_per_eu(BwdCfg<D, PASS>::WPE))) void fa_bwd_kernel(Bw
 #pragma unroll
     for (int s = 0; s < NDS; ++s) {
       x1op[fb][s] = __builtin_bit_cast(
-          bf16x8, *reinterpret_cast<const u32x4*>(x1p + (int64_t)r * D + 32 * s + 8 * grp));
+          bf16x8, *reinterpret_cast<const u32x4*>(x1p + (int64_t)r * xr + 32 * s + 8 * grp));
       x2op[fb][s] = __builtin_bit_cast(
-          bf16x8, *reinterpret_cast<const u32x4*>(x2p + (int64_t)r * D + 32 * s + 8 * grp));
+          bf16x8, *reinterpret_cast<const u32x4*>(x2p + (int64_t)r * xr + 32 * s + 8 * grp));
     }
   }
   // dQ pass: L2 and D of the fixed rows (D from the same dims as the dO operand,
@@ -171,7 +178,7 @@ __attribute__((amdgpu_waves_per_eu(BwdCfg<D, PASS>::WPE))) void fa_bwd_kernel(Bw
 #pragma unroll
       for (int s = 0; s < NDS; ++s) {
         const bf16x8 ov = __builtin_bit_cast(
-            bf16x8, *reinterpret_cast<const u32x4*>(a.o + ((int64_t)fhead * ql + r) * D + 32 * s +
+            bf16x8, *reinterpret_cast<const u32x4*>(a.o + qh_base + (int64_t)r * a.q_sr + 32 * s +
                                                      8 * grp));
 #pragma unroll
         for (int e = 0; e < 8; ++e) part += (float)ov[e] * (float)x2op[fb][s][e];
@@ -213,23 +220,24 @@ __attribute__((amdgpu_waves_per_eu(BwdCfg<D, PASS>::WPE))) void fa_bwd_kernel(Bw
   auto tile_head = [&](int t) { return KV ? g * a.group + t / n_per : hf; };
   auto tile_first = [&](int t) { return (st_lo + (KV ? t % n_per : t)) * BN; };
   auto y1_src = [&](int t) -> const uint16_t* {
-    return KV ? a.q + (int64_t)(b * a.H + tile_head(t)) * ql * D : a.k + kv_base;
+    return KV ? a.q + b * a.q_sb + tile_head(t) * a.q_sh : a.k + kv_base;
   };
   auto y2_src = [&](int t) -> const uint16_t* {
-    return KV ? a.dO + (int64_t)(b * a.H + tile_head(t)) * ql * D : a.v + kv_base;
+    return KV ? a.dO + b * a.q_sb + tile_head(t) * a.q_sh : a.v + kv_base;
   };
 
   int y1off[CopyShape<D, BN, NT>::ROUNDS], y2off[CopyShape<D, BN, NT>::ROUNDS];
-  copy_offsets<D, BN, NT, true>(tid, y1off);
-  copy_offsets<D, BN, NT, false>(tid, y2off);
+  copy_offsets<D, BN, NT, true>(tid, y1off, yr);
+  copy_offsets<D, BN, NT, false>(tid, y2off, yr);
   auto issue = [&](int t) {
     const int buf = t & 1;
-    issue_tile<D, BN, NT, true>(y1_src(t), tile_first(t), nstream, y1s[buf], tid, 64 * wave, y1off);
+    issue_tile<D, BN, NT, true>(y1_src(t), tile_first(t), nstream, y1s[buf], tid, 64 * wave, y1off,
+                                yr);
     issue_tile<D, BN, NT, false>(y2_src(t), tile_first(t), nstream, y2s[buf], tid, 64 * wave,
-                                 y2off);
+                                 y2off, yr);
     if constexpr (KV)
-      issue_tile<D, BN, NT, false>(a.o + (int64_t)(b * a.H + tile_head(t)) * ql * D, tile_first(t),
-                                   nstream, yos[buf], tid, 64 * wave, y2off);
+      issue_tile<D, BN, NT, false>(a.o + b * a.q_sb + tile_head(t) * a.q_sh, tile_first(t),
+                                   nstream, yos[buf], tid, 64 * wave, y2off, yr);
   };
   // dKV pass: L2 and D of the streamed rows of tile t (landed in LDS) into
   // srow (NT / BN threads per row, each summing D / (NT / BN) dims of O * dO)
@@ -421,7 +429,7 @@ __attribute__((amdgpu_waves_per_eu(BwdCfg<D, PASS>::WPE))) void fa_bwd_kernel(Bw
   for (int fb = 0; fb < FB; ++fb) {
     const int frow = fw0 + 16 * fb + c16;
     if (!(wave_active && frow < nfixed)) continue;
-    uint16_t* d1 = KV ? a.dk + kv_base + (int64_t)frow * D : a.dq + ((int64_t)fhead * ql + frow) * D;
+    uint16_t* d1 = (KV ? a.dk + kv_base : a.dq + qh_base) + (int64_t)frow * xr;
 #pragma unroll
     for (int da = 0; da < NDA; ++da) {
       const int d = dpart * NDA + da;
@@ -431,7 +439,7 @@ __attribute__((amdgpu_waves_per_eu(BwdCfg<D, PASS>::WPE))) void fa_bwd_kernel(Bw
       *reinterpret_cast<bf16x4*>(d1 + 16 * d + 4 * grp) = ov;
     }
     if constexpr (KV) {
-      uint16_t* d2 = a.dv + kv_base + (int64_t)frow * D;
+      uint16_t* d2 = a.dv + kv_base + (int64_t)frow * xr;
 #pragma unroll
       for (int da = 0; da < NDA; ++da) {
         const int d = dpart * NDA + da;
@@ -494,7 +502,8 @@ bool aligned_to(const void* p, uintptr_t n) { return ((uintptr_t)p % n) == 0; }
 int train_bwd(const void* q, const void* k, const void* v, const void* mask, int mask_dtype,
               int64_t mask_sb, int64_t mask_sh, const void* O, const float* L, const void* dO,
               int batch, int n_heads, int n_kv_heads, int ql, int kl, int head_dim, float scale,
-              int causal, int window, void* dQ, void* dK, void* dV, void* stream) {
+              int causal, int window, void* dQ, void* dK, void* dV, void* stream,
+              const int64_t* q_strides = nullptr, const int64_t* k_strides = nullptr) {
   if (batch < 0 || ql < 0 || kl < 0 || n_heads < 1 || n_kv_heads < 1) return FA_ERR_BAD_SIZE;
   if (n_heads % n_kv_heads != 0) return FA_ERR_HEAD_GROUPING;
   if (head_dim != 64 && head_dim != 128 && head_dim != 256) return FA_ERR_HEAD_DIM;
@@ -504,6 +513,17 @@ int train_bwd(const void* q, const void* k, const void* v, const void* mask, int
                 mask_dtype != FA_MASK_BOOL) ||
                mask_sb < 0 || mask_sh < 0))
     return FA_ERR_MASK;
+  // element strides (batch, head, row) of the Q-shaped and K-shaped tensors
+  int64_t qs[3] = {(int64_t)n_heads * ql * head_dim, (int64_t)ql * head_dim, head_dim};
+  int64_t ks[3] = {(int64_t)n_kv_heads * kl * head_dim, (int64_t)kl * head_dim, head_dim};
+  for (int i = 0; i < 3; ++i) {
+    if (q_strides) qs[i] = q_strides[i];
+    if (k_strides) ks[i] = k_strides[i];
+    if (qs[i] < 0 || ks[i] < 0) return FA_ERR_STRIDE;
+    if (qs[i] % 8 != 0 || ks[i] % 8 != 0) return FA_ERR_ALIGNMENT;  // 16-byte rows
+  }
+  // a streamed tile's rows must lie within a 32-bit buffer offset
+  if (qs[2] > (1 << 24) || ks[2] > (1 << 24)) return FA_ERR_TOO_LARGE;
   const int64_t qrows = (int64_t)batch * n_heads * ql;
   const int64_t krows = (int64_t)batch * n_kv_heads * kl;
   if (qrows == 0 && krows == 0) return FA_OK;
@@ -555,6 +575,8 @@ int train_bwd(const void* q, const void* k, const void* v, const void* mask, int
   // q_abs - window stays in int range)
   a.window = window >= 0 ? (int)std::min<int64_t>(window, (int64_t)a.causal_off + ql) : 0;
   a.scale = scale;
+  a.q_sb = qs[0], a.q_sh = qs[1], a.q_sr = (int)qs[2];
+  a.k_sb = ks[0], a.k_sh = ks[1], a.k_sr = (int)ks[2];
   // a zero scale runs with the smallest normal exp2 factor (the scores it
   // produces round to 0, so P is the same uniform one); dQ and dK use the
   // true scale and come out 0
@@ -600,4 +622,20 @@ extern "C" int fa_train_bwd_ex(const void* q, const void* k, const void* v, cons
   return train_bwd(q, k, v, mask, mask_dtype, mask_stride_b, mask_stride_h, O, L, dO, batch,
                    n_heads, n_kv_heads, ql, kl, head_dim, scale, causal, window < 0 ? -1 : window,
                    dQ, dK, dV, stream);
+}
+
+extern "C" int fa_train_bwd_strided(const void* q, const void* k, const void* v, const void* O,
+                                    const float* L, const void* dO, const long long* q_strides,
+                                    const long long* kv_strides, int batch, int n_heads,
+                                    int n_kv_heads, int ql, int kl, int head_dim, float scale,
+                                    int causal, int window, void* dQ, void* dK, void* dV,
+                                    void* stream) {
+  int64_t qs[3], ks[3];
+  for (int i = 0; i < 3; ++i) {
+    if (q_strides) qs[i] = q_strides[i];
+    if (kv_strides) ks[i] = kv_strides[i];
+  }
+  return train_bwd(q, k, v, nullptr, FA_MASK_F32, 0, 0, O, L, dO, batch, n_heads, n_kv_heads, ql,
+                   kl, head_dim, scale, causal, window, dQ, dK, dV, stream,
+                   q_strides ? qs : nullptr, kv_strides ? ks : nullptr);
 }

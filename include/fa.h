@@ -46,7 +46,8 @@ enum fa_status {
                                   workspace smaller than the split needs                */
     FA_ERR_PAGED = 12,         /* fa_paged_fwd: block_size not a positive multiple of
                                   16, or no cache blocks for a non-empty table          */
-    FA_ERR_STRIDE = 13         /* fa_train_fwd_strided: a negative stride               */
+    FA_ERR_STRIDE = 13         /* fa_train_fwd_strided, fa_train_bwd_strided: a negative
+                                  stride                                                */
 };
 
 /* Element types of an additive mask (fa_train_fwd_ex). */
@@ -334,6 +335,29 @@ int fa_train_bwd_ex(const void *q, const void *k, const void *v, const void *mas
                     const void *O, const float *L, const void *dO, int batch, int n_heads,
                     int n_kv_heads, int ql, int kl, int head_dim, float scale, int causal,
                     int window, void *dQ, void *dK, void *dV, void *stream);
+
+/*
+ * fa_train_bwd_strided - the backward of fa_train_fwd_strided (no mask): the
+ * tensors may be strided views with head_dim contiguous, in two layouts.
+ *
+ *   q_strides   host array of 3 element strides (batch, head, row) shared by
+ *               Q, O, dO and dQ (the gradient is written in Q's layout);
+ *               NULL: contiguous [batch, n_heads, ql, head_dim]
+ *   kv_strides  the same for K, V, dK and dV; NULL: contiguous
+ *   L           f32 [batch, n_heads, ql], contiguous
+ *   window      as for fa_train_bwd_ex (< 0: none; >= 0 needs causal)
+ *   others      as for fa_train_bwd.
+ *
+ * Strides are multiples of 8 elements (FA_ERR_ALIGNMENT otherwise) and >= 0
+ * (FA_ERR_STRIDE); row strides at most 2^24 elements (FA_ERR_TOO_LARGE). The
+ * gradients' rows must not overlap each other or the inputs. With both
+ * strides NULL this is fa_train_bwd_ex without a mask, bit for bit.
+ */
+int fa_train_bwd_strided(const void *q, const void *k, const void *v, const void *O,
+                         const float *L, const void *dO, const long long *q_strides,
+                         const long long *kv_strides, int batch, int n_heads, int n_kv_heads,
+                         int ql, int kl, int head_dim, float scale, int causal, int window,
+                         void *dQ, void *dK, void *dV, void *stream);
 
 /* Static, human-readable name of a status code (never NULL). */
 const char *fa_status_string(int status);

@@ -30,7 +30,8 @@ def test_header_declares_the_entry_points():
     names = _declared_functions()
     assert {"fa_train_fwd", "fa_train_fwd_swa", "fa_train_fwd_ex", "fa_train_fwd_split",
             "fa_train_fwd_split_workspace", "fa_paged_fwd", "fa_train_bwd", "fa_train_bwd_swa",
-            "fa_train_bwd_ex", "fa_train_fwd_strided", "fa_status_string"} <= names
+            "fa_train_bwd_ex", "fa_train_fwd_strided", "fa_train_bwd_strided",
+            "fa_status_string"} <= names
 
 
 def test_library_exports_every_declared_symbol():
@@ -303,3 +304,20 @@ def test_strided_invalid_arguments_are_rejected(over, code):
 
 def test_strided_status_string():
     assert "stride" in fa.status_string(13)
+
+
+BWD_STRIDED_GOOD = dict(q=A, k=A, v=A, O=A, L=A, dO=A, q_strides=None, kv_strides=None, batch=1,
+                        n_heads=4, n_kv_heads=2, ql=8, kl=8, head_dim=64, scale=0.125, causal=1,
+                        window=-1, dQ=A, dK=A, dV=A, stream=0)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(q_strides=(-8, 512, 64)), 13), (dict(kv_strides=(0, 0, -64)), 13),
+    (dict(kv_strides=(4096, 64, 12)), 6), (dict(q_strides=(4, 512, 64)), 6),
+    (dict(q_strides=(0, 0, 1 << 25)), 7), (dict(causal=0, window=3), 9), (dict(head_dim=96), 4),
+    (dict(dQ=0), 1),
+])
+def test_bwd_strided_invalid_arguments_are_rejected(over, code):
+    args = dict(BWD_STRIDED_GOOD)
+    args.update(over)
+    assert fa.fa_train_bwd_strided(**args) == code

@@ -113,3 +113,35 @@ def test_strided_errors_raise_from_binding():
     with pytest.raises(fa.FAError) as e:   # row stride 68: not 16-byte rows
         fa.train_fwd_strided(odd.transpose(1, 2), q, q)
     assert e.value.status == 6
+
+
+BWD_CASES = [
+    # (B, H, Hkv, ql, kl, D, causal, window)
+    (2, 4, 2, 300, 300, 64, True, None),
+    (1, 4, 4, 77, 200, 64, False, None),
+    (2, 8, 2, 200, 260, 128, True, None),
+    (1, 4, 1, 129, 129, 256, True, None),
+    (1, 4, 2, 333, 333, 64, True, 100),
+    (1, 2, 2, 150, 300, 256, True, 64),
+]
+
+
+@pytest.mark.parametrize("B,H,Hkv,ql,kl,D,causal,window", BWD_CASES)
+def test_backward_on_bshd_views_equals_contiguous(B, H, Hkv, ql, kl, D, causal, window):
+    """fa_train_bwd_strided on [B, L, H, D] views of Q, K, V, O, dO gives the
+    contiguous backward's dQ, dK, dV bits (written in the views' layout)."""
+    import torch
+    import flash_attention_forward_fa_amd as fa
+    case = (B, H, Hkv, ql, kl, D, causal, window)
+    print(f"case strided bwd {case}", flush=True)
+    seed = fagen.SEED_BASE + 14200 + BWD_CASES.index(case)
+    q, k, v = _inputs(seed, B, H, Hkv, ql, kl, D)
+    dO = gu.to_dev(fagen.normal_bf16(seed, 6, (B, H, ql, D)), "cuda:0")
+    O, L = fa.train_fwd_ex(q, k, v, causal=causal, window=window)
+    ref = fa.train_bwd_ex(q, k, v, O, L, dO, causal=causal, window=window)
+    qs, ks, vs, Os, dOs = (_bshd(x) for x in (q, k, v, O, dO))
+    got = fa.train_bwd_strided(qs, ks, vs, Os, L, dOs, causal=causal, window=window)
+    torch.cuda.synchronize()
+    assert got[0].stride() == qs.stride() and got[1].stride() == ks.stride()
+    for x, y in zip(ref, got):
+        assert torch.equal(x.view(torch.int16), y.contiguous().view(torch.int16))
