@@ -16,7 +16,10 @@
  *     L[b,h,i]   = log(sum_j exp(s_j))        over visible keys (-inf if none)
  *     O[b,h,i,:] = sum_j exp(s_j - L[b,h,i]) * v[b,g,j,:]        (0 if none)
  *
- * All tensors are contiguous row-major, in device memory owned by the caller.
+ * Tensors are contiguous row-major unless an entry point takes strides
+ * (fa_train_fwd_ex and fa_train_bwd_ex for the mask; fa_train_fwd_strided and
+ * fa_train_bwd_strided for Q, K, V, O and the gradients), in device memory
+ * owned by the caller (the split-KV workspace included).
  * The library allocates nothing, keeps no global mutable state and never
  * synchronises: work is enqueued on `stream` and the call returns.
  */
