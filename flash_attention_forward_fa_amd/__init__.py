@@ -52,12 +52,13 @@ def lib():
                                       ctypes.c_float, ci, ci, vp, vp, vp]
         l.fa_train_fwd_ex.restype = ci
         pll = ctypes.POINTER(ctypes.c_longlong)
-        l.fa_train_fwd_strided.argtypes = [vp, pll, vp, pll, vp, pll, ci, ci, ci, ci, ci, ci,
+        l.fa_train_fwd_strided.argtypes = [vp, pll, vp, pll, vp, pll, vp, ci, pll, ci, ci, ci, ci,
+                                           ci, ci,
                                            ctypes.c_float, ci, ci, ci, vp, ctypes.c_ulong, vp,
                                            pll, vp, vp]
         l.fa_train_fwd_strided.restype = ci
-        l.fa_train_bwd_strided.argtypes = [vp, vp, vp, vp, vp, vp, pll, pll, ci, ci, ci, ci, ci,
-                                           ci, ctypes.c_float, ci, ci, vp, vp, vp, vp]
+        l.fa_train_bwd_strided.argtypes = [vp, vp, vp, vp, vp, vp, pll, pll, vp, ci, pll, ci, ci,
+                                           ci, ci, ci, ci, ctypes.c_float, ci, ci, vp, vp, vp, vp]
         l.fa_train_bwd_strided.restype = ci
         ul = ctypes.c_ulong
         l.fa_train_fwd_split.argtypes = [vp, vp, vp, ci, ci, ci, ci, ci, ci, ctypes.c_float, ci,
@@ -265,28 +266,54 @@ def _strides3(st):
     return (ctypes.c_longlong * 3)(*(int(x) for x in st))
 
 
-def fa_train_fwd_strided(q, q_strides, k, k_strides, v, v_strides, batch, n_heads, n_kv_heads,
-                         ql, kl, head_dim, scale, causal, window, n_split, workspace,
-                         workspace_bytes, O, o_strides, L, stream):
+def fa_train_fwd_strided(q, q_strides, k, k_strides, v, v_strides, mask, mask_dtype,
+                         mask_strides, batch, n_heads, n_kv_heads, ql, kl, head_dim, scale, causal,
+                         window, n_split, workspace, workspace_bytes, O, o_strides, L, stream):
     """The C entry point with raw integer pointers (0 for NULL) and stride
     triples (or None); returns the status."""
     return lib().fa_train_fwd_strided(
         q or None, _strides3(q_strides), k or None, _strides3(k_strides), v or None,
-        _strides3(v_strides), batch, n_heads, n_kv_heads, ql, kl, head_dim, float(scale),
+        _strides3(v_strides), mask or None, int(mask_dtype), _strides3(mask_strides), batch,
+        n_heads, n_kv_heads, ql, kl, head_dim, float(scale),
         int(bool(causal)), int(window), int(n_split), workspace or None, int(workspace_bytes),
         O or None, _strides3(o_strides), L or None, stream or None)
 
 
-def train_fwd_strided(q, k, v, scale=None, causal=False, window=None, n_split=0, workspace=None,
-                      out=None, lse=None, stream=None):
+def _mask_view(mask, q, k):
+    """(pointer, dtype code, strides) of a mask view [B or 1, H or 1, ql, kl]
+    with contiguous keys (any row stride), or (0, 0, None) for none."""
+    import torch
+    if mask is None:
+        return 0, FA_MASK_F32, None
+    if not isinstance(mask, torch.Tensor) or mask.dtype not in (torch.float32, torch.bfloat16,
+                                                                 torch.bool):
+        raise ValueError("mask must be float32, bfloat16 or bool")
+    B, H, ql, _ = q.shape
+    kl = k.shape[2]
+    if (mask.dim() != 4 or mask.shape[0] not in (1, B) or mask.shape[1] not in (1, H)
+            or tuple(mask.shape[2:]) != (ql, kl)):
+        raise ValueError(f"mask must have shape [B or 1, H or 1, {ql}, {kl}]")
+    if kl > 1 and mask.stride(3) != 1:
+        raise ValueError("the mask's keys must be contiguous")
+    if mask.device != q.device:
+        raise ValueError("mask must be on q's device")
+    st = (mask.stride(0) if mask.shape[0] > 1 else 0, mask.stride(1) if mask.shape[1] > 1 else 0,
+          mask.stride(2) if ql > 1 else kl)
+    code = {torch.bfloat16: FA_MASK_BF16, torch.bool: FA_MASK_BOOL}.get(mask.dtype, FA_MASK_F32)
+    return mask.data_ptr(), code, st
+
+
+def train_fwd_strided(q, k, v, mask=None, scale=None, causal=False, window=None, n_split=0,
+                      workspace=None, out=None, lse=None, stream=None):
     """O, L = train_fwd_strided(q, k, v, scale=None, causal=False, window=None, n_split=0)
 
     The forward on strided views: q [B, H, ql, D], k and v [B, Hkv, kl, D] and
     out (optional, else a new contiguous tensor) may have any non-negative
     strides in their first three dimensions (multiples of 8 elements) with
     head_dim contiguous, e.g. q = x.transpose(1, 2) for x of layout
-    [B, ql, H, D]. L is contiguous [B, H, ql]. n_split > 0 runs split-KV (its
-    workspace allocated here when None).
+    [B, ql, H, D]. L is contiguous [B, H, ql]. mask: as for train_fwd_ex, any
+    view whose keys are contiguous (e.g. a slice [..., :ql, :kl] of a larger
+    mask). n_split > 0 runs split-KV (its workspace allocated here when None).
     """
     import torch
     for name, t in (("q", q), ("k", k), ("v", v)):
@@ -315,9 +342,11 @@ def train_fwd_strided(q, k, v, scale=None, causal=False, window=None, n_split=0,
         ws_bytes = workspace.numel() * workspace.element_size()
     s = stream if stream is not None else torch.cuda.current_stream(q.device)
     st = lambda t: t.stride()[:3]
+    mptr, mdt, mst = _mask_view(mask, q, k)
     with torch.cuda.device(q.device):
         status = fa_train_fwd_strided(
-            q.data_ptr(), st(q), k.data_ptr(), st(k), v.data_ptr(), st(v), B, H, Hkv, ql, kl, D,
+            q.data_ptr(), st(q), k.data_ptr(), st(k), v.data_ptr(), st(v), mptr, mdt, mst,
+            B, H, Hkv, ql, kl, D,
             scale, causal, -1 if window is None else window, n_split,
             workspace.data_ptr() if workspace is not None else 0, ws_bytes, O.data_ptr(), st(O),
             L.data_ptr(), s.cuda_stream)
@@ -326,17 +355,19 @@ def train_fwd_strided(q, k, v, scale=None, causal=False, window=None, n_split=0,
     return O, L
 
 
-def fa_train_bwd_strided(q, k, v, O, L, dO, q_strides, kv_strides, batch, n_heads, n_kv_heads,
-                         ql, kl, head_dim, scale, causal, window, dQ, dK, dV, stream):
+def fa_train_bwd_strided(q, k, v, O, L, dO, q_strides, kv_strides, mask, mask_dtype,
+                         mask_strides, batch, n_heads, n_kv_heads, ql, kl, head_dim, scale, causal,
+                         window, dQ, dK, dV, stream):
     """The C entry point with raw integer pointers (0 for NULL) and stride
     triples (or None); returns the status."""
     return lib().fa_train_bwd_strided(
         q or None, k or None, v or None, O or None, L or None, dO or None, _strides3(q_strides),
-        _strides3(kv_strides), batch, n_heads, n_kv_heads, ql, kl, head_dim, float(scale),
+        _strides3(kv_strides), mask or None, int(mask_dtype), _strides3(mask_strides), batch, n_heads, n_kv_heads, ql, kl, head_dim, float(scale),
         int(bool(causal)), int(window), dQ or None, dK or None, dV or None, stream or None)
 
 
-def train_bwd_strided(q, k, v, O, L, dO, scale=None, causal=False, window=None, stream=None):
+def train_bwd_strided(q, k, v, O, L, dO, mask=None, scale=None, causal=False, window=None,
+                      stream=None):
     """dQ, dK, dV = train_bwd_strided(q, k, v, O, L, dO, scale=None, causal=False,
                                       window=None)
 
@@ -366,10 +397,11 @@ def train_bwd_strided(q, k, v, O, L, dO, scale=None, causal=False, window=None, 
     dK = torch.empty_strided(k.shape, k.stride(), dtype=torch.bfloat16, device=q.device)
     dV = torch.empty_strided(k.shape, k.stride(), dtype=torch.bfloat16, device=q.device)
     s = stream if stream is not None else torch.cuda.current_stream(q.device)
+    mptr, mdt, mst = _mask_view(mask, q, k)
     with torch.cuda.device(q.device):
         status = fa_train_bwd_strided(
             q.data_ptr(), k.data_ptr(), v.data_ptr(), O.data_ptr(), L.data_ptr(), dO.data_ptr(),
-            q.stride()[:3], k.stride()[:3], B, H, Hkv, ql, kl, D, scale, causal,
+            q.stride()[:3], k.stride()[:3], mptr, mdt, mst, B, H, Hkv, ql, kl, D, scale, causal,
             -1 if window is None else window, dQ.data_ptr(), dK.data_ptr(), dV.data_ptr(),
             s.cuda_stream)
     if status != 0:

@@ -77,6 +77,7 @@ struct BwdArgs {
   const float* L;
   const void* mask;          // f32, bf16 or bool bytes (the kernel's MASK), or null
   int64_t mask_sb, mask_sh;  // mask strides of batch and head, in elements (0: broadcast)
+  int mask_sr;               // mask row stride, in elements (kl: rows contiguous)
   uint16_t* dq;
   uint16_t* dk;
   uint16_t* dv;
@@ -385,7 +386,7 @@ __attribute__((amdgpu_waves_per_eu(BwdCfg<D, PASS>::WPE))) void fa_bwd_kernel(Bw
           if constexpr (HAS_MASK) {
             const int h = KV ? th : hf;
             const float m = mask_at<MASK>(a.mask, b * a.mask_sb + h * a.mask_sh +
-                                                      (int64_t)min(qi, ql - 1) * kl +
+                                                      (int64_t)min(qi, ql - 1) * a.mask_sr +
                                                       min(kj, kl - 1));
             vis = vis && m != -INFINITY;
             x = __builtin_fmaf(s, a.c, kLog2e * m) - l2;
@@ -503,7 +504,8 @@ int train_bwd(const void* q, const void* k, const void* v, const void* mask, int
               int64_t mask_sb, int64_t mask_sh, const void* O, const float* L, const void* dO,
               int batch, int n_heads, int n_kv_heads, int ql, int kl, int head_dim, float scale,
               int causal, int window, void* dQ, void* dK, void* dV, void* stream,
-              const int64_t* q_strides = nullptr, const int64_t* k_strides = nullptr) {
+              const int64_t* q_strides = nullptr, const int64_t* k_strides = nullptr,
+              int64_t mask_sr = -1) {
   if (batch < 0 || ql < 0 || kl < 0 || n_heads < 1 || n_kv_heads < 1) return FA_ERR_BAD_SIZE;
   if (n_heads % n_kv_heads != 0) return FA_ERR_HEAD_GROUPING;
   if (head_dim != 64 && head_dim != 128 && head_dim != 256) return FA_ERR_HEAD_DIM;
@@ -556,6 +558,7 @@ int train_bwd(const void* q, const void* k, const void* v, const void* mask, int
   a.mask = mask;
   a.mask_sb = mask_sb;
   a.mask_sh = mask_sh;
+  a.mask_sr = mask_sr < 0 ? kl : (int)mask_sr;
   const int mask_kind = !mask                          ? kNoMask
                         : mask_dtype == FA_MASK_BF16 ? kMaskBF16
                         : mask_dtype == FA_MASK_BOOL ? kMaskBool
@@ -626,7 +629,9 @@ extern "C" int fa_train_bwd_ex(const void* q, const void* k, const void* v, cons
 
 extern "C" int fa_train_bwd_strided(const void* q, const void* k, const void* v, const void* O,
                                     const float* L, const void* dO, const long long* q_strides,
-                                    const long long* kv_strides, int batch, int n_heads,
+                                    const long long* kv_strides, const void* mask,
+                                    int mask_dtype, const long long* mask_strides, int batch,
+                                    int n_heads,
                                     int n_kv_heads, int ql, int kl, int head_dim, float scale,
                                     int causal, int window, void* dQ, void* dK, void* dV,
                                     void* stream) {
@@ -635,7 +640,12 @@ extern "C" int fa_train_bwd_strided(const void* q, const void* k, const void* v,
     if (q_strides) qs[i] = q_strides[i];
     if (kv_strides) ks[i] = kv_strides[i];
   }
-  return train_bwd(q, k, v, nullptr, FA_MASK_F32, 0, 0, O, L, dO, batch, n_heads, n_kv_heads, ql,
-                   kl, head_dim, scale, causal, window, dQ, dK, dV, stream,
-                   q_strides ? qs : nullptr, kv_strides ? ks : nullptr);
+  const int64_t mhead = (int64_t)ql * kl;
+  const int64_t ms[3] = {mask_strides ? mask_strides[0] : mhead * n_heads,
+                         mask_strides ? mask_strides[1] : mhead,
+                         mask_strides ? mask_strides[2] : kl};
+  if (mask && (ms[2] < 0 || ms[2] > 0x7fffffffLL)) return FA_ERR_MASK;
+  return train_bwd(q, k, v, mask, mask_dtype, ms[0], ms[1], O, L, dO, batch, n_heads, n_kv_heads,
+                   ql, kl, head_dim, scale, causal, window, dQ, dK, dV, stream,
+                   q_strides ? qs : nullptr, kv_strides ? ks : nullptr, ms[2]);
 }

@@ -99,6 +99,7 @@ struct FwdArgs {
   const uint16_t* v;
   const void* mask;          // f32, bf16 or bool bytes (the kernel's MASK), or null
   int64_t mask_sb, mask_sh;  // mask strides of batch and head, in elements (0: broadcast)
+  int mask_sr;               // mask row stride, in elements (kl: rows contiguous)
   uint16_t* o;
   float* l;
   int B, H, Hkv, ql, kl;
@@ -352,7 +353,7 @@ __device__ __forceinline__ bool fwd_tile(const FwdArgs& a, int qtile, int bh, ui
       const int qrow = qw0 + 16 * qb + c16;
       if constexpr (HAS_MASK) {
         const int64_t mrow =
-            b * a.mask_sb + h * a.mask_sh + (int64_t)min(qrow, ql - 1) * kl;
+            b * a.mask_sb + h * a.mask_sh + (int64_t)min(qrow, ql - 1) * a.mask_sr;
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
@@ -850,7 +851,8 @@ int train_fwd(const void* q, const void* k, const void* v, const void* mask, int
               int64_t mask_sb, int64_t mask_sh, int batch, int n_heads, int n_kv_heads, int ql,
               int kl, int head_dim, float scale, int causal, int window, void* O, float* L,
               void* stream, int n_split = 0, void* workspace = nullptr,
-              size_t workspace_bytes = 0, const int64_t* strides = nullptr) {
+              size_t workspace_bytes = 0, const int64_t* strides = nullptr,
+              int64_t mask_sr = -1) {
   if (batch < 0 || ql < 0 || kl < 0 || n_heads < 1 || n_kv_heads < 1) return FA_ERR_BAD_SIZE;
   if (n_heads % n_kv_heads != 0) return FA_ERR_HEAD_GROUPING;
   if (head_dim != 64 && head_dim != 128 && head_dim != 256) return FA_ERR_HEAD_DIM;
@@ -918,6 +920,7 @@ int train_fwd(const void* q, const void* k, const void* v, const void* mask, int
   a.mask = mask;
   a.mask_sb = mask_sb;
   a.mask_sh = mask_sh;
+  a.mask_sr = mask_sr < 0 ? kl : (int)mask_sr;
   const int mask_kind = !mask                          ? kNoMask
                         : mask_dtype == FA_MASK_BF16 ? kMaskBF16
                         : mask_dtype == FA_MASK_BOOL ? kMaskBool
@@ -1114,13 +1117,20 @@ extern "C" int fa_train_fwd_ex(const void* q, const void* k, const void* v, cons
 
 extern "C" int fa_train_fwd_strided(const void* q, const long long* q_strides, const void* k,
                                     const long long* k_strides, const void* v,
-                                    const long long* v_strides, int batch, int n_heads,
+                                    const long long* v_strides, const void* mask, int mask_dtype,
+                                    const long long* mask_strides, int batch, int n_heads,
                                     int n_kv_heads, int ql, int kl, int head_dim, float scale,
                                     int causal, int window, int n_split, void* workspace,
                                     unsigned long workspace_bytes, void* O,
                                     const long long* o_strides, float* L, void* stream) {
   if (n_split < 0 || n_split > kMaxSplit) return FA_ERR_SPLIT;
   if (n_split > 0 && window >= 0) return FA_ERR_WINDOW;
+  if (n_split > 0 && mask) return FA_ERR_MASK;  // split-KV takes no mask
+  const long long mhead = (long long)ql * kl;
+  const long long ms[3] = {mask_strides ? mask_strides[0] : mhead * n_heads,
+                           mask_strides ? mask_strides[1] : mhead,
+                           mask_strides ? mask_strides[2] : kl};
+  if (mask && (ms[2] < 0 || ms[2] > 0x7fffffffLL)) return FA_ERR_MASK;
   const long long* given[4] = {q_strides, k_strides, v_strides, o_strides};
   const long long hq = (long long)ql * head_dim, hk = (long long)kl * head_dim;
   const long long dflt[4][3] = {{hq * n_heads, hq, head_dim},
@@ -1130,9 +1140,9 @@ extern "C" int fa_train_fwd_strided(const void* q, const long long* q_strides, c
   int64_t st[12];
   for (int t = 0; t < 4; ++t)
     for (int i = 0; i < 3; ++i) st[3 * t + i] = given[t] ? given[t][i] : dflt[t][i];
-  return train_fwd(q, k, v, nullptr, FA_MASK_F32, 0, 0, batch, n_heads, n_kv_heads, ql, kl,
+  return train_fwd(q, k, v, mask, mask_dtype, ms[0], ms[1], batch, n_heads, n_kv_heads, ql, kl,
                    head_dim, scale, causal, window, O, L, stream, n_split, workspace,
-                   workspace_bytes, st);
+                   workspace_bytes, st, ms[2]);
 }
 
 extern "C" const char* fa_status_string(int status) {

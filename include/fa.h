@@ -157,8 +157,8 @@ int fa_train_fwd_ex(const void *q, const void *k, const void *v, const void *mas
                     int causal, int window, void *O, float *L, void *stream);
 
 /*
- * fa_train_fwd_strided - fa_train_fwd_ex (without a mask) on strided views of
- * Q, K, V and O, such as the sequence-major layout [batch, len, heads,
+ * fa_train_fwd_strided - fa_train_fwd_ex on strided views of Q, K, V, O and
+ * the mask, such as the sequence-major layout [batch, len, heads,
  * head_dim] that an adjacent attention API on the pages passes as transposed
  * views ("nuvec-core 0.3.0", tests/fast.rs, attention_kernels_match_the_fallback,
  * K and V given as views of [B, L, H, D]).
@@ -171,17 +171,24 @@ int fa_train_fwd_ex(const void *q, const void *k, const void *v, const void *mas
  *               otherwise) and >= 0 (FA_ERR_STRIDE); K and V row strides at most
  *               2^24 elements (FA_ERR_TOO_LARGE). NULL: that tensor contiguous.
  *               O's rows must not overlap one another or the inputs.
+ *   mask, mask_dtype
+ *               as for fa_train_fwd_ex (NULL: none)
+ *   mask_strides host array of 3 element strides of the mask: batch, head (0
+ *               broadcasts) and row (its keys are contiguous), each >= 0, the
+ *               row stride below 2^31 (FA_ERR_MASK); NULL: [batch, n_heads, ql, kl] contiguous. A
+ *               mask sliced from a larger buffer has a row stride above kl.
  *   L           f32 [batch, n_heads, ql], contiguous, as for fa_train_fwd.
  *   window      as for fa_train_fwd_ex (< 0: none; >= 0 needs causal).
  *   n_split     0: one launch; >= 1: split-KV with workspace, as for
- *               fa_train_fwd_split.
+ *               fa_train_fwd_split (no mask: FA_ERR_MASK).
  *   others      as for fa_train_fwd.
  *
- * With all four strides NULL this is fa_train_fwd_ex without a mask (or
- * fa_train_fwd_split with n_split >= 1), bit for bit.
+ * With all strides NULL this is fa_train_fwd_ex (or fa_train_fwd_split with
+ * n_split >= 1), bit for bit.
  */
 int fa_train_fwd_strided(const void *q, const long long *q_strides, const void *k,
                          const long long *k_strides, const void *v, const long long *v_strides,
+                         const void *mask, int mask_dtype, const long long *mask_strides,
                          int batch, int n_heads, int n_kv_heads, int ql, int kl, int head_dim,
                          float scale, int causal, int window, int n_split, void *workspace,
                          unsigned long workspace_bytes, void *O, const long long *o_strides,
@@ -340,25 +347,29 @@ int fa_train_bwd_ex(const void *q, const void *k, const void *v, const void *mas
                     int window, void *dQ, void *dK, void *dV, void *stream);
 
 /*
- * fa_train_bwd_strided - the backward of fa_train_fwd_strided (no mask): the
- * tensors may be strided views with head_dim contiguous, in two layouts.
+ * fa_train_bwd_strided - the backward of fa_train_fwd_strided: the tensors
+ * may be strided views with head_dim contiguous, in two layouts, and the
+ * mask a strided view as for fa_train_fwd_strided.
  *
  *   q_strides   host array of 3 element strides (batch, head, row) shared by
  *               Q, O, dO and dQ (the gradient is written in Q's layout);
  *               NULL: contiguous [batch, n_heads, ql, head_dim]
  *   kv_strides  the same for K, V, dK and dV; NULL: contiguous
+ *   mask, mask_dtype, mask_strides
+ *               as for fa_train_fwd_strided (NULL mask: none)
  *   L           f32 [batch, n_heads, ql], contiguous
  *   window      as for fa_train_bwd_ex (< 0: none; >= 0 needs causal)
  *   others      as for fa_train_bwd.
  *
  * Strides are multiples of 8 elements (FA_ERR_ALIGNMENT otherwise) and >= 0
  * (FA_ERR_STRIDE); row strides at most 2^24 elements (FA_ERR_TOO_LARGE). The
- * gradients' rows must not overlap each other or the inputs. With both
- * strides NULL this is fa_train_bwd_ex without a mask, bit for bit.
+ * gradients' rows must not overlap each other or the inputs. With all
+ * strides NULL this is fa_train_bwd_ex, bit for bit.
  */
 int fa_train_bwd_strided(const void *q, const void *k, const void *v, const void *O,
                          const float *L, const void *dO, const long long *q_strides,
-                         const long long *kv_strides, int batch, int n_heads, int n_kv_heads,
+                         const long long *kv_strides, const void *mask, int mask_dtype,
+                         const long long *mask_strides, int batch, int n_heads, int n_kv_heads,
                          int ql, int kl, int head_dim, float scale, int causal, int window,
                          void *dQ, void *dK, void *dV, void *stream);
 

@@ -283,7 +283,8 @@ def test_backward_ex_invalid_arguments_are_rejected(over, code):
     assert fa.fa_train_bwd_ex(**args) == code
 
 
-STRIDED_GOOD = dict(q=A, q_strides=None, k=A, k_strides=None, v=A, v_strides=None, batch=1,
+STRIDED_GOOD = dict(q=A, q_strides=None, k=A, k_strides=None, v=A, v_strides=None, mask=0,
+                    mask_dtype=0, mask_strides=None, batch=1,
                     n_heads=4, n_kv_heads=2, ql=8, kl=8, head_dim=64, scale=0.125, causal=1,
                     window=-1, n_split=0, workspace=0, workspace_bytes=0, O=A, o_strides=None,
                     L=A, stream=0)
@@ -294,7 +295,10 @@ STRIDED_GOOD = dict(q=A, q_strides=None, k=A, k_strides=None, v=A, v_strides=Non
     (dict(k_strides=(4096, 64, 12)), 6), (dict(v_strides=(4, 512, 64)), 6),
     (dict(k_strides=(0, 0, 1 << 25)), 7), (dict(n_split=2, window=3), 9),
     (dict(causal=0, window=3), 9), (dict(n_split=-1), 11), (dict(head_dim=96), 4),
-    (dict(q=0), 1), (dict(n_split=2), 1),
+    (dict(q=0), 1), (dict(n_split=2), 1), (dict(mask=A, mask_strides=(0, 0, -8)), 10),
+    (dict(mask=A, mask_strides=(-1, 0, 8)), 10), (dict(mask=A, n_split=2, workspace=A,
+                                                       workspace_bytes=1 << 20), 10),
+    (dict(mask=A, mask_dtype=5), 10), (dict(mask=A + 2), 6),
 ])
 def test_strided_invalid_arguments_are_rejected(over, code):
     args = dict(STRIDED_GOOD)
@@ -306,7 +310,8 @@ def test_strided_status_string():
     assert "stride" in fa.status_string(13)
 
 
-BWD_STRIDED_GOOD = dict(q=A, k=A, v=A, O=A, L=A, dO=A, q_strides=None, kv_strides=None, batch=1,
+BWD_STRIDED_GOOD = dict(q=A, k=A, v=A, O=A, L=A, dO=A, q_strides=None, kv_strides=None, mask=0,
+                        mask_dtype=0, mask_strides=None, batch=1,
                         n_heads=4, n_kv_heads=2, ql=8, kl=8, head_dim=64, scale=0.125, causal=1,
                         window=-1, dQ=A, dK=A, dV=A, stream=0)
 
@@ -315,7 +320,7 @@ BWD_STRIDED_GOOD = dict(q=A, k=A, v=A, O=A, L=A, dO=A, q_strides=None, kv_stride
     (dict(q_strides=(-8, 512, 64)), 13), (dict(kv_strides=(0, 0, -64)), 13),
     (dict(kv_strides=(4096, 64, 12)), 6), (dict(q_strides=(4, 512, 64)), 6),
     (dict(q_strides=(0, 0, 1 << 25)), 7), (dict(causal=0, window=3), 9), (dict(head_dim=96), 4),
-    (dict(dQ=0), 1),
+    (dict(dQ=0), 1), (dict(mask=A, mask_strides=(0, 0, -8)), 10), (dict(mask=A, mask_dtype=3), 10),
 ])
 def test_bwd_strided_invalid_arguments_are_rejected(over, code):
     args = dict(BWD_STRIDED_GOOD)

@@ -145,3 +145,40 @@ def test_backward_on_bshd_views_equals_contiguous(B, H, Hkv, ql, kl, D, causal, 
     assert got[0].stride() == qs.stride() and got[1].stride() == ks.stride()
     for x, y in zip(ref, got):
         assert torch.equal(x.view(torch.int16), y.contiguous().view(torch.int16))
+
+
+@pytest.mark.parametrize("kind", ["f32", "bf16", "bool"])
+def test_sliced_mask_equals_contiguous(kind):
+    """A mask sliced from a larger buffer ([1, H, 512, 512][..., :ql, :kl]: row
+    stride 512) with Q, K, V, O, dO as [B, L, H, D] views: forward and backward
+    bit-identical to fa_train_fwd_ex / fa_train_bwd_ex given the same mask made
+    contiguous."""
+    import torch
+    import flash_attention_forward_fa_amd as fa
+    from tests.pins import _finite_mask
+    B, H, Hkv, ql, kl, D = 2, 4, 2, 200, 300, 64
+    print(f"case strided sliced mask {kind}", flush=True)
+    seed = fagen.SEED_BASE + 14300
+    q, k, v = _inputs(seed, B, H, Hkv, ql, kl, D)
+    dO = gu.to_dev(fagen.normal_bf16(seed, 6, (B, H, ql, D)), "cuda:0")
+    big = _finite_mask(seed, 1, H, 512, 512)
+    if kind == "bool":
+        big_t = torch.from_numpy(np.isfinite(big)).cuda()
+    elif kind == "bf16":
+        bits = (np.ascontiguousarray(big).view(np.uint32) >> 16).astype(np.uint16)
+        big_t = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).cuda()
+    else:
+        big_t = torch.from_numpy(big).cuda()
+    m = big_t[:, :, :ql, :kl]
+    assert m.stride(2) == 512
+    mc = m.contiguous()
+    O1, L1 = fa.train_fwd_ex(q, k, v, mask=mc, causal=True)
+    g1 = fa.train_bwd_ex(q, k, v, O1, L1, dO, mask=mc, causal=True)
+    qs, ks, vs, dOs = (_bshd(x) for x in (q, k, v, dO))
+    O2, L2 = fa.train_fwd_strided(qs, ks, vs, mask=m, causal=True,
+                                  out=_bshd(torch.empty_like(q)))
+    g2 = fa.train_bwd_strided(qs, ks, vs, O2, L2, dOs, mask=m, causal=True)
+    torch.cuda.synchronize()
+    _same((O1, L1), (O2, L2))
+    for x, y in zip(g1, g2):
+        assert torch.equal(x.view(torch.int16), y.contiguous().view(torch.int16))
