@@ -326,3 +326,20 @@ def test_bwd_strided_invalid_arguments_are_rejected(over, code):
     args = dict(BWD_STRIDED_GOOD)
     args.update(over)
     assert fa.fa_train_bwd_strided(**args) == code
+
+
+def test_strided_and_paged_bindings_fail_loudly_without_gpu_tensors():
+    """No CPU path: CPU tensors are refused before any library call."""
+    import torch
+    q = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
+    L = torch.zeros(1, 1, 4)
+    with pytest.raises(ValueError):
+        fa.train_fwd_strided(q, q, q)
+    with pytest.raises(ValueError):
+        fa.train_fwd_strided(q.transpose(1, 2), q, q)
+    with pytest.raises(ValueError):
+        fa.train_bwd_strided(q, q, q, q, L, q)
+    with pytest.raises(ValueError):
+        fa.train_bwd_ex(q, q, q, q, L, q)
+    with pytest.raises(ValueError):
+        fa.train_fwd_split(q, q, q, 2)
