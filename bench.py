@@ -76,9 +76,17 @@ def cpu_baseline(workloads, inputs, target_rows):
         parts.append(f"{w.name}: every {stride}th row ({rows.size} rows, {dt:.1f} s)")
         log(f"cpu_baseline {w.name}: {rows.size} rows in {dt:.2f} s "
             f"({flop / dt / 1e9:.2f} GFLOP/s)")
+    host_cores = os.cpu_count()
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = host_cores
     return {"value": total_flop / total_s / 1e12, "unit": "TFLOP/s", "cores": threads,
+            "threads": threads, "host_cores": host_cores, "host_cores_usable": usable,
             "kind": "oracle", "sample": "; ".join(parts) +
-            "; metric FLOP of the sampled rows / oracle wall time"}
+            f"; metric FLOP of the sampled rows / oracle wall time; the oracle ran {threads} "
+            f"threads on a host with {host_cores} logical cores ({usable} usable by this "
+            "process)"}
 
 
 def main():

@@ -89,6 +89,73 @@ def status_string(status):
     return lib().fa_status_string(int(status)).decode()
 
 
+def _on_gpu(t):
+    """Whether tensor t lives in GPU memory (the kernels take device pointers only)."""
+    return t.is_cuda
+
+
+def _check_out(t, name, dev, dtype, shape, layout="contiguous"):
+    """Checks a caller-supplied output (or workspace) tensor before its pointer
+    reaches the library: a torch tensor of `dtype` and exactly `shape` on the
+    GPU `dev` (q's device), with layout "contiguous" or "rows" (only the last
+    dimension must be contiguous; the library then checks the strides)."""
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not _on_gpu(t) or t.device != dev:
+        raise ValueError(f"{name} must be on {dev}, got {t.device}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if layout == "contiguous" and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if layout == "rows" and t.dim() and t.shape[-1] > 1 and t.stride(-1) != 1:
+        raise ValueError(f"{name} must have a contiguous last dimension")
+    return t
+
+
+def _check_workspace(ws, need, dev):
+    """A split-KV workspace: a contiguous uint8 tensor on `dev` of at least
+    `need` bytes."""
+    import torch
+    if not isinstance(ws, torch.Tensor) or ws.dtype != torch.uint8:
+        raise TypeError("workspace must be a uint8 torch tensor")
+    if not _on_gpu(ws) or ws.device != dev:
+        raise ValueError(f"workspace must be on {dev}, got {ws.device}")
+    if not ws.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    if ws.numel() < need:
+        raise ValueError(f"workspace holds {ws.numel()} bytes, the call needs {need}")
+    return ws
+
+
+def _check_inputs(tensors, dev, layout="contiguous"):
+    """q, k, v (and O, dO) inputs: bf16 4-d tensors on the GPU `dev`."""
+    import torch
+    for name, t in tensors:
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.bfloat16:
+            raise TypeError(f"{name} must be a bfloat16 tensor")
+        if t.dim() != 4 or not _on_gpu(t) or t.device != dev:
+            raise ValueError(f"{name} must be a 4-d tensor on {dev}")
+        if layout == "contiguous" and not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if layout == "rows" and t.shape[-1] > 1 and t.stride(3) != 1:
+            raise ValueError(f"{name} must have a contiguous head_dim")
+
+
+def _non_overlapping(shape, strides):
+    """Whether no two elements of a view share an address: the dimensions of
+    size > 1, sorted by stride, each step at least the span of those below."""
+    dims = sorted((st, n) for n, st in zip(shape, strides) if n > 1)
+    span = 1
+    for st, n in dims:
+        if st < span:
+            return False
+        span = st * (n - 1) + span
+    return True
+
+
 def fa_train_fwd(q, k, v, mask, batch, n_heads, n_kv_heads, ql, kl, head_dim, scale, causal,
                  O, L, stream):
     """The C entry point with raw integer pointers (0 for NULL); returns the status."""
@@ -185,9 +252,7 @@ def train_fwd_split(q, k, v, n_split, scale=None, causal=False, workspace=None, 
     need = fa_train_fwd_split_workspace(B, H, ql, D, n_split)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-    if (workspace.dtype != torch.uint8 or not workspace.is_contiguous()
-            or workspace.device != q.device):
-        raise ValueError("workspace must be a contiguous uint8 tensor on q's device")
+    _check_workspace(workspace, need, q.device)
     with torch.cuda.device(q.device):
         status = fa_train_fwd_split(q.data_ptr(), k.data_ptr(), v.data_ptr(), B, H, Hkv, ql, kl,
                                     D, scale, causal, n_split, workspace.data_ptr(),
@@ -222,14 +287,12 @@ def paged_fwd(q, k_cache, v_cache, block_table, seq_lens, scale=None, causal=Fal
     """
     import torch
 
-    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
-        if not isinstance(t, torch.Tensor) or t.dtype != torch.bfloat16:
-            raise TypeError(f"{name} must be a bfloat16 tensor")
-        if t.dim() != 4 or not t.is_contiguous() or not t.is_cuda or t.device != q.device:
-            raise ValueError(f"{name} must be a contiguous 4-d tensor on q's GPU")
+    if not isinstance(q, torch.Tensor):
+        raise TypeError("q must be a bfloat16 tensor")
+    _check_inputs((("q", q), ("k_cache", k_cache), ("v_cache", v_cache)), q.device)
     for name, t in (("block_table", block_table), ("seq_lens", seq_lens)):
         if (not isinstance(t, torch.Tensor) or t.dtype != torch.int32 or not t.is_contiguous()
-                or t.device != q.device):
+                or not _on_gpu(t) or t.device != q.device):
             raise ValueError(f"{name} must be a contiguous int32 tensor on q's device")
     B, H, ql, D = q.shape
     n_blocks, Hkv, bs, Dk = k_cache.shape
@@ -242,11 +305,14 @@ def paged_fwd(q, k_cache, v_cache, block_table, seq_lens, scale=None, causal=Fal
         scale = 1.0 / math.sqrt(D)
     O = out if out is not None else torch.empty_like(q)
     L = lse if lse is not None else torch.empty((B, H, ql), dtype=torch.float32, device=q.device)
+    _check_out(O, "out", q.device, torch.bfloat16, (B, H, ql, D))
+    _check_out(L, "lse", q.device, torch.float32, (B, H, ql))
     ws_ptr, ws_bytes = 0, 0
     if n_split > 0:
+        need = fa_train_fwd_split_workspace(B, H, ql, D, n_split)
         if workspace is None:
-            need = fa_train_fwd_split_workspace(B, H, ql, D, n_split)
             workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+        _check_workspace(workspace, need, q.device)
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel()
     s = stream if stream is not None else torch.cuda.current_stream(q.device)
     with torch.cuda.device(q.device):
@@ -295,7 +361,7 @@ def _mask_view(mask, q, k):
         raise ValueError(f"mask must have shape [B or 1, H or 1, {ql}, {kl}]")
     if kl > 1 and mask.stride(3) != 1:
         raise ValueError("the mask's keys must be contiguous")
-    if mask.device != q.device:
+    if not _on_gpu(mask) or mask.device != q.device:
         raise ValueError("mask must be on q's device")
     st = (mask.stride(0) if mask.shape[0] > 1 else 0, mask.stride(1) if mask.shape[1] > 1 else 0,
           mask.stride(2) if ql > 1 else kl)
@@ -316,11 +382,9 @@ def train_fwd_strided(q, k, v, mask=None, scale=None, causal=False, window=None,
     mask). n_split > 0 runs split-KV (its workspace allocated here when None).
     """
     import torch
-    for name, t in (("q", q), ("k", k), ("v", v)):
-        if not isinstance(t, torch.Tensor) or t.dtype != torch.bfloat16:
-            raise TypeError(f"{name} must be a bfloat16 tensor")
-        if t.dim() != 4 or t.stride(3) != 1 or not t.is_cuda or t.device != q.device:
-            raise ValueError(f"{name} must be a 4-d tensor with contiguous head_dim on q's GPU")
+    if not isinstance(q, torch.Tensor):
+        raise TypeError("q must be a bfloat16 tensor")
+    _check_inputs((("q", q), ("k", k), ("v", v)), q.device, layout="rows")
     B, H, ql, D = q.shape
     Bk, Hkv, kl, Dk = k.shape
     if tuple(v.shape) != tuple(k.shape) or Bk != B or Dk != D:
@@ -330,16 +394,17 @@ def train_fwd_strided(q, k, v, mask=None, scale=None, causal=False, window=None,
     O = out if out is not None else torch.empty((B, H, ql, D), dtype=torch.bfloat16,
                                                 device=q.device)
     L = lse if lse is not None else torch.empty((B, H, ql), dtype=torch.float32, device=q.device)
-    if tuple(O.shape) != (B, H, ql, D) or O.dtype != torch.bfloat16 or O.stride(3) != 1:
-        raise ValueError("out must be a bf16 tensor shaped like q with contiguous head_dim")
-    if tuple(L.shape) != (B, H, ql) or L.dtype != torch.float32 or not L.is_contiguous():
-        raise ValueError("lse must be a contiguous f32 tensor [B, H, ql]")
+    _check_out(O, "out", q.device, torch.bfloat16, (B, H, ql, D), layout="rows")
+    if not _non_overlapping(O.shape, O.stride()):
+        raise ValueError("out must not have overlapping rows (its strides alias elements)")
+    _check_out(L, "lse", q.device, torch.float32, (B, H, ql))
     ws_bytes = 0
     if n_split > 0:
         ws_bytes = fa_train_fwd_split_workspace(B, H, ql, D, n_split)
         if workspace is None:
-            workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
-        ws_bytes = workspace.numel() * workspace.element_size()
+            workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
+        _check_workspace(workspace, ws_bytes, q.device)
+        ws_bytes = workspace.numel()
     s = stream if stream is not None else torch.cuda.current_stream(q.device)
     st = lambda t: t.stride()[:3]
     mptr, mdt, mst = _mask_view(mask, q, k)
@@ -375,11 +440,9 @@ def train_bwd_strided(q, k, v, O, L, dO, mask=None, scale=None, causal=False, wi
     (head_dim contiguous); dQ comes in q's layout, dK and dV in k's.
     """
     import torch
-    for name, t in (("q", q), ("k", k), ("v", v), ("O", O), ("dO", dO)):
-        if not isinstance(t, torch.Tensor) or t.dtype != torch.bfloat16:
-            raise TypeError(f"{name} must be a bfloat16 tensor")
-        if t.dim() != 4 or t.stride(3) != 1 or not t.is_cuda or t.device != q.device:
-            raise ValueError(f"{name} must be a 4-d tensor with contiguous head_dim on q's GPU")
+    if not isinstance(q, torch.Tensor):
+        raise TypeError("q must be a bfloat16 tensor")
+    _check_inputs((("q", q), ("k", k), ("v", v), ("O", O), ("dO", dO)), q.device, layout="rows")
     B, H, ql, D = q.shape
     Bk, Hkv, kl, Dk = k.shape
     if tuple(v.shape) != tuple(k.shape) or Bk != B or Dk != D:
@@ -388,9 +451,14 @@ def train_bwd_strided(q, k, v, O, L, dO, mask=None, scale=None, causal=False, wi
         raise ValueError("O and dO must be shaped like q")
     if O.stride() != q.stride() or dO.stride() != q.stride() or v.stride() != k.stride():
         raise ValueError("O and dO need q's strides, v needs k's")
-    if (L.dtype != torch.float32 or tuple(L.shape) != (B, H, ql) or not L.is_contiguous()
-            or L.device != q.device):
-        raise ValueError("L must be a contiguous f32 tensor [B, H, ql] on q's device")
+    _check_out(L, "L", q.device, torch.float32, (B, H, ql))
+    # dQ takes q's stride triple and dK, dV take k's: a view whose elements
+    # alias (e.g. K expanded over the batch) would make workgroups write the
+    # same gradient rows, so such inputs are copied to a contiguous layout first
+    if not _non_overlapping(q.shape, q.stride()):
+        q, O, dO = q.contiguous(), O.contiguous(), dO.contiguous()
+    if not _non_overlapping(k.shape, k.stride()):
+        k, v = k.contiguous(), v.contiguous()
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     dQ = torch.empty_strided(q.shape, q.stride(), dtype=torch.bfloat16, device=q.device)
@@ -413,25 +481,19 @@ def _fwd_outputs(q, k, v, scale, out, lse, stream):
     """Checks q, k, v and the outputs; returns (O, L, sizes, scale, stream)."""
     import torch
 
-    for name, t in (("q", q), ("k", k), ("v", v)):
-        if not isinstance(t, torch.Tensor) or t.dtype != torch.bfloat16:
-            raise TypeError(f"{name} must be a bfloat16 tensor")
-        if t.dim() != 4 or not t.is_contiguous() or not t.is_cuda:
-            raise ValueError(f"{name} must be a contiguous 4-d tensor on a GPU")
+    if not isinstance(q, torch.Tensor):
+        raise TypeError("q must be a bfloat16 tensor")
+    _check_inputs((("q", q), ("k", k), ("v", v)), q.device)
     B, H, ql, D = q.shape
     Bk, Hkv, kl, Dk = k.shape
     if tuple(v.shape) != tuple(k.shape) or Bk != B or Dk != D:
         raise ValueError("k and v must be [B, Hkv, kl, D] with q's B and D")
-    if k.device != q.device or v.device != q.device:
-        raise ValueError("q, k and v must be on the same device")
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     O = out if out is not None else torch.empty_like(q)
     L = lse if lse is not None else torch.empty((B, H, ql), dtype=torch.float32, device=q.device)
-    if O.shape != q.shape or O.dtype != torch.bfloat16 or not O.is_contiguous():
-        raise ValueError("out must be a contiguous bf16 tensor shaped like q")
-    if tuple(L.shape) != (B, H, ql) or L.dtype != torch.float32 or not L.is_contiguous():
-        raise ValueError("lse must be a contiguous f32 tensor [B, H, ql]")
+    _check_out(O, "out", q.device, torch.bfloat16, (B, H, ql, D))
+    _check_out(L, "lse", q.device, torch.float32, (B, H, ql))
     s = stream if stream is not None else torch.cuda.current_stream(q.device)
     return O, L, (B, H, Hkv, ql, kl, D), scale, s
 
@@ -462,32 +524,26 @@ def _train_fwd(q, k, v, mask, scale, causal, window, out, lse, stream, ex=False,
                mask_layout=None):
     import torch
 
-    for name, t in (("q", q), ("k", k), ("v", v)):
-        if not isinstance(t, torch.Tensor) or t.dtype != torch.bfloat16:
-            raise TypeError(f"{name} must be a bfloat16 tensor")
-        if t.dim() != 4 or not t.is_contiguous() or not t.is_cuda:
-            raise ValueError(f"{name} must be a contiguous 4-d tensor on a GPU")
+    if not isinstance(q, torch.Tensor):
+        raise TypeError("q must be a bfloat16 tensor")
+    _check_inputs((("q", q), ("k", k), ("v", v)), q.device)
     B, H, ql, D = q.shape
     Bk, Hkv, kl, Dk = k.shape
     if tuple(v.shape) != tuple(k.shape) or Bk != B or Dk != D:
         raise ValueError("k and v must be [B, Hkv, kl, D] with q's B and D")
-    if k.device != q.device or v.device != q.device:
-        raise ValueError("q, k and v must be on the same device")
     if mask is not None and mask_layout is None:
         if mask.dtype != torch.float32 or not mask.is_contiguous() or mask.device != q.device:
             raise ValueError("mask must be a contiguous float32 tensor on q's device")
         if tuple(mask.shape) != (B, H, ql, kl):
             raise ValueError(f"mask must have shape {(B, H, ql, kl)}")
-    if mask is not None and mask.device != q.device:
+    if mask is not None and (not _on_gpu(mask) or mask.device != q.device):
         raise ValueError("mask must be on q's device")
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     O = out if out is not None else torch.empty_like(q)
     L = lse if lse is not None else torch.empty((B, H, ql), dtype=torch.float32, device=q.device)
-    if O.shape != q.shape or O.dtype != torch.bfloat16 or not O.is_contiguous():
-        raise ValueError("out must be a contiguous bf16 tensor shaped like q")
-    if tuple(L.shape) != (B, H, ql) or L.dtype != torch.float32 or not L.is_contiguous():
-        raise ValueError("lse must be a contiguous f32 tensor [B, H, ql]")
+    _check_out(O, "out", q.device, torch.bfloat16, (B, H, ql, D))
+    _check_out(L, "lse", q.device, torch.float32, (B, H, ql))
     s = stream if stream is not None else torch.cuda.current_stream(q.device)
     mptr = mask.data_ptr() if mask is not None else 0
     with torch.cuda.device(q.device):
@@ -574,7 +630,7 @@ def _mask_layout(mask, q, k):
         raise ValueError(f"mask must have shape [B or 1, H or 1, {ql}, {kl}]")
     if ql * kl > 0 and ((kl > 1 and mask.stride(3) != 1) or (ql > 1 and mask.stride(2) != kl)):
         raise ValueError("mask rows must be contiguous (strides [.., .., kl, 1])")
-    if mask.device != q.device:
+    if not _on_gpu(mask) or mask.device != q.device:
         raise ValueError("mask must be on q's device")
     sb = mask.stride(0) if mask.shape[0] > 1 else 0
     sh = mask.stride(1) if mask.shape[1] > 1 else 0
@@ -596,20 +652,16 @@ def _train_bwd(q, k, v, O, L, dO, mask, scale, causal, window, stream, ex=False,
                mask_layout=None):
     import torch
 
-    for name, t in (("q", q), ("k", k), ("v", v), ("O", O), ("dO", dO)):
-        if not isinstance(t, torch.Tensor) or t.dtype != torch.bfloat16:
-            raise TypeError(f"{name} must be a bfloat16 tensor")
-        if t.dim() != 4 or not t.is_contiguous() or not t.is_cuda or t.device != q.device:
-            raise ValueError(f"{name} must be a contiguous 4-d tensor on q's GPU")
+    if not isinstance(q, torch.Tensor):
+        raise TypeError("q must be a bfloat16 tensor")
+    _check_inputs((("q", q), ("k", k), ("v", v), ("O", O), ("dO", dO)), q.device)
     B, H, ql, D = q.shape
     Bk, Hkv, kl, Dk = k.shape
     if tuple(v.shape) != tuple(k.shape) or Bk != B or Dk != D:
         raise ValueError("k and v must be [B, Hkv, kl, D] with q's B and D")
     if O.shape != q.shape or dO.shape != q.shape:
         raise ValueError("O and dO must be shaped like q")
-    if (L.dtype != torch.float32 or tuple(L.shape) != (B, H, ql) or not L.is_contiguous()
-            or L.device != q.device):
-        raise ValueError("L must be a contiguous f32 tensor [B, H, ql] on q's device")
+    _check_out(L, "L", q.device, torch.float32, (B, H, ql))
     if mask is not None and not ex:
         if mask.dtype != torch.float32 or not mask.is_contiguous() or mask.device != q.device:
             raise ValueError("mask must be a contiguous float32 tensor on q's device")

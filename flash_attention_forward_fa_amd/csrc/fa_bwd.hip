@@ -526,6 +526,10 @@ int train_bwd(const void* q, const void* k, const void* v, const void* mask, int
   }
   // a streamed tile's rows must lie within a 32-bit buffer offset
   if (qs[2] > (1 << 24) || ks[2] > (1 << 24)) return FA_ERR_TOO_LARGE;
+  // dQ (Q's triple) and dK, dV (K's triple) are written: no two elements of
+  // one may share an address (several workgroups would race on it)
+  const int64_t qn[3] = {batch, n_heads, ql}, kn[3] = {batch, n_kv_heads, kl};
+  if (view_overlaps(qs, qn, head_dim) || view_overlaps(ks, kn, head_dim)) return FA_ERR_STRIDE;
   const int64_t qrows = (int64_t)batch * n_heads * ql;
   const int64_t krows = (int64_t)batch * n_kv_heads * kl;
   if (qrows == 0 && krows == 0) return FA_OK;

@@ -186,6 +186,35 @@ __device__ __forceinline__ float mask_at(const void* m, int64_t idx) {
     return static_cast<const float*>(m)[idx];
 }
 
+// Host check of an output view: n[0] x n[1] x n[2] rows (batch, head, row) of
+// `row` contiguous elements at element strides st[0..2]. It maps two elements
+// to one address unless, over the dimensions of size > 1 sorted by stride,
+// every stride is at least the span of the dimensions below it (a sufficient
+// condition for distinct addresses; interleaved layouts it cannot prove are
+// rejected too).
+inline bool view_overlaps(const int64_t st[3], const int64_t n[3], int64_t row) {
+  if (row <= 0 || n[0] <= 0 || n[1] <= 0 || n[2] <= 0) return false;  // no elements
+  int64_t ds[4], dn[4];
+  int k = 0;
+  if (row > 1) ds[k] = 1, dn[k++] = row;
+  for (int i = 0; i < 3; ++i)
+    if (n[i] > 1) ds[k] = st[i], dn[k++] = n[i];
+  for (int i = 1; i < k; ++i)  // insertion sort by stride
+    for (int j = i; j > 0 && ds[j] < ds[j - 1]; --j) {
+      const int64_t t0 = ds[j], t1 = dn[j];
+      ds[j] = ds[j - 1], dn[j] = dn[j - 1];
+      ds[j - 1] = t0, dn[j - 1] = t1;
+    }
+  const int64_t kMax = INT64_MAX / 2;
+  int64_t span = 1;
+  for (int i = 0; i < k; ++i) {
+    if (ds[i] < span) return true;
+    // span of this and the lower dimensions, saturated (no address beyond it exists)
+    span = ds[i] > (kMax - span) / (dn[i] - 1) ? kMax : ds[i] * (dn[i] - 1) + span;
+  }
+  return false;
+}
+
 // Wave priority for the next instructions, pinned in place.
 template <int P> __device__ __forceinline__ void set_prio() {
   __builtin_amdgcn_sched_barrier(0);

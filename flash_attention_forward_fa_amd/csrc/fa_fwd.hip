@@ -877,6 +877,9 @@ int train_fwd(const void* q, const void* k, const void* v, const void* mask, int
     // a K/V tile's rows must lie within a 32-bit buffer offset
     if (st[5] > (1 << 24) || st[8] > (1 << 24) || st[2] > 0x7fffffffLL || st[11] > 0x7fffffffLL)
       return FA_ERR_TOO_LARGE;
+    // O is written: no two of its elements may share an address
+    const int64_t on[3] = {batch, n_heads, ql};
+    if (view_overlaps(st + 9, on, head_dim)) return FA_ERR_STRIDE;
   }
   const int64_t rows = (int64_t)batch * n_heads * ql;
   if (rows == 0) return FA_OK;
@@ -894,7 +897,10 @@ int train_fwd(const void* q, const void* k, const void* v, const void* mask, int
   // arithmetic of each row is unchanged (rows are computed independently).
   // (with strides: the group's query heads are rows h*q_sh of the packed
   // head, whose stride is G*q_sh; O likewise)
-  if (ql == 1 && n_heads > n_kv_heads && !mask && window < 0) {
+  // (the head strides become row strides, which the kernel holds as int: a
+  // head stride beyond that range leaves the heads unpacked)
+  if (ql == 1 && n_heads > n_kv_heads && !mask && window < 0 && st[1] <= 0x7fffffffLL &&
+      st[10] <= 0x7fffffffLL) {
     const int G = n_heads / n_kv_heads;
     ql = G;
     n_heads = n_kv_heads;
@@ -1161,7 +1167,8 @@ extern "C" const char* fa_status_string(int status) {
     case FA_ERR_MASK: return "mask dtype must be FA_MASK_F32, FA_MASK_BF16 or FA_MASK_BOOL, strides >= 0";
     case FA_ERR_SPLIT: return "n_split must be in 1..65536 and the workspace large enough";
     case FA_ERR_PAGED: return "block_size must be a positive multiple of 16 and the cache non-empty";
-    case FA_ERR_STRIDE: return "strides must be >= 0";
+    case FA_ERR_STRIDE:
+      return "strides must be >= 0, and those of a written tensor must not alias its elements";
     default: return "unknown status";
   }
 }

@@ -50,7 +50,8 @@ enum fa_status {
     FA_ERR_PAGED = 12,         /* fa_paged_fwd: block_size not a positive multiple of
                                   16, or no cache blocks for a non-empty table          */
     FA_ERR_STRIDE = 13         /* fa_train_fwd_strided, fa_train_bwd_strided: a negative
-                                  stride                                                */
+                                  stride, or the strides of a written tensor (O; dQ,
+                                  dK, dV) map two of its elements to one address        */
 };
 
 /* Element types of an additive mask (fa_train_fwd_ex). */
@@ -170,7 +171,10 @@ int fa_train_fwd_ex(const void *q, const void *k, const void *v, const void *mas
  *               multiple of 8 elements (16-byte rows; FA_ERR_ALIGNMENT
  *               otherwise) and >= 0 (FA_ERR_STRIDE); K and V row strides at most
  *               2^24 elements (FA_ERR_TOO_LARGE). NULL: that tensor contiguous.
- *               O's rows must not overlap one another or the inputs.
+ *               O's strides must give every element its own address: over
+ *               the dimensions of size > 1 sorted by stride, each stride at
+ *               least the span of those below it (FA_ERR_STRIDE otherwise).
+ *               O must not overlap the inputs.
  *   mask, mask_dtype
  *               as for fa_train_fwd_ex (NULL: none)
  *   mask_strides host array of 3 element strides of the mask: batch, head (0
@@ -362,9 +366,13 @@ int fa_train_bwd_ex(const void *q, const void *k, const void *v, const void *mas
  *   others      as for fa_train_bwd.
  *
  * Strides are multiples of 8 elements (FA_ERR_ALIGNMENT otherwise) and >= 0
- * (FA_ERR_STRIDE); row strides at most 2^24 elements (FA_ERR_TOO_LARGE). The
- * gradients' rows must not overlap each other or the inputs. With all
- * strides NULL this is fa_train_bwd_ex, bit for bit.
+ * (FA_ERR_STRIDE); row strides at most 2^24 elements (FA_ERR_TOO_LARGE).
+ * Since the gradients are written with these strides, each triple must give
+ * every element its own address (over the dimensions of size > 1 sorted by
+ * stride, each stride at least the span of those below it), else
+ * FA_ERR_STRIDE: inputs expanded over a dimension (stride 0) must be passed
+ * as a copy. The gradients must not overlap the inputs. With all strides NULL
+ * this is fa_train_bwd_ex, bit for bit.
  */
 int fa_train_bwd_strided(const void *q, const void *k, const void *v, const void *O,
                          const float *L, const void *dO, const long long *q_strides,
