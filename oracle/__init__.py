@@ -5,11 +5,13 @@ TEST INFRASTRUCTURE ONLY: only tests/, the smoke check of __graft_entry__ and
 the bench's cpu_baseline leg may import this package. It shares no code with
 the GPU path (flash_attention_forward_fa_amd) and never imports it.
 
-The arithmetic lives in fa_oracle.c (single precision, following the CPU
-oracle of the method's page, "mlx-native 0.9.0",
-tests/test_flash_attn_train.rs, section "CPU oracle - forward O + logsumexp
-L"). This wrapper widens bf16 inputs to f32 (exact), calls it, and rounds O
-to bf16 the way that page's oracle_for_bf16 helper does.
+The arithmetic lives in fa_oracle.c: softmax attention and its logsumexp
+written from their definition in single precision (the operation of the
+method's page, "mlx-native 0.9.0", tests/test_flash_attn_train.rs, section
+"CPU oracle - forward O + logsumexp L"), and the FA-2 backward of the same
+page's "Phase 2 - backward kernel helpers". This wrapper widens bf16 inputs
+to f32 (exact), calls it, and rounds O to bf16 the way that page's
+oracle_for_bf16 helper does.
 """
 import ctypes
 import os
@@ -34,6 +36,14 @@ def _bind(path):
     lib.fa_oracle_fwd_swa.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, i64,
                                       ctypes.c_float, i64, vp, i64, vp, vp, ctypes.c_int]
     lib.fa_oracle_fwd_swa.restype = ctypes.c_int
+    lib.fa_oracle_fwd_general.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64,
+                                          ctypes.c_float, ctypes.c_int, i64, vp, i64, vp, vp,
+                                          ctypes.c_int]
+    lib.fa_oracle_fwd_general.restype = ctypes.c_int
+    lib.fa_oracle_bwd_general.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64,
+                                          i64, ctypes.c_float, ctypes.c_int, i64, vp, i64, vp, vp,
+                                          vp, ctypes.c_int]
+    lib.fa_oracle_bwd_general.restype = ctypes.c_int
     lib.fa_oracle_round_bf16.argtypes = [vp, vp, i64]
     lib.fa_oracle_round_bf16.restype = None
     lib.fa_oracle_bwd.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64,
@@ -165,6 +175,55 @@ def bwd(q, k, v, mask, L, dO, B, H, Hkv, ql, kl, D, scale, causal, n_threads=Non
     return dQ, dK, dV
 
 
+def fwd_dv(q, k, v, mask, B, H, Hkv, ql, kl, D, Dv, scale, causal, window=None, rows=None,
+           n_threads=None, lib=None):
+    """Forward with value width Dv (q, k: [.., D]; v: [B,Hkv,kl,Dv]). All rows
+    (O [B,H,ql,Dv], L [B,H,ql]) or the flat `rows` (O [n,Dv], L [n]).
+    Returns (O_f32, O_bf16_bits, L)."""
+    qf, kf, vf, mf = _f32(q), _f32(k), _f32(v), _f32(mask)
+    lib = lib or _load()
+    if rows is None:
+        O = np.empty((B, H, ql, Dv), dtype=np.float32)
+        L = np.empty((B, H, ql), dtype=np.float32)
+        rp, n = None, 0
+    else:
+        rows = np.ascontiguousarray(rows, dtype=np.int64)
+        O = np.empty((rows.size, Dv), dtype=np.float32)
+        L = np.empty((rows.size,), dtype=np.float32)
+        rp, n = rows.ctypes.data, rows.size
+        if n == 0:
+            return O, round_bf16(O, lib), L
+    rc = lib.fa_oracle_fwd_general(_ptr(qf), _ptr(kf), _ptr(vf), _ptr(mf), B, H, Hkv, ql, kl, D,
+                                   Dv, float(scale), int(bool(causal)),
+                                   -1 if window is None else int(window), rp, n, _ptr(O),
+                                   _ptr(L), n_threads or default_threads())
+    _check(rc, "fa_oracle_fwd_general")
+    return O, round_bf16(O, lib), L
+
+
+def bwd_groups(q, k, v, mask, L, dO, B, H, Hkv, ql, kl, D, scale, causal, groups, Dv=None,
+               window=None, n_threads=None, lib=None):
+    """Backward of the kv heads `groups` (flat b * Hkv + g) only. Returns
+    (dQ [n, H/Hkv, ql, D] of each group's query heads, dK [n, kl, D],
+    dV [n, kl, Dv]), f32."""
+    Dv = D if Dv is None else Dv
+    qf, kf, vf, mf, lf, gf = _f32(q), _f32(k), _f32(v), _f32(mask), _f32(L), _f32(dO)
+    groups = np.ascontiguousarray(groups, dtype=np.int64)
+    n, G = groups.size, H // Hkv
+    dQ = np.empty((n, G, ql, D), dtype=np.float32)
+    dK = np.empty((n, kl, D), dtype=np.float32)
+    dV = np.empty((n, kl, Dv), dtype=np.float32)
+    if n == 0:
+        return dQ, dK, dV
+    lib = lib or _load()
+    rc = lib.fa_oracle_bwd_general(_ptr(qf), _ptr(kf), _ptr(vf), _ptr(mf), _ptr(lf), _ptr(gf), B,
+                                   H, Hkv, ql, kl, D, Dv, float(scale), int(bool(causal)),
+                                   -1 if window is None else int(window), groups.ctypes.data, n,
+                                   _ptr(dQ), _ptr(dK), _ptr(dV), n_threads or default_threads())
+    _check(rc, "fa_oracle_bwd_general")
+    return dQ, dK, dV
+
+
 def bind(lib_path):
     """A fwd(...) callable over another build of fa_oracle.c (used by the
     mutation tests, which plant mistakes in a copy of the source)."""
@@ -172,6 +231,15 @@ def bind(lib_path):
 
     def f(*args, **kw):
         return fwd(*args, lib=lib, **kw)
+    return f
+
+
+def bind_dv(lib_path):
+    """A fwd_dv(...) callable over another build of fa_oracle.c (mutation tests)."""
+    lib = _bind(lib_path)
+
+    def f(*args, **kw):
+        return fwd_dv(*args, lib=lib, **kw)
     return f
 
 

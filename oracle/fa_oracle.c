@@ -1,55 +1,53 @@
 /*
- * fa_oracle.c - plain CPU reference for the flash-attention training forward.
+ * fa_oracle.c - plain CPU reference for the flash-attention training forward
+ * and its backward.
  *
  * TEST INFRASTRUCTURE ONLY. Only the tests, the smoke check and the CPU
  * baseline of the bench may call this code. It shares no code, header,
  * constant or helper with the GPU path.
  *
- * What it computes follows the CPU oracle on the method's page
- * ("mlx-native 0.9.0", tests/test_flash_attn_train.rs, section "CPU oracle -
- * forward O + logsumexp L", function sdpa_reference_with_logsumexp), restated
- * here in single precision:
+ * What is computed is softmax attention with its logsumexp, the operation the
+ * method's page defines ("mlx-native 0.9.0", tests/test_flash_attn_train.rs,
+ * doc comment and section "CPU oracle - forward O + logsumexp L"; the causal
+ * alignment is that oracle's, the offset max(kl - ql, 0) clamped at zero).
+ * It is written here from the definition, in natural-log units, in single
+ * precision, one query row at a time:
  *
- *   for every batch b, query head h, query row i (kv head = h / (H / Hkv)):
- *     s_j = (sum_d q[i,d] * k[j,d]) * (scale * log2 e)       dot left to right
- *     s_j += log2 e * mask[i,j]                               if a mask is given
- *     s_j = -inf   for j > max(kl - ql, 0) + i                if causal
- *     s_j = -inf   for j < max(kl - ql, 0) + i - window       sliding window
- *     m   = max(-FLT_MAX / 2, max_j s_j)                      finite sentinel
- *     p_j = exp2(s_j - m),  S = sum_j p_j                     left to right
- *     L_i = m * ln 2 + ln S                                   (S = 0 -> -inf)
- *     O_i = sum_j (p_j / S') v_j,  S' = (S == 0 ? 1 : S)       left to right
+ *   query row i of batch b and query head h reads kv head g = h / (H / Hkv)
+ *   and sits at key position pos_i = max(kl - ql, 0) + i;
+ *   key j is allowed for it unless causal and j > pos_i, or a sliding window
+ *   w >= 0 is given and j < pos_i - w;
+ *   s_ij = scale * <q_i, k_j> + mask_ij     for an allowed key (-inf else);
+ *   a key is visible when s_ij > -inf (a -inf mask entry hides it);
+ *   no visible key:  O_i = +0,  L_i = -inf;
+ *   otherwise, with m_i = max_j s_ij (any shift gives the same values; the
+ *   maximum keeps every exponential at most 1):
+ *     L_i = m_i + log(sum_j exp(s_ij - m_i))               (logsumexp)
+ *     O_i = sum_j (exp(s_ij - m_i) / sum_k exp(s_ik - m_i)) * v_j   (softmax . V)
  *
- * The mask is additive in natural-log units (hence the log2 e factor in the
- * base-2 score space). The causal alignment is bottom-right with the offset
- * clamped at zero, as on the page (kl.saturating_sub(ql) + q_pos). O is
- * returned in f32; fa_oracle_round_bf16 rounds it to bf16 the way the page's
- * oracle_for_bf16 helper does before comparing against a bf16 output.
+ * Every sum runs in index order (dot products over d, the others over j).
+ * The sliding window is the page's section 7 band (key j kept for row i iff
+ * j <= i and j + w >= i), placed at the causal rule's position pos_i.
+ * Keys and values may have different widths (D for q and k, Dv for v and O).
  *
- * Sliding window (the same page, section 7, "SLIDING-WINDOW MASK (SWA)
- * PARITY"): the page builds it as an additive mask that keeps key j for row i
- * iff j <= i and j + window >= i. fa_oracle_fwd_swa applies that predicate
- * directly, with the causal rule's bottom-right alignment (i replaced by
- * q_abs = max(kl - ql, 0) + i, the same position the causal rule uses; the
- * two agree when ql = kl, the page's case): window + 1 keys at most.
+ * The backward (fa_oracle_bwd*) is the FA-2 backward the same page defines
+ * (section "Phase 2 - backward kernel helpers", its doc comment), written from
+ * those equations with P taken from the forward's L:
  *
- * Arithmetic is IEEE f32 with no contraction (built with -ffp-contract=off),
- * exp2f/logf from the C library.
+ *   P_ij  = exp(s_ij - L_i)  for a visible key, 0 otherwise
+ *   dP_ij = <dO_i, v_j>,   D_i = sum_j P_ij dP_ij,   dS_ij = P_ij (dP_ij - D_i)
+ *   dQ_i  = scale * sum_j dS_ij k_j
+ *   dK_j  = scale * sum_i dS_ij q_i,   dV_j = sum_i P_ij dO_i
  *
- * The backward (fa_oracle_bwd) follows the same page's CPU oracle for the
- * FA-2 backward pass (section "Phase 2 - backward kernel helpers", function
- * sdpa_backward_reference_f32), in natural-log units as written there:
+ * where the sums of dK_j and dV_j run over the query rows of every query head
+ * of the kv head's group (head by head, rows in order). D_i is written as the
+ * page computes it, sum_j P_ij dP_ij (equal to rowsum(O_i * dO_i) for the
+ * exact O). Pairs (i, j) whose key is not allowed for the row contribute
+ * exactly zero and are not visited. dQ is computed per query row, dK and dV
+ * per key, so both parallelise without shared sums.
  *
- *   S_ij  = scale * (q_i . k_j)  (+ mask_ij; a -inf mask entry gives -inf),
- *           -inf for a causally hidden key (same alignment as the forward)
- *   P_ij  = exp(S_ij - L_i)      (0 where S_ij = -inf)
- *   dP_ij = dO_i . v_j
- *   D_i   = sum_j P_ij * dP_ij
- *   dS_ij = P_ij * (dP_ij - D_i)
- *   dV_j += P_ij * dO_i,  dQ_i += scale * dS_ij * k_j,  dK_j += scale * dS_ij * q_i
- *
- * dK and dV of a kv head accumulate over every query head of its group; the
- * sums run in the page's loop order (query head, query row, key).
+ * Arithmetic is IEEE f32 with no contraction (built with -ffp-contract=off);
+ * expf and logf come from the C library.
  */
 #include <float.h>
 #include <math.h>
@@ -58,109 +56,178 @@
 #include <stdlib.h>
 #include <string.h>
 
-static const float ORACLE_LOG2E = 1.44269504088896340736f;
-static const float ORACLE_LN2 = 0.693147180559945309417f;
-
 typedef struct {
     const float *q, *k, *v, *mask;
-    int64_t H, Hkv, ql, kl, D;
+    int64_t B, H, Hkv, ql, kl, D, Dv;
     float scale;
     int causal;
     int64_t window; /* < 0: no sliding window */
 } oracle_problem;
 
-/* One query row, flat index row = (b*H + h)*ql + i. o_row gets D floats. */
-static void oracle_row(const oracle_problem *p, int64_t row, float *o_row, float *l_out,
-                       float *s)
-{
-    const int64_t D = p->D, kl = p->kl, ql = p->ql;
-    const int64_t i = row % ql;
-    const int64_t bh = row / ql;
-    const int64_t h = bh % p->H;
-    const int64_t b = bh / p->H;
-    const int64_t kvh = h / (p->H / p->Hkv);
-    const float q_scale = p->scale * ORACLE_LOG2E;
-    const float *qr = p->q + row * D;
-    const float *kh = p->k + (b * p->Hkv + kvh) * kl * D;
-    const float *vh = p->v + (b * p->Hkv + kvh) * kl * D;
+/* ---- the definition, per (query row, key) ---- */
 
-    /* scaled dot products in base-2 units */
-    for (int64_t j = 0; j < kl; ++j) {
-        float dot = 0.0f;
-        for (int64_t d = 0; d < D; ++d)
-            dot += qr[d] * kh[j * D + d];
-        s[j] = dot * q_scale;
+/* Key position of query row i (bottom-right alignment, offset clamped at 0). */
+static int64_t query_position(const oracle_problem *p, int64_t i)
+{
+    return (p->kl > p->ql ? p->kl - p->ql : 0) + i;
+}
+
+/* Whether the causal rule and the window allow key j for a query at pos (the
+   window comes with the causal rule). */
+static int key_allowed(const oracle_problem *p, int64_t pos, int64_t j)
+{
+    if ((p->causal || p->window >= 0) && j > pos)
+        return 0;
+    if (p->window >= 0 && j < pos - p->window)
+        return 0;
+    return 1;
+}
+
+/* Score of key j for flat query row `row` (natural-log units), -inf when the
+   key is not visible. qr: the row of q; kh: the kv head's keys. */
+static float score(const oracle_problem *p, int64_t row, int64_t pos, int64_t j,
+                   const float *qr, const float *kh)
+{
+    if (!key_allowed(p, pos, j))
+        return -INFINITY;
+    float dot = 0.0f;
+    for (int64_t d = 0; d < p->D; ++d)
+        dot += qr[d] * kh[j * p->D + d];
+    float s = p->scale * dot;
+    if (p->mask)
+        s += p->mask[row * p->kl + j];
+    return s;
+}
+
+/* The kv head (b * Hkv + g) a flat query row reads, and its position. */
+static void row_coords(const oracle_problem *p, int64_t row, int64_t *kvhead, int64_t *pos)
+{
+    const int64_t i = row % p->ql, bh = row / p->ql;
+    const int64_t b = bh / p->H, h = bh % p->H;
+    *kvhead = b * p->Hkv + h / (p->H / p->Hkv);
+    *pos = query_position(p, i);
+}
+
+/* Forward of one query row: o gets Dv floats, *l the logsumexp; e: kl floats
+   of scratch. */
+static void forward_row(const oracle_problem *p, int64_t row, float *o, float *l, float *e)
+{
+    int64_t kvh, pos;
+    row_coords(p, row, &kvh, &pos);
+    const float *qr = p->q + row * p->D;
+    const float *kh = p->k + kvh * p->kl * p->D;
+    const float *vh = p->v + kvh * p->kl * p->Dv;
+    float m = -INFINITY;
+    for (int64_t j = 0; j < p->kl; ++j) {
+        e[j] = score(p, row, pos, j, qr, kh);
+        if (e[j] > m)
+            m = e[j];
     }
-    /* additive mask, natural-log units converted to base 2 */
-    if (p->mask) {
-        const float *mr = p->mask + row * kl;
-        for (int64_t j = 0; j < kl; ++j)
-            s[j] += ORACLE_LOG2E * mr[j];
+    for (int64_t d = 0; d < p->Dv; ++d)
+        o[d] = 0.0f;
+    if (m == -INFINITY) { /* no visible key */
+        *l = -INFINITY;
+        return;
     }
-    /* causal: key j is visible to row i iff j <= q_abs = max(kl - ql, 0) + i */
-    const int64_t q_abs = (kl > ql ? kl - ql : 0) + i;
-    if (p->causal) {
-        for (int64_t j = q_abs + 1; j < kl; ++j)
-            s[j] = -INFINITY;
+    float z = 0.0f;
+    for (int64_t j = 0; j < p->kl; ++j) {
+        e[j] = expf(e[j] - m); /* hidden keys: exp(-inf) = 0 */
+        z += e[j];
     }
-    /* sliding window: keys more than `window` positions before q_abs are hidden */
-    if (p->window >= 0) {
-        for (int64_t j = 0; j < q_abs - p->window && j < kl; ++j)
-            s[j] = -INFINITY;
-    }
-    /* row max with the finite sentinel -FLT_MAX/2 */
-    float m = -FLT_MAX / 2.0f;
-    for (int64_t j = 0; j < kl; ++j)
-        if (s[j] > m)
-            m = s[j];
-    /* exponentials (base 2) and their sum */
-    float sum = 0.0f;
-    for (int64_t j = 0; j < kl; ++j) {
-        s[j] = exp2f(s[j] - m);
-        sum += s[j];
-    }
-    *l_out = m * ORACLE_LN2 + logf(sum);
-    /* normalised weighted sum of V rows; per output element the terms are
-       added in key order, exactly as a d-outer / j-inner loop would */
-    const float safe = (sum == 0.0f) ? 1.0f : sum;
-    for (int64_t d = 0; d < D; ++d)
-        o_row[d] = 0.0f;
-    for (int64_t j = 0; j < kl; ++j) {
-        const float w = s[j] / safe;
-        const float *vr = vh + j * D;
-        for (int64_t d = 0; d < D; ++d)
-            o_row[d] += w * vr[d];
+    *l = m + logf(z);
+    for (int64_t j = 0; j < p->kl; ++j) {
+        if (e[j] == 0.0f) /* a hidden key adds exactly zero */
+            continue;
+        const float w = e[j] / z;
+        for (int64_t d = 0; d < p->Dv; ++d)
+            o[d] += w * vh[j * p->Dv + d];
     }
 }
 
-typedef struct {
-    const oracle_problem *p;
-    const int64_t *rows; /* NULL: rows are 0..n-1 */
-    int64_t begin, end;
-    float *O, *L;
-    int failed;
-} oracle_job;
+/* ---- a parallel loop over [0, n) ---- */
 
-static void *oracle_worker(void *arg)
+typedef void (*range_fn)(const void *ctx, int64_t begin, int64_t end, float *scratch);
+
+typedef struct {
+    range_fn fn;
+    const void *ctx;
+    int64_t begin, end;
+    size_t scratch;
+    int failed;
+} range_job;
+
+static void *range_worker(void *arg)
 {
-    oracle_job *j = (oracle_job *)arg;
-    float *s = (float *)malloc(sizeof(float) * (size_t)(j->p->kl > 0 ? j->p->kl : 1));
-    if (!s) {
+    range_job *j = (range_job *)arg;
+    float *scratch = (float *)malloc(sizeof(float) * (j->scratch > 0 ? j->scratch : 1));
+    if (!scratch) {
         j->failed = 1;
         return NULL;
     }
-    for (int64_t t = j->begin; t < j->end; ++t) {
-        int64_t row = j->rows ? j->rows[t] : t;
-        oracle_row(j->p, row, j->O + t * j->p->D, j->L + t, s);
-    }
-    free(s);
+    j->fn(j->ctx, j->begin, j->end, scratch);
+    free(scratch);
     return NULL;
 }
 
-static int oracle_validate(const float *q, const float *k, const float *v, int64_t B,
-                           int64_t H, int64_t Hkv, int64_t ql, int64_t kl, int64_t D)
+/* Runs fn over [0, n) split into n_threads contiguous ranges, each with its
+   own scratch of `scratch` floats. Returns 4 when memory ran out. */
+static int run_parallel(int64_t n, int n_threads, size_t scratch, range_fn fn, const void *ctx)
 {
-    if (B < 0 || ql < 0 || kl < 0 || H < 1 || Hkv < 1 || D < 1)
+    if (n <= 0)
+        return 0;
+    if (n_threads < 1)
+        n_threads = 1;
+    if (n_threads > 256)
+        n_threads = 256;
+    if (n_threads > n)
+        n_threads = (int)n;
+    range_job jobs[256];
+    pthread_t tid[256];
+    for (int t = 0; t < n_threads; ++t) {
+        jobs[t].fn = fn;
+        jobs[t].ctx = ctx;
+        jobs[t].begin = n * t / n_threads;
+        jobs[t].end = n * (t + 1) / n_threads;
+        jobs[t].scratch = scratch;
+        jobs[t].failed = 0;
+    }
+    int started = 0;
+    for (int t = 1; t < n_threads; ++t) {
+        if (pthread_create(&tid[t], NULL, range_worker, &jobs[t]) != 0)
+            break;
+        started = t;
+    }
+    /* ranges of threads that could not be started run on this thread */
+    for (int t = started + 1; t < n_threads; ++t)
+        range_worker(&jobs[t]);
+    range_worker(&jobs[0]);
+    for (int t = 1; t <= started; ++t)
+        pthread_join(tid[t], NULL);
+    for (int t = 0; t < n_threads; ++t)
+        if (jobs[t].failed)
+            return 4;
+    return 0;
+}
+
+/* ---- forward entry points ---- */
+
+typedef struct {
+    const oracle_problem *p;
+    const int64_t *rows; /* NULL: row t is flat row t */
+    float *O, *L;
+} forward_ctx;
+
+static void forward_range(const void *ctx, int64_t begin, int64_t end, float *scratch)
+{
+    const forward_ctx *c = (const forward_ctx *)ctx;
+    for (int64_t t = begin; t < end; ++t)
+        forward_row(c->p, c->rows ? c->rows[t] : t, c->O + t * c->p->Dv, c->L + t, scratch);
+}
+
+static int validate(const float *q, const float *k, const float *v, int64_t B, int64_t H,
+                    int64_t Hkv, int64_t ql, int64_t kl, int64_t D, int64_t Dv)
+{
+    if (B < 0 || ql < 0 || kl < 0 || H < 1 || Hkv < 1 || D < 1 || Dv < 1)
         return 2;
     if (H % Hkv != 0)
         return 3;
@@ -171,113 +238,73 @@ static int oracle_validate(const float *q, const float *k, const float *v, int64
     return 0;
 }
 
-static int oracle_run(const oracle_problem *p, const int64_t *rows, int64_t n_rows, float *O,
-                      float *L, int n_threads)
+/*
+ * The general forward. Inputs are f32 host arrays (bf16 values widened
+ * exactly): q [B,H,ql,D], k [B,Hkv,kl,D], v [B,Hkv,kl,Dv], mask [B,H,ql,kl]
+ * (natural-log units, -inf hides a key) or NULL. causal: 0/1; window < 0:
+ * none, >= 0: the sliding window, which includes the causal rule (whatever
+ * `causal` says). rows == NULL: every row, O [B,H,ql,Dv] and
+ * L [B,H,ql]; otherwise the n_rows flat rows listed ((b*H + h)*ql + i),
+ * O [n_rows,Dv] and L [n_rows]. Returns 0 on success, 1 null pointer, 2 bad
+ * size or row index, 3 H % Hkv != 0, 4 out of host memory.
+ */
+int fa_oracle_fwd_general(const float *q, const float *k, const float *v, const float *mask,
+                          int64_t B, int64_t H, int64_t Hkv, int64_t ql, int64_t kl, int64_t D,
+                          int64_t Dv, float scale, int causal, int64_t window,
+                          const int64_t *rows, int64_t n_rows, float *O, float *L, int n_threads)
 {
-    if (n_rows <= 0)
+    int rc = validate(q, k, v, B, H, Hkv, ql, kl, D, Dv);
+    if (rc)
+        return rc;
+    const int64_t n = rows ? n_rows : B * H * ql;
+    if (rows) {
+        for (int64_t t = 0; t < n_rows; ++t)
+            if (rows[t] < 0 || rows[t] >= B * H * ql)
+                return 2;
+    }
+    if (n <= 0)
         return 0;
     if (!O || !L)
         return 1;
-    if (n_threads < 1)
-        n_threads = 1;
-    if (n_threads > 256)
-        n_threads = 256;
-    if (n_threads > n_rows)
-        n_threads = (int)n_rows;
-    oracle_job jobs[256];
-    pthread_t tid[256];
-    for (int t = 0; t < n_threads; ++t) {
-        jobs[t].p = p;
-        jobs[t].rows = rows;
-        jobs[t].begin = n_rows * t / n_threads;
-        jobs[t].end = n_rows * (t + 1) / n_threads;
-        jobs[t].O = O;
-        jobs[t].L = L;
-        jobs[t].failed = 0;
-    }
-    int started = 0;
-    for (int t = 1; t < n_threads; ++t) {
-        if (pthread_create(&tid[t], NULL, oracle_worker, &jobs[t]) != 0)
-            break;
-        started = t;
-    }
-    /* rows of threads that could not be started are done on this thread */
-    for (int t = started + 1; t < n_threads; ++t)
-        oracle_worker(&jobs[t]);
-    oracle_worker(&jobs[0]);
-    for (int t = 1; t <= started; ++t)
-        pthread_join(tid[t], NULL);
-    for (int t = 0; t < n_threads; ++t)
-        if (jobs[t].failed)
-            return 4;
-    return 0;
+    oracle_problem p = {q, k, v, mask, B, H, Hkv, ql, kl, D, Dv, scale, causal != 0,
+                        window < 0 ? -1 : window};
+    forward_ctx c = {&p, rows, O, L};
+    return run_parallel(n, n_threads, (size_t)(kl > 0 ? kl : 1), forward_range, &c);
 }
 
-/*
- * Full forward. Inputs are f32 host arrays (bf16 values widened exactly):
- * q [B,H,ql,D], k/v [B,Hkv,kl,D], mask [B,H,ql,kl] or NULL.
- * Outputs: O [B,H,ql,D] f32, L [B,H,ql] f32.
- * Returns 0 on success, 1 null pointer, 2 bad size, 3 H % Hkv != 0,
- * 4 out of host memory.
- */
+/* Full forward with Dv = D, no window (the layout of fa_oracle_fwd_general). */
 int fa_oracle_fwd(const float *q, const float *k, const float *v, const float *mask, int64_t B,
                   int64_t H, int64_t Hkv, int64_t ql, int64_t kl, int64_t D, float scale,
                   int causal, float *O, float *L, int n_threads)
 {
-    int rc = oracle_validate(q, k, v, B, H, Hkv, ql, kl, D);
-    if (rc)
-        return rc;
-    oracle_problem p = {q, k, v, mask, H, Hkv, ql, kl, D, scale, causal, -1};
-    return oracle_run(&p, NULL, B * H * ql, O, L, n_threads);
+    return fa_oracle_fwd_general(q, k, v, mask, B, H, Hkv, ql, kl, D, D, scale, causal, -1, NULL,
+                                 0, O, L, n_threads);
 }
 
-/*
- * Selected rows only: rows[t] is a flat row index (b*H + h)*ql + i; O gets
- * [n_rows, D] and L [n_rows]. Same inputs and return codes as fa_oracle_fwd,
- * plus 2 when a row index is out of range.
- */
+/* Selected flat rows, Dv = D, no window. */
 int fa_oracle_fwd_rows(const float *q, const float *k, const float *v, const float *mask,
                        int64_t B, int64_t H, int64_t Hkv, int64_t ql, int64_t kl, int64_t D,
                        float scale, int causal, const int64_t *rows, int64_t n_rows, float *O,
                        float *L, int n_threads)
 {
-    int rc = oracle_validate(q, k, v, B, H, Hkv, ql, kl, D);
-    if (rc)
-        return rc;
     if (n_rows > 0 && !rows)
         return 1;
-    for (int64_t t = 0; t < n_rows; ++t)
-        if (rows[t] < 0 || rows[t] >= B * H * ql)
-            return 2;
-    oracle_problem p = {q, k, v, mask, H, Hkv, ql, kl, D, scale, causal, -1};
-    return oracle_run(&p, rows, n_rows, O, L, n_threads);
+    return fa_oracle_fwd_general(q, k, v, mask, B, H, Hkv, ql, kl, D, D, scale, causal, -1,
+                                 rows ? rows : (const int64_t *)&n_rows, rows ? n_rows : 0, O, L,
+                                 n_threads);
 }
 
-/*
- * Sliding-window causal forward: key j is visible to row i iff
- * q_abs - window <= j <= q_abs, q_abs = max(kl - ql, 0) + i, window >= 0
- * (plus the additive mask when one is given). rows == NULL computes every
- * row (O [B,H,ql,D], L [B,H,ql]); otherwise the n_rows flat rows listed
- * (O [n_rows,D], L [n_rows]). Return codes as fa_oracle_fwd_rows, plus 2 for
- * a negative window.
- */
+/* Sliding-window causal forward (window >= 0, else code 2), all rows
+   (rows == NULL) or the listed ones; Dv = D. */
 int fa_oracle_fwd_swa(const float *q, const float *k, const float *v, const float *mask,
                       int64_t B, int64_t H, int64_t Hkv, int64_t ql, int64_t kl, int64_t D,
                       float scale, int64_t window, const int64_t *rows, int64_t n_rows,
                       float *O, float *L, int n_threads)
 {
-    int rc = oracle_validate(q, k, v, B, H, Hkv, ql, kl, D);
-    if (rc)
-        return rc;
     if (window < 0)
         return 2;
-    oracle_problem p = {q, k, v, mask, H, Hkv, ql, kl, D, scale, 1, window};
-    if (!rows)
-        return oracle_run(&p, NULL, B * H * ql, O, L, n_threads);
-    for (int64_t t = 0; t < n_rows; ++t)
-        if (rows[t] < 0 || rows[t] >= B * H * ql)
-            return 2;
-    return oracle_run(&p, rows, n_rows, O, L, n_threads);
+    return fa_oracle_fwd_general(q, k, v, mask, B, H, Hkv, ql, kl, D, D, scale, 1, window, rows,
+                                 n_rows, O, L, n_threads);
 }
 
 /* f32 -> bf16 bits, round to nearest, ties to even (NaN stays a quiet NaN). */
@@ -298,136 +325,166 @@ void fa_oracle_round_bf16(const float *x, uint16_t *out, int64_t n)
 /* ---- backward ---- */
 
 typedef struct {
-    const float *q, *k, *v, *mask, *L, *dO;
-    float *dQ, *dK, *dV;
-    int64_t H, Hkv, ql, kl, D;
-    float scale;
-    int causal;
-    int64_t window; /* < 0: no sliding window */
-} oracle_bwd_problem;
+    oracle_problem p;
+    const float *L, *dO;
+    const int64_t *groups; /* kv heads b * Hkv + g computed, in output order */
+    int64_t n_groups, G;
+    float *Di;             /* D_i of every computed query row (output order) */
+    float *dQ, *dK, *dV;   /* [n_groups, G, ql, D], [n_groups, kl, D], [n_groups, kl, Dv] */
+} backward_ctx;
 
-/* Every query head of kv head (b, kvh), rows in order; dK/dV of that kv head
-   and dQ of its query heads are written only here. */
-static void oracle_bwd_group(const oracle_bwd_problem *p, int64_t b, int64_t kvh, float *s,
-                             float *pr)
+/* Flat input row of output query row t (group-major: group, head, row). */
+static int64_t bwd_query_row(const backward_ctx *c, int64_t t, int64_t *pos)
 {
-    const int64_t D = p->D, kl = p->kl, ql = p->ql, G = p->H / p->Hkv;
-    const float *kh = p->k + (b * p->Hkv + kvh) * kl * D;
-    const float *vh = p->v + (b * p->Hkv + kvh) * kl * D;
-    float *dkh = p->dK + (b * p->Hkv + kvh) * kl * D;
-    float *dvh = p->dV + (b * p->Hkv + kvh) * kl * D;
-    for (int64_t t = 0; t < kl * D; ++t) {
-        dkh[t] = 0.0f;
-        dvh[t] = 0.0f;
-    }
-    for (int64_t h = kvh * G; h < (kvh + 1) * G; ++h) {
-        for (int64_t i = 0; i < ql; ++i) {
-            const int64_t row = (b * p->H + h) * ql + i;
-            const float *qr = p->q + row * D;
-            const float *dor = p->dO + row * D;
-            float *dqr = p->dQ + row * D;
-            const float l_i = p->L[row];
-            for (int64_t d = 0; d < D; ++d)
-                dqr[d] = 0.0f;
-            /* scores in natural-log units, masks */
-            for (int64_t j = 0; j < kl; ++j) {
-                float dot = 0.0f;
-                for (int64_t d = 0; d < D; ++d)
-                    dot += qr[d] * kh[j * D + d];
-                s[j] = p->scale * dot;
-                if (p->mask) {
-                    const float m = p->mask[row * kl + j];
-                    if (m == -INFINITY)
-                        s[j] = -INFINITY;
-                    else
-                        s[j] += m;
-                }
-            }
-            const int64_t q_abs = (kl > ql ? kl - ql : 0) + i;
-            if (p->causal) {
-                for (int64_t j = q_abs + 1; j < kl; ++j)
-                    s[j] = -INFINITY;
-            }
-            /* sliding window, as in the forward */
-            if (p->window >= 0) {
-                for (int64_t j = 0; j < q_abs - p->window && j < kl; ++j)
-                    s[j] = -INFINITY;
-            }
-            /* P from the forward's L */
-            for (int64_t j = 0; j < kl; ++j)
-                pr[j] = (s[j] == -INFINITY) ? 0.0f : expf(s[j] - l_i);
-            /* D_i = sum_j P_ij dP_ij; s[] now holds dP */
-            float d_i = 0.0f;
-            for (int64_t j = 0; j < kl; ++j) {
-                float dp = 0.0f;
-                for (int64_t d = 0; d < D; ++d)
-                    dp += dor[d] * vh[j * D + d];
-                s[j] = dp;
-                d_i += pr[j] * dp;
-            }
-            for (int64_t j = 0; j < kl; ++j) {
-                const float ds = pr[j] * (s[j] - d_i);
-                for (int64_t d = 0; d < D; ++d)
-                    dvh[j * D + d] += pr[j] * dor[d];
-                for (int64_t d = 0; d < D; ++d) {
-                    dqr[d] += p->scale * ds * kh[j * D + d];
-                    dkh[j * D + d] += p->scale * ds * qr[d];
-                }
-            }
+    const oracle_problem *p = &c->p;
+    const int64_t per_group = c->G * p->ql;
+    const int64_t kvh = c->groups[t / per_group], r = t % per_group;
+    const int64_t b = kvh / p->Hkv, g = kvh % p->Hkv;
+    const int64_t h = g * c->G + r / p->ql, i = r % p->ql;
+    *pos = query_position(p, i);
+    return (b * p->H + h) * p->ql + i;
+}
+
+/* dQ_i and D_i, per query row. */
+static void backward_rows(const void *ctx, int64_t begin, int64_t end, float *scratch)
+{
+    const backward_ctx *c = (const backward_ctx *)ctx;
+    const oracle_problem *p = &c->p;
+    float *P = scratch, *dP = scratch + (p->kl > 0 ? p->kl : 1);
+    for (int64_t t = begin; t < end; ++t) {
+        int64_t pos, kvh, unused;
+        const int64_t row = bwd_query_row(c, t, &pos);
+        row_coords(p, row, &kvh, &unused);
+        const float *qr = p->q + row * p->D, *gr = c->dO + row * p->Dv;
+        const float *kh = p->k + kvh * p->kl * p->D, *vh = p->v + kvh * p->kl * p->Dv;
+        const float l_i = c->L[row];
+        float d_i = 0.0f;
+        for (int64_t j = 0; j < p->kl; ++j) {
+            const float s = score(p, row, pos, j, qr, kh);
+            P[j] = (s == -INFINITY) ? 0.0f : expf(s - l_i);
+            float dp = 0.0f;
+            for (int64_t d = 0; d < p->Dv; ++d)
+                dp += gr[d] * vh[j * p->Dv + d];
+            dP[j] = dp;
+            d_i += P[j] * dp;
+        }
+        c->Di[t] = d_i;
+        float *dq = c->dQ + t * p->D;
+        for (int64_t d = 0; d < p->D; ++d)
+            dq[d] = 0.0f;
+        for (int64_t j = 0; j < p->kl; ++j) {
+            if (!key_allowed(p, pos, j))
+                continue;
+            const float coef = p->scale * (P[j] * (dP[j] - d_i));
+            for (int64_t d = 0; d < p->D; ++d)
+                dq[d] += coef * kh[j * p->D + d];
         }
     }
 }
 
-typedef struct {
-    const oracle_bwd_problem *p;
-    int64_t begin, end; /* kv-head groups (b * Hkv + kvh) */
-    int failed;
-} oracle_bwd_job;
-
-static void *oracle_bwd_worker(void *arg)
+/* dK_j and dV_j, per key (after every D_i is known). */
+static void backward_keys(const void *ctx, int64_t begin, int64_t end, float *scratch)
 {
-    oracle_bwd_job *j = (oracle_bwd_job *)arg;
-    const size_t n = (size_t)(j->p->kl > 0 ? j->p->kl : 1);
-    float *s = (float *)malloc(sizeof(float) * n);
-    float *pr = (float *)malloc(sizeof(float) * n);
-    if (!s || !pr) {
-        free(s);
-        free(pr);
-        j->failed = 1;
-        return NULL;
+    (void)scratch;
+    const backward_ctx *c = (const backward_ctx *)ctx;
+    const oracle_problem *p = &c->p;
+    for (int64_t u = begin; u < end; ++u) {
+        const int64_t gi = u / p->kl, j = u % p->kl;
+        const int64_t kvh = c->groups[gi];
+        const float *kh = p->k + kvh * p->kl * p->D, *vh = p->v + kvh * p->kl * p->Dv;
+        float *dk = c->dK + u * p->D, *dv = c->dV + u * p->Dv;
+        for (int64_t d = 0; d < p->D; ++d)
+            dk[d] = 0.0f;
+        for (int64_t d = 0; d < p->Dv; ++d)
+            dv[d] = 0.0f;
+        for (int64_t r = 0; r < c->G * p->ql; ++r) {
+            const int64_t t = gi * c->G * p->ql + r;
+            int64_t pos;
+            const int64_t row = bwd_query_row(c, t, &pos);
+            if (!key_allowed(p, pos, j))
+                continue;
+            const float *qr = p->q + row * p->D, *gr = c->dO + row * p->Dv;
+            const float s = score(p, row, pos, j, qr, kh);
+            const float P = (s == -INFINITY) ? 0.0f : expf(s - c->L[row]);
+            float dp = 0.0f;
+            for (int64_t d = 0; d < p->Dv; ++d)
+                dp += gr[d] * vh[j * p->Dv + d];
+            const float coef = p->scale * (P * (dp - c->Di[t]));
+            for (int64_t d = 0; d < p->Dv; ++d)
+                dv[d] += P * gr[d];
+            for (int64_t d = 0; d < p->D; ++d)
+                dk[d] += coef * qr[d];
+        }
     }
-    for (int64_t g = j->begin; g < j->end; ++g)
-        oracle_bwd_group(j->p, g / j->p->Hkv, g % j->p->Hkv, s, pr);
-    free(s);
-    free(pr);
-    return NULL;
 }
 
 /*
- * Backward. Inputs are f32 host arrays: q, dO [B,H,ql,D]; k, v [B,Hkv,kl,D];
- * mask [B,H,ql,kl] or NULL; L [B,H,ql] (natural-log logsumexp of the forward).
- * Outputs dQ [B,H,ql,D], dK and dV [B,Hkv,kl,D], f32. Same return codes as
- * fa_oracle_fwd.
+ * The general backward. Inputs as fa_oracle_fwd_general, plus L [B,H,ql] (the
+ * forward's natural-log logsumexp) and dO [B,H,ql,Dv]. groups: the kv heads
+ * (b * Hkv + g) to compute, or NULL for all of them in order; the outputs
+ * hold the computed kv heads in that order: dQ [n_groups, H/Hkv, ql, D] (the
+ * group's query heads), dK [n_groups, kl, D], dV [n_groups, kl, Dv]. With
+ * groups NULL that is dQ [B,H,ql,D], dK [B,Hkv,kl,D], dV [B,Hkv,kl,Dv].
+ * Return codes as fa_oracle_fwd_general.
  */
-static int oracle_bwd_run(const oracle_bwd_problem *pp, int64_t B, int n_threads);
-int fa_oracle_bwd_swa(const float *q, const float *k, const float *v, const float *mask,
-                      const float *L, const float *dO, int64_t B, int64_t H, int64_t Hkv,
-                      int64_t ql, int64_t kl, int64_t D, float scale, int causal, int64_t window,
-                      float *dQ, float *dK, float *dV, int n_threads);
+int fa_oracle_bwd_general(const float *q, const float *k, const float *v, const float *mask,
+                          const float *L, const float *dO, int64_t B, int64_t H, int64_t Hkv,
+                          int64_t ql, int64_t kl, int64_t D, int64_t Dv, float scale, int causal,
+                          int64_t window, const int64_t *groups, int64_t n_groups, float *dQ,
+                          float *dK, float *dV, int n_threads)
+{
+    int rc = validate(q, k, v, B, H, Hkv, ql, kl, D, Dv);
+    if (rc)
+        return rc;
+    int64_t *all = NULL;
+    if (!groups) {
+        n_groups = B * Hkv;
+        all = (int64_t *)malloc(sizeof(int64_t) * (size_t)(n_groups > 0 ? n_groups : 1));
+        if (!all)
+            return 4;
+        for (int64_t t = 0; t < n_groups; ++t)
+            all[t] = t;
+        groups = all;
+    } else {
+        for (int64_t t = 0; t < n_groups; ++t)
+            if (groups[t] < 0 || groups[t] >= B * Hkv) {
+                free(all);
+                return 2;
+            }
+    }
+    const int64_t G = H / Hkv;
+    const int64_t n_q = n_groups * G * ql, n_k = n_groups * kl;
+    if ((n_q > 0 && (!L || !dO || !dQ)) || (n_k > 0 && (!dK || !dV))) {
+        free(all);
+        return 1;
+    }
+    float *Di = (float *)malloc(sizeof(float) * (size_t)(n_q > 0 ? n_q : 1));
+    if (!Di) {
+        free(all);
+        return 4;
+    }
+    backward_ctx c = {{q, k, v, mask, B, H, Hkv, ql, kl, D, Dv, scale, causal != 0,
+                       window < 0 ? -1 : window},
+                      L, dO, groups, n_groups, G, Di, dQ, dK, dV};
+    rc = run_parallel(n_q, n_threads, (size_t)(2 * (kl > 0 ? kl : 1)), backward_rows, &c);
+    if (!rc)
+        rc = run_parallel(n_k, n_threads, 1, backward_keys, &c);
+    free(Di);
+    free(all);
+    return rc;
+}
 
+/* Backward of every kv head, Dv = D, no window. */
 int fa_oracle_bwd(const float *q, const float *k, const float *v, const float *mask,
                   const float *L, const float *dO, int64_t B, int64_t H, int64_t Hkv, int64_t ql,
                   int64_t kl, int64_t D, float scale, int causal, float *dQ, float *dK, float *dV,
                   int n_threads)
 {
-    return fa_oracle_bwd_swa(q, k, v, mask, L, dO, B, H, Hkv, ql, kl, D, scale, causal, -1, dQ,
-                             dK, dV, n_threads);
+    return fa_oracle_bwd_general(q, k, v, mask, L, dO, B, H, Hkv, ql, kl, D, D, scale, causal, -1,
+                                 NULL, 0, dQ, dK, dV, n_threads);
 }
 
-/*
- * Backward with an optional sliding window (window >= 0; it comes with the
- * causal rule, as in fa_oracle_fwd_swa, so causal must then be 1).
- */
+/* Backward with a sliding window (window >= 0 needs causal = 1, else code 2). */
 int fa_oracle_bwd_swa(const float *q, const float *k, const float *v, const float *mask,
                       const float *L, const float *dO, int64_t B, int64_t H, int64_t Hkv,
                       int64_t ql, int64_t kl, int64_t D, float scale, int causal, int64_t window,
@@ -435,53 +492,6 @@ int fa_oracle_bwd_swa(const float *q, const float *k, const float *v, const floa
 {
     if (window >= 0 && !causal)
         return 2;
-    int rc = oracle_validate(q, k, v, B, H, Hkv, ql, kl, D);
-    if (rc)
-        return rc;
-    if (B * H * ql > 0 && (!L || !dO || !dQ))
-        return 1;
-    if (B * Hkv * kl > 0 && (!dK || !dV))
-        return 1;
-    oracle_bwd_problem p = {q, k, v, mask, L, dO, dQ, dK, dV, H, Hkv, ql, kl, D, scale, causal,
-                            window < 0 ? -1 : window};
-    return oracle_bwd_run(&p, B, n_threads);
-}
-
-static int oracle_bwd_run(const oracle_bwd_problem *pp, int64_t B, int n_threads)
-{
-    const oracle_bwd_problem p = *pp;
-    const int64_t Hkv = p.Hkv;
-    const int64_t groups = B * Hkv;
-    if (groups <= 0)
-        return 0;
-    if (n_threads < 1)
-        n_threads = 1;
-    if (n_threads > 256)
-        n_threads = 256;
-    if (n_threads > groups)
-        n_threads = (int)groups;
-    oracle_bwd_job jobs[256];
-    pthread_t tid[256];
-    for (int t = 0; t < n_threads; ++t) {
-        jobs[t].p = &p;
-        jobs[t].begin = groups * t / n_threads;
-        jobs[t].end = groups * (t + 1) / n_threads;
-        jobs[t].failed = 0;
-    }
-    int started = 0;
-    for (int t = 1; t < n_threads; ++t) {
-        if (pthread_create(&tid[t], NULL, oracle_bwd_worker, &jobs[t]) != 0)
-            break;
-        started = t;
-    }
-    for (int t = started + 1; t < n_threads; ++t)
-        oracle_bwd_worker(&jobs[t]);
-    oracle_bwd_worker(&jobs[0]);
-    for (int t = 1; t <= started; ++t)
-        pthread_join(tid[t], NULL);
-    for (int t = 0; t < n_threads; ++t)
-        if (jobs[t].failed)
-            return 4;
-    /* a query head with ql > 0 but kv heads with kl == 0: dQ is zero */
-    return 0;
+    return fa_oracle_bwd_general(q, k, v, mask, L, dO, B, H, Hkv, ql, kl, D, D, scale, causal,
+                                 window, NULL, 0, dQ, dK, dV, n_threads);
 }

@@ -8,7 +8,8 @@ iff j <= max(kl - ql, 0) + i (the page's bottom-right alignment, offset
 clamped at zero). With a sliding window w (which implies the causal rule),
 key j is visible iff off + i - w <= j <= off + i, off = max(kl - ql, 0).
 A row with no visible key gives O = 0 and L = -inf.
-GQA: query head h reads kv head h // (H // Hkv).
+GQA: query head h reads kv head h // (H // Hkv). V (and O) may be wider or
+narrower than Q and K.
 """
 import numpy as np
 
@@ -19,8 +20,9 @@ def attention_f64(q, k, v, mask, scale, causal, window=None):
     v = np.asarray(v, dtype=np.float64)
     B, H, ql, D = q.shape
     Hkv, kl = k.shape[1], k.shape[2]
+    Dv = v.shape[3]
     group = H // Hkv
-    O = np.zeros((B, H, ql, D))
+    O = np.zeros((B, H, ql, Dv))
     L = np.full((B, H, ql), -np.inf)
     off = max(kl - ql, 0)
     for b in range(B):

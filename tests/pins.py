@@ -315,6 +315,37 @@ def pin_window_wide_is_causal(fwd):
         assert np.array_equal(a[0], b[0]) and np.array_equal(a[2], b[2]), w
 
 
+def pin_brute_force_dv(fwd_dv, B, H, Hkv, ql, kl, D, Dv, causal, masked, seed, window=None):
+    """Values wider or narrower than the keys (Dv != D) against the f64
+    textbook definition; fwd_dv(q, k, v, mask, B, H, Hkv, ql, kl, D, Dv,
+    scale, causal, window=...) -> (O [B,H,ql,Dv], O bits, L)."""
+    scale = 1.0 / math.sqrt(D)
+    q = fagen.normal_bf16(seed, 0, (B, H, ql, D))
+    k = fagen.normal_bf16(seed, 1, (B, Hkv, kl, D))
+    v = fagen.normal_bf16(seed, 2, (B, Hkv, kl, Dv))
+    mask = _finite_mask(seed, B, H, ql, kl) if masked else None
+    O, Ob, L = fwd_dv(q, k, v, mask, B, H, Hkv, ql, kl, D, Dv, scale, causal, window=window)
+    assert O.shape == (B, H, ql, Dv)
+    Oref, Lref = attention_f64(_widen(q), _widen(k), _widen(v), mask, scale, causal, window)
+    empty = np.isneginf(Lref)
+    assert np.array_equal(np.isneginf(L), empty), "fully masked rows differ"
+    assert np.all(O[empty] == 0), "empty row O != 0"
+    live = ~empty
+    if live.any():
+        errO = np.abs(O[live] - Oref[live]).max()
+        errL = (np.abs(L[live] - Lref[live]) / np.maximum(1.0, np.abs(Lref[live]))).max()
+        assert errO <= 1e-5, f"O (Dv={Dv}) vs f64 brute force: {errO:.3e}"
+        assert errL <= 1e-5, f"L (Dv={Dv}) vs f64 brute force: {errL:.3e}"
+
+
+# Pins of the forward with a separate value width (fwd_dv callables).
+DV_PINS = [
+    ("brute_dv_wide", lambda f: pin_brute_force_dv(f, 2, 4, 2, 9, 13, 8, 24, True, True, 5)),
+    ("brute_dv_narrow", lambda f: pin_brute_force_dv(f, 1, 2, 1, 11, 7, 24, 8, False, False, 6)),
+    ("brute_dv_window", lambda f: pin_brute_force_dv(f, 1, 2, 2, 12, 12, 16, 8, True, False, 7,
+                                                     window=3)),
+]
+
 ALL_PINS = [
     ("hand_worked", pin_hand_worked),
     ("brute_small", lambda f: pin_brute_force(f, 2, 4, 2, 9, 13, 8, True, True, 1)),

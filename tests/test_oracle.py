@@ -184,3 +184,21 @@ def test_window_negative_is_rejected():
     q, k, v = pins._inputs(82, 1, 1, 1, 4, 4, 8)
     with pytest.raises(ValueError):
         oracle.fwd(q, k, v, None, 1, 1, 1, 4, 4, 8, 0.3, True, window=-1)
+
+
+@pytest.mark.parametrize("D,Dv", [(8, 24), (24, 8), (96, 64), (192, 128), (64, 64)])
+@pytest.mark.parametrize("causal,masked,window", [(False, False, None), (True, True, None),
+                                                  (True, False, 4)])
+def test_value_width_matches_f64_brute_force(D, Dv, causal, masked, window):
+    """Dv != D (keys of one width, values of another) against the f64
+    textbook definition."""
+    pins.pin_brute_force_dv(oracle.fwd_dv, 2, 4, 2, 13, 19, D, Dv, causal, masked,
+                            seed=D * 7 + Dv, window=window)
+
+
+def test_value_width_equal_is_the_plain_forward():
+    q, k, v = pins._inputs(91, 1, 2, 1, 9, 14, 16)
+    a = oracle.fwd(q, k, v, None, 1, 2, 1, 9, 14, 16, 0.3, True)
+    b = oracle.fwd_dv(q, k, v, None, 1, 2, 1, 9, 14, 16, 16, 0.3, True)
+    for x, y in zip(a, b):
+        np.testing.assert_array_equal(x, y)

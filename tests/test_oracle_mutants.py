@@ -1,6 +1,6 @@
 """Planted mistakes in a copy of the oracle must each fail at least one pin.
 
-Each mutant is a one-line edit of oracle/fa_oracle.c of the kind a plausible
+Each mutant is a small edit of oracle/fa_oracle.c of the kind a plausible
 bug would make (a dropped term, a wrong sign, index or unit, a transposed
 operand, a missing guard). The copy is built on the CPU in a temporary
 directory and run through tests/pins.py; the real oracle passes all pins
@@ -18,47 +18,60 @@ from tests import pins
 SRC = os.path.join(os.path.dirname(oracle.__file__), "fa_oracle.c")
 
 MUTANTS = {
-    "mask_in_natural_units": ("s[j] += ORACLE_LOG2E * mr[j];", "s[j] += mr[j];"),
-    "mask_dropped": ("\n    if (p->mask) {", "\n    if (0) {"),
-    "exp_sign_flipped": ("s[j] = exp2f(s[j] - m);", "s[j] = exp2f(m - s[j]);"),
-    "causal_off_by_one": ("\n        for (int64_t j = q_abs + 1; j < kl; ++j)",
-                          "\n        for (int64_t j = q_abs; j < kl; ++j)"),
-    "causal_offset_dropped": ("\n    const int64_t q_abs = (kl > ql ? kl - ql : 0) + i;",
-                              "\n    const int64_t q_abs = i;"),
-    "causal_offset_unclamped": [("\n    const int64_t q_abs = (kl > ql ? kl - ql : 0) + i;",
-                                 "\n    const int64_t q_abs = (kl - ql) + i;"),
-                                ("\n        for (int64_t j = q_abs + 1; j < kl; ++j)",
-                                 "\n        for (int64_t j = (q_abs + 1 > 0 ? q_abs + 1 : 0); j < kl; ++j)")],
-    "gqa_modulo_map": ("const int64_t kvh = h / (p->H / p->Hkv);",
-                       "const int64_t kvh = h % p->Hkv;"),
-    "k_transposed": ("\n            dot += qr[d] * kh[j * D + d];",
-                     "\n            dot += qr[d] * kh[d * kl + j];"),
-    "scale_dropped": ("s[j] = dot * q_scale;", "s[j] = dot * ORACLE_LOG2E;"),
-    "log2e_dropped": ("const float q_scale = p->scale * ORACLE_LOG2E;",
-                      "const float q_scale = p->scale;"),
-    "lse_without_max": ("*l_out = m * ORACLE_LN2 + logf(sum);", "*l_out = logf(sum);"),
-    "lse_base2_max": ("*l_out = m * ORACLE_LN2 + logf(sum);", "*l_out = m + logf(sum);"),
-    "no_normalisation": ("const float w = s[j] / safe;", "const float w = s[j];"),
-    "infinite_sentinel": ("float m = -FLT_MAX / 2.0f;", "float m = -INFINITY;"),
-    "no_empty_row_guard": ("const float safe = (sum == 0.0f) ? 1.0f : sum;",
-                           "const float safe = sum;"),
-    "v_from_head_zero": ("\n    const float *vh = p->v + (b * p->Hkv + kvh) * kl * D;\n\n",
-                         "\n    const float *vh = p->v + (b * p->Hkv) * kl * D;\n\n"),
-    "k_batch_dropped": ("const float *qr = p->q + row * D;\n    const float *kh = p->k + (b * p->Hkv + kvh) * kl * D;",
-                        "const float *qr = p->q + row * D;\n    const float *kh = p->k + kvh * kl * D;"),
-    "v_row_off_by_one": ("const float *vr = vh + j * D;",
-                         "const float *vr = vh + (j + 1 < kl ? j + 1 : j) * D;"),
-    "window_off_by_one": ("for (int64_t j = 0; j < q_abs - p->window && j < kl; ++j)\n            s[j]",
-                          "for (int64_t j = 0; j <= q_abs - p->window && j < kl; ++j)\n            s[j]"),
-    "window_too_wide": ("for (int64_t j = 0; j < q_abs - p->window && j < kl; ++j)\n            s[j]",
-                        "for (int64_t j = 0; j < q_abs - p->window - 1 && j < kl; ++j)\n            s[j]"),
-    "window_offset_dropped": ("for (int64_t j = 0; j < q_abs - p->window && j < kl; ++j)\n            s[j]",
-                              "for (int64_t j = 0; j < i - p->window && j < kl; ++j)\n            s[j]"),
-    "window_ignored": ("\n    if (p->window >= 0) {", "\n    if (0) {"),
-    "window_without_causal": ("oracle_problem p = {q, k, v, mask, H, Hkv, ql, kl, D, scale, 1, window};",
-                              "oracle_problem p = {q, k, v, mask, H, Hkv, ql, kl, D, scale, 0, window};"),
-    "max_skips_last_key": ("for (int64_t j = 0; j < kl; ++j)\n        if (s[j] > m)",
-                           "for (int64_t j = 0; j + 1 < kl; ++j)\n        if (s[j] > m)"),
+    "mask_dropped": ("    if (p->mask)\n        s += p->mask[row * p->kl + j];", ""),
+    "mask_in_base2_units": ("s += p->mask[row * p->kl + j];",
+                            "s += 1.44269504f * p->mask[row * p->kl + j];"),
+    "mask_of_first_head": ("s += p->mask[row * p->kl + j];",
+                           "s += p->mask[(row % p->ql) * p->kl + j];"),
+    "exp_sign_flipped": ("e[j] = expf(e[j] - m);", "e[j] = expf(m - e[j]);"),
+    "exp_base2": ("e[j] = expf(e[j] - m);", "e[j] = exp2f(e[j] - m);"),
+    "causal_off_by_one": ("if ((p->causal || p->window >= 0) && j > pos)",
+                          "if ((p->causal || p->window >= 0) && j >= pos)"),
+    "causal_offset_dropped": ("return (p->kl > p->ql ? p->kl - p->ql : 0) + i;", "return i;"),
+    "causal_offset_unclamped": ("return (p->kl > p->ql ? p->kl - p->ql : 0) + i;",
+                                "return (p->kl - p->ql) + i;"),
+    "gqa_modulo_map": ("*kvhead = b * p->Hkv + h / (p->H / p->Hkv);",
+                       "*kvhead = b * p->Hkv + h % p->Hkv;"),
+    "k_transposed": ("dot += qr[d] * kh[j * p->D + d];", "dot += qr[d] * kh[d * p->kl + j];"),
+    "dot_drops_last_dim": ("for (int64_t d = 0; d < p->D; ++d)\n        dot +=",
+                           "for (int64_t d = 0; d + 1 < p->D; ++d)\n        dot +="),
+    "scale_dropped": ("float s = p->scale * dot;", "float s = dot;"),
+    "scale_squared": ("float s = p->scale * dot;", "float s = p->scale * p->scale * dot;"),
+    "lse_without_max": ("*l = m + logf(z);", "*l = logf(z);"),
+    "lse_base2_sum": ("*l = m + logf(z);", "*l = m + log2f(z);"),
+    "no_normalisation": ("const float w = e[j] / z;", "const float w = e[j];"),
+    "no_empty_row_guard": ("    if (m == -INFINITY) { /* no visible key */\n        *l = -INFINITY;"
+                           "\n        return;\n    }\n", ""),
+    "v_from_head_zero": ("const float *vh = p->v + kvh * p->kl * p->Dv;\n    float m",
+                         "const float *vh = p->v + (kvh - kvh % p->Hkv) * p->kl * p->Dv;\n    float m"),
+    "k_batch_dropped": ("const float *kh = p->k + kvh * p->kl * p->D;\n    const float *vh",
+                        "const float *kh = p->k + (kvh % p->Hkv) * p->kl * p->D;\n    const float *vh"),
+    "v_row_off_by_one": ("o[d] += w * vh[j * p->Dv + d];",
+                         "o[d] += w * vh[(j + 1 < p->kl ? j + 1 : j) * p->Dv + d];"),
+    "max_skips_last_key": ("if (e[j] > m)\n            m = e[j];",
+                           "if (e[j] > m && j + 1 < p->kl)\n            m = e[j];"),
+    "window_off_by_one": ("if (p->window >= 0 && j < pos - p->window)",
+                          "if (p->window >= 0 && j <= pos - p->window)"),
+    "window_too_wide": ("if (p->window >= 0 && j < pos - p->window)",
+                        "if (p->window >= 0 && j < pos - p->window - 1)"),
+    "window_offset_dropped": ("if (p->window >= 0 && j < pos - p->window)",
+                              "if (p->window >= 0 && j < pos - (p->kl > p->ql ? p->kl - p->ql : 0)"
+                              " - p->window)"),
+    "window_ignored": ("if (p->window >= 0 && j < pos - p->window)",
+                       "if (0 && j < pos - p->window)"),
+    "window_without_causal": [("if ((p->causal || p->window >= 0) && j > pos)",
+                               "if (p->causal && j > pos)"),
+                              ("D, D, scale, 1, window, rows,", "D, D, scale, 0, window, rows,")],
+    # value width: V or O addressed with the key width where it differs (the
+    # smaller of the two widths, so that every access stays inside the buffers)
+    "v_head_stride_uses_D": ("const float *vh = p->v + kvh * p->kl * p->Dv;\n    float m",
+                             "const float *vh = p->v + kvh * p->kl * (p->D < p->Dv ? p->D : p->Dv);"
+                             "\n    float m"),
+    "v_row_stride_uses_D": ("o[d] += w * vh[j * p->Dv + d];",
+                            "o[d] += w * vh[j * (p->D < p->Dv ? p->D : p->Dv) + d];"),
+    "output_width_uses_D": ("forward_row(c->p, c->rows ? c->rows[t] : t, c->O + t * c->p->Dv,",
+                            "forward_row(c->p, c->rows ? c->rows[t] : t, "
+                            "c->O + t * (c->p->D < c->p->Dv ? c->p->D : c->p->Dv),"),
 }
 
 
@@ -81,11 +94,13 @@ def _build_mutant(tmp, name, edits):
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_pins_catch_planted_mistake(name):
     with tempfile.TemporaryDirectory() as tmp:
-        fwd = oracle.bind(_build_mutant(tmp, name, MUTANTS[name]))
+        path = _build_mutant(tmp, name, MUTANTS[name])
+        fwd, fwd_dv = oracle.bind(path), oracle.bind_dv(path)
         caught = []
-        for pin_name, pin in pins.ALL_PINS:
+        for pin_name, pin, f in ([(n, p, fwd) for n, p in pins.ALL_PINS]
+                                 + [(n, p, fwd_dv) for n, p in pins.DV_PINS]):
             try:
-                pin(fwd)
+                pin(f)
             except (AssertionError, ValueError, FloatingPointError):
                 caught.append(pin_name)
         assert caught, f"no pin catches mutant {name}"
@@ -93,27 +108,36 @@ def test_pins_catch_planted_mistake(name):
 
 # Planted mistakes in the backward part of the oracle, caught by tests/pins_bwd.py.
 BWD_MUTANTS = {
-    "bwd_dq_scale_dropped": ("dqr[d] += p->scale * ds * kh[j * D + d];",
-                             "dqr[d] += ds * kh[j * D + d];"),
-    "bwd_ds_sign_flipped": ("const float ds = pr[j] * (s[j] - d_i);",
-                            "const float ds = pr[j] * (d_i - s[j]);"),
-    "bwd_D_dropped": ("d_i += pr[j] * dp;", "d_i += 0.0f * dp;"),
-    "bwd_p_base2": ("expf(s[j] - l_i)", "exp2f(s[j] - l_i)"),
-    "bwd_causal_off_by_one": ("for (int64_t j = q_abs + 1; j < kl; ++j)\n                    s[j] = -INFINITY;",
-                              "for (int64_t j = q_abs + 2; j < kl; ++j)\n                    s[j] = -INFINITY;"),
-    "bwd_dk_uses_k": ("dkh[j * D + d] += p->scale * ds * qr[d];",
-                      "dkh[j * D + d] += p->scale * ds * kh[j * D + d];"),
-    "bwd_dv_uses_q": ("dvh[j * D + d] += pr[j] * dor[d];", "dvh[j * D + d] += pr[j] * qr[d];"),
-    "bwd_group_first_head_only": ("for (int64_t h = kvh * G; h < (kvh + 1) * G; ++h) {",
-                                  "for (int64_t h = kvh * G; h < kvh * G + 1; ++h) {"),
-    "bwd_mask_ignored": ("if (p->mask) {\n                    const float m = p->mask[row * kl + j];",
-                         "if (0) {\n                    const float m = p->mask[row * kl + j];"),
-    "bwd_dp_uses_q": ("dp += dor[d] * vh[j * D + d];", "dp += qr[d] * vh[j * D + d];"),
-    "bwd_mask_base2": ("s[j] += m;", "s[j] += 1.44269504f * m;"),
-    "bwd_lse_ignored": ("expf(s[j] - l_i)", "expf(s[j])"),
-    "bwd_window_off_by_one": ("for (int64_t j = 0; j < q_abs - p->window && j < kl; ++j)\n                    s[j] = -INFINITY;",
-                              "for (int64_t j = 0; j <= q_abs - p->window && j < kl; ++j)\n                    s[j] = -INFINITY;"),
-    "bwd_window_ignored": ("if (p->window >= 0) {\n                for", "if (0) {\n                for"),
+    "bwd_dq_scale_dropped": ("const float coef = p->scale * (P[j] * (dP[j] - d_i));",
+                             "const float coef = (P[j] * (dP[j] - d_i));"),
+    "bwd_ds_sign_flipped": ("const float coef = p->scale * (P[j] * (dP[j] - d_i));",
+                            "const float coef = p->scale * (P[j] * (d_i - dP[j]));"),
+    "bwd_D_dropped": ("d_i += P[j] * dp;", "d_i += 0.0f * dp;"),
+    "bwd_p_base2": [("P[j] = (s == -INFINITY) ? 0.0f : expf(s - l_i);",
+                     "P[j] = (s == -INFINITY) ? 0.0f : exp2f(s - l_i);"),
+                    ("const float P = (s == -INFINITY) ? 0.0f : expf(s - c->L[row]);",
+                     "const float P = (s == -INFINITY) ? 0.0f : exp2f(s - c->L[row]);")],
+    "bwd_lse_ignored": [("P[j] = (s == -INFINITY) ? 0.0f : expf(s - l_i);",
+                         "P[j] = (s == -INFINITY) ? 0.0f : expf(s);"),
+                        ("const float P = (s == -INFINITY) ? 0.0f : expf(s - c->L[row]);",
+                         "const float P = (s == -INFINITY) ? 0.0f : expf(s);")],
+    "bwd_keys_position_off_by_one": ("if (!key_allowed(p, pos, j))\n                continue;\n"
+                                     "            const float *qr",
+                                     "if (!key_allowed(p, pos + 1, j))\n                continue;\n"
+                                     "            const float *qr"),
+    "bwd_dk_uses_k": ("dk[d] += coef * qr[d];", "dk[d] += coef * kh[j * p->D + d];"),
+    "bwd_dk_scale_dropped": ("const float coef = p->scale * (P * (dp - c->Di[t]));",
+                             "const float coef = (P * (dp - c->Di[t]));"),
+    "bwd_dv_uses_q": ("dv[d] += P * gr[d];", "dv[d] += P * qr[d];"),
+    "bwd_dv_missing_p": ("dv[d] += P * gr[d];", "dv[d] += gr[d];"),
+    "bwd_group_first_head_only": ("for (int64_t r = 0; r < c->G * p->ql; ++r) {",
+                                  "for (int64_t r = 0; r < p->ql; ++r) {"),
+    "bwd_D_of_group_zero": ("(dp - c->Di[t])", "(dp - c->Di[r])"),
+    "bwd_dp_uses_q": ("dp += gr[d] * vh[j * p->Dv + d];\n            dP[j] = dp;",
+                      "dp += qr[d] * vh[j * p->Dv + d];\n            dP[j] = dp;"),
+    "bwd_keys_dp_uses_q": ("dp += gr[d] * vh[j * p->Dv + d];\n            const float coef",
+                           "dp += qr[d] * vh[j * p->Dv + d];\n            const float coef"),
+    "bwd_dq_uses_q": ("dq[d] += coef * kh[j * p->D + d];", "dq[d] += coef * qr[d];"),
 }
 
 
