@@ -43,6 +43,10 @@ def _load():
         lib.fagen_mask_f32.restype = ctypes.c_int
         lib.fagen_word.argtypes = [ctypes.c_uint64, ctypes.c_uint32, ctypes.c_uint64]
         lib.fagen_word.restype = ctypes.c_uint64
+        lib.fagen_lcg_f32.argtypes = [ctypes.c_uint64, ctypes.c_uint64, ctypes.c_void_p]
+        lib.fagen_lcg_f32.restype = None
+        lib.fagen_lcg_bf16.argtypes = [ctypes.c_uint64, ctypes.c_uint64, ctypes.c_void_p]
+        lib.fagen_lcg_bf16.restype = None
         _lib = lib
     return _lib
 
@@ -81,6 +85,25 @@ def mask_f32(seed, B, H, ql, kl, p_masked=0.1, n_full_rows=4):
     if rc != 0:
         raise RuntimeError(f"fagen_mask_f32 failed ({rc})")
     return mask, rows
+
+
+def lcg_f32(seed, shape):
+    """The method's test inputs: values of its test page's 64-bit LCG from
+    `seed` (pseudo_random_f32 there), f32 in [-0.5, 0), of `shape`."""
+    n = int(np.prod(shape)) if len(shape) else 1
+    out = np.empty(n, dtype=np.float32)
+    if n:
+        _load().fagen_lcg_f32(seed & (2**64 - 1), n, out.ctypes.data)
+    return out.reshape(shape)
+
+
+def lcg_bf16(seed, shape):
+    """lcg_f32 rounded to bf16 (round to nearest even); uint16 bits of `shape`."""
+    n = int(np.prod(shape)) if len(shape) else 1
+    out = np.empty(n, dtype=np.uint16)
+    if n:
+        _load().fagen_lcg_bf16(seed & (2**64 - 1), n, out.ctypes.data)
+    return out.reshape(shape)
 
 
 @dataclass(frozen=True)

@@ -22,6 +22,15 @@
  *   - mask: each entry is -inf with probability p (uniform < p), else 0; then
  *     for every (b,h) a partial Fisher-Yates shuffle of the query rows picks
  *     n_full distinct rows that are set entirely to -inf.
+ *   - the method's own test inputs (fagen_lcg_*): the 64-bit linear
+ *     congruential generator of its test page ("mlx-native 0.9.0",
+ *     tests/test_flash_attn_train.rs, section "Test helpers",
+ *     pseudo_random_f32): state <- state * 6364136223846793005 +
+ *     1442695040888963407 (mod 2^64), starting from the seed; each value is
+ *     the top 31 bits of the new state, converted to f32 (round to nearest),
+ *     divided by the f32 value of 2^32 - 1 (which is 2^32) and lowered by 0.5,
+ *     all in f32. The values lie in [-0.5, 0): the top 31 bits are below 2^31.
+ *     Sequential by construction (one stream per seed).
  */
 #include <math.h>
 #include <pthread.h>
@@ -177,4 +186,26 @@ int fagen_mask_f32(uint64_t seed, uint32_t stream_bern, uint32_t stream_rows,
     }
     free(perm);
     return 0;
+}
+
+/* n values of the test page's LCG from `seed` (f32, in [-0.5, 0)). */
+void fagen_lcg_f32(uint64_t seed, uint64_t n, float *out)
+{
+    uint64_t state = seed;
+    const float denom = (float)UINT32_MAX; /* rounds to 2^32 */
+    for (uint64_t i = 0; i < n; ++i) {
+        state = state * 6364136223846793005ULL + 1442695040888963407ULL;
+        out[i] = (float)(state >> 33) / denom - 0.5f;
+    }
+}
+
+/* The same values rounded to bf16 (round to nearest even), as raw bits. */
+void fagen_lcg_bf16(uint64_t seed, uint64_t n, uint16_t *out)
+{
+    uint64_t state = seed;
+    const float denom = (float)UINT32_MAX;
+    for (uint64_t i = 0; i < n; ++i) {
+        state = state * 6364136223846793005ULL + 1442695040888963407ULL;
+        out[i] = f32_to_bf16_rne((float)(state >> 33) / denom - 0.5f);
+    }
 }

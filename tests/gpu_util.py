@@ -41,13 +41,19 @@ def bf16_step(x):
     return np.exp2(np.floor(np.log2(ax)) - 7)
 
 
-def compare(o_gpu, l_gpu, o_bits, ob_ref, l_ref, tol_o, tol_l, label="", one_step_ok=False):
+def compare(o_gpu, l_gpu, o_bits, ob_ref, l_ref, tol_o, tol_l, label="", o_ref_f32=None):
     """Element-wise parity: fully masked rows exact (O = +0 bits, L = -inf),
-    every other element within the absolute bounds; no NaN anywhere. With
-    one_step_ok, an O element may also differ by one bf16 rounding step of the
-    reference value (for inputs whose scores are far larger than those of the
-    five workloads, where f32 evaluation order alone moves O across rounding
-    boundaries). Returns (max |dO|, max |dL|, relative RMS of dO)."""
+    every other element within the absolute bounds; no NaN anywhere.
+
+    O is compared with the oracle's O rounded to bf16 (as the method's page
+    compares it), within tol_o. With o_ref_f32 (the oracle's unrounded f32 O)
+    the bound is instead measured against that value: the GPU's bf16 O may
+    differ from it by tol_o plus half a bf16 rounding step (the rounding of
+    the GPU's own f32 result). This is the bound for inputs whose O elements
+    reach |O| >= 1, where one bf16 step (2^-7 relative) exceeds the absolute
+    tolerance, so that an error far below tol_o can still move O across a
+    rounding boundary of the oracle's value. Returns (max |dO| against the
+    rounded oracle, max |dL|, relative RMS of dO)."""
     o_ref = widen(ob_ref)
     assert not np.isnan(o_gpu).any() and not np.isnan(l_gpu).any(), f"{label}: NaN in output"
     dead = np.isneginf(l_ref)
@@ -60,9 +66,14 @@ def compare(o_gpu, l_gpu, o_bits, ob_ref, l_ref, tol_o, tol_l, label="", one_ste
     d_l = np.abs(l_gpu[live] - l_ref[live])
     err_o, err_l = float(d_o.max()), float(d_l.max())
     rms = float(np.sqrt((d_o ** 2).mean() / max((o_ref[live] ** 2).mean(), 1e-30)))
-    if one_step_ok:
-        excess = d_o - np.maximum(tol_o, bf16_step(o_ref[live]) * 1.001)
-        assert excess.max() <= 0, f"{label}: |dO| beyond one bf16 step: {err_o:.3e}"
+    if o_ref_f32 is not None:
+        of = np.asarray(o_ref_f32, np.float32)[live]
+        g = o_gpu[live]
+        mag = np.maximum(np.abs(of) + tol_o, np.abs(g))
+        excess = np.abs(g - of) - (tol_o + 0.5 * bf16_step(mag))
+        worst = float(excess.max())
+        assert worst <= 0, (f"{label}: |dO| against the unrounded oracle exceeds tol + half a "
+                            f"bf16 step by {worst:.3e}")
     else:
         assert err_o <= tol_o, f"{label}: max|dO| = {err_o:.3e} > {tol_o:.1e}"
     assert err_l <= tol_l, f"{label}: max|dL| = {err_l:.3e} > {tol_l:.1e}"

@@ -95,3 +95,37 @@ def test_workloads_match_their_recipes():
     assert w5.metric_flop == 4 * 2 * 16 * 8192 * 8192 * 256 // 2
     w4 = fagen.WORKLOADS["d64_b8_h16_q4096_k4096_causal"]
     assert w4.metric_flop == 274877906944
+
+
+def _lcg_reference(seed, n):
+    """The page's LCG written out with Python integers and numpy f32 steps:
+    state <- state * 6364136223846793005 + 1442695040888963407 (mod 2^64),
+    value = f32(state >> 33) / f32(2^32 - 1) - 0.5 in f32."""
+    state, out = seed, []
+    for _ in range(n):
+        state = (state * 6364136223846793005 + 1442695040888963407) % 2**64
+        top = np.float32(state >> 33)  # 31-bit integer, rounded to nearest f32
+        out.append(np.float32(top / np.float32(2**32 - 1)) - np.float32(0.5))
+    return np.array(out, dtype=np.float32)
+
+
+def test_page_lcg_matches_its_definition():
+    for seed in (fagen.SEED_BASE, fagen.SEED_BASE + 1, fagen.SEED_BASE + 203, 0, 2**64 - 1):
+        got = fagen.lcg_f32(seed, (257,))
+        np.testing.assert_array_equal(got, _lcg_reference(seed, 257))
+
+
+def test_page_lcg_range_is_below_zero():
+    """The page's comment says [-0.5, 0.5]; the top 31 bits over 2^32 make it
+    [-0.5, 0)."""
+    x = fagen.lcg_f32(fagen.SEED_BASE + 7, (200000,))
+    assert x.min() >= -0.5 and x.max() < 0.0
+    assert abs(float(x.mean()) + 0.25) < 0.005
+
+
+def test_page_lcg_bf16_is_torch_rounding():
+    import torch
+    x = fagen.lcg_f32(fagen.SEED_BASE + 11, (4096,))
+    b = fagen.lcg_bf16(fagen.SEED_BASE + 11, (4096,))
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(b, ref)

@@ -70,11 +70,11 @@ def test_mask_options_match_oracle(B, H, Hkv, ql, kl, D, causal, window, mb, mh,
     m = _finite_mask(w.seed, mb, mh, ql, kl)
     dense = np.broadcast_to(m, (B, H, ql, kl)).copy()
     o, l, bits = _run_ex(inp, w, _dev_mask(m, bf16), causal, window)
-    _, ob, lr = oracle.fwd(inp["q"], inp["k"], inp["v"], dense, B, H, Hkv, ql, kl, D, w.scale,
-                           causal, window=window)
+    of, ob, lr = oracle.fwd(inp["q"], inp["k"], inp["v"], dense, B, H, Hkv, ql, kl, D, w.scale,
+                            causal, window=window)
     tol_o, tol_l = gu.tolerances(kl)
     eo, el, rms = gu.compare(o, l, bits, ob, lr, tol_o, tol_l, f"mask {B,H,ql,kl,D} bf16={bf16}",
-                             one_step_ok=True)
+                             o_ref_f32=of)
     assert rms <= 2e-3, rms
     print(f"mask {(B, H, ql, kl, D, mb, mh)} bf16={bf16}: dO={eo:.3e} dL={el:.3e} "
           f"empty rows={int(np.isneginf(lr).sum())}")
@@ -159,11 +159,10 @@ def test_broadcast_bf16_mask_at_scale_sampled_rows():
     rows = np.unique(np.concatenate([np.arange(200), rng.integers(0, B * H * ql, 200),
                                      (B * H - 1) * ql + np.arange(ql - 64, ql)])).astype(np.int64)
     dense = np.broadcast_to(m, (B, H, ql, kl))
-    _, ob, lr = oracle.fwd_rows(inp["q"], inp["k"], inp["v"], np.ascontiguousarray(dense), B, H,
-                                H, ql, kl, D, w.scale, True, rows)
+    of, ob, lr = oracle.fwd_rows(inp["q"], inp["k"], inp["v"], np.ascontiguousarray(dense), B,
+                                 H, H, ql, kl, D, w.scale, True, rows)
     o2, l2, b2 = o.reshape(-1, D)[rows], l.reshape(-1)[rows], bits.reshape(-1, D)[rows]
-    eo, el, rms = gu.compare(o2, l2, b2, ob, lr, 1e-2, 1e-2, "mask 2k broadcast",
-                             one_step_ok=True)
+    eo, el, rms = gu.compare(o2, l2, b2, ob, lr, 1e-2, 1e-2, "mask 2k broadcast", o_ref_f32=of)
     assert rms <= 2e-3, rms
     print(f"mask 2k broadcast: {rows.size} rows dO={eo:.3e} dL={el:.3e} relRMS={rms:.2e}")
 

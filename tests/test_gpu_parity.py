@@ -3,11 +3,11 @@ the same seeded inputs (run on an MI355X; these tests are marked gpu).
 
 Bounds (absolute): O <= 5e-3 and L <= 3e-3 while kl <= 256, 1e-2 for both at
 longer keys; fully masked rows exactly O = +0, L = -inf. At the training-scale
-sizes the oracle computes a sample of rows (every row of the first 160
-queries of two heads, tile-boundary rows and random rows); properties that
-hold at any size are checked on every row.
+sizes every row is compared too, and properties that hold at any size are
+checked on every row.
 """
 import math
+import time
 
 import numpy as np
 import pytest
@@ -41,30 +41,28 @@ def test_small_workloads_match_oracle(name):
                 assert np.all(bits[b, h, full[b, h]] == 0)
 
 
-def _sample_rows(w, rng):
-    rows = set()
-    for (b, h) in [(0, 0), (w.B - 1, w.H - 1)]:
-        base = (b * w.H + h) * w.ql
-        rows.update(base + i for i in range(160))
-        rows.update(base + i for i in (255, 256, 511, 512, w.ql // 2, w.ql - 129, w.ql - 128,
-                                       w.ql - 2, w.ql - 1))
-    rows.update(int(r) for r in rng.integers(0, w.B * w.H * w.ql, size=96))
-    return np.array(sorted(rows), dtype=np.int64)
-
-
 @pytest.mark.parametrize("name", LARGE)
-def test_large_workloads_sampled_rows(name):
+def test_large_workloads_all_rows(name):
+    """The two training-scale workloads, every row of O and L against the
+    oracle (about 5 s and 20 s of oracle time on 16 host threads)."""
     w = fagen.WORKLOADS[name]
     print(f"case {name}", flush=True)
     inp = fagen.generate(w)
     o, l, bits = gu.run(inp, w)
-    rng = np.random.default_rng(w.seed & 0xFFFFFFFF)
-    rows = _sample_rows(w, rng)
-    _, ob, lr = oracle.fwd_workload(w, inp, rows=rows)
+    t0 = time.perf_counter()
+    _, ob, lr = oracle.fwd_workload(w, inp)
+    print(f"{name}: oracle over all {w.B * w.H * w.ql} rows in {time.perf_counter() - t0:.1f} s",
+          flush=True)
     tol_o, tol_l = gu.tolerances(w.kl)
-    o2, l2, b2 = o.reshape(-1, w.D)[rows], l.reshape(-1)[rows], bits.reshape(-1, w.D)[rows]
-    eo, el, rms = gu.compare(o2, l2, b2, ob, lr, tol_o, tol_l, name)
-    print(f"{name}: {rows.size} rows, max|dO|={eo:.3e} max|dL|={el:.3e} relRMS(O)={rms:.3e}")
+    eo, el, rms = gu.compare(o, l, bits, ob, lr, tol_o, tol_l, name)
+    # errors per query tile position: the compensated first tile and the
+    # plain tiles the bench times
+    o_ref = gu.widen(ob)
+    first = 256 if w.D <= 128 else 128
+    d = np.abs(o - o_ref)
+    print(f"{name}: all rows max|dO|={eo:.3e} max|dL|={el:.3e} relRMS(O)={rms:.3e}; "
+          f"first tile max|dO|={d[:, :, :first].max():.3e}, "
+          f"other tiles max|dO|={d[:, :, first:].max():.3e}")
     assert rms <= 1e-2
 
     # properties on every row: finite, O inside the convex hull bound of V,
@@ -131,12 +129,14 @@ def test_other_scales(D, scale):
     print(f"case scale={scale} D={D}", flush=True)
     inp = fagen.generate(w)
     o, l, bits = gu.run(inp, w, scale=scale)
-    _, ob, lr = oracle.fwd(inp["q"], inp["k"], inp["v"], None, w.B, w.H, w.Hkv, w.ql, w.kl, w.D,
-                           scale, True)
+    of, ob, lr = oracle.fwd(inp["q"], inp["k"], inp["v"], None, w.B, w.H, w.Hkv, w.ql, w.kl,
+                            w.D, scale, True)
     # at scale 0.5 the scores are up to 4x (D=64) or 8x (D=256) those of the
-    # workloads' 1/sqrt(D): rows are nearly one-hot and |O| reaches |V|, so an
-    # O element may differ from the oracle by one bf16 rounding step.
-    gu.compare(o, l, bits, ob, lr, 5e-3, 3e-3, f"scale {scale}", one_step_ok=abs(scale) > 0.3)
+    # workloads' 1/sqrt(D): rows are nearly one-hot and |O| reaches |V|, where
+    # one bf16 step exceeds 5e-3: O is bounded against the unrounded oracle
+    # (5e-3 plus half a bf16 step).
+    gu.compare(o, l, bits, ob, lr, 5e-3, 3e-3, f"scale {scale}",
+               o_ref_f32=of if abs(scale) > 0.3 else None)
 
 
 def _times4(bits):
@@ -160,10 +160,10 @@ def test_large_outputs_take_the_compensated_redo(D, causal):
     inp = dict(fagen.generate(w))
     inp["v"] = _times4(inp["v"])
     o, l, bits = gu.run(inp, w)
-    _, ob, lr = oracle.fwd_workload(w, inp)
+    of, ob, lr = oracle.fwd_workload(w, inp)
     big_rows = int((np.abs(gu.widen(ob)) >= 1).any(axis=-1).sum())
     assert big_rows >= 20, big_rows
-    eo, el, rms = gu.compare(o, l, bits, ob, lr, 1e-2, 1e-2, f"redo D={D}", one_step_ok=True)
+    eo, el, rms = gu.compare(o, l, bits, ob, lr, 1e-2, 1e-2, f"redo D={D}", o_ref_f32=of)
     print(f"redo D={D} causal={causal}: {big_rows} rows with |O|>=1, dO={eo:.3e} dL={el:.3e} "
           f"relRMS={rms:.2e}")
     assert rms <= 5e-3  # the plain bf16-P rows carry about 2^-10 relative
@@ -199,19 +199,16 @@ def test_errors_raise_from_binding():
         fa.train_fwd(q[:, :1], q[:, :1], q[:, :1], scale=math.nan)
 
 
-def test_head_dim_128_gqa_4k_sampled_rows():
+def test_head_dim_128_gqa_4k_all_rows():
     """head_dim 128 at a training shape (B2, 32 query heads on 8 kv heads,
-    4096 tokens, causal), sampled rows against the oracle, as for the two
-    training-scale workloads."""
+    4096 tokens, causal): every row against the oracle."""
     w = fagen.Workload("d128_b2_h32kv8_q4096_k4096_causal", 2, 32, 8, 4096, 4096, 128, True,
                        seed_offset=8000)
     print(f"case {w.name}", flush=True)
     inp = fagen.generate(w)
     o, l, bits = gu.run(inp, w)
-    rows = _sample_rows(w, np.random.default_rng(8000))
-    _, ob, lr = oracle.fwd_workload(w, inp, rows=rows)
-    o2, l2, b2 = o.reshape(-1, w.D)[rows], l.reshape(-1)[rows], bits.reshape(-1, w.D)[rows]
-    eo, el, rms = gu.compare(o2, l2, b2, ob, lr, 1e-2, 1e-2, w.name)
-    print(f"{w.name}: {rows.size} rows, max|dO|={eo:.3e} max|dL|={el:.3e} relRMS(O)={rms:.3e}")
+    _, ob, lr = oracle.fwd_workload(w, inp)
+    eo, el, rms = gu.compare(o, l, bits, ob, lr, 1e-2, 1e-2, w.name)
+    print(f"{w.name}: all rows max|dO|={eo:.3e} max|dL|={el:.3e} relRMS(O)={rms:.3e}")
     assert rms <= 1e-2
     assert np.isfinite(o).all() and np.isfinite(l).all()
