@@ -249,7 +249,8 @@ def train_fwd_split(q, k, v, n_split, scale=None, causal=False, workspace=None, 
     import torch
 
     O, L, (B, H, Hkv, ql, kl, D), scale, s = _fwd_outputs(q, k, v, scale, out, lse, stream)
-    need = fa_train_fwd_split_workspace(B, H, ql, D, n_split)
+    # (no keys: the library reads no workspace)
+    need = fa_train_fwd_split_workspace(B, H, ql, D, n_split) if kl > 0 else 0
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     _check_workspace(workspace, need, q.device)
@@ -309,7 +310,8 @@ def paged_fwd(q, k_cache, v_cache, block_table, seq_lens, scale=None, causal=Fal
     _check_out(L, "lse", q.device, torch.float32, (B, H, ql))
     ws_ptr, ws_bytes = 0, 0
     if n_split > 0:
-        need = fa_train_fwd_split_workspace(B, H, ql, D, n_split)
+        # (a table that addresses no keys needs no workspace)
+        need = fa_train_fwd_split_workspace(B, H, ql, D, n_split) if max_blocks * bs > 0 else 0
         if workspace is None:
             workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
         _check_workspace(workspace, need, q.device)
@@ -400,7 +402,7 @@ def train_fwd_strided(q, k, v, mask=None, scale=None, causal=False, window=None,
     _check_out(L, "lse", q.device, torch.float32, (B, H, ql))
     ws_bytes = 0
     if n_split > 0:
-        ws_bytes = fa_train_fwd_split_workspace(B, H, ql, D, n_split)
+        ws_bytes = fa_train_fwd_split_workspace(B, H, ql, D, n_split) if kl > 0 else 0
         if workspace is None:
             workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
         _check_workspace(workspace, ws_bytes, q.device)

@@ -46,14 +46,14 @@ def compare(o_gpu, l_gpu, o_bits, ob_ref, l_ref, tol_o, tol_l, label="", o_ref_f
     every other element within the absolute bounds; no NaN anywhere.
 
     O is compared with the oracle's O rounded to bf16 (as the method's page
-    compares it), within tol_o. With o_ref_f32 (the oracle's unrounded f32 O)
-    the bound is instead measured against that value: the GPU's bf16 O may
-    differ from it by tol_o plus half a bf16 rounding step (the rounding of
-    the GPU's own f32 result). This is the bound for inputs whose O elements
-    reach |O| >= 1, where one bf16 step (2^-7 relative) exceeds the absolute
-    tolerance, so that an error far below tol_o can still move O across a
-    rounding boundary of the oracle's value. Returns (max |dO| against the
-    rounded oracle, max |dL|, relative RMS of dO)."""
+    compares it), within tol_o. Where one bf16 step of the reference value
+    exceeds tol_o (|O| >= 1 at 5e-3, |O| >= 2 at 1e-2), that comparison is
+    ill-posed: two correct f32 results a few ulps apart can round to bf16
+    values one step apart, more than the tolerance. There (given o_ref_f32,
+    the oracle's unrounded O) the GPU's bf16 O is bounded against the
+    unrounded value: tol_o plus half a bf16 step (the rounding of the GPU's
+    own f32 result). Returns (max |dO| against the rounded oracle, max |dL|,
+    relative RMS of dO)."""
     o_ref = widen(ob_ref)
     assert not np.isnan(o_gpu).any() and not np.isnan(l_gpu).any(), f"{label}: NaN in output"
     dead = np.isneginf(l_ref)
@@ -69,11 +69,13 @@ def compare(o_gpu, l_gpu, o_bits, ob_ref, l_ref, tol_o, tol_l, label="", o_ref_f
     if o_ref_f32 is not None:
         of = np.asarray(o_ref_f32, np.float32)[live]
         g = o_gpu[live]
+        coarse = bf16_step(of) > tol_o
         mag = np.maximum(np.abs(of) + tol_o, np.abs(g))
-        excess = np.abs(g - of) - (tol_o + 0.5 * bf16_step(mag))
+        excess = np.where(coarse, np.abs(g - of) - (tol_o + 0.5 * bf16_step(mag)), d_o - tol_o)
         worst = float(excess.max())
-        assert worst <= 0, (f"{label}: |dO| against the unrounded oracle exceeds tol + half a "
-                            f"bf16 step by {worst:.3e}")
+        assert worst <= 0, (f"{label}: |dO| beyond the bound by {worst:.3e} (tol {tol_o:.1e}; "
+                            f"{int(coarse.sum())} elements where a bf16 step exceeds it are "
+                            "bounded against the unrounded oracle)")
     else:
         assert err_o <= tol_o, f"{label}: max|dO| = {err_o:.3e} > {tol_o:.1e}"
     assert err_l <= tol_l, f"{label}: max|dL| = {err_l:.3e} > {tol_l:.1e}"

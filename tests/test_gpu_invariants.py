@@ -100,5 +100,5 @@ def test_dominant_key_gives_one_hot_rows():
     assert np.array_equal(o[0, 0], np.broadcast_to(v[0, 0, kl - 1], (ql, D)))
     s = 2.0 * 100.0
     assert np.abs(l[0, 0] - s).max() <= 1e-4
-    _, ob, lr = oracle.fwd(qb, kb, v, None, 1, 1, 1, ql, kl, D, 2.0, False)
+    of, ob, lr = oracle.fwd(qb, kb, v, None, 1, 1, 1, ql, kl, D, 2.0, False)
     assert np.array_equal(o, ob)

@@ -211,10 +211,10 @@ def test_boolean_mask_matches_oracle_and_the_additive_mask(B, H, Hkv, ql, kl, D,
     assert torch.equal(Ob.view(torch.int16), Of.view(torch.int16)) and torch.equal(Lb, Lf)
     bits = Ob.view(torch.int16).cpu().numpy().view(np.uint16)
     dense = np.broadcast_to(add, (B, H, ql, kl)).copy()
-    _, ob, lr = oracle.fwd(inp["q"], inp["k"], inp["v"], dense, B, H, Hkv, ql, kl, D, w.scale,
+    of, ob, lr = oracle.fwd(inp["q"], inp["k"], inp["v"], dense, B, H, Hkv, ql, kl, D, w.scale,
                            causal)
     tol_o, tol_l = gu.tolerances(kl)
     eo, el, _ = gu.compare(gu.widen(bits), Lb.cpu().numpy(), bits, ob, lr, tol_o, tol_l,
-                           f"bool mask {B,H,ql,kl,D}")
+                           f"bool mask {B,H,ql,kl,D}", o_ref_f32=of)
     assert np.isneginf(lr).any()
     print(f"bool mask {(B, H, ql, kl, D, causal, mb, mh)}: dO={eo:.3e} dL={el:.3e}")

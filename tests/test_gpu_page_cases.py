@@ -71,7 +71,7 @@ def test_page_forward_case(sec, B, H, Hkv, ql, kl, D, causal, window, off, check
     v = fagen.lcg_bf16(SEED + off + 2, (B, Hkv, kl, D))
     mask = None if window is None else _swa_mask_bf16(B, H, ql, kl, window)
     o, l, bits = _forward(q, k, v, mask, B, H, Hkv, ql, kl, D, causal)
-    _, ob, lr = oracle.fwd(q, k, v, None if mask is None else gu.widen(mask), B, H, Hkv, ql, kl,
+    of, ob, lr = oracle.fwd(q, k, v, None if mask is None else gu.widen(mask), B, H, Hkv, ql, kl,
                            D, 1.0 / math.sqrt(D), causal)
     eo = float(np.abs(o - gu.widen(ob)).max())
     el = float(np.abs(l - lr).max())

@@ -57,12 +57,12 @@ def _run(case, n_split, seed):
     o, l = gu.widen(bits), L.cpu().numpy()
     scale = 1.0 / math.sqrt(D)
     for b, n in enumerate(lens):
-        _, ob, lr = oracle.fwd(q[b:b + 1], keys[b:b + 1, :, :n].copy(),
+        of, ob, lr = oracle.fwd(q[b:b + 1], keys[b:b + 1, :, :n].copy(),
                                values[b:b + 1, :, :n].copy(), None, 1, H, Hkv, ql, n, D, scale,
                                causal)
         tol_o, tol_l = gu.tolerances(n)
         eo, el, _ = gu.compare(o[b:b + 1], l[b:b + 1], bits[b:b + 1], ob, lr, tol_o, tol_l,
-                               f"paged {case} seq {b}")
+                               f"paged {case} seq {b}", o_ref_f32=of)
         print(f"paged {case} n_split={n_split} seq {b} (len {n}): dO={eo:.3e} dL={el:.3e}")
     return o, l
 

@@ -29,9 +29,9 @@ def test_small_workloads_match_oracle(name):
     print(f"case {name}", flush=True)
     inp = fagen.generate(w)
     o, l, bits = gu.run(inp, w)
-    _, ob, lr = oracle.fwd_workload(w, inp)
+    of, ob, lr = oracle.fwd_workload(w, inp)
     tol_o, tol_l = gu.tolerances(w.kl)
-    eo, el, rms = gu.compare(o, l, bits, ob, lr, tol_o, tol_l, name)
+    eo, el, rms = gu.compare(o, l, bits, ob, lr, tol_o, tol_l, name, o_ref_f32=of)
     print(f"{name}: max|dO|={eo:.3e} max|dL|={el:.3e} relRMS(O)={rms:.3e}")
     if w.mask_p is not None:
         full = inp["full_rows"]
@@ -50,11 +50,11 @@ def test_large_workloads_all_rows(name):
     inp = fagen.generate(w)
     o, l, bits = gu.run(inp, w)
     t0 = time.perf_counter()
-    _, ob, lr = oracle.fwd_workload(w, inp)
+    of, ob, lr = oracle.fwd_workload(w, inp)
     print(f"{name}: oracle over all {w.B * w.H * w.ql} rows in {time.perf_counter() - t0:.1f} s",
           flush=True)
     tol_o, tol_l = gu.tolerances(w.kl)
-    eo, el, rms = gu.compare(o, l, bits, ob, lr, tol_o, tol_l, name)
+    eo, el, rms = gu.compare(o, l, bits, ob, lr, tol_o, tol_l, name, o_ref_f32=of)
     # errors per query tile position: the compensated first tile and the
     # plain tiles the bench times
     o_ref = gu.widen(ob)
@@ -116,9 +116,9 @@ def test_ragged_shapes_match_oracle(B, H, Hkv, ql, kl, D, causal, masked):
     print(f"case ragged {w}", flush=True)
     inp = fagen.generate(w)
     o, l, bits = gu.run(inp, w)
-    _, ob, lr = oracle.fwd_workload(w, inp)
+    of, ob, lr = oracle.fwd_workload(w, inp)
     tol_o, tol_l = gu.tolerances(kl)
-    eo, el, _ = gu.compare(o, l, bits, ob, lr, tol_o, tol_l, f"ragged {B,H,Hkv,ql,kl,D}")
+    eo, el, _ = gu.compare(o, l, bits, ob, lr, tol_o, tol_l, f"ragged {B,H,Hkv,ql,kl,D}", o_ref_f32=of)
     print(f"ragged {(B, H, Hkv, ql, kl, D, causal, masked)}: dO={eo:.3e} dL={el:.3e}")
 
 
@@ -207,8 +207,8 @@ def test_head_dim_128_gqa_4k_all_rows():
     print(f"case {w.name}", flush=True)
     inp = fagen.generate(w)
     o, l, bits = gu.run(inp, w)
-    _, ob, lr = oracle.fwd_workload(w, inp)
-    eo, el, rms = gu.compare(o, l, bits, ob, lr, 1e-2, 1e-2, w.name)
+    of, ob, lr = oracle.fwd_workload(w, inp)
+    eo, el, rms = gu.compare(o, l, bits, ob, lr, 1e-2, 1e-2, w.name, o_ref_f32=of)
     print(f"{w.name}: all rows max|dO|={eo:.3e} max|dL|={el:.3e} relRMS(O)={rms:.3e}")
     assert rms <= 1e-2
     assert np.isfinite(o).all() and np.isfinite(l).all()

@@ -45,9 +45,9 @@ def test_split_matches_oracle(B, H, Hkv, ql, kl, D, causal, n_split):
     print(f"case split {(B, H, Hkv, ql, kl, D, causal, n_split)}", flush=True)
     inp = fagen.generate(w)
     o, l, bits = run_split(inp, w, n_split)
-    _, ob, lr = oracle.fwd_workload(w, inp)
+    of, ob, lr = oracle.fwd_workload(w, inp)
     tol_o, tol_l = gu.tolerances(kl)
-    eo, el, rms = gu.compare(o, l, bits, ob, lr, tol_o, tol_l, f"split {B,H,ql,kl,D,n_split}")
+    eo, el, rms = gu.compare(o, l, bits, ob, lr, tol_o, tol_l, f"split {B,H,ql,kl,D,n_split}", o_ref_f32=of)
     print(f"split {(B, H, Hkv, ql, kl, D, causal, n_split)}: dO={eo:.3e} dL={el:.3e} "
           f"relRMS={rms:.2e}")
     assert rms <= 5e-3
@@ -66,8 +66,8 @@ def test_split_reused_workspace_and_kl_zero():
     for w in (big, small, big):
         inp = fagen.generate(w)
         o, l, bits = run_split(inp, w, 12, workspace=ws)
-        _, ob, lr = oracle.fwd_workload(w, inp)
-        gu.compare(o, l, bits, ob, lr, 1e-2, 1e-2, f"split reuse {w.name}")
+        of, ob, lr = oracle.fwd_workload(w, inp)
+        gu.compare(o, l, bits, ob, lr, 1e-2, 1e-2, f"split reuse {w.name}", o_ref_f32=of)
     q = torch.randn(1, 2, 5, 64, device="cuda:0").to(torch.bfloat16)
     k = torch.empty(1, 1, 0, 64, device="cuda:0", dtype=torch.bfloat16)
     O, L = fa.train_fwd_split(q, k, k, 4, workspace=torch.empty(0, dtype=torch.uint8,
@@ -86,9 +86,9 @@ def test_split_long_cache_sampled_rows():
     rng = np.random.default_rng(9200)
     rows = np.unique(np.concatenate([np.arange(64), rng.integers(0, w.B * w.H * w.ql, 160),
                                      31 * w.ql + np.arange(w.ql - 32, w.ql)])).astype(np.int64)
-    _, ob, lr = oracle.fwd_workload(w, inp, rows=rows)
+    of, ob, lr = oracle.fwd_workload(w, inp, rows=rows)
     o2, l2, b2 = o.reshape(-1, w.D)[rows], l.reshape(-1)[rows], bits.reshape(-1, w.D)[rows]
-    eo, el, rms = gu.compare(o2, l2, b2, ob, lr, 1e-2, 1e-2, "split long cache")
+    eo, el, rms = gu.compare(o2, l2, b2, ob, lr, 1e-2, 1e-2, "split long cache", o_ref_f32=of)
     print(f"split long cache: {rows.size} rows dO={eo:.3e} dL={el:.3e} relRMS={rms:.2e}")
     assert rms <= 1e-2
     assert np.isfinite(o).all() and np.isfinite(l).all()
@@ -101,7 +101,12 @@ def test_split_errors_raise_from_binding():
     with pytest.raises(fa.FAError) as e:
         fa.train_fwd_split(q, q, q, 0)
     assert e.value.status == 11
-    with pytest.raises(fa.FAError) as e:
-        fa.train_fwd_split(q, q, q, 2, workspace=torch.empty(16, dtype=torch.uint8,
-                                                             device="cuda:0"))
-    assert e.value.status == 11
+    # a workspace too small: refused by the binding, and by the library itself
+    small = torch.empty(16, dtype=torch.uint8, device="cuda:0")
+    with pytest.raises(ValueError):
+        fa.train_fwd_split(q, q, q, 2, workspace=small)
+    O, L = torch.empty_like(q), torch.empty(1, 1, 4, device="cuda:0")
+    st = fa.fa_train_fwd_split(q.data_ptr(), q.data_ptr(), q.data_ptr(), 1, 1, 1, 4, 4, 64, 0.125,
+                               0, 2, small.data_ptr(), 16, O.data_ptr(), L.data_ptr(),
+                               torch.cuda.current_stream().cuda_stream)
+    assert st == 11

@@ -94,11 +94,11 @@ def test_packed_qkv_slices_and_oracle():
     torch.cuda.synchronize()
     _same(ref, got)
     qn, kn, vn = (np.ascontiguousarray(qkv_np[:, :, i].transpose(0, 2, 1, 3)) for i in range(3))
-    _, ob, lr = oracle.fwd(qn, kn, vn, None, B, H, H, L, L, D, 1.0 / math.sqrt(D), True)
+    of, ob, lr = oracle.fwd(qn, kn, vn, None, B, H, H, L, L, D, 1.0 / math.sqrt(D), True)
     o, l = got
     bits = o.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
     eo, el, _ = gu.compare(gu.widen(bits), l.cpu().numpy(), bits, ob, lr, 5e-3, 3e-3,
-                           "strided packed qkv")
+                           "strided packed qkv", o_ref_f32=of)
     print(f"strided packed qkv: dO={eo:.3e} dL={el:.3e}")
 
 

@@ -36,12 +36,12 @@ def test_page_shape_matches_oracle_and_the_page_mask():
     print("case swa page shape", flush=True)
     inp = fagen.generate(w)
     o, l, bits = run_swa(inp, w, 16)
-    _, ob, lr = oracle.fwd_workload(w, inp, window=16)
-    eo, el, _ = gu.compare(o, l, bits, ob, lr, 5e-3, 3e-3, "swa page")
+    of, ob, lr = oracle.fwd_workload(w, inp, window=16)
+    eo, el, _ = gu.compare(o, l, bits, ob, lr, 5e-3, 3e-3, "swa page", o_ref_f32=of)
     print(f"swa page: dO={eo:.3e} dL={el:.3e}")
     inp_m = dict(inp, mask=swa_mask(1, 2, 64, 64, 16))
     o2, l2, b2 = gu.run(inp_m, w.with_(causal=False))
-    gu.compare(o2, l2, b2, ob, lr, 5e-3, 3e-3, "page mask through the masked forward")
+    gu.compare(o2, l2, b2, ob, lr, 5e-3, 3e-3, "page mask through the masked forward", o_ref_f32=of)
 
 
 WINDOWED = [
@@ -72,9 +72,9 @@ def test_windowed_shapes_match_oracle(B, H, Hkv, ql, kl, D, window, masked):
     print(f"case swa {(B, H, Hkv, ql, kl, D, window, masked)}", flush=True)
     inp = fagen.generate(w)
     o, l, bits = run_swa(inp, w, window)
-    _, ob, lr = oracle.fwd_workload(w, inp, window=window)
+    of, ob, lr = oracle.fwd_workload(w, inp, window=window)
     tol_o, tol_l = gu.tolerances(kl)
-    eo, el, _ = gu.compare(o, l, bits, ob, lr, tol_o, tol_l, f"swa {B,H,Hkv,ql,kl,D,window}")
+    eo, el, _ = gu.compare(o, l, bits, ob, lr, tol_o, tol_l, f"swa {B,H,Hkv,ql,kl,D,window}", o_ref_f32=of)
     print(f"swa {(B, H, Hkv, ql, kl, D, window, masked)}: dO={eo:.3e} dL={el:.3e} "
           f"empty rows={int(np.isneginf(lr).sum())}")
     if window == 0:
@@ -150,9 +150,9 @@ def test_training_scale_window_sampled_rows(name, window):
     inp = fagen.generate(w)
     o, l, bits = run_swa(inp, w, window)
     rows = _window_rows(w, window, np.random.default_rng(window))
-    _, ob, lr = oracle.fwd_workload(w, inp, rows=rows, window=window)
+    of, ob, lr = oracle.fwd_workload(w, inp, rows=rows, window=window)
     o2, l2, b2 = o.reshape(-1, w.D)[rows], l.reshape(-1)[rows], bits.reshape(-1, w.D)[rows]
-    eo, el, rms = gu.compare(o2, l2, b2, ob, lr, 1e-2, 1e-2, f"{name} window {window}")
+    eo, el, rms = gu.compare(o2, l2, b2, ob, lr, 1e-2, 1e-2, f"{name} window {window}", o_ref_f32=of)
     print(f"{name} window={window}: {rows.size} rows, dO={eo:.3e} dL={el:.3e} relRMS={rms:.2e}")
     assert rms <= 1e-2
     assert np.isfinite(o).all() and np.isfinite(l).all()
