@@ -19,8 +19,10 @@ FA_STATUS = {
     4: "FA_ERR_HEAD_DIM", 5: "FA_ERR_SCALE", 6: "FA_ERR_ALIGNMENT", 7: "FA_ERR_TOO_LARGE",
     8: "FA_ERR_LAUNCH", 9: "FA_ERR_WINDOW", 10: "FA_ERR_MASK", 11: "FA_ERR_SPLIT",
     12: "FA_ERR_PAGED",
-    13: "FA_ERR_STRIDE",
+    13: "FA_ERR_STRIDE", 14: "FA_ERR_SCRATCH",
 }
+# Bytes of the library-held scratch of fa_train_fwd_split_noalloc (per GPU).
+NOALLOC_SCRATCH_BYTES = 16 << 20
 FA_MASK_F32, FA_MASK_BF16, FA_MASK_BOOL = 0, 1, 2
 
 _lib = None
@@ -64,6 +66,9 @@ def lib():
         l.fa_train_fwd_split.argtypes = [vp, vp, vp, ci, ci, ci, ci, ci, ci, ctypes.c_float, ci,
                                          ci, vp, ul, vp, vp, vp]
         l.fa_train_fwd_split.restype = ci
+        l.fa_train_fwd_split_noalloc.argtypes = [vp, vp, vp, ci, ci, ci, ci, ci, ci,
+                                                 ctypes.c_float, ci, ci, vp, vp, vp]
+        l.fa_train_fwd_split_noalloc.restype = ci
         l.fa_train_fwd_split_workspace.argtypes = [ci, ci, ci, ci, ci]
         l.fa_train_fwd_split_workspace.restype = ul
         l.fa_paged_fwd.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, ci, ci,
@@ -230,6 +235,35 @@ def suggest_n_split(batch, n_heads, ql, head_dim, n_kv_heads=None, n_cu=256):
         n_heads, ql = n_kv_heads, n_heads // n_kv_heads
     plain = batch * n_heads * ((ql + rows - 1) // rows)
     return 1 if plain >= n_cu else max(1, (2 * n_cu + plain - 1) // plain)
+
+
+def fa_train_fwd_split_noalloc(q, k, v, batch, n_heads, n_kv_heads, ql, kl, head_dim, scale,
+                               causal, n_split, O, L, stream):
+    """The C entry point with raw integer pointers (0 for NULL); returns the status."""
+    return lib().fa_train_fwd_split_noalloc(q or None, k or None, v or None, batch, n_heads,
+                                            n_kv_heads, ql, kl, head_dim, float(scale),
+                                            int(bool(causal)), int(n_split), O or None,
+                                            L or None, stream or None)
+
+
+def train_fwd_split_noalloc(q, k, v, n_split, scale=None, causal=False, out=None, lse=None,
+                            stream=None):
+    """O, L = train_fwd_split_noalloc(q, k, v, n_split, scale=None, causal=False)
+
+    train_fwd_split with the partials in the library's own per-GPU scratch
+    (NOALLOC_SCRATCH_BYTES) instead of a workspace: the library allocates
+    nothing (pass out and lse to allocate nothing here either). Calls that may
+    overlap on one GPU share that scratch and must be ordered by the caller.
+    """
+    O, L, (B, H, Hkv, ql, kl, D), scale, s = _fwd_outputs(q, k, v, scale, out, lse, stream)
+    import torch
+    with torch.cuda.device(q.device):
+        status = fa_train_fwd_split_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), B, H, Hkv,
+                                            ql, kl, D, scale, causal, n_split, O.data_ptr(),
+                                            L.data_ptr(), s.cuda_stream)
+    if status != 0:
+        raise FAError(status, status_string(status))
+    return O, L
 
 
 def fa_train_fwd_split_workspace(batch, n_heads, ql, head_dim, n_split):

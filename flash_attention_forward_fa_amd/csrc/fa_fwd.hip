@@ -37,6 +37,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "fa.h"
 #include "fa_common.h"
@@ -1151,6 +1152,62 @@ extern "C" int fa_train_fwd_strided(const void* q, const long long* q_strides, c
                    workspace_bytes, st, ms[2]);
 }
 
+// The library-held scratch of fa_train_fwd_split_noalloc (split-KV partials
+// for callers that cannot allocate): one copy per GPU, in this code object.
+// Host code never passes this name to a kernel or a copy: on the host it is a
+// stand-in, and the device address comes from hipGetSymbolAddress, resolved
+// once per device with that device current and kept in scratch_ptr.
+static __device__ __align__(256) unsigned char scratch[FA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mutex;
+void* scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch, or nullptr (unknown device,
+// or the runtime could not locate the symbol).
+void* current_scratch() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(scratch_mutex);
+  if (!scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) {
+      (void)hipGetLastError();  // leave no sticky error for the caller's next call
+      return nullptr;
+    }
+    scratch_ptr[dev] = p;
+  }
+  return scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" int fa_train_fwd_split_noalloc(const void* q, const void* k, const void* v, int batch,
+                                          int n_heads, int n_kv_heads, int ql, int kl,
+                                          int head_dim, float scale, int causal, int n_split,
+                                          void* O, float* L, void* stream) {
+  if (n_split < 1 || n_split > kMaxSplit) return FA_ERR_SPLIT;
+  if (batch < 0 || ql < 0 || kl < 0 || n_heads < 1 || n_kv_heads < 1) return FA_ERR_BAD_SIZE;
+  if (head_dim != 64 && head_dim != 128 && head_dim != 256) return FA_ERR_HEAD_DIM;
+  const int64_t rows = (int64_t)batch * n_heads * ql;
+  void* ws = nullptr;
+  if (rows > 0 && kl > 0) {
+    // the chunks train_fwd will run, and the partials they need
+    const int64_t per = ((int64_t)kl + n_split - 1) / n_split;
+    const int64_t kchunk = (per + 63) / 64 * 64;
+    const int64_t n_eff = ((int64_t)kl + kchunk - 1) / kchunk;
+    if (split_bytes(rows, head_dim, n_eff) > (int64_t)FA_NOALLOC_SCRATCH_BYTES)
+      return FA_ERR_SCRATCH;
+    ws = current_scratch();
+    if (!ws) return FA_ERR_SCRATCH;
+  }
+  return train_fwd(q, k, v, nullptr, FA_MASK_F32, 0, 0, batch, n_heads, n_kv_heads, ql, kl,
+                   head_dim, scale, causal, -1, O, L, stream, n_split, ws,
+                   (size_t)FA_NOALLOC_SCRATCH_BYTES);
+}
+
 extern "C" const char* fa_status_string(int status) {
   switch (status) {
     case FA_OK: return "ok";
@@ -1167,6 +1224,9 @@ extern "C" const char* fa_status_string(int status) {
     case FA_ERR_MASK: return "mask dtype must be FA_MASK_F32, FA_MASK_BF16 or FA_MASK_BOOL, strides >= 0";
     case FA_ERR_SPLIT: return "n_split must be in 1..65536 and the workspace large enough";
     case FA_ERR_PAGED: return "block_size must be a positive multiple of 16 and the cache non-empty";
+    case FA_ERR_SCRATCH:
+      return "the split-KV partials exceed the library's 16 MiB scratch, or the scratch could "
+             "not be located on the current device";
     case FA_ERR_STRIDE:
       return "strides must be >= 0, and those of a written tensor must not alias its elements";
     default: return "unknown status";

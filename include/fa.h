@@ -49,10 +49,16 @@ enum fa_status {
                                   workspace smaller than the split needs                */
     FA_ERR_PAGED = 12,         /* fa_paged_fwd: block_size not a positive multiple of
                                   16, or no cache blocks for a non-empty table          */
-    FA_ERR_STRIDE = 13         /* fa_train_fwd_strided, fa_train_bwd_strided: a negative
+    FA_ERR_STRIDE = 13,        /* fa_train_fwd_strided, fa_train_bwd_strided: a negative
                                   stride, or the strides of a written tensor (O; dQ,
                                   dK, dV) map two of its elements to one address        */
+    FA_ERR_SCRATCH = 14        /* fa_train_fwd_split_noalloc: the split-KV partials
+                                  exceed FA_NOALLOC_SCRATCH_BYTES, or the library's
+                                  scratch could not be located on the current device  */
 };
+
+/* Size of the library-held scratch of fa_train_fwd_split_noalloc (per GPU). */
+#define FA_NOALLOC_SCRATCH_BYTES (16ul << 20)
 
 /* Element types of an additive mask (fa_train_fwd_ex). */
 enum fa_mask_dtype {
@@ -244,6 +250,36 @@ int fa_train_fwd_split(const void *q, const void *k, const void *v, int batch, i
 /* Workspace bytes fa_train_fwd_split needs for these sizes (0 if invalid). */
 unsigned long fa_train_fwd_split_workspace(int batch, int n_heads, int ql, int head_dim,
                                            int n_split);
+
+/*
+ * fa_train_fwd_split_noalloc - fa_train_fwd_split for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the split-KV partials go to a scratch
+ * array the library holds instead of a caller workspace. Nothing is
+ * allocated, freed or synchronised by the call.
+ *
+ * The scratch is a device array of FA_NOALLOC_SCRATCH_BYTES (16 MiB) in the
+ * library's code object: one copy on every GPU the library runs on, held
+ * until the process ends, located on the first call on a GPU. Its bytes are
+ * fa_train_fwd_split_workspace(batch, n_heads, ql, head_dim, n_split) of the
+ * chunks that run; a call that needs more returns FA_ERR_SCRATCH (e.g.
+ * head_dim 128 with batch * n_heads * ql * n_split above 32768 rows) and
+ * enqueues nothing. Every call on one GPU shares that GPU's scratch and it
+ * keeps the last call's contents (every byte a call reads is written by the
+ * same call first, so nothing needs clearing): calls whose kernels may
+ * overlap on one GPU (different streams, or other host threads) race on it
+ * and must be ordered by the caller. The scratch used is the current
+ * device's (hipGetDevice), which must be the device of the tensors and of
+ * `stream`.
+ *
+ * Arguments, outputs and the other statuses are those of fa_train_fwd_split
+ * without workspace and workspace_bytes; the kernels and the results are the
+ * same bit for bit.
+ */
+int fa_train_fwd_split_noalloc(const void *q, const void *k, const void *v, int batch,
+                               int n_heads, int n_kv_heads, int ql, int kl, int head_dim,
+                               float scale, int causal, int n_split, void *O, float *L,
+                               void *stream);
 
 /*
  * fa_paged_fwd - the forward against a block-paged KV cache, one key count per

@@ -45,7 +45,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings_cover_all_codes():
-    for code in range(0, 14):
+    for code in range(0, 15):
         s = fa.status_string(code)
         assert s and s != "unknown status"
     assert fa.status_string(12345) == "unknown status"
@@ -343,3 +343,33 @@ def test_strided_and_paged_bindings_fail_loudly_without_gpu_tensors():
         fa.train_bwd_ex(q, q, q, q, L, q)
     with pytest.raises(ValueError):
         fa.train_fwd_split(q, q, q, 2)
+
+
+NOALLOC_GOOD = dict(q=A, k=A, v=A, batch=1, n_heads=2, n_kv_heads=1, ql=8, kl=1000, head_dim=64,
+                    scale=0.125, causal=1, n_split=4, O=A, L=A, stream=0)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(n_split=0), 11), (dict(n_split=65537), 11), (dict(batch=-1), 2), (dict(n_heads=0), 2),
+    (dict(head_dim=96), 4),
+    # partials above the 16 MiB scratch: 4 * 32 * 512 rows * 128 dims * 4 B * 8 chunks
+    (dict(batch=4, n_heads=32, n_kv_heads=8, ql=512, kl=4096, head_dim=128, n_split=8), 14),
+])
+def test_noalloc_invalid_arguments_are_rejected(over, code):
+    """Checked on the host before the scratch is located or anything runs."""
+    args = dict(NOALLOC_GOOD)
+    args.update(over)
+    assert fa.fa_train_fwd_split_noalloc(**args) == code
+
+
+@pytest.mark.parametrize("over", [dict(batch=0), dict(ql=0, q=0, O=0, L=0)])
+def test_noalloc_empty_problems_are_noops(over):
+    args = dict(NOALLOC_GOOD)
+    args.update(over)
+    assert fa.fa_train_fwd_split_noalloc(**args) == 0
+
+
+def test_noalloc_scratch_size_matches_header():
+    text = open(os.path.join(ROOT, "include", "fa.h")).read()
+    assert "#define FA_NOALLOC_SCRATCH_BYTES (16ul << 20)" in text
+    assert fa.NOALLOC_SCRATCH_BYTES == 16 << 20
