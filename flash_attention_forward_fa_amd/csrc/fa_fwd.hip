@@ -65,6 +65,14 @@ template <int D> constexpr int block_m() { return Cfg<D>::W * 16 * Cfg<D>::QB; }
 // their position) are computed with the compensated P.V product (P split into
 // a bf16 high part and a bf16 remainder) from the start.
 constexpr int kPreciseKeys = 128;
+// Plain tiles (bf16 P, Q pre-scaled by c = |scale| log2(e) in bf16) run only
+// for problems of more than kPlainMinKeys keys, where the tolerance is 1e-2
+// (pre-scaling moves L by up to ~2e-3 and O by up to ~2e-3 before its own
+// rounding on the training workloads), and for c in [kPlainMinC, kPlainMaxC]
+// (c * q stays normal and finite in bf16 for ordinary inputs); everything
+// else runs compensated, with Q exact.
+constexpr int kPlainMinKeys = 256;
+constexpr float kPlainMinC = 0x1p-64f, kPlainMaxC = 8.0f;
 // After a plain pass, a row is recomputed compensated when some |O| element
 // reaches this: one bf16 rounding step of O is then 2^-7 or more, so the
 // error bf16(P) leaves in O before its own rounding (about 2^-10 at most on
@@ -159,6 +167,11 @@ __device__ __forceinline__ bool fwd_tile(const FwdArgs& a, int qtile, int bh, ui
   constexpr int TILE = BN * D;  // elements per K or V tile
   constexpr int NT = 64 * Cfg<D>::W;  // threads per workgroup
   static_assert(TILE > 0, "empty tile");
+  // Plain tiles take Q pre-scaled by c = |scale| log2(e) and rounded to bf16,
+  // so that the MFMA yields base-2 scores; their accumulators start at -m
+  // (the running max), so exp2 reads the MFMA's output directly. The
+  // compensated tiles keep Q exact and scale in f32.
+  constexpr bool PS = !PRECISE;
 
   // (the opaque copy keeps the compiler from hoisting the thread-index
   // arithmetic of both tile variants of the mixed kernel above their branch,
@@ -262,17 +275,27 @@ __device__ __forceinline__ bool fwd_tile(const FwdArgs& a, int qtile, int bh, ui
       u32x4 raw = *reinterpret_cast<const u32x4*>(qp + 32 * s);
       raw ^= a.q_sign;
       qop[qb][s] = __builtin_bit_cast(bf16x8, raw);
+      if constexpr (PS) {
+        bf16x8 sc;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sc[e] = (__bf16)((float)qop[qb][s][e] * a.c);
+        qop[qb][s] = sc;
+      }
     }
   }
 
-  // m_use: the max used in exp2 (base 2); thr: raw score above which a tile
-  // raises it (m_use + kLazy in raw units); l_run: this lane's partial row sum.
+  // m_use: the max used in exp2 (base 2); thr: the tile max above which a
+  // tile raises it (m_use + kLazy in raw units; in the plain tiles, whose
+  // scores come relative to m_use, kLazy); l_run: this lane's partial row
+  // sum. The plain tiles start m_use at 0 (their scores are then the raw
+  // ones) and take the first visible key's tile max as it; the compensated
+  // ones start at the finite sentinel -FLT_MAX/2.
   float m_use[kQB], thr[kQB], l_run[kQB];
   f32x4 oacc[NDB][kQB];
   const float inv_c = HAS_MASK ? 1.0f : 1.0f / a.c;
 #pragma unroll
   for (int qb = 0; qb < kQB; ++qb) {
-    m_use[qb] = -FLT_MAX / 2.0f;
+    m_use[qb] = PS ? 0.0f : -FLT_MAX / 2.0f;
     thr[qb] = -INFINITY;
     l_run[qb] = 0.0f;
 #pragma unroll
@@ -292,16 +315,26 @@ __device__ __forceinline__ bool fwd_tile(const FwdArgs& a, int qtile, int bh, ui
   const int lo_gap = WINDOW ? off + wave_last - a.window : 0;
   const int lo_end = lo_gap > 0 ? (lo_gap + BN - 1) / BN : 0;
 
+  const int lane_c16 = c16, lane_grp = grp;
+
   // ---- S^T = K Q^T (raw scores, f32) for the tile in ks ----
   auto kread = [&](const uint16_t* ks, int s, int kb) {
-    const int r = key_of(kb, c16);
-    return *reinterpret_cast<const bf16x8*>(ks + r * D + 8 * ((4 * s + grp) ^ kswz<D>(r)));
+    const int r = key_of(kb, lane_c16);
+    // (one index off the tile: every LDS address a short GEP chain from its
+    // buffer, so that the compiler keeps the buffer's alias scope on the read)
+    return *reinterpret_cast<const bf16x8*>(ks +
+                                            (r * D + 8 * ((4 * s + lane_grp) ^ kswz<D>(r))));
   };
   auto scores = [&](const uint16_t* ks, f32x4 (&sacc)[NKB][kQB]) {
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int qb = 0; qb < kQB; ++qb) sacc[kb][qb] = f32x4{};
+      for (int qb = 0; qb < kQB; ++qb) {
+        if constexpr (PS)
+          sacc[kb][qb] = f32x4{-m_use[qb], -m_use[qb], -m_use[qb], -m_use[qb]};
+        else
+          sacc[kb][qb] = f32x4{};
+      }
     if constexpr (D <= 128) {
 #pragma unroll
       for (int s = 0; s < NDS; ++s)
@@ -413,14 +446,28 @@ __device__ __forceinline__ bool fwd_tile(const FwdArgs& a, int qtile, int bh, ui
       for (int qb = 0; qb < kQB; ++qb) mx[qb] = group_max(mx[qb]);
     }
   };
-  auto rescale = [&](const float (&mx)[kQB]) {
+  auto rescale = [&](const float (&mx)[kQB], f32x4 (&sacc)[NKB][kQB]) {
 #pragma unroll
     for (int qb = 0; qb < kQB; ++qb) {
       const bool r = mx[qb] > thr[qb];
-      const float m_new = r ? (HAS_MASK ? mx[qb] : mx[qb] * a.c) : m_use[qb];
-      const float alpha = __builtin_amdgcn_exp2f(m_use[qb] - m_new);
+      float m_new, alpha;
+      if constexpr (PS) {
+        // scores relative to m_use: the new max is m_use + mx, and this
+        // tile's scores move down by mx (later tiles start at the new -m_use).
+        // A row's first raise may lower m_use (from 0); its sum and O are
+        // still 0 then, and alpha is kept at most 1.
+        const float shift = r ? mx[qb] : 0.0f;
+        m_new = m_use[qb] + shift;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) sacc[kb][qb] -= shift;
+        thr[qb] = r ? kLazy : thr[qb];
+        alpha = __builtin_amdgcn_exp2f(fminf(-shift, 0.0f));
+      } else {
+        m_new = r ? (HAS_MASK ? mx[qb] : mx[qb] * a.c) : m_use[qb];
+        thr[qb] = r ? (m_new + kLazy) * inv_c : thr[qb];
+        alpha = __builtin_amdgcn_exp2f(m_use[qb] - m_new);
+      }
       m_use[qb] = m_new;
-      thr[qb] = r ? (m_new + kLazy) * inv_c : thr[qb];
       l_run[qb] *= alpha;
 #pragma unroll
       for (int d = 0; d < NDB; ++d) oacc[d][qb] *= alpha;
@@ -441,7 +488,9 @@ __device__ __forceinline__ bool fwd_tile(const FwdArgs& a, int qtile, int bh, ui
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const float sv = sacc[2 * j + (e >> 2)][qb][e & 3];
-          p[e] = __builtin_amdgcn_exp2f(HAS_MASK ? sv + mneg : __builtin_fmaf(sv, a.c, mneg));
+          p[e] = __builtin_amdgcn_exp2f(HAS_MASK ? sv + mneg
+                                        : PS     ? sv
+                                                 : __builtin_fmaf(sv, a.c, mneg));
           phi[j][qb][e] = (__bf16)p[e];
         }
 #pragma unroll
@@ -468,9 +517,9 @@ __device__ __forceinline__ bool fwd_tile(const FwdArgs& a, int qtile, int bh, ui
     s16x4 half[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      const int r = 32 * j + 8 * grp + 4 * t + (c16 >> 2);
-      const int col = 16 * d + 4 * (c16 & 3);
-      const uint16_t* addr = vs + r * D + 8 * ((col >> 3) ^ vswz<D>(r)) + (col & 7);
+      const int r = 32 * j + 8 * lane_grp + 4 * t + (lane_c16 >> 2);
+      const int col = 16 * d + 4 * (lane_c16 & 3);
+      const uint16_t* addr = vs + (r * D + 8 * ((col >> 3) ^ vswz<D>(r)) + (col & 7));
       half[t] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)addr);
     }
     return __builtin_bit_cast(bf16x8,
@@ -520,15 +569,24 @@ __device__ __forceinline__ bool fwd_tile(const FwdArgs& a, int qtile, int bh, ui
   };
 
   // ---- the key loop ----
-  // one tile per step: wait for its copy, start the next one, compute it
-  if (n_kt > kt_first) issue_v(kt_first, (kt_first & 1) ? v1s : v0s);
-  for (int kt = kt_first; kt < n_kt; ++kt) {
-    const bool odd = kt & 1;
+  // One tile per step: wait for its copy, start the next one, compute it.
+  // Where registers allow (PAIRED), the steps come in pairs with fixed buffer
+  // roles (even tiles in buffer 0, odd tiles in buffer 1), so that the
+  // compiler can tell the LDS reads of a tile from the copy of the next one in
+  // flight into the other buffer: with the buffer chosen at run time it makes
+  // every wave wait for that copy before its V^T reads (measured: D=64 4k
+  // causal 326 -> 316 us, D=256 8k 1106 -> 1065 us). With fixed buffers the
+  // compiler keeps the addresses of both buffers in registers, which spills
+  // in the sliding-window, split-KV and paged kernels and in the compensated
+  // tiles of the mixed kernel (the short first tiles and the rare redo):
+  // those keep one step per iteration.
+  constexpr bool PAIRED = !WINDOW && !SPLIT && !PAGED && (!PRECISE || HAS_MASK);
+  auto step = [&](int kt, const uint16_t* kc, const uint16_t* vc, uint16_t* kn, uint16_t* vn) {
     wait_vmem();
     __syncthreads();
     if (kt + 1 < n_kt) {
-      issue_k(kt + 1, odd ? k0s : k1s);
-      issue_v(kt + 1, odd ? v0s : v1s);
+      issue_k(kt + 1, kn);
+      issue_v(kt + 1, vn);
     }
     if (kt >= wave_kt_first && kt < n_kw) {
       // A wave issuing its MFMA blocks gets a raised priority (s_setprio), so
@@ -536,19 +594,31 @@ __device__ __forceinline__ bool fwd_tile(const FwdArgs& a, int qtile, int bh, ui
       // around the P.V block for D=64 and around both blocks for D=256.
       f32x4 s[NKB][kQB];
       if (D == 256) set_prio<2>();
-      scores(odd ? k1s : k0s, s);
+      scores(kc, s);
       if (D == 256) set_prio<0>();
       if (kt >= mask_from || (WINDOW && kt < lo_end)) apply_mask(kt, s);
       float mx[kQB];
       if (__any(part_max(s, mx))) {
         complete_max(mx);
-        rescale(mx);
+        rescale(mx, s);
       }
       bf16x8 phi[NKC][kQB], plo[NKC][kQB];
       probs(s, phi, plo);
       set_prio<2>();
-      pv(odd ? v1s : v0s, phi, plo);
+      pv(vc, phi, plo);
       set_prio<0>();
+    }
+  };
+  if (n_kt > kt_first) issue_v(kt_first, (kt_first & 1) ? v1s : v0s);
+  if constexpr (PAIRED) {
+    for (int kt = kt_first & ~1; kt < n_kt; kt += 2) {
+      if (kt >= kt_first) step(kt, k0s, v0s, k1s, v1s);
+      if (kt + 1 < n_kt) step(kt + 1, k1s, v1s, k0s, v0s);
+    }
+  } else {
+    for (int kt = kt_first; kt < n_kt; ++kt) {
+      const bool odd = kt & 1;
+      step(kt, odd ? k1s : k0s, odd ? v1s : v0s, odd ? k0s : k1s, odd ? v0s : v1s);
     }
   }
 
@@ -976,9 +1046,10 @@ int train_fwd(const void* q, const void* k, const void* v, const void* mask, int
   }
 
   hipStream_t s = static_cast<hipStream_t>(stream);
-  // query tiles whose first row may see fewer than kPreciseKeys keys
+  // query tiles whose first row may see fewer than kPreciseKeys keys; every
+  // tile when the plain tiles' pre-scaled Q is not used (below)
   int64_t n_short = 0;
-  if (kl < kPreciseKeys)
+  if (kl <= kPlainMinKeys || !(a.c >= kPlainMinC && a.c <= kPlainMaxC))
     n_short = n_qtiles;
   else if (windowed && (a.window + 1 < kPreciseKeys ||
                         (ql > kl && (int64_t)ql - 1 > (int64_t)kl + a.window - kPreciseKeys)))
