@@ -118,10 +118,18 @@ __attribute__((amdgpu_waves_per_eu(BwdCfg<D, PASS>::WPE))) void fa_bwd_kernel(Bw
   constexpr bool KV = PASS == kBwdKV;
   constexpr bool HAS_MASK = MASK != kNoMask;
   static_assert(CAUSAL || !WINDOW, "the sliding window includes the causal rule");
-  __shared__ __attribute__((aligned(1024))) uint16_t y1s[2][TILE];
-  __shared__ __attribute__((aligned(1024))) uint16_t y2s[2][TILE];
-  __shared__ __attribute__((aligned(1024))) uint16_t yos[2][KV ? TILE : 8];  // dKV pass: O
-  __shared__ float srow[2][BN];  // dKV pass: L2 and D of the streamed rows
+  // the two stages of each streamed operand are separate arrays, so that the
+  // compiler can tell a stage's reads from the copy into the other one
+  __shared__ __attribute__((aligned(1024))) uint16_t y1s0[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t y1s1[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t y2s0[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t y2s1[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t yos0[KV ? TILE : 8];  // dKV pass: O
+  __shared__ __attribute__((aligned(1024))) uint16_t yos1[KV ? TILE : 8];
+  // dKV pass: L2 and D of the streamed rows (one 8-byte store per row: two
+  // separate stores were merged into one that lost the array's alias scope,
+  // and the compiler then waited for the next tile's copy before it)
+  __shared__ float2 srow[BN];
 
   const int tid = threadIdx.x;
   // wave-uniform wave index: every wave-level condition is a scalar branch
@@ -230,41 +238,39 @@ __attribute__((amdgpu_waves_per_eu(BwdCfg<D, PASS>::WPE))) void fa_bwd_kernel(Bw
   int y1off[CopyShape<D, BN, NT>::ROUNDS], y2off[CopyShape<D, BN, NT>::ROUNDS];
   copy_offsets<D, BN, NT, true>(tid, y1off, yr);
   copy_offsets<D, BN, NT, false>(tid, y2off, yr);
-  auto issue = [&](int t) {
-    const int buf = t & 1;
-    issue_tile<D, BN, NT, true>(y1_src(t), tile_first(t), nstream, y1s[buf], tid, 64 * wave, y1off,
+  auto issue = [&](int t, uint16_t* y1d, uint16_t* y2d, uint16_t* yod) {
+    issue_tile<D, BN, NT, true>(y1_src(t), tile_first(t), nstream, y1d, tid, 64 * wave, y1off,
                                 yr);
-    issue_tile<D, BN, NT, false>(y2_src(t), tile_first(t), nstream, y2s[buf], tid, 64 * wave,
-                                 y2off, yr);
+    issue_tile<D, BN, NT, false>(y2_src(t), tile_first(t), nstream, y2d, tid, 64 * wave, y2off,
+                                 yr);
     if constexpr (KV)
       issue_tile<D, BN, NT, false>(a.o + b * a.q_sb + tile_head(t) * a.q_sh, tile_first(t),
-                                   nstream, yos[buf], tid, 64 * wave, y2off, yr);
+                                   nstream, yod, tid, 64 * wave, y2off, yr);
   };
   // dKV pass: L2 and D of the streamed rows of tile t (landed in LDS) into
   // srow (NT / BN threads per row, each summing D / (NT / BN) dims of O * dO)
-  auto stream_rows = [&](int t, int sbase, int th) {
+  // (lv: this thread's row's L, loaded before the next tile's copy is issued:
+  // the load counter is in order, so a load issued after the copy would make
+  // the wait for it a wait for the copy)
+  auto stream_rows = [&](float lv, const uint16_t* y2c, const uint16_t* yoc) {
     if constexpr (KV) {
       constexpr int TPR = NT / BN;
       constexpr int DPT = D / TPR;
       const int r = tid / TPR, part = tid % TPR;
-      const int buf = t & 1;
-      const int qi = min(sbase + r, ql - 1);
-      const float lv = a.L[(int64_t)(b * a.H + th) * ql + qi];
       float acc = 0.0f;
 #pragma unroll
       for (int c = 0; c < DPT / 8; ++c) {
         const int ch = part * (DPT / 8) + c;  // 16-byte chunk of the row
         const int slot = r * D + 8 * (ch ^ vswz<D>(r));
-        const bf16x8 ov = *reinterpret_cast<const bf16x8*>(&yos[buf][slot]);
-        const bf16x8 gv = *reinterpret_cast<const bf16x8*>(&y2s[buf][slot]);
+        const bf16x8 ov = *reinterpret_cast<const bf16x8*>(yoc + slot);
+        const bf16x8 gv = *reinterpret_cast<const bf16x8*>(y2c + slot);
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc += (float)ov[e] * (float)gv[e];
       }
 #pragma unroll
       for (int m = 1; m < TPR; m <<= 1) acc += __shfl_xor(acc, m, 64);
       if (part == 0) {
-        srow[0][r] = lse2(lv);
-        srow[1][r] = acc;
+        srow[r] = make_float2(lse2(lv), acc);
       }
     }
   };
@@ -274,7 +280,9 @@ __attribute__((amdgpu_waves_per_eu(BwdCfg<D, PASS>::WPE))) void fa_bwd_kernel(Bw
   auto rread = [&](const uint16_t* buf, bool is_y1, int s, int kb) {
     const int r = key_of(kb, c16);
     const int sw = is_y1 ? kswz<D>(r) : vswz<D>(r);
-    return *reinterpret_cast<const bf16x8*>(buf + r * D + 8 * ((4 * s + grp) ^ sw));
+    // (one index off the tile: a short address chain from the buffer, so that
+    // the compiler keeps the buffer's alias scope on the read)
+    return *reinterpret_cast<const bf16x8*>(buf + (r * D + 8 * ((4 * s + grp) ^ sw)));
   };
   // transposed read (A operand of the second products): dims 16d + c16, streamed
   // rows 32j + 8grp + (0..7)
@@ -285,7 +293,7 @@ __attribute__((amdgpu_waves_per_eu(BwdCfg<D, PASS>::WPE))) void fa_bwd_kernel(Bw
       const int r = 32 * j + 8 * grp + 4 * t + (c16 >> 2);
       const int col = 16 * d + 4 * (c16 & 3);
       const int sw = is_y1 ? kswz<D>(r) : vswz<D>(r);
-      const uint16_t* addr = buf + r * D + 8 * ((col >> 3) ^ sw) + (col & 7);
+      const uint16_t* addr = buf + (r * D + 8 * ((col >> 3) ^ sw) + (col & 7));
       half[t] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)addr);
     }
     return __builtin_bit_cast(bf16x8,
@@ -309,18 +317,30 @@ __attribute__((amdgpu_waves_per_eu(BwdCfg<D, PASS>::WPE))) void fa_bwd_kernel(Bw
   };
 
   // ---- the streamed loop: wait for tile t, start tile t+1, compute tile t ----
-  if (n_st > 0) issue(0);
-  for (int t = 0; t < n_st; ++t) {
-    const int buf = t & 1;
-    wait_vmem();
-    __syncthreads();
-    if (t + 1 < n_st) issue(t + 1);
+  // Steps come in pairs with fixed buffer roles (even tiles in stage 0, odd
+  // in stage 1): with the stage chosen at run time the compiler cannot tell
+  // a tile's LDS reads from the copy of the next tile in flight, and made
+  // every wave wait for that copy before reading.
+  auto step = [&](int t, const uint16_t* b1, const uint16_t* b2, const uint16_t* bo,
+                  uint16_t* n1, uint16_t* n2, uint16_t* no) {
     // (made provably uniform: every wave-level decision below depends on them)
     const int sbase = __builtin_amdgcn_readfirstlane(tile_first(t));
     const int th = __builtin_amdgcn_readfirstlane(tile_head(t));
+    float lv = 0.0f;
+    if constexpr (KV)
+      lv = a.L[(int64_t)(b * a.H + th) * ql + min(sbase + tid / (NT / BN), ql - 1)];
+    wait_vmem();
+    __syncthreads();
+    if (t + 1 < n_st) issue(t + 1, n1, n2, no);
     if constexpr (KV) {
-      stream_rows(t, sbase, th);
-      __syncthreads();
+      stream_rows(lv, b2, bo);
+      // every wave's srow stores done before any wave reads srow: an LDS-only
+      // wait and a bare barrier (__syncthreads' release fence would also
+      // wait for the next tile's copy in flight, which nothing here reads)
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt, expcnt at their maxima
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
     }
     // does this wave see any (streamed, fixed) pair of the tile, and does the
     // tile need per-element masks?
@@ -338,9 +358,7 @@ __attribute__((amdgpu_waves_per_eu(BwdCfg<D, PASS>::WPE))) void fa_bwd_kernel(Bw
       need_mask = sbase + BN > ql || (CAUSAL && sbase < wlast - off) ||
                   (WINDOW && sbase + BN - 1 > fw0 - off + a.window);
     }
-    if (!any) continue;
-    const uint16_t* b1 = y1s[buf];
-    const uint16_t* b2 = y2s[buf];
+    if (!any) return;
     f32x4 sacc[NKB][FB], dpacc[NKB][FB];
     // (D=256: waves raise their priority while they issue MFMA blocks, as in
     // the forward; measured 2% faster for D=256, slower for D=64)
@@ -373,8 +391,9 @@ __attribute__((amdgpu_waves_per_eu(BwdCfg<D, PASS>::WPE))) void fa_bwd_kernel(Bw
           const float s = sacc[kb][fb][i];
           float l2, dd;
           if constexpr (KV) {
-            l2 = srow[0][srel];
-            dd = srow[1][srel];
+            const float2 sv = srow[srel];
+            l2 = sv.x;
+            dd = sv.y;
           } else {
             l2 = l2f[fb];
             dd = dfx[fb];
@@ -423,6 +442,22 @@ __attribute__((amdgpu_waves_per_eu(BwdCfg<D, PASS>::WPE))) void fa_bwd_kernel(Bw
         }
       }
     if constexpr (D == 256) set_prio<0>();
+  };
+  // (the D=64 dK/dV pass with a mask or window has too few registers to keep
+  // both stages' addresses: one step per iteration there)
+  constexpr bool PAIRED = !(D == 64 && KV && (WINDOW || HAS_MASK));
+  if (n_st > 0) issue(0, y1s0, y2s0, yos0);
+  if constexpr (PAIRED) {
+    for (int t = 0; t < n_st; t += 2) {
+      step(t, y1s0, y2s0, yos0, y1s1, y2s1, yos1);
+      if (t + 1 < n_st) step(t + 1, y1s1, y2s1, yos1, y1s0, y2s0, yos0);
+    }
+  } else {
+    for (int t = 0; t < n_st; ++t) {
+      const bool odd = t & 1;
+      step(t, odd ? y1s1 : y1s0, odd ? y2s1 : y2s0, odd ? yos1 : yos0, odd ? y1s0 : y1s1,
+           odd ? y2s0 : y2s1, odd ? yos0 : yos1);
+    }
   }
 
   // ---- epilogue: scale and store (fixed row c16 of block fb, dims 16d + 4grp + i) ----
