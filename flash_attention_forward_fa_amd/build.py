@@ -8,13 +8,18 @@ Flags:
   -target-feature -packed-fp32-ops  no packed f32 VALU instructions
 """
 import os
+import shutil
 import subprocess
 import sys
+import tempfile
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libfa.so")
-SOURCES = [os.path.join(HERE, "csrc", "fa_fwd.hip"), os.path.join(HERE, "csrc", "fa_bwd.hip")]
+# (the forward's key widths 80, 96 and 192 have translation units of their own,
+# which compile in parallel with the rest)
+SOURCES = [os.path.join(HERE, "csrc", f) for f in
+           ("fa_fwd.hip", "fa_fwd_d80.hip", "fa_fwd_d96.hip", "fa_fwd_d192.hip", "fa_bwd.hip")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
@@ -23,11 +28,28 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
 
 
 def build(verbose=False, extra_flags=()):
-    cmd = [HIPCC, *FLAGS, *extra_flags, "-o", LIB + ".tmp", *SOURCES]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    subprocess.run(cmd, check=True)
-    os.replace(LIB + ".tmp", LIB)
+    """Compiles every source to an object (in parallel), then links libfa.so."""
+    tmp = tempfile.mkdtemp(prefix="fa_build_")
+    try:
+        compile_flags = [f for f in FLAGS if f != "-shared"]
+        objs, procs = [], []
+        for src in SOURCES:
+            obj = os.path.join(tmp, os.path.basename(src) + ".o")
+            cmd = [HIPCC, *compile_flags, *extra_flags, "-c", "-o", obj, src]
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            objs.append(obj)
+            procs.append((cmd, subprocess.Popen(cmd)))
+        failed = [cmd for cmd, p in procs if p.wait() != 0]
+        if failed:
+            raise subprocess.CalledProcessError(1, failed[0])
+        cmd = [HIPCC, "--offload-arch=gfx950", "-fPIC", "-shared", "-o", LIB + ".tmp", *objs]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        subprocess.run(cmd, check=True)
+        os.replace(LIB + ".tmp", LIB)
+    finally:
+        shutil.rmtree(tmp, ignore_errors=True)
     return LIB
 
 

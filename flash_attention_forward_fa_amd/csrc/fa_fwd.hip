@@ -1,35 +1,9 @@
-// fa_fwd.hip - flash-attention training forward (O and L) for AMD MI355X (gfx950).
-//
-// What is computed is fixed by the CPU oracle of the method's page
-// ("mlx-native 0.9.0", tests/test_flash_attn_train.rs, doc comment and section
-// "CPU oracle - forward O + logsumexp L"): per query row, base-2 scores
-// s = scale*log2(e)*<q,k> (+ log2(e)*mask), bottom-right causal masking with the
-// offset max(kl - ql, 0), p = exp2(s - m), L = m*ln2 + ln(sum p),
-// O = sum(p v) / sum p, and O = 0, L = -inf for a row with no visible key. The
-// kernel reaches the same values tile by tile with an online (streaming)
-// softmax over key tiles.
-//
-// Work decomposition: one workgroup of 8 waves per (batch, head, query tile);
-// each wave owns 32 query rows (D=64, two blocks of 16) or 16 rows (D=256).
-// Per key tile, K and V are copied from HBM straight into LDS
-// (buffer_load_dwordx4 ... lds, no VGPR staging) into one of two buffers while
-// the previous tile is being computed. Every wave then computes, with
-// v_mfma_f32_16x16x32_bf16,
-//   S^T = K Q^T     (K rows read from LDS with ds_read_b128)
-//   O^T += V^T P^T  (V^T read from the row-major V tile with ds_read_b64_tr_b16)
-// so that in both products a lane holds one query row per 16-row block: row
-// max, row sum and rescale are per-lane scalars after a reduction over the
-// four 16-lane groups (v_permlane32_swap, v_permlane16_swap).
-//
-// Sliding window (the same page, section 7, where it is built as an additive
-// mask): key j is visible to row i iff q_abs - window <= j <= q_abs, q_abs =
-// max(kl - ql, 0) + i. The WINDOW variants skip the key tiles below the band
-// and mask only the tiles that cross one of its edges.
-//
-// Accuracy: P enters the bf16 MFMA rounded to bf16. Where that is not accurate
-// enough the product is compensated (a second MFMA with P's bf16 remainder):
-// for query tiles whose rows may see fewer than 128 keys, and for rows whose
-// plain result has some |O| >= 1, which their workgroup computes again.
+// fa_fwd.hip - host path and C-ABI entry points of the flash-attention training
+// forward (O and L) for AMD MI355X (gfx950): argument checks, the layout of
+// strides, decode packing, split-KV workspace, the choice of compensated query
+// tiles, and the launches of the kernels of fa_fwd_kernel.h for head dims 64,
+// 128 and 256 (80, 96 and 192 are built in fa_fwd_d80.hip, fa_fwd_d96.hip and
+// fa_fwd_d192.hip).
 #include <hip/hip_runtime.h>
 
 #include <float.h>
@@ -41,870 +15,35 @@
 
 #include "fa.h"
 #include "fa_common.h"
+#include "fa_fwd_kernel.h"
 
 namespace {
 
-// Per head dim: W waves per workgroup, QB 16-row query blocks per wave and BN
-// keys per tile. Eight waves (two per SIMD) share each K/V tile copy, which
-// halves the copy traffic per flop against four (measured faster for both).
-//   D=64:  2 blocks (32 rows per wave, 256 per workgroup), 64-key tiles.
-//   D=256: 1 block (16 rows per wave, 128 per workgroup), 64-key tiles (two
-//          32 KiB stages of K and V: one workgroup per CU); the O accumulator
-//          of 16 rows x 256 dims is 64 registers per lane. 64-key tiles halve
-//          the barriers per key against 32 (measured 5% faster).
-template <int D> struct Cfg;
-template <> struct Cfg<64> { static constexpr int W = 8, QB = 2, BN = 64, WPE = 4; };
-//   D=128: 2 blocks (32 rows per wave, 256 per workgroup), 64-key tiles; the O
-//          accumulator of 32 rows x 128 dims is 64 registers per lane, two waves
-//          per SIMD.
-template <> struct Cfg<128> { static constexpr int W = 8, QB = 2, BN = 64, WPE = 2; };
-template <> struct Cfg<256> { static constexpr int W = 8, QB = 1, BN = 64, WPE = 2; };
-template <int D> constexpr int block_m() { return Cfg<D>::W * 16 * Cfg<D>::QB; }
-
-// Query tiles with a row that may see fewer keys than this (a property of
-// their position) are computed with the compensated P.V product (P split into
-// a bf16 high part and a bf16 remainder) from the start.
-constexpr int kPreciseKeys = 128;
-// Plain tiles (bf16 P, Q pre-scaled by c = |scale| log2(e) in bf16) run only
-// for problems of more than kPlainMinKeys keys, where the tolerance is 1e-2
-// (pre-scaling moves L by up to ~2e-3 and O by up to ~2e-3 before its own
-// rounding on the training workloads), and for c in [kPlainMinC, kPlainMaxC]
-// (c * q stays normal and finite in bf16 for ordinary inputs); everything
-// else runs compensated, with Q exact.
-constexpr int kPlainMinKeys = 256;
-constexpr float kPlainMinC = 0x1p-64f, kPlainMaxC = 8.0f;
-// After a plain pass, a row is recomputed compensated when some |O| element
-// reaches this: one bf16 rounding step of O is then 2^-7 or more, so the
-// error bf16(P) leaves in O before its own rounding (about 2^-10 at most on
-// the workloads) can move it by a step larger than 5e-3. Below it a moved
-// rounding costs at most 2^-8. (L needs no such check: bf16(P) changes the
-// row sum by a relative 2^-9 at most.)
-constexpr float kRecheckO = 1.0f;
-// The max used in exp2 is only raised when a tile's max exceeds it by more
-// than this (base-2 units): P <= 2^kLazy and O is rarely rescaled.
-constexpr float kLazy = 8.0f;
-
-// Kernel modes. In the mixed kernel (kMixed) the query tiles below
-// n_precise (those with a row that may see fewer than kPreciseKeys keys) run
-// the compensated P.V product; the others run the bf16-P product, and when
-// some of their rows need the compensated product the workgroup runs the tile
-// again, compensated, for those rows only. The compensated kernel (kAll)
-// computes every row of every tile compensated (the masked forward).
-// In the split-KV kernel (kSplit) a workgroup computes one key chunk of its
-// query tile, compensated, and writes the chunk's normalised partial O and its
-// logsumexp to a workspace; a combine kernel merges the chunks through L.
-// The paged kernels (kPaged, kPagedSplit) read K and V from a block-paged
-// cache through a block table, with a key count per sequence; they compute
-// every tile compensated, the second one as split-KV partials.
-// kPagedBlocks and kPagedBlocksSplit are the same for caches whose blocks are
-// shorter than a key tile (block_size a multiple of 16, not of 64).
-constexpr int kMixed = 0, kAll = 1, kSplit = 2, kPaged = 3, kPagedSplit = 4, kPagedBlocks = 5,
-              kPagedBlocksSplit = 6;
-
-
-struct FwdArgs {
-  const uint16_t* q;
-  const uint16_t* k;
-  const uint16_t* v;
-  const void* mask;          // f32, bf16 or bool bytes (the kernel's MASK), or null
-  int64_t mask_sb, mask_sh;  // mask strides of batch and head, in elements (0: broadcast)
-  int mask_sr;               // mask row stride, in elements (kl: rows contiguous)
-  uint16_t* o;
-  float* l;
-  int B, H, Hkv, ql, kl;
-  int group;       // H / Hkv
-  int n_qtiles;    // ceil(ql / rows per workgroup)
-  int qt_base;     // this launch computes query tiles [qt_base, qt_base + qt_count)
-  int qt_count;
-  int n_precise;   // kMixed: query tiles below this run compensated
-  int causal_off;  // max(kl - ql, 0)
-  int window;      // WINDOW variants: keys below q_abs - window are hidden
-  int n_split;     // kSplit: key chunks per query tile (grid factor)
-  int kchunk;      // kSplit: keys per chunk (a multiple of the key tile)
-  float* ws_o;     // kSplit: partial O, f32 [n_split, B, H, ql, D]
-  float* ws_l;     // kSplit: partial L, f32 [n_split, B, H, ql]
-  const int* block_table;  // paged: int32 [B, max_blocks], block of each block_size keys
-  const int* seq_lens;     // paged: int32 [B], keys of each sequence
-  int max_blocks, block_size, n_blocks;  // paged: table width, keys per block, cache blocks
-  float c;         // |scale| * log2(e), at least FLT_MIN
-  uint32_t q_sign; // 0x80008000 flips the sign of both bf16 halves (scale < 0)
-  // element strides of batch, head and row (head_dim is contiguous) of Q, K,
-  // V and O; L is always contiguous [B, H, ql]
-  // (row strides are at most 2^24 elements for K and V, 2^31 - 1 for Q and O)
-  int64_t q_sb, q_sh, k_sb, k_sh, v_sb, v_sh, o_sb, o_sh;
-  int q_sr, k_sr, v_sr, o_sr;
-};
-
-
-// One query tile of one head: rows qtile * block_m .. of head bh. PRECISE
-// selects the compensated P.V product. Without it, a row whose result needs
-// that product is not written; its lane's redo[qb] is set instead, and the
-// return value tells the whole workgroup whether any of its rows needs it
-// (wg_flags: one int per wave). With REDO (and PRECISE), only the rows with
-// redo set are computed and written (waves without such a row only take part
-// in the tile copies).
-template <int D, bool CAUSAL, bool WINDOW, int MASK, bool PRECISE, bool REDO, bool SPLIT = false,
-          bool PAGED = false, bool SMALL_BLOCKS = false>
-__device__ __forceinline__ bool fwd_tile(const FwdArgs& a, int qtile, int bh, uint16_t* k0s,
-                                         uint16_t* v0s, uint16_t* k1s, uint16_t* v1s,
-                                         bool (&redo)[Cfg<D>::QB], int* wg_flags, int split = 0) {
-  constexpr bool HAS_MASK = MASK != kNoMask;
-  static_assert(PRECISE || !HAS_MASK, "the masked forward always runs compensated");
-  static_assert(PRECISE || !REDO, "a redo runs compensated");
-  static_assert(CAUSAL || !WINDOW, "the sliding window includes the causal rule");
-  static_assert(!SPLIT || (PRECISE && !REDO && !WINDOW && MASK == kNoMask),
-                "split-KV partials: compensated, unmasked, no window");
-  static_assert(!PAGED || (PRECISE && !REDO && !WINDOW && MASK == kNoMask),
-                "paged KV: compensated, unmasked, no window");
-  constexpr int BN = Cfg<D>::BN;
-  constexpr int kQB = Cfg<D>::QB;
-  constexpr int kRowsPerWave = 16 * kQB;
-  constexpr int kBlockM = block_m<D>();
-  constexpr int NKB = BN / 16;  // 16-key blocks per tile
-  constexpr int NKC = BN / 32;  // 32-key chunks per tile (P.V contraction steps)
-  constexpr int NDB = D / 16;   // 16-dim blocks of O
-  constexpr int NDS = D / 32;   // 32-dim steps of Q.K
-  constexpr int TILE = BN * D;  // elements per K or V tile
-  constexpr int NT = 64 * Cfg<D>::W;  // threads per workgroup
-  static_assert(TILE > 0, "empty tile");
-  // Plain tiles take Q pre-scaled by c = |scale| log2(e) and rounded to bf16,
-  // so that the MFMA yields base-2 scores; their accumulators start at -m
-  // (the running max), so exp2 reads the MFMA's output directly. The
-  // compensated tiles keep Q exact and scale in f32.
-  constexpr bool PS = !PRECISE;
-
-  // (the opaque copy keeps the compiler from hoisting the thread-index
-  // arithmetic of both tile variants of the mixed kernel above their branch,
-  // where it would stay live, and spill, across both)
-  int tid = threadIdx.x;
-  asm volatile("" : "+v"(tid));
-  // The wave index is made provably wave-uniform so that every condition
-  // derived from it (tile skipping, masking, row selection) compiles to a
-  // scalar branch: an MFMA left inside an EXEC-masked region still accumulates
-  // (with whatever its operand registers hold) when EXEC is zero.
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lane = tid & 63;
-  const int c16 = lane & 15;  // query column within a 16-row block / A-operand row
-  const int grp = lane >> 4;  // 16-lane group
-
-  const int b = bh / a.H, h = bh % a.H;
-  const int g = h / a.group;
-  // (paged KV: the sequence's own key count, at most its table's capacity, and
-  // its own causal offset)
-  const int kl = PAGED ? min(max(__builtin_amdgcn_readfirstlane(a.seq_lens[b]), 0),
-                             a.max_blocks * a.block_size)
-                       : a.kl;
-  const int ql = a.ql, off = PAGED ? max(kl - ql, 0) : a.causal_off;
-  const int q0 = qtile * kBlockM;
-  const int qw0 = q0 + wave * kRowsPerWave;
-  const uint16_t* kp = a.k + b * a.k_sb + g * a.k_sh;
-  const uint16_t* vp = a.v + b * a.v_sb + g * a.v_sh;
-  // row strides of the K and V sources (a paged cache's rows are contiguous)
-  const int k_rs = PAGED ? D : a.k_sr, v_rs = PAGED ? D : a.v_sr;
-
-  // ---- key range ----
-  // (split-KV: only the keys of chunk `split`, [split*kchunk, (split+1)*kchunk))
-  const int k_hi = SPLIT ? (split + 1) * a.kchunk : kl;
-  const int last_row = min(q0 + kBlockM, ql) - 1;
-  const int kend = min(k_hi, CAUSAL ? min(kl, off + last_row + 1) : kl);
-  const int n_kt = (kend + BN - 1) / BN;
-  // under a sliding window no row of the workgroup (of the wave) sees a key
-  // below off + (its first row) - window: those key tiles are skipped
-  const int kt_first = SPLIT ? split * a.kchunk / BN : WINDOW ? max(0, off + q0 - a.window) / BN : 0;
-  const bool wave_active = qw0 < ql;
-  const int wave_last = min(qw0 + kRowsPerWave, ql) - 1;
-  const int wave_kend = min(k_hi, CAUSAL ? min(kl, off + wave_last + 1) : kl);
-  const int wave_kt_first =
-      SPLIT ? kt_first : WINDOW ? max(0, off + qw0 - a.window) / BN : 0;
-  float* lrow_base = a.l + (int64_t)bh * ql;
-
-  bool wave_redo = false;
-#pragma unroll
-  for (int qb = 0; qb < kQB; ++qb) wave_redo |= redo[qb];
-  const bool compute = wave_active && (!REDO || __any(wave_redo));
-
-  int koff[CopyShape<D, BN, NT>::ROUNDS], voff[CopyShape<D, BN, NT>::ROUNDS];
-  copy_offsets<D, BN, NT, true>(tid, koff, k_rs);
-  copy_offsets<D, BN, NT, false>(tid, voff, v_rs);
-  // paged KV: when block_size is a multiple of BN a tile lies in one block,
-  // table[b][kt*BN / block_size], from row (kt*BN) % block_size, and its copy
-  // descriptor covers only the tile's valid rows; shorter blocks (multiples
-  // of 16) are looked up per wave instruction (issue_tile_blocks). A table
-  // entry outside the cache is clamped into it (wrong keys, never an access
-  // outside the cache).
-  const int* table_row = PAGED ? a.block_table + (int64_t)b * a.max_blocks : nullptr;
-  auto paged_src = [&](const uint16_t* cache, int kt) {
-    const int pos = kt * BN;
-    int blk = __builtin_amdgcn_readfirstlane(
-        a.block_table[(int64_t)b * a.max_blocks + pos / a.block_size]);
-    blk = min(max(blk, 0), a.n_blocks - 1);
-    return cache + (((int64_t)blk * a.Hkv + g) * a.block_size + pos % a.block_size) * D;
-  };
-  auto issue_k = [&](int kt, uint16_t* dst) {
-    if constexpr (PAGED) {
-      if constexpr (!SMALL_BLOCKS)
-        issue_tile<D, BN, NT, true>(paged_src(a.k, kt), 0, min(BN, kl - kt * BN), dst, tid,
-                                    64 * wave, koff);
-      else
-        issue_tile_blocks<D, BN, NT, true>(a.k, table_row, a.n_blocks, a.Hkv, g, a.block_size,
-                                           kt * BN, kl, dst, tid, 64 * wave);
-    } else
-      issue_tile<D, BN, NT, true>(kp, kt * BN, kl, dst, tid, 64 * wave, koff, k_rs);
-  };
-  auto issue_v = [&](int kt, uint16_t* dst) {
-    if constexpr (PAGED) {
-      if constexpr (!SMALL_BLOCKS)
-        issue_tile<D, BN, NT, false>(paged_src(a.v, kt), 0, min(BN, kl - kt * BN), dst, tid,
-                                     64 * wave, voff);
-      else
-        issue_tile_blocks<D, BN, NT, false>(a.v, table_row, a.n_blocks, a.Hkv, g, a.block_size,
-                                            kt * BN, kl, dst, tid, 64 * wave);
-    } else
-      issue_tile<D, BN, NT, false>(vp, kt * BN, kl, dst, tid, 64 * wave, voff, v_rs);
-  };
-  if (n_kt > kt_first) issue_k(kt_first, (kt_first & 1) ? k1s : k0s);
-
-  // ---- Q^T as the B operand: block qb, step s: row qw0+16qb+c16, dims 32s+8grp.. ----
-  bf16x8 qop[kQB][NDS];
-#pragma unroll
-  for (int qb = 0; qb < kQB; ++qb) {
-    const int qrow = min(qw0 + 16 * qb + c16, ql - 1);
-    const uint16_t* qp = a.q + b * a.q_sb + h * a.q_sh + (int64_t)qrow * a.q_sr + 8 * grp;
-#pragma unroll
-    for (int s = 0; s < NDS; ++s) {
-      u32x4 raw = *reinterpret_cast<const u32x4*>(qp + 32 * s);
-      raw ^= a.q_sign;
-      qop[qb][s] = __builtin_bit_cast(bf16x8, raw);
-      if constexpr (PS) {
-        bf16x8 sc;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) sc[e] = (__bf16)((float)qop[qb][s][e] * a.c);
-        qop[qb][s] = sc;
-      }
-    }
-  }
-
-  // m_use: the max used in exp2 (base 2); thr: the tile max above which a
-  // tile raises it (m_use + kLazy in raw units; in the plain tiles, whose
-  // scores come relative to m_use, kLazy); l_run: this lane's partial row
-  // sum. The plain tiles start m_use at 0 (their scores are then the raw
-  // ones) and take the first visible key's tile max as it; the compensated
-  // ones start at the finite sentinel -FLT_MAX/2.
-  float m_use[kQB], thr[kQB], l_run[kQB];
-  f32x4 oacc[NDB][kQB];
-  const float inv_c = HAS_MASK ? 1.0f : 1.0f / a.c;
-#pragma unroll
-  for (int qb = 0; qb < kQB; ++qb) {
-    m_use[qb] = PS ? 0.0f : -FLT_MAX / 2.0f;
-    thr[qb] = -INFINITY;
-    l_run[qb] = 0.0f;
-#pragma unroll
-    for (int d = 0; d < NDB; ++d) oacc[d][qb] = f32x4{};
-  }
-
-  // The wave's own key tiles, and the first of them that needs a mask (the
-  // partial last tile, or the causal diagonal of the wave's first row).
-  const int n_kw = (compute && wave_kend > 0) ? (wave_kend + BN - 1) / BN : 0;
-  int mask_from = HAS_MASK ? 0 : n_kw;
-  if (!HAS_MASK) {
-    if (kl % BN != 0) mask_from = min(mask_from, kl / BN);
-    if (CAUSAL) mask_from = min(mask_from, (off + qw0 + 1) / BN);
-  }
-  // and the tiles below lo_end, which hold keys that the wave's last row no
-  // longer sees (the window's lower edge)
-  const int lo_gap = WINDOW ? off + wave_last - a.window : 0;
-  const int lo_end = lo_gap > 0 ? (lo_gap + BN - 1) / BN : 0;
-
-  const int lane_c16 = c16, lane_grp = grp;
-
-  // ---- S^T = K Q^T (raw scores, f32) for the tile in ks ----
-  auto kread = [&](const uint16_t* ks, int s, int kb) {
-    const int r = key_of(kb, lane_c16);
-    // (one index off the tile: every LDS address a short GEP chain from its
-    // buffer, so that the compiler keeps the buffer's alias scope on the read)
-    return *reinterpret_cast<const bf16x8*>(ks +
-                                            (r * D + 8 * ((4 * s + lane_grp) ^ kswz<D>(r))));
-  };
-  auto scores = [&](const uint16_t* ks, f32x4 (&sacc)[NKB][kQB]) {
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int qb = 0; qb < kQB; ++qb) {
-        if constexpr (PS)
-          sacc[kb][qb] = f32x4{-m_use[qb], -m_use[qb], -m_use[qb], -m_use[qb]};
-        else
-          sacc[kb][qb] = f32x4{};
-      }
-    if constexpr (D <= 128) {
-#pragma unroll
-      for (int s = 0; s < NDS; ++s)
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-          const bf16x8 kop = kread(ks, s, kb);
-#pragma unroll
-          for (int qb = 0; qb < kQB; ++qb)
-            sacc[kb][qb] =
-                __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop[qb][s], sacc[kb][qb], 0, 0, 0);
-        }
-    } else {
-      // D=256: K operands in groups of SG dim steps, the next group's reads
-      // issued before the current group's MFMAs; sched_barrier keeps that
-      // order (and the register use) instead of hoisting every read.
-      constexpr int SG = NKB == 2 ? 2 : 1;
-      constexpr int NG = NDS / SG;
-      bf16x8 kop[2][SG][NKB];
-#pragma unroll
-      for (int ss = 0; ss < SG; ++ss)
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) kop[0][ss][kb] = kread(ks, ss, kb);
-#pragma unroll
-      for (int g = 0; g < NG; ++g) {
-        if (g + 1 < NG) {
-#pragma unroll
-          for (int ss = 0; ss < SG; ++ss)
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb)
-              kop[(g + 1) & 1][ss][kb] = kread(ks, (g + 1) * SG + ss, kb);
-        }
-#pragma unroll
-        for (int ss = 0; ss < SG; ++ss)
-#pragma unroll
-          for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-            for (int qb = 0; qb < kQB; ++qb)
-              sacc[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                  kop[g & 1][ss][kb], qop[qb][g * SG + ss], sacc[kb][qb], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-  };
-
-  // ---- masks of tile kt: tail keys, causal, additive ----
-  auto apply_mask = [&](int kt, f32x4 (&sacc)[NKB][kQB]) {
-    const int kbase = kt * BN;
-#pragma unroll
-    for (int qb = 0; qb < kQB; ++qb) {
-      const int qrow = qw0 + 16 * qb + c16;
-      if constexpr (HAS_MASK) {
-        const int64_t mrow =
-            b * a.mask_sb + h * a.mask_sh + (int64_t)min(qrow, ql - 1) * a.mask_sr;
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int key = kbase + 32 * (kb >> 1) + 8 * grp + 4 * (kb & 1) + i;
-            const bool vis = key < kl && (!CAUSAL || key <= off + qrow) &&
-                             (!WINDOW || key >= off + qrow - a.window);
-            // (the index is clamped so that keys past the end read inside the row)
-            const float mv = mask_at<MASK>(a.mask, mrow + min(key, kl - 1));
-            sacc[kb][qb][i] = vis ? __builtin_fmaf(sacc[kb][qb][i], a.c, kLog2e * mv) : -INFINITY;
-          }
-      } else {
-        // the last (and, under a window, the first) visible key of the row,
-        // relative to this lane's first key of the tile; each score then needs
-        // one compare with a constant per edge
-        const int last = (CAUSAL ? min(kl - 1, off + qrow) : kl - 1) - kbase - 8 * grp;
-        const int first = WINDOW ? off + qrow - a.window - kbase - 8 * grp : 0;
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int idx = 32 * (kb >> 1) + 4 * (kb & 1) + i;
-            if (idx > last || (WINDOW && idx < first)) sacc[kb][qb][i] = -INFINITY;
-          }
-      }
-    }
-  };
-
-  // ---- online softmax (base 2): row max of a tile, lazy raise ----
-  // (the decision to raise is taken per row, so a row's result never depends
-  // on its neighbours' scores)
-  // (the max is compared with thr in raw-score units; c > 0, so
-  // max(c*r) == c*max(r))
-  // The lane's own part of the row max (16 of the tile's keys for each of its
-  // rows) already tells whether the row max exceeds thr; only when some lane
-  // of the wave finds that is the max completed over the four 16-lane groups.
-  auto part_max = [&](const f32x4 (&sacc)[NKB][kQB], float (&mx)[kQB]) {
-#pragma unroll
-    for (int qb = 0; qb < kQB; ++qb) {
-      mx[qb] = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) mx[qb] = __builtin_fmaxf(mx[qb], sacc[kb][qb][i]);
-    }
-    bool raise = false;
-#pragma unroll
-    for (int qb = 0; qb < kQB; ++qb) raise |= mx[qb] > thr[qb];
-    return raise;
-  };
-  auto complete_max = [&](float (&mx)[kQB]) {
-    if constexpr (kQB == 2) {
-      group_max2(mx[0], mx[1]);
-    } else {
-#pragma unroll
-      for (int qb = 0; qb < kQB; ++qb) mx[qb] = group_max(mx[qb]);
-    }
-  };
-  auto rescale = [&](const float (&mx)[kQB], f32x4 (&sacc)[NKB][kQB]) {
-#pragma unroll
-    for (int qb = 0; qb < kQB; ++qb) {
-      const bool r = mx[qb] > thr[qb];
-      float m_new, alpha;
-      if constexpr (PS) {
-        // scores relative to m_use: the new max is m_use + mx, and this
-        // tile's scores move down by mx (later tiles start at the new -m_use).
-        // A row's first raise may lower m_use (from 0); its sum and O are
-        // still 0 then, and alpha is kept at most 1.
-        const float shift = r ? mx[qb] : 0.0f;
-        m_new = m_use[qb] + shift;
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) sacc[kb][qb] -= shift;
-        thr[qb] = r ? kLazy : thr[qb];
-        alpha = __builtin_amdgcn_exp2f(fminf(-shift, 0.0f));
-      } else {
-        m_new = r ? (HAS_MASK ? mx[qb] : mx[qb] * a.c) : m_use[qb];
-        thr[qb] = r ? (m_new + kLazy) * inv_c : thr[qb];
-        alpha = __builtin_amdgcn_exp2f(m_use[qb] - m_new);
-      }
-      m_use[qb] = m_new;
-      l_run[qb] *= alpha;
-#pragma unroll
-      for (int d = 0; d < NDB; ++d) oacc[d][qb] *= alpha;
-    }
-  };
-
-  // ---- P = exp2(s - m) in bf16 (+ remainder when compensated), row sums ----
-  auto probs = [&](const f32x4 (&sacc)[NKB][kQB], bf16x8 (&phi)[NKC][kQB],
-                   bf16x8 (&plo)[NKC][kQB]) {
-    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-#pragma unroll
-    for (int qb = 0; qb < kQB; ++qb) {
-      const float mneg = -m_use[qb];
-      float ls = l_run[qb];
-#pragma unroll
-      for (int j = 0; j < NKC; ++j) {
-        float p[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float sv = sacc[2 * j + (e >> 2)][qb][e & 3];
-          p[e] = __builtin_amdgcn_exp2f(HAS_MASK ? sv + mneg
-                                        : PS     ? sv
-                                                 : __builtin_fmaf(sv, a.c, mneg));
-          phi[j][qb][e] = (__bf16)p[e];
-        }
-#pragma unroll
-        for (int e = 0; e < 8; e += 2)
-          ls = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{phi[j][qb][e], phi[j][qb][e + 1]}, ones, ls,
-                                               false);
-        if (PRECISE) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) plo[j][qb][e] = (__bf16)(p[e] - (float)phi[j][qb][e]);
-#pragma unroll
-          for (int e = 0; e < 8; e += 2)
-            ls = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{plo[j][qb][e], plo[j][qb][e + 1]}, ones,
-                                                 ls, false);
-        }
-      }
-      l_run[qb] = ls;
-    }
-  };
-
-  // ---- O^T += V^T P^T for the tile in vs ----
-  // V^T operand of dim block d, key chunk j: dims 16d + c16, keys
-  // 32j + 8grp + (0..7), from two transposing reads of four keys each
-  auto vread = [&](const uint16_t* vs, int d, int j) {
-    s16x4 half[2];
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int r = 32 * j + 8 * lane_grp + 4 * t + (lane_c16 >> 2);
-      const int col = 16 * d + 4 * (lane_c16 & 3);
-      const uint16_t* addr = vs + (r * D + 8 * ((col >> 3) ^ vswz<D>(r)) + (col & 7));
-      half[t] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)addr);
-    }
-    return __builtin_bit_cast(bf16x8,
-                              __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7));
-  };
-  auto pv_mfma = [&](const bf16x8& vop, int d, int j, const bf16x8 (&phi)[NKC][kQB],
-                     const bf16x8 (&plo)[NKC][kQB]) {
-#pragma unroll
-    for (int qb = 0; qb < kQB; ++qb) {
-      oacc[d][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, phi[j][qb], oacc[d][qb], 0, 0, 0);
-      if (PRECISE)
-        oacc[d][qb] =
-            __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, plo[j][qb], oacc[d][qb], 0, 0, 0);
-    }
-  };
-  auto pv = [&](const uint16_t* vs, const bf16x8 (&phi)[NKC][kQB], const bf16x8 (&plo)[NKC][kQB]) {
-    if constexpr (D <= 128) {
-#pragma unroll
-      for (int d = 0; d < NDB; ++d)
-#pragma unroll
-        for (int j = 0; j < NKC; ++j) pv_mfma(vread(vs, d, j), d, j, phi, plo);
-    } else {
-      // D=256: V operands in groups of DG dim blocks, prefetched one group
-      // ahead as for K
-      constexpr int DG = NKC == 1 ? 4 : 2;
-      constexpr int NG = NDB / DG;
-      bf16x8 vop[2][DG][NKC];
-#pragma unroll
-      for (int dd = 0; dd < DG; ++dd)
-#pragma unroll
-        for (int j = 0; j < NKC; ++j) vop[0][dd][j] = vread(vs, dd, j);
-#pragma unroll
-      for (int g = 0; g < NG; ++g) {
-        if (g + 1 < NG) {
-#pragma unroll
-          for (int dd = 0; dd < DG; ++dd)
-#pragma unroll
-            for (int j = 0; j < NKC; ++j) vop[(g + 1) & 1][dd][j] = vread(vs, (g + 1) * DG + dd, j);
-        }
-#pragma unroll
-        for (int dd = 0; dd < DG; ++dd)
-#pragma unroll
-          for (int j = 0; j < NKC; ++j) pv_mfma(vop[g & 1][dd][j], g * DG + dd, j, phi, plo);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-  };
-
-  // ---- the key loop ----
-  // One tile per step: wait for its copy, start the next one, compute it.
-  // Where registers allow (PAIRED), the steps come in pairs with fixed buffer
-  // roles (even tiles in buffer 0, odd tiles in buffer 1), so that the
-  // compiler can tell the LDS reads of a tile from the copy of the next one in
-  // flight into the other buffer: with the buffer chosen at run time it makes
-  // every wave wait for that copy before its V^T reads (measured: D=64 4k
-  // causal 326 -> 316 us, D=256 8k 1106 -> 1065 us). With fixed buffers the
-  // compiler keeps the addresses of both buffers in registers, which spills
-  // in the sliding-window, split-KV and paged kernels and in the compensated
-  // tiles of the mixed kernel (the short first tiles and the rare redo):
-  // those keep one step per iteration.
-  constexpr bool PAIRED = !WINDOW && !SPLIT && !PAGED && (!PRECISE || HAS_MASK);
-  auto step = [&](int kt, const uint16_t* kc, const uint16_t* vc, uint16_t* kn, uint16_t* vn) {
-    wait_vmem();
-    __syncthreads();
-    if (kt + 1 < n_kt) {
-      issue_k(kt + 1, kn);
-      issue_v(kt + 1, vn);
-    }
-    if (kt >= wave_kt_first && kt < n_kw) {
-      // A wave issuing its MFMA blocks gets a raised priority (s_setprio), so
-      // it is not held back behind the other waves' VALU work; measured best
-      // around the P.V block for D=64 and around both blocks for D=256.
-      f32x4 s[NKB][kQB];
-      if (D == 256) set_prio<2>();
-      scores(kc, s);
-      if (D == 256) set_prio<0>();
-      if (kt >= mask_from || (WINDOW && kt < lo_end)) apply_mask(kt, s);
-      float mx[kQB];
-      if (__any(part_max(s, mx))) {
-        complete_max(mx);
-        rescale(mx, s);
-      }
-      bf16x8 phi[NKC][kQB], plo[NKC][kQB];
-      probs(s, phi, plo);
-      set_prio<2>();
-      pv(vc, phi, plo);
-      set_prio<0>();
-    }
-  };
-  if (n_kt > kt_first) issue_v(kt_first, (kt_first & 1) ? v1s : v0s);
-  if constexpr (PAIRED) {
-    for (int kt = kt_first & ~1; kt < n_kt; kt += 2) {
-      if (kt >= kt_first) step(kt, k0s, v0s, k1s, v1s);
-      if (kt + 1 < n_kt) step(kt + 1, k1s, v1s, k0s, v0s);
-    }
-  } else {
-    for (int kt = kt_first; kt < n_kt; ++kt) {
-      const bool odd = kt & 1;
-      step(kt, odd ? k1s : k0s, odd ? v1s : v0s, odd ? k0s : k1s, odd ? v0s : v1s);
-    }
-  }
-
-  // ---- epilogue: O = O_acc / l (+0 for an empty row), L = (m + log2 l) ln 2 ----
-  float l_tot[kQB];
-  bool write[kQB];
-  bool wg_any = false;
-#pragma unroll
-  for (int qb = 0; qb < kQB; ++qb) {
-    const int qrow = qw0 + 16 * qb + c16;
-    const bool row_ok = compute && qrow < ql;
-    l_tot[qb] = group_sum(l_run[qb]);
-    write[qb] = REDO ? row_ok && redo[qb] : row_ok;
-    if (!PRECISE) {
-      // rows whose plain result is not accurate enough are redone compensated
-      float omax = 0.0f;
-#pragma unroll
-      for (int d = 0; d < NDB; ++d)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) omax = __builtin_fmaxf(omax, __builtin_fabsf(oacc[d][qb][i]));
-      omax = group_max(omax);
-      redo[qb] = row_ok && l_tot[qb] > 0.0f && omax >= kRecheckO * l_tot[qb];
-      write[qb] = row_ok && !redo[qb];
-    }
-  }
-  if (!PRECISE) {
-    // one flag per wave, then every wave reads all of them (every tile copy
-    // has landed here: the last key step waited for its own)
-    bool mine = false;
-#pragma unroll
-    for (int qb = 0; qb < kQB; ++qb) mine |= redo[qb];
-    const bool wave_any = __any(mine);
-    if (lane == 0) wg_flags[wave] = wave_any;
-    __syncthreads();
-#pragma unroll
-    for (int w = 0; w < Cfg<D>::W; ++w) wg_any |= wg_flags[w] != 0;
-  }
-#pragma unroll
-  for (int qb = 0; qb < kQB; ++qb) {
-    const int qrow = qw0 + 16 * qb + c16;
-    if (write[qb]) {
-      const float lt = l_tot[qb];
-      const bool empty = !(lt > 0.0f);
-      const float inv = empty ? 0.0f : __builtin_amdgcn_rcpf(lt);
-      const float lse = empty ? -INFINITY : (m_use[qb] + __builtin_amdgcn_logf(lt)) * kLn2;
-      if constexpr (SPLIT) {
-        // the chunk's partial: O normalised by its own sum (f32), and its L
-        const int64_t prow = ((int64_t)split * a.B * a.H + bh) * ql + qrow;
-        float* op = a.ws_o + prow * D + 4 * grp;
-#pragma unroll
-        for (int d = 0; d < NDB; ++d) {
-          f32x4 ov;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) ov[i] = empty ? 0.0f : oacc[d][qb][i] * inv;
-          *reinterpret_cast<f32x4*>(op + 16 * d) = ov;
-        }
-        if (grp == 0) a.ws_l[prow] = lse;
-      } else {
-        uint16_t* orow = a.o + b * a.o_sb + h * a.o_sh + (int64_t)qrow * a.o_sr + 4 * grp;
-#pragma unroll
-        for (int d = 0; d < NDB; ++d) {
-          bf16x4 ov;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) ov[i] = empty ? (__bf16)0.0f : (__bf16)(oacc[d][qb][i] * inv);
-          *reinterpret_cast<bf16x4*>(orow + 16 * d) = ov;
-        }
-        if (grp == 0) lrow_base[qrow] = lse;
-      }
-    }
-  }
-  // no LDS copy may still be in flight when the workgroup ends (waiting for
-  // the stores here too was measured faster for D=256 than leaving them)
-  wait_vmem();
-  return wg_any;
-}
-
-template <int D, bool CAUSAL, bool WINDOW, int MASK, int MODE>
-__global__ __launch_bounds__(64 * Cfg<D>::W)
-__attribute__((amdgpu_waves_per_eu(MODE == kMixed ? Cfg<D>::WPE : 2))) void fa_fwd_kernel(FwdArgs a) {
-  static_assert(MODE < kSplit || (MASK == kNoMask && !WINDOW),
-                "split-KV and paged: unmasked, no window");
-  static_assert(MODE != kMixed || MASK == kNoMask, "the masked forward always runs compensated");
-#if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
-  constexpr int TILE = Cfg<D>::BN * D;
-  __shared__ __attribute__((aligned(1024))) uint16_t k0s[TILE];
-  __shared__ __attribute__((aligned(1024))) uint16_t v0s[TILE];
-  __shared__ __attribute__((aligned(1024))) uint16_t k1s[TILE];
-  __shared__ __attribute__((aligned(1024))) uint16_t v1s[TILE];
-  __shared__ int wg_flags[Cfg<D>::W];
-
-  // ---- work item ----
-  // Workgroups are handed to the 8 XCDs round-robin (bid mod 8). When B*H is a
-  // multiple of 8, XCD x owns the heads [x*per, (x+1)*per) (so one KV group
-  // stays within one XCD's L2), takes them in groups of 8 (when per is a
-  // multiple of 8; fewer K/V in flight per L2) and walks each group's query
-  // tiles heaviest (most keys) first, so the cheap tiles fill the tail.
-  // (Groups of 1, 2 or 4 heads were measured slower, 8 faster than all.)
-  // (split-KV: the chunk index is the fastest-varying part of the block index)
-  const int BH = a.B * a.H;
-  constexpr bool SPLIT_GRID = MODE == kSplit || MODE == kPagedSplit || MODE == kPagedBlocksSplit;
-  const int split = SPLIT_GRID ? (int)(blockIdx.x % (unsigned)a.n_split) : 0;
-  const int bid = SPLIT_GRID ? (int)(blockIdx.x / (unsigned)a.n_split) : (int)blockIdx.x;
-  int qt_rev, bh;
-  if ((BH & 7) == 0) {
-    const int xcd = bid & 7, tl = bid >> 3, per = BH >> 3;
-    const int gh = (per & 7) == 0 ? 8 : per;  // heads per group
-    const int gsz = gh * a.qt_count;          // workgroups per group
-    const int gi = tl / gsz, r = tl % gsz;
-    qt_rev = r / gh;
-    bh = xcd * per + gi * gh + r % gh;
-  } else {
-    qt_rev = bid / BH;
-    bh = bid % BH;
-  }
-  const int qtile = a.qt_base + a.qt_count - 1 - qt_rev;
-  bool redo[Cfg<D>::QB] = {};
-  if constexpr (MODE == kMixed) {
-    // the compensated tiles are the lightest, so they run last and fill the tail
-    if (qtile < a.n_precise) {
-      fwd_tile<D, CAUSAL, WINDOW, kNoMask, true, false>(a, qtile, bh, k0s, v0s, k1s, v1s, redo,
-                                                        wg_flags);
-    } else if (fwd_tile<D, CAUSAL, WINDOW, kNoMask, false, false>(a, qtile, bh, k0s, v0s, k1s, v1s,
-                                                                  redo, wg_flags)) {
-      // (the plain pass's last barrier came after every wave's last LDS read,
-      // so the redo's copies may reuse the tile buffers)
-      fwd_tile<D, CAUSAL, WINDOW, kNoMask, true, true>(a, qtile, bh, k0s, v0s, k1s, v1s, redo,
-                                                       wg_flags);
-    }
-  } else if constexpr (MODE == kSplit) {
-    fwd_tile<D, CAUSAL, false, kNoMask, true, false, true>(a, qtile, bh, k0s, v0s, k1s, v1s, redo,
-                                                           wg_flags, split);
-  } else if constexpr (MODE == kPaged) {
-    fwd_tile<D, CAUSAL, false, kNoMask, true, false, false, true>(a, qtile, bh, k0s, v0s, k1s,
-                                                                  v1s, redo, wg_flags);
-  } else if constexpr (MODE == kPagedSplit) {
-    fwd_tile<D, CAUSAL, false, kNoMask, true, false, true, true>(a, qtile, bh, k0s, v0s, k1s, v1s,
-                                                                 redo, wg_flags, split);
-  } else if constexpr (MODE == kPagedBlocks) {
-    fwd_tile<D, CAUSAL, false, kNoMask, true, false, false, true, true>(a, qtile, bh, k0s, v0s,
-                                                                        k1s, v1s, redo, wg_flags);
-  } else if constexpr (MODE == kPagedBlocksSplit) {
-    fwd_tile<D, CAUSAL, false, kNoMask, true, false, true, true, true>(
-        a, qtile, bh, k0s, v0s, k1s, v1s, redo, wg_flags, split);
-  } else {
-    fwd_tile<D, CAUSAL, WINDOW, MASK, true, false>(a, qtile, bh, k0s, v0s, k1s, v1s, redo,
-                                                   wg_flags);
-  }
-#endif
-}
-
-// Merge of the split-KV partials of each row (one wave per row, lane l holds
-// dims l*P .. l*P+P-1): L = m + ln sum_s exp(L_s - m), O = sum_s exp(L_s - L) O_s,
-// the same merge through L that combines key partitions computed apart.
-struct CombineArgs {
-  const float* ws_o;  // [n_split, rows, D]
-  const float* ws_l;  // [n_split, rows]
-  uint16_t* o;        // bf16 [rows, D]
-  float* l;           // f32 [rows]
-  int64_t rows;       // B * H * ql
-  int n_split;
-  int H, ql;
-  int64_t o_sb, o_sh;  // O's element strides of batch, head and row
-  int o_sr;
-};
-
-template <int D>
-__global__ __launch_bounds__(256) void fa_combine_kernel(CombineArgs c) {
-  constexpr int P = D / 64;
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= c.rows) return;
-  const int lane = threadIdx.x & 63;
-  float m = -INFINITY;
-  for (int s = 0; s < c.n_split; ++s) m = fmaxf(m, c.ws_l[s * c.rows + row]);
-  float acc[P] = {};
-  float z = 0.0f;
-  if (m != -INFINITY) {
-    for (int s = 0; s < c.n_split; ++s) {
-      // (a chunk with no visible key has L_s = -inf: weight 0, partial O 0)
-      const float w = __builtin_amdgcn_exp2f((c.ws_l[s * c.rows + row] - m) * kLog2e);
-      z += w;
-      const float* op = c.ws_o + (s * c.rows + row) * D + lane * P;
-#pragma unroll
-      for (int e = 0; e < P; ++e) acc[e] += w * op[e];
-    }
-  }
-  const bool empty = m == -INFINITY;
-  const float inv = empty ? 0.0f : 1.0f / z;
-  const int64_t bh = row / c.ql;
-  uint16_t* orow = c.o + (bh / c.H) * c.o_sb + (bh % c.H) * c.o_sh + (row % c.ql) * c.o_sr +
-                   lane * P;
-#pragma unroll
-  for (int e = 0; e < P; ++e)
-    orow[e] = __builtin_bit_cast(uint16_t, empty ? (__bf16)0.0f : (__bf16)(acc[e] * inv));
-  if (lane == 0) c.l[row] = empty ? -INFINITY : m + __builtin_amdgcn_logf(z) * kLn2;
-}
-
-template <int D, bool CAUSAL, bool WINDOW, int MASK, int MODE>
-hipError_t launch(const FwdArgs& a, unsigned grid, hipStream_t stream) {
-  hipLaunchKernelGGL((fa_fwd_kernel<D, CAUSAL, WINDOW, MASK, MODE>), dim3(grid),
-                     dim3(64 * Cfg<D>::W), 0, stream, a);
-  return hipGetLastError();
-}
-
-// Masked: one compensated launch over all query tiles. Unmasked: the mixed
-// launch over all tiles (compensated for the tiles with short rows, the first
-// n_short ones; plain for the others, with a compensated redo of the rows
-// that need it inside the same workgroup).
-template <int D, bool CAUSAL, bool WINDOW>
-hipError_t dispatch_c(FwdArgs a, int mask, int n_short, hipStream_t stream) {
-  const unsigned bh = (unsigned)(a.B * a.H);
-  const int n_qt = a.n_qtiles;
-  a.qt_base = 0;
-  a.qt_count = n_qt;
-  if (mask != kNoMask) {
-    a.n_precise = n_qt;
-    return mask == kMaskBF16   ? launch<D, CAUSAL, WINDOW, kMaskBF16, kAll>(a, bh * n_qt, stream)
-           : mask == kMaskBool ? launch<D, CAUSAL, WINDOW, kMaskBool, kAll>(a, bh * n_qt, stream)
-                               : launch<D, CAUSAL, WINDOW, kMaskF32, kAll>(a, bh * n_qt, stream);
-  }
-  a.n_precise = n_short;
-  return launch<D, CAUSAL, WINDOW, kNoMask, kMixed>(a, bh * n_qt, stream);
-}
-
-// Split-KV: the partials over all (chunk, head, query tile), then the merge.
-// (MODE: kSplit, kPagedSplit or kPagedBlocksSplit)
-template <int D, bool CAUSAL, int MODE = kSplit>
-hipError_t dispatch_split(FwdArgs a, hipStream_t stream) {
-  const unsigned bh = (unsigned)(a.B * a.H);
-  a.qt_base = 0;
-  a.qt_count = a.n_qtiles;
-  a.n_precise = a.n_qtiles;
-  hipError_t e = launch<D, CAUSAL, false, kNoMask, MODE>(
-      a, bh * (unsigned)a.n_qtiles * (unsigned)a.n_split, stream);
-  if (e != hipSuccess) return e;
-  CombineArgs c;
-  c.ws_o = a.ws_o;
-  c.ws_l = a.ws_l;
-  c.o = a.o;
-  c.l = a.l;
-  c.rows = (int64_t)a.B * a.H * a.ql;
-  c.n_split = a.n_split;
-  c.H = a.H;
-  c.ql = a.ql;
-  c.o_sb = a.o_sb;
-  c.o_sh = a.o_sh;
-  c.o_sr = a.o_sr;
-  hipLaunchKernelGGL(fa_combine_kernel<D>, dim3((unsigned)((c.rows + 3) / 4)), dim3(256), 0, stream,
-                     c);
-  return hipGetLastError();
-}
-
-// Paged KV: one compensated launch over all query tiles, or the split-KV pair.
-template <int D, int MODE, int SPLIT_MODE>
-hipError_t dispatch_paged_m(FwdArgs a, bool causal, hipStream_t stream) {
-  if (a.n_split > 0)
-    return causal ? dispatch_split<D, true, SPLIT_MODE>(a, stream)
-                  : dispatch_split<D, false, SPLIT_MODE>(a, stream);
-  const unsigned grid = (unsigned)(a.B * a.H) * (unsigned)a.n_qtiles;
-  a.qt_base = 0;
-  a.qt_count = a.n_qtiles;
-  a.n_precise = a.n_qtiles;
-  return causal ? launch<D, true, false, kNoMask, MODE>(a, grid, stream)
-                : launch<D, false, false, kNoMask, MODE>(a, grid, stream);
-}
-
-template <int D>
-hipError_t dispatch_paged(const FwdArgs& a, bool causal, hipStream_t stream) {
-  return a.block_size % Cfg<D>::BN == 0
-             ? dispatch_paged_m<D, kPaged, kPagedSplit>(a, causal, stream)
-             : dispatch_paged_m<D, kPagedBlocks, kPagedBlocksSplit>(a, causal, stream);
-}
-
-template <int D>
-hipError_t dispatch_d(const FwdArgs& a, bool causal, bool window, int mask, int n_short,
-                      hipStream_t stream) {
-  if (a.n_split > 0)
-    return causal ? dispatch_split<D, true>(a, stream) : dispatch_split<D, false>(a, stream);
-  if (window) return dispatch_c<D, true, true>(a, mask, n_short, stream);
-  return causal ? dispatch_c<D, true, false>(a, mask, n_short, stream)
-                : dispatch_c<D, false, false>(a, mask, n_short, stream);
-}
-
 bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
 
+// Query rows per workgroup of a (DK, DV) pair, 0 for a pair without kernels.
+int block_m_of(int dk, int dv) {
+  if (dk == dv) {
+    switch (dk) {
+      case 64: return block_m<64, 64>();
+      case 80: return block_m<80, 80>();
+      case 96: return block_m<96, 96>();
+      case 128: return block_m<128, 128>();
+      case 192: return block_m<192, 192>();
+      case 256: return block_m<256, 256>();
+    }
+    return 0;
+  }
+  if (dk == 96 && dv == 64) return block_m<96, 64>();
+  if (dk == 192 && dv == 128) return block_m<192, 128>();
+  return 0;
+}
+// Head dims of the split-KV, paged and backward paths.
+bool base_dim(int d) { return d == 64 || d == 128 || d == 256; }
+
 // Shared host path of every forward entry point; window < 0: none (window >= 0
-// requires causal). The mask is mask_dtype (FA_MASK_F32 / FA_MASK_BF16) with
+// requires causal). head_dim is the key width DK, head_dim_v the value width DV
+// (V, O and the split-KV partials). The mask is mask_dtype (FA_MASK_F32 / FA_MASK_BF16) with
 // batch and head strides in elements; its rows are contiguous (row stride kl).
 // Split-KV workspace: partial O (f32, n * rows * D) then, 256-byte aligned,
 // partial L (f32, n * rows).
@@ -920,13 +59,16 @@ constexpr int kMaxSplit = 65536;
 // workspace.
 int train_fwd(const void* q, const void* k, const void* v, const void* mask, int mask_dtype,
               int64_t mask_sb, int64_t mask_sh, int batch, int n_heads, int n_kv_heads, int ql,
-              int kl, int head_dim, float scale, int causal, int window, void* O, float* L,
-              void* stream, int n_split = 0, void* workspace = nullptr,
+              int kl, int head_dim, int head_dim_v, float scale, int causal, int window, void* O,
+              float* L, void* stream, int n_split = 0, void* workspace = nullptr,
               size_t workspace_bytes = 0, const int64_t* strides = nullptr,
               int64_t mask_sr = -1) {
   if (batch < 0 || ql < 0 || kl < 0 || n_heads < 1 || n_kv_heads < 1) return FA_ERR_BAD_SIZE;
   if (n_heads % n_kv_heads != 0) return FA_ERR_HEAD_GROUPING;
-  if (head_dim != 64 && head_dim != 128 && head_dim != 256) return FA_ERR_HEAD_DIM;
+  const int bm = block_m_of(head_dim, head_dim_v);
+  if (bm == 0 || (n_split > 0 && (head_dim != head_dim_v || !base_dim(head_dim))))
+    return FA_ERR_HEAD_DIM;
+  const int dv = head_dim_v;
   if (!isfinite(scale)) return FA_ERR_SCALE;
   if (window >= 0 && !causal) return FA_ERR_WINDOW;
   if (mask && ((mask_dtype != FA_MASK_F32 && mask_dtype != FA_MASK_BF16 &&
@@ -936,8 +78,8 @@ int train_fwd(const void* q, const void* k, const void* v, const void* mask, int
   // element strides (batch, head, row) of Q, K, V, O: given, or contiguous
   int64_t st[12] = {(int64_t)n_heads * ql * head_dim,    (int64_t)ql * head_dim, head_dim,
                     (int64_t)n_kv_heads * kl * head_dim, (int64_t)kl * head_dim, head_dim,
-                    (int64_t)n_kv_heads * kl * head_dim, (int64_t)kl * head_dim, head_dim,
-                    (int64_t)n_heads * ql * head_dim,    (int64_t)ql * head_dim, head_dim};
+                    (int64_t)n_kv_heads * kl * dv,       (int64_t)kl * dv,       dv,
+                    (int64_t)n_heads * ql * dv,          (int64_t)ql * dv,       dv};
   if (strides) {
     for (int i = 0; i < 12; ++i) {
       if (strides[i] < 0) return FA_ERR_STRIDE;
@@ -950,7 +92,7 @@ int train_fwd(const void* q, const void* k, const void* v, const void* mask, int
       return FA_ERR_TOO_LARGE;
     // O is written: no two of its elements may share an address
     const int64_t on[3] = {batch, n_heads, ql};
-    if (view_overlaps(st + 9, on, head_dim)) return FA_ERR_STRIDE;
+    if (view_overlaps(st + 9, on, dv)) return FA_ERR_STRIDE;
   }
   const int64_t rows = (int64_t)batch * n_heads * ql;
   if (rows == 0) return FA_OK;
@@ -981,14 +123,11 @@ int train_fwd(const void* q, const void* k, const void* v, const void* mask, int
     st[11] = st[10];
     st[10] *= G;
   }
-  const int bm = head_dim == 64    ? block_m<64>()
-                 : head_dim == 128 ? block_m<128>()
-                                   : block_m<256>();
   const int64_t n_qtiles = ((int64_t)ql + bm - 1) / bm;
   const int64_t grid = n_qtiles * batch * n_heads;
   if (grid > 0x7fffffffLL || (int64_t)batch * n_heads > 0x7fffffffLL ||
-      (int64_t)kl * head_dim * 2 > 0x7fffffffLL)  // one head's K or V must fit a buffer descriptor
-    return FA_ERR_TOO_LARGE;
+      (int64_t)kl * std::max(head_dim, dv) * 2 > 0x7fffffffLL)  // one head's K or V must fit a
+    return FA_ERR_TOO_LARGE;                                     // buffer descriptor
 
   FwdArgs a;
   a.q = static_cast<const uint16_t*>(q);
@@ -1036,13 +175,13 @@ int train_fwd(const void* q, const void* k, const void* v, const void* mask, int
     const int64_t n_eff = ((int64_t)kl + kchunk - 1) / kchunk;
     if (!workspace) return FA_ERR_NULL_POINTER;
     if (!aligned(workspace, 16)) return FA_ERR_ALIGNMENT;
-    if ((int64_t)workspace_bytes < split_bytes(rows, head_dim, n_eff)) return FA_ERR_SPLIT;
+    if ((int64_t)workspace_bytes < split_bytes(rows, dv, n_eff)) return FA_ERR_SPLIT;
     if (grid * n_eff > 0x7fffffffLL || (rows + 3) / 4 > 0x7fffffffLL) return FA_ERR_TOO_LARGE;
     a.n_split = (int)n_eff;
     a.kchunk = (int)kchunk;
     a.ws_o = static_cast<float*>(workspace);
     a.ws_l = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                      split_o_bytes(rows, head_dim, n_eff));
+                                      split_o_bytes(rows, dv, n_eff));
   }
 
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -1058,10 +197,17 @@ int train_fwd(const void* q, const void* k, const void* v, const void* mask, int
     n_short = n_qtiles;
   else if ((causal || windowed) && a.causal_off + 1 < kPreciseKeys)
     n_short = std::min<int64_t>(n_qtiles, (kPreciseKeys - 1 - a.causal_off + bm - 1) / bm);
-  hipError_t err =
-      head_dim == 64    ? dispatch_d<64>(a, causal != 0, windowed, mask_kind, (int)n_short, s)
-      : head_dim == 128 ? dispatch_d<128>(a, causal != 0, windowed, mask_kind, (int)n_short, s)
-                        : dispatch_d<256>(a, causal != 0, windowed, mask_kind, (int)n_short, s);
+  const bool cz = causal != 0;
+  const int ns = (int)n_short;
+  hipError_t err;
+  switch (head_dim) {
+    case 64: err = dispatch_d<64, 64>(a, cz, windowed, mask_kind, ns, s); break;
+    case 128: err = dispatch_d<128, 128>(a, cz, windowed, mask_kind, ns, s); break;
+    case 256: err = dispatch_d<256, 256>(a, cz, windowed, mask_kind, ns, s); break;
+    case 80: err = fa_fwd_detail::dispatch_d80(a, dv, cz, windowed, mask_kind, ns, s); break;
+    case 96: err = fa_fwd_detail::dispatch_d96(a, dv, cz, windowed, mask_kind, ns, s); break;
+    default: err = fa_fwd_detail::dispatch_d192(a, dv, cz, windowed, mask_kind, ns, s); break;
+  }
   return err == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
@@ -1072,7 +218,7 @@ extern "C" int fa_train_fwd(const void* q, const void* k, const void* v, const f
                             float scale, int causal, void* O, float* L, void* stream) {
   const int64_t head = (int64_t)ql * kl;
   return train_fwd(q, k, v, mask, FA_MASK_F32, head * n_heads, head, batch, n_heads, n_kv_heads,
-                   ql, kl, head_dim, scale, causal, -1, O, L, stream);
+                   ql, kl, head_dim, head_dim, scale, causal, -1, O, L, stream);
 }
 
 extern "C" int fa_train_fwd_swa(const void* q, const void* k, const void* v, const float* mask,
@@ -1082,7 +228,7 @@ extern "C" int fa_train_fwd_swa(const void* q, const void* k, const void* v, con
   if (window < 0) return FA_ERR_WINDOW;
   const int64_t head = (int64_t)ql * kl;
   return train_fwd(q, k, v, mask, FA_MASK_F32, head * n_heads, head, batch, n_heads, n_kv_heads,
-                   ql, kl, head_dim, scale, 1, window, O, L, stream);
+                   ql, kl, head_dim, head_dim, scale, 1, window, O, L, stream);
 }
 
 extern "C" unsigned long fa_train_fwd_split_workspace(int batch, int n_heads, int ql, int head_dim,
@@ -1098,7 +244,7 @@ extern "C" int fa_train_fwd_split(const void* q, const void* k, const void* v, i
                                   unsigned long workspace_bytes, void* O, float* L, void* stream) {
   if (n_split < 1 || n_split > kMaxSplit) return FA_ERR_SPLIT;
   return train_fwd(q, k, v, nullptr, FA_MASK_F32, 0, 0, batch, n_heads, n_kv_heads, ql, kl,
-                   head_dim, scale, causal, -1, O, L, stream, n_split, workspace,
+                   head_dim, head_dim, scale, causal, -1, O, L, stream, n_split, workspace,
                    workspace_bytes);
 }
 
@@ -1110,7 +256,7 @@ extern "C" int fa_paged_fwd(const void* q, const void* k_cache, const void* v_ca
   if (batch < 0 || ql < 0 || n_heads < 1 || n_kv_heads < 1 || max_blocks < 0 || n_blocks < 0)
     return FA_ERR_BAD_SIZE;
   if (n_heads % n_kv_heads != 0) return FA_ERR_HEAD_GROUPING;
-  if (head_dim != 64 && head_dim != 128 && head_dim != 256) return FA_ERR_HEAD_DIM;
+  if (!base_dim(head_dim)) return FA_ERR_HEAD_DIM;
   if (!isfinite(scale)) return FA_ERR_SCALE;
   if (block_size < 16 || block_size % 16 != 0) return FA_ERR_PAGED;
   if (n_split < 0 || n_split > kMaxSplit) return FA_ERR_SPLIT;
@@ -1131,9 +277,7 @@ extern "C" int fa_paged_fwd(const void* q, const void* k_cache, const void* v_ca
     H = n_kv_heads;
     cz = 0;
   }
-  const int bm = head_dim == 64    ? block_m<64>()
-                 : head_dim == 128 ? block_m<128>()
-                                   : block_m<256>();
+  const int bm = block_m_of(head_dim, head_dim);
   const int64_t n_qtiles = ((int64_t)qlen + bm - 1) / bm;
   const int64_t grid = n_qtiles * batch * H;
   if (grid > 0x7fffffffLL || (int64_t)batch * H > 0x7fffffffLL ||
@@ -1189,18 +333,20 @@ extern "C" int fa_train_fwd_ex(const void* q, const void* k, const void* v, cons
                                int head_dim, float scale, int causal, int window, void* O,
                                float* L, void* stream) {
   return train_fwd(q, k, v, mask, mask_dtype, mask_stride_b, mask_stride_h, batch, n_heads,
-                   n_kv_heads, ql, kl, head_dim, scale, causal, window < 0 ? -1 : window, O, L,
-                   stream);
+                   n_kv_heads, ql, kl, head_dim, head_dim, scale, causal, window < 0 ? -1 : window,
+                   O, L, stream);
 }
 
-extern "C" int fa_train_fwd_strided(const void* q, const long long* q_strides, const void* k,
-                                    const long long* k_strides, const void* v,
-                                    const long long* v_strides, const void* mask, int mask_dtype,
-                                    const long long* mask_strides, int batch, int n_heads,
-                                    int n_kv_heads, int ql, int kl, int head_dim, float scale,
-                                    int causal, int window, int n_split, void* workspace,
-                                    unsigned long workspace_bytes, void* O,
-                                    const long long* o_strides, float* L, void* stream) {
+namespace {
+
+// The strided entry points: given or contiguous strides of Q, K, V, O and the mask.
+int train_fwd_views(const void* q, const long long* q_strides, const void* k,
+                    const long long* k_strides, const void* v, const long long* v_strides,
+                    const void* mask, int mask_dtype, const long long* mask_strides, int batch,
+                    int n_heads, int n_kv_heads, int ql, int kl, int head_dim, int head_dim_v,
+                    float scale, int causal, int window, int n_split, void* workspace,
+                    unsigned long workspace_bytes, void* O, const long long* o_strides, float* L,
+                    void* stream) {
   if (n_split < 0 || n_split > kMaxSplit) return FA_ERR_SPLIT;
   if (n_split > 0 && window >= 0) return FA_ERR_WINDOW;
   if (n_split > 0 && mask) return FA_ERR_MASK;  // split-KV takes no mask
@@ -1210,17 +356,47 @@ extern "C" int fa_train_fwd_strided(const void* q, const long long* q_strides, c
                            mask_strides ? mask_strides[2] : kl};
   if (mask && (ms[2] < 0 || ms[2] > 0x7fffffffLL)) return FA_ERR_MASK;
   const long long* given[4] = {q_strides, k_strides, v_strides, o_strides};
+  const int dv = head_dim_v;
   const long long hq = (long long)ql * head_dim, hk = (long long)kl * head_dim;
+  const long long hv = (long long)kl * dv, ho = (long long)ql * dv;
   const long long dflt[4][3] = {{hq * n_heads, hq, head_dim},
                                 {hk * n_kv_heads, hk, head_dim},
-                                {hk * n_kv_heads, hk, head_dim},
-                                {hq * n_heads, hq, head_dim}};
+                                {hv * n_kv_heads, hv, dv},
+                                {ho * n_heads, ho, dv}};
   int64_t st[12];
   for (int t = 0; t < 4; ++t)
     for (int i = 0; i < 3; ++i) st[3 * t + i] = given[t] ? given[t][i] : dflt[t][i];
   return train_fwd(q, k, v, mask, mask_dtype, ms[0], ms[1], batch, n_heads, n_kv_heads, ql, kl,
-                   head_dim, scale, causal, window, O, L, stream, n_split, workspace,
+                   head_dim, dv, scale, causal, window, O, L, stream, n_split, workspace,
                    workspace_bytes, st, ms[2]);
+}
+
+}  // namespace
+
+extern "C" int fa_train_fwd_strided(const void* q, const long long* q_strides, const void* k,
+                                    const long long* k_strides, const void* v,
+                                    const long long* v_strides, const void* mask, int mask_dtype,
+                                    const long long* mask_strides, int batch, int n_heads,
+                                    int n_kv_heads, int ql, int kl, int head_dim, float scale,
+                                    int causal, int window, int n_split, void* workspace,
+                                    unsigned long workspace_bytes, void* O,
+                                    const long long* o_strides, float* L, void* stream) {
+  return train_fwd_views(q, q_strides, k, k_strides, v, v_strides, mask, mask_dtype,
+                         mask_strides, batch, n_heads, n_kv_heads, ql, kl, head_dim, head_dim,
+                         scale, causal, window, n_split, workspace, workspace_bytes, O, o_strides,
+                         L, stream);
+}
+
+extern "C" int fa_train_fwd_dv(const void* q, const long long* q_strides, const void* k,
+                               const long long* k_strides, const void* v,
+                               const long long* v_strides, const void* mask, int mask_dtype,
+                               const long long* mask_strides, int batch, int n_heads,
+                               int n_kv_heads, int ql, int kl, int head_dim, int head_dim_v,
+                               float scale, int causal, int window, void* O,
+                               const long long* o_strides, float* L, void* stream) {
+  return train_fwd_views(q, q_strides, k, k_strides, v, v_strides, mask, mask_dtype,
+                         mask_strides, batch, n_heads, n_kv_heads, ql, kl, head_dim, head_dim_v,
+                         scale, causal, window, 0, nullptr, 0, O, o_strides, L, stream);
 }
 
 // The library-held scratch of fa_train_fwd_split_noalloc (split-KV partials
@@ -1261,7 +437,7 @@ extern "C" int fa_train_fwd_split_noalloc(const void* q, const void* k, const vo
                                           void* O, float* L, void* stream) {
   if (n_split < 1 || n_split > kMaxSplit) return FA_ERR_SPLIT;
   if (batch < 0 || ql < 0 || kl < 0 || n_heads < 1 || n_kv_heads < 1) return FA_ERR_BAD_SIZE;
-  if (head_dim != 64 && head_dim != 128 && head_dim != 256) return FA_ERR_HEAD_DIM;
+  if (!base_dim(head_dim)) return FA_ERR_HEAD_DIM;
   const int64_t rows = (int64_t)batch * n_heads * ql;
   void* ws = nullptr;
   if (rows > 0 && kl > 0) {
@@ -1275,7 +451,7 @@ extern "C" int fa_train_fwd_split_noalloc(const void* q, const void* k, const vo
     if (!ws) return FA_ERR_SCRATCH;
   }
   return train_fwd(q, k, v, nullptr, FA_MASK_F32, 0, 0, batch, n_heads, n_kv_heads, ql, kl,
-                   head_dim, scale, causal, -1, O, L, stream, n_split, ws,
+                   head_dim, head_dim, scale, causal, -1, O, L, stream, n_split, ws,
                    (size_t)FA_NOALLOC_SCRATCH_BYTES);
 }
 
@@ -1285,7 +461,9 @@ extern "C" const char* fa_status_string(int status) {
     case FA_ERR_NULL_POINTER: return "a required pointer is NULL";
     case FA_ERR_BAD_SIZE: return "invalid size (batch, ql, kl < 0 or head counts < 1)";
     case FA_ERR_HEAD_GROUPING: return "n_heads is not a multiple of n_kv_heads";
-    case FA_ERR_HEAD_DIM: return "head_dim must be 64, 128 or 256";
+    case FA_ERR_HEAD_DIM:
+      return "unsupported head dims: 64, 128 or 256 everywhere; the forward also takes 80, 96, "
+             "192 and (key, value) pairs (96, 64) and (192, 128), without split-KV";
     case FA_ERR_SCALE: return "scale must be finite";
     case FA_ERR_ALIGNMENT:
       return "misaligned tensor (q, k, v, O need 16 bytes; L and an f32 mask 4, a bf16 mask 2)";

@@ -36,7 +36,10 @@ enum fa_status {
     FA_ERR_NULL_POINTER = 1,   /* q, k, v, O or L is NULL while its tensor is non-empty */
     FA_ERR_BAD_SIZE = 2,       /* batch, ql or kl < 0; n_heads or n_kv_heads < 1      */
     FA_ERR_HEAD_GROUPING = 3,  /* n_heads is not a multiple of n_kv_heads              */
-    FA_ERR_HEAD_DIM = 4,       /* head_dim is not 64, 128 or 256                       */
+    FA_ERR_HEAD_DIM = 4,       /* head dims not supported by the entry point: 64, 128
+                                  and 256 everywhere; the unsplit forward entry points
+                                  also take 80, 96 and 192, and fa_train_fwd_dv the
+                                  (key, value) pairs (96, 64) and (192, 128)          */
     FA_ERR_SCALE = 5,          /* scale is NaN or infinite                              */
     FA_ERR_ALIGNMENT = 6,      /* q, k, v or O not 16-byte aligned; mask or L not 4-byte */
     FA_ERR_TOO_LARGE = 7,      /* a grid or index would overflow the kernel's limits    */
@@ -78,7 +81,10 @@ enum fa_mask_dtype {
  *         and NaN are outside the contract.
  *   batch, n_heads, n_kv_heads, ql, kl, head_dim: sizes; n_heads must be a
  *         multiple of n_kv_heads (query head h reads kv head h / (n_heads /
- *         n_kv_heads)); head_dim is 64, 128 or 256.
+ *         n_kv_heads)); head_dim is 64, 80, 96, 128, 192 or 256 (the widths
+ *         of the adjacent SDPA page, "nuvec-core 0.3.0", tests/fast.rs,
+ *         attention_kernels_match_the_fallback, and the method's own 64 and
+ *         256; 80 computes its last 16 dims with a 16-deep MFMA step).
  *   scale finite softmax scale (usually 1/sqrt(head_dim)); negative allowed.
  *   causal nonzero: key j hidden from query row i when j > max(kl - ql, 0) + i.
  *   O     bf16 bits [batch, n_heads, ql, head_dim] (device, written; no
@@ -190,7 +196,8 @@ int fa_train_fwd_ex(const void *q, const void *k, const void *v, const void *mas
  *   L           f32 [batch, n_heads, ql], contiguous, as for fa_train_fwd.
  *   window      as for fa_train_fwd_ex (< 0: none; >= 0 needs causal).
  *   n_split     0: one launch; >= 1: split-KV with workspace, as for
- *               fa_train_fwd_split (no mask: FA_ERR_MASK).
+ *               fa_train_fwd_split (no mask: FA_ERR_MASK; head_dim 64, 128 or
+ *               256: FA_ERR_HEAD_DIM).
  *   others      as for fa_train_fwd.
  *
  * With all strides NULL this is fa_train_fwd_ex (or fa_train_fwd_split with
@@ -203,6 +210,36 @@ int fa_train_fwd_strided(const void *q, const long long *q_strides, const void *
                          float scale, int causal, int window, int n_split, void *workspace,
                          unsigned long workspace_bytes, void *O, const long long *o_strides,
                          float *L, void *stream);
+
+/*
+ * fa_train_fwd_dv - fa_train_fwd_strided (without split-KV) for a value head
+ * dim that may differ from the key head dim, as in the (D, Dv) shapes of the
+ * adjacent SDPA page ("nuvec-core 0.3.0", tests/fast.rs,
+ * attention_kernels_match_the_fallback: (96, 64) and (192, 128)). The
+ * scores use the key width, the weighted sum the value width:
+ *
+ *     s_j = scale * <q[b,h,i,:head_dim], k[b,g,j,:head_dim]> + mask[b,h,i,j]
+ *     O[b,h,i,:head_dim_v] = sum_j exp(s_j - L[b,h,i]) * v[b,g,j,:head_dim_v]
+ *
+ *   q    bf16 bits [batch, n_heads,    ql, head_dim]    (strided as q_strides)
+ *   k    bf16 bits [batch, n_kv_heads, kl, head_dim]    (strided as k_strides)
+ *   v    bf16 bits [batch, n_kv_heads, kl, head_dim_v]  (strided as v_strides)
+ *   O    bf16 bits [batch, n_heads,    ql, head_dim_v]  (strided as o_strides)
+ *   (head_dim, head_dim_v)
+ *        (64, 64), (80, 80), (96, 96), (96, 64), (128, 128), (192, 192),
+ *        (192, 128) or (256, 256); FA_ERR_HEAD_DIM otherwise. NULL strides:
+ *        that tensor contiguous in its own head dim.
+ *   others as for fa_train_fwd_strided (mask, window, L, stream, errors).
+ *
+ * With head_dim_v == head_dim this is fa_train_fwd_strided with n_split = 0,
+ * bit for bit. One kernel launch; allocates nothing; never synchronises.
+ */
+int fa_train_fwd_dv(const void *q, const long long *q_strides, const void *k,
+                    const long long *k_strides, const void *v, const long long *v_strides,
+                    const void *mask, int mask_dtype, const long long *mask_strides, int batch,
+                    int n_heads, int n_kv_heads, int ql, int kl, int head_dim, int head_dim_v,
+                    float scale, int causal, int window, void *O, const long long *o_strides,
+                    float *L, void *stream);
 
 /*
  * fa_train_fwd_split - the forward of fa_train_fwd (no mask, causal or not)
@@ -238,7 +275,8 @@ int fa_train_fwd_strided(const void *q, const long long *q_strides, const void *
  *              overwritten. Calls that share a workspace must not overlap.
  *   others     as for fa_train_fwd.
  *
- * Returns FA_ERR_SPLIT for n_split outside 1..65536 or a workspace too small,
+ * head_dim is 64, 128 or 256 (FA_ERR_HEAD_DIM otherwise). Returns
+ * FA_ERR_SPLIT for n_split outside 1..65536 or a workspace too small,
  * otherwise the statuses of fa_train_fwd. kl == 0 needs no workspace.
  * Two kernel launches; allocates nothing; never synchronises.
  */
@@ -308,6 +346,7 @@ int fa_train_fwd_split_noalloc(const void *q, const void *k, const void *v, int 
  *               fa_train_fwd_split, chunks of max_blocks*block_size keys;
  *               workspace size from fa_train_fwd_split_workspace)
  *   O, L        as for fa_train_fwd (a sequence with no key: O = 0, L = -inf)
+ *   head_dim    64, 128 or 256 (FA_ERR_HEAD_DIM otherwise)
  *   others      as for fa_train_fwd; no mask, no window.
  *
  * Every tile runs the compensated P.V product. Returns FA_ERR_PAGED for a bad
@@ -336,7 +375,8 @@ int fa_paged_fwd(const void *q, const void *k_cache, const void *v_cache, const 
  *                                  kv head's group)
  *
  *   q, k, v, mask, batch .. causal: as for fa_train_fwd (same meaning, same
- *         layouts and constraints).
+ *         layouts and constraints), with head_dim 64, 128 or 256
+ *         (FA_ERR_HEAD_DIM otherwise).
  *   O     bf16 bits [batch, n_heads, ql, head_dim]: the forward's output (read).
  *   L     f32 [batch, n_heads, ql]: the forward's logsumexp (read); -inf rows
  *         (no visible key) give zero gradients.

@@ -31,7 +31,7 @@ def test_header_declares_the_entry_points():
     assert {"fa_train_fwd", "fa_train_fwd_swa", "fa_train_fwd_ex", "fa_train_fwd_split",
             "fa_train_fwd_split_workspace", "fa_paged_fwd", "fa_train_bwd", "fa_train_bwd_swa",
             "fa_train_bwd_ex", "fa_train_fwd_strided", "fa_train_bwd_strided",
-            "fa_status_string"} <= names
+            "fa_train_fwd_dv", "fa_status_string"} <= names
 
 
 def test_library_exports_every_declared_symbol():
@@ -66,8 +66,8 @@ def _call(**over):
 @pytest.mark.parametrize("over,code", [
     (dict(q=0), 1), (dict(k=0), 1), (dict(v=0), 1), (dict(O=0), 1), (dict(L=0), 1),
     (dict(batch=-1), 2), (dict(ql=-1), 2), (dict(kl=-3), 2), (dict(n_heads=0), 2),
-    (dict(n_kv_heads=0), 2), (dict(n_heads=3, n_kv_heads=2), 3), (dict(head_dim=96), 4),
-    (dict(head_dim=0), 4), (dict(scale=math.nan), 5), (dict(scale=math.inf), 5),
+    (dict(n_kv_heads=0), 2), (dict(n_heads=3, n_kv_heads=2), 3), (dict(head_dim=72), 4),
+    (dict(head_dim=0), 4), (dict(head_dim=112), 4), (dict(scale=math.nan), 5), (dict(scale=math.inf), 5),
     (dict(scale=-math.inf), 5), (dict(q=A + 2), 6), (dict(k=A + 8), 6), (dict(O=A + 4), 6),
     (dict(mask=A + 2), 6), (dict(L=A + 1), 6),
     # (ql = 2: with ql = 1 the GQA heads would be packed into 65536-row heads,
@@ -95,7 +95,7 @@ def _call_swa(**over):
 
 @pytest.mark.parametrize("over,code", [
     (dict(window=-1), 9), (dict(window=-(2 ** 31)), 9), (dict(q=0), 1), (dict(v=0), 1),
-    (dict(L=0), 1), (dict(kl=-1), 2), (dict(n_heads=3, n_kv_heads=2), 3), (dict(head_dim=96), 4),
+    (dict(L=0), 1), (dict(kl=-1), 2), (dict(n_heads=3, n_kv_heads=2), 3), (dict(head_dim=72), 4),
     (dict(scale=math.nan), 5), (dict(k=A + 8), 6), (dict(mask=A + 2), 6),
     (dict(batch=65536, n_heads=65536, n_kv_heads=1, ql=1), 7),
 ])
@@ -294,7 +294,8 @@ STRIDED_GOOD = dict(q=A, q_strides=None, k=A, k_strides=None, v=A, v_strides=Non
     (dict(q_strides=(-8, 512, 64)), 13), (dict(o_strides=(0, 0, -64)), 13),
     (dict(k_strides=(4096, 64, 12)), 6), (dict(v_strides=(4, 512, 64)), 6),
     (dict(k_strides=(0, 0, 1 << 25)), 7), (dict(n_split=2, window=3), 9),
-    (dict(causal=0, window=3), 9), (dict(n_split=-1), 11), (dict(head_dim=96), 4),
+    (dict(causal=0, window=3), 9), (dict(n_split=-1), 11), (dict(head_dim=72), 4),
+    (dict(n_split=2, head_dim=80, workspace=A, workspace_bytes=1 << 20), 4),
     (dict(q=0), 1), (dict(n_split=2), 1), (dict(mask=A, mask_strides=(0, 0, -8)), 10),
     (dict(mask=A, mask_strides=(-1, 0, 8)), 10), (dict(mask=A, n_split=2, workspace=A,
                                                        workspace_bytes=1 << 20), 10),
@@ -304,6 +305,44 @@ def test_strided_invalid_arguments_are_rejected(over, code):
     args = dict(STRIDED_GOOD)
     args.update(over)
     assert fa.fa_train_fwd_strided(**args) == code
+
+
+DV_GOOD = {k: v for k, v in STRIDED_GOOD.items() if k not in ("n_split", "workspace",
+                                                               "workspace_bytes")}
+DV_GOOD.update(head_dim=96, head_dim_v=64)
+
+
+@pytest.mark.parametrize("over,code", [
+    # (key, value) head dims without kernels
+    (dict(head_dim=64, head_dim_v=128), 4), (dict(head_dim=96, head_dim_v=80), 4),
+    (dict(head_dim=80, head_dim_v=64), 4), (dict(head_dim=72, head_dim_v=72), 4),
+    (dict(head_dim=192, head_dim_v=64), 4), (dict(head_dim=128, head_dim_v=0), 4),
+    (dict(q=0), 1), (dict(v=0), 1), (dict(L=0), 1), (dict(kl=-1), 2),
+    (dict(n_heads=3, n_kv_heads=2), 3), (dict(scale=math.nan), 5), (dict(v=A + 8), 6),
+    (dict(v_strides=(4096, 64, 12)), 6), (dict(o_strides=(0, 0, -64)), 13),
+    (dict(causal=0, window=3), 9), (dict(mask=A, mask_dtype=5), 10),
+    # O's rows (64 elements) overlap at a row stride of 32
+    (dict(o_strides=(4 * 8 * 32, 8 * 32, 32)), 13),
+])
+def test_dv_invalid_arguments_are_rejected(over, code):
+    args = dict(DV_GOOD)
+    args.update(over)
+    assert fa.fa_train_fwd_dv(**args) == code
+
+
+@pytest.mark.parametrize("over", [dict(batch=0), dict(ql=0, q=0, k=0, v=0, O=0, L=0)])
+def test_dv_empty_problems_are_noops(over):
+    args = dict(DV_GOOD)
+    args.update(over)
+    assert fa.fa_train_fwd_dv(**args) == 0
+
+
+def test_base_dims_only_where_stated():
+    # split-KV, paged, no-alloc and backward keep to 64, 128 and 256
+    sp = dict(SPLIT_GOOD, head_dim=80)
+    assert fa.fa_train_fwd_split(**sp) == 4
+    assert fa.fa_train_fwd_split(**dict(SPLIT_GOOD, head_dim=192)) == 4
+    assert "80, 96" in fa.status_string(4)
 
 
 def test_strided_status_string():

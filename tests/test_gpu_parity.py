@@ -192,7 +192,7 @@ def test_errors_raise_from_binding():
     with pytest.raises(fa.FAError) as e:
         fa.train_fwd(q, k, k)
     assert e.value.status == 3
-    q96 = torch.zeros(1, 1, 4, 96, device="cuda:0", dtype=torch.bfloat16)
+    q96 = torch.zeros(1, 1, 4, 72, device="cuda:0", dtype=torch.bfloat16)
     with pytest.raises(fa.FAError):
         fa.train_fwd(q96, q96, q96)
     with pytest.raises(fa.FAError):

@@ -24,10 +24,15 @@ def isa(tmp_path_factory):
     from flash_attention_forward_fa_amd import build
     flags = [f for f in build.FLAGS if f not in ("-fPIC", "-shared")]
     text = ""
-    for src in build.SOURCES:
+    outs, procs = [], []
+    for src in build.SOURCES:  # (compiled in parallel)
         out = tmp_path_factory.mktemp("isa") / (os.path.basename(src) + ".s")
-        subprocess.run([build.HIPCC, *flags, "--cuda-device-only", "-S", "-o", str(out), src],
-                       check=True, capture_output=True)
+        outs.append(out)
+        procs.append(subprocess.Popen([build.HIPCC, *flags, "--cuda-device-only", "-S", "-o",
+                                       str(out), src], stdout=subprocess.DEVNULL,
+                                      stderr=subprocess.DEVNULL))
+    assert all(p.wait() == 0 for p in procs), "hipcc failed"
+    for out in outs:
         text += out.read_text() + "\n"
     kernels = {}
     name = None
@@ -45,8 +50,10 @@ def test_all_variants_present(isa):
     fwd = [n for n in isa if "fa_fwd_kernel" in n]
     bwd = [n for n in isa if "fa_bwd_kernel" in n]
     # head_dim (64, 128, 256) x {none, causal, window} x {mixed, compensated f32 mask, bf16 mask}
-    assert len(fwd) == 66  # + split-KV, paged (whole-tile and short blocks), paged split-KV
-    #                       (head_dim x causal each), bool masks
+    # + split-KV, paged (whole-tile and short blocks), paged split-KV (head_dim x causal
+    # each), bool masks: 66; the (key, value) pairs (80, 80), (96, 96), (96, 64),
+    # (192, 192), (192, 128) x {none, causal, window} x {mixed, three mask kinds}: 60
+    assert len(fwd) == 126
     assert len(bwd) == 72  # head_dim (3) x {dQ, dKV} x {none, causal, window} x mask (4 kinds)
 
 
@@ -57,6 +64,10 @@ _CLOSE = (re.compile(r"^s_or_b64 exec, exec, (s\[\d+:\d+\])"),
 # s_xor_b64 sY, exec, sX with sX a saved EXEC: sY holds the lanes the region
 # left out, and the region is closed by OR-ing them back from sY
 _RENAME = re.compile(r"^s_xor_b64 (s\[\d+:\d+\]), exec, (s\[\d+:\d+\])")
+# s_or_saveexec_b64 sY, sX with sX the lanes an if left out (the else of an
+# if/else): EXEC becomes the region's lanes again, sY saves the then-lanes and
+# the region goes on (the else) until EXEC is OR-ed back from sY
+_ELSE = re.compile(r"^s_or_saveexec_b64 (s\[\d+:\d+\]), (s\[\d+:\d+\])")
 
 
 def mfma_under_exec_mask(lines):
@@ -103,7 +114,7 @@ def mfma_under_exec_mask(lines):
         for entry in list(states[i]):
             stack = list(entry)
             for t in blocks[i][1]:
-                rn = _RENAME.search(t)
+                rn = _RENAME.search(t) or _ELSE.search(t)
                 if rn and rn.group(2) in stack:
                     stack[stack.index(rn.group(2))] = rn.group(1)
                     continue
@@ -147,6 +158,13 @@ def test_exec_check_finds_masked_mfma():
               "s_or_b64 exec, exec, s[2:3]"]
     assert not mfma_under_exec_mask(ifelse + [mf])
     assert mfma_under_exec_mask(ifelse[:4] + [mf] + ifelse[4:])
+    # the full if/else with the else entered through s_or_saveexec into another
+    # register: closed by OR-ing that register back; an MFMA in the else is masked
+    full = ["s_and_saveexec_b64 s[8:9], vcc", "s_xor_b64 s[8:9], exec, s[8:9]",
+            "v_mov_b32 v1, 0", "s_or_saveexec_b64 s[48:49], s[8:9]",
+            "s_xor_b64 exec, exec, s[48:49]", "v_mov_b32 v2, 0", "s_or_b64 exec, exec, s[48:49]"]
+    assert not mfma_under_exec_mask(full + [mf])
+    assert mfma_under_exec_mask(full[:6] + [mf] + full[6:])
 
 
 def test_no_mfma_under_exec_mask(isa):
