@@ -205,7 +205,8 @@ __device__ __forceinline__ void copy_offsets(int tid, int (&off)[CopyShape<W, BN
   }
 }
 
-template <int W, int BN, int NT, bool IS_K>
+// (BRANCH: keep the partial-tile path a branch, below)
+template <int W, int BN, int NT, bool IS_K, bool BRANCH = false>
 __device__ __forceinline__ void issue_tile(const uint16_t* src, int kbase, int kl, uint16_t* lds,
                                            int tid, int wave_base,
                                            const int (&off)[CopyShape<W, BN, NT>::ROUNDS],
@@ -222,6 +223,11 @@ __device__ __forceinline__ void issue_tile(const uint16_t* src, int kbase, int k
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             rsrc, (lds_void*)(lds + (u * NT + wave_base) * 8), 16, off[u], 0, 0, 0);
   } else {
+    // (with BRANCH, an empty volatile asm keeps this rare path a branch:
+    // speculated into the full-tile path as selects, its vector arithmetic
+    // would run for every tile; the forward kernel takes it, the backward's
+    // streaming loops have no registers to spare for it)
+    if constexpr (BRANCH) asm volatile("");
 #pragma unroll
     for (int u = 0; u < ROUNDS; ++u) {
       if ((u + 1) * NT <= SLOTS || u * NT + wave_base < SLOTS) {
@@ -234,6 +240,14 @@ __device__ __forceinline__ void issue_tile(const uint16_t* src, int kbase, int k
       }
     }
   }
+}
+
+// A read of read-only int data at a wave-uniform index through the scalar
+// cache (s_load): the constant address space tells the compiler the data is
+// not written while the kernel runs. (A vector load here would have to wait,
+// in order, behind every tile copy in flight.)
+__device__ __forceinline__ int load_uniform(const int* p, int64_t i) {
+  return ((const __attribute__((address_space(4))) int*)(uintptr_t)p)[i];
 }
 
 // The same copy from a block-paged cache whose blocks may be shorter than a
@@ -260,7 +274,7 @@ __device__ __forceinline__ void issue_tile_blocks(const uint16_t* cache, const i
     const int row0 = __builtin_amdgcn_readfirstlane((u * NT + wave_base) / CH);
     const int base_row = min(row0, rows - 1);
     const int pos = kbase + base_row;
-    int blk = __builtin_amdgcn_readfirstlane(table_row[pos / block_size]);
+    int blk = load_uniform(table_row, pos / block_size);
     blk = min(max(blk, 0), n_blocks - 1);
     const uint16_t* src =
         cache + (((int64_t)blk * n_kv_heads + g) * block_size + pos % block_size) * W;
@@ -327,6 +341,11 @@ template <int P> __device__ __forceinline__ void set_prio() {
 __device__ __forceinline__ void wait_vmem() {
   // vmcnt(0); expcnt and lgkmcnt left at their maxima
   __builtin_amdgcn_s_waitcnt(0x0F70);
+}
+// vmcnt(N) (at most N vector memory loads of this wave still outstanding)
+template <int N> __device__ __forceinline__ void wait_vmem_n() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
 }
 
 }  // namespace

@@ -180,9 +180,11 @@ constexpr int kMixed = 0, kAll = 1, kSplit = 2, kPaged = 3, kPagedSplit = 4, kPa
 // redo set are computed and written (waves without such a row only take part
 // in the tile copies).
 template <int DK, int DV, bool CAUSAL, bool WINDOW, int MASK, bool PRECISE, bool REDO,
-          bool SPLIT = false, bool PAGED = false, bool SMALL_BLOCKS = false>
+          bool SPLIT = false, bool PAGED = false, bool SMALL_BLOCKS = false, int QBX = 0>
 __device__ __forceinline__ bool fwd_tile(const FwdArgs& a, int qtile, int bh, uint16_t* k0s,
                                          uint16_t* v0s, uint16_t* k1s, uint16_t* v1s,
+                                         uint16_t* k2s, uint16_t* v2s, uint16_t* k3s,
+                                         uint16_t* v3s,
                                          bool (&redo)[Cfg<DK, DV>::QB], int* wg_flags,
                                          int split = 0) {
   constexpr bool HAS_MASK = MASK != kNoMask;
@@ -196,9 +198,13 @@ __device__ __forceinline__ bool fwd_tile(const FwdArgs& a, int qtile, int bh, ui
   static_assert((!SPLIT && !PAGED) || (DK == DV && !kPanels<DK>),
                 "split-KV and paged: head dims 64, 128 and 256");
   constexpr int BN = Cfg<DK, DV>::BN;
-  constexpr int kQB = Cfg<DK, DV>::QB;
+  // (QBX: query blocks per wave other than the pair's, for the narrow
+  // split-KV kernels of at most 16 query rows: one block, half the work of
+  // the one wave that has rows)
+  constexpr int kQB = QBX ? QBX : Cfg<DK, DV>::QB;
+  static_assert(kQB <= Cfg<DK, DV>::QB, "redo flags for at most the pair's blocks");
   constexpr int kRowsPerWave = 16 * kQB;
-  constexpr int kBlockM = block_m<DK, DV>();
+  constexpr int kBlockM = Cfg<DK, DV>::W * kRowsPerWave;
   constexpr int NKB = BN / 16;   // 16-key blocks per tile
   constexpr int NKC = BN / 32;   // 32-key chunks per tile (P.V contraction steps)
   constexpr int NDB = DV / 16;   // 16-dim blocks of O
@@ -277,34 +283,45 @@ __device__ __forceinline__ bool fwd_tile(const FwdArgs& a, int qtile, int bh, ui
   const int* table_row = PAGED ? a.block_table + (int64_t)b * a.max_blocks : nullptr;
   auto paged_src = [&](const uint16_t* cache, int kt) {
     const int pos = kt * BN;
-    int blk = __builtin_amdgcn_readfirstlane(
-        a.block_table[(int64_t)b * a.max_blocks + pos / a.block_size]);
+    int blk = load_uniform(a.block_table, (int64_t)b * a.max_blocks + pos / a.block_size);
     blk = min(max(blk, 0), a.n_blocks - 1);
     return cache + (((int64_t)blk * a.Hkv + g) * a.block_size + pos % a.block_size) * DK;
   };
   auto issue_k = [&](int kt, uint16_t* dst) {
     if constexpr (PAGED) {
       if constexpr (!SMALL_BLOCKS)
-        issue_tile<DK, BN, NT, true>(paged_src(a.k, kt), 0, min(BN, kl - kt * BN), dst, tid,
+        issue_tile<DK, BN, NT, true, true>(paged_src(a.k, kt), 0, min(BN, kl - kt * BN), dst, tid,
                                      64 * wave, koff);
       else
         issue_tile_blocks<DK, BN, NT, true>(a.k, table_row, a.n_blocks, a.Hkv, g, a.block_size,
                                             kt * BN, kl, dst, tid, 64 * wave);
     } else
-      issue_tile<DK, BN, NT, true>(kp, kt * BN, kl, dst, tid, 64 * wave, koff, k_rs);
+      issue_tile<DK, BN, NT, true, true>(kp, kt * BN, kl, dst, tid, 64 * wave, koff, k_rs);
   };
   auto issue_v = [&](int kt, uint16_t* dst) {
     if constexpr (PAGED) {
       if constexpr (!SMALL_BLOCKS)
-        issue_tile<DV, BN, NT, false>(paged_src(a.v, kt), 0, min(BN, kl - kt * BN), dst, tid,
+        issue_tile<DV, BN, NT, false, true>(paged_src(a.v, kt), 0, min(BN, kl - kt * BN), dst, tid,
                                       64 * wave, voff);
       else
         issue_tile_blocks<DV, BN, NT, false>(a.v, table_row, a.n_blocks, a.Hkv, g, a.block_size,
                                              kt * BN, kl, dst, tid, 64 * wave);
     } else
-      issue_tile<DV, BN, NT, false>(vp, kt * BN, kl, dst, tid, 64 * wave, voff, v_rs);
+      issue_tile<DV, BN, NT, false, true>(vp, kt * BN, kl, dst, tid, 64 * wave, voff, v_rs);
   };
-  if (n_kt > kt_first) issue_k(kt_first, (kt_first & 1) ? k1s : k0s);
+  // Split-KV and paged tiles of up to 128 dims run a four-stage copy pipeline
+  // (tile kt in buffer kt % 4, three tiles in flight while one is computed):
+  // their workgroups are few per CU and short, and with one tile in flight
+  // the copies' latency, not HBM, set their pace.
+  constexpr int NSTAGE = (SPLIT || PAGED) && DK <= 128 ? 4 : 2;
+  uint16_t* const kst[4] = {k0s, k1s, k2s, k3s};
+  uint16_t* const vst[4] = {v0s, v1s, v2s, v3s};
+  if constexpr (NSTAGE == 4) {
+    for (int i = 0; i < 3; ++i)
+      if (kt_first + i < n_kt) issue_k(kt_first + i, kst[(kt_first + i) & 3]);
+  } else {
+    if (n_kt > kt_first) issue_k(kt_first, (kt_first & 1) ? k1s : k0s);
+  }
 
   // ---- Q^T as the B operand: block qb, step s: row qw0+16qb+c16, dims 32s+8grp.. ----
   // (and in a 16-dim tail step: dims 32 NDS + 4grp ..)
@@ -681,8 +698,56 @@ __device__ __forceinline__ bool fwd_tile(const FwdArgs& a, int qtile, int bh, ui
       set_prio<0>();
     }
   };
-  if (n_kt > kt_first) issue_v(kt_first, (kt_first & 1) ? v1s : v0s);
-  if constexpr (PAIRED) {
+  if constexpr (NSTAGE == 4) {
+    for (int i = 0; i < 3; ++i)
+      if (kt_first + i < n_kt) issue_v(kt_first + i, vst[(kt_first + i) & 3]);
+  } else {
+    if (n_kt > kt_first) issue_v(kt_first, (kt_first & 1) ? v1s : v0s);
+  }
+  if constexpr (NSTAGE == 4) {
+    // copy instructions per thread per tile (K and V)
+    constexpr int R = CopyShape<DK, BN, NT>::ROUNDS + CopyShape<DV, BN, NT>::ROUNDS;
+    auto step4 = [&](int kt, const uint16_t* kc, const uint16_t* vc, uint16_t* kn,
+                     uint16_t* vn) {
+      // this thread's copies of tile kt have landed (the copies of the tiles
+      // after it may still be in flight: the counter drains in order), then
+      // every thread's
+      if (kt + 2 < n_kt)
+        wait_vmem_n<2 * R>();
+      else if (kt + 1 < n_kt)
+        wait_vmem_n<R>();
+      else
+        wait_vmem();
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      if (kt + 3 < n_kt) {
+        issue_k(kt + 3, kn);
+        issue_v(kt + 3, vn);
+      }
+      if (kt >= wave_kt_first && kt < n_kw) {
+        f32x4 s[NKB][kQB];
+        scores(kc, s);
+        if (kt >= mask_from) apply_mask(kt, s);
+        float mx[kQB];
+        if (__any(part_max(s, mx))) {
+          complete_max(mx);
+          rescale(mx, s);
+        }
+        bf16x8 phi[NKC][kQB], plo[NKC][kQB];
+        probs(s, phi, plo);
+        set_prio<2>();
+        pv(vc, phi, plo);
+        set_prio<0>();
+      }
+    };
+    for (int kt = kt_first & ~3; kt < n_kt; kt += 4) {
+      if (kt >= kt_first) step4(kt, k0s, v0s, k3s, v3s);
+      if (kt + 1 >= kt_first && kt + 1 < n_kt) step4(kt + 1, k1s, v1s, k0s, v0s);
+      if (kt + 2 >= kt_first && kt + 2 < n_kt) step4(kt + 2, k2s, v2s, k1s, v1s);
+      if (kt + 3 >= kt_first && kt + 3 < n_kt) step4(kt + 3, k3s, v3s, k2s, v2s);
+    }
+  } else if constexpr (PAIRED) {
     for (int kt = kt_first & ~1; kt < n_kt; kt += 2) {
       if (kt >= kt_first) step(kt, k0s, v0s, k1s, v1s);
       if (kt + 1 < n_kt) step(kt + 1, k1s, v1s, k0s, v0s);
@@ -767,7 +832,7 @@ __device__ __forceinline__ bool fwd_tile(const FwdArgs& a, int qtile, int bh, ui
   return wg_any;
 }
 
-template <int DK, int DV, bool CAUSAL, bool WINDOW, int MASK, int MODE>
+template <int DK, int DV, bool CAUSAL, bool WINDOW, int MASK, int MODE, int QBX = 0>
 __global__ __launch_bounds__((64 * Cfg<DK, DV>::W))
 __attribute__((amdgpu_waves_per_eu(MODE == kMixed ? Cfg<DK, DV>::WPE : 2))) void fa_fwd_kernel(
     FwdArgs a) {
@@ -780,6 +845,12 @@ __attribute__((amdgpu_waves_per_eu(MODE == kMixed ? Cfg<DK, DV>::WPE : 2))) void
   __shared__ __attribute__((aligned(1024))) uint16_t v0s[TILE_V];
   __shared__ __attribute__((aligned(1024))) uint16_t k1s[TILE_K];
   __shared__ __attribute__((aligned(1024))) uint16_t v1s[TILE_V];
+  // (the third and fourth stages of the split-KV and paged pipelines)
+  constexpr int TILE_X = MODE >= kSplit && DK <= 128 ? TILE_K : 8;
+  __shared__ __attribute__((aligned(1024))) uint16_t k2s[TILE_X];
+  __shared__ __attribute__((aligned(1024))) uint16_t v2s[TILE_X];
+  __shared__ __attribute__((aligned(1024))) uint16_t k3s[TILE_X];
+  __shared__ __attribute__((aligned(1024))) uint16_t v3s[TILE_X];
   __shared__ int wg_flags[Cfg<DK, DV>::W];
 
   // ---- work item ----
@@ -808,37 +879,39 @@ __attribute__((amdgpu_waves_per_eu(MODE == kMixed ? Cfg<DK, DV>::WPE : 2))) void
   }
   const int qtile = a.qt_base + a.qt_count - 1 - qt_rev;
   bool redo[Cfg<DK, DV>::QB] = {};
+#define FA_TILE_BUFFERS k0s, v0s, k1s, v1s, k2s, v2s, k3s, v3s
   if constexpr (MODE == kMixed) {
     // the compensated tiles are the lightest, so they run last and fill the tail
     if (qtile < a.n_precise) {
-      fwd_tile<DK, DV, CAUSAL, WINDOW, kNoMask, true, false>(a, qtile, bh, k0s, v0s, k1s, v1s, redo,
-                                                        wg_flags);
-    } else if (fwd_tile<DK, DV, CAUSAL, WINDOW, kNoMask, false, false>(a, qtile, bh, k0s, v0s, k1s, v1s,
-                                                                  redo, wg_flags)) {
+      fwd_tile<DK, DV, CAUSAL, WINDOW, kNoMask, true, false>(a, qtile, bh, FA_TILE_BUFFERS, redo,
+                                                             wg_flags);
+    } else if (fwd_tile<DK, DV, CAUSAL, WINDOW, kNoMask, false, false>(
+                   a, qtile, bh, FA_TILE_BUFFERS, redo, wg_flags)) {
       // (the plain pass's last barrier came after every wave's last LDS read,
       // so the redo's copies may reuse the tile buffers)
-      fwd_tile<DK, DV, CAUSAL, WINDOW, kNoMask, true, true>(a, qtile, bh, k0s, v0s, k1s, v1s, redo,
-                                                       wg_flags);
+      fwd_tile<DK, DV, CAUSAL, WINDOW, kNoMask, true, true>(a, qtile, bh, FA_TILE_BUFFERS, redo,
+                                                            wg_flags);
     }
   } else if constexpr (MODE == kSplit) {
-    fwd_tile<DK, DV, CAUSAL, false, kNoMask, true, false, true>(a, qtile, bh, k0s, v0s, k1s, v1s, redo,
-                                                           wg_flags, split);
+    fwd_tile<DK, DV, CAUSAL, false, kNoMask, true, false, true, false, false, QBX>(
+        a, qtile, bh, FA_TILE_BUFFERS, redo, wg_flags, split);
   } else if constexpr (MODE == kPaged) {
-    fwd_tile<DK, DV, CAUSAL, false, kNoMask, true, false, false, true>(a, qtile, bh, k0s, v0s, k1s,
-                                                                  v1s, redo, wg_flags);
+    fwd_tile<DK, DV, CAUSAL, false, kNoMask, true, false, false, true>(
+        a, qtile, bh, FA_TILE_BUFFERS, redo, wg_flags);
   } else if constexpr (MODE == kPagedSplit) {
-    fwd_tile<DK, DV, CAUSAL, false, kNoMask, true, false, true, true>(a, qtile, bh, k0s, v0s, k1s, v1s,
-                                                                 redo, wg_flags, split);
+    fwd_tile<DK, DV, CAUSAL, false, kNoMask, true, false, true, true, false, QBX>(
+        a, qtile, bh, FA_TILE_BUFFERS, redo, wg_flags, split);
   } else if constexpr (MODE == kPagedBlocks) {
-    fwd_tile<DK, DV, CAUSAL, false, kNoMask, true, false, false, true, true>(a, qtile, bh, k0s, v0s,
-                                                                        k1s, v1s, redo, wg_flags);
+    fwd_tile<DK, DV, CAUSAL, false, kNoMask, true, false, false, true, true>(
+        a, qtile, bh, FA_TILE_BUFFERS, redo, wg_flags);
   } else if constexpr (MODE == kPagedBlocksSplit) {
-    fwd_tile<DK, DV, CAUSAL, false, kNoMask, true, false, true, true, true>(
-        a, qtile, bh, k0s, v0s, k1s, v1s, redo, wg_flags, split);
+    fwd_tile<DK, DV, CAUSAL, false, kNoMask, true, false, true, true, true, QBX>(
+        a, qtile, bh, FA_TILE_BUFFERS, redo, wg_flags, split);
   } else {
-    fwd_tile<DK, DV, CAUSAL, WINDOW, MASK, true, false>(a, qtile, bh, k0s, v0s, k1s, v1s, redo,
-                                                   wg_flags);
+    fwd_tile<DK, DV, CAUSAL, WINDOW, MASK, true, false>(a, qtile, bh, FA_TILE_BUFFERS, redo,
+                                                        wg_flags);
   }
+#undef FA_TILE_BUFFERS
 #endif
 }
 
@@ -888,9 +961,9 @@ __global__ __launch_bounds__(256) void fa_combine_kernel(CombineArgs c) {
   if (lane == 0) c.l[row] = empty ? -INFINITY : m + __builtin_amdgcn_logf(z) * kLn2;
 }
 
-template <int DK, int DV, bool CAUSAL, bool WINDOW, int MASK, int MODE>
+template <int DK, int DV, bool CAUSAL, bool WINDOW, int MASK, int MODE, int QBX = 0>
 hipError_t launch(const FwdArgs& a, unsigned grid, hipStream_t stream) {
-  hipLaunchKernelGGL((fa_fwd_kernel<DK, DV, CAUSAL, WINDOW, MASK, MODE>), dim3(grid),
+  hipLaunchKernelGGL((fa_fwd_kernel<DK, DV, CAUSAL, WINDOW, MASK, MODE, QBX>), dim3(grid),
                      dim3(64 * Cfg<DK, DV>::W), 0, stream, a);
   return hipGetLastError();
 }
@@ -924,8 +997,15 @@ hipError_t dispatch_split(FwdArgs a, hipStream_t stream) {
   a.qt_base = 0;
   a.qt_count = a.n_qtiles;
   a.n_precise = a.n_qtiles;
-  hipError_t e = launch<DK, DV, CAUSAL, false, kNoMask, MODE>(
-      a, bh * (unsigned)a.n_qtiles * (unsigned)a.n_split, stream);
+  // (at most 16 query rows: the narrow kernel, one 16-row block per wave,
+  // where the pair's waves hold two)
+  const unsigned grid = bh * (unsigned)a.n_qtiles * (unsigned)a.n_split;
+  hipError_t e;
+  if constexpr (Cfg<DK, DV>::QB > 1)
+    e = a.ql <= 16 ? launch<DK, DV, CAUSAL, false, kNoMask, MODE, 1>(a, grid, stream)
+                   : launch<DK, DV, CAUSAL, false, kNoMask, MODE>(a, grid, stream);
+  else
+    e = launch<DK, DV, CAUSAL, false, kNoMask, MODE>(a, grid, stream);
   if (e != hipSuccess) return e;
   CombineArgs c;
   c.ws_o = a.ws_o;

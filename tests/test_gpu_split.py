@@ -35,6 +35,11 @@ CASES = [
     (1, 2, 1, 300, 200, 64, True, 3),       # ql > kl: offset 0, early chunks only
     (1, 2, 2, 100, 100, 64, True, 10),      # more chunks than key tiles
     (2, 4, 2, 64, 700, 256, True, 1),       # one chunk
+    # at most 16 query rows (the narrow kernels, one 16-row block per wave)
+    (1, 16, 1, 1, 2000, 64, False, 8),      # 16 query heads of one kv head, packed
+    (1, 2, 2, 16, 900, 64, True, 4),        # 16 rows, causal offset 884
+    (1, 2, 2, 17, 900, 128, True, 4),       # 17 rows: the two-block kernel
+    (1, 32, 8, 1, 32768, 128, True, 64),    # decoding against a 32k cache
 ]
 
 

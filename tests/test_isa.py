@@ -53,7 +53,9 @@ def test_all_variants_present(isa):
     # + split-KV, paged (whole-tile and short blocks), paged split-KV (head_dim x causal
     # each), bool masks: 66; the (key, value) pairs (80, 80), (96, 96), (96, 64),
     # (192, 192), (192, 128) x {none, causal, window} x {mixed, three mask kinds}: 60
-    assert len(fwd) == 126
+    # + the narrow split-KV kernels (at most 16 query rows) of head_dim 64 and 128:
+    # {split, paged split, short-block paged split} x causal x 2 = 12
+    assert len(fwd) == 138
     assert len(bwd) == 72  # head_dim (3) x {dQ, dKV} x {none, causal, window} x mask (4 kinds)
 
 
