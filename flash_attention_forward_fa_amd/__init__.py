@@ -232,11 +232,17 @@ def suggest_n_split(batch, n_heads, ql, head_dim, n_kv_heads=None, n_cu=256):
     """Chunks for train_fwd_split: about two workgroups per CU in total, or 1
     (use train_fwd) when the plain launch already has one per CU. With one
     query row per head and GQA (no mask, no window) the library runs a kv
-    group's query heads as one packed head: batch * n_kv_heads launch rows."""
+    group's query heads as one packed head: batch * n_kv_heads launch rows.
+    At most 16 (packed) query rows with head_dim 64 or 128 (decoding) run the
+    library's key-split decode kernel, which beats the plain launch at any
+    batch: about one workgroup per CU, and at least 8 chunks (measured best
+    on MI355X for batch 1, 4 and 8 against 32k keys)."""
     rows = 128 if head_dim == 256 else 256
     if ql == 1 and n_kv_heads and n_heads > n_kv_heads:
         n_heads, ql = n_kv_heads, n_heads // n_kv_heads
     plain = batch * n_heads * ((ql + rows - 1) // rows)
+    if ql <= 16 and head_dim in (64, 128):
+        return max(8, (n_cu + plain - 1) // plain)
     return 1 if plain >= n_cu else max(1, (2 * n_cu + plain - 1) // plain)
 
 

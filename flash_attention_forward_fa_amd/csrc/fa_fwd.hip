@@ -176,7 +176,7 @@ int train_fwd(const void* q, const void* k, const void* v, const void* mask, int
     if (!workspace) return FA_ERR_NULL_POINTER;
     if (!aligned(workspace, 16)) return FA_ERR_ALIGNMENT;
     if ((int64_t)workspace_bytes < split_bytes(rows, dv, n_eff)) return FA_ERR_SPLIT;
-    if (grid * n_eff > 0x7fffffffLL || (rows + 3) / 4 > 0x7fffffffLL) return FA_ERR_TOO_LARGE;
+    if (grid * n_eff > 0x7fffffffLL || rows > 0x7fffffffLL) return FA_ERR_TOO_LARGE;
     a.n_split = (int)n_eff;
     a.kchunk = (int)kchunk;
     a.ws_o = static_cast<float*>(workspace);
@@ -313,7 +313,7 @@ extern "C" int fa_paged_fwd(const void* q, const void* k_cache, const void* v_ca
     if (!workspace) return FA_ERR_NULL_POINTER;
     if (!aligned(workspace, 16)) return FA_ERR_ALIGNMENT;
     if ((int64_t)workspace_bytes < split_bytes(rows, head_dim, n_eff)) return FA_ERR_SPLIT;
-    if (grid * n_eff > 0x7fffffffLL || (rows + 3) / 4 > 0x7fffffffLL) return FA_ERR_TOO_LARGE;
+    if (grid * n_eff > 0x7fffffffLL || rows > 0x7fffffffLL) return FA_ERR_TOO_LARGE;
     a.n_split = (int)n_eff;
     a.kchunk = (int)kchunk;
     a.ws_o = static_cast<float*>(workspace);

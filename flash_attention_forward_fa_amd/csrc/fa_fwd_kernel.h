@@ -204,7 +204,13 @@ __device__ __forceinline__ bool fwd_tile(const FwdArgs& a, int qtile, int bh, ui
   constexpr int kQB = QBX ? QBX : Cfg<DK, DV>::QB;
   static_assert(kQB <= Cfg<DK, DV>::QB, "redo flags for at most the pair's blocks");
   constexpr int kRowsPerWave = 16 * kQB;
-  constexpr int kBlockM = Cfg<DK, DV>::W * kRowsPerWave;
+  // The narrow split-KV kernels (at most 16 query rows: decoding) split the
+  // keys, not the rows, among the waves: every wave holds the same 16 rows,
+  // each takes one 16-key block of a tile, and the waves' partial softmax
+  // states are merged through LDS at the end.
+  constexpr bool DECODE = QBX == 1 && SPLIT;
+  static_assert(!DECODE || (DK == DV && DK <= 128 && !kPanels<DK>), "decode: 64 or 128 dims");
+  constexpr int kBlockM = DECODE ? 16 : Cfg<DK, DV>::W * kRowsPerWave;
   constexpr int NKB = BN / 16;   // 16-key blocks per tile
   constexpr int NKC = BN / 32;   // 32-key chunks per tile (P.V contraction steps)
   constexpr int NDB = DV / 16;   // 16-dim blocks of O
@@ -239,12 +245,12 @@ __device__ __forceinline__ bool fwd_tile(const FwdArgs& a, int qtile, int bh, ui
   const int g = h / a.group;
   // (paged KV: the sequence's own key count, at most its table's capacity, and
   // its own causal offset)
-  const int kl = PAGED ? min(max(__builtin_amdgcn_readfirstlane(a.seq_lens[b]), 0),
+  const int kl = PAGED ? min(max(load_uniform(a.seq_lens, b), 0),
                              a.max_blocks * a.block_size)
                        : a.kl;
   const int ql = a.ql, off = PAGED ? max(kl - ql, 0) : a.causal_off;
   const int q0 = qtile * kBlockM;
-  const int qw0 = q0 + wave * kRowsPerWave;
+  const int qw0 = DECODE ? q0 : q0 + wave * kRowsPerWave;
   const uint16_t* kp = a.k + b * a.k_sb + g * a.k_sh;
   const uint16_t* vp = a.v + b * a.v_sb + g * a.v_sh;
   // row strides of the K and V sources (a paged cache's rows are contiguous)
@@ -316,7 +322,11 @@ __device__ __forceinline__ bool fwd_tile(const FwdArgs& a, int qtile, int bh, ui
   constexpr int NSTAGE = (SPLIT || PAGED) && DK <= 128 ? 4 : 2;
   uint16_t* const kst[4] = {k0s, k1s, k2s, k3s};
   uint16_t* const vst[4] = {v0s, v1s, v2s, v3s};
-  if constexpr (NSTAGE == 4) {
+  if constexpr (DECODE) {
+    // (the first three tiles, in stages 0 to 2)
+    for (int i = 0; i < 3; ++i)
+      if (kt_first + i < n_kt) issue_k(kt_first + i, kst[i]);
+  } else if constexpr (NSTAGE == 4) {
     for (int i = 0; i < 3; ++i)
       if (kt_first + i < n_kt) issue_k(kt_first + i, kst[(kt_first + i) & 3]);
   } else {
@@ -698,13 +708,157 @@ __device__ __forceinline__ bool fwd_tile(const FwdArgs& a, int qtile, int bh, ui
       set_prio<0>();
     }
   };
-  if constexpr (NSTAGE == 4) {
+  if constexpr (DECODE) {
+    for (int i = 0; i < 3; ++i)
+      if (kt_first + i < n_kt) issue_v(kt_first + i, vst[i]);
+  } else if constexpr (NSTAGE == 4) {
     for (int i = 0; i < 3; ++i)
       if (kt_first + i < n_kt) issue_v(kt_first + i, vst[(kt_first + i) & 3]);
   } else {
     if (n_kt > kt_first) issue_v(kt_first, (kt_first & 1) ? v1s : v0s);
   }
-  if constexpr (NSTAGE == 4) {
+  if constexpr (DECODE) {
+    // One tile per step, wave w < 4 taking its keys 16 w .. (the copies, not
+    // the arithmetic, set the pace here: the four other waves only copy).
+    // Tile kt_first + i sits in stage i & 3; three tiles are in flight while
+    // one is computed, and a step's copy goes to the stage the previous step
+    // read.
+    constexpr int R = CopyShape<DK, BN, NT>::ROUNDS + CopyShape<DV, BN, NT>::ROUNDS;
+    const int kb_w = wave & 3;
+    const int row = qw0 + c16;
+    float& mu = m_use[0];
+    float& th = thr[0];
+    float& lr = l_run[0];
+    auto tile_work = [&](int kt, const uint16_t* ks, const uint16_t* vs) {
+      // S^T of the block's 16 keys: lane (c16, grp) holds keys 4 grp + e of row c16
+      f32x4 sacc = {};
+#pragma unroll
+      for (int st = 0; st < NDS; ++st) {
+        const bf16x8 kop =
+            *reinterpret_cast<const bf16x8*>(ks + k_step_piece<DK>(16 * kb_w + c16, st, grp));
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop[0][st], sacc, 0, 0, 0);
+      }
+      const int key0 = kt * BN + 16 * kb_w + 4 * grp;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int key = key0 + e;
+        if (!(key < kl && (!CAUSAL || key <= off + row))) sacc[e] = -INFINITY;
+      }
+      float mx = __builtin_fmaxf(__builtin_fmaxf(sacc[0], sacc[1]), __builtin_fmaxf(sacc[2], sacc[3]));
+      if (__any(mx > th)) {
+        mx = group_max(mx);
+        const bool r = mx > th;
+        const float m_new = r ? mx * a.c : mu;
+        th = r ? (m_new + kLazy) * inv_c : th;
+        const float alpha = __builtin_amdgcn_exp2f(mu - m_new);
+        mu = m_new;
+        lr *= alpha;
+#pragma unroll
+        for (int d = 0; d < NDB; ++d) oacc[d][0] *= alpha;
+      }
+      // P = exp2(s - m) as bf16 and its bf16 remainder, and the row sum
+      bf16x4 ph, pl;
+      const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[e], a.c, -mu));
+        ph[e] = (__bf16)p;
+        pl[e] = (__bf16)(p - (float)ph[e]);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; e += 2) {
+        lr = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{ph[e], ph[e + 1]}, ones, lr, false);
+        lr = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pl[e], pl[e + 1]}, ones, lr, false);
+      }
+      // O^T += V^T P^T over the 16 keys (16x16x16 MFMA: V^T of dims 16d + c16,
+      // keys 4 grp .. from one transposing read)
+      const s16x4 bh_ = __builtin_bit_cast(s16x4, ph), bl_ = __builtin_bit_cast(s16x4, pl);
+      const int rv = 16 * kb_w + 4 * grp + (c16 >> 2);
+#pragma unroll
+      for (int d = 0; d < NDB; ++d) {
+        const s16x4 vop = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4*)(vs + v_piece<DV>(rv, d, c16 & 3)));
+        oacc[d][0] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vop, bh_, oacc[d][0], 0, 0, 0);
+        oacc[d][0] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vop, bl_, oacc[d][0], 0, 0, 0);
+      }
+    };
+    auto dstep = [&](int kt, const uint16_t* kc, const uint16_t* vc, uint16_t* kn,
+                     uint16_t* vn) {
+      // this thread's copies of tile kt have landed (those of the two tiles
+      // after it may still be in flight: the counter drains in order), then
+      // every thread's
+      if (kt + 2 < n_kt)
+        wait_vmem_n<2 * R>();
+      else if (kt + 1 < n_kt)
+        wait_vmem_n<R>();
+      else
+        wait_vmem();
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      if (kt + 3 < n_kt) {
+        issue_k(kt + 3, kn);
+        issue_v(kt + 3, vn);
+      }
+      if (wave < 4) tile_work(kt, kc, vc);
+    };
+    for (int t0 = kt_first; t0 < n_kt; t0 += 4) {
+      dstep(t0, k0s, v0s, k3s, v3s);
+      if (t0 + 1 < n_kt) dstep(t0 + 1, k1s, v1s, k0s, v0s);
+      if (t0 + 2 < n_kt) dstep(t0 + 2, k2s, v2s, k1s, v1s);
+      if (t0 + 3 < n_kt) dstep(t0 + 3, k3s, v3s, k2s, v2s);
+    }
+
+    // ---- merge of the waves' states: each wave's O (f32, unnormalised) and
+    // its max and sum per row go to LDS (two waves per K stage, the maxima
+    // and sums in V stage 0), then every thread merges a few elements ----
+    const float l_tot = group_sum(lr);
+    wait_vmem();
+    __syncthreads();
+    {
+      float* part = reinterpret_cast<float*>(wave < 2 ? k0s : wave < 4 ? k1s : wave < 6 ? k2s : k3s) +
+                    (wave & 1) * 16 * DV;
+#pragma unroll
+      for (int d = 0; d < NDB; ++d)
+        *reinterpret_cast<f32x4*>(part + c16 * DV + 16 * d + 4 * grp) = oacc[d][0];
+      float* ml = reinterpret_cast<float*>(v0s);
+      if (grp == 0) {
+        ml[wave * 16 + c16] = mu;
+        ml[128 + wave * 16 + c16] = l_tot;
+      }
+    }
+    __syncthreads();
+    const float* ml = reinterpret_cast<const float*>(v0s);
+    const float* parts[8] = {reinterpret_cast<const float*>(k0s),
+                             reinterpret_cast<const float*>(k0s) + 16 * DV,
+                             reinterpret_cast<const float*>(k1s),
+                             reinterpret_cast<const float*>(k1s) + 16 * DV,
+                             reinterpret_cast<const float*>(k2s),
+                             reinterpret_cast<const float*>(k2s) + 16 * DV,
+                             reinterpret_cast<const float*>(k3s),
+                             reinterpret_cast<const float*>(k3s) + 16 * DV};
+#pragma unroll
+    for (int i = 0; i < 16 * DV / NT; ++i) {
+      const int idx = tid + NT * i, r = idx / DV, dcol = idx % DV;
+      if (q0 + r < ql) {
+        float m = -FLT_MAX;
+#pragma unroll
+        for (int w = 0; w < 8; ++w) m = __builtin_fmaxf(m, ml[w * 16 + r]);
+        float z = 0.0f, o = 0.0f;
+#pragma unroll
+        for (int w = 0; w < 8; ++w) {
+          const float sc = __builtin_amdgcn_exp2f(ml[w * 16 + r] - m);
+          z += ml[128 + w * 16 + r] * sc;
+          o += parts[w][r * DV + dcol] * sc;
+        }
+        const bool empty = !(z > 0.0f);
+        const int64_t prow = ((int64_t)split * a.B * a.H + bh) * ql + q0 + r;
+        a.ws_o[prow * DV + dcol] = empty ? 0.0f : o / z;
+        if (dcol == 0) a.ws_l[prow] = empty ? -INFINITY : (m + __builtin_amdgcn_logf(z)) * kLn2;
+      }
+    }
+    return false;
+  } else if constexpr (NSTAGE == 4) {
     // copy instructions per thread per tile (K and V)
     constexpr int R = CopyShape<DK, BN, NT>::ROUNDS + CopyShape<DV, BN, NT>::ROUNDS;
     auto step4 = [&](int kt, const uint16_t* kc, const uint16_t* vc, uint16_t* kn,
@@ -932,16 +1086,28 @@ struct CombineArgs {
 
 template <int D>
 __global__ __launch_bounds__(256) void fa_combine_kernel(CombineArgs c) {
+  // One workgroup per row: the four waves read the chunks' partials in
+  // parallel (wave w the chunks s = w mod 4, several loads in flight each),
+  // then their sums are added through LDS. (A serial walk over the chunks,
+  // one load latency per chunk, took longer than the partials themselves.)
   constexpr int P = D / 64;
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= c.rows) return;
-  const int lane = threadIdx.x & 63;
+  __shared__ float red_o[4][D];
+  __shared__ float red_z[4], red_m[4];
+  const int64_t row = blockIdx.x;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // the largest chunk logsumexp of the row
   float m = -INFINITY;
-  for (int s = 0; s < c.n_split; ++s) m = fmaxf(m, c.ws_l[s * c.rows + row]);
+  for (int s = threadIdx.x; s < c.n_split; s += 256) m = fmaxf(m, c.ws_l[s * c.rows + row]);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  if (lane == 0) red_m[wave] = m;
+  __syncthreads();
+  m = fmaxf(fmaxf(red_m[0], red_m[1]), fmaxf(red_m[2], red_m[3]));
   float acc[P] = {};
   float z = 0.0f;
   if (m != -INFINITY) {
-    for (int s = 0; s < c.n_split; ++s) {
+#pragma unroll 8
+    for (int s = wave; s < c.n_split; s += 4) {
       // (a chunk with no visible key has L_s = -inf: weight 0, partial O 0)
       const float w = __builtin_amdgcn_exp2f((c.ws_l[s * c.rows + row] - m) * kLog2e);
       z += w;
@@ -950,14 +1116,23 @@ __global__ __launch_bounds__(256) void fa_combine_kernel(CombineArgs c) {
       for (int e = 0; e < P; ++e) acc[e] += w * op[e];
     }
   }
+#pragma unroll
+  for (int e = 0; e < P; ++e) red_o[wave][lane * P + e] = acc[e];
+  if (lane == 0) red_z[wave] = z;
+  __syncthreads();
+  if (wave != 0) return;
+  z = (red_z[0] + red_z[1]) + (red_z[2] + red_z[3]);
   const bool empty = m == -INFINITY;
   const float inv = empty ? 0.0f : 1.0f / z;
   const int64_t bh = row / c.ql;
   uint16_t* orow = c.o + (bh / c.H) * c.o_sb + (bh % c.H) * c.o_sh + (row % c.ql) * c.o_sr +
                    lane * P;
 #pragma unroll
-  for (int e = 0; e < P; ++e)
-    orow[e] = __builtin_bit_cast(uint16_t, empty ? (__bf16)0.0f : (__bf16)(acc[e] * inv));
+  for (int e = 0; e < P; ++e) {
+    const int d = lane * P + e;
+    const float o = (red_o[0][d] + red_o[1][d]) + (red_o[2][d] + red_o[3][d]);
+    orow[e] = __builtin_bit_cast(uint16_t, empty ? (__bf16)0.0f : (__bf16)(o * inv));
+  }
   if (lane == 0) c.l[row] = empty ? -INFINITY : m + __builtin_amdgcn_logf(z) * kLn2;
 }
 
@@ -1019,8 +1194,7 @@ hipError_t dispatch_split(FwdArgs a, hipStream_t stream) {
   c.o_sb = a.o_sb;
   c.o_sh = a.o_sh;
   c.o_sr = a.o_sr;
-  hipLaunchKernelGGL(fa_combine_kernel<DV>, dim3((unsigned)((c.rows + 3) / 4)), dim3(256), 0,
-                     stream, c);
+  hipLaunchKernelGGL(fa_combine_kernel<DV>, dim3((unsigned)c.rows), dim3(256), 0, stream, c);
   return hipGetLastError();
 }
 

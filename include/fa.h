@@ -264,6 +264,10 @@ int fa_train_fwd_dv(const void *q, const long long *q_strides, const void *k,
  *              when ql == 1 (below); about two workgroups per CU in total
  *              (n_split ~ 2 * 256 / that count) was near the fastest on
  *              MI355X, and at one or more per CU the plain call is faster.
+ *              At most 16 (packed) query rows with head_dim 64 or 128
+ *              (decoding) run a kernel that splits each chunk's keys among
+ *              its waves; there about one workgroup per CU and at least 8
+ *              chunks was near the fastest, at any batch.
  *
  * Decoding (ql == 1, n_heads > n_kv_heads, no mask, no window; this and the
  * other forward entry points): [B, H, 1, D] is [B, Hkv, H/Hkv, D], so a kv

@@ -231,10 +231,15 @@ def test_backward_binding_fails_loudly_without_gpu_tensors():
 
 def test_suggest_n_split():
     assert fa.suggest_n_split(1, 32, 512, 128) == 8     # 64 plain workgroups
-    assert fa.suggest_n_split(1, 32, 1, 128) == 16      # 32 plain workgroups
-    assert fa.suggest_n_split(8, 32, 1, 128) == 1       # 256: one per CU already
+    # decoding (at most 16 packed rows, head_dim 64 or 128): one workgroup per
+    # CU, at least 8 chunks
+    assert fa.suggest_n_split(1, 32, 1, 128) == 8       # 32 plain workgroups
+    assert fa.suggest_n_split(8, 32, 1, 128) == 8       # 256: still split
     assert fa.suggest_n_split(8, 32, 1, 128, n_kv_heads=8) == 8   # packed: 64
-    assert fa.suggest_n_split(1, 32, 1, 128, n_kv_heads=8) == 64  # packed: 8
+    assert fa.suggest_n_split(1, 32, 1, 128, n_kv_heads=8) == 32  # packed: 8
+    assert fa.suggest_n_split(1, 2, 16, 64) == 128      # 16 rows of 2 heads
+    assert fa.suggest_n_split(1, 2, 17, 64) == 256      # 17 rows: two per CU
+    assert fa.suggest_n_split(1, 32, 1, 256) == 16      # head_dim 256: two per CU
     assert fa.suggest_n_split(2, 16, 8192, 256) == 1
 
 
