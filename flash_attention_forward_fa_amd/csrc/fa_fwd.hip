@@ -166,6 +166,7 @@ int train_fwd(const void* q, const void* k, const void* v, const void* mask, int
   a.o_sb = st[9], a.o_sh = st[10], a.o_sr = (int)st[11];
   a.n_split = 0;
   a.kchunk = 0;
+  a.split_plain = 0;
   a.ws_o = nullptr;
   a.ws_l = nullptr;
   if (n_split > 0 && kl > 0) {
@@ -188,7 +189,10 @@ int train_fwd(const void* q, const void* k, const void* v, const void* mask, int
   // query tiles whose first row may see fewer than kPreciseKeys keys; every
   // tile when the plain tiles' pre-scaled Q is not used (below)
   int64_t n_short = 0;
-  if (kl <= kPlainMinKeys || !(a.c >= kPlainMinC && a.c <= kPlainMaxC))
+  const bool plain_ok = kl > kPlainMinKeys && a.c >= kPlainMinC && a.c <= kPlainMaxC;
+  // (split-KV chunks decide per chunk and query tile, in the kernel)
+  a.split_plain = a.n_split > 0 && plain_ok;
+  if (!plain_ok)
     n_short = n_qtiles;
   else if (windowed && (a.window + 1 < kPreciseKeys ||
                         (ql > kl && (int64_t)ql - 1 > (int64_t)kl + a.window - kPreciseKeys)))

@@ -67,6 +67,7 @@ struct FwdArgs {
   int qt_base;     // this launch computes query tiles [qt_base, qt_base + qt_count)
   int qt_count;
   int n_precise;   // kMixed: query tiles below this run compensated
+  int split_plain; // kSplit: chunks may run plain tiles (else every tile compensated)
   int causal_off;  // max(kl - ql, 0)
   int window;      // WINDOW variants: keys below q_abs - window are hidden
   int n_split;     // kSplit: key chunks per query tile (grid factor)
@@ -191,8 +192,9 @@ __device__ __forceinline__ bool fwd_tile(const FwdArgs& a, int qtile, int bh, ui
   static_assert(PRECISE || !HAS_MASK, "the masked forward always runs compensated");
   static_assert(PRECISE || !REDO, "a redo runs compensated");
   static_assert(CAUSAL || !WINDOW, "the sliding window includes the causal rule");
-  static_assert(!SPLIT || (PRECISE && !REDO && !WINDOW && MASK == kNoMask),
-                "split-KV partials: compensated, unmasked, no window");
+  static_assert(!SPLIT || (!WINDOW && MASK == kNoMask), "split-KV partials: unmasked, no window");
+  static_assert(!SPLIT || PAGED || QBX == 0 || PRECISE,
+                "the decoding split kernels run compensated");
   static_assert(!PAGED || (PRECISE && !REDO && !WINDOW && MASK == kNoMask),
                 "paged KV: compensated, unmasked, no window");
   static_assert((!SPLIT && !PAGED) || (DK == DV && !kPanels<DK>),
@@ -1047,8 +1049,28 @@ __attribute__((amdgpu_waves_per_eu(MODE == kMixed ? Cfg<DK, DV>::WPE : 2))) void
                                                             wg_flags);
     }
   } else if constexpr (MODE == kSplit) {
-    fwd_tile<DK, DV, CAUSAL, false, kNoMask, true, false, true, false, false, QBX>(
-        a, qtile, bh, FA_TILE_BUFFERS, redo, wg_flags, split);
+    // A chunk of a query tile runs compensated when some of its rows see 1 to
+    // kPreciseKeys - 1 of the chunk's keys (by position, as the mixed kernel's
+    // short tiles), or when plain tiles are off for the problem; otherwise
+    // plain, with the compensated redo of rows with some |O| >= 1.
+    bool precise = true;
+    if constexpr (QBX == 0) {
+      const int c0 = split * a.kchunk, c1 = min(c0 + a.kchunk, a.kl);
+      constexpr int kBM = block_m<DK, DV>();
+      const int r0 = qtile * kBM, r1 = min(r0 + kBM, a.ql) - 1;
+      const int n_first = max(0, (CAUSAL ? min(c1, a.causal_off + r0 + 1) : c1) - c0);
+      const int n_last = max(0, (CAUSAL ? min(c1, a.causal_off + r1 + 1) : c1) - c0);
+      precise = !a.split_plain || (n_first < kPreciseKeys && n_last >= 1);
+    }
+    if (precise) {
+      fwd_tile<DK, DV, CAUSAL, false, kNoMask, true, false, true, false, false, QBX>(
+          a, qtile, bh, FA_TILE_BUFFERS, redo, wg_flags, split);
+    } else if constexpr (QBX == 0) {
+      if (fwd_tile<DK, DV, CAUSAL, false, kNoMask, false, false, true>(
+              a, qtile, bh, FA_TILE_BUFFERS, redo, wg_flags, split))
+        fwd_tile<DK, DV, CAUSAL, false, kNoMask, true, true, true>(a, qtile, bh, FA_TILE_BUFFERS,
+                                                                   redo, wg_flags, split);
+    }
   } else if constexpr (MODE == kPaged) {
     fwd_tile<DK, DV, CAUSAL, false, kNoMask, true, false, false, true>(
         a, qtile, bh, FA_TILE_BUFFERS, redo, wg_flags);

@@ -14,12 +14,12 @@ from tests import gpu_util as gu
 pytestmark = pytest.mark.gpu
 
 
-def run_split(inp, w, n_split, workspace=None):
+def run_split(inp, w, n_split, workspace=None, scale=None):
     import torch
     import flash_attention_forward_fa_amd as fa
     q, k, v = (gu.to_dev(inp[n], "cuda:0") for n in ("q", "k", "v"))
-    O, L = fa.train_fwd_split(q, k, v, n_split, scale=w.scale, causal=w.causal,
-                              workspace=workspace)
+    O, L = fa.train_fwd_split(q, k, v, n_split, scale=w.scale if scale is None else scale,
+                              causal=w.causal, workspace=workspace)
     torch.cuda.synchronize()
     bits = O.view(torch.int16).cpu().numpy().view(np.uint16)
     return gu.widen(bits), L.cpu().numpy(), bits
@@ -40,7 +40,34 @@ CASES = [
     (1, 2, 2, 16, 900, 64, True, 4),        # 16 rows, causal offset 884
     (1, 2, 2, 17, 900, 128, True, 4),       # 17 rows: the two-block kernel
     (1, 32, 8, 1, 32768, 128, True, 64),    # decoding against a 32k cache
+    # chunks of plain tiles (more than 256 keys), compensated where a chunk's
+    # rows see 1 to 127 of its keys
+    (1, 4, 2, 700, 3000, 64, True, 3),      # ql < kl: chunks before, across, after the diagonal
+    (1, 2, 1, 1000, 1000, 128, True, 5),    # ql = kl: the diagonal crosses every chunk
+    (2, 4, 4, 300, 2000, 256, False, 6),    # not causal: a short last chunk (2000 - 5 * 384)
 ]
+
+
+@pytest.mark.parametrize("D", [64, 128, 256])
+def test_split_plain_chunks_redo(D):
+    """V times 4 (exact in bf16) and scale 1 (a concentrated softmax): many
+    rows reach |O| >= 1, so plain chunks hand them to their compensated redo;
+    every row against the oracle."""
+    w = fagen.Workload("split_redo", 1, 4, 2, 512, 4000, D, True, seed_offset=9300 + D)
+    print(f"case split redo D={D}", flush=True)
+    inp = fagen.generate(w)
+    vb = np.asarray(inp["v"], np.uint16)
+    e = (vb >> 7) & 0xFF
+    assert np.all(e < 250)
+    inp["v"] = np.where(e != 0, vb + np.uint16(2 << 7), vb).astype(np.uint16)  # exponent + 2
+    o, l, bits = run_split(inp, w, 4, scale=1.0)
+    of, ob, lr = oracle.fwd(inp["q"], inp["k"], inp["v"], None, w.B, w.H, w.Hkv, w.ql, w.kl,
+                            w.D, 1.0, w.causal)
+    big = int((np.abs(of) >= 1).any(axis=-1).sum())
+    eo, el, rms = gu.compare(o, l, bits, ob, lr, 1e-2, 1e-2, f"split redo D={D}", o_ref_f32=of)
+    print(f"split redo D={D}: {big} rows with |O| >= 1, dO={eo:.3e} dL={el:.3e} "
+          f"relRMS={rms:.2e}")
+    assert big > 0 and rms <= 5e-3
 
 
 @pytest.mark.parametrize("B,H,Hkv,ql,kl,D,causal,n_split", CASES)
