@@ -40,6 +40,10 @@ def _bind(path):
                                           ctypes.c_float, ctypes.c_int, i64, vp, i64, vp, vp,
                                           ctypes.c_int]
     lib.fa_oracle_fwd_general.restype = ctypes.c_int
+    lib.fa_oracle_fwd_sinks.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64,
+                                        ctypes.c_float, ctypes.c_int, i64, vp, vp, i64, vp, vp,
+                                        ctypes.c_int]
+    lib.fa_oracle_fwd_sinks.restype = ctypes.c_int
     lib.fa_oracle_bwd_general.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64,
                                           i64, ctypes.c_float, ctypes.c_int, i64, vp, i64, vp, vp,
                                           vp, ctypes.c_int]
@@ -176,11 +180,15 @@ def bwd(q, k, v, mask, L, dO, B, H, Hkv, ql, kl, D, scale, causal, n_threads=Non
 
 
 def fwd_dv(q, k, v, mask, B, H, Hkv, ql, kl, D, Dv, scale, causal, window=None, rows=None,
-           n_threads=None, lib=None):
+           n_threads=None, lib=None, sinks=None):
     """Forward with value width Dv (q, k: [.., D]; v: [B,Hkv,kl,Dv]). All rows
     (O [B,H,ql,Dv], L [B,H,ql]) or the flat `rows` (O [n,Dv], L [n]).
+    sinks: None or one logit per query head (f32 [H], natural-log units).
     Returns (O_f32, O_bf16_bits, L)."""
     qf, kf, vf, mf = _f32(q), _f32(k), _f32(v), _f32(mask)
+    sf = None if sinks is None else np.ascontiguousarray(sinks, dtype=np.float32)
+    if sf is not None and sf.shape != (H,):
+        raise ValueError(f"sinks must have shape ({H},)")
     lib = lib or _load()
     if rows is None:
         O = np.empty((B, H, ql, Dv), dtype=np.float32)
@@ -193,11 +201,18 @@ def fwd_dv(q, k, v, mask, B, H, Hkv, ql, kl, D, Dv, scale, causal, window=None, 
         rp, n = rows.ctypes.data, rows.size
         if n == 0:
             return O, round_bf16(O, lib), L
-    rc = lib.fa_oracle_fwd_general(_ptr(qf), _ptr(kf), _ptr(vf), _ptr(mf), B, H, Hkv, ql, kl, D,
-                                   Dv, float(scale), int(bool(causal)),
-                                   -1 if window is None else int(window), rp, n, _ptr(O),
-                                   _ptr(L), n_threads or default_threads())
-    _check(rc, "fa_oracle_fwd_general")
+    if sf is None:
+        rc = lib.fa_oracle_fwd_general(_ptr(qf), _ptr(kf), _ptr(vf), _ptr(mf), B, H, Hkv, ql, kl,
+                                       D, Dv, float(scale), int(bool(causal)),
+                                       -1 if window is None else int(window), rp, n, _ptr(O),
+                                       _ptr(L), n_threads or default_threads())
+        _check(rc, "fa_oracle_fwd_general")
+    else:
+        rc = lib.fa_oracle_fwd_sinks(_ptr(qf), _ptr(kf), _ptr(vf), _ptr(mf), B, H, Hkv, ql, kl,
+                                     D, Dv, float(scale), int(bool(causal)),
+                                     -1 if window is None else int(window), _ptr(sf), rp, n,
+                                     _ptr(O), _ptr(L), n_threads or default_threads())
+        _check(rc, "fa_oracle_fwd_sinks")
     return O, round_bf16(O, lib), L
 
 

@@ -29,6 +29,12 @@
  * The sliding window is the page's section 7 band (key j kept for row i iff
  * j <= i and j + w >= i), placed at the causal rule's position pos_i.
  * Keys and values may have different widths (D for q and k, Dv for v and O).
+ * An optional sink logit per query head (fa_oracle_fwd_sinks) joins every
+ * row's softmax as one more term with a zero value: it enters the maximum and
+ * the sum, so L_i = log(exp(sink_h) + sum_j exp(s_ij)) and O_i's weights are
+ * exp(s_ij - L_i). (The adjacent SDPA page passes sinks [Hq] without defining
+ * them; this is the reading its name and shape fix: a per-head logit with no
+ * value.) A row with no visible key then has O_i = +0, L_i = sink_h.
  *
  * The backward (fa_oracle_bwd*) is the FA-2 backward the same page defines
  * (section "Phase 2 - backward kernel helpers", its doc comment), written from
@@ -62,6 +68,7 @@ typedef struct {
     float scale;
     int causal;
     int64_t window; /* < 0: no sliding window */
+    const float *sinks; /* [H] natural-log logits, or NULL */
 } oracle_problem;
 
 /* ---- the definition, per (query row, key) ---- */
@@ -99,6 +106,12 @@ static float score(const oracle_problem *p, int64_t row, int64_t pos, int64_t j,
     return s;
 }
 
+/* The sink logit of a flat query row's head (-inf without sinks). */
+static float row_sink(const oracle_problem *p, int64_t row)
+{
+    return p->sinks ? p->sinks[(row / p->ql) % p->H] : -INFINITY;
+}
+
 /* The kv head (b * Hkv + g) a flat query row reads, and its position. */
 static void row_coords(const oracle_problem *p, int64_t row, int64_t *kvhead, int64_t *pos)
 {
@@ -123,6 +136,9 @@ static void forward_row(const oracle_problem *p, int64_t row, float *o, float *l
         if (e[j] > m)
             m = e[j];
     }
+    const float sink = row_sink(p, row);
+    if (sink > m)
+        m = sink;
     for (int64_t d = 0; d < p->Dv; ++d)
         o[d] = 0.0f;
     if (m == -INFINITY) { /* no visible key */
@@ -134,6 +150,7 @@ static void forward_row(const oracle_problem *p, int64_t row, float *o, float *l
         e[j] = expf(e[j] - m); /* hidden keys: exp(-inf) = 0 */
         z += e[j];
     }
+    z += expf(sink - m); /* the sink's term (exactly 0 without one) */
     *l = m + logf(z);
     for (int64_t j = 0; j < p->kl; ++j) {
         if (e[j] == 0.0f) /* a hidden key adds exactly zero */
@@ -241,17 +258,18 @@ static int validate(const float *q, const float *k, const float *v, int64_t B, i
 /*
  * The general forward. Inputs are f32 host arrays (bf16 values widened
  * exactly): q [B,H,ql,D], k [B,Hkv,kl,D], v [B,Hkv,kl,Dv], mask [B,H,ql,kl]
- * (natural-log units, -inf hides a key) or NULL. causal: 0/1; window < 0:
+ * (natural-log units, -inf hides a key) or NULL; sinks [H] (natural-log
+ * logits) or NULL. causal: 0/1; window < 0:
  * none, >= 0: the sliding window, which includes the causal rule (whatever
  * `causal` says). rows == NULL: every row, O [B,H,ql,Dv] and
  * L [B,H,ql]; otherwise the n_rows flat rows listed ((b*H + h)*ql + i),
  * O [n_rows,Dv] and L [n_rows]. Returns 0 on success, 1 null pointer, 2 bad
  * size or row index, 3 H % Hkv != 0, 4 out of host memory.
  */
-int fa_oracle_fwd_general(const float *q, const float *k, const float *v, const float *mask,
-                          int64_t B, int64_t H, int64_t Hkv, int64_t ql, int64_t kl, int64_t D,
-                          int64_t Dv, float scale, int causal, int64_t window,
-                          const int64_t *rows, int64_t n_rows, float *O, float *L, int n_threads)
+int fa_oracle_fwd_sinks(const float *q, const float *k, const float *v, const float *mask,
+                        int64_t B, int64_t H, int64_t Hkv, int64_t ql, int64_t kl, int64_t D,
+                        int64_t Dv, float scale, int causal, int64_t window, const float *sinks,
+                        const int64_t *rows, int64_t n_rows, float *O, float *L, int n_threads)
 {
     int rc = validate(q, k, v, B, H, Hkv, ql, kl, D, Dv);
     if (rc)
@@ -267,9 +285,19 @@ int fa_oracle_fwd_general(const float *q, const float *k, const float *v, const 
     if (!O || !L)
         return 1;
     oracle_problem p = {q, k, v, mask, B, H, Hkv, ql, kl, D, Dv, scale, causal != 0,
-                        window < 0 ? -1 : window};
+                        window < 0 ? -1 : window, sinks};
     forward_ctx c = {&p, rows, O, L};
     return run_parallel(n, n_threads, (size_t)(kl > 0 ? kl : 1), forward_range, &c);
+}
+
+/* The general forward without sinks. */
+int fa_oracle_fwd_general(const float *q, const float *k, const float *v, const float *mask,
+                          int64_t B, int64_t H, int64_t Hkv, int64_t ql, int64_t kl, int64_t D,
+                          int64_t Dv, float scale, int causal, int64_t window,
+                          const int64_t *rows, int64_t n_rows, float *O, float *L, int n_threads)
+{
+    return fa_oracle_fwd_sinks(q, k, v, mask, B, H, Hkv, ql, kl, D, Dv, scale, causal, window,
+                               NULL, rows, n_rows, O, L, n_threads);
 }
 
 /* Full forward with Dv = D, no window (the layout of fa_oracle_fwd_general). */
@@ -464,7 +492,7 @@ int fa_oracle_bwd_general(const float *q, const float *k, const float *v, const 
         return 4;
     }
     backward_ctx c = {{q, k, v, mask, B, H, Hkv, ql, kl, D, Dv, scale, causal != 0,
-                       window < 0 ? -1 : window},
+                       window < 0 ? -1 : window, NULL},
                       L, dO, groups, n_groups, G, Di, dQ, dK, dV};
     rc = run_parallel(n_q, n_threads, (size_t)(2 * (kl > 0 ? kl : 1)), backward_rows, &c);
     if (!rc)

@@ -14,7 +14,7 @@ narrower than Q and K.
 import numpy as np
 
 
-def attention_f64(q, k, v, mask, scale, causal, window=None):
+def attention_f64(q, k, v, mask, scale, causal, window=None, sinks=None):
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
@@ -37,13 +37,16 @@ def attention_f64(q, k, v, mask, scale, causal, window=None):
                 s = np.where(j > off + i, -np.inf, s)
             if window is not None:
                 s = np.where(j < off + i - window, -np.inf, s)
+            # a sink: one more logit in the row's softmax, with a zero value
+            sink = -np.inf if sinks is None else float(sinks[h])
             for i in range(ql):
                 row = s[i]
-                if kl == 0 or not np.isfinite(row).any():
+                if (kl == 0 or not np.isfinite(row).any()) and not np.isfinite(sink):
                     continue
-                m = row[np.isfinite(row)].max()
+                m = max(row[np.isfinite(row)].max() if np.isfinite(row).any() else -np.inf,
+                        sink)
                 e = np.exp(row - m)
-                z = e.sum()
+                z = e.sum() + np.exp(sink - m)
                 L[b, h, i] = m + np.log(z)
                 O[b, h, i] = (e @ v[b, kvh]) / z
     return O, L

@@ -346,6 +346,68 @@ DV_PINS = [
                                                      window=3)),
 ]
 
+def pin_brute_force_sinks(fwd_dv, B, H, Hkv, ql, kl, D, Dv, causal, masked, seed, sinks):
+    """Per-head sink logits against the f64 definition (one more softmax term
+    with a zero value); fwd_dv as for pin_brute_force_dv, with sinks=."""
+    scale = 1.0 / math.sqrt(D)
+    q = fagen.normal_bf16(seed, 0, (B, H, ql, D))
+    k = fagen.normal_bf16(seed, 1, (B, Hkv, kl, D))
+    v = fagen.normal_bf16(seed, 2, (B, Hkv, kl, Dv))
+    mask = _finite_mask(seed, B, H, ql, kl) if masked else None
+    sinks = np.asarray(sinks, dtype=np.float32)
+    O, _, L = fwd_dv(q, k, v, mask, B, H, Hkv, ql, kl, D, Dv, scale, causal, sinks=sinks)
+    Oref, Lref = attention_f64(_widen(q), _widen(k), _widen(v), mask, scale, causal,
+                               sinks=sinks)
+    empty = np.isneginf(Lref)
+    assert np.array_equal(np.isneginf(L), empty), "rows with L = -inf differ"
+    assert np.all(O[empty] == 0), "empty row O != 0"
+    live = ~empty
+    errO = np.abs(O[live] - Oref[live]).max()
+    errL = (np.abs(L[live] - Lref[live]) / np.maximum(1.0, np.abs(Lref[live]))).max()
+    assert errO <= 1e-5, f"O with sinks vs f64 brute force: {errO:.3e}"
+    assert errL <= 1e-5, f"L with sinks vs f64 brute force: {errL:.3e}"
+
+
+def pin_sinks_closed_forms(fwd_dv):
+    """What the definition fixes exactly: sinks of -inf change nothing (bit for
+    bit); a row with no visible key gets O = +0 and L = its head's sink; a sink
+    far above every score takes all the weight (O -> 0, L -> sink); and with a
+    sink s, L' = logaddexp(L, s) and O' = O exp(L - L') for the row's no-sink
+    L and O."""
+    B, H, Hkv, ql, kl, D = 1, 4, 2, 6, 9, 8
+    q, k, v = _inputs(11, B, H, Hkv, ql, kl, D)
+    scale = 0.4
+    O0, _, L0 = fwd_dv(q, k, v, None, B, H, Hkv, ql, kl, D, D, scale, True)
+    neg = np.full(H, -np.inf, dtype=np.float32)
+    On, _, Ln = fwd_dv(q, k, v, None, B, H, Hkv, ql, kl, D, D, scale, True, sinks=neg)
+    assert np.array_equal(On, O0) and np.array_equal(Ln, L0), "sinks of -inf changed the result"
+    s = np.array([-2.0, 0.5, 3.0, 1.25], dtype=np.float32)
+    O1, _, L1 = fwd_dv(q, k, v, None, B, H, Hkv, ql, kl, D, D, scale, True, sinks=s)
+    Lx = np.logaddexp(L0.astype(np.float64), s[None, :, None].astype(np.float64))
+    assert np.abs(L1 - Lx).max() <= 1e-5 * max(1.0, np.abs(Lx).max()), "L != logaddexp(L, sink)"
+    Ox = O0 * np.exp(L0.astype(np.float64) - Lx)[..., None]
+    assert np.abs(O1 - Ox).max() <= 1e-5, "O != O exp(L - L')"
+    big = np.full(H, 120.0, dtype=np.float32)
+    Ob, _, Lb = fwd_dv(q, k, v, None, B, H, Hkv, ql, kl, D, D, scale, True, sinks=big)
+    assert np.all(np.isfinite(Lb)) and np.abs(Lb - 120.0).max() <= 1e-4, "a dominant sink"
+    assert np.abs(Ob).max() <= 1e-30, "a dominant sink leaves no weight to the keys"
+    mask = np.zeros((B, H, ql, kl), dtype=np.float32)
+    mask[:, :, 2] = -np.inf  # row 2 of every head sees no key
+    Om, _, Lm = fwd_dv(q, k, v, mask, B, H, Hkv, ql, kl, D, D, scale, True, sinks=s)
+    assert np.all(Lm[0, :, 2] == s), "an empty row's L must be its head's sink"
+    assert np.all(_bf16_bits(Om[0, :, 2]) == 0) and not np.signbit(Om[0, :, 2]).any(), \
+        "an empty row's O must be +0"
+
+
+# Pins of the forward with sinks (fwd_dv callables taking sinks=).
+SINK_PINS = [
+    ("sinks_closed_forms", pin_sinks_closed_forms),
+    ("brute_sinks", lambda f: pin_brute_force_sinks(f, 2, 4, 2, 9, 13, 8, 8, True, True, 8,
+                                                    [-1.0, 0.0, 2.5, -np.inf])),
+    ("brute_sinks_dv", lambda f: pin_brute_force_sinks(f, 1, 2, 1, 7, 5, 16, 8, False, False, 9,
+                                                       [1.5, -0.5])),
+]
+
 ALL_PINS = [
     ("hand_worked", pin_hand_worked),
     ("brute_small", lambda f: pin_brute_force(f, 2, 4, 2, 9, 13, 8, True, True, 1)),

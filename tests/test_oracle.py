@@ -202,3 +202,10 @@ def test_value_width_equal_is_the_plain_forward():
     b = oracle.fwd_dv(q, k, v, None, 1, 2, 1, 9, 14, 16, 16, 0.3, True)
     for x, y in zip(a, b):
         np.testing.assert_array_equal(x, y)
+
+
+@pytest.mark.parametrize("name,pin", pins.SINK_PINS, ids=[n for n, _ in pins.SINK_PINS])
+def test_sinks_pins(name, pin):
+    """Per-head sink logits (one more softmax term with a zero value): closed
+    forms and the f64 brute force of that definition."""
+    pin(oracle.fwd_dv)

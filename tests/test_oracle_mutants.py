@@ -72,6 +72,12 @@ MUTANTS = {
     "output_width_uses_D": ("forward_row(c->p, c->rows ? c->rows[t] : t, c->O + t * c->p->Dv,",
                             "forward_row(c->p, c->rows ? c->rows[t] : t, "
                             "c->O + t * (c->p->D < c->p->Dv ? c->p->D : c->p->Dv),"),
+    # sinks: left out of the max, out of the sum, read for the wrong head, or
+    # taken in base-2 units
+    "sink_not_in_max": ("    if (sink > m)\n        m = sink;\n", ""),
+    "sink_not_in_sum": ("    z += expf(sink - m);", "    z += 0.0f * expf(sink - m);"),
+    "sink_of_kv_head": ("p->sinks[(row / p->ql) % p->H]", "p->sinks[(row / p->ql) % p->Hkv]"),
+    "sink_base2": ("    z += expf(sink - m);", "    z += exp2f(sink - m);"),
 }
 
 
@@ -98,7 +104,8 @@ def test_pins_catch_planted_mistake(name):
         fwd, fwd_dv = oracle.bind(path), oracle.bind_dv(path)
         caught = []
         for pin_name, pin, f in ([(n, p, fwd) for n, p in pins.ALL_PINS]
-                                 + [(n, p, fwd_dv) for n, p in pins.DV_PINS]):
+                                 + [(n, p, fwd_dv) for n, p in pins.DV_PINS]
+                                 + [(n, p, fwd_dv) for n, p in pins.SINK_PINS]):
             try:
                 pin(f)
             except (AssertionError, ValueError, FloatingPointError):
