@@ -62,7 +62,7 @@ int train_fwd(const void* q, const void* k, const void* v, const void* mask, int
               int kl, int head_dim, int head_dim_v, float scale, int causal, int window, void* O,
               float* L, void* stream, int n_split = 0, void* workspace = nullptr,
               size_t workspace_bytes = 0, const int64_t* strides = nullptr,
-              int64_t mask_sr = -1) {
+              int64_t mask_sr = -1, const float* sinks = nullptr) {
   if (batch < 0 || ql < 0 || kl < 0 || n_heads < 1 || n_kv_heads < 1) return FA_ERR_BAD_SIZE;
   if (n_heads % n_kv_heads != 0) return FA_ERR_HEAD_GROUPING;
   const int bm = block_m_of(head_dim, head_dim_v);
@@ -98,7 +98,8 @@ int train_fwd(const void* q, const void* k, const void* v, const void* mask, int
   if (rows == 0) return FA_OK;
   const bool kv_used = kl > 0;
   if (!q || !O || !L || (kv_used && (!k || !v))) return FA_ERR_NULL_POINTER;
-  if (!aligned(q, 16) || !aligned(O, 16) || !aligned(L, 4) ||
+  if (sinks && n_split > 0) return FA_ERR_SPLIT;  // (the merge would need the sink once)
+  if (!aligned(q, 16) || !aligned(O, 16) || !aligned(L, 4) || (sinks && !aligned(sinks, 4)) ||
       (kv_used && (!aligned(k, 16) || !aligned(v, 16))) ||
       (mask && !aligned(mask, mask_dtype == FA_MASK_BF16 ? 2 : mask_dtype == FA_MASK_BOOL ? 1 : 4)))
     return FA_ERR_ALIGNMENT;
@@ -112,9 +113,12 @@ int train_fwd(const void* q, const void* k, const void* v, const void* mask, int
   // head, whose stride is G*q_sh; O likewise)
   // (the head strides become row strides, which the kernel holds as int: a
   // head stride beyond that range leaves the heads unpacked)
-  if (ql == 1 && n_heads > n_kv_heads && !mask && window < 0 && st[1] <= 0x7fffffffLL &&
-      st[10] <= 0x7fffffffLL) {
+  // (a sink logit then follows its row: query head g * G + row)
+  int sink_group = 1;
+  if (ql == 1 && n_heads > n_kv_heads && !mask && window < 0 &&
+      st[1] <= 0x7fffffffLL && st[10] <= 0x7fffffffLL) {
     const int G = n_heads / n_kv_heads;
+    sink_group = G;
     ql = G;
     n_heads = n_kv_heads;
     causal = 0;
@@ -167,6 +171,8 @@ int train_fwd(const void* q, const void* k, const void* v, const void* mask, int
   a.n_split = 0;
   a.kchunk = 0;
   a.split_plain = 0;
+  a.sinks = sinks;
+  a.sink_group = sink_group;
   a.ws_o = nullptr;
   a.ws_l = nullptr;
   if (n_split > 0 && kl > 0) {
@@ -350,7 +356,7 @@ int train_fwd_views(const void* q, const long long* q_strides, const void* k,
                     int n_heads, int n_kv_heads, int ql, int kl, int head_dim, int head_dim_v,
                     float scale, int causal, int window, int n_split, void* workspace,
                     unsigned long workspace_bytes, void* O, const long long* o_strides, float* L,
-                    void* stream) {
+                    void* stream, const float* sinks = nullptr) {
   if (n_split < 0 || n_split > kMaxSplit) return FA_ERR_SPLIT;
   if (n_split > 0 && window >= 0) return FA_ERR_WINDOW;
   if (n_split > 0 && mask) return FA_ERR_MASK;  // split-KV takes no mask
@@ -372,7 +378,7 @@ int train_fwd_views(const void* q, const long long* q_strides, const void* k,
     for (int i = 0; i < 3; ++i) st[3 * t + i] = given[t] ? given[t][i] : dflt[t][i];
   return train_fwd(q, k, v, mask, mask_dtype, ms[0], ms[1], batch, n_heads, n_kv_heads, ql, kl,
                    head_dim, dv, scale, causal, window, O, L, stream, n_split, workspace,
-                   workspace_bytes, st, ms[2]);
+                   workspace_bytes, st, ms[2], sinks);
 }
 
 }  // namespace
@@ -396,11 +402,11 @@ extern "C" int fa_train_fwd_dv(const void* q, const long long* q_strides, const 
                                const long long* v_strides, const void* mask, int mask_dtype,
                                const long long* mask_strides, int batch, int n_heads,
                                int n_kv_heads, int ql, int kl, int head_dim, int head_dim_v,
-                               float scale, int causal, int window, void* O,
+                               float scale, int causal, int window, const float* sinks, void* O,
                                const long long* o_strides, float* L, void* stream) {
   return train_fwd_views(q, q_strides, k, k_strides, v, v_strides, mask, mask_dtype,
                          mask_strides, batch, n_heads, n_kv_heads, ql, kl, head_dim, head_dim_v,
-                         scale, causal, window, 0, nullptr, 0, O, o_strides, L, stream);
+                         scale, causal, window, 0, nullptr, 0, O, o_strides, L, stream, sinks);
 }
 
 // The library-held scratch of fa_train_fwd_split_noalloc (split-KV partials

@@ -68,6 +68,9 @@ struct FwdArgs {
   int qt_count;
   int n_precise;   // kMixed: query tiles below this run compensated
   int split_plain; // kSplit: chunks may run plain tiles (else every tile compensated)
+  const float* sinks;  // f32 sink logits (natural log) of the query heads, or null
+  int sink_group;      // 1: head h's sink is sinks[h]; G > 1 (query heads packed as the
+                       // G rows of kv head h): row r's is sinks[h * G + r]
   int causal_off;  // max(kl - ql, 0)
   int window;      // WINDOW variants: keys below q_abs - window are hidden
   int n_split;     // kSplit: key chunks per query tile (grid factor)
@@ -953,10 +956,23 @@ __device__ __forceinline__ bool fwd_tile(const FwdArgs& a, int qtile, int bh, ui
   for (int qb = 0; qb < kQB; ++qb) {
     const int qrow = qw0 + 16 * qb + c16;
     if (write[qb]) {
-      const float lt = l_tot[qb];
+      float lt = l_tot[qb], mu = m_use[qb], osc = 1.0f;
+      if constexpr (!SPLIT) {
+        // a sink logit of the row's head: one more term of the softmax with a
+        // zero value, folded into the max and the sum here (an empty row then
+        // gets O = 0 and L = the sink)
+        if (a.sinks) {
+          const int sh = a.sink_group > 1 ? h * a.sink_group + qrow : h;
+          const float s2 = a.sinks[sh] * kLog2e;
+          const float mf = __builtin_fmaxf(mu, s2);
+          osc = __builtin_amdgcn_exp2f(mu - mf);
+          lt = lt * osc + __builtin_amdgcn_exp2f(s2 - mf);
+          mu = mf;
+        }
+      }
       const bool empty = !(lt > 0.0f);
-      const float inv = empty ? 0.0f : __builtin_amdgcn_rcpf(lt);
-      const float lse = empty ? -INFINITY : (m_use[qb] + __builtin_amdgcn_logf(lt)) * kLn2;
+      const float inv = empty ? 0.0f : __builtin_amdgcn_rcpf(lt) * osc;
+      const float lse = empty ? -INFINITY : (mu + __builtin_amdgcn_logf(lt)) * kLn2;
       if constexpr (SPLIT) {
         // the chunk's partial: O normalised by its own sum (f32), and its L
         const int64_t prow = ((int64_t)split * a.B * a.H + bh) * ql + qrow;

@@ -213,10 +213,11 @@ int fa_train_fwd_strided(const void *q, const long long *q_strides, const void *
 
 /*
  * fa_train_fwd_dv - fa_train_fwd_strided (without split-KV) for a value head
- * dim that may differ from the key head dim, as in the (D, Dv) shapes of the
- * adjacent SDPA page ("nuvec-core 0.3.0", tests/fast.rs,
- * attention_kernels_match_the_fallback: (96, 64) and (192, 128)). The
- * scores use the key width, the weighted sum the value width:
+ * dim that may differ from the key head dim, and with optional attention
+ * sinks, as in the adjacent SDPA page's attention API ("nuvec-core 0.3.0",
+ * tests/fast.rs, attention_kernels_match_the_fallback: (D, Dv) pairs (96, 64)
+ * and (192, 128), and sinks [Hq]). The scores use the key width, the weighted
+ * sum the value width:
  *
  *     s_j = scale * <q[b,h,i,:head_dim], k[b,g,j,:head_dim]> + mask[b,h,i,j]
  *     O[b,h,i,:head_dim_v] = sum_j exp(s_j - L[b,h,i]) * v[b,g,j,:head_dim_v]
@@ -229,17 +230,25 @@ int fa_train_fwd_strided(const void *q, const long long *q_strides, const void *
  *        (64, 64), (80, 80), (96, 96), (96, 64), (128, 128), (192, 192),
  *        (192, 128) or (256, 256); FA_ERR_HEAD_DIM otherwise. NULL strides:
  *        that tensor contiguous in its own head dim.
+ *   sinks f32 [n_heads] (device, read; 4-byte aligned) or NULL: one logit per
+ *        query head, in natural-log units, that joins every row's softmax as
+ *        one more term with a zero value (the SDPA page's `sinks [Hq]`, which
+ *        it passes without defining; this is the reading their name and shape
+ *        fix): L = log(exp(sink_h) + sum_j exp(s_j)), O = sum_j exp(s_j - L) v_j.
+ *        A row with no visible key gets O = +0 and L = sink_h. -inf sinks
+ *        change nothing.
  *   others as for fa_train_fwd_strided (mask, window, L, stream, errors).
  *
- * With head_dim_v == head_dim this is fa_train_fwd_strided with n_split = 0,
- * bit for bit. One kernel launch; allocates nothing; never synchronises.
+ * With head_dim_v == head_dim and no sinks this is fa_train_fwd_strided with
+ * n_split = 0, bit for bit. One kernel launch; allocates nothing; never
+ * synchronises.
  */
 int fa_train_fwd_dv(const void *q, const long long *q_strides, const void *k,
                     const long long *k_strides, const void *v, const long long *v_strides,
                     const void *mask, int mask_dtype, const long long *mask_strides, int batch,
                     int n_heads, int n_kv_heads, int ql, int kl, int head_dim, int head_dim_v,
-                    float scale, int causal, int window, void *O, const long long *o_strides,
-                    float *L, void *stream);
+                    float scale, int causal, int window, const float *sinks, void *O,
+                    const long long *o_strides, float *L, void *stream);
 
 /*
  * fa_train_fwd_split - the forward of fa_train_fwd (no mask, causal or not)

@@ -314,7 +314,7 @@ def test_strided_invalid_arguments_are_rejected(over, code):
 
 DV_GOOD = {k: v for k, v in STRIDED_GOOD.items() if k not in ("n_split", "workspace",
                                                                "workspace_bytes")}
-DV_GOOD.update(head_dim=96, head_dim_v=64)
+DV_GOOD.update(head_dim=96, head_dim_v=64, sinks=0)
 
 
 @pytest.mark.parametrize("over,code", [
@@ -328,6 +328,8 @@ DV_GOOD.update(head_dim=96, head_dim_v=64)
     (dict(causal=0, window=3), 9), (dict(mask=A, mask_dtype=5), 10),
     # O's rows (64 elements) overlap at a row stride of 32
     (dict(o_strides=(4 * 8 * 32, 8 * 32, 32)), 13),
+    # sinks: f32, 4-byte aligned; checked like the other operands
+    (dict(sinks=A + 2), 6), (dict(sinks=A + 2, head_dim=64, head_dim_v=128), 4),
 ])
 def test_dv_invalid_arguments_are_rejected(over, code):
     args = dict(DV_GOOD)
@@ -335,7 +337,8 @@ def test_dv_invalid_arguments_are_rejected(over, code):
     assert fa.fa_train_fwd_dv(**args) == code
 
 
-@pytest.mark.parametrize("over", [dict(batch=0), dict(ql=0, q=0, k=0, v=0, O=0, L=0)])
+@pytest.mark.parametrize("over", [dict(batch=0), dict(ql=0, q=0, k=0, v=0, O=0, L=0),
+                                  dict(batch=0, sinks=A)])
 def test_dv_empty_problems_are_noops(over):
     args = dict(DV_GOOD)
     args.update(over)
