@@ -28,7 +28,9 @@ PEAK_HBM_GBS = 8000.0
 EXTRA_WARMUP = 20
 HEADLINE = ["d64_b8_h16_q4096_k4096_causal", "d256_gqa_b2_h16kv4_q8192_k8192_causal"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SOURCE = os.path.join(ROOT, "flash_attention_forward_fa_amd", "csrc", "fa_fwd.hip")
+# the forward kernel's sources: the stored counters hold only while these are unchanged
+KERNEL_SOURCES = [os.path.join(ROOT, "flash_attention_forward_fa_amd", "csrc", n)
+                  for n in ("fa_fwd_kernel.h", "fa_common.h", "fa_fwd.hip")]
 
 
 def log(*a):
@@ -36,8 +38,12 @@ def log(*a):
 
 
 def kernel_source_hash():
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """sha256[:16] over the forward kernel's source files, in order."""
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def stored_counters(workload):
