@@ -60,7 +60,8 @@ def lib():
                                            pll, vp, vp]
         l.fa_train_fwd_strided.restype = ci
         l.fa_train_fwd_dv.argtypes = [vp, pll, vp, pll, vp, pll, vp, ci, pll, ci, ci, ci, ci, ci,
-                                      ci, ci, ctypes.c_float, ci, ci, vp, vp, pll, vp, vp]
+                                      ci, ci, ctypes.c_float, ci, ci, vp, ci, vp, ctypes.c_ulong,
+                                      vp, pll, vp, vp]
         l.fa_train_fwd_dv.restype = ci
         l.fa_train_bwd_strided.argtypes = [vp, vp, vp, vp, vp, vp, pll, pll, vp, ci, pll, ci, ci,
                                            ci, ci, ci, ci, ctypes.c_float, ci, ci, vp, vp, vp, vp]
@@ -467,20 +468,21 @@ def train_fwd_strided(q, k, v, mask=None, scale=None, causal=False, window=None,
 
 def fa_train_fwd_dv(q, q_strides, k, k_strides, v, v_strides, mask, mask_dtype, mask_strides,
                     batch, n_heads, n_kv_heads, ql, kl, head_dim, head_dim_v, scale, causal,
-                    window, sinks, O, o_strides, L, stream):
+                    window, sinks, n_split, workspace, workspace_bytes, O, o_strides, L, stream):
     """The C entry point with raw integer pointers (0 for NULL) and stride
     triples (or None); returns the status."""
     return lib().fa_train_fwd_dv(
         q or None, _strides3(q_strides), k or None, _strides3(k_strides), v or None,
         _strides3(v_strides), mask or None, int(mask_dtype), _strides3(mask_strides), batch,
         n_heads, n_kv_heads, ql, kl, head_dim, head_dim_v, float(scale), int(bool(causal)),
-        int(window), sinks or None, O or None, _strides3(o_strides), L or None, stream or None)
+        int(window), sinks or None, int(n_split), workspace or None, int(workspace_bytes),
+        O or None, _strides3(o_strides), L or None, stream or None)
 
 
 def train_fwd_dv(q, k, v, mask=None, scale=None, causal=False, window=None, sinks=None,
-                 out=None, lse=None, stream=None):
+                 n_split=0, workspace=None, out=None, lse=None, stream=None):
     """O, L = train_fwd_dv(q, k, v, mask=None, scale=None, causal=False, window=None,
-                           sinks=None)
+                           sinks=None, n_split=0)
 
     The forward with a value head dim Dv that may differ from the key head dim
     D: q [B, H, ql, D], k [B, Hkv, kl, D], v [B, Hkv, kl, Dv], out [B, H, ql, Dv]
@@ -489,7 +491,9 @@ def train_fwd_dv(q, k, v, mask=None, scale=None, causal=False, window=None, sink
     (256, 256). mask, window, scale (default 1/sqrt(D)) as for
     train_fwd_strided; L is contiguous [B, H, ql]. sinks: None or a float32
     tensor [H] on q's device, one logit per query head that joins every row's
-    softmax as one more term with a zero value (include/fa.h).
+    softmax as one more term with a zero value (include/fa.h). n_split > 0
+    runs split-KV (Dv == D in {64, 128, 256}, no mask or window; the
+    workspace allocated here when None).
     """
     import torch
     if not isinstance(q, torch.Tensor):
@@ -511,6 +515,13 @@ def train_fwd_dv(q, k, v, mask=None, scale=None, causal=False, window=None, sink
     _check_out(L, "lse", q.device, torch.float32, (B, H, ql))
     if sinks is not None:
         _check_out(sinks, "sinks", q.device, torch.float32, (H,))
+    ws_bytes = 0
+    if n_split > 0:
+        ws_bytes = fa_train_fwd_split_workspace(B, H, ql, Dv, n_split) if kl > 0 else 0
+        if workspace is None:
+            workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
+        _check_workspace(workspace, ws_bytes, q.device)
+        ws_bytes = workspace.numel()
     s = stream if stream is not None else torch.cuda.current_stream(q.device)
     st = lambda t: t.stride()[:3]
     mptr, mdt, mst = _mask_view(mask, q, k)
@@ -518,8 +529,9 @@ def train_fwd_dv(q, k, v, mask=None, scale=None, causal=False, window=None, sink
         status = fa_train_fwd_dv(
             q.data_ptr(), st(q), k.data_ptr(), st(k), v.data_ptr(), st(v), mptr, mdt, mst,
             B, H, Hkv, ql, kl, D, Dv, scale, causal, -1 if window is None else window,
-            sinks.data_ptr() if sinks is not None else 0, O.data_ptr(), st(O), L.data_ptr(),
-            s.cuda_stream)
+            sinks.data_ptr() if sinks is not None else 0, n_split,
+            workspace.data_ptr() if workspace is not None else 0, ws_bytes, O.data_ptr(), st(O),
+            L.data_ptr(), s.cuda_stream)
     if status != 0:
         raise FAError(status, status_string(status))
     return O, L

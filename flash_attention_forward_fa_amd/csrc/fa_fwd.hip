@@ -98,7 +98,6 @@ int train_fwd(const void* q, const void* k, const void* v, const void* mask, int
   if (rows == 0) return FA_OK;
   const bool kv_used = kl > 0;
   if (!q || !O || !L || (kv_used && (!k || !v))) return FA_ERR_NULL_POINTER;
-  if (sinks && n_split > 0) return FA_ERR_SPLIT;  // (the merge would need the sink once)
   if (!aligned(q, 16) || !aligned(O, 16) || !aligned(L, 4) || (sinks && !aligned(sinks, 4)) ||
       (kv_used && (!aligned(k, 16) || !aligned(v, 16))) ||
       (mask && !aligned(mask, mask_dtype == FA_MASK_BF16 ? 2 : mask_dtype == FA_MASK_BOOL ? 1 : 4)))
@@ -402,11 +401,13 @@ extern "C" int fa_train_fwd_dv(const void* q, const long long* q_strides, const 
                                const long long* v_strides, const void* mask, int mask_dtype,
                                const long long* mask_strides, int batch, int n_heads,
                                int n_kv_heads, int ql, int kl, int head_dim, int head_dim_v,
-                               float scale, int causal, int window, const float* sinks, void* O,
-                               const long long* o_strides, float* L, void* stream) {
+                               float scale, int causal, int window, const float* sinks,
+                               int n_split, void* workspace, unsigned long workspace_bytes,
+                               void* O, const long long* o_strides, float* L, void* stream) {
   return train_fwd_views(q, q_strides, k, k_strides, v, v_strides, mask, mask_dtype,
                          mask_strides, batch, n_heads, n_kv_heads, ql, kl, head_dim, head_dim_v,
-                         scale, causal, window, 0, nullptr, 0, O, o_strides, L, stream, sinks);
+                         scale, causal, window, n_split, workspace, workspace_bytes, O, o_strides,
+                         L, stream, sinks);
 }
 
 // The library-held scratch of fa_train_fwd_split_noalloc (split-KV partials

@@ -1120,6 +1120,8 @@ struct CombineArgs {
   int H, ql;
   int64_t o_sb, o_sh;  // O's element strides of batch, head and row
   int o_sr;
+  const float* sinks;  // sink logits as in FwdArgs (null: none), merged once here
+  int sink_group;
 };
 
 template <int D>
@@ -1141,6 +1143,14 @@ __global__ __launch_bounds__(256) void fa_combine_kernel(CombineArgs c) {
   if (lane == 0) red_m[wave] = m;
   __syncthreads();
   m = fmaxf(fmaxf(red_m[0], red_m[1]), fmaxf(red_m[2], red_m[3]));
+  // the row's sink: one more term of the merged sum with a zero value
+  const int64_t bh = row / c.ql;
+  float sink = -INFINITY;
+  if (c.sinks) {
+    const int h = (int)(bh % c.H);
+    sink = c.sinks[c.sink_group > 1 ? h * c.sink_group + (int)(row % c.ql) : h];
+    m = fmaxf(m, sink);
+  }
   float acc[P] = {};
   float z = 0.0f;
   if (m != -INFINITY) {
@@ -1161,8 +1171,8 @@ __global__ __launch_bounds__(256) void fa_combine_kernel(CombineArgs c) {
   if (wave != 0) return;
   z = (red_z[0] + red_z[1]) + (red_z[2] + red_z[3]);
   const bool empty = m == -INFINITY;
+  if (!empty) z += __builtin_amdgcn_exp2f((sink - m) * kLog2e);
   const float inv = empty ? 0.0f : 1.0f / z;
-  const int64_t bh = row / c.ql;
   uint16_t* orow = c.o + (bh / c.H) * c.o_sb + (bh % c.H) * c.o_sh + (row % c.ql) * c.o_sr +
                    lane * P;
 #pragma unroll
@@ -1232,6 +1242,8 @@ hipError_t dispatch_split(FwdArgs a, hipStream_t stream) {
   c.o_sb = a.o_sb;
   c.o_sh = a.o_sh;
   c.o_sr = a.o_sr;
+  c.sinks = a.sinks;
+  c.sink_group = a.sink_group;
   hipLaunchKernelGGL(fa_combine_kernel<DV>, dim3((unsigned)c.rows), dim3(256), 0, stream, c);
   return hipGetLastError();
 }

@@ -212,9 +212,9 @@ int fa_train_fwd_strided(const void *q, const long long *q_strides, const void *
                          float *L, void *stream);
 
 /*
- * fa_train_fwd_dv - fa_train_fwd_strided (without split-KV) for a value head
- * dim that may differ from the key head dim, and with optional attention
- * sinks, as in the adjacent SDPA page's attention API ("nuvec-core 0.3.0",
+ * fa_train_fwd_dv - fa_train_fwd_strided for a value head dim that may differ
+ * from the key head dim, and with optional attention sinks, as in the
+ * adjacent SDPA page's attention API ("nuvec-core 0.3.0",
  * tests/fast.rs, attention_kernels_match_the_fallback: (D, Dv) pairs (96, 64)
  * and (192, 128), and sinks [Hq]). The scores use the key width, the weighted
  * sum the value width:
@@ -236,18 +236,22 @@ int fa_train_fwd_strided(const void *q, const long long *q_strides, const void *
  *        it passes without defining; this is the reading their name and shape
  *        fix): L = log(exp(sink_h) + sum_j exp(s_j)), O = sum_j exp(s_j - L) v_j.
  *        A row with no visible key gets O = +0 and L = sink_h. -inf sinks
- *        change nothing.
+ *        change nothing. With split-KV the chunks' merge adds the sink once.
+ *   n_split, workspace, workspace_bytes
+ *        0: one launch; >= 1: split-KV as for fa_train_fwd_strided (no mask,
+ *        no window; head_dim_v == head_dim in {64, 128, 256}, else
+ *        FA_ERR_HEAD_DIM).
  *   others as for fa_train_fwd_strided (mask, window, L, stream, errors).
  *
  * With head_dim_v == head_dim and no sinks this is fa_train_fwd_strided with
- * n_split = 0, bit for bit. One kernel launch; allocates nothing; never
- * synchronises.
+ * the same n_split, bit for bit. Allocates nothing; never synchronises.
  */
 int fa_train_fwd_dv(const void *q, const long long *q_strides, const void *k,
                     const long long *k_strides, const void *v, const long long *v_strides,
                     const void *mask, int mask_dtype, const long long *mask_strides, int batch,
                     int n_heads, int n_kv_heads, int ql, int kl, int head_dim, int head_dim_v,
-                    float scale, int causal, int window, const float *sinks, void *O,
+                    float scale, int causal, int window, const float *sinks, int n_split,
+                    void *workspace, unsigned long workspace_bytes, void *O,
                     const long long *o_strides, float *L, void *stream);
 
 /*

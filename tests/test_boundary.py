@@ -312,9 +312,7 @@ def test_strided_invalid_arguments_are_rejected(over, code):
     assert fa.fa_train_fwd_strided(**args) == code
 
 
-DV_GOOD = {k: v for k, v in STRIDED_GOOD.items() if k not in ("n_split", "workspace",
-                                                               "workspace_bytes")}
-DV_GOOD.update(head_dim=96, head_dim_v=64, sinks=0)
+DV_GOOD = dict(STRIDED_GOOD, head_dim=96, head_dim_v=64, sinks=0)
 
 
 @pytest.mark.parametrize("over,code", [
@@ -330,6 +328,15 @@ DV_GOOD.update(head_dim=96, head_dim_v=64, sinks=0)
     (dict(o_strides=(4 * 8 * 32, 8 * 32, 32)), 13),
     # sinks: f32, 4-byte aligned; checked like the other operands
     (dict(sinks=A + 2), 6), (dict(sinks=A + 2, head_dim=64, head_dim_v=128), 4),
+    # split-KV: equal base widths only, no mask or window, a large enough workspace
+    (dict(n_split=2, workspace=A, workspace_bytes=1 << 20), 4),
+    (dict(n_split=2, head_dim=80, head_dim_v=80, workspace=A, workspace_bytes=1 << 20), 4),
+    (dict(n_split=-1, head_dim=64, head_dim_v=64), 11),
+    (dict(n_split=2, head_dim=64, head_dim_v=64, sinks=A, workspace=A, workspace_bytes=16), 11),
+    (dict(n_split=2, head_dim=64, head_dim_v=64, window=3), 9),
+    (dict(n_split=2, head_dim=64, head_dim_v=64, mask=A), 10),
+    (dict(n_split=2, head_dim=64, head_dim_v=64, sinks=A + 2, workspace=A,
+          workspace_bytes=1 << 20), 6),
 ])
 def test_dv_invalid_arguments_are_rejected(over, code):
     args = dict(DV_GOOD)

@@ -188,3 +188,46 @@ def test_sinks_binding_checks():
         fa.train_fwd_dv(q, q, q, sinks=torch.zeros(4, device="cuda:0", dtype=torch.float64))
     with pytest.raises(ValueError):
         fa.train_fwd_dv(q, q, q, sinks=torch.zeros(4))
+
+
+SPLIT_CASES = [
+    # (B, H, Hkv, ql, kl, D, causal, n_split)
+    (1, 8, 1, 1, 1100, 128, False, 8),     # the SDPA page's decode shapes (packed GQA decode)
+    (1, 16, 2, 1, 9000, 128, False, 32),
+    (2, 32, 8, 1, 5000, 64, True, 16),
+    (1, 4, 2, 300, 5000, 64, True, 8),     # prefill against a longer cache
+    (1, 2, 1, 300, 200, 64, True, 3),      # ql > kl: chunks no row sees (L_c = -inf)
+    (1, 2, 1, 257, 1000, 256, False, 4),
+    (1, 2, 2, 17, 900, 128, True, 4),
+]
+
+
+@pytest.mark.parametrize("B,H,Hkv,ql,kl,D,causal,n_split", SPLIT_CASES)
+def test_sinks_split_kv(B, H, Hkv, ql, kl, D, causal, n_split):
+    """Split-KV with sinks: the chunks' merge adds each row's sink once."""
+    import torch
+    seed = fagen.SEED_BASE + 0xE00 + ql + kl + D + n_split
+    q, k, v = _inputs(seed, B, H, Hkv, ql, kl, D, D)
+    s = _sinks(seed, H, kl)
+    case = f"sinks split {(B, H, Hkv, ql, kl, D, causal, n_split)}"
+    print(f"case {case}", flush=True)
+    dev = "cuda:0"
+    tq, tk, tv = gu.to_dev(q, dev), gu.to_dev(k, dev), gu.to_dev(v, dev)
+    ts = torch.from_numpy(s).to(dev)
+    O, L = fa.train_fwd_dv(tq, tk, tv, causal=causal, sinks=ts, n_split=n_split)
+    O0, L0 = fa.train_fwd_dv(tq, tk, tv, causal=causal, n_split=n_split)
+    neg = torch.full((H,), -math.inf, dtype=torch.float32, device=dev)
+    On, Ln = fa.train_fwd_dv(tq, tk, tv, causal=causal, sinks=neg, n_split=n_split)
+    torch.cuda.synchronize()
+    bits = O.view(torch.int16).cpu().numpy().view(np.uint16)
+    of, ob, lr = oracle.fwd_dv(q, k, v, None, B, H, Hkv, ql, kl, D, D, 1.0 / math.sqrt(D), causal,
+                               sinks=s)
+    tol_o, tol_l = gu.tolerances(kl)
+    eo, el, rms = gu.compare(gu.widen(bits), L.cpu().numpy(), bits, ob, lr, tol_o, tol_l,
+                             label=case, o_ref_f32=of)
+    print(f"{case}: dO={eo:.3e} dL={el:.3e} relRMS={rms:.2e}")
+    # -inf sinks: the bits of the same split without sinks
+    assert torch.equal(On.view(torch.int16), O0.view(torch.int16))
+    assert torch.equal(Ln, L0)
+    # the sinks moved L (they sit near the rows' key mass)
+    assert float((L - L0).abs().max()) > 0.1
