@@ -76,7 +76,7 @@ def lib():
         l.fa_train_fwd_split_workspace.argtypes = [ci, ci, ci, ci, ci]
         l.fa_train_fwd_split_workspace.restype = ul
         l.fa_paged_fwd.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, ci, ci,
-                                   ctypes.c_float, ci, ci, vp, ul, vp, vp, vp]
+                                   ctypes.c_float, ci, vp, ci, vp, ul, vp, vp, vp]
         l.fa_paged_fwd.restype = ci
         l.fa_train_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci,
                                    ctypes.c_float, ci, vp, vp, vp, vp]
@@ -308,27 +308,28 @@ def train_fwd_split(q, k, v, n_split, scale=None, causal=False, workspace=None, 
 
 
 def fa_paged_fwd(q, k_cache, v_cache, block_table, seq_lens, batch, n_heads, n_kv_heads, ql,
-                 n_blocks, block_size, max_blocks, head_dim, scale, causal, n_split, workspace,
-                 workspace_bytes, O, L, stream):
+                 n_blocks, block_size, max_blocks, head_dim, scale, causal, sinks, n_split,
+                 workspace, workspace_bytes, O, L, stream):
     """The C entry point with raw integer pointers (0 for NULL); returns the status."""
     return lib().fa_paged_fwd(q or None, k_cache or None, v_cache or None, block_table or None,
                               seq_lens or None, batch, n_heads, n_kv_heads, ql, n_blocks,
                               block_size, max_blocks, head_dim, float(scale), int(bool(causal)),
-                              int(n_split), workspace or None, int(workspace_bytes), O or None,
-                              L or None, stream or None)
+                              sinks or None, int(n_split), workspace or None,
+                              int(workspace_bytes), O or None, L or None, stream or None)
 
 
 def paged_fwd(q, k_cache, v_cache, block_table, seq_lens, scale=None, causal=False, n_split=0,
-              workspace=None, out=None, lse=None, stream=None):
+              workspace=None, sinks=None, out=None, lse=None, stream=None):
     """O, L = paged_fwd(q, k_cache, v_cache, block_table, seq_lens, scale=None, causal=False,
-                        n_split=0, workspace=None)
+                        n_split=0, workspace=None, sinks=None)
 
     q: bf16 [B, H, ql, D]; k_cache, v_cache: bf16 [n_blocks, Hkv, block_size, D]
     (block_size a positive multiple of 16);
     block_table: int32 [B, max_blocks]; seq_lens: int32 [B] (all on q's GPU).
     Sequence b attends to its first seq_lens[b] keys (key position p at row
     p % block_size of block block_table[b, p // block_size]). n_split > 0 uses
-    split-KV with a workspace (allocated here when None).
+    split-KV with a workspace (allocated here when None). sinks: None or a
+    float32 tensor [H] on q's device, as for train_fwd_dv.
     """
     import torch
 
@@ -352,6 +353,8 @@ def paged_fwd(q, k_cache, v_cache, block_table, seq_lens, scale=None, causal=Fal
     L = lse if lse is not None else torch.empty((B, H, ql), dtype=torch.float32, device=q.device)
     _check_out(O, "out", q.device, torch.bfloat16, (B, H, ql, D))
     _check_out(L, "lse", q.device, torch.float32, (B, H, ql))
+    if sinks is not None:
+        _check_out(sinks, "sinks", q.device, torch.float32, (H,))
     ws_ptr, ws_bytes = 0, 0
     if n_split > 0:
         # (a table that addresses no keys needs no workspace)
@@ -364,7 +367,8 @@ def paged_fwd(q, k_cache, v_cache, block_table, seq_lens, scale=None, causal=Fal
     with torch.cuda.device(q.device):
         status = fa_paged_fwd(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
                               block_table.data_ptr(), seq_lens.data_ptr(), B, H, Hkv, ql,
-                              n_blocks, bs, max_blocks, D, scale, causal, n_split, ws_ptr,
+                              n_blocks, bs, max_blocks, D, scale, causal,
+                              sinks.data_ptr() if sinks is not None else 0, n_split, ws_ptr,
                               ws_bytes, O.data_ptr(), L.data_ptr(), s.cuda_stream)
     if status != 0:
         raise FAError(status, status_string(status))

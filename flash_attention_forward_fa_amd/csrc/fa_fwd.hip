@@ -260,8 +260,9 @@ extern "C" int fa_train_fwd_split(const void* q, const void* k, const void* v, i
 extern "C" int fa_paged_fwd(const void* q, const void* k_cache, const void* v_cache,
                             const int* block_table, const int* seq_lens, int batch, int n_heads,
                             int n_kv_heads, int ql, int n_blocks, int block_size, int max_blocks,
-                            int head_dim, float scale, int causal, int n_split, void* workspace,
-                            unsigned long workspace_bytes, void* O, float* L, void* stream) {
+                            int head_dim, float scale, int causal, const float* sinks,
+                            int n_split, void* workspace, unsigned long workspace_bytes, void* O,
+                            float* L, void* stream) {
   if (batch < 0 || ql < 0 || n_heads < 1 || n_kv_heads < 1 || max_blocks < 0 || n_blocks < 0)
     return FA_ERR_BAD_SIZE;
   if (n_heads % n_kv_heads != 0) return FA_ERR_HEAD_GROUPING;
@@ -277,14 +278,17 @@ extern "C" int fa_paged_fwd(const void* q, const void* k_cache, const void* v_ca
   if (!q || !O || !L || !seq_lens || (cap > 0 && (!k_cache || !v_cache || !block_table)))
     return FA_ERR_NULL_POINTER;
   if (!aligned(q, 16) || !aligned(O, 16) || !aligned(L, 4) || !aligned(seq_lens, 4) ||
+      (sinks && !aligned(sinks, 4)) ||
       (cap > 0 && (!aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(block_table, 4))))
     return FA_ERR_ALIGNMENT;
-  // decoding: a kv group's query heads as the rows of one head (as in train_fwd)
-  int H = n_heads, qlen = ql, cz = causal;
+  // decoding: a kv group's query heads as the rows of one head (as in train_fwd;
+  // row r of packed head g takes query head g * G + r's sink)
+  int H = n_heads, qlen = ql, cz = causal, sink_group = 1;
   if (ql == 1 && n_heads > n_kv_heads) {
     qlen = n_heads / n_kv_heads;
     H = n_kv_heads;
     cz = 0;
+    sink_group = qlen;
   }
   const int bm = block_m_of(head_dim, head_dim);
   const int64_t n_qtiles = ((int64_t)qlen + bm - 1) / bm;
@@ -315,6 +319,8 @@ extern "C" int fa_paged_fwd(const void* q, const void* k_cache, const void* v_ca
   a.max_blocks = max_blocks;
   a.block_size = block_size;
   a.n_blocks = n_blocks;
+  a.sinks = sinks;
+  a.sink_group = sink_group;
   if (n_split > 0 && cap > 0) {
     const int64_t per = (cap + n_split - 1) / n_split;
     const int64_t kchunk = (per + 63) / 64 * 64;

@@ -362,7 +362,11 @@ int fa_train_fwd_split_noalloc(const void *q, const void *k, const void *v, int 
  *   n_split     0: one launch; >= 1: split-KV with workspace (as for
  *               fa_train_fwd_split, chunks of max_blocks*block_size keys;
  *               workspace size from fa_train_fwd_split_workspace)
- *   O, L        as for fa_train_fwd (a sequence with no key: O = 0, L = -inf)
+ *   sinks       f32 [n_heads] sink logits (device, read; 4-byte aligned) or
+ *               NULL, as for fa_train_fwd_dv (one more softmax term per query
+ *               head with a zero value; with split-KV the merge adds it once)
+ *   O, L        as for fa_train_fwd (a sequence with no key: O = 0, and L =
+ *               -inf, or the head's sink)
  *   head_dim    64, 128 or 256 (FA_ERR_HEAD_DIM otherwise)
  *   others      as for fa_train_fwd; no mask, no window.
  *
@@ -374,8 +378,8 @@ int fa_train_fwd_split_noalloc(const void *q, const void *k, const void *v, int 
 int fa_paged_fwd(const void *q, const void *k_cache, const void *v_cache, const int *block_table,
                  const int *seq_lens, int batch, int n_heads, int n_kv_heads, int ql, int n_blocks,
                  int block_size, int max_blocks, int head_dim, float scale, int causal,
-                 int n_split, void *workspace, unsigned long workspace_bytes, void *O, float *L,
-                 void *stream);
+                 const float *sinks, int n_split, void *workspace, unsigned long workspace_bytes,
+                 void *O, float *L, void *stream);
 
 /*
  * fa_train_bwd - enqueue the training backward pass of the same attention.

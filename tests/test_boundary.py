@@ -245,8 +245,8 @@ def test_suggest_n_split():
 
 PAGED_GOOD = dict(q=A, k_cache=A, v_cache=A, block_table=A, seq_lens=A, batch=2, n_heads=4,
                   n_kv_heads=2, ql=1, n_blocks=8, block_size=64, max_blocks=4, head_dim=128,
-                  scale=0.1, causal=1, n_split=0, workspace=0, workspace_bytes=0, O=A, L=A,
-                  stream=0)
+                  scale=0.1, causal=1, sinks=0, n_split=0, workspace=0, workspace_bytes=0, O=A,
+                  L=A, stream=0)
 
 
 def _call_paged(**over):
@@ -262,7 +262,7 @@ def _call_paged(**over):
     (dict(head_dim=80), 4), (dict(n_heads=3), 3), (dict(scale=math.inf), 5),
     (dict(max_blocks=-1), 2), (dict(n_blocks=-1), 2), (dict(n_split=-1), 11),
     (dict(n_split=4), 1), (dict(n_split=4, workspace=A, workspace_bytes=16), 11),
-    (dict(max_blocks=1 << 25, block_size=128), 7),
+    (dict(max_blocks=1 << 25, block_size=128), 7), (dict(sinks=A + 2), 6),
 ])
 def test_paged_invalid_arguments_are_rejected(over, code):
     assert _call_paged(**over) == code

@@ -37,7 +37,7 @@ def _paged(keys, values, bs, seed):
     return kc, vc, table
 
 
-def _run(case, n_split, seed):
+def _run(case, n_split, seed, with_sinks=False):
     import torch
     import flash_attention_forward_fa_amd as fa
     B, H, Hkv, ql, D, bs, lens, causal = case
@@ -48,18 +48,24 @@ def _run(case, n_split, seed):
     values = fagen.normal_bf16(s, 2, (B, Hkv, N, D))
     kc, vc, table = _paged(keys, values, bs, seed)
     dev = "cuda:0"
+    # sinks: log(longest sequence) + N(0, 2^2), rounded through bf16
+    sinks = None
+    if with_sinks:
+        z = fagen.bf16_bits_to_f32(fagen.normal_bf16(s, 5, (H,), sigma=2.0))
+        sinks = (np.float32(math.log(N)) + z).astype(np.float32)
     O, L = fa.paged_fwd(gu.to_dev(q, dev), gu.to_dev(kc, dev), gu.to_dev(vc, dev),
                         torch.from_numpy(table).to(dev),
                         torch.tensor(lens, dtype=torch.int32, device=dev), causal=causal,
-                        n_split=n_split)
+                        n_split=n_split,
+                        sinks=None if sinks is None else torch.from_numpy(sinks).to(dev))
     torch.cuda.synchronize()
     bits = O.view(torch.int16).cpu().numpy().view(np.uint16)
     o, l = gu.widen(bits), L.cpu().numpy()
     scale = 1.0 / math.sqrt(D)
     for b, n in enumerate(lens):
-        of, ob, lr = oracle.fwd(q[b:b + 1], keys[b:b + 1, :, :n].copy(),
-                               values[b:b + 1, :, :n].copy(), None, 1, H, Hkv, ql, n, D, scale,
-                               causal)
+        of, ob, lr = oracle.fwd_dv(q[b:b + 1], keys[b:b + 1, :, :n].copy(),
+                                   values[b:b + 1, :, :n].copy(), None, 1, H, Hkv, ql, n, D, D,
+                                   scale, causal, sinks=sinks)
         tol_o, tol_l = gu.tolerances(n)
         eo, el, _ = gu.compare(o[b:b + 1], l[b:b + 1], bits[b:b + 1], ob, lr, tol_o, tol_l,
                                f"paged {case} seq {b}", o_ref_f32=of)
@@ -96,6 +102,16 @@ CASES = [
 def test_paged_matches_contiguous_oracle(case, n_split):
     print(f"case paged {case} n_split={n_split}", flush=True)
     _run(case, n_split, seed=11000 + CASES.index(case))
+
+
+@pytest.mark.parametrize("n_split", [0, 8])
+@pytest.mark.parametrize("case", [CASES[i] for i in (1, 3, 7, 9, 12, 15, 17)],
+                         ids=[str(i) for i in (1, 3, 7, 9, 12, 15, 17)])
+def test_paged_sinks_match_contiguous_oracle(case, n_split):
+    """Sinks through the paged forward (packed GQA decode, prefill, a sequence
+    with no key: O = +0 and L = its head's sink), plain and split-KV."""
+    print(f"case paged sinks {case} n_split={n_split}", flush=True)
+    _run(case, n_split, seed=11500 + CASES.index(case), with_sinks=True)
 
 
 @pytest.mark.parametrize("D", [64, 128, 256])
