@@ -46,6 +46,30 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
+def device_info(dev_index):
+    """The GPU's own figures (HIP device attributes): compute units, peak
+    clock, and the dense bf16 MFMA peak they give at 4096 FLOP per clock and
+    CU; the published peak stays the roofline's. None where HIP is not found."""
+    import ctypes
+    import torch
+    p = torch.cuda.get_device_properties(dev_index)
+    out = {"name": p.name, "arch": getattr(p, "gcnArchName", None),
+           "compute_units": p.multi_processor_count, "l2_bytes": getattr(p, "L2_cache_size", None),
+           "hbm_bytes": p.total_memory}
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+        v = ctypes.c_int(0)
+        # hipDeviceAttributeClockRate (peak clock, kHz) is attribute 5 in
+        # hip_runtime_api.h's hipDeviceAttribute_t
+        if hip.hipDeviceGetAttribute(ctypes.byref(v), 5, dev_index) == 0 and v.value > 0:
+            out["peak_clock_mhz"] = v.value / 1e3
+            out["bf16_peak_from_device_tflops"] = (p.multi_processor_count * v.value * 1e3 * 4096
+                                                   / 1e12)
+    except OSError:
+        pass
+    return out
+
+
 def stored_counters(workload):
     """rocprofv3 --pmc figures of the workload's forward launch (HBM bytes from
     FETCH_SIZE/WRITE_SIZE, MFMA/VALU/LDS activity from the SQ counters), if they
@@ -424,6 +448,7 @@ def main():
                    "parallelism": "none (one GPU)"},
         "per_workload": per,
         "roofline": roofline,
+        "device": device_info(dev.index if dev.index is not None else 0),
     }
     if bwd:
         result["backward"] = bwd

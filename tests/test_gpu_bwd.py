@@ -37,6 +37,9 @@ CASES = [
     ("d128_gqa_causal", 2, 8, 2, 300, 300, 128, True, None),
     ("d128_masked", 1, 2, 1, 96, 200, 128, False, "random"),
     ("d128_long", 1, 2, 1, 1024, 1024, 128, True, None),
+    # the SDPA page's gradient check ("nuvec-core 0.3.0", tests/fast.rs, the
+    # attention vjp): 4 query heads on 2 kv heads, 40 x 40, head_dim 64, causal
+    ("sdpa_page_vjp", 1, 4, 2, 40, 40, 64, True, None),
 ]
 
 
