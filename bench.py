@@ -314,8 +314,8 @@ def main():
     # Few query tiles against a long KV cache (head_dim 128, 32 query
     # heads on 8 kv heads, causal): prefill of 512 tokens and decoding 1 token
     # (batch 1 and 8) against 32768 keys, the plain launch against the split-KV
-    # one (suggest_n_split chunks), and for decoding also the same keys in a
-    # block-paged cache (fa_paged_fwd); not part of the headline metric. FLOP:
+    # one (suggest_n_split chunks), and the same keys in a block-paged cache
+    # (fa_paged_fwd, same chunks); not part of the headline metric. FLOP:
     # 4*D per visible score; K+V GB/s: the cache's bytes over the call's time.
     split_kv = {}
     if args.split_steps > 0:
@@ -354,39 +354,39 @@ def main():
                 res[f"{label}_ms_avg"] = ms
                 res[f"{label}_tflops"] = flop / (ms * 1e-3) / 1e12
                 res[f"{label}_kv_gbs"] = res["kv_bytes"] / (ms * 1e-3) / 1e9
-            if ql == 1:
-                # the same keys in a block-paged cache (blocks of 64 and of 16
-                # keys in a seeded shuffled order), read through fa_paged_fwd
-                # with the same chunks
-                for bs, tag in ((64, "paged_split"), (16, "paged16_split")):
-                    per = kl // bs
-                    order = torch.from_numpy(np.random.default_rng(ql + B).permutation(B * per)
-                                             .astype(np.int64)).to(dev)
-                    kc = torch.empty((B * per, w.Hkv, bs, w.D), dtype=torch.bfloat16, device=dev)
-                    vc = torch.empty_like(kc)
-                    kc[order] = k.view(B, w.Hkv, per, bs, w.D).permute(0, 2, 1, 3, 4).reshape(
-                        B * per, w.Hkv, bs, w.D)
-                    vc[order] = v.view(B, w.Hkv, per, bs, w.D).permute(0, 2, 1, 3, 4).reshape(
-                        B * per, w.Hkv, bs, w.D)
-                    table = order.view(B, per).to(torch.int32)
-                    lens = torch.full((B,), kl, dtype=torch.int32, device=dev)
-                    call = lambda: fa.paged_fwd(q, kc, vc, table, lens, scale=w.scale,
-                                                causal=True, n_split=n_split, workspace=ws,
-                                                out=O, lse=L)
-                    for _ in range(EXTRA_WARMUP):
-                        call()
-                    torch.cuda.synchronize()
-                    a = torch.cuda.Event(enable_timing=True)
-                    b = torch.cuda.Event(enable_timing=True)
-                    a.record(stream)
-                    for _ in range(args.split_steps):
-                        call()
-                    b.record(stream)
-                    torch.cuda.synchronize()
-                    ms = a.elapsed_time(b) / args.split_steps
-                    res[f"{tag}_ms_avg"] = ms
-                    res[f"{tag}_kv_gbs"] = res["kv_bytes"] / (ms * 1e-3) / 1e9
-                    del kc, vc, table, lens
+            # the same keys in a block-paged cache (blocks of 64 and of 16
+            # keys in a seeded shuffled order), read through fa_paged_fwd
+            # with the same chunks
+            for bs, tag in ((64, "paged_split"), (16, "paged16_split")):
+                per = kl // bs
+                order = torch.from_numpy(np.random.default_rng(ql + B).permutation(B * per)
+                                         .astype(np.int64)).to(dev)
+                kc = torch.empty((B * per, w.Hkv, bs, w.D), dtype=torch.bfloat16, device=dev)
+                vc = torch.empty_like(kc)
+                kc[order] = k.view(B, w.Hkv, per, bs, w.D).permute(0, 2, 1, 3, 4).reshape(
+                    B * per, w.Hkv, bs, w.D)
+                vc[order] = v.view(B, w.Hkv, per, bs, w.D).permute(0, 2, 1, 3, 4).reshape(
+                    B * per, w.Hkv, bs, w.D)
+                table = order.view(B, per).to(torch.int32)
+                lens = torch.full((B,), kl, dtype=torch.int32, device=dev)
+                call = lambda: fa.paged_fwd(q, kc, vc, table, lens, scale=w.scale,
+                                            causal=True, n_split=n_split, workspace=ws,
+                                            out=O, lse=L)
+                for _ in range(EXTRA_WARMUP):
+                    call()
+                torch.cuda.synchronize()
+                a = torch.cuda.Event(enable_timing=True)
+                b = torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                for _ in range(args.split_steps):
+                    call()
+                b.record(stream)
+                torch.cuda.synchronize()
+                ms = a.elapsed_time(b) / args.split_steps
+                res[f"{tag}_ms_avg"] = ms
+                res[f"{tag}_tflops"] = flop / (ms * 1e-3) / 1e12
+                res[f"{tag}_kv_gbs"] = res["kv_bytes"] / (ms * 1e-3) / 1e9
+                del kc, vc, table, lens
             split_kv[name] = res
             log(f"{name}: plain {res['plain_ms_avg'] * 1e3:.1f} us, split({n_split}) "
                 f"{res['split_ms_avg'] * 1e3:.1f} us ({res['split_tflops']:.1f} TFLOP/s, "

@@ -321,6 +321,10 @@ extern "C" int fa_paged_fwd(const void* q, const void* k_cache, const void* v_ca
   a.n_blocks = n_blocks;
   a.sinks = sinks;
   a.sink_group = sink_group;
+  // plain tiles where a sequence's rows see enough keys (decided per sequence,
+  // query tile and chunk in the kernel), for scales whose pre-scaled Q stays in
+  // bf16's normal range
+  a.split_plain = a.c >= kPlainMinC && a.c <= kPlainMaxC;
   if (n_split > 0 && cap > 0) {
     const int64_t per = (cap + n_split - 1) / n_split;
     const int64_t kchunk = (per + 63) / 64 * 64;

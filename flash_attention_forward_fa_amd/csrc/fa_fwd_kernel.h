@@ -67,7 +67,8 @@ struct FwdArgs {
   int qt_base;     // this launch computes query tiles [qt_base, qt_base + qt_count)
   int qt_count;
   int n_precise;   // kMixed: query tiles below this run compensated
-  int split_plain; // kSplit: chunks may run plain tiles (else every tile compensated)
+  int split_plain; // split-KV and paged: chunks (or, unsplit, the key range of a paged
+                   // sequence) may run plain tiles; else every tile compensated
   const float* sinks;  // f32 sink logits (natural log) of the query heads, or null
   int sink_group;      // 1: head h's sink is sinks[h]; G > 1 (query heads packed as the
                        // G rows of kv head h): row r's is sinks[h * G + r]
@@ -198,8 +199,7 @@ __device__ __forceinline__ bool fwd_tile(const FwdArgs& a, int qtile, int bh, ui
   static_assert(!SPLIT || (!WINDOW && MASK == kNoMask), "split-KV partials: unmasked, no window");
   static_assert(!SPLIT || PAGED || QBX == 0 || PRECISE,
                 "the decoding split kernels run compensated");
-  static_assert(!PAGED || (PRECISE && !REDO && !WINDOW && MASK == kNoMask),
-                "paged KV: compensated, unmasked, no window");
+  static_assert(!PAGED || (!WINDOW && MASK == kNoMask), "paged KV: unmasked, no window");
   static_assert((!SPLIT && !PAGED) || (DK == DV && !kPanels<DK>),
                 "split-KV and paged: head dims 64, 128 and 256");
   constexpr int BN = Cfg<DK, DV>::BN;
@@ -1064,41 +1064,42 @@ __attribute__((amdgpu_waves_per_eu(MODE == kMixed ? Cfg<DK, DV>::WPE : 2))) void
       fwd_tile<DK, DV, CAUSAL, WINDOW, kNoMask, true, true>(a, qtile, bh, FA_TILE_BUFFERS, redo,
                                                             wg_flags);
     }
-  } else if constexpr (MODE == kSplit) {
-    // A chunk of a query tile runs compensated when some of its rows see 1 to
-    // kPreciseKeys - 1 of the chunk's keys (by position, as the mixed kernel's
-    // short tiles), or when plain tiles are off for the problem; otherwise
-    // plain, with the compensated redo of rows with some |O| >= 1.
+  } else if constexpr (MODE >= kSplit && MODE <= kPagedBlocksSplit) {
+    // Split-KV and paged: a chunk of a query tile (unsplit paged: the
+    // sequence's whole key range) runs compensated when some of its rows see 1
+    // to kPreciseKeys - 1 of its keys (by position, as the mixed kernel's short
+    // tiles), when the problem (a paged sequence) has at most kPlainMinKeys
+    // keys, or when plain tiles are off for the call; otherwise plain, with the
+    // compensated redo of rows with some |O| >= 1. The decoding kernels (QBX)
+    // stay compensated.
+    constexpr bool SP = SPLIT_GRID;
+    constexpr bool PG = MODE != kSplit;
+    constexpr bool SB = MODE == kPagedBlocks || MODE == kPagedBlocksSplit;
     bool precise = true;
     if constexpr (QBX == 0) {
-      const int c0 = split * a.kchunk, c1 = min(c0 + a.kchunk, a.kl);
+      // (paged: the sequence's own key count and causal offset, as fwd_tile
+      // takes them)
+      const int kl = PG ? min(max(load_uniform(a.seq_lens, bh / a.H), 0),
+                              a.max_blocks * a.block_size)
+                        : a.kl;
+      const int off = PG ? max(kl - a.ql, 0) : a.causal_off;
+      const int c0 = SP ? split * a.kchunk : 0, c1 = SP ? min(c0 + a.kchunk, kl) : kl;
       constexpr int kBM = block_m<DK, DV>();
       const int r0 = qtile * kBM, r1 = min(r0 + kBM, a.ql) - 1;
-      const int n_first = max(0, (CAUSAL ? min(c1, a.causal_off + r0 + 1) : c1) - c0);
-      const int n_last = max(0, (CAUSAL ? min(c1, a.causal_off + r1 + 1) : c1) - c0);
-      precise = !a.split_plain || (n_first < kPreciseKeys && n_last >= 1);
+      const int n_first = max(0, (CAUSAL ? min(c1, off + r0 + 1) : c1) - c0);
+      const int n_last = max(0, (CAUSAL ? min(c1, off + r1 + 1) : c1) - c0);
+      precise = !a.split_plain || (PG && kl <= kPlainMinKeys) ||
+                (n_first < kPreciseKeys && n_last >= 1);
     }
     if (precise) {
-      fwd_tile<DK, DV, CAUSAL, false, kNoMask, true, false, true, false, false, QBX>(
+      fwd_tile<DK, DV, CAUSAL, false, kNoMask, true, false, SP, PG, SB, QBX>(
           a, qtile, bh, FA_TILE_BUFFERS, redo, wg_flags, split);
     } else if constexpr (QBX == 0) {
-      if (fwd_tile<DK, DV, CAUSAL, false, kNoMask, false, false, true>(
+      if (fwd_tile<DK, DV, CAUSAL, false, kNoMask, false, false, SP, PG, SB>(
               a, qtile, bh, FA_TILE_BUFFERS, redo, wg_flags, split))
-        fwd_tile<DK, DV, CAUSAL, false, kNoMask, true, true, true>(a, qtile, bh, FA_TILE_BUFFERS,
-                                                                   redo, wg_flags, split);
+        fwd_tile<DK, DV, CAUSAL, false, kNoMask, true, true, SP, PG, SB>(
+            a, qtile, bh, FA_TILE_BUFFERS, redo, wg_flags, split);
     }
-  } else if constexpr (MODE == kPaged) {
-    fwd_tile<DK, DV, CAUSAL, false, kNoMask, true, false, false, true>(
-        a, qtile, bh, FA_TILE_BUFFERS, redo, wg_flags);
-  } else if constexpr (MODE == kPagedSplit) {
-    fwd_tile<DK, DV, CAUSAL, false, kNoMask, true, false, true, true, false, QBX>(
-        a, qtile, bh, FA_TILE_BUFFERS, redo, wg_flags, split);
-  } else if constexpr (MODE == kPagedBlocks) {
-    fwd_tile<DK, DV, CAUSAL, false, kNoMask, true, false, false, true, true>(
-        a, qtile, bh, FA_TILE_BUFFERS, redo, wg_flags);
-  } else if constexpr (MODE == kPagedBlocksSplit) {
-    fwd_tile<DK, DV, CAUSAL, false, kNoMask, true, false, true, true, true, QBX>(
-        a, qtile, bh, FA_TILE_BUFFERS, redo, wg_flags, split);
   } else {
     fwd_tile<DK, DV, CAUSAL, WINDOW, MASK, true, false>(a, qtile, bh, FA_TILE_BUFFERS, redo,
                                                         wg_flags);

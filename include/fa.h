@@ -370,7 +370,9 @@ int fa_train_fwd_split_noalloc(const void *q, const void *k, const void *v, int 
  *   head_dim    64, 128 or 256 (FA_ERR_HEAD_DIM otherwise)
  *   others      as for fa_train_fwd; no mask, no window.
  *
- * Every tile runs the compensated P.V product. Returns FA_ERR_PAGED for a bad
+ * Sequences of more than 256 keys run plain tiles where every row of a query
+ * tile (chunk) sees none or at least 128 of the keys, as fa_train_fwd does.
+ * Returns FA_ERR_PAGED for a bad
  * block_size or an empty cache behind a non-empty table, FA_ERR_SPLIT as for
  * fa_train_fwd_split, otherwise the statuses of fa_train_fwd. Never
  * synchronises, allocates nothing.

@@ -5,7 +5,8 @@ block order with a few unused blocks, a block table, a key count per
 sequence): the paged result must equal attention over each sequence's first
 seq_lens[b] keys, which the oracle computes from the contiguous keys. Bounds
 as for the plain forward (by each sequence's key count); a sequence with no
-key gives O = +0 and L = -inf exactly.
+key gives O = +0 and L = -inf exactly. Sequences of more than 256 keys run
+plain tiles (with the compensated redo) where the accuracy rule allows.
 """
 import math
 
@@ -102,6 +103,51 @@ CASES = [
 def test_paged_matches_contiguous_oracle(case, n_split):
     print(f"case paged {case} n_split={n_split}", flush=True)
     _run(case, n_split, seed=11000 + CASES.index(case))
+
+
+@pytest.mark.parametrize("n_split", [0, 6])
+@pytest.mark.parametrize("D", [64, 128, 256])
+def test_paged_plain_tiles_and_redo(D, n_split):
+    """Sequences of more than 256 keys run plain tiles (pre-scaled Q, bf16 P)
+    where every row of a tile (chunk) sees none or at least 128 of its keys.
+    V times 4 (exact in bf16) at scale 1 concentrates the softmax so that
+    many rows reach |O| >= 1 and take the compensated redo; a 200-key sequence
+    stays compensated. Every row against the oracle."""
+    import torch
+    import flash_attention_forward_fa_amd as fa
+    B, H, Hkv, ql, bs = 3, 4, 2, 200, 64
+    lens = [1500, 200, 700]
+    N = max(lens)
+    s = fagen.SEED_BASE + 11900 + D + n_split
+    print(f"case paged plain/redo D={D} n_split={n_split}", flush=True)
+    q = fagen.normal_bf16(s, 0, (B, H, ql, D))
+    keys = fagen.normal_bf16(s, 1, (B, Hkv, N, D))
+    vb = fagen.normal_bf16(s, 2, (B, Hkv, N, D))
+    e = (vb >> 7) & 0xFF
+    assert np.all(e < 250)
+    values = np.where(e != 0, vb + np.uint16(2 << 7), vb).astype(np.uint16)  # exponent + 2
+    kc, vc, table = _paged(keys, values, bs, 11900 + D)
+    dev = "cuda:0"
+    O, L = fa.paged_fwd(gu.to_dev(q, dev), gu.to_dev(kc, dev), gu.to_dev(vc, dev),
+                        torch.from_numpy(table).to(dev),
+                        torch.tensor(lens, dtype=torch.int32, device=dev), scale=1.0,
+                        causal=True, n_split=n_split)
+    torch.cuda.synchronize()
+    bits = O.view(torch.int16).cpu().numpy().view(np.uint16)
+    o, l = gu.widen(bits), L.cpu().numpy()
+    big = 0
+    for b, n in enumerate(lens):
+        of, ob, lr = oracle.fwd(q[b:b + 1], keys[b:b + 1, :, :n].copy(),
+                               values[b:b + 1, :, :n].copy(), None, 1, H, Hkv, ql, n, D, 1.0,
+                               True)
+        big += int((np.abs(of) >= 1).any(axis=-1).sum())
+        tol_o, tol_l = gu.tolerances(n)
+        eo, el, rms = gu.compare(o[b:b + 1], l[b:b + 1], bits[b:b + 1], ob, lr, tol_o, tol_l,
+                                 f"paged plain D={D} seq {b}", o_ref_f32=of)
+        print(f"paged plain/redo D={D} n_split={n_split} seq {b} (len {n}): dO={eo:.3e} "
+              f"dL={el:.3e} relRMS={rms:.2e}")
+        assert rms <= 5e-3
+    assert big > 0
 
 
 @pytest.mark.parametrize("n_split", [0, 8])
