@@ -55,6 +55,12 @@ int64_t split_bytes(int64_t rows, int head_dim, int64_t n) {
 }
 constexpr int kMaxSplit = 65536;
 
+// Whether the plain tiles' pre-scaled Q is accurate enough at c = |scale|
+// log2(e) for key head dim head_dim (see kPlainMaxScaleRootD).
+bool plain_scale_ok(float c, int head_dim) {
+  return c >= kPlainMinC && c * sqrtf((float)head_dim) <= kPlainMaxScaleRootD * kLog2e;
+}
+
 // n_split > 0 selects the split-KV path (no mask, no window) with the given
 // workspace.
 int train_fwd(const void* q, const void* k, const void* v, const void* mask, int mask_dtype,
@@ -194,7 +200,7 @@ int train_fwd(const void* q, const void* k, const void* v, const void* mask, int
   // query tiles whose first row may see fewer than kPreciseKeys keys; every
   // tile when the plain tiles' pre-scaled Q is not used (below)
   int64_t n_short = 0;
-  const bool plain_ok = kl > kPlainMinKeys && a.c >= kPlainMinC && a.c <= kPlainMaxC;
+  const bool plain_ok = kl > kPlainMinKeys && plain_scale_ok(a.c, head_dim);
   // (split-KV chunks decide per chunk and query tile, in the kernel)
   a.split_plain = a.n_split > 0 && plain_ok;
   if (!plain_ok)
@@ -324,7 +330,7 @@ extern "C" int fa_paged_fwd(const void* q, const void* k_cache, const void* v_ca
   // plain tiles where a sequence's rows see enough keys (decided per sequence,
   // query tile and chunk in the kernel), for scales whose pre-scaled Q stays in
   // bf16's normal range
-  a.split_plain = a.c >= kPlainMinC && a.c <= kPlainMaxC;
+  a.split_plain = plain_scale_ok(a.c, head_dim);
   if (n_split > 0 && cap > 0) {
     const int64_t per = (cap + n_split - 1) / n_split;
     const int64_t kchunk = (per + 63) / 64 * 64;

@@ -140,11 +140,13 @@ constexpr int kPreciseKeys = 128;
 // Plain tiles (bf16 P, Q pre-scaled by c = |scale| log2(e) in bf16) run only
 // for problems of more than kPlainMinKeys keys, where the tolerance is 1e-2
 // (pre-scaling moves L by up to ~2e-3 and O by up to ~2e-3 before its own
-// rounding on the training workloads), and for c in [kPlainMinC, kPlainMaxC]
-// (c * q stays normal and finite in bf16 for ordinary inputs); everything
-// else runs compensated, with Q exact.
+// rounding on the training workloads), for c >= kPlainMinC (c * q stays
+// normal in bf16) and for |scale| * sqrt(head_dim) <= kPlainMaxScaleRootD:
+// the rounding of c * q moves each base-2 score by about 2^-9 c sqrt(D) |q||k|,
+// so at three times the usual 1/sqrt(D) a concentrated softmax's O moved by
+// 1.5e-2. Everything else runs compensated, with Q exact.
 constexpr int kPlainMinKeys = 256;
-constexpr float kPlainMinC = 0x1p-64f, kPlainMaxC = 8.0f;
+constexpr float kPlainMinC = 0x1p-64f, kPlainMaxScaleRootD = 1.5f;
 // After a plain pass, a row is recomputed compensated when some |O| element
 // reaches this: one bf16 rounding step of O is then 2^-7 or more, so the
 // error bf16(P) leaves in O before its own rounding (about 2^-10 at most on

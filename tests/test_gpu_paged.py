@@ -110,9 +110,9 @@ def test_paged_matches_contiguous_oracle(case, n_split):
 def test_paged_plain_tiles_and_redo(D, n_split):
     """Sequences of more than 256 keys run plain tiles (pre-scaled Q, bf16 P)
     where every row of a tile (chunk) sees none or at least 128 of its keys.
-    V times 4 (exact in bf16) at scale 1 concentrates the softmax so that
-    many rows reach |O| >= 1 and take the compensated redo; a 200-key sequence
-    stays compensated. Every row against the oracle."""
+    V times 16 (exact in bf16) at the usual scale makes many rows reach
+    |O| >= 1 and take the compensated redo; a 200-key sequence stays
+    compensated. Every row against the oracle."""
     import torch
     import flash_attention_forward_fa_amd as fa
     B, H, Hkv, ql, bs = 3, 4, 2, 200, 64
@@ -125,12 +125,12 @@ def test_paged_plain_tiles_and_redo(D, n_split):
     vb = fagen.normal_bf16(s, 2, (B, Hkv, N, D))
     e = (vb >> 7) & 0xFF
     assert np.all(e < 250)
-    values = np.where(e != 0, vb + np.uint16(2 << 7), vb).astype(np.uint16)  # exponent + 2
+    values = np.where(e != 0, vb + np.uint16(4 << 7), vb).astype(np.uint16)  # exponent + 4
     kc, vc, table = _paged(keys, values, bs, 11900 + D)
     dev = "cuda:0"
     O, L = fa.paged_fwd(gu.to_dev(q, dev), gu.to_dev(kc, dev), gu.to_dev(vc, dev),
                         torch.from_numpy(table).to(dev),
-                        torch.tensor(lens, dtype=torch.int32, device=dev), scale=1.0,
+                        torch.tensor(lens, dtype=torch.int32, device=dev),
                         causal=True, n_split=n_split)
     torch.cuda.synchronize()
     bits = O.view(torch.int16).cpu().numpy().view(np.uint16)
@@ -138,8 +138,8 @@ def test_paged_plain_tiles_and_redo(D, n_split):
     big = 0
     for b, n in enumerate(lens):
         of, ob, lr = oracle.fwd(q[b:b + 1], keys[b:b + 1, :, :n].copy(),
-                               values[b:b + 1, :, :n].copy(), None, 1, H, Hkv, ql, n, D, 1.0,
-                               True)
+                               values[b:b + 1, :, :n].copy(), None, 1, H, Hkv, ql, n, D,
+                               1.0 / math.sqrt(D), True)
         big += int((np.abs(of) >= 1).any(axis=-1).sum())
         tol_o, tol_l = gu.tolerances(n)
         eo, el, rms = gu.compare(o[b:b + 1], l[b:b + 1], bits[b:b + 1], ob, lr, tol_o, tol_l,

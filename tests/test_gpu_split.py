@@ -50,19 +50,19 @@ CASES = [
 
 @pytest.mark.parametrize("D", [64, 128, 256])
 def test_split_plain_chunks_redo(D):
-    """V times 4 (exact in bf16) and scale 1 (a concentrated softmax): many
-    rows reach |O| >= 1, so plain chunks hand them to their compensated redo;
-    every row against the oracle."""
+    """V times 16 (exact in bf16) at the usual scale: many rows reach
+    |O| >= 1, so plain chunks hand them to their compensated redo; every row
+    against the oracle."""
     w = fagen.Workload("split_redo", 1, 4, 2, 512, 4000, D, True, seed_offset=9300 + D)
     print(f"case split redo D={D}", flush=True)
     inp = fagen.generate(w)
     vb = np.asarray(inp["v"], np.uint16)
     e = (vb >> 7) & 0xFF
     assert np.all(e < 250)
-    inp["v"] = np.where(e != 0, vb + np.uint16(2 << 7), vb).astype(np.uint16)  # exponent + 2
-    o, l, bits = run_split(inp, w, 4, scale=1.0)
+    inp["v"] = np.where(e != 0, vb + np.uint16(4 << 7), vb).astype(np.uint16)  # exponent + 4
+    o, l, bits = run_split(inp, w, 4)
     of, ob, lr = oracle.fwd(inp["q"], inp["k"], inp["v"], None, w.B, w.H, w.Hkv, w.ql, w.kl,
-                            w.D, 1.0, w.causal)
+                            w.D, w.scale, w.causal)
     big = int((np.abs(of) >= 1).any(axis=-1).sum())
     eo, el, rms = gu.compare(o, l, bits, ob, lr, 1e-2, 1e-2, f"split redo D={D}", o_ref_f32=of)
     print(f"split redo D={D}: {big} rows with |O| >= 1, dO={eo:.3e} dL={el:.3e} "
