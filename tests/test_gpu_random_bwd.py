@@ -1,0 +1,108 @@
+"""Seeded random configurations of the backward against the oracle (marked
+gpu).
+
+Each case draws, from its own seed: the head dim (64, 128, 256), the batch,
+the kv heads and the GQA group, ragged query and key counts (ql > kl too),
+the scale, and one of: no mask, the causal rule, a sliding window, a boolean,
+f32 or bf16 mask (dense or broadcast over batch and heads), on contiguous
+tensors or on transposed views of [B, L, H, D]. The forward runs through
+fa_train_fwd_dv (O in q's layout), the backward through fa_train_bwd_strided;
+the oracle is fa_oracle_fwd_general (for L) and fa_oracle_bwd on the same bf16
+inputs. Bounds as in the other backward tests (check_grads: every element
+within 1e-2 times the tensor's largest gradient, at least 1; relative RMS
+error at most 4e-3).
+"""
+import math
+
+import numpy as np
+import pytest
+
+import fagen
+import oracle
+import flash_attention_forward_fa_amd as fa
+from tests import gpu_util as gu
+from tests.test_gpu_bwd import check_grads
+
+pytestmark = pytest.mark.gpu
+
+N_CASES = 32
+
+
+def _draw(i):
+    """The configuration of case i (a pure function of i)."""
+    r = np.random.default_rng(0xBAC4 + 104729 * i)
+    D = int(r.choice([64, 128, 256]))
+    B = int(r.integers(1, 3))
+    Hkv = int(r.choice([1, 2, 4]))
+    G = int(r.choice([1, 2, 4]))
+    ql = int(r.choice([1, int(r.integers(2, 40)), int(r.integers(40, 260))], p=[0.1, 0.3, 0.6]))
+    kl = int(r.choice([int(r.integers(1, 40)), int(r.integers(40, 400))], p=[0.25, 0.75]))
+    scale = float(1.0 / math.sqrt(D) if r.random() < 0.6 else r.uniform(0.03, 0.2))
+    kind = str(r.choice(["none", "causal", "window", "bool", "f32", "bf16"]))
+    window = int(r.integers(0, 200)) if kind == "window" else None
+    bshape = (int(r.choice([1, B])), int(r.choice([1, Hkv * G])))
+    views = bool(r.random() < 0.35)
+    return dict(D=D, B=B, Hkv=Hkv, H=Hkv * G, ql=ql, kl=kl, scale=scale, kind=kind,
+                window=window, bshape=bshape, views=views)
+
+
+def _mask(c, seed):
+    """(torch mask for the calls or None, f32 oracle mask [B, H, ql, kl] or None)."""
+    import torch
+    kind, (mb, mh), B, H, ql, kl = c["kind"], c["bshape"], c["B"], c["H"], c["ql"], c["kl"]
+    if kind not in ("bool", "f32", "bf16"):
+        return None, None
+    if kind == "bool":
+        add, _ = fagen.mask_f32(seed, mb, mh, ql, kl, p_masked=0.3,
+                                n_full_rows=1 if ql >= 4 else 0)
+        t = torch.from_numpy(add == 0.0)
+    else:
+        vals = fagen.bf16_bits_to_f32(fagen.normal_bf16(seed, fagen.STREAM_MASK, (mb, mh, ql, kl)))
+        hid, _ = fagen.mask_f32(seed + 1, mb, mh, ql, kl, p_masked=0.1, n_full_rows=0)
+        add = (vals + hid).astype(np.float32)
+        t = torch.from_numpy(add)
+        if kind == "bf16":
+            t = t.to(torch.bfloat16)
+    ref = np.ascontiguousarray(np.broadcast_to(add, (B, H, ql, kl)), dtype=np.float32)
+    return t.to("cuda:0"), ref
+
+
+@pytest.mark.parametrize("i", range(N_CASES))
+def test_random_backward_matches_oracle(i):
+    import torch
+    c = _draw(i)
+    B, H, Hkv, ql, kl, D = c["B"], c["H"], c["Hkv"], c["ql"], c["kl"], c["D"]
+    causal = c["kind"] in ("causal", "window")
+    print(f"case random bwd {i}: {c}", flush=True)
+    seed = fagen.SEED_BASE + 0x7800 + i
+    q = fagen.normal_bf16(seed, fagen.STREAM_Q, (B, H, ql, D))
+    k = fagen.normal_bf16(seed, fagen.STREAM_K, (B, Hkv, kl, D))
+    v = fagen.normal_bf16(seed, fagen.STREAM_V, (B, Hkv, kl, D))
+    dO = fagen.normal_bf16(seed, 6, (B, H, ql, D))
+    dev = "cuda:0"
+    tq, tk, tv, tg = (gu.to_dev(x, dev) for x in (q, k, v, dO))
+    if c["views"]:
+        tq, tk, tv, tg = (t.transpose(1, 2).contiguous().transpose(1, 2) for t in (tq, tk, tv, tg))
+    tm, ref_mask = _mask(c, seed)
+    O = torch.empty_strided(tq.shape, tq.stride(), dtype=torch.bfloat16, device=dev)
+    O, L = fa.train_fwd_dv(tq, tk, tv, mask=tm, scale=c["scale"], causal=causal,
+                           window=c["window"], out=O)
+    dQ, dK, dV = fa.train_bwd_strided(tq, tk, tv, O, L, tg, mask=tm, scale=c["scale"],
+                                      causal=causal, window=c["window"])
+    torch.cuda.synchronize()
+    got = [gu.widen(t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16))
+           for t in (dQ, dK, dV)]
+    _, _, Lr = oracle.fwd_dv(q, k, v, ref_mask, B, H, Hkv, ql, kl, D, D, c["scale"], causal,
+                             window=c["window"])
+    ref = oracle.bwd(q, k, v, ref_mask, Lr, dO, B, H, Hkv, ql, kl, D, c["scale"], causal,
+                     window=c["window"])
+    check_grads(f"random bwd {i}", got, ref)
+
+
+def test_draws_cover_every_option():
+    """The seeded draws include every head dim, mask kind, views and ql > kl."""
+    cs = [_draw(i) for i in range(N_CASES)]
+    assert {c["D"] for c in cs} == {64, 128, 256}
+    assert {c["kind"] for c in cs} == {"none", "causal", "window", "bool", "f32", "bf16"}
+    assert any(c["views"] for c in cs) and any(c["ql"] > c["kl"] for c in cs)
+    assert any(c["bshape"] != (c["B"], c["H"]) for c in cs if c["kind"] in ("bool", "f32", "bf16"))
