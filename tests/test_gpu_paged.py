@@ -222,3 +222,30 @@ def test_paged_errors_raise_from_binding():
     assert e.value.status == 12
     with pytest.raises(ValueError):
         fa.paged_fwd(q, c, c, t.float(), n)
+
+
+def _draw_paged(i):
+    """A seeded random paged configuration (a pure function of i)."""
+    r = np.random.default_rng(0xFA9E + 15485863 * i)
+    D = int(r.choice([64, 128, 256]))
+    B = int(r.integers(1, 4))
+    Hkv = int(r.choice([1, 2, 4]))
+    G = int(r.choice([1, 2, 4]))
+    ql = int(r.choice([1, int(r.integers(2, 17)), int(r.integers(17, 260))], p=[0.4, 0.2, 0.4]))
+    bs = int(16 * r.integers(1, 9))
+    lens = [int(r.choice([0, int(r.integers(1, 300)), int(r.integers(300, 2500))],
+                         p=[0.1, 0.4, 0.5])) for _ in range(B)]
+    causal = bool(r.random() < 0.7)
+    n_split = int(r.choice([0, 0, 2, 8, 24]))
+    sinks = bool(r.random() < 0.3)
+    return (B, Hkv * G, Hkv, ql, D, bs, lens, causal), n_split, sinks
+
+
+@pytest.mark.parametrize("i", range(24))
+def test_paged_random_configs(i):
+    """24 seeded random paged configurations (block sizes of 16 to 128 keys,
+    per-sequence lengths from 0 to 2500, one to 259 query rows, split-KV,
+    sinks) against the oracle per sequence."""
+    case, n_split, sinks = _draw_paged(i)
+    print(f"case paged random {i}: {case} n_split={n_split} sinks={sinks}", flush=True)
+    _run(case, n_split, seed=12000 + i, with_sinks=sinks)
