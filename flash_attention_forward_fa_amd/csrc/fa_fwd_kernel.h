@@ -154,6 +154,10 @@ constexpr float kPlainMinC = 0x1p-64f, kPlainMaxScaleRootD = 1.5f;
 // rounding costs at most 2^-8. (L needs no such check: bf16(P) changes the
 // row sum by a relative 2^-9 at most.)
 constexpr float kRecheckO = 1.0f;
+// Operand groups (4 MFMAs each) whose LDS reads are in flight ahead of the
+// MFMAs in the wide (D > 128) products. (Two ran no faster for D=256 and use
+// 249 VGPRs; three spill.)
+constexpr int kWidePrefetch = 1;
 // The max used in exp2 is only raised when a tile's max exceeds it by more
 // than this (base-2 units): P <= 2^kLazy and O is rarely rescaled.
 constexpr float kLazy = 8.0f;
@@ -454,24 +458,27 @@ __device__ __forceinline__ bool fwd_tile(const FwdArgs& a, int qtile, int bh, ui
         }
       }
     } else {
-      // DK > 128: K operands in groups of SG dim steps, the next group's reads
-      // issued before the current group's MFMAs; sched_barrier keeps that
-      // order (and the register use) instead of hoisting every read.
+      // DK > 128: K operands in groups of SG dim steps, the reads of group
+      // g + kWidePrefetch issued before the MFMAs of group g; sched_barrier
+      // keeps that order (and the register use) instead of hoisting every read.
       constexpr int SG = NKB == 2 ? 2 : 1;
       constexpr int NG = NDS / SG;
-      bf16x8 kop[2][SG][NKB];
+      constexpr int PD = kWidePrefetch, NR = PD + 1;
+      bf16x8 kop[NR][SG][NKB];
 #pragma unroll
-      for (int ss = 0; ss < SG; ++ss)
+      for (int p = 0; p < PD && p < NG; ++p)
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) kop[0][ss][kb] = kread(ks, ss, kb);
+        for (int ss = 0; ss < SG; ++ss)
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb) kop[p][ss][kb] = kread(ks, p * SG + ss, kb);
 #pragma unroll
       for (int g = 0; g < NG; ++g) {
-        if (g + 1 < NG) {
+        if (g + PD < NG) {
 #pragma unroll
           for (int ss = 0; ss < SG; ++ss)
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb)
-              kop[(g + 1) & 1][ss][kb] = kread(ks, (g + 1) * SG + ss, kb);
+              kop[(g + PD) % NR][ss][kb] = kread(ks, (g + PD) * SG + ss, kb);
         }
 #pragma unroll
         for (int ss = 0; ss < SG; ++ss)
@@ -480,7 +487,7 @@ __device__ __forceinline__ bool fwd_tile(const FwdArgs& a, int qtile, int bh, ui
 #pragma unroll
             for (int qb = 0; qb < kQB; ++qb)
               sacc[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                  kop[g & 1][ss][kb], qop[qb][g * SG + ss], sacc[kb][qb], 0, 0, 0);
+                  kop[g % NR][ss][kb], qop[qb][g * SG + ss], sacc[kb][qb], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -648,27 +655,31 @@ __device__ __forceinline__ bool fwd_tile(const FwdArgs& a, int qtile, int bh, ui
 #pragma unroll
         for (int j = 0; j < NKC; ++j) pv_mfma(vread(vs, d, j), d, j, phi, plo);
     } else {
-      // DV > 128: V operands in groups of DG dim blocks, prefetched one group
-      // ahead as for K
+      // DV > 128: V operands in groups of DG dim blocks, prefetched
+      // kWidePrefetch groups ahead as for K
       constexpr int DG = NKC == 1 ? 4 : 2;
       constexpr int NG = NDB / DG;
-      bf16x8 vop[2][DG][NKC];
+      constexpr int PD = kWidePrefetch, NR = PD + 1;
+      bf16x8 vop[NR][DG][NKC];
 #pragma unroll
-      for (int dd = 0; dd < DG; ++dd)
+      for (int p = 0; p < PD && p < NG; ++p)
 #pragma unroll
-        for (int j = 0; j < NKC; ++j) vop[0][dd][j] = vread(vs, dd, j);
+        for (int dd = 0; dd < DG; ++dd)
+#pragma unroll
+          for (int j = 0; j < NKC; ++j) vop[p][dd][j] = vread(vs, p * DG + dd, j);
 #pragma unroll
       for (int g = 0; g < NG; ++g) {
-        if (g + 1 < NG) {
+        if (g + PD < NG) {
 #pragma unroll
           for (int dd = 0; dd < DG; ++dd)
 #pragma unroll
-            for (int j = 0; j < NKC; ++j) vop[(g + 1) & 1][dd][j] = vread(vs, (g + 1) * DG + dd, j);
+            for (int j = 0; j < NKC; ++j)
+              vop[(g + PD) % NR][dd][j] = vread(vs, (g + PD) * DG + dd, j);
         }
 #pragma unroll
         for (int dd = 0; dd < DG; ++dd)
 #pragma unroll
-          for (int j = 0; j < NKC; ++j) pv_mfma(vop[g & 1][dd][j], g * DG + dd, j, phi, plo);
+          for (int j = 0; j < NKC; ++j) pv_mfma(vop[g % NR][dd][j], g * DG + dd, j, phi, plo);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
