@@ -182,6 +182,20 @@ struct CopyShape {
   static constexpr int ROUNDS = (SLOTS + NT - 1) / NT; // chunks per thread (at most)
   static_assert(SLOTS % 64 == 0, "a tile must be whole wave instructions");
   static_assert(!kPanels<W> || BN == 64, "panel layouts hold 64-row tiles");
+  // Rounds whose lanes' offsets repeat: with whole rounds of whole rows
+  // (NT % CH == 0, no panels) and the row permutations of kswz/vswz, which
+  // repeat every 32 rows, round u's lane reads the chunk of round u % PERIOD
+  // (NT / CH) * (u - u % PERIOD) rows further on, a uniform offset; so only
+  // PERIOD offsets per lane are kept in registers, the rest go as the scalar
+  // offset. Used for 4-wave workgroups only (the head_dim-64 window kernels,
+  // where it removed the spills); with 8 waves the registers were to spare
+  // and the head_dim-128 forward ran 5% slower with it. (PERIOD = ROUNDS: one
+  // register per round.)
+  static constexpr int RPR = NT / CH;  // rows per round
+  static constexpr int PERIOD =
+      (NT != 256 || kPanels<W> || NT % CH != 0 || SLOTS % NT != 0) ? ROUNDS
+      : RPR >= 32                                                   ? 1
+                  : (32 / RPR < ROUNDS ? 32 / RPR : ROUNDS);
 };
 
 // (rs: the source's row stride in elements, W when its rows are contiguous)
@@ -216,12 +230,16 @@ __device__ __forceinline__ void issue_tile(const uint16_t* src, int kbase, int k
   const int rows = kl - kbase;
   const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(src + (int64_t)kbase * rs), 0, ((min(rows, BN) - 1) * rs + W) * 2, kRsrcWord3);
+  constexpr int PERIOD = CopyShape<W, BN, NT>::PERIOD, RPR = CopyShape<W, BN, NT>::RPR;
+  // (full tiles: round u's uniform part as the scalar offset, outside the
+  // range check, which the lane's part, within round 0's rows, passes)
   if (rows >= BN) {
 #pragma unroll
     for (int u = 0; u < ROUNDS; ++u)
       if ((u + 1) * NT <= SLOTS || u * NT + wave_base < SLOTS)  // (wave-uniform)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rsrc, (lds_void*)(lds + (u * NT + wave_base) * 8), 16, off[u], 0, 0, 0);
+            rsrc, (lds_void*)(lds + (u * NT + wave_base) * 8), 16, off[u % PERIOD],
+            (u - u % PERIOD) * RPR * rs * 2, 0, 0);
   } else {
     // (with BRANCH, an empty volatile asm keeps this rare path a branch:
     // speculated into the full-tile path as selects, its vector arithmetic
@@ -234,7 +252,9 @@ __device__ __forceinline__ void issue_tile(const uint16_t* src, int kbase, int k
         // (this thread's row moved back to the last valid one)
         int row, c;
         slot_chunk<W, IS_K>(u * NT + tid, row, c);
-        const int o = off[u] - max(row - (rows - 1), 0) * rs * 2;
+        // (the whole offset in the lane's register: the buffer's range check
+        // sees only that part, and the clamped row may lie before round 0's)
+        const int o = off[u % PERIOD] + ((u - u % PERIOD) * RPR - max(row - (rows - 1), 0)) * rs * 2;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             rsrc, (lds_void*)(lds + (u * NT + wave_base) * 8), 16, o, 0, 0, 0);
       }

@@ -21,11 +21,12 @@ namespace {
 
 bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
 
-// Query rows per workgroup of a (DK, DV) pair, 0 for a pair without kernels.
-int block_m_of(int dk, int dv) {
+// Query rows per workgroup of a (DK, DV) pair (of its sliding-window kernels
+// when window), 0 for a pair without kernels.
+int block_m_of(int dk, int dv, bool window = false) {
   if (dk == dv) {
     switch (dk) {
-      case 64: return block_m<64, 64>();
+      case 64: return window ? block_m<64, 64, true>() : block_m<64, 64>();
       case 80: return block_m<80, 80>();
       case 96: return block_m<96, 96>();
       case 128: return block_m<128, 128>();
@@ -71,12 +72,15 @@ int train_fwd(const void* q, const void* k, const void* v, const void* mask, int
               int64_t mask_sr = -1, const float* sinks = nullptr) {
   if (batch < 0 || ql < 0 || kl < 0 || n_heads < 1 || n_kv_heads < 1) return FA_ERR_BAD_SIZE;
   if (n_heads % n_kv_heads != 0) return FA_ERR_HEAD_GROUPING;
-  const int bm = block_m_of(head_dim, head_dim_v);
+  if (window >= 0 && !causal) return FA_ERR_WINDOW;
+  // a window that hides no key (q_abs - window <= 0 for every row) is the
+  // causal problem: it runs the causal kernels, and gives their bits
+  if (window >= 0 && (int64_t)window >= (int64_t)std::max(kl - ql, 0) + ql - 1) window = -1;
+  const int bm = block_m_of(head_dim, head_dim_v, window >= 0);
   if (bm == 0 || (n_split > 0 && (head_dim != head_dim_v || !base_dim(head_dim))))
     return FA_ERR_HEAD_DIM;
   const int dv = head_dim_v;
   if (!isfinite(scale)) return FA_ERR_SCALE;
-  if (window >= 0 && !causal) return FA_ERR_WINDOW;
   if (mask && ((mask_dtype != FA_MASK_F32 && mask_dtype != FA_MASK_BF16 &&
                 mask_dtype != FA_MASK_BOOL) ||
                mask_sb < 0 || mask_sh < 0))

@@ -129,8 +129,13 @@ template <> struct Cfg<96, 96> { static constexpr int W = 8, QB = 2, BN = 64, WP
 template <> struct Cfg<96, 64> { static constexpr int W = 8, QB = 2, BN = 64, WPE = 2; };
 template <> struct Cfg<192, 192> { static constexpr int W = 8, QB = 1, BN = 64, WPE = 2; };
 template <> struct Cfg<192, 128> { static constexpr int W = 8, QB = 1, BN = 64, WPE = 2; };
-template <int DK, int DV> constexpr int block_m() {
-  return Cfg<DK, DV>::W * 16 * Cfg<DK, DV>::QB;
+// The sliding-window kernels may use their own shape: with head_dim 64, 4-wave
+// workgroups of 128 rows, whose union of the rows' key bands is closer to each
+// row's own band than for 256 rows (measured 7% faster at a window of 1024).
+template <int DK, int DV, bool WINDOW> struct KCfg : Cfg<DK, DV> {};
+template <> struct KCfg<64, 64, true> { static constexpr int W = 4, QB = 2, BN = 64, WPE = 4; };
+template <int DK, int DV, bool WINDOW = false> constexpr int block_m() {
+  return KCfg<DK, DV, WINDOW>::W * 16 * KCfg<DK, DV, WINDOW>::QB;
 }
 
 // Query tiles with a row that may see fewer keys than this (a property of
@@ -196,7 +201,7 @@ __device__ __forceinline__ bool fwd_tile(const FwdArgs& a, int qtile, int bh, ui
                                          uint16_t* v0s, uint16_t* k1s, uint16_t* v1s,
                                          uint16_t* k2s, uint16_t* v2s, uint16_t* k3s,
                                          uint16_t* v3s,
-                                         bool (&redo)[Cfg<DK, DV>::QB], int* wg_flags,
+                                         bool (&redo)[KCfg<DK, DV, WINDOW>::QB], int* wg_flags,
                                          int split = 0) {
   constexpr bool HAS_MASK = MASK != kNoMask;
   static_assert(PRECISE || !HAS_MASK, "the masked forward always runs compensated");
@@ -208,12 +213,13 @@ __device__ __forceinline__ bool fwd_tile(const FwdArgs& a, int qtile, int bh, ui
   static_assert(!PAGED || (!WINDOW && MASK == kNoMask), "paged KV: unmasked, no window");
   static_assert((!SPLIT && !PAGED) || (DK == DV && !kPanels<DK>),
                 "split-KV and paged: head dims 64, 128 and 256");
-  constexpr int BN = Cfg<DK, DV>::BN;
+  using C = KCfg<DK, DV, WINDOW>;
+  constexpr int BN = C::BN;
   // (QBX: query blocks per wave other than the pair's, for the narrow
   // split-KV kernels of at most 16 query rows: one block, half the work of
   // the one wave that has rows)
-  constexpr int kQB = QBX ? QBX : Cfg<DK, DV>::QB;
-  static_assert(kQB <= Cfg<DK, DV>::QB, "redo flags for at most the pair's blocks");
+  constexpr int kQB = QBX ? QBX : C::QB;
+  static_assert(kQB <= C::QB, "redo flags for at most the pair's blocks");
   constexpr int kRowsPerWave = 16 * kQB;
   // The narrow split-KV kernels (at most 16 query rows: decoding) split the
   // keys, not the rows, among the waves: every wave holds the same 16 rows,
@@ -221,14 +227,14 @@ __device__ __forceinline__ bool fwd_tile(const FwdArgs& a, int qtile, int bh, ui
   // states are merged through LDS at the end.
   constexpr bool DECODE = QBX == 1 && SPLIT;
   static_assert(!DECODE || (DK == DV && DK <= 128 && !kPanels<DK>), "decode: 64 or 128 dims");
-  constexpr int kBlockM = DECODE ? 16 : Cfg<DK, DV>::W * kRowsPerWave;
+  constexpr int kBlockM = DECODE ? 16 : C::W * kRowsPerWave;
   constexpr int NKB = BN / 16;   // 16-key blocks per tile
   constexpr int NKC = BN / 32;   // 32-key chunks per tile (P.V contraction steps)
   constexpr int NDB = DV / 16;   // 16-dim blocks of O
   constexpr int NDS = DK / 32;   // 32-dim steps of Q.K
   // a last 16-dim step of Q.K (DK = 80), with the 16x16x16 MFMA
   constexpr bool KTAIL = DK % 32 == 16;
-  constexpr int NT = 64 * Cfg<DK, DV>::W;  // threads per workgroup
+  constexpr int NT = 64 * C::W;  // threads per workgroup
   // the wide key dims (one query block per wave): grouped operand reads
   constexpr bool WIDE = DK > 128;
   static_assert(DK % 16 == 0 && DV % 16 == 0 && NDS > 0, "head dims: multiples of 16, >= 32");
@@ -963,7 +969,7 @@ __device__ __forceinline__ bool fwd_tile(const FwdArgs& a, int qtile, int bh, ui
     if (lane == 0) wg_flags[wave] = wave_any;
     __syncthreads();
 #pragma unroll
-    for (int w = 0; w < Cfg<DK, DV>::W; ++w) wg_any |= wg_flags[w] != 0;
+    for (int w = 0; w < C::W; ++w) wg_any |= wg_flags[w] != 0;
   }
 #pragma unroll
   for (int qb = 0; qb < kQB; ++qb) {
@@ -1018,14 +1024,15 @@ __device__ __forceinline__ bool fwd_tile(const FwdArgs& a, int qtile, int bh, ui
 }
 
 template <int DK, int DV, bool CAUSAL, bool WINDOW, int MASK, int MODE, int QBX = 0>
-__global__ __launch_bounds__((64 * Cfg<DK, DV>::W))
-__attribute__((amdgpu_waves_per_eu(MODE == kMixed ? Cfg<DK, DV>::WPE : 2))) void fa_fwd_kernel(
+__global__ __launch_bounds__((64 * KCfg<DK, DV, WINDOW>::W))
+__attribute__((amdgpu_waves_per_eu(MODE == kMixed ? KCfg<DK, DV, WINDOW>::WPE : 2))) void fa_fwd_kernel(
     FwdArgs a) {
   static_assert(MODE < kSplit || (MASK == kNoMask && !WINDOW),
                 "split-KV and paged: unmasked, no window");
   static_assert(MODE != kMixed || MASK == kNoMask, "the masked forward always runs compensated");
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
-  constexpr int TILE_K = Cfg<DK, DV>::BN * DK, TILE_V = Cfg<DK, DV>::BN * DV;
+  using C = KCfg<DK, DV, WINDOW>;
+  constexpr int TILE_K = C::BN * DK, TILE_V = C::BN * DV;
   __shared__ __attribute__((aligned(1024))) uint16_t k0s[TILE_K];
   __shared__ __attribute__((aligned(1024))) uint16_t v0s[TILE_V];
   __shared__ __attribute__((aligned(1024))) uint16_t k1s[TILE_K];
@@ -1036,7 +1043,7 @@ __attribute__((amdgpu_waves_per_eu(MODE == kMixed ? Cfg<DK, DV>::WPE : 2))) void
   __shared__ __attribute__((aligned(1024))) uint16_t v2s[TILE_X];
   __shared__ __attribute__((aligned(1024))) uint16_t k3s[TILE_X];
   __shared__ __attribute__((aligned(1024))) uint16_t v3s[TILE_X];
-  __shared__ int wg_flags[Cfg<DK, DV>::W];
+  __shared__ int wg_flags[C::W];
 
   // ---- work item ----
   // Workgroups are handed to the 8 XCDs round-robin (bid mod 8). When B*H is a
@@ -1063,7 +1070,7 @@ __attribute__((amdgpu_waves_per_eu(MODE == kMixed ? Cfg<DK, DV>::WPE : 2))) void
     bh = bid % BH;
   }
   const int qtile = a.qt_base + a.qt_count - 1 - qt_rev;
-  bool redo[Cfg<DK, DV>::QB] = {};
+  bool redo[C::QB] = {};
 #define FA_TILE_BUFFERS k0s, v0s, k1s, v1s, k2s, v2s, k3s, v3s
   if constexpr (MODE == kMixed) {
     // the compensated tiles are the lightest, so they run last and fill the tail
@@ -1201,7 +1208,7 @@ __global__ __launch_bounds__(256) void fa_combine_kernel(CombineArgs c) {
 template <int DK, int DV, bool CAUSAL, bool WINDOW, int MASK, int MODE, int QBX = 0>
 hipError_t launch(const FwdArgs& a, unsigned grid, hipStream_t stream) {
   hipLaunchKernelGGL((fa_fwd_kernel<DK, DV, CAUSAL, WINDOW, MASK, MODE, QBX>), dim3(grid),
-                     dim3(64 * Cfg<DK, DV>::W), 0, stream, a);
+                     dim3(64 * KCfg<DK, DV, WINDOW>::W), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -115,9 +115,44 @@ template <int W> static bool check_width() {
   return check_layout<W, true>() && check_layout<W, false>() && check_pieces<W>();
 }
 
+// The copies keep per-lane offsets for CopyShape::PERIOD rounds only and
+// reach round u through a uniform row offset: for every thread and round, the
+// chunk the thread copies in round u must be that of round u % PERIOD, in the
+// row (u - u % PERIOD) * RPR further on.
+template <int W, int BN, int NT, bool IS_K> static bool check_rounds() {
+  using CS = CopyShape<W, BN, NT>;
+  for (int t = 0; t < NT; ++t)
+    for (int u = 0; u < CS::ROUNDS; ++u) {
+      const int p = u * NT + t, p0 = (u % CS::PERIOD) * NT + t;
+      if (p >= CS::SLOTS) continue;
+      int r, c, r0, c0;
+      slot_chunk<W, IS_K>(p, r, c);
+      slot_chunk<W, IS_K>(p0, r0, c0);
+      if (c != c0 || r != r0 + (u - u % CS::PERIOD) * CS::RPR) {
+        printf("W=%d BN=%d NT=%d %s: round %d of thread %d is not round %d shifted\n", W, BN,
+               NT, IS_K ? "K" : "V", u, t, u % CS::PERIOD);
+        return false;
+      }
+    }
+  return true;
+}
+
+template <int W, int BN, int NT> static bool check_rounds_kv() {
+  printf("rounds W=%d BN=%d NT=%d: %d rounds, %d kept\n", W, BN, NT, CopyShape<W, BN, NT>::ROUNDS,
+         CopyShape<W, BN, NT>::PERIOD);
+  return check_rounds<W, BN, NT, true>() && check_rounds<W, BN, NT, false>();
+}
+
 int main() {
   const bool ok = check_width<64>() && check_width<80>() && check_width<96>() &&
-                  check_width<128>() && check_width<192>() && check_width<256>();
+                  check_width<128>() && check_width<192>() && check_width<256>() &&
+                  check_rounds_kv<64, 64, 256>() && check_rounds_kv<64, 64, 512>() &&
+                  check_rounds_kv<64, 32, 256>() && check_rounds_kv<128, 64, 256>() &&
+                  check_rounds_kv<128, 64, 512>() && check_rounds_kv<128, 32, 512>() &&
+                  check_rounds_kv<256, 64, 512>() && check_rounds_kv<256, 32, 512>() &&
+                  check_rounds_kv<256, 64, 256>() && check_rounds_kv<256, 32, 256>() &&
+                  check_rounds_kv<80, 64, 512>() && check_rounds_kv<96, 64, 512>() &&
+                  check_rounds_kv<192, 64, 512>();
   printf(ok ? "ok\n" : "FAILED\n");
   return ok ? 0 : 1;
 }
