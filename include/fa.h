@@ -33,7 +33,8 @@ extern "C" {
 /* Status codes returned by every entry point. */
 enum fa_status {
     FA_OK = 0,
-    FA_ERR_NULL_POINTER = 1,   /* q, k, v, O or L is NULL while its tensor is non-empty */
+    FA_ERR_NULL_POINTER = 1,   /* q, k, v, O or L is NULL while its tensor is non-empty
+                                  (or a required table, length array or workspace)   */
     FA_ERR_BAD_SIZE = 2,       /* batch, ql or kl < 0; n_heads or n_kv_heads < 1      */
     FA_ERR_HEAD_GROUPING = 3,  /* n_heads is not a multiple of n_kv_heads              */
     FA_ERR_HEAD_DIM = 4,       /* head dims not supported by the entry point: 64, 128
@@ -41,15 +42,17 @@ enum fa_status {
                                   also take 80, 96 and 192, and fa_train_fwd_dv the
                                   (key, value) pairs (96, 64) and (192, 128)          */
     FA_ERR_SCALE = 5,          /* scale is NaN or infinite                              */
-    FA_ERR_ALIGNMENT = 6,      /* q, k, v or O not 16-byte aligned; mask or L not 4-byte */
+    FA_ERR_ALIGNMENT = 6,      /* q, k, v, O or a workspace not 16-byte aligned; L,
+                                  sinks, a block table or lengths not 4-byte; a mask
+                                  not aligned to its element                           */
     FA_ERR_TOO_LARGE = 7,      /* a grid or index would overflow the kernel's limits    */
     FA_ERR_LAUNCH = 8,         /* the HIP launch failed (hipGetLastError)               */
     FA_ERR_WINDOW = 9,         /* window < 0 (fa_train_fwd_swa); window >= 0 without
-                                  causal (fa_train_fwd_ex)                              */
-    FA_ERR_MASK = 10,          /* fa_train_fwd_ex: unknown mask dtype or a negative
-                                  mask stride                                           */
-    FA_ERR_SPLIT = 11,         /* fa_train_fwd_split: n_split outside 1..65536, or the
-                                  workspace smaller than the split needs                */
+                                  causal, or with split-KV                              */
+    FA_ERR_MASK = 10,          /* unknown mask dtype, a negative mask stride, or a mask
+                                  with split-KV                                         */
+    FA_ERR_SPLIT = 11,         /* n_split outside 1..65536 (0 allowed where it means no
+                                  split), or the workspace smaller than the split needs */
     FA_ERR_PAGED = 12,         /* fa_paged_fwd: block_size not a positive multiple of
                                   16, or no cache blocks for a non-empty table          */
     FA_ERR_STRIDE = 13,        /* fa_train_fwd_strided, fa_train_bwd_strided: a negative
