@@ -497,11 +497,15 @@ extern "C" const char* fa_status_string(int status) {
              "192 and (key, value) pairs (96, 64) and (192, 128), without split-KV";
     case FA_ERR_SCALE: return "scale must be finite";
     case FA_ERR_ALIGNMENT:
-      return "misaligned tensor (q, k, v, O need 16 bytes; L and an f32 mask 4, a bf16 mask 2)";
+      return "misaligned tensor (q, k, v, O and a workspace need 16 bytes; L, sinks, tables "
+             "and an f32 mask 4, a bf16 mask 2)";
     case FA_ERR_TOO_LARGE: return "problem too large for the kernel's grid or index range";
     case FA_ERR_LAUNCH: return "HIP kernel launch failed";
-    case FA_ERR_WINDOW: return "sliding window must be >= 0 and comes with causal masking";
-    case FA_ERR_MASK: return "mask dtype must be FA_MASK_F32, FA_MASK_BF16 or FA_MASK_BOOL, strides >= 0";
+    case FA_ERR_WINDOW:
+      return "sliding window must be >= 0 and comes with causal masking, without split-KV";
+    case FA_ERR_MASK:
+      return "mask dtype must be FA_MASK_F32, FA_MASK_BF16 or FA_MASK_BOOL, strides >= 0, and "
+             "no mask with split-KV";
     case FA_ERR_SPLIT: return "n_split must be in 1..65536 and the workspace large enough";
     case FA_ERR_PAGED: return "block_size must be a positive multiple of 16 and the cache non-empty";
     case FA_ERR_SCRATCH:
