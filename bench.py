@@ -459,7 +459,7 @@ def main():
     if split_kv:
         result["split_kv"] = split_kv
     if not args.no_cpu_baseline:
-        target = {w.name: (args.cpu_rows or (524288 if w.D == 64 else 65536)) for w in workloads}
+        target = {w.name: (args.cpu_rows or (524288 if w.D == 64 else 262144)) for w in workloads}
         result["cpu_baseline"] = cpu_baseline(workloads, inputs, target)
     print(json.dumps(result), flush=True)
 
