@@ -86,7 +86,8 @@ def stored_counters(workload):
 
 
 def cpu_baseline(workloads, inputs, target_rows):
-    """The oracle, as it stands, on a strided sample of rows of each workload."""
+    """The oracle, as it stands, on every row of each workload (or a strided
+    sample of target_rows rows)."""
     import numpy as np
     import oracle
     threads = oracle.default_threads()
@@ -103,7 +104,8 @@ def cpu_baseline(workloads, inputs, target_rows):
         flop = w.metric_flop * rows.size / n_rows
         total_flop += flop
         total_s += dt
-        parts.append(f"{w.name}: every {stride}th row ({rows.size} rows, {dt:.1f} s)")
+        which = "every row" if stride == 1 else f"every {stride}th row"
+        parts.append(f"{w.name}: {which} ({rows.size} rows, {dt:.1f} s)")
         log(f"cpu_baseline {w.name}: {rows.size} rows in {dt:.2f} s "
             f"({flop / dt / 1e9:.2f} GFLOP/s)")
     host_cores = os.cpu_count()
