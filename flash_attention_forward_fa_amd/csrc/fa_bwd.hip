@@ -15,14 +15,19 @@
 // (D_i = rowsum(dO_i * O_i) equals the page's sum_j P_ij dP_ij when O is the
 // forward's output.) The WINDOW variants apply the forward's sliding window
 // (key j visible to row i iff q_abs - window <= j <= q_abs) and stream only the
-// tiles inside the band. Two launches, no atomics and no workspace: one kernel
-// template serves both. A workgroup keeps a block of "fixed" rows in registers
-// and streams tiles of the other side through LDS:
+// tiles inside the band. Three launches, no atomics and no workspace:
 //
-//   dQ pass  (kBwdQ):  fixed = query rows (Q, dO, L, D), streamed = keys (K, V)
+//   rows pass:         per query row, L2_i = L_i log2(e) (+inf for a row with
+//                      no visible key) and D_i, stored as two floats at the
+//                      start of the row's dQ memory (dQ is written only by the
+//                      last launch, so until then its rows serve as scratch)
 //   dKV pass (kBwdKV): fixed = key rows (K, V), streamed = query rows of every
-//                      head of the group (Q, dO, and L, D per row)
+//                      head of the group (Q, dO, and L2, D per row)
+//   dQ pass  (kBwdQ):  fixed = query rows (Q, dO, and their L2, D, read
+//                      before the rows are overwritten), streamed = keys (K, V)
 //
+// The last two share one kernel template: a workgroup keeps a block of "fixed"
+// rows in registers and streams tiles of the other side through LDS.
 // Per streamed tile every wave computes, with v_mfma_f32_16x16x32_bf16 and the
 // same operand layouts as the forward kernel,
 //   S^T  = Y1 X1^T (raw scores)   dP^T = Y2 X2^T
@@ -51,8 +56,7 @@ namespace {
 constexpr int kBwdQ = 0, kBwdKV = 1;
 
 // Per head dim and pass: W waves, FB fixed 16-row blocks per wave, BN streamed
-// rows per tile, WPE waves per SIMD (register budget). The D=256 dK/dV pass
-// streams three tiles (Q, dO, O) through 96 KiB of LDS in 32-row tiles.
+// rows per tile, WPE waves per SIMD (register budget).
 template <int D, int PASS> struct BwdCfg;
 // DS waves share each fixed block, each accumulating D/DS of the output dims
 // (the D=256 dK/dV pass: two waves per 16 key rows, each with half of dK and
@@ -76,7 +80,7 @@ struct BwdArgs {
   const uint16_t* v;
   const uint16_t* o;
   const uint16_t* dO;
-  const float* L;
+  const float* L;            // rows pass only (the others read L2 from dQ's rows)
   const void* mask;          // f32, bf16 or bool bytes (the kernel's MASK), or null
   int64_t mask_sb, mask_sh;  // mask strides of batch and head, in elements (0: broadcast)
   int mask_sr;               // mask row stride, in elements (kl: rows contiguous)
@@ -99,6 +103,40 @@ struct BwdArgs {
 // log2-units logsumexp of a row; a row with no visible key (L = -inf) gets
 // +inf, so that every P of that row is 0
 __device__ __forceinline__ float lse2(float l) { return l == -INFINITY ? INFINITY : l * kLog2e; }
+
+// The rows pass: for every query row, (L2, D) = (lse2(L), sum_d O_d dO_d) as
+// two floats at the start of the row's dQ memory (8 of its >= 128 bytes; dQ's
+// rows are 16-byte aligned). D/8 lanes per row, 16 bytes of O and dO each;
+// a grid-stride loop over groups of 256/(D/8) rows.
+template <int D>
+__global__ __launch_bounds__(256) void fa_bwd_rows_kernel(BwdArgs a) {
+  constexpr int LPR = D / 8;
+  constexpr int RPB = 256 / LPR;
+  const int part = threadIdx.x % LPR;
+  const int64_t nrows = (int64_t)a.B * a.H * a.ql;
+  for (int64_t r0 = (int64_t)blockIdx.x * RPB; r0 < nrows; r0 += (int64_t)gridDim.x * RPB) {
+    const int64_t row = r0 + threadIdx.x / LPR;
+    const bool live = row < nrows;
+    int64_t base = 0;
+    float acc = 0.0f;
+    if (live) {
+      const int64_t bh = row / a.ql;
+      const int i = (int)(row - bh * a.ql);
+      base = bh / a.H * a.q_sb + bh % a.H * a.q_sh + (int64_t)i * a.q_sr;
+      const bf16x8 ov = __builtin_bit_cast(
+          bf16x8, *reinterpret_cast<const u32x4*>(a.o + base + 8 * part));
+      const bf16x8 gv = __builtin_bit_cast(
+          bf16x8, *reinterpret_cast<const u32x4*>(a.dO + base + 8 * part));
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc += (float)ov[e] * (float)gv[e];
+    }
+    // (LPR divides 64: a row's lanes are consecutive lanes of one wave)
+#pragma unroll
+    for (int m = 1; m < LPR; m <<= 1) acc += __shfl_xor(acc, m, 64);
+    if (live && part == 0)
+      *reinterpret_cast<float2*>(a.dq + base) = make_float2(lse2(a.L[row]), acc);
+  }
+}
 
 template <int D, int PASS, bool CAUSAL, bool WINDOW, int MASK>
 __global__ __launch_bounds__((64 * BwdCfg<D, PASS>::W))
@@ -126,12 +164,11 @@ __attribute__((amdgpu_waves_per_eu(BwdCfg<D, PASS>::WPE))) void fa_bwd_kernel(Bw
   __shared__ __attribute__((aligned(1024))) uint16_t y1s1[TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t y2s0[TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t y2s1[TILE];
-  __shared__ __attribute__((aligned(1024))) uint16_t yos0[KV ? TILE : 8];  // dKV pass: O
-  __shared__ __attribute__((aligned(1024))) uint16_t yos1[KV ? TILE : 8];
-  // dKV pass: L2 and D of the streamed rows (one 8-byte store per row: two
-  // separate stores were merged into one that lost the array's alias scope,
-  // and the compiler then waited for the next tile's copy before it)
-  __shared__ float2 srow[BN];
+  // dKV pass: L2 and D of the streamed rows (the first 16 bytes of their dQ
+  // rows: L2, D and two unused floats), one array per stage, copied with the
+  // stage's tiles (64 entries: one per lane of the copying wave)
+  __shared__ float4 srow0[KV ? 64 : 1];
+  __shared__ float4 srow1[KV ? 64 : 1];
 
   const int tid = threadIdx.x;
   // wave-uniform wave index: every wave-level condition is a scalar branch
@@ -178,24 +215,17 @@ __attribute__((amdgpu_waves_per_eu(BwdCfg<D, PASS>::WPE))) void fa_bwd_kernel(Bw
           bf16x8, *reinterpret_cast<const u32x4*>(x2p + (int64_t)r * xr + 32 * s + 8 * grp));
     }
   }
-  // dQ pass: L2 and D of the fixed rows (D from the same dims as the dO operand,
-  // summed over the four 16-lane groups)
+  // dQ pass: L2 and D of the fixed rows, from the rows pass (read here, before
+  // this workgroup overwrites its rows; a wave past the end reads the last row,
+  // whose values it never uses)
   float l2f[FB], dfx[FB];
   if constexpr (!KV) {
 #pragma unroll
     for (int fb = 0; fb < FB; ++fb) {
       const int r = min(fw0 + 16 * fb + c16, nfixed - 1);
-      float part = 0.0f;
-#pragma unroll
-      for (int s = 0; s < NDS; ++s) {
-        const bf16x8 ov = __builtin_bit_cast(
-            bf16x8, *reinterpret_cast<const u32x4*>(a.o + qh_base + (int64_t)r * a.q_sr + 32 * s +
-                                                     8 * grp));
-#pragma unroll
-        for (int e = 0; e < 8; ++e) part += (float)ov[e] * (float)x2op[fb][s][e];
-      }
-      dfx[fb] = group_sum(part);
-      l2f[fb] = lse2(a.L[(int64_t)fhead * ql + r]);
+      const float2 sv = *reinterpret_cast<const float2*>(a.dq + qh_base + (int64_t)r * a.q_sr);
+      l2f[fb] = sv.x;
+      dfx[fb] = sv.y;
     }
   }
 
@@ -240,40 +270,29 @@ __attribute__((amdgpu_waves_per_eu(BwdCfg<D, PASS>::WPE))) void fa_bwd_kernel(Bw
   int y1off[CopyShape<D, BN, NT>::ROUNDS], y2off[CopyShape<D, BN, NT>::ROUNDS];
   copy_offsets<D, BN, NT, true>(tid, y1off, yr);
   copy_offsets<D, BN, NT, false>(tid, y2off, yr);
-  auto issue = [&](int t, uint16_t* y1d, uint16_t* y2d, uint16_t* yod) {
+  auto issue = [&](int t, uint16_t* y1d, uint16_t* y2d) {
     issue_tile<D, BN, NT, true>(y1_src(t), tile_first(t), nstream, y1d, tid, 64 * wave, y1off,
                                 yr);
     issue_tile<D, BN, NT, false>(y2_src(t), tile_first(t), nstream, y2d, tid, 64 * wave, y2off,
                                  yr);
-    if constexpr (KV)
-      issue_tile<D, BN, NT, false>(a.o + b * a.q_sb + tile_head(t) * a.q_sh, tile_first(t),
-                                   nstream, yod, tid, 64 * wave, y2off, yr);
   };
-  // dKV pass: L2 and D of the streamed rows of tile t (landed in LDS) into
-  // srow (NT / BN threads per row, each summing D / (NT / BN) dims of O * dO)
-  // (lv: this thread's row's L, loaded before the next tile's copy is issued:
-  // the load counter is in order, so a load issued after the copy would make
-  // the wait for it a wait for the copy)
-  auto stream_rows = [&](float lv, const uint16_t* y2c, const uint16_t* yoc) {
-    if constexpr (KV) {
-      constexpr int TPR = NT / BN;
-      constexpr int DPT = D / TPR;
-      const int r = tid / TPR, part = tid % TPR;
-      float acc = 0.0f;
-#pragma unroll
-      for (int c = 0; c < DPT / 8; ++c) {
-        const int ch = part * (DPT / 8) + c;  // 16-byte chunk of the row
-        const int slot = r * D + 8 * (ch ^ vswz<D>(r));
-        const bf16x8 ov = *reinterpret_cast<const bf16x8*>(yoc + slot);
-        const bf16x8 gv = *reinterpret_cast<const bf16x8*>(y2c + slot);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc += (float)ov[e] * (float)gv[e];
-      }
-#pragma unroll
-      for (int m = 1; m < TPR; m <<= 1) acc += __shfl_xor(acc, m, 64);
-      if (part == 0) {
-        srow[r] = make_float2(lse2(lv), acc);
-      }
+  // dKV pass: wave 0 copies (L2, D) of tile t's rows from the rows pass
+  // straight into LDS, one row per lane (rows past ql repeat the last one),
+  // with the same direct-to-LDS loads as the tiles (no registers held)
+  auto issue_rows = [&](int t, float4* srow) {
+    if (KV && wave == 0) {
+      const int first = tile_first(t);
+      const int n = min(ql - first, 64);
+      const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(a.dq + b * a.q_sb + tile_head(t) * a.q_sh + (int64_t)first * a.q_sr), 0,
+          ((n - 1) * a.q_sr + 8) * 2, kRsrcWord3);
+      // (the lane index recomputed here, in an asm the compiler cannot hoist:
+      // kept live across the loop it was spilled, and its reload waited for
+      // the tile copies in flight)
+      int l;
+      asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)srow, 16,
+                                               min(l, n - 1) * a.q_sr * 2, 0, 0, 0);
     }
   };
 
@@ -301,20 +320,21 @@ __attribute__((amdgpu_waves_per_eu(BwdCfg<D, PASS>::WPE))) void fa_bwd_kernel(Bw
     return __builtin_bit_cast(bf16x8,
                               __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7));
   };
-  auto products = [&](const uint16_t* buf, bool is_y1, const bf16x8 (&xop)[FB][NDS],
-                      f32x4 (&out)[NKB][FB]) {
+  // the two 16-row blocks (2j, 2j + 1) of 32-row chunk j of the streamed tile
+  auto products = [&](const uint16_t* buf, bool is_y1, const bf16x8 (&xop)[FB][NDS], int j,
+                      f32x4 (&out)[2][FB]) {
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int fb = 0; fb < FB; ++fb) out[kb][fb] = f32x4{};
+      for (int fb = 0; fb < FB; ++fb) out[h][fb] = f32x4{};
 #pragma unroll
     for (int s = 0; s < NDS; ++s)
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        const bf16x8 yop = rread(buf, is_y1, s, kb);
+      for (int h = 0; h < 2; ++h) {
+        const bf16x8 yop = rread(buf, is_y1, s, 2 * j + h);
 #pragma unroll
         for (int fb = 0; fb < FB; ++fb)
-          out[kb][fb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(yop, xop[fb][s], out[kb][fb], 0, 0, 0);
+          out[h][fb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(yop, xop[fb][s], out[h][fb], 0, 0, 0);
       }
   };
 
@@ -323,27 +343,21 @@ __attribute__((amdgpu_waves_per_eu(BwdCfg<D, PASS>::WPE))) void fa_bwd_kernel(Bw
   // in stage 1): with the stage chosen at run time the compiler cannot tell
   // a tile's LDS reads from the copy of the next tile in flight, and made
   // every wave wait for that copy before reading.
-  auto step = [&](int t, const uint16_t* b1, const uint16_t* b2, const uint16_t* bo,
-                  uint16_t* n1, uint16_t* n2, uint16_t* no) {
+  auto step = [&](int t, const uint16_t* b1, const uint16_t* b2, const float4* srow,
+                  uint16_t* n1, uint16_t* n2, float4* nrow) {
     // (made provably uniform: every wave-level decision below depends on them)
     const int sbase = __builtin_amdgcn_readfirstlane(tile_first(t));
     const int th = __builtin_amdgcn_readfirstlane(tile_head(t));
-    float lv = 0.0f;
-    if constexpr (KV)
-      lv = a.L[(int64_t)(b * a.H + th) * ql + min(sbase + tid / (NT / BN), ql - 1)];
     wait_vmem();
     __syncthreads();
-    if (t + 1 < n_st) issue(t + 1, n1, n2, no);
-    if constexpr (KV) {
-      stream_rows(lv, b2, bo);
-      // every wave's srow stores done before any wave reads srow: an LDS-only
-      // wait and a bare barrier (__syncthreads' release fence would also
-      // wait for the next tile's copy in flight, which nothing here reads)
-      asm volatile("" ::: "memory");
-      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt, expcnt at their maxima
-      __builtin_amdgcn_s_barrier();
-      asm volatile("" ::: "memory");
+    if (t + 1 < n_st) {
+      issue(t + 1, n1, n2);
+      issue_rows(t + 1, nrow);
     }
+    // (nothing of the tile's work is scheduled above the copies: hoisted
+    // there, its LDS reads held registers across the copy code, and the D=64
+    // dK/dV pass spilled)
+    __builtin_amdgcn_sched_barrier(0);
     // does this wave see any (streamed, fixed) pair of the tile, and does the
     // tile need per-element masks?
     bool any = wave_active, need_mask;
@@ -361,39 +375,42 @@ __attribute__((amdgpu_waves_per_eu(BwdCfg<D, PASS>::WPE))) void fa_bwd_kernel(Bw
                   (WINDOW && sbase + BN - 1 > fw0 - off + a.window);
     }
     if (!any) return;
-    f32x4 sacc[NKB][FB], dpacc[NKB][FB];
-    // (D=256: waves raise their priority while they issue MFMA blocks, as in
-    // the forward; measured 2% faster for D=256, slower for D=64)
-    if constexpr (D == 256) set_prio<2>();
-    products(b1, true, x1op, sacc);
-    products(b2, false, x2op, dpacc);
-    if constexpr (D == 256) set_prio<0>();
-    bf16x8 pb[NKC][FB], dsb[NKC][FB];
+    // One 32-row chunk of the streamed tile at a time (its S and dP, P and dS,
+    // and its part of the second products): a third of the registers of the
+    // whole tile's scores at once.
 #pragma unroll
-    for (int fb = 0; fb < FB; ++fb) {
-      const int frow = fw0 + 16 * fb + c16;  // fixed row of this lane
-      // the streamed rows [s_lo, s_hi] this fixed row sees (causal, window);
-      // rows at or past s_end do not exist
-      const int s_end = KV ? ql : kl;
-      int s_lo = INT_MIN, s_hi = INT_MAX;
-      if constexpr (KV) {
-        if (CAUSAL) s_lo = frow - off;
-        if (WINDOW) s_hi = frow - off + a.window;
-      } else {
-        if (WINDOW) s_lo = off + frow - a.window;
-        if (CAUSAL) s_hi = off + frow;
-      }
+    for (int j = 0; j < NKC; ++j) {
+      f32x4 sacc[2][FB], dpacc[2][FB];
+      // (D=256: waves raise their priority while they issue MFMA blocks, as
+      // in the forward; measured 2% faster for D=256, slower for D=64)
+      if constexpr (D == 256) set_prio<2>();
+      products(b1, true, x1op, j, sacc);
+      products(b2, false, x2op, j, dpacc);
+      if constexpr (D == 256) set_prio<0>();
+      bf16x8 pb[FB], dsb[FB];
 #pragma unroll
-      for (int j = 0; j < NKC; ++j)
+      for (int fb = 0; fb < FB; ++fb) {
+        const int frow = fw0 + 16 * fb + c16;  // fixed row of this lane
+        // the streamed rows [s_lo, s_hi] this fixed row sees (causal, window);
+        // rows at or past s_end do not exist
+        const int s_end = KV ? ql : kl;
+        int s_lo = INT_MIN, s_hi = INT_MAX;
+        if constexpr (KV) {
+          if (CAUSAL) s_lo = frow - off;
+          if (WINDOW) s_hi = frow - off + a.window;
+        } else {
+          if (WINDOW) s_lo = off + frow - a.window;
+          if (CAUSAL) s_hi = off + frow;
+        }
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const int kb = 2 * j + (e >> 2), i = e & 3;
-          const int srel = 32 * (kb >> 1) + 8 * grp + 4 * (kb & 1) + i;  // streamed row in tile
+          const int h = e >> 2, i = e & 3;
+          const int srel = 32 * j + 8 * grp + 4 * h + i;  // streamed row in tile
           const int sr = sbase + srel;
-          const float s = sacc[kb][fb][i];
+          const float s = sacc[h][fb][i];
           float l2, dd;
           if constexpr (KV) {
-            const float2 sv = srow[srel];
+            const float2 sv = *reinterpret_cast<const float2*>(srow + srel);
             l2 = sv.x;
             dd = sv.y;
           } else {
@@ -405,8 +422,8 @@ __attribute__((amdgpu_waves_per_eu(BwdCfg<D, PASS>::WPE))) void fa_bwd_kernel(Bw
           if (need_mask) vis = sr < s_end && sr >= s_lo && sr <= s_hi;
           float x;
           if constexpr (HAS_MASK) {
-            const int h = KV ? th : hf;
-            const float m = mask_at<MASK>(a.mask, b * a.mask_sb + h * a.mask_sh +
+            const int mh = KV ? th : hf;
+            const float m = mask_at<MASK>(a.mask, b * a.mask_sb + mh * a.mask_sh +
                                                       (int64_t)min(qi, ql - 1) * a.mask_sr +
                                                       min(kj, kl - 1));
             vis = vis && m != -INFINITY;
@@ -415,50 +432,52 @@ __attribute__((amdgpu_waves_per_eu(BwdCfg<D, PASS>::WPE))) void fa_bwd_kernel(Bw
             x = __builtin_fmaf(s, a.c, -l2);
           }
           const float p = vis ? __builtin_amdgcn_exp2f(x) : 0.0f;
-          const float ds = p * (dpacc[kb][fb][i] - dd);
-          pb[j][fb][e] = (__bf16)p;
-          dsb[j][fb][e] = (__bf16)ds;
+          const float ds = p * (dpacc[h][fb][i] - dd);
+          pb[fb][e] = (__bf16)p;
+          dsb[fb][e] = (__bf16)ds;
           // (with a mask, one chunk's mask loads at a time: all of them in
           // flight at once would not fit the registers)
           if (HAS_MASK && e == 7) __builtin_amdgcn_sched_barrier(0);
         }
-    }
-    // second products: dQ^T += Y1^T dS^T, or dK^T += Y1^T dS and dV^T += Y2^T P
-    if constexpr (D == 256) set_prio<2>();
+      }
+      // second products of the chunk: dQ^T += Y1^T dS^T, or dK^T += Y1^T dS
+      // and dV^T += Y2^T P
+      if constexpr (D == 256) set_prio<2>();
 #pragma unroll
-    for (int da = 0; da < NDA; ++da)
-#pragma unroll
-      for (int j = 0; j < NKC; ++j) {
+      for (int da = 0; da < NDA; ++da) {
         const int d = dpart * NDA + da;
         const bf16x8 t1 = tread(b1, true, d, j);
 #pragma unroll
         for (int fb = 0; fb < FB; ++fb)
-          acc1[da][fb] =
-              __builtin_amdgcn_mfma_f32_16x16x32_bf16(t1, dsb[j][fb], acc1[da][fb], 0, 0, 0);
+          acc1[da][fb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(t1, dsb[fb], acc1[da][fb], 0, 0, 0);
         if constexpr (KV) {
           const bf16x8 t2 = tread(b2, false, d, j);
 #pragma unroll
           for (int fb = 0; fb < FB; ++fb)
             acc2[da][fb] =
-                __builtin_amdgcn_mfma_f32_16x16x32_bf16(t2, pb[j][fb], acc2[da][fb], 0, 0, 0);
+                __builtin_amdgcn_mfma_f32_16x16x32_bf16(t2, pb[fb], acc2[da][fb], 0, 0, 0);
         }
       }
-    if constexpr (D == 256) set_prio<0>();
+      if constexpr (D == 256) set_prio<0>();
+    }
   };
   // (the D=64 dK/dV pass with a mask or window has too few registers to keep
   // both stages' addresses: one step per iteration there)
   constexpr bool PAIRED = !(D == 64 && KV && (WINDOW || HAS_MASK));
-  if (n_st > 0) issue(0, y1s0, y2s0, yos0);
+  if (n_st > 0) {
+    issue(0, y1s0, y2s0);
+    issue_rows(0, srow0);
+  }
   if constexpr (PAIRED) {
     for (int t = 0; t < n_st; t += 2) {
-      step(t, y1s0, y2s0, yos0, y1s1, y2s1, yos1);
-      if (t + 1 < n_st) step(t + 1, y1s1, y2s1, yos1, y1s0, y2s0, yos0);
+      step(t, y1s0, y2s0, srow0, y1s1, y2s1, srow1);
+      if (t + 1 < n_st) step(t + 1, y1s1, y2s1, srow1, y1s0, y2s0, srow0);
     }
   } else {
     for (int t = 0; t < n_st; ++t) {
       const bool odd = t & 1;
-      step(t, odd ? y1s1 : y1s0, odd ? y2s1 : y2s0, odd ? yos1 : yos0, odd ? y1s0 : y1s1,
-           odd ? y2s0 : y2s1, odd ? yos0 : yos1);
+      step(t, odd ? y1s1 : y1s0, odd ? y2s1 : y2s0, odd ? srow1 : srow0, odd ? y1s0 : y1s1,
+           odd ? y2s0 : y2s1, odd ? srow0 : srow1);
     }
   }
 
@@ -499,18 +518,29 @@ hipError_t launch_bwd(const BwdArgs& a, unsigned grid, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// The three launches, in order: rows (L2, D into dQ's rows), dK/dV (reads
+// them), dQ (reads its rows' values, then overwrites the rows).
 template <int D, bool CAUSAL, bool WINDOW, int MASK>
 hipError_t dispatch_bwd(BwdArgs a, hipStream_t stream) {
-  if (a.ql > 0) {
-    a.n_ftiles = (a.ql + fixed_rows<D, kBwdQ>() - 1) / fixed_rows<D, kBwdQ>();
-    hipError_t e = launch_bwd<D, kBwdQ, CAUSAL, WINDOW, MASK>(
-        a, (unsigned)(a.n_ftiles * a.B * a.H), stream);
+  const int64_t qrows = (int64_t)a.B * a.H * a.ql;
+  if (qrows > 0) {
+    constexpr int RPB = 256 / (D / 8);
+    const int64_t groups = (qrows + RPB - 1) / RPB;
+    hipLaunchKernelGGL(fa_bwd_rows_kernel<D>, dim3((unsigned)std::min<int64_t>(groups, 1 << 16)),
+                       dim3(256), 0, stream, a);
+    const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (a.kl > 0) {
     a.n_ftiles = (a.kl + fixed_rows<D, kBwdKV>() - 1) / fixed_rows<D, kBwdKV>();
-    return launch_bwd<D, kBwdKV, CAUSAL, WINDOW, MASK>(
+    const hipError_t e = launch_bwd<D, kBwdKV, CAUSAL, WINDOW, MASK>(
         a, (unsigned)(a.n_ftiles * a.B * a.Hkv), stream);
+    if (e != hipSuccess) return e;
+  }
+  if (a.ql > 0) {
+    a.n_ftiles = (a.ql + fixed_rows<D, kBwdQ>() - 1) / fixed_rows<D, kBwdQ>();
+    return launch_bwd<D, kBwdQ, CAUSAL, WINDOW, MASK>(a, (unsigned)(a.n_ftiles * a.B * a.H),
+                                                      stream);
   }
   return hipSuccess;
 }
