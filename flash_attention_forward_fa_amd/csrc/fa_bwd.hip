@@ -58,18 +58,20 @@ constexpr int kBwdQ = 0, kBwdKV = 1;
 // Per head dim and pass: W waves, FB fixed 16-row blocks per wave, BN streamed
 // rows per tile, WPE waves per SIMD (register budget).
 template <int D, int PASS> struct BwdCfg;
-// DS waves share each fixed block, each accumulating D/DS of the output dims
-// (the D=256 dK/dV pass: two waves per 16 key rows, each with half of dK and
-// dV, so that the accumulators allow two waves per SIMD; both compute the
-// block's full S and dP). The D=64 dQ pass keeps one 16-row block per wave at
-// four waves per SIMD (two workgroups per CU): same results as two blocks at two
-// waves per SIMD, measured 1-2.5% faster for the whole backward.
+// DS waves may share each fixed block, each accumulating D/DS of the output
+// dims (both then compute the block's full S and dP); every pass now runs
+// DS = 1. With the operand reads' XOR addressing the D=256 dK/dV pass holds
+// one 16-key block with its full dK and dV per wave at two waves per SIMD
+// (240 VGPRs; two waves per block: 4.96 -> 3.99 ms for D=256 GQA 8k causal),
+// and the D=64 dK/dV pass one block per wave at four waves per SIMD. The D=64
+// dQ pass keeps one 16-row block per wave at four waves per SIMD (two
+// workgroups per CU).
 template <> struct BwdCfg<64, kBwdQ> { static constexpr int W = 8, FB = 1, BN = 64, WPE = 4, DS = 1; };
-template <> struct BwdCfg<64, kBwdKV> { static constexpr int W = 8, FB = 2, BN = 64, WPE = 2, DS = 1; };
+template <> struct BwdCfg<64, kBwdKV> { static constexpr int W = 8, FB = 1, BN = 64, WPE = 4, DS = 1; };
 template <> struct BwdCfg<128, kBwdQ> { static constexpr int W = 8, FB = 1, BN = 64, WPE = 2, DS = 1; };
 template <> struct BwdCfg<128, kBwdKV> { static constexpr int W = 8, FB = 1, BN = 64, WPE = 2, DS = 1; };
 template <> struct BwdCfg<256, kBwdQ> { static constexpr int W = 8, FB = 1, BN = 64, WPE = 2, DS = 1; };
-template <> struct BwdCfg<256, kBwdKV> { static constexpr int W = 8, FB = 1, BN = 32, WPE = 2, DS = 2; };
+template <> struct BwdCfg<256, kBwdKV> { static constexpr int W = 8, FB = 1, BN = 32, WPE = 2, DS = 1; };
 template <int D, int PASS> constexpr int fixed_rows() {
   return BwdCfg<D, PASS>::W / BwdCfg<D, PASS>::DS * 16 * BwdCfg<D, PASS>::FB;
 }
@@ -99,6 +101,17 @@ struct BwdArgs {
   int64_t q_sb, q_sh, k_sb, k_sh;
   int q_sr, k_sr;
 };
+
+// x ^ c computed in the iteration that uses it: an asm that also takes the
+// loop's tile index (unused), so the compiler can neither hoist it out of the
+// loop nor fold it, and one base offset stays live in place of one register
+// per XOR pattern (c wave-uniform). Not volatile: it schedules as an ordinary
+// VALU instruction (a volatile asm held the LDS reads in place, 4-15% slower).
+__device__ __forceinline__ int xor_here(int x, int c, int t) {
+  int r;
+  asm("v_xor_b32 %0, %1, %2 ; tile %3" : "=v"(r) : "s"(c), "v"(x), "s"(t));
+  return r;
+}
 
 // log2-units logsumexp of a row; a row with no visible key (L = -inf) gets
 // +inf, so that every P of that row is 0
@@ -148,6 +161,7 @@ __attribute__((amdgpu_waves_per_eu(BwdCfg<D, PASS>::WPE))) void fa_bwd_kernel(Bw
   constexpr int FR = fixed_rows<D, PASS>();
   constexpr int NKB = BN / 16;  // 16-row blocks of a streamed tile
   constexpr int NKC = BN / 32;  // 32-row chunks (contraction steps of the second products)
+  static_assert(BN == 32 || BN == 64, "a tile is one or two 32-row chunks (one copying wave's rows)");
   constexpr int NDB = D / 16;   // 16-dim blocks
   constexpr int DS = C::DS;
   constexpr int NDA = NDB / DS;  // 16-dim blocks of this wave's accumulators
@@ -297,32 +311,45 @@ __attribute__((amdgpu_waves_per_eu(BwdCfg<D, PASS>::WPE))) void fa_bwd_kernel(Bw
   };
 
   // ---- operand reads from the LDS tiles ----
+  // Byte offsets in a tile of this lane's reads for s = 0, kb = 0 (row reads)
+  // and d = 0, j = 0, t = 0 (transposed reads), per swizzle (K-type for Y1,
+  // V-type for Y2). Row r's 16-byte chunk c sits at 2rD + 16 (c ^ sw(r)), and
+  // the rows a lane reads for other kb, j and t differ from these by 4 or 32
+  // rows, which leave sw unchanged; a row is a multiple of 128 bytes and the
+  // chunk index below D/8, so the other reads are these offsets XORed with
+  // 64 s (row reads: chunk 4s + grp) or 32 d (transposed: chunk 2d + (c16&3)/2),
+  // plus whole rows.
+  const int rr0 = key_of(0, c16);
+  const int tr0 = 8 * grp + (c16 >> 2), tx = (c16 & 3) >> 1;
+  const int rbase[2] = {2 * rr0 * D + 16 * (grp ^ kswz<D>(rr0)),
+                        2 * rr0 * D + 16 * (grp ^ vswz<D>(rr0))};
+  const int tbase[2] = {2 * tr0 * D + 16 * (tx ^ kswz<D>(tr0)) + 8 * (c16 & 1),
+                        2 * tr0 * D + 16 * (tx ^ vswz<D>(tr0)) + 8 * (c16 & 1)};
   // row read (A operand of S^T / dP^T): streamed row key_of(kb, c16), dims 32s + 8grp..
-  auto rread = [&](const uint16_t* buf, bool is_y1, int s, int kb) {
-    const int r = key_of(kb, c16);
-    const int sw = is_y1 ? kswz<D>(r) : vswz<D>(r);
-    // (one index off the tile: a short address chain from the buffer, so that
-    // the compiler keeps the buffer's alias scope on the read)
-    return *reinterpret_cast<const bf16x8*>(buf + (r * D + 8 * ((4 * s + grp) ^ sw)));
+  auto rread = [&](const uint16_t* buf, bool is_y1, int s, int kb, int t) {
+    const int x = rbase[is_y1 ? 0 : 1];
+    const int o = (s == 0 ? x : xor_here(x, 64 * s, t)) + 2 * D * (32 * (kb >> 1) + 4 * (kb & 1));
+    // (one offset from the tile: a short address chain from the buffer, so
+    // that the compiler keeps the buffer's alias scope on the read)
+    return *reinterpret_cast<const bf16x8*>(reinterpret_cast<const char*>(buf) + o);
   };
   // transposed read (A operand of the second products): dims 16d + c16, streamed
   // rows 32j + 8grp + (0..7)
-  auto tread = [&](const uint16_t* buf, bool is_y1, int d, int j) {
+  auto tread = [&](const uint16_t* buf, bool is_y1, int d, int j, int t) {
+    const int x = tbase[is_y1 ? 0 : 1];
+    const int o = xor_here(x, 32 * d, t) + 2 * D * 32 * j;
     s16x4 half[2];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int r = 32 * j + 8 * grp + 4 * t + (c16 >> 2);
-      const int col = 16 * d + 4 * (c16 & 3);
-      const int sw = is_y1 ? kswz<D>(r) : vswz<D>(r);
-      const uint16_t* addr = buf + (r * D + 8 * ((col >> 3) ^ sw) + (col & 7));
-      half[t] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)addr);
+    for (int u = 0; u < 2; ++u) {
+      const char* addr = reinterpret_cast<const char*>(buf) + (o + 2 * D * 4 * u);
+      half[u] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)addr);
     }
     return __builtin_bit_cast(bf16x8,
                               __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7));
   };
   // the two 16-row blocks (2j, 2j + 1) of 32-row chunk j of the streamed tile
   auto products = [&](const uint16_t* buf, bool is_y1, const bf16x8 (&xop)[FB][NDS], int j,
-                      f32x4 (&out)[2][FB]) {
+                      int t, f32x4 (&out)[2][FB]) {
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -331,7 +358,7 @@ __attribute__((amdgpu_waves_per_eu(BwdCfg<D, PASS>::WPE))) void fa_bwd_kernel(Bw
     for (int s = 0; s < NDS; ++s)
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const bf16x8 yop = rread(buf, is_y1, s, 2 * j + h);
+        const bf16x8 yop = rread(buf, is_y1, s, 2 * j + h, t);
 #pragma unroll
         for (int fb = 0; fb < FB; ++fb)
           out[h][fb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(yop, xop[fb][s], out[h][fb], 0, 0, 0);
@@ -384,8 +411,8 @@ __attribute__((amdgpu_waves_per_eu(BwdCfg<D, PASS>::WPE))) void fa_bwd_kernel(Bw
       // (D=256: waves raise their priority while they issue MFMA blocks, as
       // in the forward; measured 2% faster for D=256, slower for D=64)
       if constexpr (D == 256) set_prio<2>();
-      products(b1, true, x1op, j, sacc);
-      products(b2, false, x2op, j, dpacc);
+      products(b1, true, x1op, j, t, sacc);
+      products(b2, false, x2op, j, t, dpacc);
       if constexpr (D == 256) set_prio<0>();
       bf16x8 pb[FB], dsb[FB];
 #pragma unroll
@@ -446,12 +473,12 @@ __attribute__((amdgpu_waves_per_eu(BwdCfg<D, PASS>::WPE))) void fa_bwd_kernel(Bw
 #pragma unroll
       for (int da = 0; da < NDA; ++da) {
         const int d = dpart * NDA + da;
-        const bf16x8 t1 = tread(b1, true, d, j);
+        const bf16x8 t1 = tread(b1, true, d, j, t);
 #pragma unroll
         for (int fb = 0; fb < FB; ++fb)
           acc1[da][fb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(t1, dsb[fb], acc1[da][fb], 0, 0, 0);
         if constexpr (KV) {
-          const bf16x8 t2 = tread(b2, false, d, j);
+          const bf16x8 t2 = tread(b2, false, d, j, t);
 #pragma unroll
           for (int fb = 0; fb < FB; ++fb)
             acc2[da][fb] =
