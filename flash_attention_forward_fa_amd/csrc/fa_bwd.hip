@@ -18,12 +18,12 @@
 // tiles inside the band. Three launches, no atomics and no workspace:
 //
 //   rows pass:         per query row, L2_i = L_i log2(e) (+inf for a row with
-//                      no visible key) and D_i, stored as two floats at the
+//                      no visible key) and -D_i, stored as two floats at the
 //                      start of the row's dQ memory (dQ is written only by the
 //                      last launch, so until then its rows serve as scratch)
 //   dKV pass (kBwdKV): fixed = key rows (K, V), streamed = query rows of every
-//                      head of the group (Q, dO, and L2, D per row)
-//   dQ pass  (kBwdQ):  fixed = query rows (Q, dO, and their L2, D, read
+//                      head of the group (Q, dO, and L2, -D per row)
+//   dQ pass  (kBwdQ):  fixed = query rows (Q, dO, and their L2, -D, read
 //                      before the rows are overwritten), streamed = keys (K, V)
 //
 // The last two share one kernel template: a workgroup keeps a block of "fixed"
@@ -63,11 +63,12 @@ template <int D, int PASS> struct BwdCfg;
 // DS = 1. With the operand reads' XOR addressing the D=256 dK/dV pass holds
 // one 16-key block with its full dK and dV per wave at two waves per SIMD
 // (240 VGPRs; two waves per block: 4.96 -> 3.99 ms for D=256 GQA 8k causal),
-// and the D=64 dK/dV pass one block per wave at four waves per SIMD. The D=64
+// and the D=64 dK/dV pass one block per wave at four waves per SIMD, streaming
+// 128-row tiles (2% faster than 64 for D=64; slower for D=128). The D=64
 // dQ pass keeps one 16-row block per wave at four waves per SIMD (two
 // workgroups per CU).
 template <> struct BwdCfg<64, kBwdQ> { static constexpr int W = 8, FB = 1, BN = 64, WPE = 4, DS = 1; };
-template <> struct BwdCfg<64, kBwdKV> { static constexpr int W = 8, FB = 1, BN = 64, WPE = 4, DS = 1; };
+template <> struct BwdCfg<64, kBwdKV> { static constexpr int W = 8, FB = 1, BN = 128, WPE = 4, DS = 1; };
 template <> struct BwdCfg<128, kBwdQ> { static constexpr int W = 8, FB = 1, BN = 64, WPE = 2, DS = 1; };
 template <> struct BwdCfg<128, kBwdKV> { static constexpr int W = 8, FB = 1, BN = 64, WPE = 2, DS = 1; };
 template <> struct BwdCfg<256, kBwdQ> { static constexpr int W = 8, FB = 1, BN = 64, WPE = 2, DS = 1; };
@@ -113,11 +114,13 @@ __device__ __forceinline__ int xor_here(int x, int c, int t) {
   return r;
 }
 
+template <bool B> struct BoolTag { static constexpr bool value = B; };
+
 // log2-units logsumexp of a row; a row with no visible key (L = -inf) gets
 // +inf, so that every P of that row is 0
 __device__ __forceinline__ float lse2(float l) { return l == -INFINITY ? INFINITY : l * kLog2e; }
 
-// The rows pass: for every query row, (L2, D) = (lse2(L), sum_d O_d dO_d) as
+// The rows pass: for every query row, (L2, -D) = (lse2(L), -sum_d O_d dO_d) as
 // two floats at the start of the row's dQ memory (8 of its >= 128 bytes; dQ's
 // rows are 16-byte aligned). D/8 lanes per row, 16 bytes of O and dO each;
 // a grid-stride loop over groups of 256/(D/8) rows.
@@ -147,7 +150,7 @@ __global__ __launch_bounds__(256) void fa_bwd_rows_kernel(BwdArgs a) {
 #pragma unroll
     for (int m = 1; m < LPR; m <<= 1) acc += __shfl_xor(acc, m, 64);
     if (live && part == 0)
-      *reinterpret_cast<float2*>(a.dq + base) = make_float2(lse2(a.L[row]), acc);
+      *reinterpret_cast<float2*>(a.dq + base) = make_float2(lse2(a.L[row]), -acc);
   }
 }
 
@@ -161,7 +164,8 @@ __attribute__((amdgpu_waves_per_eu(BwdCfg<D, PASS>::WPE))) void fa_bwd_kernel(Bw
   constexpr int FR = fixed_rows<D, PASS>();
   constexpr int NKB = BN / 16;  // 16-row blocks of a streamed tile
   constexpr int NKC = BN / 32;  // 32-row chunks (contraction steps of the second products)
-  static_assert(BN == 32 || BN == 64, "a tile is one or two 32-row chunks (one copying wave's rows)");
+  static_assert(BN == 32 || BN == 64 || BN == 128, "a tile is 1, 2 or 4 chunks of 32 rows");
+  constexpr int NRW = BN > 64 ? BN / 64 : 1;  // waves that copy the tile's (L2, D) rows
   constexpr int NDB = D / 16;   // 16-dim blocks
   constexpr int DS = C::DS;
   constexpr int NDA = NDB / DS;  // 16-dim blocks of this wave's accumulators
@@ -181,8 +185,8 @@ __attribute__((amdgpu_waves_per_eu(BwdCfg<D, PASS>::WPE))) void fa_bwd_kernel(Bw
   // dKV pass: L2 and D of the streamed rows (the first 16 bytes of their dQ
   // rows: L2, D and two unused floats), one array per stage, copied with the
   // stage's tiles (64 entries: one per lane of the copying wave)
-  __shared__ float4 srow0[KV ? 64 : 1];
-  __shared__ float4 srow1[KV ? 64 : 1];
+  __shared__ float4 srow0[KV ? 64 * NRW : 1];
+  __shared__ float4 srow1[KV ? 64 * NRW : 1];
 
   const int tid = threadIdx.x;
   // wave-uniform wave index: every wave-level condition is a scalar branch
@@ -229,7 +233,7 @@ __attribute__((amdgpu_waves_per_eu(BwdCfg<D, PASS>::WPE))) void fa_bwd_kernel(Bw
           bf16x8, *reinterpret_cast<const u32x4*>(x2p + (int64_t)r * xr + 32 * s + 8 * grp));
     }
   }
-  // dQ pass: L2 and D of the fixed rows, from the rows pass (read here, before
+  // dQ pass: L2 and -D of the fixed rows, from the rows pass (read here, before
   // this workgroup overwrites its rows; a wave past the end reads the last row,
   // whose values it never uses)
   float l2f[FB], dfx[FB];
@@ -290,13 +294,14 @@ __attribute__((amdgpu_waves_per_eu(BwdCfg<D, PASS>::WPE))) void fa_bwd_kernel(Bw
     issue_tile<D, BN, NT, false>(y2_src(t), tile_first(t), nstream, y2d, tid, 64 * wave, y2off,
                                  yr);
   };
-  // dKV pass: wave 0 copies (L2, D) of tile t's rows from the rows pass
-  // straight into LDS, one row per lane (rows past ql repeat the last one),
+  // dKV pass: the first BN/64 waves (at least one) copy (L2, D) of tile t's
+  // rows from the rows pass straight into LDS, one row per lane (rows past ql
+  // repeat the last one),
   // with the same direct-to-LDS loads as the tiles (no registers held)
   auto issue_rows = [&](int t, float4* srow) {
-    if (KV && wave == 0) {
+    if (KV && wave < NRW) {
       const int first = tile_first(t);
-      const int n = min(ql - first, 64);
+      const int n = min(ql - first, BN);
       const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
           (void*)(a.dq + b * a.q_sb + tile_head(t) * a.q_sh + (int64_t)first * a.q_sr), 0,
           ((n - 1) * a.q_sr + 8) * 2, kRsrcWord3);
@@ -305,8 +310,8 @@ __attribute__((amdgpu_waves_per_eu(BwdCfg<D, PASS>::WPE))) void fa_bwd_kernel(Bw
       // the tile copies in flight)
       int l;
       asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)srow, 16,
-                                               min(l, n - 1) * a.q_sr * 2, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(srow + 64 * wave), 16,
+                                               min(64 * wave + l, n - 1) * a.q_sr * 2, 0, 0, 0);
     }
   };
 
@@ -348,12 +353,9 @@ __attribute__((amdgpu_waves_per_eu(BwdCfg<D, PASS>::WPE))) void fa_bwd_kernel(Bw
                               __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7));
   };
   // the two 16-row blocks (2j, 2j + 1) of 32-row chunk j of the streamed tile
+  // (out enters holding the accumulators' starting values)
   auto products = [&](const uint16_t* buf, bool is_y1, const bf16x8 (&xop)[FB][NDS], int j,
                       int t, f32x4 (&out)[2][FB]) {
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int fb = 0; fb < FB; ++fb) out[h][fb] = f32x4{};
 #pragma unroll
     for (int s = 0; s < NDS; ++s)
 #pragma unroll
@@ -407,65 +409,96 @@ __attribute__((amdgpu_waves_per_eu(BwdCfg<D, PASS>::WPE))) void fa_bwd_kernel(Bw
     // whole tile's scores at once.
 #pragma unroll
     for (int j = 0; j < NKC; ++j) {
+      // S from zero; for D=256, dP from -D of its query row, so that the
+      // product leaves dP - D (one subtraction per score fewer: 2.5% faster
+      // there, 1-2% slower for D=64 and 128, which keep the add)
+      constexpr bool DINIT = D == 256;
       f32x4 sacc[2][FB], dpacc[2][FB];
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int fb = 0; fb < FB; ++fb) {
+          sacc[h][fb] = f32x4{};
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            dpacc[h][fb][i] =
+                !DINIT ? 0.0f
+                : KV   ? reinterpret_cast<const float2*>(srow + 32 * j + 8 * grp + 4 * h + i)->y
+                       : dfx[fb];
+        }
       // (D=256: waves raise their priority while they issue MFMA blocks, as
       // in the forward; measured 2% faster for D=256, slower for D=64)
       if constexpr (D == 256) set_prio<2>();
       products(b1, true, x1op, j, t, sacc);
       products(b2, false, x2op, j, t, dpacc);
       if constexpr (D == 256) set_prio<0>();
+      // P and dS of the chunk; the per-element visibility tests only on tiles
+      // that need them (MK), as a branch of its own: folded into selects, they
+      // ran on every tile and were about half of the D=64 passes' VALU work
       bf16x8 pb[FB], dsb[FB];
+      auto p_ds = [&](auto mk) {
+        constexpr bool MK = decltype(mk)::value;
 #pragma unroll
-      for (int fb = 0; fb < FB; ++fb) {
-        const int frow = fw0 + 16 * fb + c16;  // fixed row of this lane
-        // the streamed rows [s_lo, s_hi] this fixed row sees (causal, window);
-        // rows at or past s_end do not exist
-        const int s_end = KV ? ql : kl;
-        int s_lo = INT_MIN, s_hi = INT_MAX;
-        if constexpr (KV) {
-          if (CAUSAL) s_lo = frow - off;
-          if (WINDOW) s_hi = frow - off + a.window;
-        } else {
-          if (WINDOW) s_lo = off + frow - a.window;
-          if (CAUSAL) s_hi = off + frow;
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int h = e >> 2, i = e & 3;
-          const int srel = 32 * j + 8 * grp + 4 * h + i;  // streamed row in tile
-          const int sr = sbase + srel;
-          const float s = sacc[h][fb][i];
-          float l2, dd;
+        for (int fb = 0; fb < FB; ++fb) {
+          const int frow = fw0 + 16 * fb + c16;  // fixed row of this lane
+          // the streamed rows [s_lo, s_hi] this fixed row sees (causal,
+          // window); rows at or past s_end do not exist
+          const int s_end = KV ? ql : kl;
+          int s_lo = INT_MIN, s_hi = INT_MAX;
           if constexpr (KV) {
-            const float2 sv = *reinterpret_cast<const float2*>(srow + srel);
-            l2 = sv.x;
-            dd = sv.y;
+            if (CAUSAL) s_lo = frow - off;
+            if (WINDOW) s_hi = frow - off + a.window;
           } else {
-            l2 = l2f[fb];
-            dd = dfx[fb];
+            if (WINDOW) s_lo = off + frow - a.window;
+            if (CAUSAL) s_hi = off + frow;
           }
-          const int qi = KV ? sr : frow, kj = KV ? frow : sr;
-          bool vis = true;
-          if (need_mask) vis = sr < s_end && sr >= s_lo && sr <= s_hi;
-          float x;
-          if constexpr (HAS_MASK) {
-            const int mh = KV ? th : hf;
-            const float m = mask_at<MASK>(a.mask, b * a.mask_sb + mh * a.mask_sh +
-                                                      (int64_t)min(qi, ql - 1) * a.mask_sr +
-                                                      min(kj, kl - 1));
-            vis = vis && m != -INFINITY;
-            x = __builtin_fmaf(s, a.c, kLog2e * m) - l2;
-          } else {
-            x = __builtin_fmaf(s, a.c, -l2);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int h = e >> 2, i = e & 3;
+            const int srel = 32 * j + 8 * grp + 4 * h + i;  // streamed row in tile
+            const int sr = sbase + srel;
+            const float s = sacc[h][fb][i];
+            float l2, dd;
+            if constexpr (KV) {
+              const float2 sv = *reinterpret_cast<const float2*>(srow + srel);
+              l2 = sv.x;
+              dd = sv.y;
+            } else {
+              l2 = l2f[fb];
+              dd = dfx[fb];
+            }
+            const int qi = KV ? sr : frow, kj = KV ? frow : sr;
+            bool vis = true;
+            if constexpr (MK) vis = sr < s_end && sr >= s_lo && sr <= s_hi;
+            float x;
+            if constexpr (HAS_MASK) {
+              const int mh = KV ? th : hf;
+              const float m = mask_at<MASK>(a.mask, b * a.mask_sb + mh * a.mask_sh +
+                                                        (int64_t)min(qi, ql - 1) * a.mask_sr +
+                                                        min(kj, kl - 1));
+              vis = vis && m != -INFINITY;
+              x = __builtin_fmaf(s, a.c, kLog2e * m) - l2;
+            } else {
+              x = __builtin_fmaf(s, a.c, -l2);
+            }
+            const float p = (MK || HAS_MASK) ? (vis ? __builtin_amdgcn_exp2f(x) : 0.0f)
+                                             : __builtin_amdgcn_exp2f(x);
+            const float ds = p * (DINIT ? dpacc[h][fb][i] : dpacc[h][fb][i] + dd);  // dd = -D
+            pb[fb][e] = (__bf16)p;
+            dsb[fb][e] = (__bf16)ds;
+            // (with a mask, one chunk's mask loads at a time: all of them in
+            // flight at once would not fit the registers)
+            if (HAS_MASK && e == 7) __builtin_amdgcn_sched_barrier(0);
           }
-          const float p = vis ? __builtin_amdgcn_exp2f(x) : 0.0f;
-          const float ds = p * (dpacc[h][fb][i] - dd);
-          pb[fb][e] = (__bf16)p;
-          dsb[fb][e] = (__bf16)ds;
-          // (with a mask, one chunk's mask loads at a time: all of them in
-          // flight at once would not fit the registers)
-          if (HAS_MASK && e == 7) __builtin_amdgcn_sched_barrier(0);
         }
+      };
+      if (need_mask) {
+        // (an empty volatile asm: the compiler can neither speculate this
+        // side nor merge the two into selects)
+        asm volatile("");
+        p_ds(BoolTag<true>{});
+      } else {
+        p_ds(BoolTag<false>{});
       }
       // second products of the chunk: dQ^T += Y1^T dS^T, or dK^T += Y1^T dS
       // and dV^T += Y2^T P

@@ -412,7 +412,7 @@ int fa_paged_fwd(const void *q, const void *k_cache, const void *v_cache, const 
  *   dV    bf16 bits [batch, n_kv_heads, kl, head_dim] (written, fully).
  *   stream hipStream_t to enqueue on (NULL: the default stream).
  *
- * Three kernel launches on `stream`: per query row, L log2(e) and D_i into
+ * Three kernel launches on `stream`: per query row, L log2(e) and -D_i into
  * the first 8 bytes of the row's dQ memory (dQ serves as scratch until the
  * last launch overwrites it), then dK and dV, then dQ; no atomics, so the
  * result is deterministic. Same validation and status codes as fa_train_fwd
