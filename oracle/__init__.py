@@ -56,6 +56,10 @@ def _bind(path):
     lib.fa_oracle_bwd_swa.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64,
                                       ctypes.c_float, ctypes.c_int, i64, vp, vp, vp, ctypes.c_int]
     lib.fa_oracle_bwd_swa.restype = ctypes.c_int
+    lib.fa_oracle_bwd_sinks.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64,
+                                        i64, ctypes.c_float, ctypes.c_int, i64, vp, vp,
+                                        ctypes.c_int]
+    lib.fa_oracle_bwd_sinks.restype = ctypes.c_int
     return lib
 
 
@@ -179,6 +183,26 @@ def bwd(q, k, v, mask, L, dO, B, H, Hkv, ql, kl, D, scale, causal, n_threads=Non
     return dQ, dK, dV
 
 
+def bwd_sinks(q, k, v, mask, L, dO, B, H, Hkv, ql, kl, D, scale, causal, sinks, window=None,
+              n_threads=None, lib=None):
+    """The gradient of sum(O * dO) with respect to each query head's sink
+    logit: dsink_h = -sum over (b, i) of exp(sink_h - L_i) * D_i, with D_i the
+    backward's sum_j P_ij dP_ij. L: the forward's logsumexp with the same sinks.
+    Returns dsinks [H], f32. (dQ, dK and dV with sinks are bwd() given that L.)"""
+    qf, kf, vf, mf, lf, gf = _f32(q), _f32(k), _f32(v), _f32(mask), _f32(L), _f32(dO)
+    sf = np.ascontiguousarray(sinks, dtype=np.float32)
+    if sf.shape != (H,):
+        raise ValueError(f"sinks must have shape ({H},)")
+    out = np.empty(H, dtype=np.float32)
+    lib = lib or _load()
+    rc = lib.fa_oracle_bwd_sinks(_ptr(qf), _ptr(kf), _ptr(vf), _ptr(mf), _ptr(lf), _ptr(gf), B, H,
+                                 Hkv, ql, kl, D, D, float(scale), int(bool(causal)),
+                                 -1 if window is None else int(window), _ptr(sf), _ptr(out),
+                                 n_threads or default_threads())
+    _check(rc, "fa_oracle_bwd_sinks")
+    return out
+
+
 def fwd_dv(q, k, v, mask, B, H, Hkv, ql, kl, D, Dv, scale, causal, window=None, rows=None,
            n_threads=None, lib=None, sinks=None):
     """Forward with value width Dv (q, k: [.., D]; v: [B,Hkv,kl,Dv]). All rows
@@ -264,6 +288,15 @@ def bind_bwd(lib_path):
 
     def f(*args, **kw):
         return bwd(*args, lib=lib, **kw)
+    return f
+
+
+def bind_bwd_sinks(lib_path):
+    """A bwd_sinks(...) callable over another build of fa_oracle.c (mutation tests)."""
+    lib = _bind(lib_path)
+
+    def f(*args, **kw):
+        return bwd_sinks(*args, lib=lib, **kw)
     return f
 
 

@@ -50,7 +50,10 @@
  * page computes it, sum_j P_ij dP_ij (equal to rowsum(O_i * dO_i) for the
  * exact O). Pairs (i, j) whose key is not allowed for the row contribute
  * exactly zero and are not visited. dQ is computed per query row, dK and dV
- * per key, so both parallelise without shared sums.
+ * per key, so both parallelise without shared sums. With sinks the same
+ * equations hold given the forward's L (the sink has no value, so it adds
+ * nothing to dP or D_i); fa_oracle_bwd_sinks adds the sink logits' own
+ * gradient, dsink_h = -sum_{b,i} exp(sink_h - L_i) D_i.
  *
  * Arithmetic is IEEE f32 with no contraction (built with -ffp-contract=off);
  * expf and logf come from the C library.
@@ -522,4 +525,90 @@ int fa_oracle_bwd_swa(const float *q, const float *k, const float *v, const floa
         return 2;
     return fa_oracle_bwd_general(q, k, v, mask, L, dO, B, H, Hkv, ql, kl, D, D, scale, causal,
                                  window, NULL, 0, dQ, dK, dV, n_threads);
+}
+
+/* ---- the gradient of the sink logits ---- */
+
+typedef struct {
+    oracle_problem p;
+    const float *L, *dO;
+    float *Di; /* D_i of every query row, [B,H,ql] */
+} sink_ctx;
+
+/* D_i = sum_j P_ij dP_ij of each flat query row, as the backward computes it. */
+static void sink_rows(const void *ctx, int64_t begin, int64_t end, float *scratch)
+{
+    (void)scratch;
+    const sink_ctx *c = (const sink_ctx *)ctx;
+    const oracle_problem *p = &c->p;
+    for (int64_t row = begin; row < end; ++row) {
+        int64_t kvh, pos;
+        row_coords(p, row, &kvh, &pos);
+        const float *qr = p->q + row * p->D, *gr = c->dO + row * p->Dv;
+        const float *kh = p->k + kvh * p->kl * p->D, *vh = p->v + kvh * p->kl * p->Dv;
+        float d_i = 0.0f;
+        for (int64_t j = 0; j < p->kl; ++j) {
+            const float s = score(p, row, pos, j, qr, kh);
+            if (s == -INFINITY)
+                continue;
+            const float P = expf(s - c->L[row]);
+            float dp = 0.0f;
+            for (int64_t d = 0; d < p->Dv; ++d)
+                dp += gr[d] * vh[j * p->Dv + d];
+            d_i += P * dp;
+        }
+        c->Di[row] = d_i;
+    }
+}
+
+/*
+ * The gradient of the loss with respect to each query head's sink logit, for
+ * the forward with sinks (the reading above: one more softmax term, with a
+ * zero value). O_i depends on sink_h only through L_i, whose derivative is
+ * the sink's own weight p_i = exp(sink_h - L_i); so dO_i/dsink_h = -p_i O_i,
+ * and with D_i = <dO_i, O_i> = sum_j P_ij dP_ij (as the backward computes it)
+ *
+ *     dsink_h = -sum_{b,i} p_i D_i     (over every batch and row of head h).
+ *
+ * A sink of -inf has p_i = 0 and a zero gradient. Inputs as
+ * fa_oracle_bwd_general (L from the forward with the same sinks), sinks [H]
+ * (read), dsinks [H] (written). p_i and each product in f32, the sum over
+ * (b, i) in f64, in index order. Return codes as fa_oracle_fwd_general.
+ */
+int fa_oracle_bwd_sinks(const float *q, const float *k, const float *v, const float *mask,
+                        const float *L, const float *dO, int64_t B, int64_t H, int64_t Hkv,
+                        int64_t ql, int64_t kl, int64_t D, int64_t Dv, float scale, int causal,
+                        int64_t window, const float *sinks, float *dsinks, int n_threads)
+{
+    int rc = validate(q, k, v, B, H, Hkv, ql, kl, D, Dv);
+    if (rc)
+        return rc;
+    if (window >= 0 && !causal)
+        return 2;
+    const int64_t n = B * H * ql;
+    if (!sinks || !dsinks || (n > 0 && (!L || !dO)))
+        return 1;
+    float *Di = (float *)malloc(sizeof(float) * (size_t)(n > 0 ? n : 1));
+    if (!Di)
+        return 4;
+    sink_ctx c = {{q, k, v, mask, B, H, Hkv, ql, kl, D, Dv, scale, causal != 0,
+                   window < 0 ? -1 : window, sinks},
+                  L, dO, Di};
+    rc = run_parallel(n, n_threads, 1, sink_rows, &c);
+    if (!rc) {
+        for (int64_t h = 0; h < H; ++h) {
+            double acc = 0.0;
+            if (sinks[h] != -INFINITY) {
+                for (int64_t b = 0; b < B; ++b)
+                    for (int64_t i = 0; i < ql; ++i) {
+                        const int64_t row = (b * H + h) * ql + i;
+                        const float p_i = expf(sinks[h] - L[row]);
+                        acc += (double)(p_i * Di[row]);
+                    }
+            }
+            dsinks[h] = (float)(-acc);
+        }
+    }
+    free(Di);
+    return rc;
 }

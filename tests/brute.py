@@ -52,14 +52,16 @@ def attention_f64(q, k, v, mask, scale, causal, window=None, sinks=None):
     return O, L
 
 
-def attention_grads_f64(q, k, v, mask, dO, scale, causal, window=None):
+def attention_grads_f64(q, k, v, mask, dO, scale, causal, window=None, sinks=None):
     """Gradients of sum(O * dO) with respect to q, k, v for the same textbook
     definition, by torch's autograd in float64 on the CPU (a library routine
     serving as the differentiation step). Rows with no visible key have O = 0
-    and contribute nothing. Returns numpy (dQ, dK, dV)."""
+    and contribute nothing. Returns numpy (dQ, dK, dV); with sinks (one logit
+    per query head, one more softmax term with a zero value), also dsinks [H]."""
     import torch
     t = lambda a: torch.tensor(np.asarray(a, dtype=np.float64), dtype=torch.float64)
     qt, kt, vt = t(q).requires_grad_(), t(k).requires_grad_(), t(v).requires_grad_()
+    st = None if sinks is None else t(sinks).requires_grad_()
     B, H, ql, D = qt.shape
     Hkv, kl = kt.shape[1], kt.shape[2]
     group = H // Hkv
@@ -74,9 +76,18 @@ def attention_grads_f64(q, k, v, mask, dO, scale, causal, window=None):
         s = s.masked_fill(torch.arange(kl)[None, :] > q_abs, float("-inf"))
     if window is not None:
         s = s.masked_fill(torch.arange(kl)[None, :] < q_abs - window, float("-inf"))
+    if st is not None:
+        # the sink as one more column of every row's logits; its weight is
+        # dropped from the weighted sum (a zero value)
+        col = st[None, :, None, None].expand(s.shape[0], s.shape[1], s.shape[2], 1)
+        s = torch.cat([s, col], dim=-1)
     live = torch.isfinite(s).any(dim=-1, keepdim=True)
     s = torch.where(live, s, torch.zeros_like(s))
     p = torch.softmax(s, dim=-1) * live
+    if st is not None:
+        p = p[..., :kl]
     O = torch.matmul(p, vr)
     (O * t(dO)).sum().backward()
-    return qt.grad.numpy(), kt.grad.numpy(), vt.grad.numpy()
+    if st is None:
+        return qt.grad.numpy(), kt.grad.numpy(), vt.grad.numpy()
+    return qt.grad.numpy(), kt.grad.numpy(), vt.grad.numpy(), st.grad.numpy()

@@ -143,6 +143,89 @@ def pin_bwd_window_is_the_page_mask(bwd):
             assert np.array_equal(x, y), (ql, kl, w)
 
 
+def _lse_sinks(q, k, v, mask, scale, causal, sinks):
+    _, L = attention_f64(_widen(q), _widen(k), _widen(v), mask, scale, causal, sinks=sinks)
+    return L.astype(np.float32)
+
+
+def pin_bwd_sinks_autograd(bwd, bwd_sinks, B, H, Hkv, ql, kl, D, causal, mask_kind, seed,
+                           sinks):
+    """With per-head sinks (one more softmax term with a zero value), dQ, dK and
+    dV from the sink-aware L, and each sink's own gradient, against float64
+    autograd of the textbook definition. mask_kind: None, "finite", or "rows"
+    (some rows with no visible key, which keep only the sink)."""
+    scale = 1.0 / math.sqrt(D)
+    q, k, v, dO, mask = _case(seed, B, H, Hkv, ql, kl, D, mask_kind == "finite")
+    if mask_kind == "rows":
+        mask, _ = fagen.mask_f32(seed, B, H, ql, kl, 0.1, 2)
+    sinks = np.asarray(sinks, dtype=np.float32)
+    L = _lse_sinks(q, k, v, mask, scale, causal, sinks)
+    got = list(bwd(q, k, v, mask, L, dO, B, H, Hkv, ql, kl, D, scale, causal))
+    got.append(bwd_sinks(q, k, v, mask, L, dO, B, H, Hkv, ql, kl, D, scale, causal, sinks))
+    ref = attention_grads_f64(_widen(q).reshape(B, H, ql, D), _widen(k).reshape(B, Hkv, kl, D),
+                              _widen(v).reshape(B, Hkv, kl, D), mask,
+                              _widen(dO).reshape(B, H, ql, D), scale, causal, sinks=sinks)
+    for name, g, r in zip(("dQ", "dK", "dV", "dsinks"), got, ref):
+        err = np.abs(g - r).max() if r.size else 0.0
+        tol = 2e-5 * max(1.0, np.abs(r).max() if r.size else 1.0)
+        assert err <= tol, f"{name} with sinks vs f64 autograd: {err:.3e} > {tol:.3e}"
+
+
+def pin_bwd_sinks_finite_difference(bwd, bwd_sinks, seed=53):
+    """Central differences of sum(O * dO) of the float64 forward in each sink."""
+    B, H, Hkv, ql, kl, D, scale = 2, 3, 1, 6, 9, 8, 0.4
+    q, k, v, dO, _ = _case(seed, B, H, Hkv, ql, kl, D, False)
+    sinks = np.array([0.7, -1.3, 2.1], np.float32)
+    L = _lse_sinks(q, k, v, None, scale, True, sinks)
+    ds = bwd_sinks(q, k, v, None, L, dO, B, H, Hkv, ql, kl, D, scale, True, sinks)
+    qf, kf, vf, gf = (_widen(x).astype(np.float64) for x in (q, k, v, dO))
+    qf, gf = qf.reshape(B, H, ql, D), gf.reshape(B, H, ql, D)
+    kf, vf = kf.reshape(B, Hkv, kl, D), vf.reshape(B, Hkv, kl, D)
+    loss = lambda s: float((attention_f64(qf, kf, vf, None, scale, True, sinks=s)[0] * gf).sum())
+    h = 1e-4
+    for i in range(H):
+        plus, minus = sinks.astype(np.float64), sinks.astype(np.float64)
+        plus[i] += h
+        minus[i] -= h
+        fd = (loss(plus) - loss(minus)) / (2 * h)
+        assert abs(fd - ds[i]) <= 1e-4 * max(1.0, abs(fd)), \
+            f"dsink[{i}]: finite difference {fd:.6f}, oracle {ds[i]:.6f}"
+
+
+def pin_bwd_sinks_closed_forms(bwd, bwd_sinks):
+    """Sinks of -inf get exactly zero gradient; with every V row equal to one
+    vector c, O_i = (1 - p_i) c with p_i = exp(sink_h - L_i), so
+    dsink_h = -sum_i p_i (1 - p_i) <dO_i, c>."""
+    B, H, Hkv, ql, kl, D, scale = 1, 2, 1, 7, 11, 16, 0.35
+    q, k, _, dO, _ = _case(59, B, H, Hkv, ql, kl, D, False)
+    c = fagen.normal_bf16(59, 5, (D,), 1.0)
+    v = np.tile(c, B * Hkv * kl).reshape(B, Hkv, kl, D)
+    neg = np.full(H, -np.inf, np.float32)
+    L0 = _lse(q, k, v, None, scale, True)
+    assert np.all(bwd_sinks(q, k, v, None, L0, dO, B, H, Hkv, ql, kl, D, scale, True, neg) == 0)
+    sinks = np.array([1.5, -0.5], np.float32)
+    L = _lse_sinks(q, k, v, None, scale, True, sinks)
+    ds = bwd_sinks(q, k, v, None, L, dO, B, H, Hkv, ql, kl, D, scale, True, sinks)
+    Lf = L.astype(np.float64).reshape(B, H, ql)
+    gc = (_widen(dO).astype(np.float64).reshape(B, H, ql, D) @ _widen(c).astype(np.float64))
+    p = np.exp(sinks.astype(np.float64)[None, :, None] - Lf)
+    want = -(p * (1 - p) * gc).sum(axis=(0, 2))
+    assert np.abs(ds - want).max() <= 2e-5 * max(1.0, np.abs(want).max()), (ds, want)
+
+
+SINK_PINS = [
+    ("sinks_autograd", lambda b, s: pin_bwd_sinks_autograd(b, s, 2, 4, 2, 7, 13, 16, True, None, 61,
+                                                           [0.4, -2.0, 1.1, 3.0])),
+    ("sinks_autograd_masked", lambda b, s: pin_bwd_sinks_autograd(b, s, 1, 2, 2, 9, 6, 8, False,
+                                                                  "finite", 62, [-0.3, 0.9])),
+    ("sinks_autograd_empty_rows", lambda b, s: pin_bwd_sinks_autograd(b, s, 2, 2, 1, 8, 10, 8,
+                                                                      True, "rows", 63,
+                                                                      [0.5, -np.inf])),
+    ("sinks_finite_difference", pin_bwd_sinks_finite_difference),
+    ("sinks_closed_forms", pin_bwd_sinks_closed_forms),
+]
+
+
 AUTOGRAD_CASES = [
     # B, H, Hkv, ql, kl, D, causal, masked, seed
     (1, 1, 1, 1, 1, 4, False, False, 1),

@@ -17,3 +17,8 @@ def test_backward_oracle_kl_zero_gives_zero_dq():
     L = np.full((1, 1, 3), -np.inf, np.float32)
     dQ, dK, dV = oracle.bwd(q, k, k, None, L, q, 1, 1, 1, 3, 0, 4, 0.5, False)
     assert dQ.shape == (1, 1, 3, 4) and np.all(dQ == 0) and dK.size == 0 and dV.size == 0
+
+
+@pytest.mark.parametrize("name,pin", pins_bwd.SINK_PINS, ids=[n for n, _ in pins_bwd.SINK_PINS])
+def test_backward_sink_oracle_pin(name, pin):
+    pin(oracle.bwd, oracle.bwd_sinks)

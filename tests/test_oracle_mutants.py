@@ -160,3 +160,34 @@ def test_backward_pins_catch_planted_mistake(name):
             except (AssertionError, ValueError, FloatingPointError):
                 caught.append(pin_name)
         assert caught, f"no backward pin catches mutant {name}"
+
+
+# Planted mistakes in the sink-gradient part of the oracle, caught by the sink
+# pins of tests/pins_bwd.py.
+SINK_BWD_MUTANTS = {
+    "sink_grad_sign_flipped": ("dsinks[h] = (float)(-acc);", "dsinks[h] = (float)(acc);"),
+    "sink_grad_weight_inverted": ("const float p_i = expf(sinks[h] - L[row]);",
+                                  "const float p_i = expf(L[row] - sinks[h]);"),
+    "sink_grad_weight_dropped": ("acc += (double)(p_i * Di[row]);", "acc += (double)(Di[row]);"),
+    "sink_grad_first_batch_only": ("for (int64_t b = 0; b < B; ++b)\n                    for",
+                                   "for (int64_t b = 0; b < 1; ++b)\n                    for"),
+    "sink_grad_rows_of_head_zero": ("const int64_t row = (b * H + h) * ql + i;",
+                                    "const int64_t row = (b * H) * ql + i;"),
+    "sink_grad_D_unweighted": ("            d_i += P * dp;\n        }\n        c->Di[row] = d_i;",
+                               "            d_i += dp;\n        }\n        c->Di[row] = d_i;"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(SINK_BWD_MUTANTS))
+def test_sink_pins_catch_planted_mistake(name):
+    from tests import pins_bwd
+    with tempfile.TemporaryDirectory() as tmp:
+        path = _build_mutant(tmp, name, SINK_BWD_MUTANTS[name])
+        bwd, bwd_sinks = oracle.bind_bwd(path), oracle.bind_bwd_sinks(path)
+        caught = []
+        for pin_name, pin in pins_bwd.SINK_PINS:
+            try:
+                pin(bwd, bwd_sinks)
+            except (AssertionError, ValueError, FloatingPointError):
+                caught.append(pin_name)
+        assert caught, f"no sink pin catches mutant {name}"
