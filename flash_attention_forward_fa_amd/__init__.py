@@ -66,6 +66,10 @@ def lib():
         l.fa_train_bwd_strided.argtypes = [vp, vp, vp, vp, vp, vp, pll, pll, vp, ci, pll, ci, ci,
                                            ci, ci, ci, ci, ctypes.c_float, ci, ci, vp, vp, vp, vp]
         l.fa_train_bwd_strided.restype = ci
+        l.fa_train_bwd_sinks.argtypes = [vp, vp, vp, vp, vp, vp, pll, pll, vp, ci, pll, ci, ci,
+                                         ci, ci, ci, ci, ctypes.c_float, ci, ci, vp, vp, vp, vp,
+                                         vp, vp]
+        l.fa_train_bwd_sinks.restype = ci
         ul = ctypes.c_ulong
         l.fa_train_fwd_split.argtypes = [vp, vp, vp, ci, ci, ci, ci, ci, ci, ctypes.c_float, ci,
                                          ci, vp, ul, vp, vp, vp]
@@ -596,6 +600,65 @@ def train_bwd_strided(q, k, v, O, L, dO, mask=None, scale=None, causal=False, wi
     if status != 0:
         raise FAError(status, status_string(status))
     return dQ, dK, dV
+
+
+def fa_train_bwd_sinks(q, k, v, O, L, dO, q_strides, kv_strides, mask, mask_dtype,
+                       mask_strides, batch, n_heads, n_kv_heads, ql, kl, head_dim, scale, causal,
+                       window, sinks, dQ, dK, dV, dsinks, stream):
+    """The C entry point with raw integer pointers (0 for NULL) and stride
+    triples (or None); returns the status."""
+    return lib().fa_train_bwd_sinks(
+        q or None, k or None, v or None, O or None, L or None, dO or None, _strides3(q_strides),
+        _strides3(kv_strides), mask or None, int(mask_dtype), _strides3(mask_strides), batch,
+        n_heads, n_kv_heads, ql, kl, head_dim, float(scale), int(bool(causal)), int(window),
+        sinks or None, dQ or None, dK or None, dV or None, dsinks or None, stream or None)
+
+
+def train_bwd_sinks(q, k, v, O, L, dO, sinks, mask=None, scale=None, causal=False, window=None,
+                    stream=None):
+    """dQ, dK, dV, dsinks = train_bwd_sinks(q, k, v, O, L, dO, sinks, mask=None,
+                                          scale=None, causal=False, window=None)
+
+    The backward of train_fwd_dv with sinks (float32 [H] on q's device; the
+    value width equal to the key width): the gradients of train_bwd_strided
+    (O and L from that forward, with the same sinks), and dsinks, float32 [H],
+    the gradient of each query head's sink logit.
+    """
+    import torch
+    if not isinstance(q, torch.Tensor):
+        raise TypeError("q must be a bfloat16 tensor")
+    _check_inputs((("q", q), ("k", k), ("v", v), ("O", O), ("dO", dO)), q.device, layout="rows")
+    B, H, ql, D = q.shape
+    Bk, Hkv, kl, Dk = k.shape
+    if tuple(v.shape) != tuple(k.shape) or Bk != B or Dk != D:
+        raise ValueError("k and v must be [B, Hkv, kl, D] with q's B and D")
+    if O.shape != q.shape or dO.shape != q.shape:
+        raise ValueError("O and dO must be shaped like q")
+    if O.stride() != q.stride() or dO.stride() != q.stride() or v.stride() != k.stride():
+        raise ValueError("O and dO need q's strides, v needs k's")
+    _check_out(L, "L", q.device, torch.float32, (B, H, ql))
+    _check_out(sinks, "sinks", q.device, torch.float32, (H,))
+    if not _non_overlapping(q.shape, q.stride()):
+        q, O, dO = q.contiguous(), O.contiguous(), dO.contiguous()
+    if not _non_overlapping(k.shape, k.stride()):
+        k, v = k.contiguous(), v.contiguous()
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    dQ = torch.empty_strided(q.shape, q.stride(), dtype=torch.bfloat16, device=q.device)
+    dK = torch.empty_strided(k.shape, k.stride(), dtype=torch.bfloat16, device=q.device)
+    dV = torch.empty_strided(k.shape, k.stride(), dtype=torch.bfloat16, device=q.device)
+    dsinks = torch.empty(H, dtype=torch.float32, device=q.device)
+    s = stream if stream is not None else torch.cuda.current_stream(q.device)
+    mptr, mdt, mst = _mask_view(mask, q, k)
+    with torch.cuda.device(q.device):
+        status = fa_train_bwd_sinks(
+            q.data_ptr(), k.data_ptr(), v.data_ptr(), O.data_ptr(), L.data_ptr(), dO.data_ptr(),
+            q.stride()[:3], k.stride()[:3], mptr, mdt, mst, B, H, Hkv, ql, kl, D, scale, causal,
+            -1 if window is None else window, sinks.data_ptr(), dQ.data_ptr(), dK.data_ptr(),
+            dV.data_ptr(), dsinks.data_ptr(), s.cuda_stream)
+    if status != 0:
+        raise FAError(status, status_string(status))
+    return dQ, dK, dV, dsinks
 
 
 def _fwd_outputs(q, k, v, scale, out, lse, stream):

@@ -101,6 +101,8 @@ struct BwdArgs {
   // O, dO and dQ, k_* for K, V, dK and dV; L is contiguous [B, H, ql]
   int64_t q_sb, q_sh, k_sb, k_sh;
   int q_sr, k_sr;
+  const float* sinks;  // per-head sink logits [H] (natural log), or null
+  float* dsinks;       // their gradient [H] (written when sinks is set)
 };
 
 // x ^ c computed in the iteration that uses it: an asm that also takes the
@@ -149,9 +151,42 @@ __global__ __launch_bounds__(256) void fa_bwd_rows_kernel(BwdArgs a) {
     // (LPR divides 64: a row's lanes are consecutive lanes of one wave)
 #pragma unroll
     for (int m = 1; m < LPR; m <<= 1) acc += __shfl_xor(acc, m, 64);
-    if (live && part == 0)
-      *reinterpret_cast<float2*>(a.dq + base) = make_float2(lse2(a.L[row]), -acc);
+    if (live && part == 0) {
+      const float l2 = lse2(a.L[row]);
+      if (a.sinks) {
+        // with sinks, also the row's term of its head's sink gradient,
+        // p (-D) with p = exp(sink - L) the sink's weight (0 for a -inf
+        // sink), as a third float of the row
+        const float p = __builtin_amdgcn_exp2f(a.sinks[row / a.ql % a.H] * kLog2e - l2);
+        *reinterpret_cast<float4*>(a.dq + base) = make_float4(l2, -acc, p * -acc, 0.0f);
+      } else {
+        *reinterpret_cast<float2*>(a.dq + base) = make_float2(l2, -acc);
+      }
+    }
   }
+}
+
+// The sink gradient of head blockIdx.x: the sum, over every batch and row,
+// of the rows pass's third float, in a fixed order (each thread a strided
+// run of the rows, then a tree over the threads), so the result is
+// deterministic. It runs before the dQ pass overwrites the rows.
+__global__ __launch_bounds__(256) void fa_bwd_sinks_kernel(BwdArgs a) {
+  __shared__ float part[256];
+  const int h = blockIdx.x;
+  const int64_t n = (int64_t)a.B * a.ql;
+  float acc = 0.0f;
+  for (int64_t t = threadIdx.x; t < n; t += 256) {
+    const int64_t b = t / a.ql, i = t - b * a.ql;
+    acc += reinterpret_cast<const float*>(a.dq + b * a.q_sb + h * a.q_sh + i * a.q_sr)[2];
+  }
+  part[threadIdx.x] = acc;
+  __syncthreads();
+#pragma unroll
+  for (int w = 128; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) part[threadIdx.x] += part[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) a.dsinks[h] = part[0];
 }
 
 template <int D, int PASS, bool CAUSAL, bool WINDOW, int MASK>
@@ -578,8 +613,9 @@ hipError_t launch_bwd(const BwdArgs& a, unsigned grid, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// The three launches, in order: rows (L2, D into dQ's rows), dK/dV (reads
-// them), dQ (reads its rows' values, then overwrites the rows).
+// The launches, in order: rows (L2, -D into dQ's rows), with sinks the
+// per-head sum of the sink gradient's row terms, dK/dV (reads the rows'
+// values), dQ (reads its rows' values, then overwrites the rows).
 template <int D, bool CAUSAL, bool WINDOW, int MASK>
 hipError_t dispatch_bwd(BwdArgs a, hipStream_t stream) {
   const int64_t qrows = (int64_t)a.B * a.H * a.ql;
@@ -591,13 +627,19 @@ hipError_t dispatch_bwd(BwdArgs a, hipStream_t stream) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (a.kl > 0) {
+  if (a.sinks) {
+    // (every head, also with no rows: its gradient is then 0)
+    hipLaunchKernelGGL(fa_bwd_sinks_kernel, dim3((unsigned)a.H), dim3(256), 0, stream, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (a.kl > 0 && a.B > 0) {
     a.n_ftiles = (a.kl + fixed_rows<D, kBwdKV>() - 1) / fixed_rows<D, kBwdKV>();
     const hipError_t e = launch_bwd<D, kBwdKV, CAUSAL, WINDOW, MASK>(
         a, (unsigned)(a.n_ftiles * a.B * a.Hkv), stream);
     if (e != hipSuccess) return e;
   }
-  if (a.ql > 0) {
+  if (a.ql > 0 && a.B > 0) {
     a.n_ftiles = (a.ql + fixed_rows<D, kBwdQ>() - 1) / fixed_rows<D, kBwdQ>();
     return launch_bwd<D, kBwdQ, CAUSAL, WINDOW, MASK>(a, (unsigned)(a.n_ftiles * a.B * a.H),
                                                       stream);
@@ -632,7 +674,7 @@ int train_bwd(const void* q, const void* k, const void* v, const void* mask, int
               int batch, int n_heads, int n_kv_heads, int ql, int kl, int head_dim, float scale,
               int causal, int window, void* dQ, void* dK, void* dV, void* stream,
               const int64_t* q_strides = nullptr, const int64_t* k_strides = nullptr,
-              int64_t mask_sr = -1) {
+              int64_t mask_sr = -1, const float* sinks = nullptr, float* dsinks = nullptr) {
   if (batch < 0 || ql < 0 || kl < 0 || n_heads < 1 || n_kv_heads < 1) return FA_ERR_BAD_SIZE;
   if (n_heads % n_kv_heads != 0) return FA_ERR_HEAD_GROUPING;
   if (head_dim != 64 && head_dim != 128 && head_dim != 256) return FA_ERR_HEAD_DIM;
@@ -659,7 +701,11 @@ int train_bwd(const void* q, const void* k, const void* v, const void* mask, int
   if (view_overlaps(qs, qn, head_dim) || view_overlaps(ks, kn, head_dim)) return FA_ERR_STRIDE;
   const int64_t qrows = (int64_t)batch * n_heads * ql;
   const int64_t krows = (int64_t)batch * n_kv_heads * kl;
-  if (qrows == 0 && krows == 0) return FA_OK;
+  if (sinks && !dsinks) return FA_ERR_NULL_POINTER;
+  if ((sinks && !aligned_to(sinks, 4)) || (dsinks && sinks && !aligned_to(dsinks, 4)))
+    return FA_ERR_ALIGNMENT;
+  // (with sinks the heads' gradients are written even when there are no rows)
+  if (qrows == 0 && krows == 0 && !sinks) return FA_OK;
   if (qrows > 0 && (!q || !O || !L || !dO || !dQ)) return FA_ERR_NULL_POINTER;
   if (krows > 0 && (!k || !v || !dK || !dV)) return FA_ERR_NULL_POINTER;
   if (qrows > 0 && krows > 0 && (!q || !k || !v)) return FA_ERR_NULL_POINTER;
@@ -716,6 +762,8 @@ int train_bwd(const void* q, const void* k, const void* v, const void* mask, int
   // true scale and come out 0
   const float c = scale * kLog2e;
   a.c = c == 0.0f ? FLT_MIN : c;
+  a.sinks = sinks;
+  a.dsinks = sinks ? dsinks : nullptr;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool windowed = window >= 0;
   const hipError_t err =
@@ -779,4 +827,26 @@ extern "C" int fa_train_bwd_strided(const void* q, const void* k, const void* v,
   return train_bwd(q, k, v, mask, mask_dtype, ms[0], ms[1], O, L, dO, batch, n_heads, n_kv_heads,
                    ql, kl, head_dim, scale, causal, window, dQ, dK, dV, stream,
                    q_strides ? qs : nullptr, kv_strides ? ks : nullptr, ms[2]);
+}
+
+extern "C" int fa_train_bwd_sinks(const void* q, const void* k, const void* v, const void* O,
+                                  const float* L, const void* dO, const long long* q_strides,
+                                  const long long* kv_strides, const void* mask, int mask_dtype,
+                                  const long long* mask_strides, int batch, int n_heads,
+                                  int n_kv_heads, int ql, int kl, int head_dim, float scale,
+                                  int causal, int window, const float* sinks, void* dQ, void* dK,
+                                  void* dV, float* dsinks, void* stream) {
+  int64_t qs[3], ks[3];
+  for (int i = 0; i < 3; ++i) {
+    if (q_strides) qs[i] = q_strides[i];
+    if (kv_strides) ks[i] = kv_strides[i];
+  }
+  const int64_t mhead = (int64_t)ql * kl;
+  const int64_t ms[3] = {mask_strides ? mask_strides[0] : mhead * n_heads,
+                         mask_strides ? mask_strides[1] : mhead,
+                         mask_strides ? mask_strides[2] : kl};
+  if (mask && (ms[2] < 0 || ms[2] > 0x7fffffffLL)) return FA_ERR_MASK;
+  return train_bwd(q, k, v, mask, mask_dtype, ms[0], ms[1], O, L, dO, batch, n_heads, n_kv_heads,
+                   ql, kl, head_dim, scale, causal, window, dQ, dK, dV, stream,
+                   q_strides ? qs : nullptr, kv_strides ? ks : nullptr, ms[2], sinks, dsinks);
 }

@@ -34,7 +34,8 @@ extern "C" {
 enum fa_status {
     FA_OK = 0,
     FA_ERR_NULL_POINTER = 1,   /* q, k, v, O or L is NULL while its tensor is non-empty
-                                  (or a required table, length array or workspace)   */
+                                  (or a required table, length array or workspace, or
+                                  fa_train_bwd_sinks' dsinks with sinks set)          */
     FA_ERR_BAD_SIZE = 2,       /* batch, ql or kl < 0; n_heads or n_kv_heads < 1      */
     FA_ERR_HEAD_GROUPING = 3,  /* n_heads is not a multiple of n_kv_heads              */
     FA_ERR_HEAD_DIM = 4,       /* head dims not supported by the entry point: 64, 128
@@ -43,8 +44,8 @@ enum fa_status {
                                   (key, value) pairs (96, 64) and (192, 128)          */
     FA_ERR_SCALE = 5,          /* scale is NaN or infinite                              */
     FA_ERR_ALIGNMENT = 6,      /* q, k, v, O or a workspace not 16-byte aligned; L,
-                                  sinks, a block table or lengths not 4-byte; a mask
-                                  not aligned to its element                           */
+                                  sinks, dsinks, a block table or lengths not 4-byte;
+                                  a mask not aligned to its element                    */
     FA_ERR_TOO_LARGE = 7,      /* a grid or index would overflow the kernel's limits    */
     FA_ERR_LAUNCH = 8,         /* the HIP launch failed (hipGetLastError)               */
     FA_ERR_WINDOW = 9,         /* window < 0 (fa_train_fwd_swa); window >= 0 without
@@ -55,7 +56,8 @@ enum fa_status {
                                   split), or the workspace smaller than the split needs */
     FA_ERR_PAGED = 12,         /* fa_paged_fwd: block_size not a positive multiple of
                                   16, or no cache blocks for a non-empty table          */
-    FA_ERR_STRIDE = 13,        /* fa_train_fwd_strided, fa_train_bwd_strided: a negative
+    FA_ERR_STRIDE = 13,        /* the strided entry points (fa_train_*_strided,
+                                  fa_train_fwd_dv, fa_train_bwd_sinks): a negative
                                   stride, or the strides of a written tensor (O; dQ,
                                   dK, dV) map two of its elements to one address        */
     FA_ERR_SCRATCH = 14        /* fa_train_fwd_split_noalloc: the split-KV partials
@@ -484,6 +486,43 @@ int fa_train_bwd_strided(const void *q, const void *k, const void *v, const void
                          const long long *mask_strides, int batch, int n_heads, int n_kv_heads,
                          int ql, int kl, int head_dim, float scale, int causal, int window,
                          void *dQ, void *dK, void *dV, void *stream);
+
+/*
+ * fa_train_bwd_sinks - the backward of fa_train_fwd_dv with attention sinks
+ * (head_dim_v == head_dim): dQ, dK and dV as fa_train_bwd_strided, and the
+ * gradient of each query head's sink logit.
+ *
+ * The sink is one more term of every row's softmax with a zero value (the
+ * reading fa_train_fwd_dv states for the adjacent SDPA page's `sinks [Hq]`).
+ * O_i depends on sink_h only through L_i, whose derivative is the sink's own
+ * weight p_i = exp(sink_h - L_i), so dO_i/dsink_h = -p_i O_i and
+ *
+ *   dsinks[h] = -sum over every batch b and row i of head h of p_i D_i,
+ *               D_i = sum_d O_id dO_id.
+ *
+ * dQ, dK and dV need nothing more than the forward's L (which includes the
+ * sinks): the sink has no value, so it adds nothing to dP or D.
+ *
+ *   sinks   f32 [n_heads] (device, read; 4-byte aligned), the logits the
+ *           forward used, or NULL (then this is fa_train_bwd_strided and
+ *           dsinks is not touched)
+ *   dsinks  f32 [n_heads] (device, written fully, also when batch * ql = 0;
+ *           4-byte aligned); required when sinks is set (FA_ERR_NULL_POINTER)
+ *   L       the forward's logsumexp with the same sinks
+ *   others  as for fa_train_bwd_strided.
+ *
+ * One more launch than fa_train_bwd_strided: after the rows pass has put each
+ * row's term p_i (-D_i) into its dQ memory, one workgroup per head sums them
+ * in a fixed order, so dsinks is deterministic too. Allocates nothing; never
+ * synchronises.
+ */
+int fa_train_bwd_sinks(const void *q, const void *k, const void *v, const void *O,
+                       const float *L, const void *dO, const long long *q_strides,
+                       const long long *kv_strides, const void *mask, int mask_dtype,
+                       const long long *mask_strides, int batch, int n_heads, int n_kv_heads,
+                       int ql, int kl, int head_dim, float scale, int causal, int window,
+                       const float *sinks, void *dQ, void *dK, void *dV, float *dsinks,
+                       void *stream);
 
 /* Static, human-readable name of a status code (never NULL). */
 const char *fa_status_string(int status);

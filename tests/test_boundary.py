@@ -31,7 +31,7 @@ def test_header_declares_the_entry_points():
     assert {"fa_train_fwd", "fa_train_fwd_swa", "fa_train_fwd_ex", "fa_train_fwd_split",
             "fa_train_fwd_split_workspace", "fa_paged_fwd", "fa_train_bwd", "fa_train_bwd_swa",
             "fa_train_bwd_ex", "fa_train_fwd_strided", "fa_train_bwd_strided",
-            "fa_train_fwd_dv", "fa_status_string"} <= names
+            "fa_train_fwd_dv", "fa_train_bwd_sinks", "fa_status_string"} <= names
 
 
 def test_library_exports_every_declared_symbol():
@@ -380,6 +380,28 @@ def test_bwd_strided_invalid_arguments_are_rejected(over, code):
     args = dict(BWD_STRIDED_GOOD)
     args.update(over)
     assert fa.fa_train_bwd_strided(**args) == code
+
+
+BWD_SINKS_GOOD = dict(BWD_STRIDED_GOOD, sinks=A, dsinks=A)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(dsinks=0), 1), (dict(sinks=A + 2), 6), (dict(dsinks=A + 2), 6), (dict(dQ=0), 1),
+    (dict(head_dim=96), 4), (dict(q_strides=(-8, 512, 64)), 13), (dict(causal=0, window=3), 9),
+])
+def test_bwd_sinks_invalid_arguments_are_rejected(over, code):
+    """Host checks of fa_train_bwd_sinks, before any HIP call (no GPU here)."""
+    args = dict(BWD_SINKS_GOOD)
+    args.update(over)
+    assert fa.fa_train_bwd_sinks(**args) == code
+
+
+def test_bwd_sinks_binding_fails_loudly_without_gpu_tensors():
+    import torch
+    q = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
+    L = torch.zeros(1, 1, 4)
+    with pytest.raises(ValueError):
+        fa.train_bwd_sinks(q, q, q, q, L, q, torch.zeros(1))
 
 
 def test_strided_and_paged_bindings_fail_loudly_without_gpu_tensors():
