@@ -15,7 +15,8 @@
 // (D_i = rowsum(dO_i * O_i) equals the page's sum_j P_ij dP_ij when O is the
 // forward's output.) The WINDOW variants apply the forward's sliding window
 // (key j visible to row i iff q_abs - window <= j <= q_abs) and stream only the
-// tiles inside the band. Three launches, no atomics and no workspace:
+// tiles inside the band. Three launches (four with sinks), no atomics and no
+// workspace:
 //
 //   rows pass:         per query row, L2_i = L_i log2(e) (+inf for a row with
 //                      no visible key) and -D_i, stored as two floats at the
@@ -25,6 +26,10 @@
 //                      head of the group (Q, dO, and L2, -D per row)
 //   dQ pass  (kBwdQ):  fixed = query rows (Q, dO, and their L2, -D, read
 //                      before the rows are overwritten), streamed = keys (K, V)
+//
+// With attention sinks the rows pass also stores each row's term of its
+// head's sink gradient, which one more launch sums per head before the dQ
+// pass (fa_bwd_sinks_kernel).
 //
 // The last two share one kernel template: a workgroup keeps a block of "fixed"
 // rows in registers and streams tiles of the other side through LDS.
@@ -123,9 +128,9 @@ template <bool B> struct BoolTag { static constexpr bool value = B; };
 __device__ __forceinline__ float lse2(float l) { return l == -INFINITY ? INFINITY : l * kLog2e; }
 
 // The rows pass: for every query row, (L2, -D) = (lse2(L), -sum_d O_d dO_d) as
-// two floats at the start of the row's dQ memory (8 of its >= 128 bytes; dQ's
-// rows are 16-byte aligned). D/8 lanes per row, 16 bytes of O and dO each;
-// a grid-stride loop over groups of 256/(D/8) rows.
+// two floats at the start of the row's dQ memory (8 of its >= 128 bytes, 16
+// with sinks; dQ's rows are 16-byte aligned). D/8 lanes per row, 16 bytes of
+// O and dO each; a grid-stride loop over groups of 256/(D/8) rows.
 template <int D>
 __global__ __launch_bounds__(256) void fa_bwd_rows_kernel(BwdArgs a) {
   constexpr int LPR = D / 8;
