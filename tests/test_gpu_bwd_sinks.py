@@ -45,12 +45,15 @@ def _inputs(seed, B, H, Hkv, ql, kl, D, mask_kind):
 
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
 def test_backward_with_sinks_matches_oracle(case):
+    _run(case, fagen.SEED_BASE + 8100 + CASES.index(case))
+
+
+def _run(case, seed):
     import torch
     import flash_attention_forward_fa_amd as fa
     name, B, H, Hkv, ql, kl, D, causal, window, mask_kind, sinks = case
     print(f"case bwd-sinks {name}: B{B} H{H}/{Hkv} ql{ql} kl{kl} D{D} causal={causal} "
           f"window={window} mask={mask_kind} sinks={sinks}", flush=True)
-    seed = fagen.SEED_BASE + 8100 + CASES.index(case)
     q, k, v, dO, mask = _inputs(seed, B, H, Hkv, ql, kl, D, mask_kind)
     s = np.asarray(sinks, np.float32)
     scale = 1.0 / math.sqrt(D)
@@ -128,3 +131,33 @@ def test_sink_gradient_written_without_rows():
     assert st == 0, fa.status_string(st)
     torch.cuda.synchronize()
     assert torch.all(ds == 0)
+
+
+N_RANDOM = 16
+
+
+def _draw(i):
+    """Configuration of random case i (a pure function of i): head dim, batch,
+    GQA, ragged ql and kl (ql > kl too), causal / window / none, and sinks near
+    the log of a row's key count (some -inf)."""
+    r = np.random.default_rng(0x51F7 + 7919 * i)
+    D = int(r.choice([64, 128, 256]))
+    B = int(r.integers(1, 3))
+    Hkv = int(r.choice([1, 2]))
+    H = Hkv * int(r.choice([1, 2, 4]))
+    ql = int(r.choice([1, int(r.integers(2, 70)), int(r.integers(70, 300))], p=[0.1, 0.3, 0.6]))
+    kl = int(r.choice([int(r.integers(1, 60)), int(r.integers(60, 400))], p=[0.25, 0.75]))
+    kind = str(r.choice(["none", "causal", "window"]))
+    window = int(r.integers(0, 80)) if kind == "window" else None
+    sinks = (math.log(max(kl, 1)) + 2.0 * r.standard_normal(H)).astype(np.float32)
+    sinks[r.random(H) < 0.15] = -np.inf
+    return dict(D=D, B=B, Hkv=Hkv, H=H, ql=ql, kl=kl, causal=kind != "none", window=window,
+                sinks=sinks)
+
+
+@pytest.mark.parametrize("i", range(N_RANDOM))
+def test_random_backward_with_sinks_matches_oracle(i):
+    c = _draw(i)
+    case = (f"random{i}", c["B"], c["H"], c["Hkv"], c["ql"], c["kl"], c["D"], c["causal"],
+            c["window"], None, list(c["sinks"]))
+    _run(case, fagen.SEED_BASE + 8200 + i)
