@@ -60,6 +60,10 @@ def _bind(path):
                                         i64, ctypes.c_float, ctypes.c_int, i64, vp, vp,
                                         ctypes.c_int]
     lib.fa_oracle_bwd_sinks.restype = ctypes.c_int
+    lib.fa_oracle_bwd_given_o.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
+                                          i64, i64, ctypes.c_float, ctypes.c_int, i64, vp, vp,
+                                          vp, ctypes.c_int]
+    lib.fa_oracle_bwd_given_o.restype = ctypes.c_int
     return lib
 
 
@@ -156,10 +160,12 @@ def fwd_rows(q, k, v, mask, B, H, Hkv, ql, kl, D, scale, causal, rows, n_threads
 
 
 def bwd(q, k, v, mask, L, dO, B, H, Hkv, ql, kl, D, scale, causal, n_threads=None,
-        lib=None, window=None):
+        lib=None, window=None, O=None):
     """Backward (the page's FA-2 backward oracle). q/k/v/dO: bf16 bits or f32;
     mask f32 or None; L: the forward's natural-log logsumexp [B,H,ql];
-    window: None or a sliding window (>= 0, with causal).
+    window: None or a sliding window (>= 0, with causal). O: None (D_i is
+    sum_j P_ij dP_ij) or the O [B,H,ql,D] (bf16 bits or f32) that
+    D_i = rowsum(O_i * dO_i) is read from.
 
     Returns (dQ [B,H,ql,D], dK [B,Hkv,kl,D], dV [B,Hkv,kl,D]), all f32."""
     qf, kf, vf, mf, lf, gf = _f32(q), _f32(k), _f32(v), _f32(mask), _f32(L), _f32(dO)
@@ -167,7 +173,17 @@ def bwd(q, k, v, mask, L, dO, B, H, Hkv, ql, kl, D, scale, causal, n_threads=Non
     dK = np.empty((B, Hkv, kl, D), dtype=np.float32)
     dV = np.empty((B, Hkv, kl, D), dtype=np.float32)
     lib = lib or _load()
-    if window is not None:
+    if O is not None:
+        of = _f32(O)
+        if of.size != B * H * ql * D:
+            raise ValueError(f"O must hold {B * H * ql * D} values")
+        rc = lib.fa_oracle_bwd_given_o(_ptr(qf), _ptr(kf), _ptr(vf), _ptr(mf), _ptr(lf),
+                                       _ptr(gf), _ptr(of), B, H, Hkv, ql, kl, D, D, float(scale),
+                                       int(bool(causal)), -1 if window is None else int(window),
+                                       _ptr(dQ), _ptr(dK), _ptr(dV),
+                                       n_threads or default_threads())
+        _check(rc, "fa_oracle_bwd_given_o")
+    elif window is not None:
         rc = lib.fa_oracle_bwd_swa(_ptr(qf), _ptr(kf), _ptr(vf), _ptr(mf), _ptr(lf), _ptr(gf), B,
                                    H, Hkv, ql, kl, D, float(scale), int(bool(causal)),
                                    int(window), _ptr(dQ), _ptr(dK), _ptr(dV),

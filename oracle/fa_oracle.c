@@ -48,7 +48,10 @@
  * where the sums of dK_j and dV_j run over the query rows of every query head
  * of the kv head's group (head by head, rows in order). D_i is written as the
  * page computes it, sum_j P_ij dP_ij (equal to rowsum(O_i * dO_i) for the
- * exact O). Pairs (i, j) whose key is not allowed for the row contribute
+ * exact O); fa_oracle_bwd_given_o instead reads D_i = rowsum(O_i * dO_i) from
+ * an O the caller hands in, the doc comment's own form for bf16-rounded
+ * inputs, so that both sides of a comparison see the same rounded O. Pairs
+ * (i, j) whose key is not allowed for the row contribute
  * exactly zero and are not visited. dQ is computed per query row, dK and dV
  * per key, so both parallelise without shared sums. With sinks the same
  * equations hold given the forward's L (the sink has no value, so it adds
@@ -358,6 +361,7 @@ void fa_oracle_round_bf16(const float *x, uint16_t *out, int64_t n)
 typedef struct {
     oracle_problem p;
     const float *L, *dO;
+    const float *O;        /* NULL, or the given O [B,H,ql,Dv] that D_i is read from */
     const int64_t *groups; /* kv heads b * Hkv + g computed, in output order */
     int64_t n_groups, G;
     float *Di;             /* D_i of every computed query row (output order) */
@@ -398,6 +402,12 @@ static void backward_rows(const void *ctx, int64_t begin, int64_t end, float *sc
                 dp += gr[d] * vh[j * p->Dv + d];
             dP[j] = dp;
             d_i += P[j] * dp;
+        }
+        if (c->O) { /* D_i = rowsum(O_i * dO_i) of the O the caller hands in */
+            const float *orow = c->O + row * p->Dv;
+            d_i = 0.0f;
+            for (int64_t d = 0; d < p->Dv; ++d)
+                d_i += orow[d] * gr[d];
         }
         c->Di[t] = d_i;
         float *dq = c->dQ + t * p->D;
@@ -451,18 +461,20 @@ static void backward_keys(const void *ctx, int64_t begin, int64_t end, float *sc
 
 /*
  * The general backward. Inputs as fa_oracle_fwd_general, plus L [B,H,ql] (the
- * forward's natural-log logsumexp) and dO [B,H,ql,Dv]. groups: the kv heads
+ * forward's natural-log logsumexp), dO [B,H,ql,Dv] and O (NULL: D_i is
+ * sum_j P_ij dP_ij; else the O [B,H,ql,Dv] that D_i = rowsum(O_i * dO_i)
+ * reads). groups: the kv heads
  * (b * Hkv + g) to compute, or NULL for all of them in order; the outputs
  * hold the computed kv heads in that order: dQ [n_groups, H/Hkv, ql, D] (the
  * group's query heads), dK [n_groups, kl, D], dV [n_groups, kl, Dv]. With
  * groups NULL that is dQ [B,H,ql,D], dK [B,Hkv,kl,D], dV [B,Hkv,kl,Dv].
  * Return codes as fa_oracle_fwd_general.
  */
-int fa_oracle_bwd_general(const float *q, const float *k, const float *v, const float *mask,
-                          const float *L, const float *dO, int64_t B, int64_t H, int64_t Hkv,
-                          int64_t ql, int64_t kl, int64_t D, int64_t Dv, float scale, int causal,
-                          int64_t window, const int64_t *groups, int64_t n_groups, float *dQ,
-                          float *dK, float *dV, int n_threads)
+static int backward(const float *q, const float *k, const float *v, const float *mask,
+                    const float *L, const float *dO, const float *O, int64_t B, int64_t H,
+                    int64_t Hkv, int64_t ql, int64_t kl, int64_t D, int64_t Dv, float scale,
+                    int causal, int64_t window, const int64_t *groups, int64_t n_groups,
+                    float *dQ, float *dK, float *dV, int n_threads)
 {
     int rc = validate(q, k, v, B, H, Hkv, ql, kl, D, Dv);
     if (rc)
@@ -496,13 +508,44 @@ int fa_oracle_bwd_general(const float *q, const float *k, const float *v, const 
     }
     backward_ctx c = {{q, k, v, mask, B, H, Hkv, ql, kl, D, Dv, scale, causal != 0,
                        window < 0 ? -1 : window, NULL},
-                      L, dO, groups, n_groups, G, Di, dQ, dK, dV};
+                      L, dO, O, groups, n_groups, G, Di, dQ, dK, dV};
     rc = run_parallel(n_q, n_threads, (size_t)(2 * (kl > 0 ? kl : 1)), backward_rows, &c);
     if (!rc)
         rc = run_parallel(n_k, n_threads, 1, backward_keys, &c);
     free(Di);
     free(all);
     return rc;
+}
+
+int fa_oracle_bwd_general(const float *q, const float *k, const float *v, const float *mask,
+                          const float *L, const float *dO, int64_t B, int64_t H, int64_t Hkv,
+                          int64_t ql, int64_t kl, int64_t D, int64_t Dv, float scale, int causal,
+                          int64_t window, const int64_t *groups, int64_t n_groups, float *dQ,
+                          float *dK, float *dV, int n_threads)
+{
+    return backward(q, k, v, mask, L, dO, NULL, B, H, Hkv, ql, kl, D, Dv, scale, causal, window,
+                    groups, n_groups, dQ, dK, dV, n_threads);
+}
+
+/*
+ * The backward with D_i read from a given O [B,H,ql,Dv] (f32 values, e.g. the
+ * forward's bf16 output widened): D_i = rowsum(O_i * dO_i), the form the
+ * page's backward-helper doc comment states for bf16-rounded inputs. Every
+ * other step as fa_oracle_bwd_general, for every kv head (window < 0: none,
+ * else causal = 1 is needed, as fa_oracle_bwd_swa). O NULL: code 1.
+ */
+int fa_oracle_bwd_given_o(const float *q, const float *k, const float *v, const float *mask,
+                          const float *L, const float *dO, const float *O, int64_t B, int64_t H,
+                          int64_t Hkv, int64_t ql, int64_t kl, int64_t D, int64_t Dv, float scale,
+                          int causal, int64_t window, float *dQ, float *dK, float *dV,
+                          int n_threads)
+{
+    if (!O && B * H * ql * Dv > 0)
+        return 1;
+    if (window >= 0 && !causal)
+        return 2;
+    return backward(q, k, v, mask, L, dO, O, B, H, Hkv, ql, kl, D, Dv, scale, causal, window,
+                    NULL, 0, dQ, dK, dV, n_threads);
 }
 
 /* Backward of every kv head, Dv = D, no window. */

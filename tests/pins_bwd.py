@@ -226,6 +226,65 @@ SINK_PINS = [
 ]
 
 
+
+def pin_bwd_given_o_autograd(bwd, B, H, Hkv, ql, kl, D, causal, masked, seed, window=None):
+    """D_i read from a given O: handed the float64 forward's O (as f32), the
+    gradients equal float64 autograd of the textbook definition, for every
+    row of every head (an O row of the wrong row or head would not)."""
+    scale = 1.0 / math.sqrt(D)
+    q, k, v, dO, mask = _case(seed, B, H, Hkv, ql, kl, D, masked)
+    O, L = attention_f64(_widen(q), _widen(k), _widen(v), mask, scale, causal, window)
+    got = bwd(q, k, v, mask, L.astype(np.float32), dO, B, H, Hkv, ql, kl, D, scale, causal,
+              window=window, O=O.astype(np.float32))
+    ref = attention_grads_f64(_widen(q).reshape(B, H, ql, D), _widen(k).reshape(B, Hkv, kl, D),
+                              _widen(v).reshape(B, Hkv, kl, D), mask,
+                              _widen(dO).reshape(B, H, ql, D), scale, causal, window)
+    for name, g, r in zip(("dQ", "dK", "dV"), got, ref):
+        err = np.abs(g - r).max() if r.size else 0.0
+        tol = 2e-5 * max(1.0, np.abs(r).max() if r.size else 1.0)
+        assert err <= tol, f"{name} (given O) vs f64 autograd: {err:.3e} > {tol:.3e}"
+
+
+def pin_bwd_given_o_single_key(bwd):
+    """One key (kl = 1): P_i0 = 1 on every row that sees it, so with a given
+    O' the closed forms are dQ_i = scale (dO_i.v_0 - O'_i.dO_i) k_0,
+    dK_0 = scale sum_i (dO_i.v_0 - O'_i.dO_i) q_i over the group's rows and
+    dV_0 = sum_i dO_i; a row whose key is masked (P = 0) gives dQ_i = 0 and
+    adds nothing, whatever O'_i holds."""
+    B, H, Hkv, ql, kl, D, scale = 1, 2, 1, 5, 1, 8, 0.35
+    q, k, v, dO, _ = _case(71, B, H, Hkv, ql, kl, D, False)
+    qf, gf = (_widen(x).astype(np.float64).reshape(B, H, ql, D) for x in (q, dO))
+    k0, v0 = (_widen(x).astype(np.float64).reshape(D) for x in (k, v))
+    mask = np.zeros((B, H, ql, kl), np.float32)
+    mask[0, 1, 2, 0] = -np.inf
+    live = np.isfinite(mask[..., 0])
+    delta = np.random.default_rng(72).normal(0.0, 0.05, (B, H, ql, D))
+    Op = np.where(live[..., None], v0 + delta, 3.0 + delta)
+    L = np.where(live, scale * (qf @ k0), -np.inf).astype(np.float32)
+    dQ, dK, dV = bwd(q, k, v, mask, L, dO, B, H, Hkv, ql, kl, D, scale, False,
+                     O=Op.astype(np.float32))
+    c = np.where(live, gf @ v0 - (Op.astype(np.float32).astype(np.float64) * gf).sum(-1), 0.0)
+    want_dq = scale * c[..., None] * k0
+    want_dk = scale * (c[..., None] * qf).sum(axis=(1, 2))
+    want_dv = (live[..., None] * gf).sum(axis=(1, 2))
+    for name, g, w in (("dQ", dQ, want_dq), ("dK", dK.reshape(B, D), want_dk),
+                       ("dV", dV.reshape(B, D), want_dv)):
+        tol = 2e-5 * max(1.0, np.abs(w).max())
+        assert np.abs(g.reshape(w.shape) - w).max() <= tol, f"{name} (given O, one key)"
+    assert np.all(dQ[0, 1, 2] == 0.0)
+
+
+GIVEN_O_PINS = [
+    ("given_o_autograd", lambda f: pin_bwd_given_o_autograd(f, 2, 4, 2, 7, 13, 16, True, True,
+                                                            81)),
+    ("given_o_autograd_ql_gt_kl", lambda f: pin_bwd_given_o_autograd(f, 1, 2, 1, 12, 5, 8, True,
+                                                                     False, 82)),
+    ("given_o_autograd_window", lambda f: pin_bwd_given_o_autograd(f, 1, 2, 2, 9, 17, 16, True,
+                                                                   False, 83, window=3)),
+    ("given_o_single_key", pin_bwd_given_o_single_key),
+]
+
+
 AUTOGRAD_CASES = [
     # B, H, Hkv, ql, kl, D, causal, masked, seed
     (1, 1, 1, 1, 1, 4, False, False, 1),

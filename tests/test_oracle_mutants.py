@@ -191,3 +191,29 @@ def test_sink_pins_catch_planted_mistake(name):
             except (AssertionError, ValueError, FloatingPointError):
                 caught.append(pin_name)
         assert caught, f"no sink pin catches mutant {name}"
+
+
+# Planted mistakes in the given-O reading of D (D_i = rowsum(O_i * dO_i)),
+# caught by the given-O pins of tests/pins_bwd.py.
+GIVEN_O_MUTANTS = {
+    "given_o_ignored": ("if (c->O) {", "if (0) {"),
+    "given_o_row_of_head_zero": ("c->O + row * p->Dv", "c->O + (row % p->ql) * p->Dv"),
+    "given_o_sign_flipped": ("d_i += orow[d] * gr[d];", "d_i -= orow[d] * gr[d];"),
+    "given_o_not_reset": ("            d_i = 0.0f;\n            for (int64_t d = 0; d < p->Dv",
+                          "            for (int64_t d = 0; d < p->Dv"),
+    "given_o_squares_o": ("d_i += orow[d] * gr[d];", "d_i += orow[d] * orow[d];"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(GIVEN_O_MUTANTS))
+def test_given_o_pins_catch_planted_mistake(name):
+    from tests import pins_bwd
+    with tempfile.TemporaryDirectory() as tmp:
+        bwd = oracle.bind_bwd(_build_mutant(tmp, name, GIVEN_O_MUTANTS[name]))
+        caught = []
+        for pin_name, pin in pins_bwd.GIVEN_O_PINS:
+            try:
+                pin(bwd)
+            except (AssertionError, ValueError, FloatingPointError):
+                caught.append(pin_name)
+        assert caught, f"no given-O pin catches mutant {name}"
