@@ -142,6 +142,8 @@ def test_sink_gradient_written_without_rows():
 
 
 N_RANDOM = 16
+# one-key draws (kl = 1), where dP - D nearly cancels
+ONE_KEY_SEEDS = (366, 554)
 
 
 def _draw(i):
@@ -163,7 +165,7 @@ def _draw(i):
                 sinks=sinks)
 
 
-@pytest.mark.parametrize("i", range(N_RANDOM))
+@pytest.mark.parametrize("i", list(range(N_RANDOM)) + list(ONE_KEY_SEEDS))
 def test_random_backward_with_sinks_matches_oracle(i):
     c = _draw(i)
     case = (f"random{i}", c["B"], c["H"], c["Hkv"], c["ql"], c["kl"], c["D"], c["causal"],

@@ -33,6 +33,11 @@ from tests.test_gpu_bwd import check_grads
 pytestmark = pytest.mark.gpu
 
 N_CASES = 32
+# Seeds whose dQ or dK exceed the RMS bound when D is read from an O rounded
+# independently of the oracle's (most have 2 to 13 keys or one query row,
+# where dP - D nearly cancels): run beside the first N_CASES so that the
+# regime where O's rounding dominates stays covered.
+FEW_KEY_SEEDS = (458, 496, 625, 715, 785, 788, 938, 966, 969, 1203, 1242, 1317, 1768)
 
 
 def _draw(i):
@@ -74,7 +79,7 @@ def _mask(c, seed):
     return t.to("cuda:0"), ref
 
 
-@pytest.mark.parametrize("i", range(N_CASES))
+@pytest.mark.parametrize("i", list(range(N_CASES)) + list(FEW_KEY_SEEDS))
 def test_random_backward_matches_oracle(i):
     import torch
     c = _draw(i)
